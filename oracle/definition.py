@@ -1,0 +1,520 @@
+"""Mode D: the guided denoising step written out as its definition, in float64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).  Plain, slow and meant to
+be checked by eye against the pages.  Pages cited:
+
+* "12 · Samplers, schedulers and CFG" (ComfyUI guide, sampling chapter) --
+  sections "sigma sequence", "denoise below 1", "core of CFG", "the cfg = 1
+  optimisation", "calc_cond_batch()", "inpaint and mask", "data shapes of one
+  sampling step".
+* "10 · ModelPatcher and weight views" (ComfyUI guide, model-patcher chapter)
+  -- section "strength_model and strength_patch" (the affine form
+  W' = strength_model*W + strength_patch*dW, used here as an identity pin).
+* The SGLang diffusion BCG write-up (zwxr.cn news 258547) -- sections 2 "BCG
+  core mechanism" (bucket assignment snippet), 3 "bucket construction under
+  tensor parallelism" (BucketPlan, split/combine, [uncond... | cond...]
+  layout), 4 "debug chain" (scale 0 / 1 checks, norm logging, fp32 guidance),
+  5 "performance and edge cases" (guidance curve shapes).
+
+Readings taken where the pages are silent are stated at each function.  Pins
+(tests/test_oracle_pins.py) tie every function here to closed forms, brute
+force, special cases the pages fix or library routines.  ``area_box`` is the
+one rule with no such pin beyond self-consistency: parity unpinned for the
+rounding of fractional box coordinates.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# Storage rounding
+# --------------------------------------------------------------------------
+
+
+def round_bf16(x):
+    """Round to the nearest bfloat16 value, ties to even, returned as float64.
+
+    bfloat16 keeps 8 significant bits.  Writing x = m * 2**e with
+    0.5 <= |m| < 1 (frexp), the nearest 8-bit significand is rint(m * 256)
+    (numpy's rint rounds halves to even), so the rounded value is
+    rint(m*256)/256 * 2**e.  Valid in bfloat16's normal range (every value of
+    this path is far inside it); NaN and infinities pass through.
+    The half-precision guidance passage (SGLang write-up section 4, stage 4:
+    compute in fp32, cast back to the storage dtype) fixes the order: the
+    state is computed wide and rounded on store.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def to_storage(x, dtype: str):
+    """Value of ``x`` after a store in the storage dtype ("f32" or "bf16")."""
+    if dtype == "f32":
+        return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f64":
+        return np.asarray(x, np.float64)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# a1: sigma schedule ("12 · Samplers...", sections "sigma sequence" and
+# "denoise below 1")
+# --------------------------------------------------------------------------
+
+
+def base_steps(steps: int, denoise: float) -> int:
+    """Length of the base schedule built for ``denoise`` < 1.
+
+    The page says a longer base step count is built and its tail taken, but
+    gives no formula.  Reading: the smallest N with N*denoise >= steps,
+    i.e. ceil(steps/denoise) evaluated in float64; denoise = 1 gives steps.
+    (The regional + inpaint workload fixes 34 base steps for 20 kept at 0.6,
+    which a truncating int() would miss.)
+    """
+    if denoise >= 1.0:
+        return steps
+    return int(math.ceil(steps / denoise))
+
+
+def sigma_schedule(sigma_max: float, sigma_min: float, steps: int,
+                   denoise: float = 1.0):
+    """Descending log-linear sigmas, a terminal 0, and the denoise tail.
+
+    Base schedule of N = base_steps(steps, denoise) points, evenly spaced in
+    log(sigma) from sigma_max to sigma_min (both endpoints exact), then 0.
+    Keep the last steps+1 values.  Returned as float32 (the schedule is stored
+    in float32), plus N.  Computed point by point with the C library's
+    exp/log through ``math``.
+    """
+    N = base_steps(steps, denoise)
+    la, lb = math.log(sigma_max), math.log(sigma_min)
+    base = []
+    for i in range(N):
+        if i == 0:
+            s = sigma_max
+        elif i == N - 1:
+            s = sigma_min
+        else:
+            s = math.exp(la + (lb - la) * (i / (N - 1)))
+        base.append(s)
+    base.append(0.0)
+    sig = np.array(base[N - steps:], dtype=np.float64).astype(np.float32)
+    return sig, N
+
+
+# --------------------------------------------------------------------------
+# a2: bucket plan (SGLang write-up sections 2 and 3)
+# --------------------------------------------------------------------------
+
+
+def bucket_id(t: int, steps: int, nb: int) -> int:
+    """progress = t/steps; bucket = min(int(progress*nb), nb-1), in integers.
+
+    The page writes the progress as a float; its floor is taken here exactly
+    as floor(t*nb/steps) so the id is the one brute-force enumeration gives
+    (a float64 product misplaces some (t, steps, nb), e.g. t=3, steps=11,
+    nb=55).
+    """
+    return min((t * nb) // steps, nb - 1)
+
+
+def bucket_id_bruteforce(t: int, steps: int, nb: int) -> int:
+    """The unique b with b*steps <= t*nb < (b+1)*steps, clipped to nb-1."""
+    for b in range(nb + t * nb // max(steps, 1) + 2):
+        if b * steps <= t * nb < (b + 1) * steps:
+            return min(b, nb - 1)
+    raise AssertionError("no bucket")
+
+
+def bucket_table(kind: str, p0: float, p1: float, p2: float, nb: int):
+    """Scale per bucket from a continuous guidance curve (float32 table).
+
+    Section 2 of the write-up discretises a continuous curve into buckets,
+    constant within a bucket; section 5 names the shapes: linear decay (e.g.
+    2.0 -> 1.2) and front-high (strong for the first 20% of progress, weak
+    after).  Reading: bucket b samples the curve at u = b/(nb-1) (u = 0 when
+    nb = 1), so a linear curve hits both end values exactly.
+    """
+    out = []
+    for b in range(nb):
+        u = 0.0 if nb == 1 else b / (nb - 1)
+        if kind == "const":
+            v = p0
+        elif kind == "linear":
+            v = p0 + (p1 - p0) * u
+        elif kind == "front_high":
+            v = p0 if u < p2 else p1
+        else:
+            raise ValueError(kind)
+        out.append(v)
+    return np.array(out, dtype=np.float64).astype(np.float32)
+
+
+def area_box(frac, H: int, W: int):
+    """Area fractions (fy, fx, fh, fw) -> half-open latent slice (y0, y1, x0, x1).
+
+    "12 · Samplers...", calc_cond_batch(): area percentages are turned into
+    latent slices.  The rounding is not stated.  Reading: side lengths and
+    offsets round half up in float64, the side is clamped to [1, extent] and
+    the offset so that the box stays inside.  Parity unpinned (no example on
+    the pages); pinned only by bounds and self-consistency.
+    """
+    fy, fx, fh, fw = (float(v) for v in frac)
+    h = min(max(int(math.floor(fh * H + 0.5)), 1), H)
+    w = min(max(int(math.floor(fw * W + 0.5)), 1), W)
+    y0 = min(max(int(math.floor(fy * H + 0.5)), 0), H - h)
+    x0 = min(max(int(math.floor(fx * W + 0.5)), 0), W - w)
+    return (y0, y0 + h, x0, x0 + w)
+
+
+def covers_frame(boxes, strengths, H: int, W: int) -> bool:
+    """True when the boxes with positive strength cover every latent pixel."""
+    cov = np.zeros((H, W), bool)
+    for (y0, y1, x0, x1), s in zip(boxes, strengths):
+        if s > 0:
+            cov[y0:y1, x0:x1] = True
+    return bool(cov.all())
+
+
+def build_plan(t, steps: int, nb: int, table, override=None, covered=None):
+    """Bucket plan of one step: ids, scales, skip set, layout and offsets.
+
+    * bucket id per active sample (t in [0, steps)), scale = its override if
+      given (not NaN) else table[bucket]   -- write-up sections 2, 4 (stage 1:
+      re-bucketing each step with update_guidance_scales).
+    * the uncond branch is skipped when the scale is exactly 1 and nothing
+      forces it ("12 · Samplers...", section "the cfg = 1 optimisation");
+      a sample whose regional conds leave pixels uncovered is forced to keep
+      it (those pixels take the uncond prediction, see regional_cond).
+    * layout [uncond rows | cond rows] (write-up section 3, layout fix).
+      Reading: cond rows are the active samples stably ordered by
+      (bucket, sample id); the uncond half is the same order with skipped
+      samples removed (compacted).  bucket_offset / uncond_offset are the
+      exclusive prefix sums of per-bucket row counts in each half
+      (BucketPlan.bucket_offset).  Inactive samples get no rows.
+    """
+    t = np.asarray(t, np.int64)
+    n = t.size
+    table = np.asarray(table, np.float32)
+    if override is None:
+        override = np.full(n, np.nan, np.float32)
+    override = np.asarray(override, np.float32)
+    if covered is None:
+        covered = np.ones(n, bool)
+    bid = np.full(n, -1, np.int32)
+    scale = np.zeros(n, np.float32)
+    need_u = np.zeros(n, bool)
+    active = (t >= 0) & (t < steps)
+    for i in range(n):
+        if not active[i]:
+            continue
+        b = bucket_id(int(t[i]), steps, nb)
+        bid[i] = b
+        w = override[i] if not np.isnan(override[i]) else table[b]
+        scale[i] = w
+        need_u[i] = not (w == np.float32(1.0) and covered[i])
+    order = sorted((int(bid[i]), i) for i in range(n) if active[i])
+    order = np.array([i for _, i in order], np.int32)
+    n_act = order.size
+    uorder = np.array([i for i in order if need_u[i]], np.int32)
+    m = uorder.size
+    count = np.zeros(nb, np.int32)
+    ucount = np.zeros(nb, np.int32)
+    for i in order:
+        count[bid[i]] += 1
+        if need_u[i]:
+            ucount[bid[i]] += 1
+    offset = np.zeros(nb + 1, np.int32)
+    uoffset = np.zeros(nb + 1, np.int32)
+    for b in range(nb):
+        offset[b + 1] = offset[b] + count[b]
+        uoffset[b + 1] = uoffset[b] + ucount[b]
+    cond_row = np.full(n, -1, np.int32)
+    uncond_row = np.full(n, -1, np.int32)
+    for pos, i in enumerate(order):
+        cond_row[i] = m + pos
+    for pos, i in enumerate(uorder):
+        uncond_row[i] = pos
+    return dict(bucket_id=bid, scale=scale, need_uncond=need_u, order=order,
+                n_active=n_act, n_uncond=m, bucket_count=count,
+                bucket_offset=offset, uncond_offset=uoffset,
+                cond_row=cond_row, uncond_row=uncond_row)
+
+
+# --------------------------------------------------------------------------
+# a3: stand-in denoiser (closed form; the pages fix no network)
+# --------------------------------------------------------------------------
+
+
+def denoise(x, sigma: float, mu, s2: float):
+    """Posterior mean of Gaussian data N(mu_c, s^2) seen through noise sigma.
+
+    D(x, sigma) = (s^2 x + sigma^2 mu_c) / (s^2 + sigma^2), mu per channel
+    (x is [C,H,W], mu is [C]).  This replaces model.apply_model
+    ("12 · Samplers...", calc_cond_batch()).
+    """
+    x = np.asarray(x, np.float64)
+    mu = np.asarray(mu, np.float64)[:, None, None]
+    return (s2 * x + sigma * sigma * mu) / (s2 + sigma * sigma)
+
+
+# --------------------------------------------------------------------------
+# a4: regional conds ("12 · Samplers...", calc_cond_batch())
+# --------------------------------------------------------------------------
+
+
+def feather_1d(d, L: int, F: int):
+    """Linear edge ramp of F pixels along one axis of a box of length L.
+
+    Reading of "handle mask and feathering": weight (d+1)/F at the first
+    pixel, rising by 1/F per pixel until it reaches 1, on both ends; 0 outside
+    the box; F <= 0 means no feathering.
+    """
+    d = np.asarray(d, np.float64)
+    inside = (d >= 0) & (d < L)
+    if F <= 0:
+        return inside.astype(np.float64)
+    g = np.minimum(1.0, (d + 1.0) / F) * np.minimum(1.0, (L - d) / F)
+    return np.where(inside, g, 0.0)
+
+
+def region_weight(box, strength: float, H: int, W: int, F: int):
+    """strength * feathered box mask, [H,W] float64 (separable in y and x)."""
+    y0, y1, x0, x1 = box
+    gy = feather_1d(np.arange(H) - y0, y1 - y0, F)
+    gx = feather_1d(np.arange(W) - x0, x1 - x0, F)
+    return float(strength) * gy[:, None] * gx[None, :]
+
+
+def regional_cond(preds, weights, uncond):
+    """Accumulate region predictions by weight and normalise by the weight sum.
+
+    C(p) = sum_r w_r(p) * D_r(p) / sum_r w_r(p), summed in ascending r.
+    Where no region has weight the pages leave the value open.  Reading:
+    there is no conditional signal there, so the cond prediction is the
+    uncond prediction (zero guidance at that pixel).
+    """
+    num = np.zeros_like(uncond, dtype=np.float64)
+    den = np.zeros(uncond.shape[1:], np.float64)
+    for P, w in zip(preds, weights):
+        num = num + w[None] * P
+        den = den + w
+    safe = np.where(den > 0, den, 1.0)
+    return np.where(den[None] > 0, num / safe[None], uncond)
+
+
+# --------------------------------------------------------------------------
+# a5, a6: guidance combine and inpaint blend
+# --------------------------------------------------------------------------
+
+
+def cfg_combine(u, c, w: float):
+    """pred = uncond + cfg * (cond - uncond) ("12 · Samplers...", core of CFG).
+
+    With cfg = 1 the result is the cond prediction itself (section "the cfg = 1
+    optimisation"), returned exactly rather than through u + (c - u).
+    """
+    if w == 1.0:
+        return np.array(c, np.float64, copy=True)
+    return u + w * (c - u)
+
+
+def inpaint_blend(pred, x_orig, mask):
+    """mask*pred + (1-mask)*x_orig, mask [H,W] broadcast over channels.
+
+    "12 · Samplers...", section "inpaint and mask": each step the unmasked
+    region is blended with the original latent.  Reading: the blend is applied
+    to the denoised prediction before the sampler update, at every model
+    evaluation; mask 1 means "regenerate".
+    """
+    m = np.asarray(mask, np.float64)[None]
+    return m * pred + (1.0 - m) * x_orig
+
+
+# --------------------------------------------------------------------------
+# a3-a7 for one sample
+# --------------------------------------------------------------------------
+
+
+class SampleParams:
+    """Per-sample constants of the path (everything except x and t)."""
+
+    def __init__(self, mu_u, mu_c, s2, regions=(), feather=0, H=0, W=0,
+                 mask=None, x_orig=None):
+        self.mu_u = np.asarray(mu_u, np.float64)
+        self.mu_c = np.asarray(mu_c, np.float64)
+        self.s2 = float(s2)
+        # regions: list of (box, strength, mu_r[C])
+        self.regions = list(regions)
+        self.weights = [region_weight(b, s, H, W, feather) for b, s, _ in self.regions]
+        self.mask = None if mask is None else np.asarray(mask, np.float64)
+        self.x_orig = None if x_orig is None else np.asarray(x_orig, np.float64)
+
+
+def guided_pred(x, sigma: float, w: float, prm: SampleParams):
+    """The guided, blended prediction P(x, sigma) the sampler steps with."""
+    u = denoise(x, sigma, prm.mu_u, prm.s2)
+    if prm.regions:
+        preds = [denoise(x, sigma, mu_r, prm.s2) for _, _, mu_r in prm.regions]
+        c = regional_cond(preds, prm.weights, u)
+    else:
+        c = denoise(x, sigma, prm.mu_c, prm.s2)
+    pred = cfg_combine(u, c, w)
+    if prm.mask is not None:
+        pred = inpaint_blend(pred, prm.x_orig, prm.mask)
+    return pred
+
+
+def step(x, sigma: float, sigma_next: float, w: float, prm: SampleParams,
+         sampler: str):
+    """One sampler step from sigma to sigma_next (float64).
+
+    The pages give no update formula ("the sampler decides the update between
+    adjacent points"; some samplers evaluate the model more than once per
+    step).  Euler and Heun are taken from Karras et al. 2022 (EDM), Alg. 1:
+      d  = (x - P(x, sigma)) / sigma,  x' = x + (sigma' - sigma) d
+      Heun: x~ = x + h d, d' = (x~ - P(x~, sigma')) / sigma',
+            x' = x + h (d + d') / 2, with h = sigma' - sigma.
+    The step to sigma' = 0 is the Euler step, which lands on P(x, sigma)
+    exactly.
+    """
+    x = np.asarray(x, np.float64)
+    sigma = float(sigma)
+    sigma_next = float(sigma_next)
+    P = guided_pred(x, sigma, w, prm)
+    if sigma_next == 0.0:
+        return P
+    h = sigma_next - sigma
+    d = (x - P) / sigma
+    if sampler == "euler":
+        return x + h * d
+    if sampler == "heun":
+        xt = x + h * d
+        P2 = guided_pred(xt, sigma_next, w, prm)
+        d2 = (xt - P2) / sigma_next
+        return x + h * (d + d2) / 2.0
+    raise ValueError(sampler)
+
+
+def norm_stats(x, sigma: float, w: float, prm: SampleParams, need_uncond: bool):
+    """Per-sample norm check before/after guidance.
+
+    SGLang write-up section 4 logs hidden_states.norm(dim=-1).mean() before and
+    after apply_guidance.  Reading: per sample, the mean over (channel, row)
+    of the L2 norm over the last (width) axis, for the cond prediction C, the
+    uncond prediction U (0 when its branch is skipped) and the guided pred
+    (before the inpaint blend), from the evaluation at (x, sigma).
+    """
+    u = denoise(x, sigma, prm.mu_u, prm.s2)
+    if prm.regions:
+        preds = [denoise(x, sigma, mu_r, prm.s2) for _, _, mu_r in prm.regions]
+        c = regional_cond(preds, prm.weights, u)
+    else:
+        c = denoise(x, sigma, prm.mu_c, prm.s2)
+    pred = cfg_combine(u, c, w)
+    nrm = lambda v: float(np.sqrt((v * v).sum(axis=-1)).mean())
+    return np.array([nrm(c), nrm(u) if need_uncond else 0.0, nrm(pred)])
+
+
+# --------------------------------------------------------------------------
+# Whole trajectory
+# --------------------------------------------------------------------------
+
+
+def sample_params(inp, i: int, sig_dtype=np.float64):
+    """SampleParams of sample i from a ``workloads.Inputs``."""
+    sp = inp.spec
+    regions = []
+    for r in range(int(inp.region_count[i])):
+        box = area_box(inp.region_frac[i, r], sp.H, sp.W)
+        regions.append((box, float(inp.region_strength[i, r]), inp.mu_region[i, r]))
+    return SampleParams(inp.mu_uncond[i], inp.mu_cond[i], sp.s2, regions,
+                        sp.feather, sp.H, sp.W,
+                        None if inp.mask is None else inp.mask[i, 0],
+                        None if inp.x_orig is None else inp.x_orig[i])
+
+
+def coverage(inp):
+    """Per-sample full-coverage flag (samples without regions are covered)."""
+    sp = inp.spec
+    out = np.ones(sp.n, bool)
+    for i in range(sp.n):
+        k = int(inp.region_count[i])
+        if k > 0:
+            boxes = [area_box(inp.region_frac[i, r], sp.H, sp.W) for r in range(k)]
+            out[i] = covers_frame(boxes, inp.region_strength[i, :k], sp.H, sp.W)
+    return out
+
+
+def run_setup(inp):
+    """Schedule, bucket table, coverage and per-sample params of a workload."""
+    sp = inp.spec
+    sig, _ = sigma_schedule(sp.sigma_max, sp.sigma_min, sp.steps, sp.denoise)
+    c = sp.curve
+    table = bucket_table(c.kind, c.p0, c.p1, c.p2, sp.num_buckets)
+    return sig, table, coverage(inp)
+
+
+def init_latent(inp, sig, storage: str):
+    """x = latent + noise * sigma[start] per sample, stored in the storage dtype.
+
+    "12 · Samplers...", section "disable_noise": a latent input still follows
+    the sigma trajectory, so the start is the latent plus noise at the first
+    sigma of the sample.  The latent is the original latent when inpainting,
+    zero otherwise.  Reading for mixed progress: sample i joins at its own
+    start step with noise at that level.
+    """
+    sp = inp.spec
+    x = np.asarray(inp.noise, np.float64) * sig.astype(np.float64)[
+        inp.start_step][:, None, None, None]
+    if inp.x_orig is not None:
+        x = np.asarray(inp.x_orig, np.float64) + x
+    return to_storage(x, storage)
+
+
+def trajectory(inp, storage: str | None = None, launches: int | None = None,
+               samples=None, keep=False):
+    """Run the sampler loop in mode D.
+
+    Launch k moves every active sample i (t_i = start_i + k < steps) one step.
+    The state is stored in the workload's storage dtype after every step
+    (``storage`` overrides it, "f64" keeps it unrounded).  Returns the final
+    state [n,C,H,W] (float64 values), and the list of states if ``keep``.
+    """
+    sp = inp.spec
+    storage = storage or sp.dtype
+    sig, table, cov = run_setup(inp)
+    sig64 = sig.astype(np.float64)
+    idx = range(sp.n) if samples is None else samples
+    prms = {i: sample_params(inp, i) for i in idx}
+    x = init_latent(inp, sig, storage)
+    states = [x.copy()] if keep else None
+    L = sp.steps if launches is None else launches
+    for k in range(L):
+        t = inp.start_step.astype(np.int64) + k
+        plan = build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+        for i in idx:
+            if plan["bucket_id"][i] < 0:
+                continue
+            ti = int(t[i])
+            x[i] = to_storage(step(x[i], sig64[ti], sig64[ti + 1],
+                                   float(plan["scale"][i]), prms[i], sp.sampler),
+                              storage)
+        if keep:
+            states.append(x.copy())
+    return (x, states) if keep else x
+
+
+def pf_ode_exact(x, sigma: float, sigma_next: float, mean, s2: float):
+    """Exact probability-flow solution for Gaussian data N(mean, s^2).
+
+    With D(x, sigma) = (s^2 x + sigma^2 mean)/(s^2 + sigma^2) the ODE
+    dx/dsigma = (x - D)/sigma = (x - mean) sigma/(s^2 + sigma^2) integrates to
+    x(sigma') = mean + (x - mean) sqrt((s^2 + sigma'^2)/(s^2 + sigma^2)).
+    """
+    return mean + (x - mean) * math.sqrt((s2 + sigma_next ** 2) / (s2 + sigma ** 2))

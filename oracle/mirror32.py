@@ -1,0 +1,234 @@
+"""Mode M: the guided step as a fixed sequence of IEEE float32 operations.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+Why this mode exists: with bf16 storage the stored state is an 8-bit
+significand code chosen from a float32 result.  For |x| >= 4 one bf16 ulp is
+0.03125, above the 2e-2 final-latent bound, so the expected code has to be
+decided in the same precision and order as the device decides it: every
+operation below is one correctly rounded float32 operation (numpy float32
+arithmetic; no fused multiply-add; division correctly rounded), evaluated in
+the order written.  Mode M is pinned to mode D (``definition``) by the
+per-step tolerance and to the exact special cases (scale 0 -> uncond, scale 1
+-> cond, mask 0 -> original latent, ...).
+
+The evaluation order (a specification both sides implement independently):
+
+per sample, from sigma = sig[t], sigma' = sig[t+1]:
+    v = sigma*sigma; den = s2 + v; a = s2/den; b_k[c] = (v*mu_k[c])/den
+    Euler: q = (sigma' - sigma)/sigma
+    Heun:  h = sigma' - sigma; i = 1/sigma; i' = 1/sigma'; hh = h*0.5,
+           and a', b'_k from sigma' as above
+per pixel (regional launches):
+    f_r = float(ny_r*nx_r) * (1/F^4)  with ny = min(dy+1,F)*min(h_r-dy,F),
+                                           nx likewise, 0 outside the box
+    w_r = strength_r*f_r; W = ((w_0 + w_1) + w_2) ...
+    covered = W > 0; iW = 1/W (0 if not covered); wh_r = w_r*iW
+    inpaint: om = 1 - m
+per element:
+    ax = a*x; u = ax + bu[c]
+    c  = ax + bc[c]                                (no regions)
+       = ((wh_0*(ax + br_0[c])) + wh_1*(ax + br_1[c])) + ...   (regions)
+    pred = u + w*(c - u)                     (scale != 1, no regions)
+         = u + (covered ? w : 0)*(c - u)     (scale != 1, regions)
+         = covered ? c : u                   (scale == 1, uncond kept)
+         = c                                 (uncond skipped)
+    pb = m*pred + om*xo  (inpaint)  else pred
+    sigma' == 0: x' = pb
+    Euler: x' = x + (x - pb)*q
+    Heun:  d = (x - pb)*i; xt = x + h*d; pb2 = P'(xt);
+           d2 = (xt - pb2)*i'; x' = x + (d + d2)*hh
+    store float32, or round to bf16 (nearest, ties to even)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import definition as D
+
+f32 = np.float32
+
+
+def _store(x, dtype):
+    x = np.asarray(x, np.float32)
+    if dtype == "bf16":
+        return D.round_bf16(x).astype(np.float32)
+    return x
+
+
+def _ramp_counts(d, L, F):
+    """Integer feather numerators min(d+1,F)*min(L-d,F) (0 outside [0,L))."""
+    F = max(int(F), 1)
+    d = np.asarray(d, np.int64)
+    num = np.minimum(d + 1, F) * np.minimum(L - d, F)
+    return np.where((d >= 0) & (d < L), num, 0)
+
+
+def pixel_weights(boxes, strengths, H, W, F):
+    """Normalised per-pixel region weights wh[R,H,W] and the covered flag."""
+    Fe = max(int(F), 1)
+    inv_f4 = f32(1.0) / f32(Fe * Fe * Fe * Fe)
+    ws = []
+    for (y0, y1, x0, x1), s in zip(boxes, strengths):
+        ny = _ramp_counts(np.arange(H) - y0, y1 - y0, Fe)
+        nx = _ramp_counts(np.arange(W) - x0, x1 - x0, Fe)
+        f = (ny[:, None] * nx[None, :]).astype(np.float32) * inv_f4
+        ws.append(f32(s) * f)
+    Wsum = ws[0]
+    for w in ws[1:]:
+        Wsum = Wsum + w
+    covered = Wsum > f32(0)
+    iW = np.where(covered, f32(1.0) / np.where(covered, Wsum, f32(1)), f32(0)).astype(np.float32)
+    return [w * iW for w in ws], covered, Wsum
+
+
+class Params32:
+    """Per-sample constants in float32."""
+
+    def __init__(self, mu_u, mu_c, s2, boxes=(), strengths=(), mu_r=(), feather=0,
+                 H=0, W=0, mask=None, x_orig=None):
+        self.mu_u = np.asarray(mu_u, np.float32)
+        self.mu_c = np.asarray(mu_c, np.float32)
+        self.s2 = f32(s2)
+        self.mu_r = [np.asarray(m, np.float32) for m in mu_r]
+        self.nr = len(self.mu_r)
+        if self.nr:
+            self.wh, self.covered, self.wsum = pixel_weights(boxes, strengths, H, W, feather)
+        self.mask = None if mask is None else np.asarray(mask, np.float32)
+        self.x_orig = None if x_orig is None else np.asarray(x_orig, np.float32)
+
+
+def _coef(sigma, prm):
+    v = sigma * sigma
+    den = prm.s2 + v
+    a = prm.s2 / den
+    bu = (v * prm.mu_u) / den
+    bc = (v * prm.mu_c) / den
+    br = [(v * m) / den for m in prm.mu_r]
+    return a, bu, bc, br
+
+
+def _pred(x, sigma, w, mode, prm):
+    a, bu, bc, br = _coef(sigma, prm)
+    ax = a * x
+    u = ax + bu[:, None, None]
+    if prm.nr == 0:
+        c = ax + bc[:, None, None]
+    else:
+        c = prm.wh[0][None] * (ax + br[0][:, None, None])
+        for r in range(1, prm.nr):
+            c = c + prm.wh[r][None] * (ax + br[r][:, None, None])
+    if mode == "C":
+        pred = c
+    elif mode == "B":
+        pred = c if prm.nr == 0 else np.where(prm.covered[None], c, u)
+    else:
+        if prm.nr == 0:
+            pred = u + w * (c - u)
+        else:
+            weff = np.where(prm.covered, w, f32(0)).astype(np.float32)
+            pred = u + weff[None] * (c - u)
+    if prm.mask is not None:
+        m = prm.mask[None]
+        om = f32(1) - m
+        pred = m * pred + om * prm.x_orig
+    return pred.astype(np.float32)
+
+
+def step32(x, sigma, sigma_next, w, need_uncond, prm, sampler):
+    """One step in mode M.  ``x`` float32 [C,H,W]; returns float32 (unstored)."""
+    x = np.asarray(x, np.float32)
+    sigma, sigma_next, w = f32(sigma), f32(sigma_next), f32(w)
+    mode = "C" if not need_uncond else ("B" if w == f32(1) else "A")
+    pb = _pred(x, sigma, w, mode, prm)
+    if sigma_next == f32(0):
+        return pb
+    if sampler == "euler":
+        q = (sigma_next - sigma) / sigma
+        return x + (x - pb) * q
+    h = sigma_next - sigma
+    i1 = f32(1) / sigma
+    i2 = f32(1) / sigma_next
+    hh = h * f32(0.5)
+    d = (x - pb) * i1
+    xt = x + h * d
+    pb2 = _pred(xt, sigma_next, w, mode, prm)
+    d2 = (xt - pb2) * i2
+    return x + (d + d2) * hh
+
+
+def params32(inp, i):
+    sp = inp.spec
+    k = int(inp.region_count[i])
+    boxes = [D.area_box(inp.region_frac[i, r], sp.H, sp.W) for r in range(k)]
+    return Params32(inp.mu_uncond[i], inp.mu_cond[i], sp.s2, boxes,
+                    inp.region_strength[i, :k], [inp.mu_region[i, r] for r in range(k)],
+                    sp.feather, sp.H, sp.W,
+                    None if inp.mask is None else inp.mask[i, 0],
+                    None if inp.x_orig is None else inp.x_orig[i])
+
+
+def init_latent32(inp, sig):
+    sp = inp.spec
+    x = inp.noise.astype(np.float32) * sig[inp.start_step][:, None, None, None]
+    if inp.x_orig is not None:
+        x = inp.x_orig.astype(np.float32) + x
+    return _store(x, sp.dtype)
+
+
+def trajectory32(inp, launches=None, samples=None, keep=False):
+    """The sampler loop in mode M (same plan and schedule as mode D)."""
+    sp = inp.spec
+    sig, table, cov = D.run_setup(inp)
+    idx = range(sp.n) if samples is None else samples
+    prms = {i: params32(inp, i) for i in idx}
+    x = init_latent32(inp, sig)
+    states = [x.copy()] if keep else None
+    L = sp.steps if launches is None else launches
+    for k in range(L):
+        t = inp.start_step.astype(np.int64) + k
+        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+        for i in idx:
+            if plan["bucket_id"][i] < 0:
+                continue
+            ti = int(t[i])
+            x[i] = _store(step32(x[i], sig[ti], sig[ti + 1], plan["scale"][i],
+                                 bool(plan["need_uncond"][i]), prms[i], sp.sampler),
+                          sp.dtype)
+        if keep:
+            states.append(x.copy())
+    return (x, states) if keep else x
+
+
+def area_accumulate32(crops, boxes, strengths, H, W, F, fallback=None):
+    """Standalone regional accumulation in mode M.
+
+    ``crops[r]`` is the [C, h_r, w_r] prediction of region r.  Returns the
+    normalised cond prediction [C,H,W] (fallback, else 0, where no region has
+    weight) and the weight sum [H,W].  Terms of regions that do not contain a
+    pixel are left out of its sum (they are exact zeros in the fused step).
+    """
+    wh, covered, wsum = pixel_weights(boxes, strengths, H, W, F)
+    C = crops[0].shape[0]
+    acc = np.zeros((C, H, W), np.float32)
+    started = np.zeros((H, W), bool)
+    for r, (y0, y1, x0, x1) in enumerate(boxes):
+        full = np.zeros((C, H, W), np.float32)
+        full[:, y0:y1, x0:x1] = crops[r]
+        inb = np.zeros((H, W), bool)
+        inb[y0:y1, x0:x1] = True
+        term = wh[r][None] * full
+        acc = np.where(inb[None], np.where(started[None], acc + term, term), acc)
+        started |= inb
+    if fallback is not None:
+        acc = np.where(covered[None], acc, np.asarray(fallback, np.float32))
+    else:
+        acc = np.where(covered[None], acc, f32(0))
+    return acc.astype(np.float32), wsum
+
+
+def mask_blend32(a, b, mask, dtype):
+    """out = m*a + (1-m)*b in float32, mask [.,1,H,W] broadcast over channels."""
+    m = np.asarray(mask, np.float32)
+    om = f32(1) - m
+    return _store(m * np.asarray(a, np.float32) + om * np.asarray(b, np.float32), dtype)

@@ -1,0 +1,437 @@
+"""Pins of the CPU oracle to facts fixed outside itself (no GPU needed).
+
+Each test ties an oracle function to a closed form, brute force, a special
+case the pages fix, or a library routine -- chosen so that a dropped term, a
+wrong sign or index, or a transposed operand fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import definition as D
+from oracle import mirror32 as M
+
+
+# ---------------------------------------------------------------- bf16 store
+
+def test_round_bf16_matches_library_rne():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    # exact ties: a bf16 value plus half an ulp, both parities of the last bit
+    base = torch.from_numpy(x[:2000]).to(torch.bfloat16).to(torch.float32).numpy()
+    bits = base.view(np.uint32) | np.uint32(0x8000)
+    ties = bits.view(np.float32)
+    x = np.concatenate([x, ties, np.float32([0.0, -0.0, 1.0, -1.0, 3.0e38])])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = D.round_bf16(x).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_round_bf16_nan_inf_pass_through():
+    v = D.round_bf16(np.array([np.nan, np.inf, -np.inf]))
+    assert np.isnan(v[0]) and v[1] == np.inf and v[2] == -np.inf
+
+
+# ---------------------------------------------------------------- schedule
+
+@pytest.mark.parametrize("steps,denoise", [(10, 1.0), (50, 1.0), (30, 1.0), (20, 0.6), (7, 0.35)])
+def test_sigma_schedule_closed_form(steps, denoise):
+    sig, N = D.sigma_schedule(14.6, 0.03, steps, denoise)
+    assert sig.dtype == np.float32 and sig.size == steps + 1
+    assert sig[-1] == 0.0
+    assert sig[-2] == np.float32(0.03)
+    assert N * denoise >= steps and (N - 1) * denoise < steps
+    # independent closed form: the power form sigma_max*(min/max)**(i/(N-1))
+    i = np.arange(N - steps, N)
+    pw = 14.6 * (0.03 / 14.6) ** (i / (N - 1))
+    np.testing.assert_allclose(sig[:-1], pw, rtol=2e-7)
+    # log-equal spacing (constant ratio)
+    r = np.log(sig[1:-1].astype(np.float64)) - np.log(sig[:-2].astype(np.float64))
+    np.testing.assert_allclose(r, math.log(0.03 / 14.6) / (N - 1), atol=3e-7)
+    if denoise == 1.0:
+        assert sig[0] == np.float32(14.6) and N == steps
+
+
+def test_denoise_tail_of_regional_workload():
+    # 20 steps at denoise 0.6 are taken from a 34-step base schedule.
+    sig, N = D.sigma_schedule(14.6, 0.03, 20, 0.6)
+    assert N == 34
+    assert abs(float(sig[0]) - 14.6 * (0.03 / 14.6) ** (14 / 33)) < 2e-7
+    full, _ = D.sigma_schedule(14.6, 0.03, 34, 1.0)
+    assert np.array_equal(full[14:], sig)
+
+
+# ---------------------------------------------------------------- buckets
+
+def test_bucket_id_bruteforce_enumeration():
+    for steps in range(1, 61):
+        for nb in range(1, 21):
+            for t in range(steps):
+                assert D.bucket_id(t, steps, nb) == D.bucket_id_bruteforce(t, steps, nb)
+
+
+def test_bucket_id_matches_page_formula_on_workloads():
+    # the write-up's float formula min(int(t/steps*nb), nb-1) for every
+    # (steps, nb) pair the workloads use
+    for steps, nb in [(10, 1), (50, 8), (30, 16), (20, 8)]:
+        for t in range(steps):
+            assert D.bucket_id(t, steps, nb) == min(int(t / steps * nb), nb - 1)
+
+
+def test_bucket_id_exact_where_float_product_fails():
+    assert min(int(3 / 11 * 55), 54) == 14        # float64 rounding below 15
+    assert D.bucket_id(3, 11, 55) == 15           # 3*55 = 165 = 15*11
+
+
+def test_bucket_tables():
+    lin = D.bucket_table("linear", 2.0, 1.2, 0.0, 8)
+    assert lin[0] == np.float32(2.0) and lin[-1] == np.float32(1.2)
+    assert np.all(np.diff(lin) < 0)
+    np.testing.assert_allclose(lin, np.linspace(2.0, 1.2, 8), rtol=1e-7)
+    assert np.array_equal(D.bucket_table("const", 7.0, 0, 0, 1), np.float32([7.0]))
+    fh = D.bucket_table("front_high", 2.0, 1.2, 0.2, 16)
+    # front-high at 30 steps: exactly the first 20% (6 steps) are strong
+    per_step = [fh[D.bucket_id(t, 30, 16)] for t in range(30)]
+    assert per_step[:6] == [np.float32(2.0)] * 6
+    assert per_step[6:] == [np.float32(1.2)] * 24
+
+
+# ---------------------------------------------------------------- plan
+
+def _brute_plan_checks(t, steps, nb, table, override, covered, plan):
+    n = len(t)
+    act = [i for i in range(n) if 0 <= t[i] < steps]
+    assert plan["n_active"] == len(act)
+    assert sorted(plan["order"].tolist()) == act
+    # stable (bucket, id) order
+    keys = [(int(plan["bucket_id"][i]), i) for i in plan["order"]]
+    assert keys == sorted(keys)
+    for b in range(nb):
+        cnt = sum(1 for i in act if D.bucket_id(t[i], steps, nb) == b)
+        assert plan["bucket_count"][b] == cnt
+        assert plan["bucket_offset"][b + 1] - plan["bucket_offset"][b] == cnt
+        ucnt = sum(1 for i in act if D.bucket_id(t[i], steps, nb) == b and plan["need_uncond"][i])
+        assert plan["uncond_offset"][b + 1] - plan["uncond_offset"][b] == ucnt
+    m = plan["n_uncond"]
+    for i in range(n):
+        if i not in act:
+            assert plan["bucket_id"][i] == -1 and plan["cond_row"][i] == -1
+            assert plan["uncond_row"][i] == -1
+            continue
+        w = override[i] if not np.isnan(override[i]) else table[plan["bucket_id"][i]]
+        assert plan["scale"][i] == w
+        assert plan["need_uncond"][i] == (not (w == 1.0 and covered[i]))
+        # rows: cond rows follow the uncond half; within each half samples of
+        # bucket b sit inside [offset[b], offset[b+1])
+        b = plan["bucket_id"][i]
+        r = plan["cond_row"][i] - m
+        assert plan["bucket_offset"][b] <= r < plan["bucket_offset"][b + 1]
+        if plan["need_uncond"][i]:
+            u = plan["uncond_row"][i]
+            assert plan["uncond_offset"][b] <= u < plan["uncond_offset"][b + 1]
+        else:
+            assert plan["uncond_row"][i] == -1
+    assert sorted(plan["cond_row"][plan["cond_row"] >= 0].tolist()) == list(range(m, m + len(act)))
+    assert sorted(plan["uncond_row"][plan["uncond_row"] >= 0].tolist()) == list(range(m))
+
+
+def test_plan_bruteforce_random():
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        n = int(rng.integers(1, 40))
+        steps = int(rng.integers(1, 60))
+        nb = int(rng.integers(1, 17))
+        t = rng.integers(-3, steps + 3, size=n)
+        table = D.bucket_table("linear", 2.0, 1.0, 0, nb)
+        ov = np.where(rng.random(n) < 0.3, 1.0, np.nan).astype(np.float32)
+        cov = rng.random(n) < 0.8
+        plan = D.build_plan(t, steps, nb, table, ov, cov)
+        _brute_plan_checks(t, steps, nb, table, ov, cov, plan)
+
+
+def test_plan_layout_scale_one_samples_skip():
+    # throughput workload: a quarter of the samples carry cfg 1 and lose
+    # their uncond row; the rest keep it
+    inp = W.make_inputs(W.config("throughput_bf16_heun"))
+    sig, table, cov = D.run_setup(inp)
+    plan = D.build_plan(np.zeros(64, np.int64), 30, 16, table, inp.cfg_override, cov)
+    assert plan["n_active"] == 64 and plan["n_uncond"] == 48
+    assert set(np.nonzero(~plan["need_uncond"])[0]) == set(np.nonzero(inp.cfg_override == 1.0)[0])
+
+
+# ---------------------------------------------------------------- areas
+
+def test_area_box_bounds_and_sizes():
+    inp = W.make_inputs(W.config("regional_inpaint"))
+    for i in range(16):
+        for r in range(3):
+            y0, y1, x0, x1 = D.area_box(inp.region_frac[i, r], 128, 128)
+            assert 0 <= y0 < y1 <= 128 and 0 <= x0 < x1 <= 128
+            assert round(0.2 * 128) - 1 <= y1 - y0 <= round(0.8 * 128) + 1
+    assert D.area_box((0, 0, 1, 1), 40, 72) == (0, 40, 0, 72)
+    assert D.area_box((0.5, 0.25, 0.5, 0.5), 8, 8) == (4, 8, 2, 6)
+    assert D.area_box((0.99, 0.99, 0.001, 0.001), 8, 8) == (7, 8, 7, 8)
+
+
+def test_feather_dyadic_values_and_symmetry():
+    wgt = D.region_weight((10, 40, 20, 60), 1.0, 64, 80, 8)
+    assert wgt[25, 40] == 1.0                 # interior
+    assert wgt[10, 40] == 1 / 8               # top edge
+    assert wgt[39, 40] == 1 / 8               # bottom edge
+    assert wgt[10, 20] == 1 / 64              # corner
+    assert wgt[13, 40] == 4 / 8
+    assert wgt[9, 40] == 0 and wgt[40, 40] == 0 and wgt[25, 19] == 0 and wgt[25, 60] == 0
+    # separable and mirror-symmetric inside the box
+    box = wgt[10:40, 20:60]
+    assert np.array_equal(box, box[::-1, :]) and np.array_equal(box, box[:, ::-1])
+    assert np.allclose(box, np.outer(box[:, 20], box[15, :]))
+    # no feathering: the box indicator
+    w0 = D.region_weight((1, 3, 2, 5), 2.0, 4, 6, 0)
+    ind = np.zeros((4, 6)); ind[1:3, 2:5] = 2.0
+    assert np.array_equal(w0, ind)
+
+
+def test_feather_integer_form_equals_ramp_product():
+    # the mirror's integer numerators over F^4 are the same dyadic weights
+    for F in (1, 2, 3, 8):
+        for L in (1, 2, 5, 17, 30):
+            ny = M._ramp_counts(np.arange(-2, L + 2), L, F)
+            g = D.feather_1d(np.arange(-2, L + 2), L, F)
+            np.testing.assert_allclose(ny / F ** 2, g, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- denoiser
+
+def test_denoiser_is_gaussian_posterior_mean_by_quadrature():
+    # E[y | x] for y ~ N(mu, s^2), x = y + sigma*eps, by direct numerical
+    # integration over y (independent of the closed form).
+    s2, mu = 0.25, np.array([0.7])
+    y = np.linspace(-12, 12, 400001)
+    for sigma in (0.03, 0.5, 3.0, 14.6):
+        for x in (-4.0, 0.2, 9.0):
+            p = np.exp(-(y - mu[0]) ** 2 / (2 * s2) - (x - y) ** 2 / (2 * sigma ** 2))
+            want = (y * p).sum() / p.sum()
+            got = D.denoise(np.full((1, 1, 1), x), sigma, mu, s2)[0, 0, 0]
+            assert abs(got - want) < 1e-7 * max(1.0, abs(want))
+
+
+def test_denoiser_limits():
+    x = np.random.default_rng(0).standard_normal((2, 3, 3))
+    mu = np.array([0.3, -1.0])
+    assert np.array_equal(D.denoise(x, 0.0, mu, 0.25), x)
+    np.testing.assert_allclose(D.denoise(x, 1e8, mu, 0.25), np.broadcast_to(mu[:, None, None], x.shape), atol=1e-12)
+
+
+# ---------------------------------------------------------------- regions
+
+def _region_setup(seed=0, H=20, W=24, F=3):
+    rng = np.random.default_rng(seed)
+    C = 2
+    x = rng.standard_normal((C, H, W))
+    mus = [rng.standard_normal(C) for _ in range(3)]
+    boxes = [(0, 12, 0, 15), (5, 20, 8, 24), (3, 9, 2, 7)]
+    strengths = [0.7, 1.3, 0.9]
+    wts = [D.region_weight(b, s, H, W, F) for b, s in zip(boxes, strengths)]
+    return x, mus, boxes, strengths, wts
+
+
+def test_regional_cond_closed_form_mean():
+    x, mus, boxes, strengths, wts = _region_setup()
+    sigma, s2 = 1.7, 0.25
+    u = D.denoise(x, sigma, np.array([0.1, 0.2]), s2)
+    preds = [D.denoise(x, sigma, m, s2) for m in mus]
+    c = D.regional_cond(preds, wts, u)
+    wsum = sum(wts)
+    cov = wsum > 0
+    mbar = sum(w[None] * m[:, None, None] for w, m in zip(wts, mus)) / np.where(cov, wsum, 1)[None]
+    closed = (s2 * x + sigma ** 2 * mbar) / (s2 + sigma ** 2)
+    np.testing.assert_allclose(c[:, cov], closed[:, cov], rtol=1e-13, atol=1e-13)
+    assert np.array_equal(c[:, ~cov], u[:, ~cov])
+    assert (~cov).any()
+
+
+def test_regional_cond_invariances():
+    x, mus, boxes, strengths, wts = _region_setup(1)
+    u = D.denoise(x, 2.0, np.zeros(2), 0.25)
+    preds = [D.denoise(x, 2.0, m, 0.25) for m in mus]
+    c = D.regional_cond(preds, wts, u)
+    np.testing.assert_allclose(D.regional_cond(preds, [3.5 * w for w in wts], u), c, rtol=1e-13, atol=1e-15)
+    zero = [0 * wts[0]]
+    np.testing.assert_allclose(D.regional_cond(preds + [preds[0] * 9], wts + zero, u), c, rtol=0, atol=0)
+    # one full-frame region reproduces its own prediction
+    full = [D.region_weight((0, 20, 0, 24), 0.8, 20, 24, 0)]
+    np.testing.assert_allclose(D.regional_cond(preds[:1], full, u), preds[0], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- combine / blend
+
+def test_cfg_combine_special_cases_and_affine_form():
+    rng = np.random.default_rng(5)
+    u, c = rng.standard_normal((2, 3, 4, 5))
+    assert np.array_equal(D.cfg_combine(u, c, 0.0), u)          # scale 0 -> uncond
+    assert np.array_equal(D.cfg_combine(u, c, 1.0), c)          # scale 1 -> cond
+    for w in (0.3, 1.2, 2.0, 7.0):
+        # W' = sm*W + sp*dW with W = u, dW = c - u, sm = 1, sp = w, and the
+        # equivalent (1-w) u + w c
+        np.testing.assert_allclose(D.cfg_combine(u, c, w), (1 - w) * u + w * c, rtol=1e-13, atol=1e-13)
+        u2, c2 = rng.standard_normal((2, 3, 4, 5))
+        lhs = D.cfg_combine(2 * u - 0.5 * u2, 2 * c - 0.5 * c2, w)
+        rhs = 2 * D.cfg_combine(u, c, w) - 0.5 * D.cfg_combine(u2, c2, w)
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_inpaint_blend_extremes():
+    rng = np.random.default_rng(6)
+    p, xo = rng.standard_normal((2, 2, 3, 4))
+    assert np.array_equal(D.inpaint_blend(p, xo, np.ones((3, 4))), p)
+    assert np.array_equal(D.inpaint_blend(p, xo, np.zeros((3, 4))), xo)
+
+
+# ---------------------------------------------------------------- sampler
+
+def _tiny_prm():
+    rng = np.random.default_rng(11)
+    return D.SampleParams(rng.standard_normal(2), rng.standard_normal(2), 0.25), rng
+
+
+@pytest.mark.parametrize("sampler,order", [("euler", 1), ("heun", 2)])
+def test_sampler_converges_to_probability_flow(sampler, order):
+    prm, rng = _tiny_prm()
+    w = 7.0
+    x0 = 14.6 * rng.standard_normal((2, 3, 3))
+    mean = (prm.mu_u + w * (prm.mu_c - prm.mu_u))[:, None, None]
+    exact = D.pf_ode_exact(x0, 14.6, 0.03, mean, 0.25)
+    errs = []
+    for N in (10, 20, 40, 80, 160):
+        sig = [14.6 * (0.03 / 14.6) ** (i / (N - 1)) for i in range(N)]
+        x = x0.copy()
+        for k in range(N - 1):
+            x = D.step(x, sig[k], sig[k + 1], w, prm, sampler)
+        errs.append(np.abs(x - exact).max())
+    ratios = [errs[i] / errs[i + 1] for i in range(len(errs) - 1)]
+    target = 2.0 ** order
+    assert all(abs(r - target) < 0.25 * target for r in ratios[1:]), ratios
+    assert errs[-1] < (0.05 if order == 1 else 0.01)
+
+
+def test_final_step_lands_on_prediction():
+    prm, rng = _tiny_prm()
+    x = rng.standard_normal((2, 3, 3))
+    for s in ("euler", "heun"):
+        assert np.array_equal(D.step(x, 0.03, 0.0, 2.0, prm, s), D.guided_pred(x, 0.03, 2.0, prm))
+
+
+def test_unmasked_region_follows_original_plus_noise():
+    sp = W.small_spec(n=2, C=2, H=10, W=12, inpaint=True, regions=0, steps=8,
+                      mixed_start=False, skip_frac=0.0)
+    inp = W.make_inputs(sp)
+    inp.mask[:, :, :, :6] = 0.0
+    sig, _ = D.sigma_schedule(sp.sigma_max, sp.sigma_min, sp.steps)
+    _, states = D.trajectory(inp, storage="f64", keep=True)
+    for k in range(sp.steps):
+        want = (inp.x_orig[:, :, :, :6].astype(np.float64)
+                + inp.noise[:, :, :, :6].astype(np.float64) * float(sig[k]))
+        np.testing.assert_allclose(states[k][:, :, :, :6], want, atol=1e-11)
+    assert np.array_equal(states[-1][:, :, :, :6], inp.x_orig[:, :, :, :6])
+    # mask 1 everywhere is the plain run
+    inp1 = W.make_inputs(sp); inp1.mask[:] = 1.0
+    plain = W.make_inputs(dataclasses_replace(sp, inpaint=False))
+    plain.x_orig = inp1.x_orig  # same starting latent
+    x_mask1 = D.trajectory(inp1, storage="f64")
+    x_plain = D.trajectory(plain, storage="f64")
+    assert np.array_equal(x_mask1, x_plain)
+
+
+def dataclasses_replace(sp, **kw):
+    import dataclasses
+    return dataclasses.replace(sp, **kw)
+
+
+def test_scale_one_skip_ignores_uncond_and_scale_zero_ignores_cond():
+    sp = W.small_spec(n=3, C=2, H=6, W=8, steps=5, mixed_start=False, skip_frac=0.0,
+                      curve=W.Curve("const", 1.0), num_buckets=1)
+    inp = W.make_inputs(sp)
+    a = D.trajectory(inp, storage="f64")
+    inp.mu_uncond[:] = 99.0
+    assert np.array_equal(D.trajectory(inp, storage="f64"), a)
+    sp0 = dataclasses_replace(sp, curve=W.Curve("const", 0.0))
+    inp0 = W.make_inputs(sp0)
+    b = D.trajectory(inp0, storage="f64")
+    inp0.mu_cond[:] = -42.0
+    assert np.array_equal(D.trajectory(inp0, storage="f64"), b)
+
+
+def test_per_sample_independence():
+    sp = W.small_spec(n=5, C=2, H=9, W=11, regions=2, inpaint=True, steps=6)
+    inp = W.make_inputs(sp)
+    full = D.trajectory(inp)
+    sub = D.trajectory(inp.subset([1, 3]))
+    assert np.array_equal(sub, full[[1, 3]])
+
+
+def test_bucket_count_invariance():
+    # equal scales in every bucket -> identical trajectories for 1/4/8/16 buckets
+    base = W.small_spec(n=3, C=2, H=6, W=8, steps=16, curve=W.Curve("const", 1.7))
+    outs = [D.trajectory(W.make_inputs(dataclasses_replace(base, num_buckets=nb)))
+            for nb in (1, 4, 8, 16)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# ---------------------------------------------------------------- mode M vs mode D
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype="f32", sampler="euler"),
+    dict(dtype="f32", sampler="heun", regions=3, inpaint=True),
+    dict(dtype="bf16", sampler="heun"),
+    dict(dtype="bf16", sampler="euler", regions=2),
+])
+def test_mirror_per_step_within_tolerance_of_definition(kw):
+    sp = W.small_spec(n=4, C=3, H=12, W=16, steps=7, **kw)
+    inp = W.make_inputs(sp)
+    sig, table, cov = D.run_setup(inp)
+    x = D.init_latent(inp, sig, "f32")
+    for k in range(sp.steps):
+        t = inp.start_step.astype(np.int64) + k
+        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+        for i in range(sp.n):
+            if plan["bucket_id"][i] < 0:
+                continue
+            ti = int(t[i])
+            ref = D.step(x[i], float(sig[ti]), float(sig[ti + 1]), float(plan["scale"][i]),
+                         D.sample_params(inp, i), sp.sampler)
+            got = M.step32(x[i].astype(np.float32), sig[ti], sig[ti + 1], plan["scale"][i],
+                           bool(plan["need_uncond"][i]), M.params32(inp, i), sp.sampler)
+            assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+            x[i] = ref.astype(np.float32)
+
+
+def test_mirror_exact_special_cases():
+    sp = W.small_spec(n=2, C=2, H=6, W=8, steps=4, inpaint=True, mixed_start=False)
+    inp = W.make_inputs(sp)
+    inp.mask[:] = 0.0
+    xf = M.trajectory32(inp)
+    assert np.array_equal(xf, inp.x_orig)
+    prm = M.Params32(np.float32([0.5, -1]), np.float32([2, 3]), 0.25)
+    x = np.random.default_rng(2).standard_normal((2, 3, 3)).astype(np.float32)
+    # scale 1, uncond skipped: uncond means play no part
+    a = M.step32(x, 3.0, 2.0, 1.0, False, prm, "heun")
+    prm2 = M.Params32(np.float32([7, 7]), np.float32([2, 3]), 0.25)
+    assert np.array_equal(a, M.step32(x, 3.0, 2.0, 1.0, False, prm2, "heun"))
+    # scale 0: cond means play no part
+    b = M.step32(x, 3.0, 2.0, 0.0, True, prm, "euler")
+    prm3 = M.Params32(np.float32([0.5, -1]), np.float32([-9, 9]), 0.25)
+    assert np.array_equal(b, M.step32(x, 3.0, 2.0, 0.0, True, prm3, "euler"))
+
+
+def test_norm_stats_special_cases():
+    prm, rng = _tiny_prm()
+    x = rng.standard_normal((2, 3, 4))
+    s0 = D.norm_stats(x, 1.3, 0.0, prm, True)
+    s1 = D.norm_stats(x, 1.3, 1.0, prm, False)
+    assert s0[2] == s0[1] and s1[2] == s1[0] and s1[1] == 0.0
+    v = D.denoise(x, 1.3, prm.mu_c, prm.s2)
+    assert abs(s1[0] - np.mean([np.linalg.norm(v[c, h]) for c in range(2) for h in range(3)])) < 1e-12
