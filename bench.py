@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Throughput of the fused guided denoising step on one MI355X.
+
+One bench step = one sampler step of the large bf16 workload: 256 samples,
+latent 16x128x128 stored in bf16 (fp32 arithmetic), 2 feathered regional
+conds + uncond per sample, 8 guidance buckets on a linear 2.0 -> 1.2 curve,
+mixed per-sample progress over a 50-step log-linear Euler schedule.  Each
+step builds the bucket plan on the host, uploads it and runs one fused
+guided_step launch over every sample, all inside libbcg's native loop.
+Progress is steady-state continuous batching (sample i at step
+(start_i + k) mod 50), so every launch is full and mixes all 8 buckets.
+With --replicas R > 1, R independent batches are served round-robin, which
+keeps the working set (R x 128 MiB) beyond the 256 MB last-level cache so
+every launch streams from HBM.
+
+Prints one JSON line (metric, value in latent element-steps/s, roofline of
+the guided_step kernel against 8 TB/s HBM, and the CPU oracle's rate).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "latent element-steps/sec on 1 GPU + achieved HBM GB/s as % of peak"
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_api.hip", "bcg_step_bf16.hip",
+                  "bcg_step_f32.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "guided_step_large_bf16_traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bucketed_classifier_free_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_element(spec) -> float:
+    """Algorithmic HBM bytes per latent element-step of guided_step: read x,
+    write x', plus x_orig and a mask shared by the C channels when inpainting."""
+    es = 2 if spec.dtype == "bf16" else 4
+    b = 2 * es
+    if spec.inpaint:
+        b += es + 4.0 / spec.C
+    return b
+
+
+def cpu_baseline(inp, seconds: float):
+    """The float64 oracle's step function on a bounded sample of the workload."""
+    import numpy as np
+    from oracle import definition as D
+    sp = inp.spec
+    sig, table, cov = D.run_setup(inp)
+    x = D.init_latent(inp, sig, sp.dtype)
+    t = inp.start_step.astype(np.int64)
+    plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+    elems = 0
+    done = 0
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        ti = int(t[i])
+        D.step(x[i], float(sig[ti]), float(sig[ti + 1]), float(plan["scale"][i]),
+               D.sample_params(inp, i), sp.sampler)
+        elems += sp.C * sp.H * sp.W
+        done += 1
+        i = (i + 1) % sp.n
+    dt = time.perf_counter() - t0
+    return {"value": elems / dt, "unit": "element-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} sample-steps of {sp.name} (float64 NumPy definition, one thread; "
+                      f"{len(os.sched_getaffinity(0))} cores available), {dt:.1f} s"}
+
+
+def copy_probe(mib: int, iters: int):
+    """Plain device copy of a known size (counter scale reference)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    print(json.dumps({"copy_probe_mib": mib, "ms": ms, "GBps": 2 * mib * (1 << 20) / ms / 1e6}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="large_bf16")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path keeps every sample on one device and its "
+              "multi-GPU form (sample-sharded, no per-step communication) is not built; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from bucketed_classifier_free_amd import GuidedSampler, load
+
+    load()
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 50)
+        return
+    torch.cuda.set_device(0)
+    spec = W.config(args.workload)
+    inp = W.make_inputs(spec)
+    s = GuidedSampler.from_inputs(inp, wrap=True)
+    R = max(1, args.replicas)
+    x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
+    for r in range(R):
+        s.init_state(x[r])
+    loop = s.native_loop(x if R > 1 else x[0])
+    loop.run(0, args.warmup)
+    torch.cuda.synchronize()
+    elems_per_launch = spec.n * spec.C * spec.H * spec.W  # every sample active (steady state)
+    t0 = time.perf_counter()
+    kernel_ms = loop.run(args.warmup, args.steps, timing=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not torch.isfinite(x.float()).all():
+        raise RuntimeError("non-finite state after the timed steps")
+
+    value = elems_per_launch * args.steps / wall
+    launch_ms = kernel_ms / args.steps
+    bpe = bytes_per_element(spec)
+    alg_bytes = bpe * elems_per_launch
+    achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == spec.name:
+            traffic = tr.get("bytes_per_launch")
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "element-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.n, "latent": [spec.C, spec.H, spec.W],
+                   "storage": spec.dtype, "sampler": spec.sampler, "schedule_steps": spec.steps,
+                   "buckets": spec.num_buckets, "regions": spec.regions,
+                   "progress": "mixed, steady state", "replicas": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "kernel": {"name": "guided_step", "avg_launch_us": launch_ms * 1e3,
+                   "algorithmic_bytes_per_launch": alg_bytes, "bytes_per_element_step": bpe,
+                   "element_steps_per_s_kernel_only": elems_per_launch / (launch_ms * 1e-3),
+                   "kernel_hash": kernel_hash()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    loop.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""Thin Python wrappers over libbcg with the C ABI's names.
+
+Argument marshalling only: checks of dtype, device, contiguity and shape
+(raising ValueError before any call), pointer extraction, and the current
+torch stream as the HIP stream.  Every step of the path runs inside libbcg.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.BCG_F32, torch.bfloat16: L.BCG_BF16}
+_SAMPLER = {"euler": L.BCG_EULER, "heun": L.BCG_HEUN}
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _np(a, dtype, shape=None, name="array"):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=dtype)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"{name}: shape {a.shape}, expected {tuple(shape)}")
+    return a
+
+
+def _dev(t, name, dtype=None, shape=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ---------------------------------------------------------------- host calls
+
+def sigma_schedule(sigma_max: float, sigma_min: float, steps: int, denoise: float = 1.0,
+                   kind: int = L.BCG_SCHED_LOGLINEAR):
+    """float32[steps+1] descending sigmas and the base schedule length."""
+    out = np.empty(steps + 1 if steps >= 1 else 1, np.float32)
+    nb = ct.c_int(0)
+    L.check(L.lib().sigma_schedule(kind, sigma_max, sigma_min, steps, denoise, _np_ptr(out),
+                                   ct.byref(nb)))
+    return out, nb.value
+
+
+def bucket_table(curve: str, p0: float, p1: float = 0.0, p2: float = 0.0, num_buckets: int = 1):
+    if curve not in L.BCG_CURVE:
+        raise ValueError(f"unknown curve {curve!r}")
+    out = np.empty(max(num_buckets, 1), np.float32)
+    L.check(L.lib().bucket_table(L.BCG_CURVE[curve], p0, p1, p2, num_buckets, _np_ptr(out)))
+    return out
+
+
+@dataclass
+class Plan:
+    bucket_id: np.ndarray
+    scale: np.ndarray
+    uncond_row: np.ndarray
+    cond_row: np.ndarray
+    order: np.ndarray
+    bucket_count: np.ndarray
+    bucket_offset: np.ndarray
+    uncond_offset: np.ndarray
+    region_box: np.ndarray | None
+    region_off: np.ndarray | None
+    n_active: int
+    n_uncond: int
+
+
+def plan_out_arrays(n, nb, R, bucket_id=None, scale=None, uncond_row=None, order=None):
+    """Output arrays of bcg_plan_build (optionally writing into given views)."""
+    z = lambda a, k, dt: a if a is not None else np.empty(k, dt)
+    return dict(bucket_id=z(bucket_id, n, np.int32), scale=z(scale, n, np.float32),
+                uncond_row=z(uncond_row, n, np.int32), cond_row=np.empty(n, np.int32),
+                order=z(order, n, np.int32), bucket_count=np.empty(nb, np.int32),
+                bucket_offset=np.empty(nb + 1, np.int32), uncond_offset=np.empty(nb + 1, np.int32),
+                region_box=np.empty((n, R, 4), np.int32) if R > 0 else None,
+                region_off=np.empty(n * R + 1, np.int64) if R > 0 else None)
+
+
+def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, W: int = 1,
+                   cfg_override=None, region_count=None, region_frac=None,
+                   region_strength=None, max_regions: int = 0, out=None) -> Plan:
+    """Bucket plan of one step (host arrays in, host arrays out)."""
+    step_idx = _np(step_idx, np.int32, name="step_idx")
+    n = step_idx.size
+    cfg = _np(bucket_cfg, np.float32, name="bucket_cfg")
+    nb = cfg.size
+    R = int(max_regions)
+    ov = _np(cfg_override, np.float32, (n,), "cfg_override")
+    rc = _np(region_count, np.int32, (n,), "region_count") if R > 0 and region_count is not None else None
+    rf = _np(region_frac, np.float64, (n, R, 4), "region_frac") if rc is not None else None
+    rs = _np(region_strength, np.float32, (n, R), "region_strength") if rc is not None else None
+    o = out if out is not None else plan_out_arrays(n, nb, R)
+    pin = L.PlanIn(n, steps, nb, C, H, W, R, _np_ptr(cfg), _np_ptr(step_idx), _np_ptr(ov),
+                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs))
+    pout = L.PlanOut(*(_np_ptr(o[k]) for k in ("bucket_id", "scale", "uncond_row", "cond_row",
+                                               "order", "bucket_count", "bucket_offset",
+                                               "uncond_offset", "region_box", "region_off")),
+                     0, 0)
+    L.check(L.lib().bcg_plan_build(ct.byref(pin), ct.byref(pout)))
+    return Plan(o["bucket_id"], o["scale"], o["uncond_row"], o["cond_row"], o["order"],
+                o["bucket_count"], o["bucket_offset"], o["uncond_offset"], o["region_box"],
+                o["region_off"], int(pout.n_active), int(pout.n_uncond))
+
+
+# ---------------------------------------------------------------- device calls
+
+def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
+    return int(L.lib().guided_step_workspace_size(n, C, H, W, _DT[dtype]))
+
+
+def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond, mu_cond, *,
+                n_active: int, sampler: str, s2: float, feather: int = 0,
+                region_count=None, region_box=None, region_strength=None, mu_region=None,
+                x_orig=None, mask=None, stats=None, workspace=None, stream=None):
+    """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU."""
+    _dev(x, "x")
+    if x.dim() != 4:
+        raise ValueError("x must be [n, C, H, W]")
+    if x.dtype not in _DT:
+        raise ValueError(f"x: unsupported dtype {x.dtype}")
+    n, Cc, H, W = x.shape
+    _dev(x_out, "x_out", x.dtype, x.shape)
+    _dev(sigmas, "sigmas", torch.float32)
+    if sigmas.dim() != 1:
+        raise ValueError("sigmas must be 1-D")
+    _dev(order, "order", torch.int32)
+    if order.numel() < n_active:
+        raise ValueError("order shorter than n_active")
+    for t, nm, dt in ((step_idx, "step_idx", torch.int32), (scale, "scale", torch.float32),
+                      (uncond_row, "uncond_row", torch.int32)):
+        _dev(t, nm, dt)
+        if t.numel() < n:
+            raise ValueError(f"{nm}: needs {n} entries")
+    _dev(mu_uncond, "mu_uncond", torch.float32, (n, Cc))
+    _dev(mu_cond, "mu_cond", torch.float32, (n, Cc))
+    R = 0
+    if region_count is not None:
+        _dev(region_count, "region_count", torch.int32, (n,))
+        _dev(region_box, "region_box", torch.int32)
+        if region_box.dim() != 3 or region_box.shape[0] != n or region_box.shape[2] != 4:
+            raise ValueError("region_box must be [n, R, 4]")
+        R = region_box.shape[1]
+        _dev(region_strength, "region_strength", torch.float32, (n, R))
+        _dev(mu_region, "mu_region", torch.float32, (n, R, Cc))
+    mps = 0
+    if x_orig is not None or mask is not None:
+        _dev(x_orig, "x_orig", x.dtype, x.shape)
+        _dev(mask, "mask", torch.float32)
+        if tuple(mask.shape) == (n, 1, H, W):
+            mps = 1
+        elif tuple(mask.shape) != (1, 1, H, W):
+            raise ValueError(f"mask: shape {tuple(mask.shape)} is neither [n,1,H,W] nor [1,1,H,W]")
+    wsb = 0
+    if stats is not None:
+        _dev(stats, "stats", torch.float32, (n, 3))
+        _dev(workspace, "workspace")
+        wsb = workspace.numel() * workspace.element_size()
+    if sampler not in _SAMPLER:
+        raise ValueError(f"unknown sampler {sampler!r}")
+    a = L.StepArgs(n, Cc, H, W, _DT[x.dtype], _SAMPLER[sampler], R, int(feather), int(n_active),
+                   sigmas.numel(), mps, float(s2),
+                   _ptr(x), _ptr(x_out), _ptr(sigmas), _ptr(order), _ptr(step_idx), _ptr(scale),
+                   _ptr(uncond_row), _ptr(mu_uncond), _ptr(mu_cond), _ptr(region_count),
+                   _ptr(region_box), _ptr(region_strength), _ptr(mu_region), _ptr(x_orig),
+                   _ptr(mask), _ptr(stats), _ptr(workspace), wsb)
+    L.check(L.lib().guided_step(ct.byref(a), _stream(stream)))
+
+
+def latent_init(noise, sigmas, step_idx, x_out, latent=None, stream=None):
+    """x_out = latent + noise * sigmas[step_idx[i]] per sample (see include/bcg.h)."""
+    _dev(x_out, "x_out")
+    if x_out.dim() != 4 or x_out.dtype not in _DT:
+        raise ValueError("x_out must be a [n,C,H,W] float32/bfloat16 tensor")
+    n, Cc, H, W = x_out.shape
+    _dev(noise, "noise", torch.float32, x_out.shape)
+    _dev(sigmas, "sigmas", torch.float32)
+    _dev(step_idx, "step_idx", torch.int32, (n,))
+    _dev(latent, "latent", x_out.dtype, x_out.shape, allow_none=True)
+    L.check(L.lib().latent_init(n, Cc, H, W, _DT[x_out.dtype], _ptr(noise), _ptr(latent),
+                                _ptr(sigmas), sigmas.numel(), _ptr(step_idx), _ptr(x_out),
+                                _stream(stream)))
+
+
+def area_accumulate(region_pred, region_off, region_count, region_box, region_strength, cond_out,
+                    *, feather: int, fallback=None, wsum_out=None, stream=None):
+    """Regional accumulation of packed crops into the full latent (include/bcg.h)."""
+    _dev(cond_out, "cond_out", torch.float32)
+    if cond_out.dim() != 4:
+        raise ValueError("cond_out must be [n,C,H,W]")
+    n, Cc, H, W = cond_out.shape
+    _dev(region_pred, "region_pred", torch.float32)
+    _dev(region_count, "region_count", torch.int32, (n,))
+    _dev(region_box, "region_box", torch.int32)
+    if region_box.dim() != 3 or region_box.shape[0] != n or region_box.shape[2] != 4:
+        raise ValueError("region_box must be [n, R, 4]")
+    R = region_box.shape[1]
+    _dev(region_off, "region_off", torch.int64, (n * R + 1,))
+    _dev(region_strength, "region_strength", torch.float32, (n, R))
+    _dev(fallback, "fallback", torch.float32, cond_out.shape, allow_none=True)
+    _dev(wsum_out, "wsum_out", torch.float32, (n, H, W), allow_none=True)
+    L.check(L.lib().area_accumulate(n, Cc, H, W, int(feather), R, _ptr(region_pred),
+                                    region_pred.numel(), _ptr(region_off), _ptr(region_count),
+                                    _ptr(region_box), _ptr(region_strength), _ptr(fallback),
+                                    _ptr(cond_out), _ptr(wsum_out), _stream(stream)))
+
+
+def mask_blend(a, b, mask, out, stream=None):
+    """out = mask*a + (1-mask)*b, mask broadcast over channels (include/bcg.h)."""
+    _dev(a, "a")
+    if a.dim() != 4 or a.dtype not in _DT:
+        raise ValueError("a must be a [n,C,H,W] float32/bfloat16 tensor")
+    n, Cc, H, W = a.shape
+    _dev(b, "b", a.dtype, a.shape)
+    _dev(out, "out", a.dtype, a.shape)
+    _dev(mask, "mask", torch.float32)
+    if tuple(mask.shape) == (n, 1, H, W):
+        mps = 1
+    elif tuple(mask.shape) == (1, 1, H, W):
+        mps = 0
+    else:
+        raise ValueError(f"mask: shape {tuple(mask.shape)} is neither [n,1,H,W] nor [1,1,H,W]")
+    L.check(L.lib().mask_blend(n, Cc, H, W, _DT[a.dtype], _ptr(a), _ptr(b), _ptr(mask), mps,
+                               _ptr(out), _stream(stream)))

@@ -1,0 +1,456 @@
+// Device half of libbcg's C ABI: argument checks and launches of the fused
+// guided step, its optional norm statistics, the latent initialiser and the
+// standalone regional accumulation and mask blend kernels.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "bcg_common.h"
+#include "bcg_device.h"
+
+using bcg::fail;
+
+namespace bcg {
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(int dtype) { return dtype == BCG_BF16 ? 2 : 4; }
+
+// Two byte ranges overlap without being the same range.
+bool partial_overlap(const void* a, const void* b, size_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    if (x == y) return false;
+    return x < y + bytes && y < x + bytes;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(BCG_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return BCG_OK;
+}
+
+// Workgroup size: 256 lanes unless the grid would leave the 256 CUs thin.
+int pick_block(int64_t samples, int64_t nvec) {
+    int bs = 256;
+    while (bs > 64 && samples * ((nvec + bs - 1) / bs) < 2048) bs /= 2;
+    return bs;
+}
+
+// ------------------------------------------------------------ norm stats
+
+// Wave-level reduction over the 64 lanes, fixed butterfly order.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// One wavefront per latent row (sample j, channel c, row y): the L2 norm over
+// W of the cond prediction C, the uncond prediction U and the guided pred at
+// the step's first evaluation point.  Same per-element arithmetic as the step.
+template <typename T>
+__global__ __launch_bounds__(256) void stats_rows_kernel(const StepParams p, float* rows) {
+    const int64_t CH = (int64_t)p.C * p.H;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (g >= (int64_t)p.n_active * CH) return;
+    const int j = (int)(g / CH);
+    const int rem = (int)(g - (int64_t)j * CH);
+    const int c = rem / p.H, y = rem - (rem / p.H) * p.H;
+    float* out = rows + g * 3;
+    const int i = p.order[j];
+    int t = -1;
+    if (i >= 0 && i < p.n) t = p.step_idx[i];
+    if (i < 0 || i >= p.n || t < 0 || t + 1 >= p.num_sigmas) {
+        if (lane == 0) { out[0] = 0.f; out[1] = 0.f; out[2] = 0.f; }
+        return;
+    }
+    const float sig = p.sigmas[t];
+    const float w = p.scale[i];
+    const bool keep_u = p.uncond_row[i] >= 0;
+    int cnt = p.R > 0 ? p.region_count[i] : 0;
+    cnt = std::max(0, std::min(cnt, std::min(p.R, BCG_MAX_REGIONS)));
+    const float s2 = p.s2;
+    const float v = sig * sig;
+    const float den = s2 + v;
+    const float a = s2 / den;
+    const float bu = (v * p.mu_uncond[(int64_t)i * p.C + c]) / den;
+    const float bc = (v * p.mu_cond[(int64_t)i * p.C + c]) / den;
+    float br[BCG_MAX_REGIONS];
+    RegionDesc rd[BCG_MAX_REGIONS];
+    for (int r = 0; r < BCG_MAX_REGIONS; ++r) {
+        br[r] = 0.f;
+        rd[r] = RegionDesc{0, 0, 0, 0, 0.f};
+        if (r < cnt) {
+            br[r] = (v * p.mu_region[((int64_t)i * p.R + r) * p.C + c]) / den;
+            const int32_t* b = p.region_box + ((int64_t)i * p.R + r) * 4;
+            rd[r] = RegionDesc{b[0], b[1] - b[0], b[2], b[3] - b[2],
+                               p.region_strength[(int64_t)i * p.R + r]};
+        }
+    }
+    const T* xs = static_cast<const T*>(p.x) + ((int64_t)i * p.C + c) * p.HW + (int64_t)y * p.W;
+    float sc = 0.f, su = 0.f, sp = 0.f;
+    for (int x = lane; x < p.W; x += 64) {
+        float xv[1];
+        Io<T, 1>::load(xs + x, xv);
+        const float ax = a * xv[0];
+        const float u = ax + bu;
+        float cc, pred;
+        if (cnt == 0) {
+            cc = ax + bc;
+            pred = (w == 1.0f) ? cc : u + w * (cc - u);
+        } else {
+            float ws[BCG_MAX_REGIONS];
+            float wsum = 0.f;
+            for (int r = 0; r < cnt; ++r) {
+                ws[r] = region_weight(rd[r], y, x, p.feather, p.inv_f4);
+                wsum = r == 0 ? ws[0] : wsum + ws[r];
+            }
+            const bool cv = wsum > 0.0f;
+            const float iw = cv ? 1.0f / wsum : 0.0f;
+            cc = (ws[0] * iw) * (ax + br[0]);
+            for (int r = 1; r < cnt; ++r) cc = cc + (ws[r] * iw) * (ax + br[r]);
+            if (w == 1.0f) pred = (keep_u ? cv : true) ? cc : u;
+            else pred = u + (cv ? w : 0.0f) * (cc - u);
+            if (!cv) cc = u;  // the cond prediction where no region has weight
+        }
+        sc += cc * cc;
+        su += u * u;
+        sp += pred * pred;
+    }
+    sc = wave_sum(sc);
+    su = wave_sum(su);
+    sp = wave_sum(sp);
+    if (lane == 0) {
+        out[0] = sqrtf(sc);
+        out[1] = keep_u ? sqrtf(su) : 0.f;
+        out[2] = sqrtf(sp);
+    }
+}
+
+// Mean of the row norms per sample: one workgroup per active sample, fixed
+// strided partial sums then a fixed-order tree in LDS (deterministic).
+__global__ __launch_bounds__(256) void stats_final_kernel(const StepParams p, const float* rows,
+                                                          float* stats) {
+    __shared__ float part[3][256];
+    const int j = blockIdx.x;
+    const int64_t CH = (int64_t)p.C * p.H;
+    const float* r0 = rows + (int64_t)j * CH * 3;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+    for (int64_t g = threadIdx.x; g < CH; g += 256) {
+        a0 += r0[g * 3 + 0];
+        a1 += r0[g * 3 + 1];
+        a2 += r0[g * 3 + 2];
+    }
+    part[0][threadIdx.x] = a0;
+    part[1][threadIdx.x] = a1;
+    part[2][threadIdx.x] = a2;
+    __syncthreads();
+    for (int s = 128; s >= 1; s >>= 1) {
+        if ((int)threadIdx.x < s) {
+            part[0][threadIdx.x] += part[0][threadIdx.x + s];
+            part[1][threadIdx.x] += part[1][threadIdx.x + s];
+            part[2][threadIdx.x] += part[2][threadIdx.x + s];
+        }
+        __syncthreads();
+    }
+    const int i = p.order[j];
+    if (threadIdx.x < 3 && i >= 0 && i < p.n) stats[(int64_t)i * 3 + threadIdx.x] = part[threadIdx.x][0] / float(CH);
+}
+
+// ------------------------------------------------------------ latent init
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void latent_init_kernel(int n, int C, int64_t HW, const float* noise,
+                                                          const T* latent, const float* sigmas,
+                                                          int num_sigmas, const int32_t* step_idx,
+                                                          T* out) {
+    const int64_t nv = HW / V;
+    const int64_t per = (int64_t)C * nv;
+    const int64_t total = (int64_t)n * per;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int i = (int)(k / per);
+        const int t = step_idx[i];
+        if (t < 0 || t >= num_sigmas) continue;
+        const float sg = sigmas[t];
+        const int64_t e0 = k * V;
+        float nz[V], lt[V], o[V];
+        Io<float, V>::load(noise + e0, nz);
+        if (latent) Io<T, V>::load(latent + e0, lt);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float z = nz[e] * sg;
+            o[e] = latent ? lt[e] + z : z;
+        }
+        Io<T, V>::store(out + e0, o);
+    }
+}
+
+// ------------------------------------------------------------ mask blend
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void mask_blend_kernel(int n, int C, int64_t HW, const T* a,
+                                                         const T* b, const float* mask,
+                                                         int64_t mask_stride, T* out) {
+    const int64_t nv = HW / V;
+    const int64_t total = (int64_t)n * C * nv;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < total;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t ic = k / nv;
+        const int64_t pv = k - ic * nv;
+        const int64_t i = ic / C;
+        const int64_t e0 = k * V;
+        float av[V], bv[V], m[V], o[V];
+        Io<T, V>::load(a + e0, av);
+        Io<T, V>::load(b + e0, bv);
+        Io<float, V>::load(mask + i * mask_stride + pv * V, m);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float om = 1.0f - m[e];
+            o[e] = m[e] * av[e] + om * bv[e];
+        }
+        Io<T, V>::store(out + e0, o);
+    }
+}
+
+// ------------------------------------------------------------ area accumulate
+
+// Gather form: one lane per output pixel walks the regions that contain it.
+__global__ __launch_bounds__(256) void area_accumulate_kernel(
+    int n, int C, int H, int W, int F, float inv_f4, int R, const float* pred, int64_t pred_elems,
+    const int64_t* region_off, const int32_t* region_count, const int32_t* region_box,
+    const float* region_strength, const float* fallback, float* cond_out, float* wsum_out,
+    int tiles) {
+    const int i = blockIdx.x / tiles;
+    const int tile = blockIdx.x - i * tiles;
+    if (i >= n) return;
+    const int64_t HW = (int64_t)H * W;
+    const int64_t p = (int64_t)tile * blockDim.x + threadIdx.x;
+    if (p >= HW) return;
+    const int y = (int)(p / W), x = (int)(p - (int64_t)(p / W) * W);
+    int cnt = region_count[i];
+    cnt = std::max(0, std::min(cnt, std::min(R, BCG_MAX_REGIONS)));
+    RegionDesc rd[BCG_MAX_REGIONS];
+    int64_t off[BCG_MAX_REGIONS];
+    bool ok[BCG_MAX_REGIONS];
+    float ws[BCG_MAX_REGIONS];
+    float wsum = 0.f;
+    for (int r = 0; r < BCG_MAX_REGIONS; ++r) {
+        ok[r] = false;
+        ws[r] = 0.f;
+        if (r >= cnt) continue;
+        const int32_t* b = region_box + ((int64_t)i * R + r) * 4;
+        const int y0 = b[0], y1 = b[1], x0 = b[2], x1 = b[3];
+        const int64_t o = region_off[(int64_t)i * R + r];
+        const int64_t o_next = region_off[(int64_t)i * R + r + 1];
+        const int64_t sz = (int64_t)C * (y1 - y0) * (x1 - x0);
+        ok[r] = 0 <= y0 && y0 < y1 && y1 <= H && 0 <= x0 && x0 < x1 && x1 <= W && o >= 0 &&
+                o + sz <= pred_elems && o + sz <= o_next;
+        if (!ok[r]) continue;
+        rd[r] = RegionDesc{y0, y1 - y0, x0, x1 - x0, region_strength[(int64_t)i * R + r]};
+        off[r] = o;
+        ws[r] = region_weight(rd[r], y, x, F, inv_f4);
+        wsum = r == 0 ? ws[0] : wsum + ws[r];
+    }
+    const bool cv = wsum > 0.0f;
+    const float iw = cv ? 1.0f / wsum : 0.0f;
+    float wh[BCG_MAX_REGIONS];
+    bool in[BCG_MAX_REGIONS];
+    for (int r = 0; r < BCG_MAX_REGIONS; ++r) {
+        wh[r] = ws[r] * iw;
+        in[r] = ok[r] && y >= rd[r].y0 && y < rd[r].y0 + rd[r].h && x >= rd[r].x0 &&
+                x < rd[r].x0 + rd[r].w;
+    }
+    for (int c = 0; c < C; ++c) {
+        float acc = 0.f;
+        bool started = false;
+        for (int r = 0; r < cnt; ++r) {
+            if (!in[r]) continue;
+            const float v = pred[off[r] + ((int64_t)c * rd[r].h + (y - rd[r].y0)) * rd[r].w + (x - rd[r].x0)];
+            const float term = wh[r] * v;
+            acc = started ? acc + term : term;
+            started = true;
+        }
+        const int64_t q = ((int64_t)i * C + c) * HW + p;
+        cond_out[q] = cv ? acc : (fallback ? fallback[q] : 0.0f);
+    }
+    if (wsum_out) wsum_out[(int64_t)i * HW + p] = wsum;
+}
+
+int grid_for(int64_t work, int block) {
+    const int64_t g = (work + block - 1) / block;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20));
+}
+
+}  // namespace
+}  // namespace bcg
+
+using namespace bcg;
+
+extern "C" size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype) {
+    (void)W;
+    (void)dtype;
+    if (n <= 0 || C <= 0 || H <= 0) return 0;
+    return (size_t)n * C * H * 3 * sizeof(float);
+}
+
+extern "C" int guided_step(const bcg_step_args* a, void* stream) {
+    bcg::clear_error();
+    if (!a) return fail(BCG_EINVAL, "guided_step: args is NULL");
+    if (a->n < 0 || a->C < 1 || a->C > BCG_MAX_CHANNELS || a->H < 1 || a->W < 1)
+        return fail(BCG_ESHAPE, "guided_step: bad shape n=%d C=%d H=%d W=%d (C must be in [1, %d])",
+                    a->n, a->C, a->H, a->W, BCG_MAX_CHANNELS);
+    const int64_t HW = (int64_t)a->H * a->W;
+    if (HW > (int64_t(1) << 30)) return fail(BCG_ESHAPE, "guided_step: H*W too large");
+    if (a->dtype != BCG_F32 && a->dtype != BCG_BF16) return fail(BCG_EDTYPE, "guided_step: unknown dtype %d", a->dtype);
+    if (a->sampler != BCG_EULER && a->sampler != BCG_HEUN) return fail(BCG_EINVAL, "guided_step: unknown sampler %d", a->sampler);
+    if (a->max_regions < 0 || a->max_regions > BCG_MAX_REGIONS)
+        return fail(BCG_EINVAL, "guided_step: max_regions %d not in [0, %d]", a->max_regions, BCG_MAX_REGIONS);
+    if (a->feather < 0 || a->feather > BCG_MAX_FEATHER) return fail(BCG_EINVAL, "guided_step: feather %d out of range", a->feather);
+    if (a->n_active < 0 || a->n_active > a->n) return fail(BCG_EINVAL, "guided_step: n_active %d not in [0, n]", a->n_active);
+    if (a->num_sigmas < 2) return fail(BCG_EINVAL, "guided_step: num_sigmas %d < 2", a->num_sigmas);
+    if (!(a->s2 > 0.0f) || !std::isfinite(a->s2)) return fail(BCG_EINVAL, "guided_step: s2 must be finite and > 0");
+    if (a->mask_per_sample != 0 && a->mask_per_sample != 1) return fail(BCG_EINVAL, "guided_step: mask_per_sample must be 0 or 1");
+    if (a->n_active == 0) return BCG_OK;
+    if (!a->x || !a->x_out || !a->sigmas || !a->order || !a->step_idx || !a->scale || !a->uncond_row ||
+        !a->mu_uncond || !a->mu_cond)
+        return fail(BCG_EINVAL, "guided_step: NULL device pointer");
+    if (a->max_regions > 0 && (!a->region_count || !a->region_box || !a->region_strength || !a->mu_region))
+        return fail(BCG_EINVAL, "guided_step: max_regions > 0 needs region_count/box/strength/mu_region");
+    if ((a->x_orig == nullptr) != (a->mask == nullptr))
+        return fail(BCG_EINVAL, "guided_step: x_orig and mask must be given together");
+    const size_t bytes = (size_t)a->n * a->C * HW * elem_size(a->dtype);
+    if (partial_overlap(a->x, a->x_out, bytes)) return fail(BCG_EINVAL, "guided_step: x and x_out partially overlap");
+    if (a->stats) {
+        const size_t need = guided_step_workspace_size(a->n_active, a->C, a->H, a->W, a->dtype);
+        if (!a->workspace || a->workspace_bytes < need)
+            return fail(BCG_EINVAL, "guided_step: stats need a workspace of %zu bytes", need);
+    }
+    const bool inpaint = a->x_orig != nullptr;
+    const int VV = a->dtype == BCG_BF16 ? 8 : 4;
+    const bool vec = HW % VV == 0 && aligned16(a->x) && aligned16(a->x_out) &&
+                     (!inpaint || (aligned16(a->x_orig) && aligned16(a->mask)));
+
+    StepParams p{};
+    p.n = a->n; p.C = a->C; p.H = a->H; p.W = a->W; p.R = a->max_regions;
+    p.feather = std::max(a->feather, 1);
+    p.inv_f4 = 1.0f / float(p.feather * p.feather * p.feather * p.feather);
+    p.n_active = a->n_active;
+    p.num_sigmas = a->num_sigmas;
+    p.HW = HW;
+    p.nvec = (int)(vec ? HW / VV : HW);
+    p.mask_stride = a->mask_per_sample ? (int)HW : 0;
+    p.s2 = a->s2;
+    p.x = a->x; p.x_out = a->x_out; p.sigmas = a->sigmas; p.order = a->order;
+    p.step_idx = a->step_idx; p.scale = a->scale; p.uncond_row = a->uncond_row;
+    p.mu_uncond = a->mu_uncond; p.mu_cond = a->mu_cond; p.region_count = a->region_count;
+    p.region_box = a->region_box; p.region_strength = a->region_strength; p.mu_region = a->mu_region;
+    p.x_orig = a->x_orig; p.mask = a->mask;
+    const int block = pick_block(p.n_active, p.nvec);
+    p.tiles = (p.nvec + block - 1) / block;
+    if ((int64_t)p.n_active * p.tiles > INT32_MAX) return fail(BCG_ESHAPE, "guided_step: grid too large");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    if (a->stats) {
+        float* rows = static_cast<float*>(a->workspace);
+        const int64_t nrows = (int64_t)p.n_active * p.C * p.H;
+        const int g = (int)((nrows + 3) / 4);
+        if (a->dtype == BCG_BF16) hipLaunchKernelGGL(stats_rows_kernel<bf16_t>, dim3(g), dim3(256), 0, st, p, rows);
+        else hipLaunchKernelGGL(stats_rows_kernel<float>, dim3(g), dim3(256), 0, st, p, rows);
+        int rc = hip_status(hipGetLastError(), "guided_step: stats launch");
+        if (rc) return rc;
+        hipLaunchKernelGGL(stats_final_kernel, dim3(p.n_active), dim3(256), 0, st, p, rows, a->stats);
+        rc = hip_status(hipGetLastError(), "guided_step: stats launch");
+        if (rc) return rc;
+    }
+    const bool heun = a->sampler == BCG_HEUN;
+    const hipError_t e = a->dtype == BCG_BF16 ? launch_step_bf16(p, vec, heun, inpaint, block, st)
+                                              : launch_step_f32(p, vec, heun, inpaint, block, st);
+    return hip_status(e, "guided_step: launch");
+}
+
+extern "C" int latent_init(int n, int C, int H, int W, int dtype, const float* noise, const void* latent,
+                           const float* sigmas, int num_sigmas, const int32_t* step_idx, void* x_out,
+                           void* stream) {
+    bcg::clear_error();
+    if (n < 0 || C < 1 || H < 1 || W < 1) return fail(BCG_ESHAPE, "latent_init: bad shape");
+    if (dtype != BCG_F32 && dtype != BCG_BF16) return fail(BCG_EDTYPE, "latent_init: unknown dtype %d", dtype);
+    if (num_sigmas < 1) return fail(BCG_EINVAL, "latent_init: num_sigmas < 1");
+    if (n == 0) return BCG_OK;
+    if (!noise || !sigmas || !step_idx || !x_out) return fail(BCG_EINVAL, "latent_init: NULL device pointer");
+    const int64_t HW = (int64_t)H * W;
+    const int64_t total = (int64_t)n * C * HW;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool vec = HW % 8 == 0 && aligned16(noise) && aligned16(x_out) && (!latent || aligned16(latent));
+    const int block = 256;
+    if (dtype == BCG_BF16) {
+        const bf16_t* lt = static_cast<const bf16_t*>(latent);
+        bf16_t* o = static_cast<bf16_t*>(x_out);
+        if (vec) hipLaunchKernelGGL((latent_init_kernel<bf16_t, 8>), dim3(grid_for(total / 8, block)), dim3(block), 0, st, n, C, HW, noise, lt, sigmas, num_sigmas, step_idx, o);
+        else hipLaunchKernelGGL((latent_init_kernel<bf16_t, 1>), dim3(grid_for(total, block)), dim3(block), 0, st, n, C, HW, noise, lt, sigmas, num_sigmas, step_idx, o);
+    } else {
+        const float* lt = static_cast<const float*>(latent);
+        float* o = static_cast<float*>(x_out);
+        if (vec) hipLaunchKernelGGL((latent_init_kernel<float, 4>), dim3(grid_for(total / 4, block)), dim3(block), 0, st, n, C, HW, noise, lt, sigmas, num_sigmas, step_idx, o);
+        else hipLaunchKernelGGL((latent_init_kernel<float, 1>), dim3(grid_for(total, block)), dim3(block), 0, st, n, C, HW, noise, lt, sigmas, num_sigmas, step_idx, o);
+    }
+    return hip_status(hipGetLastError(), "latent_init: launch");
+}
+
+extern "C" int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void* b,
+                          const float* mask, int mask_per_sample, void* out, void* stream) {
+    bcg::clear_error();
+    if (n < 0 || C < 1 || H < 1 || W < 1) return fail(BCG_ESHAPE, "mask_blend: bad shape");
+    if (dtype != BCG_F32 && dtype != BCG_BF16) return fail(BCG_EDTYPE, "mask_blend: unknown dtype %d", dtype);
+    if (mask_per_sample != 0 && mask_per_sample != 1) return fail(BCG_EINVAL, "mask_blend: mask_per_sample must be 0 or 1");
+    if (n == 0) return BCG_OK;
+    if (!a || !b || !mask || !out) return fail(BCG_EINVAL, "mask_blend: NULL device pointer");
+    const int64_t HW = (int64_t)H * W;
+    const int64_t total = (int64_t)n * C * HW;
+    const size_t bytes = (size_t)total * elem_size(dtype);
+    if (partial_overlap(a, out, bytes) || partial_overlap(b, out, bytes))
+        return fail(BCG_EINVAL, "mask_blend: out partially overlaps an input");
+    const int64_t ms = mask_per_sample ? HW : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int block = 256;
+    if (dtype == BCG_BF16) {
+        const bool vec = HW % 8 == 0 && aligned16(a) && aligned16(b) && aligned16(mask) && aligned16(out);
+        auto A = static_cast<const bf16_t*>(a); auto B = static_cast<const bf16_t*>(b); auto O = static_cast<bf16_t*>(out);
+        if (vec) hipLaunchKernelGGL((mask_blend_kernel<bf16_t, 8>), dim3(grid_for(total / 8, block)), dim3(block), 0, st, n, C, HW, A, B, mask, ms, O);
+        else hipLaunchKernelGGL((mask_blend_kernel<bf16_t, 1>), dim3(grid_for(total, block)), dim3(block), 0, st, n, C, HW, A, B, mask, ms, O);
+    } else {
+        const bool vec = HW % 4 == 0 && aligned16(a) && aligned16(b) && aligned16(mask) && aligned16(out);
+        auto A = static_cast<const float*>(a); auto B = static_cast<const float*>(b); auto O = static_cast<float*>(out);
+        if (vec) hipLaunchKernelGGL((mask_blend_kernel<float, 4>), dim3(grid_for(total / 4, block)), dim3(block), 0, st, n, C, HW, A, B, mask, ms, O);
+        else hipLaunchKernelGGL((mask_blend_kernel<float, 1>), dim3(grid_for(total, block)), dim3(block), 0, st, n, C, HW, A, B, mask, ms, O);
+    }
+    return hip_status(hipGetLastError(), "mask_blend: launch");
+}
+
+extern "C" int area_accumulate(int n, int C, int H, int W, int feather, int max_regions,
+                               const float* region_pred, int64_t pred_elems, const int64_t* region_off,
+                               const int32_t* region_count, const int32_t* region_box,
+                               const float* region_strength, const float* fallback, float* cond_out,
+                               float* wsum_out, void* stream) {
+    bcg::clear_error();
+    if (n < 0 || C < 1 || H < 1 || W < 1) return fail(BCG_ESHAPE, "area_accumulate: bad shape");
+    if (max_regions < 1 || max_regions > BCG_MAX_REGIONS)
+        return fail(BCG_EINVAL, "area_accumulate: max_regions %d not in [1, %d]", max_regions, BCG_MAX_REGIONS);
+    if (feather < 0 || feather > BCG_MAX_FEATHER) return fail(BCG_EINVAL, "area_accumulate: feather out of range");
+    if (pred_elems < 0) return fail(BCG_EINVAL, "area_accumulate: pred_elems < 0");
+    if (n == 0) return BCG_OK;
+    if (!region_pred || !region_off || !region_count || !region_box || !region_strength || !cond_out)
+        return fail(BCG_EINVAL, "area_accumulate: NULL device pointer");
+    const int64_t HW = (int64_t)H * W;
+    if (HW > (int64_t(1) << 30)) return fail(BCG_ESHAPE, "area_accumulate: H*W too large");
+    const int F = std::max(feather, 1);
+    const float inv_f4 = 1.0f / float(F * F * F * F);
+    const int block = 256;
+    const int tiles = (int)((HW + block - 1) / block);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(area_accumulate_kernel, dim3((unsigned)((int64_t)n * tiles)), dim3(block), 0, st, n, C, H, W,
+                       F, inv_f4, max_regions, region_pred, pred_elems, region_off, region_count, region_box,
+                       region_strength, fallback, cond_out, wsum_out, tiles);
+    return hip_status(hipGetLastError(), "area_accumulate: launch");
+}

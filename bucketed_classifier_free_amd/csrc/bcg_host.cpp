@@ -1,0 +1,240 @@
+// Host half of libbcg: error state, sigma schedule, bucket table and the
+// per-step bucket plan.  Pure C++ (no HIP calls), O(n) per step.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "bcg_common.h"
+
+namespace bcg {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+}  // namespace bcg
+
+using bcg::fail;
+
+extern "C" const char* bcg_last_error(void) { return bcg::g_err; }
+
+extern "C" int bcg_abi_version(void) { return 1; }
+
+// "12 · Samplers, schedulers and CFG", sections "sigma sequence" and
+// "denoise below 1": the schedule runs from high to low noise and ends at 0;
+// for denoise < 1 a longer base schedule is built and its tail kept.  The base
+// length is the smallest N with N*denoise >= steps, computed as ceil(steps /
+// denoise) in double.
+extern "C" int sigma_schedule(int kind, double sigma_max, double sigma_min, int steps,
+                              double denoise, float* sigmas, int* base_steps) {
+    bcg::clear_error();
+    if (kind != BCG_SCHED_LOGLINEAR) return fail(BCG_EINVAL, "sigma_schedule: unknown kind %d", kind);
+    if (!(std::isfinite(sigma_max) && std::isfinite(sigma_min) && sigma_min > 0.0 &&
+          sigma_max > sigma_min))
+        return fail(BCG_EINVAL, "sigma_schedule: need sigma_max > sigma_min > 0 (got %g, %g)",
+                    sigma_max, sigma_min);
+    if (steps < 1 || steps > 100000) return fail(BCG_EINVAL, "sigma_schedule: steps %d out of range", steps);
+    if (!(denoise > 0.0 && denoise <= 1.0))
+        return fail(BCG_EINVAL, "sigma_schedule: denoise %g not in (0, 1]", denoise);
+    if (!sigmas) return fail(BCG_EINVAL, "sigma_schedule: sigmas is NULL");
+    double nb = denoise >= 1.0 ? double(steps) : std::ceil(double(steps) / denoise);
+    if (nb > 1e7) return fail(BCG_EINVAL, "sigma_schedule: base schedule too long (%g)", nb);
+    const int N = int(nb);
+    const double la = std::log(sigma_max), lb = std::log(sigma_min);
+    // Point i of the base schedule (i in [0, N]); index N is the terminal 0.
+    auto point = [&](int i) -> double {
+        if (i == N) return 0.0;
+        if (i == 0) return sigma_max;
+        if (i == N - 1) return sigma_min;
+        return std::exp(la + (lb - la) * (double(i) / double(N - 1)));
+    };
+    for (int k = 0; k <= steps; ++k) sigmas[k] = float(point(N - steps + k));
+    if (base_steps) *base_steps = N;
+    return BCG_OK;
+}
+
+// SGLang BCG write-up, section 2 (a continuous curve cut into buckets,
+// constant per bucket) and section 5 (linear decay and front-high shapes).
+extern "C" int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
+                            float* table) {
+    bcg::clear_error();
+    if (num_buckets < 1 || num_buckets > BCG_MAX_BUCKETS)
+        return fail(BCG_EINVAL, "bucket_table: num_buckets %d out of range", num_buckets);
+    if (!table) return fail(BCG_EINVAL, "bucket_table: table is NULL");
+    if (!(std::isfinite(p0) && std::isfinite(p1) && std::isfinite(p2)))
+        return fail(BCG_EINVAL, "bucket_table: non-finite curve parameter");
+    if (curve < BCG_CURVE_CONST || curve > BCG_CURVE_FRONT_HIGH)
+        return fail(BCG_EINVAL, "bucket_table: unknown curve %d", curve);
+    for (int b = 0; b < num_buckets; ++b) {
+        const double u = num_buckets == 1 ? 0.0 : double(b) / double(num_buckets - 1);
+        double v = p0;
+        if (curve == BCG_CURVE_LINEAR) v = p0 + (p1 - p0) * u;
+        else if (curve == BCG_CURVE_FRONT_HIGH) v = u < p2 ? p0 : p1;
+        table[b] = float(v);
+    }
+    return BCG_OK;
+}
+
+namespace {
+
+// "calc_cond_batch()": area fractions become latent slices.  Round half up,
+// then clamp so the box keeps at least one pixel and stays inside.
+void area_slice(const double* f, int H, int W, int32_t* box) {
+    const double fy = f[0], fx = f[1], fh = f[2], fw = f[3];
+    auto rnd = [](double v) -> long long { return (long long)std::floor(v + 0.5); };
+    long long h = std::min<long long>(std::max<long long>(rnd(fh * H), 1), H);
+    long long w = std::min<long long>(std::max<long long>(rnd(fw * W), 1), W);
+    long long y0 = std::min<long long>(std::max<long long>(rnd(fy * H), 0), H - h);
+    long long x0 = std::min<long long>(std::max<long long>(rnd(fx * W), 0), W - w);
+    box[0] = int32_t(y0);
+    box[1] = int32_t(y0 + h);
+    box[2] = int32_t(x0);
+    box[3] = int32_t(x0 + w);
+}
+
+// True when the union of the boxes covers [0,H) x [0,W).  Coordinate
+// compression over the box edges: every elementary cell is tested.
+bool covers(const int32_t (*boxes)[4], int k, int H, int W) {
+    if (k == 0) return false;
+    std::vector<int> ys{0, H}, xs{0, W};
+    for (int r = 0; r < k; ++r) {
+        ys.push_back(boxes[r][0]); ys.push_back(boxes[r][1]);
+        xs.push_back(boxes[r][2]); xs.push_back(boxes[r][3]);
+    }
+    std::sort(ys.begin(), ys.end()); ys.erase(std::unique(ys.begin(), ys.end()), ys.end());
+    std::sort(xs.begin(), xs.end()); xs.erase(std::unique(xs.begin(), xs.end()), xs.end());
+    for (size_t a = 0; a + 1 < ys.size(); ++a)
+        for (size_t b = 0; b + 1 < xs.size(); ++b) {
+            const int cy = ys[a], cx = xs[b];  // cell [ys[a], ys[a+1]) x [xs[b], xs[b+1])
+            bool hit = false;
+            for (int r = 0; r < k && !hit; ++r)
+                hit = boxes[r][0] <= cy && cy < boxes[r][1] && boxes[r][2] <= cx && cx < boxes[r][3];
+            if (!hit) return false;
+        }
+    return true;
+}
+
+}  // namespace
+
+// SGLang BCG write-up, section 2 (assign_bucket), section 3 (BucketPlan with
+// per-sample (bucket, scale) and per-bucket offsets; the [uncond | cond]
+// layout), section 4 stage 3 (the plan is built in the scheduler, before the
+// launch); "12 · Samplers...", "the cfg = 1 optimisation".
+extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
+    bcg::clear_error();
+    if (!in || !out) return fail(BCG_EINVAL, "bcg_plan_build: NULL argument");
+    const int n = in->n, steps = in->steps, nb = in->num_buckets, R = in->max_regions;
+    if (n < 0 || n > (1 << 24)) return fail(BCG_ESHAPE, "bcg_plan_build: n %d out of range", n);
+    if (steps < 1) return fail(BCG_EINVAL, "bcg_plan_build: steps %d < 1", steps);
+    if (nb < 1 || nb > BCG_MAX_BUCKETS) return fail(BCG_EINVAL, "bcg_plan_build: num_buckets %d out of range", nb);
+    if (R < 0 || R > BCG_MAX_REGIONS) return fail(BCG_EINVAL, "bcg_plan_build: max_regions %d out of range", R);
+    if (in->C < 1 || in->H < 1 || in->W < 1) return fail(BCG_ESHAPE, "bcg_plan_build: bad C/H/W");
+    if (!in->bucket_cfg || (n > 0 && !in->step_idx))
+        return fail(BCG_EINVAL, "bcg_plan_build: bucket_cfg/step_idx is NULL");
+    if (!out->bucket_id || !out->scale || !out->uncond_row || !out->cond_row || !out->order ||
+        !out->bucket_count || !out->bucket_offset || !out->uncond_offset)
+        return fail(BCG_EINVAL, "bcg_plan_build: NULL output array");
+    const bool regions = R > 0 && in->region_count;
+    if (regions && (!in->region_frac || !in->region_strength))
+        return fail(BCG_EINVAL, "bcg_plan_build: region_count given without region_frac/strength");
+    for (int b = 0; b < nb; ++b)
+        if (!std::isfinite(in->bucket_cfg[b])) return fail(BCG_EINVAL, "bcg_plan_build: bucket_cfg[%d] not finite", b);
+    for (int i = 0; i < n; ++i) {
+        if (in->cfg_override) {
+            const float o = in->cfg_override[i];
+            if (std::isinf(o)) return fail(BCG_EINVAL, "bcg_plan_build: cfg_override[%d] infinite", i);
+        }
+        if (regions) {
+            const int k = in->region_count[i];
+            if (k < 0 || k > R) return fail(BCG_EINVAL, "bcg_plan_build: region_count[%d] = %d not in [0, %d]", i, k, R);
+            for (int r = 0; r < k; ++r) {
+                const float s = in->region_strength[i * R + r];
+                if (!(s == 0.0f || (s >= 1e-30f && s <= 1e30f)))
+                    return fail(BCG_EINVAL, "bcg_plan_build: region_strength[%d][%d] = %g not 0 or in [1e-30, 1e30]", i, r, double(s));
+                const double* f = in->region_frac + (size_t(i) * R + r) * 4;
+                for (int q = 0; q < 4; ++q)
+                    if (!std::isfinite(f[q]) || std::fabs(f[q]) > 1e6)
+                        return fail(BCG_EINVAL, "bcg_plan_build: region_frac[%d][%d] not finite", i, r);
+            }
+        }
+    }
+
+    // Region boxes, crop offsets and per-sample coverage.
+    std::vector<char> covered(size_t(n), 1);
+    int64_t off = 0;
+    for (int i = 0; i < n; ++i) {
+        const int k = regions ? in->region_count[i] : 0;
+        int32_t boxes[BCG_MAX_REGIONS][4] = {};
+        int32_t live[BCG_MAX_REGIONS][4] = {};
+        int nlive = 0;
+        for (int r = 0; r < R; ++r) {
+            if (r < k) {
+                area_slice(in->region_frac + (size_t(i) * R + r) * 4, in->H, in->W, boxes[r]);
+                if (in->region_strength[i * R + r] > 0.0f) {
+                    std::memcpy(live[nlive++], boxes[r], sizeof boxes[r]);
+                }
+            }
+            if (out->region_box) std::memcpy(out->region_box + (size_t(i) * R + r) * 4, boxes[r], sizeof boxes[r]);
+            if (out->region_off) out->region_off[size_t(i) * R + r] = off;
+            if (r < k) off += int64_t(in->C) * (boxes[r][1] - boxes[r][0]) * (boxes[r][3] - boxes[r][2]);
+        }
+        if (k > 0) covered[i] = covers(live, nlive, in->H, in->W);
+    }
+    if (out->region_off && R > 0) out->region_off[size_t(n) * R] = off;
+
+    // Buckets, scales and the skip decision.
+    std::vector<char> need_u(size_t(n), 0);
+    int n_act = 0;
+    for (int b = 0; b < nb; ++b) out->bucket_count[b] = 0;
+    for (int i = 0; i < n; ++i) {
+        const long long t = in->step_idx[i];
+        out->uncond_row[i] = -1;
+        out->cond_row[i] = -1;
+        if (t < 0 || t >= steps) {
+            out->bucket_id[i] = -1;
+            out->scale[i] = 0.0f;
+            continue;
+        }
+        const int b = int(std::min<long long>(t * nb / steps, nb - 1));
+        out->bucket_id[i] = b;
+        float w = in->bucket_cfg[b];
+        if (in->cfg_override && !std::isnan(in->cfg_override[i])) w = in->cfg_override[i];
+        out->scale[i] = w;
+        need_u[i] = !(w == 1.0f && covered[i]);
+        out->bucket_count[b] += 1;
+        ++n_act;
+    }
+    // Stable counting sort by bucket: order = active samples by (bucket, i).
+    std::vector<int> ucount(size_t(nb), 0);
+    out->bucket_offset[0] = 0;
+    for (int b = 0; b < nb; ++b) out->bucket_offset[b + 1] = out->bucket_offset[b] + out->bucket_count[b];
+    for (int i = 0; i < n; ++i)
+        if (out->bucket_id[i] >= 0 && need_u[i]) ucount[out->bucket_id[i]] += 1;
+    out->uncond_offset[0] = 0;
+    for (int b = 0; b < nb; ++b) out->uncond_offset[b + 1] = out->uncond_offset[b] + ucount[b];
+    const int m = out->uncond_offset[nb];
+    std::vector<int> cpos(out->bucket_offset, out->bucket_offset + nb);
+    std::vector<int> upos(out->uncond_offset, out->uncond_offset + nb);
+    for (int i = 0; i < n; ++i) {
+        const int b = out->bucket_id[i];
+        if (b < 0) continue;
+        const int p = cpos[b]++;
+        out->order[p] = i;
+        out->cond_row[i] = m + p;
+        if (need_u[i]) out->uncond_row[i] = upos[b]++;
+    }
+    for (int j = n_act; j < n; ++j) out->order[j] = -1;
+    out->n_active = n_act;
+    out->n_uncond = m;
+    return BCG_OK;
+}

@@ -1,0 +1,295 @@
+/*
+ * bcg.h -- C ABI of libbcg: the per-step guided denoising update of a
+ * diffusion sampler with bucketed classifier-free guidance (BCG), for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (page title and section):
+ *   [S] "12 · Samplers, schedulers and CFG" (ComfyUI guide, sampling chapter):
+ *       "sigma sequence", "denoise below 1", "core of CFG", "the cfg = 1
+ *       optimisation", "calc_cond_batch()", "inpaint and mask",
+ *       "data shapes of one sampling step".
+ *   [B] SGLang diffusion BCG write-up (zwxr.cn news 258547): section 2 "BCG
+ *       core mechanism" (bucket assignment), section 3 "bucket construction
+ *       under tensor parallelism" (BucketPlan, per-bucket offsets, split and
+ *       combine, the [uncond_0..uncond_n | cond_0..cond_n] layout), section 4
+ *       "debug chain" (plan built in the scheduler before launch, guidance in
+ *       fp32 for half-precision storage, norm logging), section 5 (guidance
+ *       curve shapes).
+ *
+ * Conventions (all entry points):
+ *   - Every function returns an int status: BCG_OK (0) or a negative code.
+ *     bcg_last_error() returns a thread-local message for the last failure.
+ *   - Arguments are validated before anything is launched; a failed call has
+ *     no side effects.  A HIP launch failure is reported as BCG_EHIP.
+ *   - The library never allocates, frees, moves or casts caller memory.
+ *     "host" arrays are ordinary CPU memory; "device" arrays are GPU memory
+ *     (e.g. torch tensor storage), contiguous, row-major as stated.
+ *   - Device work is asynchronous on the caller's stream (a hipStream_t,
+ *     passed as void*; NULL is the null stream).  Nothing synchronises.
+ *   - Latents are [n, C, H, W] contiguous in the storage dtype (BCG_F32 or
+ *     BCG_BF16); all arithmetic is fp32, stores round to nearest even.
+ */
+#ifndef BCG_H
+#define BCG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { BCG_OK = 0, BCG_EINVAL = -1, BCG_ESHAPE = -2, BCG_EDTYPE = -3, BCG_EHIP = -4 };
+enum { BCG_F32 = 0, BCG_BF16 = 1 };
+enum { BCG_EULER = 0, BCG_HEUN = 1 };
+enum { BCG_SCHED_LOGLINEAR = 0 };
+enum { BCG_CURVE_CONST = 0, BCG_CURVE_LINEAR = 1, BCG_CURVE_FRONT_HIGH = 2 };
+
+#define BCG_MAX_REGIONS 4    /* regional conds per sample */
+#define BCG_MAX_CHANNELS 64  /* latent channels */
+#define BCG_MAX_FEATHER 64   /* feather width in latent pixels */
+#define BCG_MAX_BUCKETS 4096
+
+/* Thread-local message describing the last failed call ("" if none). */
+const char* bcg_last_error(void);
+
+/* ABI version of this header (incremented on any layout change). */
+int bcg_abi_version(void);
+
+/*
+ * sigma_schedule -- [S] "sigma sequence", "denoise below 1".
+ * Descending noise levels for `steps` sampler steps.  A base schedule of
+ * N = ceil(steps/denoise) points (N = steps when denoise >= 1) evenly spaced
+ * in log(sigma) from sigma_max down to sigma_min (endpoints exact), then a
+ * terminal 0; the last steps+1 values are written.
+ *   kind        BCG_SCHED_LOGLINEAR
+ *   sigma_max > sigma_min > 0, steps in [1, 100000], denoise in (0, 1]
+ *   sigmas      host float[steps+1], out
+ *   base_steps  host int*, out (N), may be NULL
+ * Errors: BCG_EINVAL for any argument out of range.
+ */
+int sigma_schedule(int kind, double sigma_max, double sigma_min, int steps,
+                   double denoise, float* sigmas, int* base_steps);
+
+/*
+ * bucket_table -- [B] sections 2 and 5.  Guidance scale per bucket from a
+ * continuous curve sampled at u = b/(num_buckets-1) (u = 0 for one bucket):
+ *   BCG_CURVE_CONST       p0
+ *   BCG_CURVE_LINEAR      p0 + (p1 - p0) u
+ *   BCG_CURVE_FRONT_HIGH  p0 if u < p2 else p1
+ * Evaluated in double, stored as float.  table: host float[num_buckets], out.
+ * Errors: BCG_EINVAL (unknown curve, num_buckets out of [1, BCG_MAX_BUCKETS],
+ * non-finite value).
+ */
+int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
+                 float* table);
+
+/*
+ * bcg_plan_build -- [B] section 2 (assign_bucket), section 3 (BucketPlan:
+ * per-sample bucket and scale, per-bucket offsets; the [uncond | cond]
+ * layout), section 4 stage 3 (the plan is built before launch and is
+ * immutable during the step); [S] "the cfg = 1 optimisation", and
+ * "calc_cond_batch()" (area fractions -> latent slices).
+ *
+ * All arrays are host memory.  For every sample i with 0 <= step_idx[i] < steps
+ * (active):
+ *   bucket_id[i] = min(floor(step_idx[i]*num_buckets/steps), num_buckets-1)
+ *                  (exact integer arithmetic)
+ *   scale[i]     = cfg_override[i] if given and not NaN, else bucket_cfg[bucket]
+ *   the uncond branch is skipped iff scale[i] == 1.0f and the sample's conds
+ *   cover every latent pixel (no regions, or the boxes with strength > 0
+ *   cover the frame); otherwise it is kept (uncovered pixels use it).
+ * Layout: cond rows are the active samples stably ordered by (bucket, i) and
+ * follow the uncond half; the uncond half is the same order without skipped
+ * samples.  order[0..n_active) lists the active samples in that order.
+ * Inactive samples: bucket_id = -1, scale = 0, rows = -1.
+ * Region boxes (half-open y0,y1,x0,x1) from fractions (fy,fx,fh,fw):
+ *   h = clamp(floor(fh*H + 0.5), 1, H); y0 = clamp(floor(fy*H + 0.5), 0, H-h);
+ *   same for x.  region_off[i*R + r] is the element offset of region r's
+ *   packed [C,h,w] crop (size 0 for r >= region_count[i]); region_off[n*R] is
+ *   the total.
+ */
+typedef struct {
+    int32_t n;                       /* samples, >= 0 */
+    int32_t steps;                   /* trajectory length, >= 1 */
+    int32_t num_buckets;             /* [1, BCG_MAX_BUCKETS] */
+    int32_t C, H, W;                 /* latent shape (for region slices) */
+    int32_t max_regions;             /* R in [0, BCG_MAX_REGIONS], array stride */
+    const float* bucket_cfg;         /* [num_buckets] */
+    const int32_t* step_idx;         /* [n] t_i; outside [0, steps) = inactive */
+    const float* cfg_override;       /* [n] or NULL; NaN = none; else finite */
+    const int32_t* region_count;     /* [n] in [0, R], or NULL (all 0) */
+    const double* region_frac;       /* [n][R][4] (fy,fx,fh,fw), or NULL if R == 0 */
+    const float* region_strength;    /* [n][R]: 0 or in [1e-30, 1e30], or NULL if R == 0 */
+} bcg_plan_in;
+
+typedef struct {
+    int32_t* bucket_id;              /* [n] */
+    float* scale;                    /* [n] */
+    int32_t* uncond_row;             /* [n] row in the uncond half, -1 = skipped/inactive */
+    int32_t* cond_row;               /* [n] row of the full batch (n_uncond + pos), -1 = inactive */
+    int32_t* order;                  /* [n] first n_active entries valid */
+    int32_t* bucket_count;           /* [num_buckets] active samples per bucket */
+    int32_t* bucket_offset;          /* [num_buckets+1] exclusive prefix, cond half */
+    int32_t* uncond_offset;          /* [num_buckets+1] exclusive prefix, uncond half */
+    int32_t* region_box;             /* [n][R][4] or NULL */
+    int64_t* region_off;             /* [n*R+1] or NULL */
+    int32_t n_active;                /* out */
+    int32_t n_uncond;                /* out */
+} bcg_plan_out;
+
+int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out);
+
+/*
+ * guided_step -- one sampler step of the guided update, fused in one pass
+ * over the latent.  [S] "core of CFG", "the cfg = 1 optimisation",
+ * "calc_cond_batch()", "inpaint and mask"; [B] section 3 (per-sample scales
+ * over a mixed-bucket batch), section 4 (fp32 guidance for bf16 storage).
+ *
+ * For each sample i = order[j], j < n_active, with t = step_idx[i],
+ * sigma = sigmas[t], sigma' = sigmas[t+1], w = scale[i]:
+ *   branch predictions (closed-form stand-in denoiser, Gaussian data
+ *     N(mu_k, s2)):  D_k(x) = (s2*x + sigma^2*mu_k[c]) / (s2 + sigma^2)
+ *   U = D_uncond; C = D_cond, or with regions
+ *     C = sum_r w_r(p) D_r / sum_r w_r(p), w_r = strength_r * feather_r(p),
+ *     and C = U where no region has weight
+ *   pred = C if w == 1, else U + w (C - U)   (U not evaluated if uncond_row[i] < 0)
+ *   inpaint: pred = m pred + (1 - m) x_orig
+ *   Euler: x' = x + (sigma' - sigma)(x - pred)/sigma;  Heun adds a second
+ *   evaluation at the Euler point and averages the slopes; x' = pred when
+ *   sigma' = 0.
+ * The evaluation order is a fixed sequence of fp32 operations (no fused
+ * multiply-add); stores round to the storage dtype.
+ *
+ * x_out may equal x (in place); otherwise the two must not overlap.  Samples
+ * not in order[0..n_active) are neither read nor written.  Entries of order
+ * outside [0, n), and samples whose t or t+1 falls outside [0, num_sigmas),
+ * are skipped on the device.  Feather: linear ramp of `feather` pixels on
+ * each box edge (weight (d+1)/F ... 1), separable in y and x.
+ * Stats (optional): stats[i][0..2] = mean over (c, row) of the L2 norm over W
+ * of C, U (0 if skipped) and pred (before the inpaint blend), from the first
+ * evaluation; needs a device workspace of guided_step_workspace_size() bytes.
+ * Errors: BCG_ESHAPE (sizes), BCG_EDTYPE (dtype), BCG_EINVAL (NULL pointer,
+ * sampler, R > 0 without region arrays, inpaint arrays half given, stats
+ * without workspace or with too small a workspace), BCG_EHIP.
+ */
+typedef struct {
+    int32_t n, C, H, W;              /* n >= 0, C in [1, 64], H, W >= 1 */
+    int32_t dtype;                   /* BCG_F32 | BCG_BF16: x, x_out, x_orig */
+    int32_t sampler;                 /* BCG_EULER | BCG_HEUN */
+    int32_t max_regions;             /* R in [0, BCG_MAX_REGIONS]; 0 = no regions */
+    int32_t feather;                 /* [0, BCG_MAX_FEATHER] */
+    int32_t n_active;                /* entries of order[] to process, [0, n] */
+    int32_t num_sigmas;              /* length of sigmas */
+    int32_t mask_per_sample;         /* 1: mask [n,1,H,W]; 0: [1,1,H,W] */
+    float s2;                        /* stand-in data variance, > 0 */
+    const void* x;                   /* device [n,C,H,W] */
+    void* x_out;                     /* device [n,C,H,W] */
+    const float* sigmas;             /* device [num_sigmas] */
+    const int32_t* order;            /* device [n_active] sample ids */
+    const int32_t* step_idx;         /* device [n] */
+    const float* scale;              /* device [n] */
+    const int32_t* uncond_row;       /* device [n]; < 0 = uncond branch skipped */
+    const float* mu_uncond;          /* device [n][C] */
+    const float* mu_cond;            /* device [n][C] (samples with 0 regions) */
+    const int32_t* region_count;     /* device [n] or NULL when R == 0 */
+    const int32_t* region_box;       /* device [n][R][4] y0,y1,x0,x1 */
+    const float* region_strength;    /* device [n][R] */
+    const float* mu_region;          /* device [n][R][C] */
+    const void* x_orig;              /* device [n,C,H,W] or NULL (no inpaint) */
+    const float* mask;               /* device mask or NULL (with x_orig) */
+    float* stats;                    /* device [n][3] or NULL */
+    void* workspace;                 /* device scratch for stats, or NULL */
+    size_t workspace_bytes;
+} bcg_step_args;
+
+int guided_step(const bcg_step_args* args, void* stream);
+
+/* Bytes of device workspace guided_step needs for stats at this shape. */
+size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
+
+/*
+ * latent_init -- [S] "deterministic noise", "disable_noise": the sampler
+ * starts from the latent plus noise at the sample's first sigma,
+ *   x_out[i] = latent[i] + noise[i] * sigmas[step_idx[i]]   (fp32, rounded on store)
+ * latent (storage dtype) may be NULL (zero).  noise is device fp32
+ * [n,C,H,W] (drawn on the host by the caller).  Samples whose step_idx is
+ * outside [0, num_sigmas) are not written.
+ */
+int latent_init(int n, int C, int H, int W, int dtype, const float* noise,
+                const void* latent, const float* sigmas, int num_sigmas,
+                const int32_t* step_idx, void* x_out, void* stream);
+
+/*
+ * area_accumulate -- [S] "calc_cond_batch()": region outputs are accumulated
+ * into the full latent by strength and mask and overlaps are normalised by
+ * the weight sum.  Gather form (one writer per output element, no atomics).
+ *   region_pred  device fp32, packed crops: region r of sample i is [C,h,w]
+ *                at region_pred + region_off[i*R + r] (h, w from its box)
+ *   cond_out[i,c,y,x] = sum_r wh_r(y,x) * crop_r[c, y-y0_r, x-x0_r], with
+ *                wh_r = w_r / sum_r w_r over regions containing the pixel, or
+ *                fallback[i,c,y,x] (0 if fallback is NULL) where the sum is 0
+ *   wsum_out[i,y,x] = sum_r w_r(y,x)  (optional)
+ * Per-pixel weights are the guided_step ones.  Boxes whose crop does not fit
+ * between consecutive region_off entries, or past pred_elems, are skipped.
+ */
+int area_accumulate(int n, int C, int H, int W, int feather, int max_regions,
+                    const float* region_pred, int64_t pred_elems,
+                    const int64_t* region_off, const int32_t* region_count,
+                    const int32_t* region_box, const float* region_strength,
+                    const float* fallback, float* cond_out, float* wsum_out,
+                    void* stream);
+
+/*
+ * mask_blend -- [S] "inpaint and mask": out = m*a + (1 - m)*b with the mask
+ * broadcast over channels (mask [n,1,H,W] if mask_per_sample, else
+ * [1,1,H,W]); a, b, out in the storage dtype, out may alias a or b.
+ */
+int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void* b,
+               const float* mask, int mask_per_sample, void* out, void* stream);
+
+/*
+ * bcg_loop_* -- the sampler loop's per-step host work in native code: for
+ * launches k = k0 .. k0+count-1, t_i = start[i] + k (mod steps when wrap is
+ * set: steady-state continuous batching, every sample always active), the
+ * bucket plan is built (bcg_plan_build) straight into pinned staging row
+ * k mod rows, copied to the device row on `stream` (hipMemcpyAsync) and one
+ * guided_step is launched with that row.  SGLang BCG write-up, section 4
+ * stage 3: the plan is built by the scheduler before the launch and is
+ * immutable while the step runs.  A staging row is rewritten only after its
+ * previous copy has completed (an event per row).
+ *
+ * The descriptor is copied at create time; the arrays it points to (host plan
+ * inputs, the staging rows, every device array of `step`) are owned by the
+ * caller and must outlive the loop.  Row layout (4n int32):
+ *   [step_idx | scale (float bits) | uncond_row | order].
+ * step.order / step_idx / scale / uncond_row / n_active are ignored (filled
+ * per launch).  With replicas > 1, launch k advances replica k mod replicas:
+ * step.x and step.x_out are offset by (k mod replicas) * replica_stride bytes
+ * (several independent batches served round-robin).  If kernel_ms is not NULL, each guided_step launch is
+ * bracketed by HIP events on `stream`, bcg_loop_run waits for the last one,
+ * and *kernel_ms receives the summed launch durations.
+ * Errors: as bcg_plan_build and guided_step; BCG_EHIP for runtime failures.
+ */
+typedef struct {
+    bcg_plan_in plan;                /* plan.step_idx is ignored */
+    const int32_t* start;            /* host [n] start step of each sample */
+    int32_t wrap;                    /* 1: t = (start + k) mod steps */
+    int32_t rows;                    /* staging rows, >= 1 */
+    int32_t* host_slab;              /* pinned host [rows][4n] */
+    int32_t* dev_slab;               /* device [rows][4n] */
+    int32_t replicas;                /* >= 1 independent states of the batch */
+    int64_t replica_stride;          /* bytes between replicas of x and x_out */
+    bcg_step_args step;              /* launch template (replica 0) */
+} bcg_loop_desc;
+
+typedef struct bcg_loop bcg_loop;
+
+int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out);
+int bcg_loop_run(bcg_loop* loop, int k0, int count, void* stream, float* kernel_ms);
+int bcg_loop_destroy(bcg_loop* loop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BCG_H */

@@ -436,7 +436,14 @@ def sample_params(inp, i: int, sig_dtype=np.float64):
     return SampleParams(inp.mu_uncond[i], inp.mu_cond[i], sp.s2, regions,
                         sp.feather, sp.H, sp.W,
                         None if inp.mask is None else inp.mask[i, 0],
-                        None if inp.x_orig is None else inp.x_orig[i])
+                        None if inp.x_orig is None else stored_orig(inp)[i])
+
+
+def stored_orig(inp):
+    """The original latent as held by the path: in the storage dtype, like every
+    latent of the step (reading: the inpaint source latent is stored the same
+    way as the state it is blended into)."""
+    return to_storage(inp.x_orig, inp.spec.dtype)
 
 
 def coverage(inp):
@@ -473,7 +480,7 @@ def init_latent(inp, sig, storage: str):
     x = np.asarray(inp.noise, np.float64) * sig.astype(np.float64)[
         inp.start_step][:, None, None, None]
     if inp.x_orig is not None:
-        x = np.asarray(inp.x_orig, np.float64) + x
+        x = stored_orig(inp) + x
     return to_storage(x, storage)
 
 

@@ -165,14 +165,14 @@ def params32(inp, i):
                     inp.region_strength[i, :k], [inp.mu_region[i, r] for r in range(k)],
                     sp.feather, sp.H, sp.W,
                     None if inp.mask is None else inp.mask[i, 0],
-                    None if inp.x_orig is None else inp.x_orig[i])
+                    None if inp.x_orig is None else _store(inp.x_orig[i], sp.dtype))
 
 
 def init_latent32(inp, sig):
     sp = inp.spec
     x = inp.noise.astype(np.float32) * sig[inp.start_step][:, None, None, None]
     if inp.x_orig is not None:
-        x = inp.x_orig.astype(np.float32) + x
+        x = _store(inp.x_orig, sp.dtype) + x
     return _store(x, sp.dtype)
 
 

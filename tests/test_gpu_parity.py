@@ -1,0 +1,354 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars (written into each test):
+  * integers (plans, boxes) bit-exact -- covered on the CPU in test_host_lib;
+  * every stored state equal to mode M (the fixed fp32 evaluation order) bit
+    for bit, step after step, over whole trajectories;
+  * each step, teacher-forced from the mode D state, within 1e-5 of
+    max|ref| per sample (fp32 storage), or within half a bf16 ulp of the
+    unrounded mode D value plus that 1e-5 (bf16 storage);
+  * the final latent within 2e-2 absolute of mode M (bf16 storage; at most
+    1e-5 of the elements beyond it vs mode D, from storage rounding flips),
+    and within 1e-4 relative of mode D for fp32 storage.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import definition as D
+from oracle import mirror32 as M
+
+from gpu_helpers import (bf16_ulp, gpu_step_from, gpu_trajectory, oracle_step_D,
+                          oracle_step_M, per_sample_rel_err, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bucketed_classifier_free_amd
+    bucketed_classifier_free_amd.load()  # fails loudly without libbcg.so
+
+
+def _sampler(inp, **kw):
+    from bucketed_classifier_free_amd import GuidedSampler
+    return GuidedSampler.from_inputs(inp, **kw)
+
+
+def _check_step_vs_D(inp, got, ref_d, tag):
+    for i, ref in ref_d.items():
+        scale = max(np.abs(ref).max(), 1e-30)
+        err = np.abs(got[i].astype(np.float64) - ref)
+        if inp.spec.dtype == "f32":
+            assert err.max() <= 1e-5 * scale, f"{tag} sample {i}: {err.max() / scale:.3g} rel"
+        else:
+            bound = 0.5 * bf16_ulp(ref) + 1e-5 * scale
+            assert np.all(err <= bound), f"{tag} sample {i}: {float((err - bound).max()):.3g} over"
+
+
+def _check_full(inp, idx, launches=None):
+    """Whole trajectory on the GPU vs mode M (bit-exact, every launch) and mode D."""
+    sp = inp.spec
+    s = _sampler(inp)
+    xg, states = gpu_trajectory(s, launches, keep_samples=idx)
+    xm, mstates = M.trajectory32(inp, launches=launches, samples=idx, keep=True)
+    for k, st in enumerate(states):
+        ref = mstates[k + 1][idx]
+        bad = ~(st == ref)
+        assert not bad.any(), (f"{sp.name}: launch {k} differs from mode M at {int(bad.sum())} "
+                               f"elements, max {float(np.abs(st - ref).max()):.3g}")
+    xd = D.trajectory(inp, launches=launches, samples=idx)
+    err = np.abs(xg[idx].astype(np.float64) - xd[idx])
+    if sp.dtype == "bf16":
+        # 2e-2 absolute vs mode M (the same fp32 decisions; in fact identical) ...
+        assert np.abs(xg[idx] - xm[idx]).max() <= 2e-2
+        # ... and vs mode D, whose float64 arithmetic takes a different bf16 code
+        # now and then; a code flip while |x| is large survives the contraction
+        # of later steps as up to ~0.03 absolute.  Bound: at most 1e-5 of the
+        # elements beyond 2e-2, none beyond 0.0625.
+        assert (err > 2e-2).mean() <= 1e-5, float((err > 2e-2).mean())
+        assert err.max() <= 0.0625, float(err.max())
+    else:
+        assert per_sample_rel_err(xg, xd, idx).max() <= 1e-4
+    return xg
+
+
+def _teacher_forced(inp, idx, launches):
+    sp = inp.spec
+    sig, table, cov = D.run_setup(inp)
+    s = _sampler(inp)
+    _, dstates = D.trajectory(inp, launches=max(launches) + 1, samples=idx, keep=True)
+    for k in launches:
+        x_in = D.init_latent(inp, sig, sp.dtype).astype(np.float32)
+        x_in[idx] = dstates[k][idx]
+        got, plan = gpu_step_from(s, k, x_in)
+        p = D.build_plan(inp.start_step.astype(np.int64) + k, sp.steps, sp.num_buckets, table,
+                         inp.cfg_override, cov)
+        _check_step_vs_D(inp, got, oracle_step_D(inp, sig, p, k, x_in, idx), f"{sp.name} k={k}")
+        ref_m = oracle_step_M(inp, sig, p, k, x_in, idx)
+        for i, r in ref_m.items():
+            assert np.array_equal(got[i], r), f"{sp.name} k={k} sample {i} differs from mode M"
+        # inactive samples are not written
+        for i in idx:
+            if p["bucket_id"][i] < 0:
+                assert np.isnan(got[i]).all()
+
+
+# ---------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["tiny", "mixed_bucket", "throughput_bf16_heun", "regional_inpaint"])
+def test_workload_full_trajectory(name):
+    inp = W.make_inputs(W.config(name))
+    _check_full(inp, list(range(inp.spec.n)))
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixed_bucket", "throughput_bf16_heun", "regional_inpaint"])
+def test_workload_teacher_forced_steps(name):
+    inp = W.make_inputs(W.config(name))
+    sp = inp.spec
+    launches = list(range(sp.steps)) if sp.n * sp.C * sp.H * sp.W <= 1 << 20 else \
+        [0, 1, sp.steps // 2, sp.steps - 2, sp.steps - 1]
+    idx = list(range(sp.n)) if sp.n <= 16 else list(range(0, sp.n, 5))
+    _teacher_forced(inp, idx, launches)
+
+
+LARGE_SAMPLES = [0, 37, 101, 255]
+
+
+def test_large_full_size_sampled_trajectories():
+    """Full-size large workload in the bench's launch shape; sampled samples checked."""
+    inp = W.make_inputs(W.config("large_bf16"))
+    _check_full(inp, LARGE_SAMPLES)
+
+
+def test_large_full_size_teacher_forced():
+    inp = W.make_inputs(W.config("large_bf16"))
+    _teacher_forced(inp, LARGE_SAMPLES, [0, 24, 49])
+
+
+# ---------------------------------------------------------------- small shapes, edge cases
+
+SMALL = [
+    dict(dtype="f32", sampler="euler"),
+    dict(dtype="f32", sampler="heun"),
+    dict(dtype="bf16", sampler="euler"),
+    dict(dtype="bf16", sampler="heun"),
+    dict(dtype="f32", sampler="euler", regions=1),
+    dict(dtype="f32", sampler="heun", regions=3, inpaint=True),
+    dict(dtype="bf16", sampler="euler", regions=2, inpaint=True),
+    dict(dtype="bf16", sampler="heun", regions=4),
+    dict(dtype="f32", sampler="euler", regions=4, inpaint=True),
+]
+
+
+@pytest.mark.parametrize("shape", [(3, 3, 17, 40), (4, 2, 13, 21), (2, 5, 1, 8), (3, 64, 4, 8)])
+@pytest.mark.parametrize("kw", SMALL)
+def test_small_shapes_full_trajectory(shape, kw):
+    # (17, 40): vector path with a ragged last tile; (13, 21): H*W odd -> scalar
+    # path; (1, 8): a single row; C = 64: the channel limit
+    n, C, H, Wd = shape
+    sp = W.small_spec(n=n, C=C, H=H, W=Wd, steps=5, num_buckets=3, feather=3, **kw)
+    _check_full(W.make_inputs(sp), list(range(n)))
+
+
+def test_region_edge_cases():
+    sp = W.small_spec(n=5, C=3, H=16, W=24, regions=3, steps=4, skip_frac=0.0, mixed_start=False,
+                      curve=W.Curve("const", 1.0), num_buckets=1, feather=4)
+    inp = W.make_inputs(sp)
+    inp.region_count[:] = [0, 1, 2, 3, 3]            # a sample with no regions
+    inp.region_strength[4, 1] = 0.0                  # a zero-strength region
+    inp.region_frac[3, 0] = (0, 0, 1, 1)             # a full-frame region (covers -> skip)
+    _check_full(inp, list(range(5)))
+    # feather 0 (no ramp) and a feather wider than the boxes
+    for F in (0, 64):
+        _check_full(W.make_inputs(dataclasses.replace(sp, feather=F)), list(range(5)))
+
+
+def test_scale_zero_and_one_special_cases():
+    base = W.small_spec(n=3, C=2, H=8, W=16, steps=4, skip_frac=0.0, num_buckets=1,
+                        mixed_start=False, regions=2)
+    for v in (0.0, 1.0):
+        inp = W.make_inputs(dataclasses.replace(base, curve=W.Curve("const", v)))
+        _check_full(inp, [0, 1, 2])
+
+
+def test_all_inactive_launch_writes_nothing():
+    sp = W.small_spec(n=3, C=2, H=8, W=8, steps=4)
+    inp = W.make_inputs(sp)
+    inp.start_step[:] = 9                            # beyond the trajectory
+    s = _sampler(inp)
+    x = to_dev(np.ones((3, 2, 8, 8)), sp.dtype)
+    s.step(0, x)
+    torch.cuda.synchronize()
+    assert (to_np(x) == 1).all()
+
+
+def test_in_place_equals_out_of_place_and_deterministic():
+    inp = W.make_inputs(W.small_spec(n=4, C=4, H=32, W=32, regions=2, inpaint=True,
+                                     dtype="bf16", sampler="heun"))
+    s = _sampler(inp)
+    x0 = s.init_state()
+    a = x0.clone(); b = torch.empty_like(x0); c = x0.clone()
+    s.step(1, a)
+    s.step(1, x0, b)
+    s.step(1, c)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_batch_permutation_permutes_outputs():
+    inp = W.make_inputs(W.small_spec(n=6, C=3, H=16, W=16, regions=2, steps=6))
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    xa, _ = gpu_trajectory(_sampler(inp))
+    xb, _ = gpu_trajectory(_sampler(inp.subset(perm)))
+    assert np.array_equal(xa[perm], xb)
+
+
+def test_bucket_count_invariance_gpu():
+    base = W.small_spec(n=3, C=2, H=8, W=16, steps=16, curve=W.Curve("const", 1.7))
+    outs = [gpu_trajectory(_sampler(W.make_inputs(dataclasses.replace(base, num_buckets=nb))))[0]
+            for nb in (1, 4, 8, 16)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_resume_equals_uninterrupted():
+    from bucketed_classifier_free_amd import Interrupted
+    inp = W.make_inputs(W.small_spec(n=3, C=2, H=8, W=16, steps=6, sampler="heun"))
+    full, _ = gpu_trajectory(_sampler(inp))
+    s = _sampler(inp)
+    x = s.init_state()
+    with pytest.raises(Interrupted) as e:
+        s.run(x, cancel=lambda k=iter(range(100)): next(k) >= 3)
+    assert e.value.step == 3
+    for k in range(3, 6):
+        s.step(k, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(x), full)
+
+
+def test_mask_broadcast_single_mask():
+    sp = W.small_spec(n=3, C=2, H=8, W=16, steps=4, inpaint=True)
+    inp = W.make_inputs(sp)
+    inp.mask[:] = inp.mask[0]
+    a, _ = gpu_trajectory(_sampler(inp))
+    from bucketed_classifier_free_amd import GuidedSampler
+    s = GuidedSampler.from_inputs(inp)
+    s.d_mask = s.d_mask[:1].contiguous()
+    b, _ = gpu_trajectory(s)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- latent init, stats
+
+@pytest.mark.parametrize("name", ["tiny", "regional_inpaint", "throughput_bf16_heun"])
+def test_latent_init_matches_oracle(name):
+    inp = W.make_inputs(W.config(name))
+    s = _sampler(inp)
+    x = to_np(s.init_state())
+    sig, _, _ = D.run_setup(inp)
+    assert np.array_equal(x, M.init_latent32(inp, sig))
+    d = D.init_latent(inp, sig, inp.spec.dtype)
+    assert np.abs(x - d).max() <= (1e-6 * np.abs(d).max() if inp.spec.dtype == "f32"
+                                   else 0.5 * bf16_ulp(np.abs(d).max()) + 1e-6)
+
+
+@pytest.mark.parametrize("kw", [dict(regions=0), dict(regions=3, inpaint=True), dict(regions=2, dtype="bf16")])
+def test_norm_stats_match_oracle(kw):
+    from bucketed_classifier_free_amd import guided_step_workspace_size
+    inp = W.make_inputs(W.small_spec(n=5, C=3, H=12, W=100, steps=5, skip_frac=0.4, **kw))
+    sp = inp.spec
+    s = _sampler(inp)
+    sig, table, cov = D.run_setup(inp)
+    x = s.init_state()
+    x_np = to_np(x)
+    stats = torch.zeros((sp.n, 3), device="cuda")
+    ws = torch.empty(guided_step_workspace_size(sp.n, sp.C, sp.H, sp.W) // 4 + 1, device="cuda")
+    p = s.step(0, x, torch.empty_like(x), stats=stats, workspace=ws)
+    torch.cuda.synchronize()
+    got = to_np(stats)
+    dplan = D.build_plan(inp.start_step.astype(np.int64), sp.steps, sp.num_buckets, table,
+                         inp.cfg_override, cov)
+    for i in range(sp.n):
+        if p.bucket_id[i] < 0:
+            continue
+        t = int(inp.start_step[i])
+        ref = D.norm_stats(x_np[i].astype(np.float64), float(sig[t]), float(p.scale[i]),
+                           D.sample_params(inp, i), bool(dplan["need_uncond"][i]))
+        np.testing.assert_allclose(got[i], ref, rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------- standalone kernels
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 4, 16, 32), (2, 3, 7, 9)])
+def test_mask_blend_matches_oracle(dtype, shape):
+    from bucketed_classifier_free_amd import mask_blend
+    rng = np.random.default_rng(4)
+    n, C, H, Wd = shape
+    a = rng.standard_normal(shape).astype(np.float32)
+    b = rng.standard_normal(shape).astype(np.float32)
+    m = np.where(rng.random((n, 1, H, Wd)) < 0.5, 1.0, rng.random((n, 1, H, Wd))).astype(np.float32)
+    if dtype == "bf16":
+        a = D.round_bf16(a).astype(np.float32); b = D.round_bf16(b).astype(np.float32)
+    A, B = to_dev(a, dtype), to_dev(b, dtype)
+    out = torch.empty_like(A)
+    mask_blend(A, B, torch.from_numpy(m).cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), M.mask_blend32(a, b, m, dtype))
+    ref = np.stack([D.inpaint_blend(a[i].astype(np.float64), b[i].astype(np.float64), m[i, 0])
+                    for i in range(n)])
+    err = np.abs(to_np(out) - ref)
+    if dtype == "f32":
+        assert err.max() <= 1e-6 * np.abs(ref).max()
+    else:
+        assert np.all(err <= 0.5 * bf16_ulp(ref) + 1e-6)
+    # in place into a, and the single broadcast mask
+    mask_blend(A, B, torch.from_numpy(m[:1]).cuda(), A)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(A), M.mask_blend32(a, b, np.broadcast_to(m[:1], m.shape), dtype))
+
+
+@pytest.mark.parametrize("shape,R", [((3, 4, 20, 30), 3), ((2, 2, 9, 13), 4), ((2, 3, 16, 16), 1)])
+def test_area_accumulate_matches_oracle(shape, R):
+    from bucketed_classifier_free_amd import area_accumulate, bcg_plan_build
+    n, C, H, Wd = shape
+    rng = np.random.default_rng(5)
+    frac = np.stack([rng.uniform(0, 0.6, (n, R)), rng.uniform(0, 0.6, (n, R)),
+                     rng.uniform(0.2, 0.6, (n, R)), rng.uniform(0.2, 0.6, (n, R))], -1)
+    cnt = np.full(n, R, np.int32)
+    cnt[-1] = max(R - 1, 1)
+    st = rng.uniform(0.5, 1.5, (n, R)).astype(np.float32)
+    plan = bcg_plan_build(np.zeros(n, np.int32), 1, np.float32([2.0]), C=C, H=H, W=Wd,
+                          region_count=cnt, region_frac=frac, region_strength=st, max_regions=R)
+    total = int(plan.region_off[-1])
+    pred = rng.standard_normal(total).astype(np.float32)
+    fb = rng.standard_normal(shape).astype(np.float32)
+    out = torch.empty(shape, device="cuda")
+    ws = torch.empty((n, H, Wd), device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    area_accumulate(dev(pred), dev(plan.region_off), dev(cnt), dev(plan.region_box), dev(st), out,
+                    feather=3, fallback=dev(fb), wsum_out=ws)
+    torch.cuda.synchronize()
+    got, gws = to_np(out), to_np(ws)
+    for i in range(n):
+        boxes = [tuple(plan.region_box[i, r]) for r in range(cnt[i])]
+        crops = []
+        for r, (y0, y1, x0, x1) in enumerate(boxes):
+            o = int(plan.region_off[i * R + r])
+            crops.append(pred[o:o + C * (y1 - y0) * (x1 - x0)].reshape(C, y1 - y0, x1 - x0))
+        want, wsum = M.area_accumulate32(crops, boxes, st[i, :cnt[i]], H, Wd, 3, fb[i])
+        assert np.array_equal(got[i], want)
+        assert np.array_equal(gws[i], wsum)
+        # mode D: weighted mean of the crops, fallback where uncovered
+        wts = [D.region_weight(b, s, H, Wd, 3) for b, s in zip(boxes, st[i, :cnt[i]])]
+        full = []
+        for (y0, y1, x0, x1), cr in zip(boxes, crops):
+            f = np.zeros((C, H, Wd)); f[:, y0:y1, x0:x1] = cr; full.append(f)
+        ref = D.regional_cond(full, wts, fb[i].astype(np.float64))
+        assert np.abs(got[i] - ref).max() <= 1e-5 * np.abs(ref).max()

@@ -1,0 +1,190 @@
+"""Host half of libbcg against the oracle, on the CPU (no GPU calls).
+
+The library must load and export every function include/bcg.h declares;
+sigma_schedule, bucket_table and bcg_plan_build are plain host code and are
+compared with the oracle bit for bit; argument errors come back as status
+codes before anything is launched.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bucketed_classifier_free_amd as bcg
+from bucketed_classifier_free_amd import _lib as L
+import workloads as W
+from oracle import definition as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "bcg.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 13, names
+    lib = C.CDLL(L.LIB_PATH)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+    assert sorted(L.EXPORTS) == names
+    assert lib.bcg_abi_version() == 1
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_sigma_schedule_bit_exact_on_workloads(name):
+    sp = W.config(name)
+    got, nb = bcg.sigma_schedule(sp.sigma_max, sp.sigma_min, sp.steps, sp.denoise)
+    want, nb2 = D.sigma_schedule(sp.sigma_max, sp.sigma_min, sp.steps, sp.denoise)
+    assert nb == nb2
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_sigma_schedule_bit_exact_random():
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        steps = int(rng.integers(1, 400))
+        den = float(rng.choice([1.0, rng.uniform(0.05, 1.0)]))
+        smax = float(rng.uniform(1.0, 100.0))
+        smin = float(rng.uniform(1e-3, 0.9))
+        got, nb = bcg.sigma_schedule(smax, smin, steps, den)
+        want, nb2 = D.sigma_schedule(smax, smin, steps, den)
+        assert nb == nb2
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_bucket_table_bit_exact():
+    for kind, p in (("const", (7.0, 0, 0)), ("linear", (2.0, 1.2, 0)), ("front_high", (2.0, 1.2, 0.2)),
+                    ("linear", (0.5, 9.0, 0))):
+        for nb in (1, 2, 3, 8, 16, 64):
+            got = bcg.bucket_table(kind, *p, num_buckets=nb)
+            want = D.bucket_table(kind, *p, nb)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def _compare_plan(got, want):
+    for k in ("bucket_id", "uncond_row", "cond_row", "bucket_count", "bucket_offset"):
+        assert np.array_equal(getattr(got, k), want[k]), k
+    assert np.array_equal(got.uncond_offset, want["uncond_offset"])
+    assert np.array_equal(got.scale.view(np.uint32), want["scale"].view(np.uint32))
+    assert got.n_active == want["n_active"] and got.n_uncond == want["n_uncond"]
+    assert np.array_equal(got.order[:got.n_active], want["order"])
+    assert np.all(got.order[got.n_active:] == -1)
+
+
+def test_plan_build_bit_exact_random():
+    rng = np.random.default_rng(9)
+    for _ in range(400):
+        n = int(rng.integers(0, 50))
+        steps = int(rng.integers(1, 80))
+        nb = int(rng.integers(1, 20))
+        t = rng.integers(-4, steps + 4, size=n).astype(np.int32)
+        table = D.bucket_table("linear", 2.0, rng.choice([1.0, 1.2]), 0, nb)
+        ov = np.where(rng.random(n) < 0.3, rng.choice([1.0, 3.5]), np.nan).astype(np.float32)
+        got = bcg.bcg_plan_build(t, steps, table, cfg_override=ov)
+        _compare_plan(got, D.build_plan(t, steps, nb, table, ov, None))
+
+
+@pytest.mark.parametrize("name", ["regional_inpaint", "large_bf16"])
+def test_plan_regions_bit_exact_on_workloads(name):
+    inp = W.make_inputs(W.config(name))
+    sp = inp.spec
+    sig, table, cov = D.run_setup(inp)
+    for k in (0, 7, sp.steps - 1):
+        t = inp.start_step + k
+        got = bcg.bcg_plan_build(t, sp.steps, table, C=sp.C, H=sp.H, W=sp.W,
+                                 cfg_override=inp.cfg_override, region_count=inp.region_count,
+                                 region_frac=inp.region_frac, region_strength=inp.region_strength,
+                                 max_regions=sp.regions)
+        _compare_plan(got, D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov))
+    off = 0
+    for i in range(sp.n):
+        for r in range(sp.regions):
+            box = D.area_box(inp.region_frac[i, r], sp.H, sp.W)
+            assert tuple(got.region_box[i, r]) == box
+            assert got.region_off[i * sp.regions + r] == off
+            off += sp.C * (box[1] - box[0]) * (box[3] - box[2])
+    assert got.region_off[-1] == off
+
+
+def test_plan_coverage_forces_uncond_at_scale_one():
+    # two samples at cfg 1: one fully covered by its regions, one not
+    frac = np.array([[[0, 0, 1, 0.5], [0, 0.5, 1, 0.5]],
+                     [[0, 0, 0.5, 0.5], [0.5, 0.5, 0.5, 0.5]]], np.float64)
+    plan = bcg.bcg_plan_build(np.zeros(2, np.int32), 4, np.float32([1.0]), C=2, H=8, W=8,
+                              region_count=np.int32([2, 2]), region_frac=frac,
+                              region_strength=np.float32([[1, 1], [1, 1]]), max_regions=2)
+    assert plan.uncond_row[0] == -1 and plan.uncond_row[1] == 0
+    # a zero-strength region does not cover
+    plan = bcg.bcg_plan_build(np.zeros(2, np.int32), 4, np.float32([1.0]), C=2, H=8, W=8,
+                              region_count=np.int32([2, 2]), region_frac=frac,
+                              region_strength=np.float32([[1, 0], [1, 1]]), max_regions=2)
+    assert plan.uncond_row[0] >= 0
+
+
+def test_plan_coverage_matches_bruteforce_random():
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        n, R = 6, int(rng.integers(1, 5))
+        H, Wd = int(rng.integers(1, 20)), int(rng.integers(1, 20))
+        frac = rng.uniform(-0.2, 1.2, size=(n, R, 4))
+        frac[..., 2:] = rng.uniform(0.0, 1.1, size=(n, R, 2))
+        cnt = rng.integers(0, R + 1, size=n).astype(np.int32)
+        st = np.where(rng.random((n, R)) < 0.2, 0.0, 1.0).astype(np.float32)
+        plan = bcg.bcg_plan_build(np.zeros(n, np.int32), 3, np.float32([1.0]), C=1, H=H, W=Wd,
+                                  region_count=cnt, region_frac=frac, region_strength=st,
+                                  max_regions=R)
+        for i in range(n):
+            boxes = [D.area_box(frac[i, r], H, Wd) for r in range(cnt[i])]
+            cov = True if cnt[i] == 0 else D.covers_frame(boxes, st[i, :cnt[i]], H, Wd)
+            assert (plan.uncond_row[i] == -1) == cov
+            for r in range(cnt[i]):
+                assert tuple(plan.region_box[i, r]) == boxes[r]
+
+
+def test_error_paths_return_codes():
+    with pytest.raises(L.BCGError) as e:
+        bcg.sigma_schedule(1.0, 2.0, 10)
+    assert e.value.code == L.BCG_EINVAL and "sigma_max" in str(e.value)
+    with pytest.raises(L.BCGError):
+        bcg.sigma_schedule(14.6, 0.03, 10, denoise=0.0)
+    with pytest.raises(L.BCGError):
+        bcg.bucket_table("linear", 2.0, 1.2, 0.0, num_buckets=0)
+    with pytest.raises(L.BCGError) as e:
+        bcg.bcg_plan_build(np.zeros(2, np.int32), 5, np.float32([2.0]), C=1, H=4, W=4,
+                           region_count=np.int32([3, 0]), region_frac=np.zeros((2, 2, 4)),
+                           region_strength=np.ones((2, 2), np.float32), max_regions=2)
+    assert e.value.code == L.BCG_EINVAL
+    with pytest.raises(L.BCGError):
+        bcg.bcg_plan_build(np.zeros(1, np.int32), 5, np.float32([np.inf]))
+    with pytest.raises(L.BCGError):  # negative strength
+        bcg.bcg_plan_build(np.zeros(1, np.int32), 5, np.float32([2.0]), C=1, H=4, W=4,
+                           region_count=np.int32([1]), region_frac=np.zeros((1, 1, 4)),
+                           region_strength=np.float32([[-1.0]]), max_regions=1)
+
+
+def test_device_entry_points_validate_before_launch():
+    lib = L.lib()
+    a = L.StepArgs()
+    a.n, a.C, a.H, a.W = 2, 0, 4, 4
+    assert lib.guided_step(C.byref(a), None) == L.BCG_ESHAPE
+    a.C = 4
+    a.dtype = 7
+    assert lib.guided_step(C.byref(a), None) == L.BCG_EDTYPE
+    a.dtype, a.sampler, a.num_sigmas, a.s2, a.n_active = 0, 5, 11, 0.25, 1
+    assert lib.guided_step(C.byref(a), None) == L.BCG_EINVAL
+    a.sampler = 0
+    assert lib.guided_step(C.byref(a), None) == L.BCG_EINVAL      # NULL device pointers
+    assert b"NULL" in lib.bcg_last_error()
+    a.n_active = 0
+    assert lib.guided_step(C.byref(a), None) == L.BCG_OK          # nothing to do, no launch
+    assert lib.latent_init(1, 1, 1, 1, 9, None, None, None, 1, None, None, None) == L.BCG_EDTYPE
+    assert lib.mask_blend(1, 1, 1, 1, 0, None, None, None, 3, None, None) == L.BCG_EINVAL
+    assert lib.area_accumulate(1, 1, 1, 1, 0, 0, None, 0, None, None, None, None, None, None,
+                               None, None) == L.BCG_EINVAL
+    assert lib.guided_step_workspace_size(4, 16, 128, 128, 1) == 4 * 16 * 128 * 3 * 4
