@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "latent element-steps/sec on 1 GPU + achieved HBM GB/s as % of peak"
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_api.hip", "bcg_step_bf16.hip",
-                  "bcg_step_f32.hip"]
+                  "bcg_step_f32.hip", "bcg_step_bf16_nt.hip", "bcg_step_f32_nt.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "guided_step_large_bf16_traffic.json")
 
 
@@ -99,6 +99,35 @@ def copy_probe(mib: int, iters: int):
     print(json.dumps({"copy_probe_mib": mib, "ms": ms, "GBps": 2 * mib * (1 << 20) / ms / 1e6}))
 
 
+def _counter_means(path, counter):
+    import csv
+    import collections
+    acc = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, workload):
+    """Per-launch HBM bytes of guided_step from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for a plain device copy of copy_mib MiB."""
+    copy_bytes = copy_mib * (1 << 20)
+    pick = lambda d, key: max((v for k, v in d.items() if key in k), default=None)
+    cf = pick(_counter_means(copy_fetch_csv, "FETCH_SIZE"), "copyBuffer")
+    cw = pick(_counter_means(copy_write_csv, "WRITE_SIZE"), "copyBuffer")
+    f = pick(_counter_means(fetch_csv, "FETCH_SIZE"), "guided_step_kernel")
+    w = pick(_counter_means(write_csv, "WRITE_SIZE"), "guided_step_kernel")
+    rf, rw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    return {"workload": workload, "kernel_hash": kernel_hash(),
+            "fetch_kib_raw": f, "write_kib_raw": w, "copy_fetch_kib_raw": cf,
+            "copy_write_kib_raw": cw, "copy_mib": copy_mib,
+            "fetch_scale": rf, "write_scale": rw,
+            "bytes_per_launch": f * 1024 * rf + w * 1024 * rw}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,7 +138,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--upload-batch", type=int, default=8)
+    ap.add_argument("--async-upload", type=int, default=0)
+    ap.add_argument("--timing-every", type=int, default=10,
+                    help="bracket every m-th launch with HIP events (kernel duration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the traffic record from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_from_counters(*args.traffic_from, 256, args.workload)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path keeps every sample on one device and its "
               "multi-GPU form (sample-sharded, no per-step communication) is not built; "
@@ -134,19 +175,19 @@ def main():
     x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
     for r in range(R):
         s.init_state(x[r])
-    loop = s.native_loop(x if R > 1 else x[0])
+    loop = s.native_loop(x if R > 1 else x[0], upload_batch=args.upload_batch,
+                         async_upload=bool(args.async_upload), timing_every=args.timing_every)
     loop.run(0, args.warmup)
     torch.cuda.synchronize()
     elems_per_launch = spec.n * spec.C * spec.H * spec.W  # every sample active (steady state)
     t0 = time.perf_counter()
-    kernel_ms = loop.run(args.warmup, args.steps, timing=True)
+    launch_ms = loop.run(args.warmup, args.steps, timing=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if not torch.isfinite(x.float()).all():
         raise RuntimeError("non-finite state after the timed steps")
 
     value = elems_per_launch * args.steps / wall
-    launch_ms = kernel_ms / args.steps
     bpe = bytes_per_element(spec)
     alg_bytes = bpe * elems_per_launch
     achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
@@ -172,10 +213,12 @@ def main():
         "config": {"workload": spec.name, "batch": spec.n, "latent": [spec.C, spec.H, spec.W],
                    "storage": spec.dtype, "sampler": spec.sampler, "schedule_steps": spec.steps,
                    "buckets": spec.num_buckets, "regions": spec.regions,
-                   "progress": "mixed, steady state", "replicas": R},
+                   "progress": "mixed, steady state", "replicas": R,
+                   "plan_upload_batch": args.upload_batch, "async_upload": bool(args.async_upload)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "kernel": {"name": "guided_step", "avg_launch_us": launch_ms * 1e3,
+                   "timed_launches": (args.steps + args.timing_every - 1) // args.timing_every,
                    "algorithmic_bytes_per_launch": alg_bytes, "bytes_per_element_step": bpe,
                    "element_steps_per_s_kernel_only": elems_per_launch / (launch_ms * 1e-3),
                    "kernel_hash": kernel_hash()},

@@ -12,6 +12,7 @@ BCG_OK, BCG_EINVAL, BCG_ESHAPE, BCG_EDTYPE, BCG_EHIP = 0, -1, -2, -3, -4
 BCG_F32, BCG_BF16 = 0, 1
 BCG_EULER, BCG_HEUN = 0, 1
 BCG_SCHED_LOGLINEAR = 0
+BCG_CACHE_KEEP, BCG_CACHE_STREAM = 0, 1
 BCG_CURVE = {"const": 0, "linear": 1, "front_high": 2}
 BCG_MAX_REGIONS = 4
 BCG_MAX_CHANNELS = 64
@@ -32,21 +33,22 @@ class PlanIn(C.Structure):
                 ("C", C.c_int32), ("H", C.c_int32), ("W", C.c_int32),
                 ("max_regions", C.c_int32),
                 ("bucket_cfg", vp), ("step_idx", vp), ("cfg_override", vp),
-                ("region_count", vp), ("region_frac", vp), ("region_strength", vp)]
+                ("region_count", vp), ("region_frac", vp), ("region_strength", vp),
+                ("covered", vp)]
 
 
 class PlanOut(C.Structure):
     _fields_ = [("bucket_id", vp), ("scale", vp), ("uncond_row", vp), ("cond_row", vp),
                 ("order", vp), ("bucket_count", vp), ("bucket_offset", vp),
                 ("uncond_offset", vp), ("region_box", vp), ("region_off", vp),
-                ("n_active", C.c_int32), ("n_uncond", C.c_int32)]
+                ("covered_out", vp), ("n_active", C.c_int32), ("n_uncond", C.c_int32)]
 
 
 class StepArgs(C.Structure):
     _fields_ = [("n", C.c_int32), ("C", C.c_int32), ("H", C.c_int32), ("W", C.c_int32),
                 ("dtype", C.c_int32), ("sampler", C.c_int32), ("max_regions", C.c_int32),
                 ("feather", C.c_int32), ("n_active", C.c_int32), ("num_sigmas", C.c_int32),
-                ("mask_per_sample", C.c_int32), ("s2", C.c_float),
+                ("mask_per_sample", C.c_int32), ("cache_hint", C.c_int32), ("s2", C.c_float),
                 ("x", vp), ("x_out", vp), ("sigmas", vp), ("order", vp), ("step_idx", vp),
                 ("scale", vp), ("uncond_row", vp), ("mu_uncond", vp), ("mu_cond", vp),
                 ("region_count", vp), ("region_box", vp), ("region_strength", vp),
@@ -57,7 +59,8 @@ class StepArgs(C.Structure):
 class LoopDesc(C.Structure):
     _fields_ = [("plan", PlanIn), ("start", vp), ("wrap", C.c_int32), ("rows", C.c_int32),
                 ("host_slab", vp), ("dev_slab", vp), ("replicas", C.c_int32),
-                ("replica_stride", C.c_int64), ("step", StepArgs)]
+                ("replica_stride", C.c_int64), ("upload_batch", C.c_int32),
+                ("async_upload", C.c_int32), ("timing_every", C.c_int32), ("step", StepArgs)]
 
 
 _lib = None

@@ -90,6 +90,7 @@ class Plan:
     uncond_offset: np.ndarray
     region_box: np.ndarray | None
     region_off: np.ndarray | None
+    covered: np.ndarray
     n_active: int
     n_uncond: int
 
@@ -102,13 +103,17 @@ def plan_out_arrays(n, nb, R, bucket_id=None, scale=None, uncond_row=None, order
                 order=z(order, n, np.int32), bucket_count=np.empty(nb, np.int32),
                 bucket_offset=np.empty(nb + 1, np.int32), uncond_offset=np.empty(nb + 1, np.int32),
                 region_box=np.empty((n, R, 4), np.int32) if R > 0 else None,
-                region_off=np.empty(n * R + 1, np.int64) if R > 0 else None)
+                region_off=np.empty(n * R + 1, np.int64) if R > 0 else None,
+                covered=np.empty(n, np.uint8))
 
 
 def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, W: int = 1,
                    cfg_override=None, region_count=None, region_frac=None,
-                   region_strength=None, max_regions: int = 0, out=None) -> Plan:
-    """Bucket plan of one step (host arrays in, host arrays out)."""
+                   region_strength=None, max_regions: int = 0, covered=None, out=None) -> Plan:
+    """Bucket plan of one step (host arrays in, host arrays out).
+
+    ``covered`` (optional, [n] bool/uint8) supplies the per-sample coverage
+    flags of an earlier plan; the region arrays are then not used."""
     step_idx = _np(step_idx, np.int32, name="step_idx")
     n = step_idx.size
     cfg = _np(bucket_cfg, np.float32, name="bucket_cfg")
@@ -118,17 +123,20 @@ def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, 
     rc = _np(region_count, np.int32, (n,), "region_count") if R > 0 and region_count is not None else None
     rf = _np(region_frac, np.float64, (n, R, 4), "region_frac") if rc is not None else None
     rs = _np(region_strength, np.float32, (n, R), "region_strength") if rc is not None else None
+    cov = _np(covered, np.uint8, (n,), "covered")
     o = out if out is not None else plan_out_arrays(n, nb, R)
     pin = L.PlanIn(n, steps, nb, C, H, W, R, _np_ptr(cfg), _np_ptr(step_idx), _np_ptr(ov),
-                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs))
+                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs), _np_ptr(cov))
     pout = L.PlanOut(*(_np_ptr(o[k]) for k in ("bucket_id", "scale", "uncond_row", "cond_row",
                                                "order", "bucket_count", "bucket_offset",
-                                               "uncond_offset", "region_box", "region_off")),
+                                               "uncond_offset", "region_box", "region_off",
+                                               "covered")),
                      0, 0)
     L.check(L.lib().bcg_plan_build(ct.byref(pin), ct.byref(pout)))
     return Plan(o["bucket_id"], o["scale"], o["uncond_row"], o["cond_row"], o["order"],
                 o["bucket_count"], o["bucket_offset"], o["uncond_offset"], o["region_box"],
-                o["region_off"], int(pout.n_active), int(pout.n_uncond))
+                o["region_off"], o["covered"].astype(bool), int(pout.n_active),
+                int(pout.n_uncond))
 
 
 # ---------------------------------------------------------------- device calls
@@ -140,7 +148,8 @@ def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
 def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond, mu_cond, *,
                 n_active: int, sampler: str, s2: float, feather: int = 0,
                 region_count=None, region_box=None, region_strength=None, mu_region=None,
-                x_orig=None, mask=None, stats=None, workspace=None, stream=None):
+                x_orig=None, mask=None, stats=None, workspace=None, cache_hint: int = 0,
+                stream=None):
     """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU."""
     _dev(x, "x")
     if x.dim() != 4:
@@ -187,7 +196,7 @@ def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond,
     if sampler not in _SAMPLER:
         raise ValueError(f"unknown sampler {sampler!r}")
     a = L.StepArgs(n, Cc, H, W, _DT[x.dtype], _SAMPLER[sampler], R, int(feather), int(n_active),
-                   sigmas.numel(), mps, float(s2),
+                   sigmas.numel(), mps, int(cache_hint), float(s2),
                    _ptr(x), _ptr(x_out), _ptr(sigmas), _ptr(order), _ptr(step_idx), _ptr(scale),
                    _ptr(uncond_row), _ptr(mu_uncond), _ptr(mu_cond), _ptr(region_count),
                    _ptr(region_box), _ptr(region_strength), _ptr(mu_region), _ptr(x_orig),

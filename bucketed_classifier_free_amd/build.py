@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbcg.so")
 
-SOURCES = ["bcg_host.cpp", "bcg_api.hip", "bcg_loop.hip", "bcg_step_f32.hip", "bcg_step_bf16.hip"]
+SOURCES = ["bcg_host.cpp", "bcg_api.hip", "bcg_loop.hip", "bcg_step_f32.hip", "bcg_step_bf16.hip",
+           "bcg_step_f32_nt.hip", "bcg_step_bf16_nt.hip"]
 ARCH = "gfx950"
 
 

@@ -29,11 +29,24 @@ int hip_status(hipError_t e, const char* what) {
     return BCG_OK;
 }
 
-// Workgroup size: 256 lanes unless the grid would leave the 256 CUs thin.
-int pick_block(int64_t samples, int64_t nvec) {
-    int bs = 256;
-    while (bs > 64 && samples * ((nvec + bs - 1) / bs) < 2048) bs /= 2;
-    return bs;
+// Launch shape of the fused step: workgroups of `block` lanes, each lane
+// taking `vpt` vectors.  Large batches get about one resident round of
+// workgroups (4 per CU on 256 CUs) with vpt > 1, so the per-workgroup set-up
+// is amortised and no partial second round is left; small batches shrink the
+// workgroup so the grid still spreads over the CUs.
+struct LaunchShape {
+    int block, vpt;
+};
+LaunchShape pick_shape(int64_t samples, int64_t nvec) {
+    constexpr int64_t kResident = 256 * 4;
+    int bs = 256, vpt = 1;
+    auto blocks = [&](int b, int v) { return samples * ((nvec + (int64_t)b * v - 1) / ((int64_t)b * v)); };
+    if (blocks(bs, vpt) > kResident * 3 / 2) {
+        while (vpt < 8 && blocks(bs, vpt) > kResident * 3 / 2) vpt *= 2;
+    } else {
+        while (bs > 64 && blocks(bs, vpt) < kResident) bs /= 2;
+    }
+    return {bs, vpt};
 }
 
 // ------------------------------------------------------------ norm stats
@@ -312,6 +325,8 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     if (a->num_sigmas < 2) return fail(BCG_EINVAL, "guided_step: num_sigmas %d < 2", a->num_sigmas);
     if (!(a->s2 > 0.0f) || !std::isfinite(a->s2)) return fail(BCG_EINVAL, "guided_step: s2 must be finite and > 0");
     if (a->mask_per_sample != 0 && a->mask_per_sample != 1) return fail(BCG_EINVAL, "guided_step: mask_per_sample must be 0 or 1");
+    if (a->cache_hint != BCG_CACHE_KEEP && a->cache_hint != BCG_CACHE_STREAM)
+        return fail(BCG_EINVAL, "guided_step: unknown cache_hint %d", a->cache_hint);
     if (a->n_active == 0) return BCG_OK;
     if (!a->x || !a->x_out || !a->sigmas || !a->order || !a->step_idx || !a->scale || !a->uncond_row ||
         !a->mu_uncond || !a->mu_cond)
@@ -340,6 +355,7 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     p.num_sigmas = a->num_sigmas;
     p.HW = HW;
     p.nvec = (int)(vec ? HW / VV : HW);
+    p.rows_aligned = vec ? (a->W % VV == 0) : 1;
     p.mask_stride = a->mask_per_sample ? (int)HW : 0;
     p.s2 = a->s2;
     p.x = a->x; p.x_out = a->x_out; p.sigmas = a->sigmas; p.order = a->order;
@@ -347,8 +363,10 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     p.mu_uncond = a->mu_uncond; p.mu_cond = a->mu_cond; p.region_count = a->region_count;
     p.region_box = a->region_box; p.region_strength = a->region_strength; p.mu_region = a->mu_region;
     p.x_orig = a->x_orig; p.mask = a->mask;
-    const int block = pick_block(p.n_active, p.nvec);
-    p.tiles = (p.nvec + block - 1) / block;
+    const LaunchShape shape = pick_shape(p.n_active, p.nvec);
+    const int block = shape.block;
+    p.vpt = shape.vpt;
+    p.tiles = (int)(((int64_t)p.nvec + (int64_t)block * p.vpt - 1) / ((int64_t)block * p.vpt));
     if ((int64_t)p.n_active * p.tiles > INT32_MAX) return fail(BCG_ESHAPE, "guided_step: grid too large");
     hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -365,8 +383,13 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
         if (rc) return rc;
     }
     const bool heun = a->sampler == BCG_HEUN;
-    const hipError_t e = a->dtype == BCG_BF16 ? launch_step_bf16(p, vec, heun, inpaint, block, st)
-                                              : launch_step_f32(p, vec, heun, inpaint, block, st);
+    hipError_t e;
+    if (vec && a->cache_hint == BCG_CACHE_STREAM)
+        e = a->dtype == BCG_BF16 ? launch_step_bf16_stream(p, heun, inpaint, block, st)
+                                 : launch_step_f32_stream(p, heun, inpaint, block, st);
+    else
+        e = a->dtype == BCG_BF16 ? launch_step_bf16(p, vec, heun, inpaint, block, st)
+                                 : launch_step_f32(p, vec, heun, inpaint, block, st);
     return hip_status(e, "guided_step: launch");
 }
 

@@ -30,48 +30,75 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ __forceinline__ bf16_t to_bf16(float a) { return __builtin_bit_cast(bf16_t, (__bf16)a); }
 
-// V consecutive elements of storage type T as fp32.  V * sizeof(T) is 16
-// bytes on the vector path (one 128-bit access per lane) or one element.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Global load/store, optionally with the nontemporal (streaming) hint.
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void st(V* p, V v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// V consecutive elements of storage type T: one raw access (16 bytes on the
+// vector path, one element otherwise), unpacked to / packed from fp32.
 template <typename T, int V> struct Io;
 
 template <> struct Io<float, 1> {
+    typedef float Raw;
+    template <bool NT = false> __device__ static __forceinline__ Raw load_raw(const float* p) { return ld<NT>(p); }
+    __device__ static __forceinline__ void unpack(const Raw& r, float (&v)[1]) { v[0] = r; }
     __device__ static __forceinline__ void load(const float* p, float (&v)[1]) { v[0] = *p; }
-    __device__ static __forceinline__ void store(float* p, const float (&v)[1]) { *p = v[0]; }
+    template <bool NT = false> __device__ static __forceinline__ void store(float* p, const float (&v)[1]) { st<NT>(p, v[0]); }
 };
 template <> struct Io<float, 4> {
-    __device__ static __forceinline__ void load(const float* p, float (&v)[4]) {
-        const float4 q = *reinterpret_cast<const float4*>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    typedef f32x4_t Raw;
+    template <bool NT = false> __device__ static __forceinline__ Raw load_raw(const float* p) {
+        return ld<NT>(reinterpret_cast<const f32x4_t*>(p));
     }
-    __device__ static __forceinline__ void store(float* p, const float (&v)[4]) {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    __device__ static __forceinline__ void unpack(const Raw& r, float (&v)[4]) {
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    __device__ static __forceinline__ void load(const float* p, float (&v)[4]) { unpack(load_raw(p), v); }
+    template <bool NT = false> __device__ static __forceinline__ void store(float* p, const float (&v)[4]) {
+        const f32x4_t q = {v[0], v[1], v[2], v[3]};
+        st<NT>(reinterpret_cast<f32x4_t*>(p), q);
     }
 };
-template <> struct Io<float, 8> {
+template <> struct Io<float, 8> {  // the fp32 mask of a bf16 lane
     __device__ static __forceinline__ void load(const float* p, float (&v)[8]) {
-        const float4 q0 = reinterpret_cast<const float4*>(p)[0];
-        const float4 q1 = reinterpret_cast<const float4*>(p)[1];
+        const f32x4_t q0 = reinterpret_cast<const f32x4_t*>(p)[0];
+        const f32x4_t q1 = reinterpret_cast<const f32x4_t*>(p)[1];
         v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
         v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
     }
 };
 template <> struct Io<bf16_t, 1> {
-    __device__ static __forceinline__ void load(const bf16_t* p, float (&v)[1]) {
-        v[0] = __uint_as_float(uint32_t(*p) << 16);
-    }
-    __device__ static __forceinline__ void store(bf16_t* p, const float (&v)[1]) { *p = to_bf16(v[0]); }
+    typedef bf16_t Raw;
+    template <bool NT = false> __device__ static __forceinline__ Raw load_raw(const bf16_t* p) { return ld<NT>(p); }
+    __device__ static __forceinline__ void unpack(const Raw& r, float (&v)[1]) { v[0] = __uint_as_float(uint32_t(r) << 16); }
+    __device__ static __forceinline__ void load(const bf16_t* p, float (&v)[1]) { unpack(*p, v); }
+    template <bool NT = false> __device__ static __forceinline__ void store(bf16_t* p, const float (&v)[1]) { st<NT>(p, to_bf16(v[0])); }
 };
 template <> struct Io<bf16_t, 8> {
-    __device__ static __forceinline__ void load(const bf16_t* p, float (&v)[8]) {
-        const uint4 q = *reinterpret_cast<const uint4*>(p);
+    typedef u32x4_t Raw;
+    template <bool NT = false> __device__ static __forceinline__ Raw load_raw(const bf16_t* p) {
+        return ld<NT>(reinterpret_cast<const u32x4_t*>(p));
+    }
+    __device__ static __forceinline__ void unpack(const Raw& q, float (&v)[8]) {
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     }
-    __device__ static __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
-        uint4 q;
-        q.x = pack_bf16x2(v[0], v[1]); q.y = pack_bf16x2(v[2], v[3]);
-        q.z = pack_bf16x2(v[4], v[5]); q.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(p) = q;
+    __device__ static __forceinline__ void load(const bf16_t* p, float (&v)[8]) { unpack(load_raw(p), v); }
+    template <bool NT = false> __device__ static __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
+        const u32x4_t q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        st<NT>(reinterpret_cast<u32x4_t*>(p), q);
     }
 };
 
@@ -111,6 +138,8 @@ struct StepParams {
     int64_t HW;
     int nvec;                     // vectors of V pixels per sample
     int tiles;                    // blocks per sample
+    int vpt;                      // vectors per lane (blockDim apart)
+    int rows_aligned;             // W % V == 0: a lane's V pixels share a row
     int mask_stride;              // HW if per-sample mask, else 0
     float s2;
     const void* x;
@@ -130,11 +159,15 @@ struct StepParams {
     const float* mask;
 };
 
-// Per-launch launchers, one per storage dtype (bcg_step_f32.hip,
-// bcg_step_bf16.hip).  `vec` selects the 128-bit path.
+// Launchers, one per storage dtype and cache behaviour (bcg_step_*.hip).
+// `vec` selects the 128-bit path; the streaming launchers take only it.
 hipError_t launch_step_f32(const StepParams& p, bool vec, bool heun, bool inpaint, int block,
                            hipStream_t s);
 hipError_t launch_step_bf16(const StepParams& p, bool vec, bool heun, bool inpaint, int block,
                             hipStream_t s);
+hipError_t launch_step_f32_stream(const StepParams& p, bool heun, bool inpaint, int block,
+                                  hipStream_t s);
+hipError_t launch_step_bf16_stream(const StepParams& p, bool heun, bool inpaint, int block,
+                                   hipStream_t s);
 
 }  // namespace bcg

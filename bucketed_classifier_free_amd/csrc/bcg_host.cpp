@@ -28,7 +28,7 @@ using bcg::fail;
 
 extern "C" const char* bcg_last_error(void) { return bcg::g_err; }
 
-extern "C" int bcg_abi_version(void) { return 1; }
+extern "C" int bcg_abi_version(void) { return 2; }
 
 // "12 · Samplers, schedulers and CFG", sections "sigma sequence" and
 // "denoise below 1": the schedule runs from high to low noise and ends at 0;
@@ -102,20 +102,28 @@ void area_slice(const double* f, int H, int W, int32_t* box) {
     box[3] = int32_t(x0 + w);
 }
 
+// Sorted distinct values of a small array, in place; returns the count.
+int sort_unique(int* v, int m) {
+    std::sort(v, v + m);
+    return int(std::unique(v, v + m) - v);
+}
+
 // True when the union of the boxes covers [0,H) x [0,W).  Coordinate
 // compression over the box edges: every elementary cell is tested.
 bool covers(const int32_t (*boxes)[4], int k, int H, int W) {
     if (k == 0) return false;
-    std::vector<int> ys{0, H}, xs{0, W};
+    int ys[2 * BCG_MAX_REGIONS + 2] = {0, H}, xs[2 * BCG_MAX_REGIONS + 2] = {0, W};
+    int ny = 2, nx = 2;
     for (int r = 0; r < k; ++r) {
-        ys.push_back(boxes[r][0]); ys.push_back(boxes[r][1]);
-        xs.push_back(boxes[r][2]); xs.push_back(boxes[r][3]);
+        ys[ny++] = boxes[r][0]; ys[ny++] = boxes[r][1];
+        xs[nx++] = boxes[r][2]; xs[nx++] = boxes[r][3];
     }
-    std::sort(ys.begin(), ys.end()); ys.erase(std::unique(ys.begin(), ys.end()), ys.end());
-    std::sort(xs.begin(), xs.end()); xs.erase(std::unique(xs.begin(), xs.end()), xs.end());
-    for (size_t a = 0; a + 1 < ys.size(); ++a)
-        for (size_t b = 0; b + 1 < xs.size(); ++b) {
+    ny = sort_unique(ys, ny);
+    nx = sort_unique(xs, nx);
+    for (int a = 0; a + 1 < ny; ++a)
+        for (int b = 0; b + 1 < nx; ++b) {
             const int cy = ys[a], cx = xs[b];  // cell [ys[a], ys[a+1]) x [xs[b], xs[b+1])
+            if (cy < 0 || cy >= H || cx < 0 || cx >= W) continue;
             bool hit = false;
             for (int r = 0; r < k && !hit; ++r)
                 hit = boxes[r][0] <= cy && cy < boxes[r][1] && boxes[r][2] <= cx && cx < boxes[r][3];
@@ -144,7 +152,7 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
     if (!out->bucket_id || !out->scale || !out->uncond_row || !out->cond_row || !out->order ||
         !out->bucket_count || !out->bucket_offset || !out->uncond_offset)
         return fail(BCG_EINVAL, "bcg_plan_build: NULL output array");
-    const bool regions = R > 0 && in->region_count;
+    const bool regions = R > 0 && in->region_count && !in->covered;
     if (regions && (!in->region_frac || !in->region_strength))
         return fail(BCG_EINVAL, "bcg_plan_build: region_count given without region_frac/strength");
     for (int b = 0; b < nb; ++b)
@@ -169,11 +177,13 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
         }
     }
 
-    // Region boxes, crop offsets and per-sample coverage.
+    // Region boxes, crop offsets and per-sample coverage (unless given).
     std::vector<char> covered(size_t(n), 1);
+    if (in->covered)
+        for (int i = 0; i < n; ++i) covered[i] = in->covered[i] != 0;
     int64_t off = 0;
-    for (int i = 0; i < n; ++i) {
-        const int k = regions ? in->region_count[i] : 0;
+    for (int i = 0; regions && i < n; ++i) {
+        const int k = in->region_count[i];
         int32_t boxes[BCG_MAX_REGIONS][4] = {};
         int32_t live[BCG_MAX_REGIONS][4] = {};
         int nlive = 0;
@@ -190,7 +200,9 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
         }
         if (k > 0) covered[i] = covers(live, nlive, in->H, in->W);
     }
-    if (out->region_off && R > 0) out->region_off[size_t(n) * R] = off;
+    if (regions && out->region_off && R > 0) out->region_off[size_t(n) * R] = off;
+    if (out->covered_out)
+        for (int i = 0; i < n; ++i) out->covered_out[i] = covered[i] ? 1 : 0;
 
     // Buckets, scales and the skip decision.
     std::vector<char> need_u(size_t(n), 0);

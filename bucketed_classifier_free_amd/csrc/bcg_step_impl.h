@@ -12,12 +12,16 @@
 //
 // Design for gfx950 (bandwidth-bound, no contraction => no MFMA):
 //   * one workgroup = one sample x a tile of `blockDim` 128-bit pixel vectors;
-//     per-sample scalars come from uniform loads, per-channel branch offsets
-//     b_k[c] = sigma^2 mu_k[c] / (s2 + sigma^2) are computed once per
-//     workgroup into LDS and read back as broadcasts;
+//     per-sample scalars come from uniform (scalar) loads, the per-channel
+//     branch offsets b_k[c] = sigma^2 mu_k[c] / (s2 + sigma^2) are computed
+//     once per workgroup into LDS and read back as broadcasts;
 //   * each lane owns V consecutive pixels (16 bytes of storage) and computes
 //     their region weights, coverage, mask and normalisers once, then walks
-//     the C channels (stride H*W), 4 channels of loads in flight at a time;
+//     the C channels (stride H*W);
+//   * the first U channels are requested before the coefficient set-up (the
+//     LDS barrier waits on LDS traffic only), and the channel walk is
+//     software-pipelined: the loads of channels c+U.. are in flight while
+//     channels c.. are computed and stored;
 //   * every element is read once and written once (in place allowed);
 //   * per-sample modes (scale == 1, last step, sample without regions) are
 //     uniform branches taken outside the channel loop.
@@ -33,14 +37,24 @@
 
 namespace bcg {
 
-constexpr int kBranches = 2 + BCG_MAX_REGIONS;   // uncond, cond, regions
+constexpr int kBranches = 2 + BCG_MAX_REGIONS;      // uncond, cond, regions
 constexpr int kSet = kBranches * BCG_MAX_CHANNELS;  // one sigma's coefficients
+
+// Compile-time tuning of the streaming loop.
+template <int U_, bool NT_>
+struct Tune {
+    static constexpr int U = U_;     // channels per pipeline stage
+    static constexpr bool NT = NT_;  // nontemporal (streaming) loads and stores
+};
+typedef Tune<2, false> KeepTune;    // ordinary loads/stores (BCG_CACHE_KEEP)
+typedef Tune<2, true> StreamTune;   // nontemporal loads/stores (BCG_CACHE_STREAM)
+typedef KeepTune DefaultTune;
 
 // Per-sample scalars of one step.
 struct StepScalars {
-    float a, a2;      // s2/(s2 + sigma^2) at sigma and sigma'
-    float w;          // guidance scale
-    float q;          // Euler: (sigma' - sigma)/sigma
+    float a, a2;           // s2/(s2 + sigma^2) at sigma and sigma'
+    float w;               // guidance scale
+    float q;               // Euler: (sigma' - sigma)/sigma
     float h, is, isn, hh;  // Heun: sigma' - sigma, 1/sigma, 1/sigma', h*0.5
 };
 
@@ -79,7 +93,7 @@ __device__ __forceinline__ float guided_pred(const LaneState<V, NR>& L, int e, f
     return pred;
 }
 
-template <typename T, int V, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+template <int V, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
 __device__ __forceinline__ void update_vec(const LaneState<V, NR>& L, const StepScalars& s,
                                            const float* __restrict__ coef, int c,
                                            const float (&xv)[V], const float (&ov)[V],
@@ -115,60 +129,162 @@ __device__ __forceinline__ void update_vec(const LaneState<V, NR>& L, const Step
     }
 }
 
-template <typename T, int V, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
-__device__ __forceinline__ void channel_loop(const LaneState<V, NR>& L, const StepScalars& s,
-                                             const float* __restrict__ coef, const T* xs, T* xd,
-                                             const T* xo, int C, int64_t HW) {
-    constexpr int U = 4;  // channels of loads in flight per lane
-    int c = 0;
-    for (; c + U <= C; c += U) {
-        float xv[U][V], ov[U][V];
+// One pipeline stage: the raw vectors of U consecutive channels (x and, when
+// inpainting, the original latent).
+template <typename T, int V, int U, bool INP>
+struct Stage {
+    typename Io<T, V>::Raw x[U];
+    typename Io<T, V>::Raw o[INP ? U : 1];
+};
+
+template <typename T, int V, typename TN, bool INP>
+__device__ __forceinline__ void load_stage(Stage<T, V, TN::U, INP>& sg, const T* xs, const T* xo,
+                                           int c0, int C, int64_t HW) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            Io<T, V>::load(xs + (c + u) * HW, xv[u]);
-            if constexpr (INP) Io<T, V>::load(xo + (c + u) * HW, ov[u]);
-            else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) ov[u][e] = 0.f;
-            }
+    for (int u = 0; u < TN::U; ++u) {
+        if (c0 + u < C) {
+            sg.x[u] = Io<T, V>::template load_raw<TN::NT>(xs + (c0 + u) * HW);
+            if constexpr (INP) sg.o[u] = Io<T, V>::template load_raw<TN::NT>(xo + (c0 + u) * HW);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float out[V];
-            update_vec<T, V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c + u, xv[u], ov[u], out);
-            Io<T, V>::store(xd + (c + u) * HW, out);
-        }
-    }
-    for (; c < C; ++c) {
-        float xv[V], ov[V], out[V];
-        Io<T, V>::load(xs + c * HW, xv);
-        if constexpr (INP) Io<T, V>::load(xo + c * HW, ov);
-        else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) ov[e] = 0.f;
-        }
-        update_vec<T, V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c, xv, ov, out);
-        Io<T, V>::store(xd + c * HW, out);
     }
 }
 
-template <typename T, int V, int NR, int NRB, bool INP, bool HEUN>
-__device__ __forceinline__ void dispatch_modes(bool one, bool fin, const LaneState<V, NR>& L,
-                                               const StepScalars& s, const float* coef,
-                                               const T* xs, T* xd, const T* xo, int C, int64_t HW) {
+template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+__device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg, const LaneState<V, NR>& L,
+                                              const StepScalars& s, const float* __restrict__ coef,
+                                              T* xd, int c0, int C, int64_t HW) {
+#pragma unroll
+    for (int u = 0; u < TN::U; ++u) {
+        if (c0 + u < C) {
+            float xv[V], ov[V], out[V];
+            Io<T, V>::unpack(sg.x[u], xv);
+            if constexpr (INP) Io<T, V>::unpack(sg.o[u], ov);
+            else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) ov[e] = 0.f;
+            }
+            update_vec<V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c0 + u, xv, ov, out);
+            Io<T, V>::template store<TN::NT>(xd + (c0 + u) * HW, out);
+        }
+    }
+}
+
+// The channel walk, two stages in flight (ping-pong): stage `a` arrives
+// holding channels [0, U) already requested.
+template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+__device__ __forceinline__ void channel_loop(Stage<T, V, TN::U, INP>& a, const LaneState<V, NR>& L,
+                                             const StepScalars& s, const float* __restrict__ coef,
+                                             const T* xs, T* xd, const T* xo, int C, int64_t HW) {
+    constexpr int U = TN::U;
+    Stage<T, V, U, INP> b;
+    for (int c0 = 0;; c0 += 2 * U) {
+        if (c0 + U < C) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, C, HW);
+        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, C, HW);
+        if (c0 + U >= C) break;
+        if (c0 + 2 * U < C) load_stage<T, V, TN, INP>(a, xs, xo, c0 + 2 * U, C, HW);
+        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, xd, c0 + U, C, HW);
+        if (c0 + 2 * U >= C) break;
+    }
+}
+
+// Per-sample constants a lane needs to set up its pixels.
+template <int NR>
+struct SampleRegions {
+    RegionDesc rd[NR > 0 ? NR : 1];
+    int cnt;
+};
+
+// Region weights, coverage and mask of the V pixels starting at p0.
+template <int V, int NR, int NRB, bool INP>
+__device__ __forceinline__ void setup_lane(LaneState<V, NR>& L, const SampleRegions<NR>& sr,
+                                           const StepParams& p, int i, int64_t p0, float w,
+                                           bool keep_u) {
+    if constexpr (NRB > 0) {
+        const int F = p.feather;
+        const float inv_f4 = p.inv_f4;
+        const int y = (int)(p0 / p.W);
+        const int xx = (int)(p0 - (int64_t)y * p.W);
+        int ny[NRB];  // feather numerators of the lane's row (row-aligned lanes)
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+            const int dy = y - sr.rd[r].y0;
+            ny[r] = (dy >= 0 && dy < sr.rd[r].h) ? min(dy + 1, F) * min(sr.rd[r].h - dy, F) : 0;
+        }
+        const bool aligned = p.rows_aligned != 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            float ws[NRB];
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) {
+                if (aligned) {
+                    const int dx = xx + e - sr.rd[r].x0;
+                    const int nx = (dx >= 0 && dx < sr.rd[r].w) ? min(dx + 1, F) * min(sr.rd[r].w - dx, F) : 0;
+                    const float f = float(ny[r] * nx) * inv_f4;
+                    ws[r] = sr.rd[r].strength * f;
+                } else {
+                    const int px = xx + e;  // walk the row, wrapping to the next
+                    ws[r] = region_weight(sr.rd[r], y + px / p.W, px - (px / p.W) * p.W, F, inv_f4);
+                }
+            }
+            float wsum = ws[0];
+#pragma unroll
+            for (int r = 1; r < NRB; ++r) wsum = wsum + ws[r];
+            const bool cv = wsum > 0.0f;
+            const float iw = cv ? 1.0f / wsum : 0.0f;
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) L.wh[r][e] = ws[r] * iw;
+            L.weff[e] = cv ? w : 0.0f;
+            L.sel[e] = keep_u ? cv : true;
+        }
+    }
+    if constexpr (INP) {
+        Io<float, V>::load(p.mask + (int64_t)i * p.mask_stride + p0, L.m);
+#pragma unroll
+        for (int e = 0; e < V; ++e) L.om[e] = 1.0f - L.m[e];
+    }
+}
+
+// A lane's vectors vi0, vi0 + blockDim, ... (p.vpt of them) of one sample.
+template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+__device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, const SampleRegions<NR>& sr,
+                                         const StepParams& p, const StepScalars& s,
+                                         const float* __restrict__ coef, int i, int vi0,
+                                         bool keep_u) {
+    const int C = p.C;
+    const int64_t sbase = (int64_t)i * C * p.HW;
+    for (int v = 0; v < p.vpt; ++v) {
+        const int vi = vi0 + v * (int)blockDim.x;
+        if (vi >= p.nvec) return;
+        const int64_t p0 = (int64_t)vi * V;
+        const T* xs = static_cast<const T*>(p.x) + sbase + p0;
+        T* xd = static_cast<T*>(p.x_out) + sbase + p0;
+        const T* xo = INP ? static_cast<const T*>(p.x_orig) + sbase + p0 : nullptr;
+        if (v > 0) load_stage<T, V, TN, INP>(a, xs, xo, 0, C, p.HW);
+        LaneState<V, NR> L;
+        setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
+        channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xs, xd, xo, C, p.HW);
+    }
+}
+
+template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN>
+__device__ __forceinline__ void dispatch_modes(bool one, bool fin, Stage<T, V, TN::U, INP>& a,
+                                               const SampleRegions<NR>& sr, const StepParams& p,
+                                               const StepScalars& s, const float* coef, int i,
+                                               int vi0, bool keep_u) {
     if (one) {
-        if (fin) channel_loop<T, V, NR, NRB, INP, HEUN, true, true>(L, s, coef, xs, xd, xo, C, HW);
-        else channel_loop<T, V, NR, NRB, INP, HEUN, true, false>(L, s, coef, xs, xd, xo, C, HW);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, sr, p, s, coef, i, vi0, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, sr, p, s, coef, i, vi0, keep_u);
     } else {
-        if (fin) channel_loop<T, V, NR, NRB, INP, HEUN, false, true>(L, s, coef, xs, xd, xo, C, HW);
-        else channel_loop<T, V, NR, NRB, INP, HEUN, false, false>(L, s, coef, xs, xd, xo, C, HW);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, sr, p, s, coef, i, vi0, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, sr, p, s, coef, i, vi0, keep_u);
     }
 }
 
 // NR: regions evaluated per pixel (>= the sample's count; extra regions are
 // zero-weight padding).  V: pixels per lane (16 bytes, or 1 for shapes whose
-// H*W is not a multiple of the vector).
-template <typename T, int V, int NR, bool INP, bool HEUN>
+// H*W is not a multiple of the vector).  Each workgroup covers blockDim * vpt
+// vectors of one sample (vpt per lane, blockDim apart).
+template <typename T, int V, int NR, bool INP, bool HEUN, typename TN = DefaultTune>
 __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     __shared__ float coef[2 * kSet];
     const int j = blockIdx.x / p.tiles;
@@ -176,21 +292,32 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     if (j >= p.n_active) return;
     const int i = p.order[j];
     if (i < 0 || i >= p.n) return;
+    const int C = p.C;
     const int t = p.step_idx[i];
     if (t < 0 || t + 1 >= p.num_sigmas) return;
+
+    // Request the first stage as soon as the sample is known.
+    const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
+    const bool lane_ok = vi0 < p.nvec;
+    Stage<T, V, TN::U, INP> a;
+    if (lane_ok) {
+        const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
+        load_stage<T, V, TN, INP>(a, static_cast<const T*>(p.x) + base,
+                                  INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, C, p.HW);
+    }
 
     const float sig = p.sigmas[t];
     const float sgn = p.sigmas[t + 1];
     const float w = p.scale[i];
     const bool keep_u = p.uncond_row[i] >= 0;
-    int cnt = 0;
+    SampleRegions<NR> sr;
+    sr.cnt = 0;
     if constexpr (NR > 0) {
-        cnt = p.region_count[i];
+        int cnt = p.region_count[i];
         cnt = cnt < 0 ? 0 : cnt;
         cnt = cnt > p.R ? p.R : cnt;
-        cnt = cnt > NR ? NR : cnt;
+        sr.cnt = cnt > NR ? NR : cnt;
     }
-    const int C = p.C;
     const float s2 = p.s2;
     const float v = sig * sig;
     const float den = s2 + v;
@@ -209,16 +336,13 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const float mu_r = r < cnt ? p.mu_region[((int64_t)i * p.R + r) * C + k] : 0.0f;
+            const float mu_r = r < sr.cnt ? p.mu_region[((int64_t)i * p.R + r) * C + k] : 0.0f;
             coef[(2 + r) * BCG_MAX_CHANNELS + k] = (v * mu_r) / den;
             if constexpr (HEUN) coef[kSet + (2 + r) * BCG_MAX_CHANNELS + k] = (v2 * mu_r) / den2;
         }
     }
     __syncthreads();
-
-    const int vi = tile * (int)blockDim.x + (int)threadIdx.x;
-    if (vi >= p.nvec) return;
-    const int64_t p0 = (int64_t)vi * V;
+    if (!lane_ok) return;
 
     StepScalars s;
     s.a = s2 / den;
@@ -230,90 +354,66 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     s.isn = 1.0f / sgn;
     s.hh = s.h * 0.5f;
 
-    LaneState<V, NR> L;
     if constexpr (NR > 0) {
-        RegionDesc rd[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            if (r < cnt) {
+            if (r < sr.cnt) {
                 const int32_t* b = p.region_box + ((int64_t)i * p.R + r) * 4;
-                rd[r].y0 = b[0];
-                rd[r].h = b[1] - b[0];
-                rd[r].x0 = b[2];
-                rd[r].w = b[3] - b[2];
-                rd[r].strength = p.region_strength[(int64_t)i * p.R + r];
+                sr.rd[r].y0 = b[0];
+                sr.rd[r].h = b[1] - b[0];
+                sr.rd[r].x0 = b[2];
+                sr.rd[r].w = b[3] - b[2];
+                sr.rd[r].strength = p.region_strength[(int64_t)i * p.R + r];
             } else {
-                rd[r].y0 = rd[r].x0 = 0;
-                rd[r].h = rd[r].w = 0;
-                rd[r].strength = 0.0f;
+                sr.rd[r].y0 = sr.rd[r].x0 = 0;
+                sr.rd[r].h = sr.rd[r].w = 0;
+                sr.rd[r].strength = 0.0f;
             }
         }
-        int y = (int)(p0 / p.W);
-        int xx = (int)(p0 - (int64_t)y * p.W);
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            float ws[NR];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) ws[r] = region_weight(rd[r], y, xx, p.feather, p.inv_f4);
-            float wsum = ws[0];
-#pragma unroll
-            for (int r = 1; r < NR; ++r) wsum = wsum + ws[r];
-            const bool cv = wsum > 0.0f;
-            const float iw = cv ? 1.0f / wsum : 0.0f;
-#pragma unroll
-            for (int r = 0; r < NR; ++r) L.wh[r][e] = ws[r] * iw;
-            L.weff[e] = cv ? w : 0.0f;
-            L.sel[e] = keep_u ? cv : true;
-            if (++xx == p.W) { xx = 0; ++y; }
-        }
-    }
-    if constexpr (INP) {
-        Io<float, V>::load(p.mask + (int64_t)i * p.mask_stride + p0, L.m);
-#pragma unroll
-        for (int e = 0; e < V; ++e) L.om[e] = 1.0f - L.m[e];
     }
 
-    const int64_t base = (int64_t)i * C * p.HW + p0;
-    const T* xs = static_cast<const T*>(p.x) + base;
-    T* xd = static_cast<T*>(p.x_out) + base;
-    const T* xo = INP ? static_cast<const T*>(p.x_orig) + base : nullptr;
     const bool one = (w == 1.0f);
     const bool fin = (sgn == 0.0f);
-    if (NR > 0 && cnt > 0)
-        dispatch_modes<T, V, NR, NR, INP, HEUN>(one, fin, L, s, coef, xs, xd, xo, C, p.HW);
+    if (NR > 0 && sr.cnt > 0)
+        dispatch_modes<T, V, TN, NR, NR, INP, HEUN>(one, fin, a, sr, p, s, coef, i, vi0, keep_u);
     else
-        dispatch_modes<T, V, NR, 0, INP, HEUN>(one, fin, L, s, coef, xs, xd, xo, C, p.HW);
+        dispatch_modes<T, V, TN, NR, 0, INP, HEUN>(one, fin, a, sr, p, s, coef, i, vi0, keep_u);
 }
 
-template <typename T, int V, int NR>
+template <typename T, int V, int NR, typename TN = DefaultTune>
 hipError_t launch_nr(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles)), blk((unsigned)block);
     if (heun) {
-        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true>), grid, blk, 0, st, p);
+        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true, TN>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true, TN>), grid, blk, 0, st, p);
     } else {
-        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, false>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, false>), grid, blk, 0, st, p);
+        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, false, TN>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, false, TN>), grid, blk, 0, st, p);
     }
     return hipGetLastError();
 }
 
-template <typename T>
+// Launch of one storage type and tuning.  The scalar path (shapes the 128-bit
+// path cannot take) is instantiated only where SCALAR is set.
+template <typename T, typename TN, bool SCALAR>
 hipError_t launch_step(const StepParams& p, bool vec, bool heun, bool inp, int block, hipStream_t st) {
     if (p.n_active == 0) return hipSuccess;
     constexpr int VV = VecWidth<T>::value;
     if (!vec) {
-        // Scalar path for shapes the 128-bit path cannot take; regions run
-        // with the maximum count (extra regions are zero-weight padding).
-        if (p.R > 0) return launch_nr<T, 1, BCG_MAX_REGIONS>(p, heun, inp, block, st);
-        return launch_nr<T, 1, 0>(p, heun, inp, block, st);
+        if constexpr (SCALAR) {
+            // regions run with the maximum count (extra regions are zero-weight padding)
+            if (p.R > 0) return launch_nr<T, 1, BCG_MAX_REGIONS, TN>(p, heun, inp, block, st);
+            return launch_nr<T, 1, 0, TN>(p, heun, inp, block, st);
+        } else {
+            return hipErrorInvalidValue;
+        }
     }
     switch (p.R) {
-        case 0: return launch_nr<T, VV, 0>(p, heun, inp, block, st);
-        case 1: return launch_nr<T, VV, 1>(p, heun, inp, block, st);
-        case 2: return launch_nr<T, VV, 2>(p, heun, inp, block, st);
-        case 3: return launch_nr<T, VV, 3>(p, heun, inp, block, st);
-        default: return launch_nr<T, VV, 4>(p, heun, inp, block, st);
+        case 0: return launch_nr<T, VV, 0, TN>(p, heun, inp, block, st);
+        case 1: return launch_nr<T, VV, 1, TN>(p, heun, inp, block, st);
+        case 2: return launch_nr<T, VV, 2, TN>(p, heun, inp, block, st);
+        case 3: return launch_nr<T, VV, 3, TN>(p, heun, inp, block, st);
+        default: return launch_nr<T, VV, 4, TN>(p, heun, inp, block, st);
     }
 }
 

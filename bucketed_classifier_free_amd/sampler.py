@@ -75,9 +75,12 @@ class GuidedSampler:
         self.d_slab = torch.empty((self.steps, 4 * n), dtype=torch.int32, device=dev)
         self._row_ev = [None] * self.steps
         self._tmp = api.plan_out_arrays(n, self.nb, R)
-        # Region boxes do not change between steps: one plan gives them.
+        # Region boxes and coverage do not change between steps: one full plan
+        # gives them, later plans reuse the coverage flags.
+        self.covered = None
         if R > 0:
             p = self._plan(np.zeros(n, np.int32), self._tmp)
+            self.covered = p.covered.astype(np.uint8)
             self.d_region_box = torch.from_numpy(p.region_box.copy()).to(dev)
             self.d_region_count = torch.from_numpy(self.region_count).to(dev)
             self.d_region_strength = f32(self.region_strength)
@@ -105,11 +108,12 @@ class GuidedSampler:
     # ------------------------------------------------------------ host plan
 
     def _plan(self, t, out):
+        cov = getattr(self, "covered", None)
         return api.bcg_plan_build(t, self.steps, self.table, C=self.C, H=self.H, W=self.W,
                                   cfg_override=self.override, region_count=self.region_count,
                                   region_frac=self.region_frac,
                                   region_strength=self.region_strength, max_regions=self.R,
-                                  out=out)
+                                  covered=cov, out=out)
 
     def step_indices(self, k: int) -> np.ndarray:
         t = self.start.astype(np.int64) + k
@@ -153,7 +157,7 @@ class GuidedSampler:
         self._row_ev[row].record()
         return p, d
 
-    def launch(self, d, n_active, x, x_out=None, stats=None, workspace=None):
+    def launch(self, d, n_active, x, x_out=None, stats=None, workspace=None, cache_hint=0):
         n = self.n
         api.guided_step(x, x if x_out is None else x_out, self.d_sigmas, d[3 * n:4 * n], d[:n],
                         d[n:2 * n].view(torch.float32), d[2 * n:3 * n], self.d_mu_u, self.d_mu_c,
@@ -161,12 +165,12 @@ class GuidedSampler:
                         feather=self.feather, region_count=self.d_region_count,
                         region_box=self.d_region_box, region_strength=self.d_region_strength,
                         mu_region=self.d_mu_region, x_orig=self.d_x_orig, mask=self.d_mask,
-                        stats=stats, workspace=workspace)
+                        stats=stats, workspace=workspace, cache_hint=cache_hint)
 
-    def step(self, k: int, x, x_out=None, stats=None, workspace=None):
+    def step(self, k: int, x, x_out=None, stats=None, workspace=None, cache_hint=0):
         """Launch k of the loop: plan, upload, one fused guided step."""
         p, d = self.upload_plan(k)
-        self.launch(d, p.n_active, x, x_out, stats, workspace)
+        self.launch(d, p.n_active, x, x_out, stats, workspace, cache_hint)
         return p
 
     def run(self, x=None, launches=None, callback=None, cancel=None):
@@ -187,20 +191,23 @@ class GuidedSampler:
 
     # ------------------------------------------------------------ native loop
 
-    def native_loop(self, x, x_out=None, rows=None):
+    def native_loop(self, x, x_out=None, upload_batch=8, async_upload=False, cache_hint=None,
+                    timing_every=1):
         """A C++ loop (bcg_loop_*) advancing ``x`` (in place unless x_out).
 
         ``x`` may also be [replicas, n, C, H, W]: launch k then advances
         replica k mod replicas (independent batches served round-robin)."""
-        return NativeLoop(self, x, x_out, rows)
+        return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint, timing_every)
 
 
 class NativeLoop:
     """Owner of a bcg_loop handle and of the host/device arrays it points to."""
 
-    def __init__(self, s: GuidedSampler, x, x_out=None, rows=None):
+    def __init__(self, s: GuidedSampler, x, x_out=None, upload_batch=8, async_upload=False,
+                 cache_hint=None, timing_every=1):
         n = s.n
-        rows = int(rows or s.steps)
+        P = int(upload_batch)
+        rows = 8 * P
         self.s = s
         self.x, self.x_out = x, (x if x_out is None else x_out)
         reps = x.shape[0] if x.dim() == 5 else 1
@@ -208,6 +215,8 @@ class NativeLoop:
         api._dev(x, "x", s.tdtype, shape)
         api._dev(self.x_out, "x_out", s.tdtype, shape)
         stride = n * s.C * s.H * s.W * x.element_size()
+        if cache_hint is None:  # several batches in rotation: stream them past the caches
+            cache_hint = L.BCG_CACHE_STREAM if reps > 1 else L.BCG_CACHE_KEEP
         self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
         self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
         keep = self._keep = []
@@ -222,24 +231,28 @@ class NativeLoop:
         R = s.R
         plan = L.PlanIn(n, s.steps, s.nb, s.C, s.H, s.W, R, npp(s.table, np.float32), None,
                         npp(s.override, np.float32), npp(s.region_count, np.int32),
-                        npp(s.region_frac, np.float64), npp(s.region_strength, np.float32))
+                        npp(s.region_frac, np.float64), npp(s.region_strength, np.float32),
+                        npp(s.covered, np.uint8))
         ptr = api._ptr
         step = L.StepArgs(n, s.C, s.H, s.W, api._DT[s.tdtype], api._SAMPLER[s.sampler], R,
                           s.feather, 0, s.d_sigmas.numel(),
-                          1 if s.d_mask is not None and s.d_mask.shape[0] == n else 0, s.s2,
+                          1 if s.d_mask is not None and s.d_mask.shape[0] == n else 0,
+                          int(cache_hint), s.s2,
                           ptr(self.x), ptr(self.x_out), ptr(s.d_sigmas), None, None, None, None,
                           ptr(s.d_mu_u), ptr(s.d_mu_c), ptr(s.d_region_count),
                           ptr(s.d_region_box), ptr(s.d_region_strength), ptr(s.d_mu_region),
                           ptr(s.d_x_orig), ptr(s.d_mask), None, None, 0)
         self.desc = L.LoopDesc(plan, npp(s.start, np.int32), 1 if s.wrap else 0, rows,
                                self.h_slab.data_ptr(), self.d_slab.data_ptr(), reps,
-                               stride if reps > 1 else 0, step)
+                               stride if reps > 1 else 0, P, 1 if async_upload else 0,
+                               int(timing_every), step)
         self.handle = ct.c_void_p()
         L.check(L.lib().bcg_loop_create(ct.byref(self.desc), ct.byref(self.handle)))
 
     def run(self, k0: int, count: int, timing: bool = False):
         """Launches k0 .. k0+count-1 on the current stream; with ``timing`` the
-        summed guided_step durations (ms, HIP events) are returned."""
+        mean guided_step duration (ms, HIP events around every timing_every-th
+        launch) is returned."""
         ms = ct.c_float(0.0)
         L.check(L.lib().bcg_loop_run(self.handle, int(k0), int(count),
                                      torch.cuda.current_stream().cuda_stream,

@@ -44,6 +44,14 @@ enum { BCG_F32 = 0, BCG_BF16 = 1 };
 enum { BCG_EULER = 0, BCG_HEUN = 1 };
 enum { BCG_SCHED_LOGLINEAR = 0 };
 enum { BCG_CURVE_CONST = 0, BCG_CURVE_LINEAR = 1, BCG_CURVE_FRONT_HIGH = 2 };
+/* Cache behaviour of the latent streams of guided_step:
+ *   BCG_CACHE_KEEP    ordinary loads/stores: the state is expected back soon
+ *                     (one batch advanced in place; the 256 MB last-level cache
+ *                     can hold it between steps)
+ *   BCG_CACHE_STREAM  nontemporal loads/stores: the state will not be read
+ *                     again before the caches turn over (several batches served
+ *                     round-robin, each larger than the cache) */
+enum { BCG_CACHE_KEEP = 0, BCG_CACHE_STREAM = 1 };
 
 #define BCG_MAX_REGIONS 4    /* regional conds per sample */
 #define BCG_MAX_CHANNELS 64  /* latent channels */
@@ -107,7 +115,9 @@ int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
  *   h = clamp(floor(fh*H + 0.5), 1, H); y0 = clamp(floor(fy*H + 0.5), 0, H-h);
  *   same for x.  region_off[i*R + r] is the element offset of region r's
  *   packed [C,h,w] crop (size 0 for r >= region_count[i]); region_off[n*R] is
- *   the total.
+ *   the total.  Boxes and coverage depend only on the conds, not on the step:
+ *   a sampler computes them once (covered_out) and passes them back as
+ *   `covered` on every step, which leaves only the O(n) bucket work per step.
  */
 typedef struct {
     int32_t n;                       /* samples, >= 0 */
@@ -121,6 +131,10 @@ typedef struct {
     const int32_t* region_count;     /* [n] in [0, R], or NULL (all 0) */
     const double* region_frac;       /* [n][R][4] (fy,fx,fh,fw), or NULL if R == 0 */
     const float* region_strength;    /* [n][R]: 0 or in [1e-30, 1e30], or NULL if R == 0 */
+    const uint8_t* covered;          /* [n] or NULL: precomputed coverage flags (1 = the
+                                        sample's conds cover the frame), e.g. from an
+                                        earlier call's covered_out; when given, region
+                                        arrays are not read and region outputs not written */
 } bcg_plan_in;
 
 typedef struct {
@@ -134,6 +148,7 @@ typedef struct {
     int32_t* uncond_offset;          /* [num_buckets+1] exclusive prefix, uncond half */
     int32_t* region_box;             /* [n][R][4] or NULL */
     int64_t* region_off;             /* [n*R+1] or NULL */
+    uint8_t* covered_out;            /* [n] or NULL: coverage flags used for the skip */
     int32_t n_active;                /* out */
     int32_t n_uncond;                /* out */
 } bcg_plan_out;
@@ -182,6 +197,7 @@ typedef struct {
     int32_t n_active;                /* entries of order[] to process, [0, n] */
     int32_t num_sigmas;              /* length of sigmas */
     int32_t mask_per_sample;         /* 1: mask [n,1,H,W]; 0: [1,1,H,W] */
+    int32_t cache_hint;              /* BCG_CACHE_KEEP | BCG_CACHE_STREAM */
     float s2;                        /* stand-in data variance, > 0 */
     const void* x;                   /* device [n,C,H,W] */
     void* x_out;                     /* device [n,C,H,W] */
@@ -253,8 +269,10 @@ int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void*
  * launches k = k0 .. k0+count-1, t_i = start[i] + k (mod steps when wrap is
  * set: steady-state continuous batching, every sample always active), the
  * bucket plan is built (bcg_plan_build) straight into pinned staging row
- * k mod rows, copied to the device row on `stream` (hipMemcpyAsync) and one
- * guided_step is launched with that row.  SGLang BCG write-up, section 4
+ * k mod rows, copied to the device row (hipMemcpyAsync, P rows per copy) and
+ * one guided_step is launched with that row.  Every plan is built on the host
+ * before its launch is queued; batching only merges the copies (a plan
+ * depends on the step index, never on the state).  SGLang BCG write-up, section 4
  * stage 3: the plan is built by the scheduler before the launch and is
  * immutable while the step runs.  A staging row is rewritten only after its
  * previous copy has completed (an event per row).
@@ -266,9 +284,10 @@ int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void*
  * step.order / step_idx / scale / uncond_row / n_active are ignored (filled
  * per launch).  With replicas > 1, launch k advances replica k mod replicas:
  * step.x and step.x_out are offset by (k mod replicas) * replica_stride bytes
- * (several independent batches served round-robin).  If kernel_ms is not NULL, each guided_step launch is
- * bracketed by HIP events on `stream`, bcg_loop_run waits for the last one,
- * and *kernel_ms receives the summed launch durations.
+ * (several independent batches served round-robin).  If kernel_ms is not
+ * NULL, every timing_every-th guided_step launch is bracketed by HIP events
+ * on `stream`, bcg_loop_run waits for the last one, and *kernel_ms receives
+ * the mean duration of the bracketed launches (ms).
  * Errors: as bcg_plan_build and guided_step; BCG_EHIP for runtime failures.
  */
 typedef struct {
@@ -280,6 +299,13 @@ typedef struct {
     int32_t* dev_slab;               /* device [rows][4n] */
     int32_t replicas;                /* >= 1 independent states of the batch */
     int64_t replica_stride;          /* bytes between replicas of x and x_out */
+    int32_t upload_batch;            /* P in [1, 64]: plans of P consecutive launches are
+                                        built, then uploaded with one copy; rows must
+                                        be a multiple of P */
+    int32_t async_upload;            /* 1: uploads on the loop's own copy stream,
+                                        overlapping earlier launches; 0: on `stream` */
+    int32_t timing_every;            /* m >= 1: with kernel_ms, launches j with
+                                        j % m == 0 are bracketed by events */
     bcg_step_args step;              /* launch template (replica 0) */
 } bcg_loop_desc;
 

@@ -156,6 +156,12 @@ def test_small_shapes_full_trajectory(shape, kw):
     _check_full(W.make_inputs(sp), list(range(n)))
 
 
+def test_many_samples_multi_vector_lanes():
+    # enough samples that each lane takes several vectors, with a ragged last tile
+    sp = W.small_spec(n=700, C=1, H=40, W=64, steps=3, regions=2, inpaint=True, feather=4)
+    _check_full(W.make_inputs(sp), list(range(0, 700, 7)))
+
+
 def test_region_edge_cases():
     sp = W.small_spec(n=5, C=3, H=16, W=24, regions=3, steps=4, skip_frac=0.0, mixed_start=False,
                       curve=W.Curve("const", 1.0), num_buckets=1, feather=4)
@@ -199,6 +205,51 @@ def test_in_place_equals_out_of_place_and_deterministic():
     s.step(1, c)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("kw", [dict(dtype="bf16", regions=2), dict(dtype="f32", inpaint=True, regions=3, sampler="heun")])
+def test_streaming_cache_hint_is_bit_identical(kw):
+    inp = W.make_inputs(W.small_spec(n=4, C=4, H=32, W=32, **kw))
+    s = _sampler(inp)
+    x0 = s.init_state()
+    a = torch.empty_like(x0); b = torch.empty_like(x0)
+    s.step(1, x0, a, cache_hint=0)
+    s.step(1, x0, b, cache_hint=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("upload_batch,async_upload", [(1, False), (3, False), (8, True), (2, True)])
+def test_native_loop_matches_python_loop(upload_batch, async_upload):
+    inp = W.make_inputs(W.small_spec(n=5, C=3, H=16, W=24, regions=2, inpaint=True, steps=7,
+                                     sampler="heun", dtype="bf16"))
+    ref, _ = gpu_trajectory(_sampler(inp))
+    s = _sampler(inp)
+    x = s.init_state()
+    loop = s.native_loop(x, upload_batch=upload_batch, async_upload=async_upload)
+    loop.run(0, 3)
+    ms = loop.run(3, 4, timing=True)
+    torch.cuda.synchronize()
+    loop.close()
+    assert ms > 0
+    assert np.array_equal(to_np(x), ref)
+
+
+def test_native_loop_replicas_round_robin():
+    inp = W.make_inputs(W.small_spec(n=3, C=2, H=8, W=16, regions=1, steps=6))
+    s = _sampler(inp)
+    x = torch.stack([s.init_state(), s.init_state()])
+    loop = s.native_loop(x, upload_batch=2)
+    loop.run(0, 6)
+    torch.cuda.synchronize()
+    loop.close()
+    s2 = _sampler(inp)
+    for r in range(2):
+        y = s2.init_state()
+        for k in range(r, 6, 2):
+            s2.step(k, y)
+        torch.cuda.synchronize()
+        assert torch.equal(x[r], y)
 
 
 def test_batch_permutation_permutes_outputs():

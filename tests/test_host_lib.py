@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == 1
+    assert lib.bcg_abi_version() == 2
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -188,3 +188,21 @@ def test_device_entry_points_validate_before_launch():
     assert lib.area_accumulate(1, 1, 1, 1, 0, 0, None, 0, None, None, None, None, None, None,
                                None, None) == L.BCG_EINVAL
     assert lib.guided_step_workspace_size(4, 16, 128, 128, 1) == 4 * 16 * 128 * 3 * 4
+
+
+def test_plan_with_cached_coverage_equals_full_plan():
+    inp = W.make_inputs(W.config("regional_inpaint"))
+    sp = inp.spec
+    table = bcg.bucket_table("linear", 2.0, 1.2, 0, sp.num_buckets)
+    ov = inp.cfg_override.copy()
+    ov[::3] = 1.0
+    full = bcg.bcg_plan_build(inp.start_step + 3, sp.steps, table, C=sp.C, H=sp.H, W=sp.W,
+                              cfg_override=ov, region_count=inp.region_count,
+                              region_frac=inp.region_frac, region_strength=inp.region_strength,
+                              max_regions=sp.regions)
+    fast = bcg.bcg_plan_build(inp.start_step + 3, sp.steps, table, C=sp.C, H=sp.H, W=sp.W,
+                              cfg_override=ov, max_regions=sp.regions, covered=full.covered)
+    for k in ("bucket_id", "scale", "uncond_row", "cond_row", "order", "bucket_offset",
+              "uncond_offset", "covered"):
+        assert np.array_equal(getattr(full, k), getattr(fast, k)), k
+    assert fast.n_active == full.n_active and fast.n_uncond == full.n_uncond
