@@ -106,12 +106,12 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const StepParams p, flo
     for (int x = lane; x < p.W; x += 64) {
         float xv[1];
         Io<T, 1>::load(xs + x, xv);
-        const float ax = a * xv[0];
-        const float u = ax + bu;
+        const float xx = xv[0];
+        const float u = __builtin_fmaf(a, xx, bu);
         float cc, pred;
         if (cnt == 0) {
-            cc = ax + bc;
-            pred = (w == 1.0f) ? cc : u + w * (cc - u);
+            cc = __builtin_fmaf(a, xx, bc);
+            pred = (w == 1.0f) ? cc : __builtin_fmaf(w, cc - u, u);
         } else {
             float ws[BCG_MAX_REGIONS];
             float wsum = 0.f;
@@ -121,10 +121,10 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const StepParams p, flo
             }
             const bool cv = wsum > 0.0f;
             const float iw = cv ? 1.0f / wsum : 0.0f;
-            cc = (ws[0] * iw) * (ax + br[0]);
-            for (int r = 1; r < cnt; ++r) cc = cc + (ws[r] * iw) * (ax + br[r]);
+            cc = (ws[0] * iw) * __builtin_fmaf(a, xx, br[0]);
+            for (int r = 1; r < cnt; ++r) cc = __builtin_fmaf(ws[r] * iw, __builtin_fmaf(a, xx, br[r]), cc);
             if (w == 1.0f) pred = (keep_u ? cv : true) ? cc : u;
-            else pred = u + (cv ? w : 0.0f) * (cc - u);
+            else pred = __builtin_fmaf(cv ? w : 0.0f, cc - u, u);
             if (!cv) cc = u;  // the cond prediction where no region has weight
         }
         sc += cc * cc;
@@ -193,8 +193,7 @@ __global__ __launch_bounds__(256) void latent_init_kernel(int n, int C, int64_t 
         if (latent) Io<T, V>::load(latent + e0, lt);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-            const float z = nz[e] * sg;
-            o[e] = latent ? lt[e] + z : z;
+            o[e] = latent ? __builtin_fmaf(nz[e], sg, lt[e]) : nz[e] * sg;
         }
         Io<T, V>::store(out + e0, o);
     }
@@ -221,7 +220,7 @@ __global__ __launch_bounds__(256) void mask_blend_kernel(int n, int C, int64_t H
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             const float om = 1.0f - m[e];
-            o[e] = m[e] * av[e] + om * bv[e];
+            o[e] = __builtin_fmaf(m[e], av[e], om * bv[e]);
         }
         Io<T, V>::store(out + e0, o);
     }
@@ -281,8 +280,7 @@ __global__ __launch_bounds__(256) void area_accumulate_kernel(
         for (int r = 0; r < cnt; ++r) {
             if (!in[r]) continue;
             const float v = pred[off[r] + ((int64_t)c * rd[r].h + (y - rd[r].y0)) * rd[r].w + (x - rd[r].x0)];
-            const float term = wh[r] * v;
-            acc = started ? acc + term : term;
+            acc = started ? __builtin_fmaf(wh[r], v, acc) : wh[r] * v;
             started = true;
         }
         const int64_t q = ((int64_t)i * C + c) * HW + p;

@@ -25,12 +25,14 @@
 //   * every element is read once and written once (in place allowed);
 //   * per-sample modes (scale == 1, last step, sample without regions) are
 //     uniform branches taken outside the channel loop.
-// Evaluation order (fp32, contraction off), identical for every path:
-//   ax = a*x; u = ax + bu; c = ax + bc  |  c = sum_r wh_r*(ax + br_r)
-//   pred = u + w*(c - u) | u + weff*(c - u) | c | (sel ? c : u)
-//   pred = m*pred + (1-m)*xo;  Euler x' = x + (x - pred)*q
-//   Heun d = (x - pred)*is; xt = x + h*d; d2 = (xt - pred(xt))*isn;
-//        x' = x + (d + d2)*hh;  last step x' = pred.
+// Evaluation order (fp32; contraction off, so the only fused operations are
+// the explicit fma(a, b, c) = a*b + c rounded once), identical for every path:
+//   u = fma(a, x, bu);  c = fma(a, x, bc)  |  c = wh_0*t_0, c = fma(wh_r, t_r, c)
+//                                              with t_r = fma(a, x, br_r)
+//   pred = fma(w, c - u, u) | fma(weff, c - u, u) | c | (sel ? c : u)
+//   pred = fma(m, pred, (1-m)*xo);  Euler x' = fma(x - pred, q, x)
+//   Heun d = (x - pred)*is; xt = fma(h, d, x); d2 = (xt - pred(xt))*isn;
+//        x' = fma(d + d2, hh, x);  last step x' = pred.
 #pragma once
 
 #include "bcg_device.h"
@@ -71,25 +73,24 @@ template <int V, int NR, int NRB, bool INP, bool ONE>
 __device__ __forceinline__ float guided_pred(const LaneState<V, NR>& L, int e, float x, float xo,
                                              float a, float w, float bu, float bc,
                                              const float (&br)[NRB > 0 ? NRB : 1]) {
-    const float ax = a * x;
-    const float u = ax + bu;
+    const float u = __builtin_fmaf(a, x, bu);
     float c;
     if constexpr (NRB == 0) {
-        c = ax + bc;
+        c = __builtin_fmaf(a, x, bc);
     } else {
-        c = L.wh[0][e] * (ax + br[0]);
+        c = L.wh[0][e] * __builtin_fmaf(a, x, br[0]);
 #pragma unroll
-        for (int r = 1; r < NRB; ++r) c = c + L.wh[r][e] * (ax + br[r]);
+        for (int r = 1; r < NRB; ++r) c = __builtin_fmaf(L.wh[r][e], __builtin_fmaf(a, x, br[r]), c);
     }
     float pred;
     if constexpr (!ONE) {
-        if constexpr (NRB == 0) pred = u + w * (c - u);
-        else pred = u + L.weff[e] * (c - u);
+        if constexpr (NRB == 0) pred = __builtin_fmaf(w, c - u, u);
+        else pred = __builtin_fmaf(L.weff[e], c - u, u);
     } else {
         if constexpr (NRB == 0) pred = c;
         else pred = L.sel[e] ? c : u;
     }
-    if constexpr (INP) pred = L.m[e] * pred + L.om[e] * xo;
+    if constexpr (INP) pred = __builtin_fmaf(L.m[e], pred, L.om[e] * xo);
     return pred;
 }
 
@@ -118,13 +119,13 @@ __device__ __forceinline__ void update_vec(const LaneState<V, NR>& L, const Step
         if constexpr (FINAL) {
             out[e] = pb;
         } else if constexpr (!HEUN) {
-            out[e] = x + (x - pb) * s.q;
+            out[e] = __builtin_fmaf(x - pb, s.q, x);
         } else {
             const float d = (x - pb) * s.is;
-            const float xt = x + s.h * d;
+            const float xt = __builtin_fmaf(s.h, d, x);
             const float pb2 = guided_pred<V, NR, NRB, INP, ONE>(L, e, xt, ov[e], s.a2, s.w, bu2, bc2, br2);
             const float d2 = (xt - pb2) * s.isn;
-            out[e] = x + (d + d2) * s.hh;
+            out[e] = __builtin_fmaf(d + d2, s.hh, x);
         }
     }
 }

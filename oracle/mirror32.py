@@ -7,8 +7,9 @@ significand code chosen from a float32 result.  For |x| >= 4 one bf16 ulp is
 0.03125, above the 2e-2 final-latent bound, so the expected code has to be
 decided in the same precision and order as the device decides it: every
 operation below is one correctly rounded float32 operation (numpy float32
-arithmetic; no fused multiply-add; division correctly rounded), evaluated in
-the order written.  Mode M is pinned to mode D (``definition``) by the
+arithmetic; division correctly rounded; fma(a, b, c) is IEEE 754
+fusedMultiplyAdd, a*b + c rounded once, emulated exactly by ``fma32``),
+evaluated in the order written.  Mode M is pinned to mode D (``definition``) by the
 per-step tolerance and to the exact special cases (scale 0 -> uncond, scale 1
 -> cond, mask 0 -> original latent, ...).
 
@@ -26,18 +27,19 @@ per pixel (regional launches):
     covered = W > 0; iW = 1/W (0 if not covered); wh_r = w_r*iW
     inpaint: om = 1 - m
 per element:
-    ax = a*x; u = ax + bu[c]
-    c  = ax + bc[c]                                (no regions)
-       = ((wh_0*(ax + br_0[c])) + wh_1*(ax + br_1[c])) + ...   (regions)
-    pred = u + w*(c - u)                     (scale != 1, no regions)
-         = u + (covered ? w : 0)*(c - u)     (scale != 1, regions)
+    u  = fma(a, x, bu[c])
+    c  = fma(a, x, bc[c])                          (no regions)
+       = fma(wh_1, fma(a, x, br_1[c]), wh_0*fma(a, x, br_0[c])) ...   (regions:
+         c = wh_0*t_0, then c = fma(wh_r, t_r, c) for r = 1, 2, ...)
+    pred = fma(w, c - u, u)                  (scale != 1, no regions)
+         = fma(covered ? w : 0, c - u, u)    (scale != 1, regions)
          = covered ? c : u                   (scale == 1, uncond kept)
          = c                                 (uncond skipped)
-    pb = m*pred + om*xo  (inpaint)  else pred
+    pb = fma(m, pred, om*xo)  (inpaint)  else pred
     sigma' == 0: x' = pb
-    Euler: x' = x + (x - pb)*q
-    Heun:  d = (x - pb)*i; xt = x + h*d; pb2 = P'(xt);
-           d2 = (xt - pb2)*i'; x' = x + (d + d2)*hh
+    Euler: x' = fma(x - pb, q, x)
+    Heun:  d = (x - pb)*i; xt = fma(h, d, x); pb2 = P'(xt);
+           d2 = (xt - pb2)*i'; x' = fma(d + d2, hh, x)
     store float32, or round to bf16 (nearest, ties to even)
 """
 from __future__ import annotations
@@ -47,6 +49,32 @@ import numpy as np
 from . import definition as D
 
 f32 = np.float32
+
+
+def fma32(a, b, c):
+    """IEEE 754 float32 fusedMultiplyAdd: a*b + c rounded once (to nearest even).
+
+    float64 holds a*b exactly (24 + 24 significant bits).  The sum s = a*b + c
+    in float64 is rounded once; TwoSum gives its exact error e.  Turning s
+    into the round-to-odd value (if e != 0 and the last bit of s is even, step
+    one ulp towards the exact sum) and then rounding to float32 yields the
+    correctly rounded float32 sum, because float64 carries at least 24 + 2
+    bits (Boldo and Melquiond, "Emulation of FMA and correctly rounded sums:
+    proved algorithms using rounding to odd", IEEE Trans. Computers 2008).
+    """
+    a = np.asarray(a, np.float32).astype(np.float64)
+    b = np.asarray(b, np.float32).astype(np.float64)
+    c = np.asarray(c, np.float32).astype(np.float64)
+    p = a * b
+    s = p + c
+    bv = s - p
+    e = (p - (s - bv)) + (c - bv)
+    s = np.asarray(s, np.float64)
+    odd = (s.view(np.int64) & 1) == 1
+    fix = (e != 0) & ~odd
+    toward = np.where(e > 0, np.inf, -np.inf)
+    s = np.where(fix, np.nextafter(s, toward), s)
+    return s.astype(np.float32)
 
 
 def _store(x, dtype):
@@ -110,29 +138,28 @@ def _coef(sigma, prm):
 
 def _pred(x, sigma, w, mode, prm):
     a, bu, bc, br = _coef(sigma, prm)
-    ax = a * x
-    u = ax + bu[:, None, None]
+    u = fma32(a, x, bu[:, None, None])
     if prm.nr == 0:
-        c = ax + bc[:, None, None]
+        c = fma32(a, x, bc[:, None, None])
     else:
-        c = prm.wh[0][None] * (ax + br[0][:, None, None])
+        c = prm.wh[0][None] * fma32(a, x, br[0][:, None, None])
         for r in range(1, prm.nr):
-            c = c + prm.wh[r][None] * (ax + br[r][:, None, None])
+            c = fma32(prm.wh[r][None], fma32(a, x, br[r][:, None, None]), c)
     if mode == "C":
         pred = c
     elif mode == "B":
         pred = c if prm.nr == 0 else np.where(prm.covered[None], c, u)
     else:
         if prm.nr == 0:
-            pred = u + w * (c - u)
+            pred = fma32(w, c - u, u)
         else:
             weff = np.where(prm.covered, w, f32(0)).astype(np.float32)
-            pred = u + weff[None] * (c - u)
+            pred = fma32(weff[None], c - u, u)
     if prm.mask is not None:
         m = prm.mask[None]
         om = f32(1) - m
-        pred = m * pred + om * prm.x_orig
-    return pred.astype(np.float32)
+        pred = fma32(m, pred, om * prm.x_orig)
+    return np.asarray(pred, np.float32)
 
 
 def step32(x, sigma, sigma_next, w, need_uncond, prm, sampler):
@@ -145,16 +172,16 @@ def step32(x, sigma, sigma_next, w, need_uncond, prm, sampler):
         return pb
     if sampler == "euler":
         q = (sigma_next - sigma) / sigma
-        return x + (x - pb) * q
+        return fma32(x - pb, q, x)
     h = sigma_next - sigma
     i1 = f32(1) / sigma
     i2 = f32(1) / sigma_next
     hh = h * f32(0.5)
     d = (x - pb) * i1
-    xt = x + h * d
+    xt = fma32(h, d, x)
     pb2 = _pred(xt, sigma_next, w, mode, prm)
     d2 = (xt - pb2) * i2
-    return x + (d + d2) * hh
+    return fma32(d + d2, hh, x)
 
 
 def params32(inp, i):
@@ -170,9 +197,11 @@ def params32(inp, i):
 
 def init_latent32(inp, sig):
     sp = inp.spec
-    x = inp.noise.astype(np.float32) * sig[inp.start_step][:, None, None, None]
+    z = sig[inp.start_step][:, None, None, None]
     if inp.x_orig is not None:
-        x = _store(inp.x_orig, sp.dtype) + x
+        x = fma32(inp.noise, z, _store(inp.x_orig, sp.dtype))
+    else:
+        x = inp.noise.astype(np.float32) * z
     return _store(x, sp.dtype)
 
 
@@ -217,8 +246,8 @@ def area_accumulate32(crops, boxes, strengths, H, W, F, fallback=None):
         full[:, y0:y1, x0:x1] = crops[r]
         inb = np.zeros((H, W), bool)
         inb[y0:y1, x0:x1] = True
-        term = wh[r][None] * full
-        acc = np.where(inb[None], np.where(started[None], acc + term, term), acc)
+        acc = np.where(inb[None], np.where(started[None], fma32(wh[r][None], full, acc),
+                                           wh[r][None] * full), acc)
         started |= inb
     if fallback is not None:
         acc = np.where(covered[None], acc, np.asarray(fallback, np.float32))
@@ -231,4 +260,4 @@ def mask_blend32(a, b, mask, dtype):
     """out = m*a + (1-m)*b in float32, mask [.,1,H,W] broadcast over channels."""
     m = np.asarray(mask, np.float32)
     om = f32(1) - m
-    return _store(m * np.asarray(a, np.float32) + om * np.asarray(b, np.float32), dtype)
+    return _store(fma32(m, np.asarray(a, np.float32), om * np.asarray(b, np.float32)), dtype)

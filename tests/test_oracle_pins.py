@@ -435,3 +435,63 @@ def test_norm_stats_special_cases():
     assert s0[2] == s0[1] and s1[2] == s1[0] and s1[1] == 0.0
     v = D.denoise(x, 1.3, prm.mu_c, prm.s2)
     assert abs(s1[0] - np.mean([np.linalg.norm(v[c, h]) for c in range(2) for h in range(3)])) < 1e-12
+
+
+# ---------------------------------------------------------------- exact fp32 fused multiply-add
+
+def _rn_f32(q):
+    """Exact round-to-nearest-even of a rational to float32 (normal range)."""
+    from fractions import Fraction
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    scale = Fraction(2) ** (e - 23)
+    m = q / scale
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return np.float32(float(sign * fl * scale))
+
+
+def test_fma32_matches_exact_rational_rounding():
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    a = (rng.standard_normal(3000) * np.exp(rng.uniform(-8, 8, 3000))).astype(np.float32)
+    b = (rng.standard_normal(3000) * np.exp(rng.uniform(-8, 8, 3000))).astype(np.float32)
+    c = (rng.standard_normal(3000) * np.exp(rng.uniform(-16, 16, 3000))).astype(np.float32)
+    c[:1000] = -(a[:1000].astype(np.float64) * b[:1000]).astype(np.float32)  # heavy cancellation
+    got = M.fma32(a, b, c)
+    for k in range(a.size):
+        want = _rn_f32(Fraction(float(a[k])) * Fraction(float(b[k])) + Fraction(float(c[k])))
+        assert got[k] == want, (a[k], b[k], c[k], got[k], want)
+
+
+def test_fma32_double_rounding_trap():
+    # a*b = 1 + 2^-11 + 2^-24 sits exactly halfway between two float32 values;
+    # a tiny c breaks the tie upwards.  Rounding a*b + c to float64 first would
+    # lose c and then round the tie to even (downwards).
+    a = np.float32(1 + 2.0 ** -12)
+    c = np.float32(2.0 ** -70)
+    naive = np.float32(np.float64(a) * np.float64(a) + np.float64(c))
+    assert naive == np.float32(1 + 2.0 ** -11)
+    assert M.fma32(a, a, c) == np.float32(1 + 2.0 ** -11 + 2.0 ** -23)
+    assert M.fma32(a, a, -c) == np.float32(1 + 2.0 ** -11)
+    # the exact residual of a rounded product is representable and recovered
+    p = np.float32(np.float64(a) * np.float64(a))
+    assert M.fma32(a, a, -p) == np.float32(2.0 ** -24)
+
+
+def test_fma32_identities():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(1000).astype(np.float32)
+    y = rng.standard_normal(1000).astype(np.float32)
+    assert np.array_equal(M.fma32(np.float32(0), x, y), y)
+    assert np.array_equal(M.fma32(np.float32(1), x, np.float32(0)), x)
+    assert np.array_equal(M.fma32(x, np.float32(2), np.float32(0)), x * np.float32(2))
