@@ -271,7 +271,8 @@ def denoise(x, sigma: float, mu, s2: float):
 def feather_1d(d, L: int, F: int):
     """Linear edge ramp of F pixels along one axis of a box of length L.
 
-    Reading of "handle mask and feathering": weight (d+1)/F at the first
+    The page lists mask and feathering handling per cond without the ramp
+    shape.  Reading: weight (d+1)/F at the first
     pixel, rising by 1/F per pixel until it reaches 1, on both ends; 0 outside
     the box; F <= 0 means no feathering.
     """
@@ -374,9 +375,9 @@ def step(x, sigma: float, sigma_next: float, w: float, prm: SampleParams,
          sampler: str):
     """One sampler step from sigma to sigma_next (float64).
 
-    The pages give no update formula ("the sampler decides the update between
-    adjacent points"; some samplers evaluate the model more than once per
-    step).  Euler and Heun are taken from Karras et al. 2022 (EDM), Alg. 1:
+    The pages give no update formula (they leave the update between
+    neighbouring sigmas to the sampler, and note that some samplers evaluate
+    the model more than once per step).  Euler and Heun are taken from Karras et al. 2022 (EDM), Alg. 1:
       d  = (x - P(x, sigma)) / sigma,  x' = x + (sigma' - sigma) d
       Heun: x~ = x + h d, d' = (x~ - P(x~, sigma')) / sigma',
             x' = x + h (d + d') / 2, with h = sigma' - sigma.
