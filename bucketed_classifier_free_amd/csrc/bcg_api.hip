@@ -354,6 +354,7 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     p.HW = HW;
     p.nvec = (int)(vec ? HW / VV : HW);
     p.rows_aligned = vec ? (a->W % VV == 0) : 1;
+    p.identity = a->n_active == a->n ? 1 : 0;
     p.mask_stride = a->mask_per_sample ? (int)HW : 0;
     p.s2 = a->s2;
     p.x = a->x; p.x_out = a->x_out; p.sigmas = a->sigmas; p.order = a->order;

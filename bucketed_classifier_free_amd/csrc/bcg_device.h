@@ -140,6 +140,7 @@ struct StepParams {
     int tiles;                    // blocks per sample
     int vpt;                      // vectors per lane (blockDim apart)
     int rows_aligned;             // W % V == 0: a lane's V pixels share a row
+    int identity;                 // every sample active: workgroup j takes sample j
     int mask_stride;              // HW if per-sample mask, else 0
     float s2;
     const void* x;

@@ -247,10 +247,10 @@ __device__ __forceinline__ void setup_lane(LaneState<V, NR>& L, const SampleRegi
 
 // A lane's vectors vi0, vi0 + blockDim, ... (p.vpt of them) of one sample.
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
-__device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, const SampleRegions<NR>& sr,
-                                         const StepParams& p, const StepScalars& s,
-                                         const float* __restrict__ coef, int i, int vi0,
-                                         bool keep_u) {
+__device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V, NR>& L,
+                                         const SampleRegions<NR>& sr, const StepParams& p,
+                                         const StepScalars& s, const float* __restrict__ coef, int i,
+                                         int vi0, bool keep_u) {
     const int C = p.C;
     const int64_t sbase = (int64_t)i * C * p.HW;
     for (int v = 0; v < p.vpt; ++v) {
@@ -260,75 +260,35 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, const Sampl
         const T* xs = static_cast<const T*>(p.x) + sbase + p0;
         T* xd = static_cast<T*>(p.x_out) + sbase + p0;
         const T* xo = INP ? static_cast<const T*>(p.x_orig) + sbase + p0 : nullptr;
-        if (v > 0) load_stage<T, V, TN, INP>(a, xs, xo, 0, C, p.HW);
-        LaneState<V, NR> L;
-        setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
+        if (v > 0) {  // the first pass's head stage and pixel set-up come from the caller
+            load_stage<T, V, TN, INP>(a, xs, xo, 0, C, p.HW);
+            setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
+        }
         channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xs, xd, xo, C, p.HW);
     }
 }
 
+// After the head stage is requested: the first pass's pixel set-up (it
+// overlaps the latent loads), then the branch offsets into this wavefront's
+// own LDS slice (lane k computes channel k's; no workgroup barrier), then the
+// channel walks.
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN>
-__device__ __forceinline__ void dispatch_modes(bool one, bool fin, Stage<T, V, TN::U, INP>& a,
-                                               const SampleRegions<NR>& sr, const StepParams& p,
-                                               const StepScalars& s, const float* coef, int i,
-                                               int vi0, bool keep_u) {
-    if (one) {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, sr, p, s, coef, i, vi0, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, sr, p, s, coef, i, vi0, keep_u);
-    } else {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, sr, p, s, coef, i, vi0, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, sr, p, s, coef, i, vi0, keep_u);
-    }
-}
+__device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, bool lane_ok,
+                                           const SampleRegions<NR>& sr, const StepParams& p,
+                                           StepScalars s, float* coef, int i, int vi0, bool keep_u,
+                                           float sig, float sgn, float mu_u, float mu_c,
+                                           const float (&mu_r)[NR > 0 ? NR : 1]) {
+    LaneState<V, NR> L;
+    if (lane_ok) setup_lane<V, NR, NRB, INP>(L, sr, p, i, (int64_t)vi0 * V, s.w, keep_u);
 
-// NR: regions evaluated per pixel (>= the sample's count; extra regions are
-// zero-weight padding).  V: pixels per lane (16 bytes, or 1 for shapes whose
-// H*W is not a multiple of the vector).  Each workgroup covers blockDim * vpt
-// vectors of one sample (vpt per lane, blockDim apart).
-template <typename T, int V, int NR, bool INP, bool HEUN, typename TN = DefaultTune>
-__global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
-    __shared__ float coef[2 * kSet];
-    const int j = blockIdx.x / p.tiles;
-    const int tile = blockIdx.x - j * p.tiles;
-    if (j >= p.n_active) return;
-    const int i = p.order[j];
-    if (i < 0 || i >= p.n) return;
     const int C = p.C;
-    const int t = p.step_idx[i];
-    if (t < 0 || t + 1 >= p.num_sigmas) return;
-
-    // Request the first stage as soon as the sample is known.
-    const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
-    const bool lane_ok = vi0 < p.nvec;
-    Stage<T, V, TN::U, INP> a;
-    if (lane_ok) {
-        const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
-        load_stage<T, V, TN, INP>(a, static_cast<const T*>(p.x) + base,
-                                  INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, C, p.HW);
-    }
-
-    const float sig = p.sigmas[t];
-    const float sgn = p.sigmas[t + 1];
-    const float w = p.scale[i];
-    const bool keep_u = p.uncond_row[i] >= 0;
-    SampleRegions<NR> sr;
-    sr.cnt = 0;
-    if constexpr (NR > 0) {
-        int cnt = p.region_count[i];
-        cnt = cnt < 0 ? 0 : cnt;
-        cnt = cnt > p.R ? p.R : cnt;
-        sr.cnt = cnt > NR ? NR : cnt;
-    }
     const float s2 = p.s2;
     const float v = sig * sig;
     const float den = s2 + v;
     const float v2 = sgn * sgn;
     const float den2 = s2 + v2;
-
-    // Branch offsets b_k[c] = (sigma^2 mu_k[c]) / (s2 + sigma^2) into LDS.
-    for (int k = threadIdx.x; k < C; k += blockDim.x) {
-        const float mu_u = p.mu_uncond[(int64_t)i * C + k];
-        const float mu_c = p.mu_cond[(int64_t)i * C + k];
+    const int k = (int)threadIdx.x & 63;
+    if (k < C) {
         coef[k] = (v * mu_u) / den;
         coef[BCG_MAX_CHANNELS + k] = (v * mu_c) / den;
         if constexpr (HEUN) {
@@ -336,29 +296,91 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
             coef[kSet + BCG_MAX_CHANNELS + k] = (v2 * mu_c) / den2;
         }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const float mu_r = r < sr.cnt ? p.mu_region[((int64_t)i * p.R + r) * C + k] : 0.0f;
-            coef[(2 + r) * BCG_MAX_CHANNELS + k] = (v * mu_r) / den;
-            if constexpr (HEUN) coef[kSet + (2 + r) * BCG_MAX_CHANNELS + k] = (v2 * mu_r) / den2;
+        for (int r = 0; r < NRB; ++r) {
+            coef[(2 + r) * BCG_MAX_CHANNELS + k] = (v * mu_r[r]) / den;
+            if constexpr (HEUN) coef[kSet + (2 + r) * BCG_MAX_CHANNELS + k] = (v2 * mu_r[r]) / den2;
         }
     }
-    __syncthreads();
+    // LDS writes of this wavefront become visible to all its lanes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (!lane_ok) return;
 
-    StepScalars s;
     s.a = s2 / den;
     s.a2 = s2 / den2;
-    s.w = w;
     s.q = (sgn - sig) / sig;
     s.h = sgn - sig;
     s.is = 1.0f / sig;
     s.isn = 1.0f / sgn;
     s.hh = s.h * 0.5f;
+    const bool one = (s.w == 1.0f);
+    const bool fin = (sgn == 0.0f);
+    if (one) {
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, L, sr, p, s, coef, i, vi0, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, L, sr, p, s, coef, i, vi0, keep_u);
+    } else {
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, L, sr, p, s, coef, i, vi0, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, L, sr, p, s, coef, i, vi0, keep_u);
+    }
+}
 
+// NR: regions evaluated per pixel (>= the sample's count; extra regions are
+// zero-weight padding).  V: pixels per lane (16 bytes, or 1 for shapes whose
+// H*W is not a multiple of the vector).  Each workgroup covers blockDim * vpt
+// vectors of one sample (vpt per lane, blockDim apart); its wavefronts do not
+// synchronise with each other.  When every sample is active the workgroup
+// index maps to the sample directly (the processing order is immaterial), so
+// the first latent loads wait on no other load.
+template <typename T, int V, int NR, bool INP, bool HEUN, typename TN = DefaultTune>
+__global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
+    __shared__ float coef_all[4][2 * kSet];  // one slice per wavefront
+    float* coef = coef_all[threadIdx.x >> 6];
+    const int j = blockIdx.x / p.tiles;
+    const int tile = blockIdx.x - j * p.tiles;
+    if (j >= p.n_active) return;
+    const int i = p.identity ? j : p.order[j];
+    if (i < 0 || i >= p.n) return;
+    const int C = p.C;
+    const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
+    const bool lane_ok = vi0 < p.nvec;
+
+    // Channel k's means (lane k), then the head stage of the latent.
+    const int k = (int)threadIdx.x & 63;
+    const int kk = k < C ? k : 0;
+    const float mu_u = p.mu_uncond[(int64_t)i * C + kk];
+    const float mu_c = p.mu_cond[(int64_t)i * C + kk];
+    int cnt = 0;
+    if constexpr (NR > 0) {
+        cnt = p.region_count[i];
+        cnt = cnt < 0 ? 0 : cnt;
+        cnt = cnt > p.R ? p.R : cnt;
+        cnt = cnt > NR ? NR : cnt;
+    }
+    float mu_r[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int r = 0; r < (NR > 0 ? NR : 1); ++r)
+        mu_r[r] = (NR > 0 && r < cnt) ? p.mu_region[((int64_t)i * p.R + r) * C + kk] : 0.0f;
+    Stage<T, V, TN::U, INP> a;
+    if (lane_ok) {
+        const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
+        load_stage<T, V, TN, INP>(a, static_cast<const T*>(p.x) + base,
+                                  INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, C, p.HW);
+    }
+    const int t = p.step_idx[i];
+    if (t < 0 || t + 1 >= p.num_sigmas) return;
+
+    const float sig = p.sigmas[t];
+    const float sgn = p.sigmas[t + 1];
+    StepScalars s;
+    s.w = p.scale[i];
+    const bool keep_u = p.uncond_row[i] >= 0;
+    SampleRegions<NR> sr;
+    sr.cnt = cnt;
     if constexpr (NR > 0) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            if (r < sr.cnt) {
+            if (r < cnt) {
                 const int32_t* b = p.region_box + ((int64_t)i * p.R + r) * 4;
                 sr.rd[r].y0 = b[0];
                 sr.rd[r].h = b[1] - b[0];
@@ -372,13 +394,10 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
             }
         }
     }
-
-    const bool one = (w == 1.0f);
-    const bool fin = (sgn == 0.0f);
-    if (NR > 0 && sr.cnt > 0)
-        dispatch_modes<T, V, TN, NR, NR, INP, HEUN>(one, fin, a, sr, p, s, coef, i, vi0, keep_u);
+    if (NR > 0 && cnt > 0)
+        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, keep_u, sig, sgn, mu_u, mu_c, mu_r);
     else
-        dispatch_modes<T, V, TN, NR, 0, INP, HEUN>(one, fin, a, sr, p, s, coef, i, vi0, keep_u);
+        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, keep_u, sig, sgn, mu_u, mu_c, mu_r);
 }
 
 template <typename T, int V, int NR, typename TN = DefaultTune>
