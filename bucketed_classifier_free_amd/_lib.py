@@ -17,12 +17,15 @@ BCG_CURVE = {"const": 0, "linear": 1, "front_high": 2}
 BCG_MAX_REGIONS = 4
 BCG_MAX_CHANNELS = 64
 BCG_MAX_FEATHER = 64
+BCG_MAX_DEVICE_BUCKETS = 1024
+BCG_MAX_DEVICE_STEPS = 1 << 20
+ABI_VERSION = 3
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "bucket_table",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
-           "area_accumulate", "mask_blend", "bcg_loop_create", "bcg_loop_run",
-           "bcg_loop_destroy"]
+           "area_accumulate", "mask_blend", "bcg_plan_device", "guided_step_dplan",
+           "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy"]
 
 vp, i32p, i64p, f32p, f64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64),
                               C.POINTER(C.c_float), C.POINTER(C.c_double))
@@ -56,11 +59,21 @@ class StepArgs(C.Structure):
                 ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
+class DevicePlan(C.Structure):
+    _fields_ = [("steps", C.c_int32), ("num_buckets", C.c_int32), ("wrap", C.c_int32),
+                ("bucket_cfg", vp), ("cfg_override", vp), ("covered", vp), ("step_in", vp),
+                ("step_out", vp), ("bucket_id", vp), ("scale", vp), ("uncond_row", vp),
+                ("cond_row", vp), ("order", vp), ("bucket_count", vp), ("bucket_offset", vp),
+                ("uncond_offset", vp), ("totals", vp)]
+
+
 class LoopDesc(C.Structure):
     _fields_ = [("plan", PlanIn), ("start", vp), ("wrap", C.c_int32), ("rows", C.c_int32),
                 ("host_slab", vp), ("dev_slab", vp), ("replicas", C.c_int32),
                 ("replica_stride", C.c_int64), ("upload_batch", C.c_int32),
-                ("async_upload", C.c_int32), ("timing_every", C.c_int32), ("step", StepArgs)]
+                ("async_upload", C.c_int32), ("timing_every", C.c_int32), ("step", StepArgs),
+                ("device_plan", C.c_int32), ("graph_launches", C.c_int32), ("dev_steps", vp),
+                ("dplan", DevicePlan)]
 
 
 _lib = None
@@ -81,6 +94,8 @@ def lib():
         L.bucket_table.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp]
         L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
         L.guided_step.argtypes = [C.POINTER(StepArgs), vp]
+        L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]
+        L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_workspace_size.argtypes = [C.c_int] * 5
         L.guided_step_workspace_size.restype = C.c_size_t
         L.latent_init.argtypes = [C.c_int] * 5 + [vp, vp, vp, C.c_int, vp, vp, vp]

@@ -145,12 +145,11 @@ def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
     return int(L.lib().guided_step_workspace_size(n, C, H, W, _DT[dtype]))
 
 
-def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond, mu_cond, *,
-                n_active: int, sampler: str, s2: float, feather: int = 0,
-                region_count=None, region_box=None, region_strength=None, mu_region=None,
-                x_orig=None, mask=None, stats=None, workspace=None, cache_hint: int = 0,
-                stream=None):
-    """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU."""
+def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sampler, s2, feather,
+               region_count, region_box, region_strength, mu_region, x_orig, mask, stats,
+               workspace, cache_hint):
+    """Checks the tensors of a guided step and packs them into StepArgs.
+    ``plan_rows`` = (order, step_idx, scale, uncond_row) or None (device plan)."""
     _dev(x, "x")
     if x.dim() != 4:
         raise ValueError("x must be [n, C, H, W]")
@@ -161,14 +160,17 @@ def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond,
     _dev(sigmas, "sigmas", torch.float32)
     if sigmas.dim() != 1:
         raise ValueError("sigmas must be 1-D")
-    _dev(order, "order", torch.int32)
-    if order.numel() < n_active:
-        raise ValueError("order shorter than n_active")
-    for t, nm, dt in ((step_idx, "step_idx", torch.int32), (scale, "scale", torch.float32),
-                      (uncond_row, "uncond_row", torch.int32)):
-        _dev(t, nm, dt)
-        if t.numel() < n:
-            raise ValueError(f"{nm}: needs {n} entries")
+    order = step_idx = scale = uncond_row = None
+    if plan_rows is not None:
+        order, step_idx, scale, uncond_row = plan_rows
+        _dev(order, "order", torch.int32)
+        if order.numel() < n_active:
+            raise ValueError("order shorter than n_active")
+        for t, nm, dt in ((step_idx, "step_idx", torch.int32), (scale, "scale", torch.float32),
+                          (uncond_row, "uncond_row", torch.int32)):
+            _dev(t, nm, dt)
+            if t.numel() < n:
+                raise ValueError(f"{nm}: needs {n} entries")
     _dev(mu_uncond, "mu_uncond", torch.float32, (n, Cc))
     _dev(mu_cond, "mu_cond", torch.float32, (n, Cc))
     R = 0
@@ -195,13 +197,93 @@ def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond,
         wsb = workspace.numel() * workspace.element_size()
     if sampler not in _SAMPLER:
         raise ValueError(f"unknown sampler {sampler!r}")
-    a = L.StepArgs(n, Cc, H, W, _DT[x.dtype], _SAMPLER[sampler], R, int(feather), int(n_active),
-                   sigmas.numel(), mps, int(cache_hint), float(s2),
-                   _ptr(x), _ptr(x_out), _ptr(sigmas), _ptr(order), _ptr(step_idx), _ptr(scale),
-                   _ptr(uncond_row), _ptr(mu_uncond), _ptr(mu_cond), _ptr(region_count),
-                   _ptr(region_box), _ptr(region_strength), _ptr(mu_region), _ptr(x_orig),
-                   _ptr(mask), _ptr(stats), _ptr(workspace), wsb)
+    return L.StepArgs(n, Cc, H, W, _DT[x.dtype], _SAMPLER[sampler], R, int(feather), int(n_active),
+                      sigmas.numel(), mps, int(cache_hint), float(s2),
+                      _ptr(x), _ptr(x_out), _ptr(sigmas), _ptr(order), _ptr(step_idx), _ptr(scale),
+                      _ptr(uncond_row), _ptr(mu_uncond), _ptr(mu_cond), _ptr(region_count),
+                      _ptr(region_box), _ptr(region_strength), _ptr(mu_region), _ptr(x_orig),
+                      _ptr(mask), _ptr(stats), _ptr(workspace), wsb)
+
+
+def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond, mu_cond, *,
+                n_active: int, sampler: str, s2: float, feather: int = 0,
+                region_count=None, region_box=None, region_strength=None, mu_region=None,
+                x_orig=None, mask=None, stats=None, workspace=None, cache_hint: int = 0,
+                stream=None):
+    """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU."""
+    a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, (order, step_idx, scale, uncond_row),
+                   n_active=n_active, sampler=sampler, s2=s2, feather=feather,
+                   region_count=region_count, region_box=region_box,
+                   region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
+                   stats=stats, workspace=workspace, cache_hint=cache_hint)
     L.check(L.lib().guided_step(ct.byref(a), _stream(stream)))
+
+
+# ---------------------------------------------------------------- device plans
+
+_PLAN_KEYS = ("bucket_id", "scale", "uncond_row", "cond_row", "order", "bucket_count",
+              "bucket_offset", "uncond_offset", "totals")
+
+
+def device_plan_arrays(n: int, nb: int, device="cuda") -> dict:
+    """Device output arrays of one device-built plan."""
+    e = lambda k, dt: torch.empty(k, dtype=dt, device=device)
+    i32 = torch.int32
+    return dict(bucket_id=e(n, i32), scale=e(n, torch.float32), uncond_row=e(n, i32),
+                cond_row=e(n, i32), order=e(n, i32), bucket_count=e(nb, i32),
+                bucket_offset=e(nb + 1, i32), uncond_offset=e(nb + 1, i32), totals=e(2, i32))
+
+
+def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
+                covered=None, wrap: bool = False, out=None) -> L.DevicePlan:
+    """Packs the device arrays of a device-built plan (see include/bcg.h)."""
+    _dev(step_in, "step_in", torch.int32)
+    n = step_in.numel()
+    _dev(bucket_cfg, "bucket_cfg", torch.float32)
+    nb = bucket_cfg.numel()
+    _dev(step_out, "step_out", torch.int32, allow_none=True)
+    if step_out is not None and step_out.numel() < n:
+        raise ValueError("step_out: needs n entries")
+    _dev(cfg_override, "cfg_override", torch.float32, (n,), allow_none=True)
+    _dev(covered, "covered", torch.int32, (n,), allow_none=True)
+    ptrs = [None] * len(_PLAN_KEYS)
+    if out is not None:
+        for k, dt, size in (("bucket_id", torch.int32, n), ("scale", torch.float32, n),
+                            ("uncond_row", torch.int32, n), ("cond_row", torch.int32, n),
+                            ("order", torch.int32, n), ("bucket_count", torch.int32, nb),
+                            ("bucket_offset", torch.int32, nb + 1),
+                            ("uncond_offset", torch.int32, nb + 1), ("totals", torch.int32, 2)):
+            _dev(out[k], k, dt)
+            if out[k].numel() < size:
+                raise ValueError(f"{k}: needs {size} entries")
+        ptrs = [_ptr(out[k]) for k in _PLAN_KEYS]
+    return L.DevicePlan(int(steps), nb, 1 if wrap else 0, _ptr(bucket_cfg), _ptr(cfg_override),
+                        _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs)
+
+
+def bcg_plan_device(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
+                    covered=None, wrap: bool = False, out=None, stream=None):
+    """The plan of one step built on the device (and the step advance)."""
+    d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
+                    covered=covered, wrap=wrap, out=out)
+    L.check(L.lib().bcg_plan_device(step_in.numel(), ct.byref(d), _stream(stream)))
+
+
+def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucket_cfg, step_in,
+                      step_out=None, cfg_override=None, covered=None, wrap: bool = False,
+                      plan_out=None, sampler: str, s2: float, feather: int = 0,
+                      region_count=None, region_box=None, region_strength=None, mu_region=None,
+                      x_orig=None, mask=None, cache_hint: int = 0, stream=None):
+    """guided_step with the plan of the step built on the device, same launch."""
+    a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, None, n_active=0, sampler=sampler,
+                   s2=s2, feather=feather, region_count=region_count, region_box=region_box,
+                   region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
+                   stats=None, workspace=None, cache_hint=cache_hint)
+    if step_in.numel() != x.shape[0]:
+        raise ValueError("step_in: needs one entry per sample")
+    d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
+                    covered=covered, wrap=wrap, out=plan_out)
+    L.check(L.lib().guided_step_dplan(ct.byref(a), ct.byref(d), _stream(stream)))
 
 
 def latent_init(noise, sigmas, step_idx, x_out, latent=None, stream=None):

@@ -7,6 +7,7 @@
 
 #include "bcg_common.h"
 #include "bcg_device.h"
+#include "bcg_plan_dev.h"
 
 using bcg::fail;
 
@@ -294,6 +295,58 @@ int grid_for(int64_t work, int block) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20));
 }
 
+// ------------------------------------------------------------ device plan
+
+__global__ __launch_bounds__(256) void plan_kernel(const StepParams p) {
+    __shared__ int sh[2 * BCG_MAX_DEVICE_BUCKETS];
+    plan_workgroup(p, sh);
+}
+
+// Checks a device plan for n samples; `step` says whether it drives a step.
+int check_dplan(const bcg_device_plan* d, int n, bool step, const char* who) {
+    if (!d) return fail(BCG_EINVAL, "%s: plan is NULL", who);
+    if (d->steps < 1 || d->steps > BCG_MAX_DEVICE_STEPS)
+        return fail(BCG_EINVAL, "%s: steps %d not in [1, %d]", who, d->steps, BCG_MAX_DEVICE_STEPS);
+    if (d->num_buckets < 1 || d->num_buckets > BCG_MAX_DEVICE_BUCKETS)
+        return fail(BCG_EINVAL, "%s: num_buckets %d not in [1, %d]", who, d->num_buckets, BCG_MAX_DEVICE_BUCKETS);
+    if (d->wrap != 0 && d->wrap != 1) return fail(BCG_EINVAL, "%s: wrap must be 0 or 1", who);
+    if (n == 0) return BCG_OK;
+    if (!d->bucket_cfg || !d->step_in) return fail(BCG_EINVAL, "%s: bucket_cfg/step_in is NULL", who);
+    const void* outs[] = {d->bucket_id, d->scale, d->uncond_row, d->cond_row, d->order,
+                          d->bucket_count, d->bucket_offset, d->uncond_offset, d->totals};
+    int given = 0;
+    for (const void* o : outs) given += o != nullptr;
+    if (given != 0 && given != 9) return fail(BCG_EINVAL, "%s: plan outputs must be all given or all NULL", who);
+    if (!step && given == 0 && !d->step_out) return fail(BCG_EINVAL, "%s: nothing to write", who);
+    if (d->step_out) {
+        const size_t bytes = (size_t)n * sizeof(int32_t);
+        const uintptr_t a = reinterpret_cast<uintptr_t>(d->step_in), b = reinterpret_cast<uintptr_t>(d->step_out);
+        if (a < b + bytes && b < a + bytes) return fail(BCG_EINVAL, "%s: step_out overlaps step_in", who);
+    }
+    return BCG_OK;
+}
+
+void fill_dplan(StepParams& p, const bcg_device_plan* d) {
+    p.dplan = 1;
+    p.steps = d->steps;
+    p.nb = d->num_buckets;
+    p.wrap = d->wrap;
+    p.bucket_cfg = d->bucket_cfg;
+    p.cfg_override = d->cfg_override;
+    p.covered = d->covered;
+    p.step_idx = d->step_in;
+    p.step_out = d->step_out;
+    p.plan_bucket_id = d->bucket_id;
+    p.plan_scale = d->scale;
+    p.plan_uncond_row = d->uncond_row;
+    p.plan_cond_row = d->cond_row;
+    p.plan_order = d->order;
+    p.plan_bucket_count = d->bucket_count;
+    p.plan_bucket_offset = d->bucket_offset;
+    p.plan_uncond_offset = d->uncond_offset;
+    p.plan_totals = d->totals;
+}
+
 }  // namespace
 }  // namespace bcg
 
@@ -306,39 +359,62 @@ extern "C" size_t guided_step_workspace_size(int n, int C, int H, int W, int dty
     return (size_t)n * C * H * 3 * sizeof(float);
 }
 
-extern "C" int guided_step(const bcg_step_args* a, void* stream) {
-    bcg::clear_error();
-    if (!a) return fail(BCG_EINVAL, "guided_step: args is NULL");
+namespace {
+
+int hip_status_of(hipError_t e, const char* who, const char* what) {
+    if (e != hipSuccess) return fail(BCG_EHIP, "%s: %s: %s", who, what, hipGetErrorString(e));
+    return BCG_OK;
+}
+
+// guided_step with the host plan (d == NULL) or a device-built one (d).
+int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, const char* who) {
+    if (!a) return fail(BCG_EINVAL, "%s: args is NULL", who);
     if (a->n < 0 || a->C < 1 || a->C > BCG_MAX_CHANNELS || a->H < 1 || a->W < 1)
-        return fail(BCG_ESHAPE, "guided_step: bad shape n=%d C=%d H=%d W=%d (C must be in [1, %d])",
+        return fail(BCG_ESHAPE, "%s: bad shape n=%d C=%d H=%d W=%d (C must be in [1, %d])", who,
                     a->n, a->C, a->H, a->W, BCG_MAX_CHANNELS);
     const int64_t HW = (int64_t)a->H * a->W;
-    if (HW > (int64_t(1) << 30)) return fail(BCG_ESHAPE, "guided_step: H*W too large");
-    if (a->dtype != BCG_F32 && a->dtype != BCG_BF16) return fail(BCG_EDTYPE, "guided_step: unknown dtype %d", a->dtype);
-    if (a->sampler != BCG_EULER && a->sampler != BCG_HEUN) return fail(BCG_EINVAL, "guided_step: unknown sampler %d", a->sampler);
+    if (HW > (int64_t(1) << 30)) return fail(BCG_ESHAPE, "%s: H*W too large", who);
+    if (a->dtype != BCG_F32 && a->dtype != BCG_BF16) return fail(BCG_EDTYPE, "%s: unknown dtype %d", who, a->dtype);
+    if (a->sampler != BCG_EULER && a->sampler != BCG_HEUN)
+        return fail(BCG_EINVAL, "%s: unknown sampler %d", who, a->sampler);
     if (a->max_regions < 0 || a->max_regions > BCG_MAX_REGIONS)
-        return fail(BCG_EINVAL, "guided_step: max_regions %d not in [0, %d]", a->max_regions, BCG_MAX_REGIONS);
-    if (a->feather < 0 || a->feather > BCG_MAX_FEATHER) return fail(BCG_EINVAL, "guided_step: feather %d out of range", a->feather);
-    if (a->n_active < 0 || a->n_active > a->n) return fail(BCG_EINVAL, "guided_step: n_active %d not in [0, n]", a->n_active);
-    if (a->num_sigmas < 2) return fail(BCG_EINVAL, "guided_step: num_sigmas %d < 2", a->num_sigmas);
-    if (!(a->s2 > 0.0f) || !std::isfinite(a->s2)) return fail(BCG_EINVAL, "guided_step: s2 must be finite and > 0");
-    if (a->mask_per_sample != 0 && a->mask_per_sample != 1) return fail(BCG_EINVAL, "guided_step: mask_per_sample must be 0 or 1");
+        return fail(BCG_EINVAL, "%s: max_regions %d not in [0, %d]", who, a->max_regions, BCG_MAX_REGIONS);
+    if (a->feather < 0 || a->feather > BCG_MAX_FEATHER)
+        return fail(BCG_EINVAL, "%s: feather %d out of range", who, a->feather);
+    if (!d && (a->n_active < 0 || a->n_active > a->n))
+        return fail(BCG_EINVAL, "%s: n_active %d not in [0, n]", who, a->n_active);
+    if (a->num_sigmas < 2) return fail(BCG_EINVAL, "%s: num_sigmas %d < 2", who, a->num_sigmas);
+    if (!(a->s2 > 0.0f) || !std::isfinite(a->s2)) return fail(BCG_EINVAL, "%s: s2 must be finite and > 0", who);
+    if (a->mask_per_sample != 0 && a->mask_per_sample != 1)
+        return fail(BCG_EINVAL, "%s: mask_per_sample must be 0 or 1", who);
     if (a->cache_hint != BCG_CACHE_KEEP && a->cache_hint != BCG_CACHE_STREAM)
-        return fail(BCG_EINVAL, "guided_step: unknown cache_hint %d", a->cache_hint);
-    if (a->n_active == 0) return BCG_OK;
-    if (!a->x || !a->x_out || !a->sigmas || !a->order || !a->step_idx || !a->scale || !a->uncond_row ||
-        !a->mu_uncond || !a->mu_cond)
-        return fail(BCG_EINVAL, "guided_step: NULL device pointer");
+        return fail(BCG_EINVAL, "%s: unknown cache_hint %d", who, a->cache_hint);
+    if (d) {
+        const int rc = check_dplan(d, a->n, true, who);
+        if (rc) return rc;
+        if (a->order || a->step_idx || a->scale || a->uncond_row)
+            return fail(BCG_EINVAL, "%s: order/step_idx/scale/uncond_row come from the device plan and must be NULL", who);
+        if (a->stats) return fail(BCG_EINVAL, "%s: stats need the host plan", who);
+        if (a->num_sigmas < d->steps + 1)
+            return fail(BCG_EINVAL, "%s: num_sigmas %d < steps + 1 = %d", who, a->num_sigmas, d->steps + 1);
+        if (a->max_regions > 0 && a->region_count && !d->covered)
+            return fail(BCG_EINVAL, "%s: a step with regions needs the coverage flags", who);
+    }
+    const int n_run = d ? a->n : a->n_active;  // samples the grid covers
+    if (n_run == 0) return BCG_OK;
+    if (!a->x || !a->x_out || !a->sigmas || !a->mu_uncond || !a->mu_cond ||
+        (!d && (!a->order || !a->step_idx || !a->scale || !a->uncond_row)))
+        return fail(BCG_EINVAL, "%s: NULL device pointer", who);
     if (a->max_regions > 0 && (!a->region_count || !a->region_box || !a->region_strength || !a->mu_region))
-        return fail(BCG_EINVAL, "guided_step: max_regions > 0 needs region_count/box/strength/mu_region");
+        return fail(BCG_EINVAL, "%s: max_regions > 0 needs region_count/box/strength/mu_region", who);
     if ((a->x_orig == nullptr) != (a->mask == nullptr))
-        return fail(BCG_EINVAL, "guided_step: x_orig and mask must be given together");
+        return fail(BCG_EINVAL, "%s: x_orig and mask must be given together", who);
     const size_t bytes = (size_t)a->n * a->C * HW * elem_size(a->dtype);
-    if (partial_overlap(a->x, a->x_out, bytes)) return fail(BCG_EINVAL, "guided_step: x and x_out partially overlap");
+    if (partial_overlap(a->x, a->x_out, bytes)) return fail(BCG_EINVAL, "%s: x and x_out partially overlap", who);
     if (a->stats) {
         const size_t need = guided_step_workspace_size(a->n_active, a->C, a->H, a->W, a->dtype);
         if (!a->workspace || a->workspace_bytes < need)
-            return fail(BCG_EINVAL, "guided_step: stats need a workspace of %zu bytes", need);
+            return fail(BCG_EINVAL, "%s: stats need a workspace of %zu bytes", who, need);
     }
     const bool inpaint = a->x_orig != nullptr;
     const int VV = a->dtype == BCG_BF16 ? 8 : 4;
@@ -349,12 +425,12 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     p.n = a->n; p.C = a->C; p.H = a->H; p.W = a->W; p.R = a->max_regions;
     p.feather = std::max(a->feather, 1);
     p.inv_f4 = 1.0f / float(p.feather * p.feather * p.feather * p.feather);
-    p.n_active = a->n_active;
+    p.n_active = n_run;
     p.num_sigmas = a->num_sigmas;
     p.HW = HW;
     p.nvec = (int)(vec ? HW / VV : HW);
     p.rows_aligned = vec ? (a->W % VV == 0) : 1;
-    p.identity = a->n_active == a->n ? 1 : 0;
+    p.identity = n_run == a->n ? 1 : 0;
     p.mask_stride = a->mask_per_sample ? (int)HW : 0;
     p.s2 = a->s2;
     p.x = a->x; p.x_out = a->x_out; p.sigmas = a->sigmas; p.order = a->order;
@@ -362,11 +438,18 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     p.mu_uncond = a->mu_uncond; p.mu_cond = a->mu_cond; p.region_count = a->region_count;
     p.region_box = a->region_box; p.region_strength = a->region_strength; p.mu_region = a->mu_region;
     p.x_orig = a->x_orig; p.mask = a->mask;
+    p.t_end = a->num_sigmas - 1;
+    p.plan_block = -1;
+    if (d) {
+        fill_dplan(p, d);
+        p.t_end = d->steps;
+    }
     const LaunchShape shape = pick_shape(p.n_active, p.nvec);
     const int block = shape.block;
     p.vpt = shape.vpt;
     p.tiles = (int)(((int64_t)p.nvec + (int64_t)block * p.vpt - 1) / ((int64_t)block * p.vpt));
-    if ((int64_t)p.n_active * p.tiles > INT32_MAX) return fail(BCG_ESHAPE, "guided_step: grid too large");
+    if ((int64_t)p.n_active * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
+    if (d && (d->step_out || d->bucket_id)) p.plan_block = (int)((int64_t)p.n_active * p.tiles);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     if (a->stats) {
@@ -375,10 +458,10 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
         const int g = (int)((nrows + 3) / 4);
         if (a->dtype == BCG_BF16) hipLaunchKernelGGL(stats_rows_kernel<bf16_t>, dim3(g), dim3(256), 0, st, p, rows);
         else hipLaunchKernelGGL(stats_rows_kernel<float>, dim3(g), dim3(256), 0, st, p, rows);
-        int rc = hip_status(hipGetLastError(), "guided_step: stats launch");
+        int rc = hip_status_of(hipGetLastError(), who, "stats launch");
         if (rc) return rc;
         hipLaunchKernelGGL(stats_final_kernel, dim3(p.n_active), dim3(256), 0, st, p, rows, a->stats);
-        rc = hip_status(hipGetLastError(), "guided_step: stats launch");
+        rc = hip_status_of(hipGetLastError(), who, "stats launch");
         if (rc) return rc;
     }
     const bool heun = a->sampler == BCG_HEUN;
@@ -389,7 +472,35 @@ extern "C" int guided_step(const bcg_step_args* a, void* stream) {
     else
         e = a->dtype == BCG_BF16 ? launch_step_bf16(p, vec, heun, inpaint, block, st)
                                  : launch_step_f32(p, vec, heun, inpaint, block, st);
-    return hip_status(e, "guided_step: launch");
+    return hip_status_of(e, who, "launch");
+}
+
+}  // namespace
+
+extern "C" int guided_step(const bcg_step_args* a, void* stream) {
+    bcg::clear_error();
+    return step_impl(a, nullptr, stream, "guided_step");
+}
+
+extern "C" int guided_step_dplan(const bcg_step_args* a, const bcg_device_plan* d, void* stream) {
+    bcg::clear_error();
+    if (!d) return fail(BCG_EINVAL, "guided_step_dplan: plan is NULL");
+    return step_impl(a, d, stream, "guided_step_dplan");
+}
+
+extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
+    bcg::clear_error();
+    if (n < 0 || n > (1 << 24)) return fail(BCG_ESHAPE, "bcg_plan_device: n %d out of range", n);
+    const int rc = check_dplan(d, n, false, "bcg_plan_device");
+    if (rc) return rc;
+    if (n == 0) return BCG_OK;
+    StepParams p{};
+    p.n = n;
+    fill_dplan(p, d);
+    p.t_end = d->steps;
+    p.plan_block = 0;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+    return hip_status(hipGetLastError(), "bcg_plan_device: launch");
 }
 
 extern "C" int latent_init(int n, int C, int H, int W, int dtype, const float* noise, const void* latent,

@@ -158,6 +158,27 @@ struct StepParams {
     const float* mu_region;
     const void* x_orig;
     const float* mask;
+    // Device-built plan (dplan = 1): step_idx holds this step's indices and
+    // the sample's bucket, scale and uncond decision are derived in the
+    // kernel; workgroup plan_block (if >= 0) writes the full plan and the
+    // step advance.
+    int dplan;
+    int t_end;                    // samples with t outside [0, t_end) are skipped
+    int steps, nb, wrap;
+    int plan_block;
+    const float* bucket_cfg;
+    const float* cfg_override;
+    const int32_t* covered;
+    int32_t* step_out;
+    int32_t* plan_bucket_id;
+    float* plan_scale;
+    int32_t* plan_uncond_row;
+    int32_t* plan_cond_row;
+    int32_t* plan_order;
+    int32_t* plan_bucket_count;
+    int32_t* plan_bucket_offset;
+    int32_t* plan_uncond_offset;
+    int32_t* plan_totals;
 };
 
 // Launchers, one per storage dtype and cache behaviour (bcg_step_*.hip).

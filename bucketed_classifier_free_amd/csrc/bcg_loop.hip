@@ -1,8 +1,12 @@
-// Native sampler loop: per-step plan build, staging, upload and launch with no
-// interpreter in between.  Plan uploads run on a copy stream of the loop's own
-// (default priority) so they overlap the previous step's kernel; the compute
-// stream waits on the upload's event, and an upload into a device row waits
-// for the kernel that last read that row.
+// Native sampler loop with no interpreter in between launches.
+//   Host plans: per-step plan build, staging and upload, then the launch.
+//   Plan uploads run on the compute stream, or on a copy stream of the loop's
+//   own (default priority) where the compute stream waits on the upload's
+//   event and an upload into a device row waits for the kernel that last
+//   read that row.
+//   Device plans: one guided_step_dplan per launch, which builds the plan
+//   and advances the step indices on the device; optionally replays of a
+//   captured graph of G launches.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -25,12 +29,171 @@ struct bcg_loop {
     std::vector<int32_t> region_box;
     std::vector<int64_t> region_off;
     std::vector<uint8_t> covered;     // per-sample coverage, computed once
+    // device plans
+    int64_t k_next = 0;               // launches done since the last restart
+    std::vector<int32_t> t0;          // initial step indices (from start)
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t graph_exec = nullptr;
 };
 
 namespace {
 
 int hip_ok(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(BCG_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return BCG_OK;
+}
+
+// Validates the device-plan launch template without launching anything.
+int check_dplan(bcg_loop* L, const char* who) {
+    bcg_step_args a = L->d.step;
+    a.order = nullptr;
+    a.step_idx = nullptr;
+    a.scale = nullptr;
+    a.uncond_row = nullptr;
+    const bcg_device_plan& d = L->d.dplan;
+    if (d.steps < 1 || d.steps > BCG_MAX_DEVICE_STEPS || d.num_buckets > BCG_MAX_DEVICE_BUCKETS)
+        return fail(BCG_EINVAL, "%s: device plans need steps <= %d and num_buckets <= %d", who,
+                    BCG_MAX_DEVICE_STEPS, BCG_MAX_DEVICE_BUCKETS);
+    if (a.num_sigmas < d.steps + 1) return fail(BCG_EINVAL, "%s: num_sigmas < steps + 1", who);
+    if (a.stats) return fail(BCG_EINVAL, "%s: stats need host plans", who);
+    if (a.n > 0 && !d.bucket_cfg) return fail(BCG_EINVAL, "%s: dplan.bucket_cfg is NULL", who);
+    if (a.max_regions > 0 && a.region_count && !d.covered)
+        return fail(BCG_EINVAL, "%s: a step with regions needs dplan.covered", who);
+    return BCG_OK;
+}
+
+// Writes the initial step indices into buffer 0 of every replica.
+int reset_steps(bcg_loop* L, hipStream_t st) {
+    const int n = L->d.plan.n;
+    for (int r = 0; r < L->d.replicas && n > 0; ++r) {
+        const int rc = hip_ok(hipMemcpyAsync(L->d.dev_steps + size_t(2 * r) * n, L->t0.data(),
+                                             sizeof(int32_t) * size_t(n), hipMemcpyHostToDevice, st),
+                              "bcg_loop: step index upload");
+        if (rc) return rc;
+    }
+    L->k_next = 0;
+    return hip_ok(hipStreamSynchronize(st), "bcg_loop: step index upload");
+}
+
+// Launch k of a device-plan loop (replica k mod R, its own launch k / R).
+int launch_dplan(bcg_loop* L, int64_t k, hipStream_t st) {
+    const bcg_loop_desc& d = L->d;
+    const int n = d.plan.n;
+    const int64_t r = k % d.replicas, m = k / d.replicas;
+    bcg_step_args a = d.step;
+    if (d.replicas > 1) {
+        a.x = static_cast<const char*>(a.x) + r * d.replica_stride;
+        a.x_out = static_cast<char*>(a.x_out) + r * d.replica_stride;
+    }
+    a.order = nullptr;
+    a.step_idx = nullptr;
+    a.scale = nullptr;
+    a.uncond_row = nullptr;
+    bcg_device_plan dp = d.dplan;
+    dp.step_in = d.dev_steps + size_t(2 * r + (m & 1)) * n;
+    dp.step_out = d.dev_steps + size_t(2 * r + ((m + 1) & 1)) * n;
+    return guided_step_dplan(&a, &dp, st);
+}
+
+// Captures launches 0 .. G-1 (one period of the buffer pattern, repeated)
+// into a graph on the loop's own stream.
+int build_graph(bcg_loop* L) {
+    const int G = L->d.graph_launches;
+    int rc = hip_ok(hipStreamBeginCapture(L->copy, hipStreamCaptureModeThreadLocal), "bcg_loop: begin capture");
+    if (rc) return rc;
+    int rc_launch = BCG_OK;
+    for (int k = 0; k < G && rc_launch == BCG_OK; ++k) rc_launch = launch_dplan(L, k, L->copy);
+    hipGraph_t g = nullptr;
+    rc = hip_ok(hipStreamEndCapture(L->copy, &g), "bcg_loop: end capture");
+    if (rc_launch || rc) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc_launch ? rc_launch : rc;
+    }
+    rc = hip_ok(hipGraphInstantiate(&L->graph_exec, g, nullptr, nullptr, 0), "bcg_loop: graph instantiate");
+    if (rc) {
+        (void)hipGraphDestroy(g);
+        L->graph_exec = nullptr;
+        return rc;
+    }
+    L->graph = g;
+    return BCG_OK;
+}
+
+hipEvent_t* timing_event(bcg_loop* L, size_t idx, int* rc) {
+    while (L->t_ev.size() <= idx) {
+        hipEvent_t e;
+        *rc = hip_ok(hipEventCreate(&e), "bcg_loop_run: hipEventCreate");
+        if (*rc) return nullptr;
+        L->t_ev.push_back(e);
+    }
+    return &L->t_ev[idx];
+}
+
+// bcg_loop_run with device plans.
+int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms) {
+    const bcg_loop_desc& d = L->d;
+    int rc = BCG_OK;
+    if (k0 == 0 && L->k_next != 0) {
+        rc = reset_steps(L, st);
+        if (rc) return rc;
+    } else if (k0 != L->k_next) {
+        return fail(BCG_EINVAL, "bcg_loop_run: device plans continue at launch %lld (or restart at 0), not %d",
+                    (long long)L->k_next, k0);
+    }
+    const int G = d.graph_launches;
+    const int64_t period = 2 * int64_t(d.replicas);
+    int64_t k = k0;
+    int j = 0;
+    size_t pairs = 0;
+    std::vector<int> weight;  // launches per bracketed pair
+    while (j < count) {
+        const bool replay = G > 0 && k % period == 0 && count - j >= G;
+        const int span = replay ? G : 1;
+        const bool timed = kernel_ms && (replay || (G == 0 && j % d.timing_every == 0));
+        if (timed) {
+            hipEvent_t* e = timing_event(L, 2 * pairs, &rc);
+            if (rc) return rc;
+            rc = hip_ok(hipEventRecord(*e, st), "bcg_loop_run: event record");
+            if (rc) return rc;
+        }
+        if (replay) {
+            if (!L->graph_exec) {
+                rc = build_graph(L);
+                if (rc) return rc;
+            }
+            rc = hip_ok(hipGraphLaunch(L->graph_exec, st), "bcg_loop_run: graph launch");
+        } else {
+            rc = launch_dplan(L, k, st);
+        }
+        if (rc) return rc;
+        if (timed) {
+            hipEvent_t* e = timing_event(L, 2 * pairs + 1, &rc);
+            if (rc) return rc;
+            rc = hip_ok(hipEventRecord(*e, st), "bcg_loop_run: event record");
+            if (rc) return rc;
+            weight.push_back(span);
+            ++pairs;
+        }
+        k += span;
+        j += span;
+        L->k_next = k;
+    }
+    if (kernel_ms) {
+        *kernel_ms = 0.0f;
+        if (pairs == 0) return BCG_OK;
+        rc = hip_ok(hipEventSynchronize(L->t_ev[2 * pairs - 1]), "bcg_loop_run: timing wait");
+        if (rc) return rc;
+        double total = 0.0;
+        long long launches = 0;
+        for (size_t q = 0; q < pairs; ++q) {
+            float ms = 0.0f;
+            rc = hip_ok(hipEventElapsedTime(&ms, L->t_ev[2 * q], L->t_ev[2 * q + 1]), "bcg_loop_run: elapsed");
+            if (rc) return rc;
+            total += ms;
+            launches += weight[q];
+        }
+        *kernel_ms = float(total / double(launches));
+    }
     return BCG_OK;
 }
 
@@ -43,16 +206,27 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
     if (n < 0 || nb < 1 || nb > BCG_MAX_BUCKETS || R < 0 || R > BCG_MAX_REGIONS)
         return fail(BCG_EINVAL, "bcg_loop_create: bad plan sizes");
     if (desc->rows < 1) return fail(BCG_EINVAL, "bcg_loop_create: rows < 1");
-    if (n > 0 && (!desc->start || !desc->host_slab || !desc->dev_slab))
+    if (n > 0 && (!desc->start || (!desc->device_plan && (!desc->host_slab || !desc->dev_slab))))
         return fail(BCG_EINVAL, "bcg_loop_create: NULL start/staging pointer");
     if (desc->step.n != n) return fail(BCG_ESHAPE, "bcg_loop_create: step.n != plan.n");
     if (desc->step.max_regions != R) return fail(BCG_EINVAL, "bcg_loop_create: step/plan max_regions differ");
     if (desc->replicas < 1 || (desc->replicas > 1 && desc->replica_stride <= 0))
         return fail(BCG_EINVAL, "bcg_loop_create: replicas must be >= 1 with a positive stride");
     if (desc->timing_every < 1) return fail(BCG_EINVAL, "bcg_loop_create: timing_every must be >= 1");
-    if (desc->upload_batch < 1 || desc->upload_batch > 64 || desc->rows % desc->upload_batch != 0)
+    if (desc->device_plan != 0 && desc->device_plan != 1)
+        return fail(BCG_EINVAL, "bcg_loop_create: device_plan must be 0 or 1");
+    if (!desc->device_plan &&
+        (desc->upload_batch < 1 || desc->upload_batch > 64 || desc->rows % desc->upload_batch != 0))
         return fail(BCG_EINVAL, "bcg_loop_create: upload_batch %d must be in [1, 64] and divide rows %d",
                     desc->upload_batch, desc->rows);
+    if (desc->device_plan) {
+        if (n > 0 && !desc->dev_steps) return fail(BCG_EINVAL, "bcg_loop_create: dev_steps is NULL");
+        if (desc->graph_launches < 0 || desc->graph_launches % (2 * desc->replicas) != 0)
+            return fail(BCG_EINVAL, "bcg_loop_create: graph_launches %d must be a non-negative multiple of 2*replicas",
+                        desc->graph_launches);
+    } else if (desc->graph_launches != 0) {
+        return fail(BCG_EINVAL, "bcg_loop_create: graph_launches needs device plans");
+    }
     auto* L = new bcg_loop();
     L->d = *desc;
     L->row_ev.assign(size_t(desc->rows), nullptr);
@@ -100,6 +274,27 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
         }
         L->d.plan.covered = L->covered.data();
     }
+    if (desc->device_plan) {
+        bcg_device_plan& dp = L->d.dplan;
+        dp.steps = desc->plan.steps;
+        dp.num_buckets = desc->plan.num_buckets;
+        dp.wrap = desc->wrap ? 1 : 0;
+        L->t0.resize(size_t(n));
+        for (int i = 0; i < n; ++i) {
+            long long t = desc->start[i];
+            if (desc->wrap && t >= 0) t %= desc->plan.steps;
+            L->t0[size_t(i)] = int32_t(t);
+        }
+        // Check the launch template once with the first launch's pointers.
+        dp.step_in = desc->dev_steps;
+        dp.step_out = desc->dev_steps + n;
+        int rc2 = check_dplan(L, "bcg_loop_create");
+        if (rc2 == BCG_OK) rc2 = reset_steps(L, nullptr);
+        if (rc2) {
+            bcg_loop_destroy(L);
+            return rc2;
+        }
+    }
     *out = L;
     return BCG_OK;
 }
@@ -114,6 +309,8 @@ extern "C" int bcg_loop_destroy(bcg_loop* L) {
     if (L->copy) (void)hipStreamDestroy(L->copy);
     for (auto e : L->t_ev)
         if (e) (void)hipEventDestroy(e);
+    if (L->graph_exec) (void)hipGraphExecDestroy(L->graph_exec);
+    if (L->graph) (void)hipGraphDestroy(L->graph);
     delete L;
     return BCG_OK;
 }
@@ -124,6 +321,7 @@ extern "C" int bcg_loop_run(bcg_loop* L, int k0, int count, void* stream, float*
     if (count < 0 || k0 < 0) return fail(BCG_EINVAL, "bcg_loop_run: negative k0/count");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bcg_loop_desc& d = L->d;
+    if (d.device_plan) return run_device(L, k0, count, st, kernel_ms);
     const int n = d.plan.n, steps = d.plan.steps, P = d.upload_batch;
     hipStream_t up = d.async_upload ? L->copy : st;
     const int every = d.timing_every;
@@ -161,8 +359,8 @@ extern "C" int bcg_loop_run(bcg_loop* L, int k0, int count, void* stream, float*
         for (int q = 0; q < m; ++q) {
             int32_t* h = h0 + size_t(q) * row_elems;
             for (int i = 0; i < n; ++i) {
-                long long t = (long long)d.start[i] + (k + q);
-                if (d.wrap) t %= steps;
+                long long t = (long long)d.start[i] + (k + q) / d.replicas;
+                if (d.wrap && t >= 0) t %= steps;
                 h[i] = int32_t(t);
             }
             bcg_plan_in pin = d.plan;

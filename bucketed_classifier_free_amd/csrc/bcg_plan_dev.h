@@ -1,0 +1,151 @@
+// The bucket plan of one step built on the GPU (SGLang BCG write-up, section
+// 2: bucket assignment; section 3: BucketPlan, per-bucket offsets and the
+// [uncond | cond] layout; ComfyUI guide "12 · Samplers, schedulers and CFG",
+// "the cfg = 1 optimisation").  Same definition as the host plan build:
+//   bucket = min(floor(t * nb / steps), nb - 1)       exact integer arithmetic
+//   scale  = override if given and not NaN, else bucket_cfg[bucket]
+//   uncond kept unless scale == 1 and the sample's conds cover the frame
+//   order  = active samples stably sorted by (bucket, sample)
+// Included by the .hip translation units only.
+#pragma once
+
+#include "bcg_device.h"
+
+namespace bcg {
+
+// Bucket, scale and uncond decision of sample i at an active step t.
+// t * nb < 2^20 * 2^10 fits 32 bits (both limits are checked on the host).
+__device__ __forceinline__ void dplan_sample(const StepParams& p, int i, int t, int& b, float& w,
+                                             bool& need_u) {
+    b = (int)(((uint32_t)t * (uint32_t)p.nb) / (uint32_t)p.steps);
+    b = b < p.nb - 1 ? b : p.nb - 1;
+    w = p.bucket_cfg[b];
+    if (p.cfg_override) {
+        const float o = p.cfg_override[i];
+        if (o == o) w = o;  // NaN = no override
+    }
+    const bool cov = p.covered ? p.covered[i] != 0 : true;
+    need_u = !(w == 1.0f && cov);
+}
+
+// The step index after this step: t + 1, modulo steps once non-negative
+// when wrapping (a finished slot restarts at step 0).
+__device__ __forceinline__ int dplan_next(const StepParams& p, int t) {
+    if (t == 0x7fffffff) return t;
+    const int nt = t + 1;
+    return (p.wrap && nt >= 0) ? nt % p.steps : nt;
+}
+
+// The full plan and the step advance, by one workgroup (blockDim >= 64,
+// a multiple of 64).  `sh` holds 2 * nb ints of LDS.
+//   pass 1 (all lanes): per sample, bucket/scale (or the inactive markers)
+//     and the step advance; per-bucket counts of the cond and uncond halves
+//     by LDS atomics;
+//   pass 2 (wavefront 0): exclusive prefix sums of the counts, 64 buckets at
+//     a time, which become the running write cursors of each bucket;
+//   pass 3 (wavefront 0): samples in index order, 64 at a time; the lanes of
+//     one bucket take consecutive slots in lane order (ballot + popcount), so
+//     the order within a bucket is the sample order.
+__device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh) {
+    const int n = p.n, nb = p.nb;
+    const int tid = (int)threadIdx.x, T = (int)blockDim.x;
+    const bool full = p.plan_bucket_id != nullptr;
+    int* cnt = sh;
+    int* ucnt = sh + nb;
+    if (full)
+        for (int b = tid; b < nb; b += T) {
+            cnt[b] = 0;
+            ucnt[b] = 0;
+        }
+    __syncthreads();
+    for (int i = tid; i < n; i += T) {
+        const int t = p.step_idx[i];
+        if (p.step_out) p.step_out[i] = dplan_next(p, t);
+        if (!full) continue;
+        if (t >= 0 && t < p.steps) {
+            int b;
+            float w;
+            bool need_u;
+            dplan_sample(p, i, t, b, w, need_u);
+            p.plan_bucket_id[i] = b;
+            p.plan_scale[i] = w;
+            atomicAdd(&cnt[b], 1);
+            if (need_u) atomicAdd(&ucnt[b], 1);
+        } else {
+            p.plan_bucket_id[i] = -1;
+            p.plan_scale[i] = 0.0f;
+            p.plan_uncond_row[i] = -1;
+            p.plan_cond_row[i] = -1;
+        }
+    }
+    if (!full) return;
+    __syncthreads();
+    if (tid >= 64) return;
+
+    int run = 0, urun = 0;
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+        const int b = b0 + tid;
+        const int c = b < nb ? cnt[b] : 0;
+        const int u = b < nb ? ucnt[b] : 0;
+        int ic = c, iu = u;  // inclusive scans over the 64 lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int xc = __shfl_up(ic, o, 64);
+            const int xu = __shfl_up(iu, o, 64);
+            if (tid >= o) {
+                ic += xc;
+                iu += xu;
+            }
+        }
+        if (b < nb) {
+            p.plan_bucket_count[b] = c;
+            p.plan_bucket_offset[b] = run + ic - c;
+            p.plan_uncond_offset[b] = urun + iu - u;
+            cnt[b] = run + ic - c;
+            ucnt[b] = urun + iu - u;
+        }
+        run += __shfl(ic, 63, 64);
+        urun += __shfl(iu, 63, 64);
+    }
+    if (tid == 0) {
+        p.plan_bucket_offset[nb] = run;
+        p.plan_uncond_offset[nb] = urun;
+        p.plan_totals[0] = run;
+        p.plan_totals[1] = urun;
+    }
+
+    const int m = urun;  // rows of the uncond half
+    const unsigned long long below = tid == 0 ? 0ull : (~0ull >> (64 - tid));
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + tid;
+        const int t = i < n ? p.step_idx[i] : -1;
+        const bool act = t >= 0 && t < p.steps;
+        int b = -1;
+        float w = 0.0f;
+        bool need_u = false;
+        if (act) dplan_sample(p, i, t, b, w, need_u);
+        unsigned long long rest = __ballot(act);
+        while (rest) {
+            const int leader = __ffsll(rest) - 1;
+            const int bl = __shfl(b, leader, 64);
+            const bool mine = act && b == bl;
+            const unsigned long long mm = __ballot(mine);
+            const unsigned long long mu = __ballot(mine && need_u);
+            const int cbase = cnt[bl], ubase = ucnt[bl];
+            if (mine) {
+                const int pos = cbase + __popcll(mm & below);
+                p.plan_order[pos] = i;
+                p.plan_cond_row[i] = m + pos;
+                p.plan_uncond_row[i] = need_u ? ubase + __popcll(mu & below) : -1;
+            }
+            if (tid == leader) {
+                cnt[bl] = cbase + __popcll(mm);
+                ucnt[bl] = ubase + __popcll(mu);
+            }
+            rest &= ~mm;
+        }
+    }
+    for (int j = run + tid; j < n; j += 64) p.plan_order[j] = -1;
+}
+
+}  // namespace bcg

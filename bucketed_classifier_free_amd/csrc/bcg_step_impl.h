@@ -36,6 +36,7 @@
 #pragma once
 
 #include "bcg_device.h"
+#include "bcg_plan_dev.h"
 
 namespace bcg {
 
@@ -331,11 +332,20 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, bool lane
 // vectors of one sample (vpt per lane, blockDim apart); its wavefronts do not
 // synchronise with each other.  When every sample is active the workgroup
 // index maps to the sample directly (the processing order is immaterial), so
-// the first latent loads wait on no other load.
+// the first latent loads wait on no other load.  With a device-built plan the
+// grid covers every sample (inactive ones exit at once) and one more
+// workgroup, the last, builds the step's full plan alongside the streaming.
 template <typename T, int V, int NR, bool INP, bool HEUN, typename TN = DefaultTune>
 __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
-    __shared__ float coef_all[4][2 * kSet];  // one slice per wavefront
-    float* coef = coef_all[threadIdx.x >> 6];
+    __shared__ union {
+        float coef[4][2 * kSet];               // one slice per wavefront
+        int plan[2 * BCG_MAX_DEVICE_BUCKETS];  // the plan workgroup's counters
+    } sh;
+    if ((int)blockIdx.x == p.plan_block) {
+        plan_workgroup(p, sh.plan);
+        return;
+    }
+    float* coef = sh.coef[threadIdx.x >> 6];
     const int j = blockIdx.x / p.tiles;
     const int tile = blockIdx.x - j * p.tiles;
     if (j >= p.n_active) return;
@@ -368,13 +378,19 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
                                   INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, C, p.HW);
     }
     const int t = p.step_idx[i];
-    if (t < 0 || t + 1 >= p.num_sigmas) return;
+    if (t < 0 || t >= p.t_end) return;
 
     const float sig = p.sigmas[t];
     const float sgn = p.sigmas[t + 1];
     StepScalars s;
-    s.w = p.scale[i];
-    const bool keep_u = p.uncond_row[i] >= 0;
+    bool keep_u;
+    if (p.dplan) {
+        int b;
+        dplan_sample(p, i, t, b, s.w, keep_u);
+    } else {
+        s.w = p.scale[i];
+        keep_u = p.uncond_row[i] >= 0;
+    }
     SampleRegions<NR> sr;
     sr.cnt = cnt;
     if constexpr (NR > 0) {
@@ -402,7 +418,8 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
 
 template <typename T, int V, int NR, typename TN = DefaultTune>
 hipError_t launch_nr(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
-    const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles)), blk((unsigned)block);
+    const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0))),
+        blk((unsigned)block);
     if (heun) {
         if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true, TN>), grid, blk, 0, st, p);
         else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true, TN>), grid, blk, 0, st, p);

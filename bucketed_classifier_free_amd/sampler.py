@@ -34,8 +34,9 @@ class GuidedSampler:
     """One batch of samples with per-sample progress and bucketed guidance.
 
     ``wrap`` (steady-state continuous batching): sample i is at step
-    (start_i + k) mod steps at launch k, so every launch is full; otherwise
-    sample i is active while start_i + k < steps.
+    (start_i + k) mod steps at launch k once start_i + k >= 0 (a finished
+    slot restarts at step 0); otherwise sample i is active while
+    0 <= start_i + k < steps.
     """
 
     def __init__(self, *, noise, mu_uncond, mu_cond, start_step, steps, num_buckets, curve,
@@ -89,6 +90,11 @@ class GuidedSampler:
             self.region_off = p.region_off.copy()
         else:
             self.d_region_box = self.d_region_count = self.d_region_strength = self.d_mu_region = None
+        # Device copies of the plan inputs, for plans built on the device.
+        self.d_table = f32(self.table)
+        self.d_override = None if self.override is None else f32(self.override)
+        self.d_covered = (None if self.covered is None else
+                          torch.from_numpy(self.covered.astype(np.int32)).to(dev))
 
     @classmethod
     def from_inputs(cls, inp, **kw):
@@ -118,7 +124,7 @@ class GuidedSampler:
     def step_indices(self, k: int) -> np.ndarray:
         t = self.start.astype(np.int64) + k
         if self.wrap:
-            t = t % self.steps
+            t = np.where(t >= 0, t % self.steps, t)
         return t.astype(np.int32)
 
     def plan(self, k: int):
@@ -173,6 +179,18 @@ class GuidedSampler:
         self.launch(d, p.n_active, x, x_out, stats, workspace, cache_hint)
         return p
 
+    def dplan_step(self, x, step_in, step_out=None, x_out=None, plan_out=None, cache_hint=0):
+        """One fused step whose plan is built on the device from ``step_in``
+        (device int32 [n]); ``step_out`` receives the next step indices."""
+        api.guided_step_dplan(x, x if x_out is None else x_out, self.d_sigmas, self.d_mu_u,
+                              self.d_mu_c, steps=self.steps, bucket_cfg=self.d_table,
+                              step_in=step_in, step_out=step_out, cfg_override=self.d_override,
+                              covered=self.d_covered, wrap=self.wrap, plan_out=plan_out,
+                              sampler=self.sampler, s2=self.s2, feather=self.feather,
+                              region_count=self.d_region_count, region_box=self.d_region_box,
+                              region_strength=self.d_region_strength, mu_region=self.d_mu_region,
+                              x_orig=self.d_x_orig, mask=self.d_mask, cache_hint=cache_hint)
+
     def run(self, x=None, launches=None, callback=None, cancel=None):
         """Whole loop from the initial latent; returns the final state.
 
@@ -192,19 +210,25 @@ class GuidedSampler:
     # ------------------------------------------------------------ native loop
 
     def native_loop(self, x, x_out=None, upload_batch=8, async_upload=False, cache_hint=None,
-                    timing_every=1):
+                    timing_every=1, device_plan=False, graph_launches=0, plan_outputs=True):
         """A C++ loop (bcg_loop_*) advancing ``x`` (in place unless x_out).
 
         ``x`` may also be [replicas, n, C, H, W]: launch k then advances
-        replica k mod replicas (independent batches served round-robin)."""
-        return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint, timing_every)
+        replica k mod replicas by one step of its own trajectory
+        (independent batches served round-robin).  ``device_plan`` builds
+        each step's plan on the device inside the step's launch (into
+        ``loop.plan_out`` when ``plan_outputs``); ``graph_launches`` > 0
+        replays a captured graph of that many launches."""
+        return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint, timing_every,
+                          device_plan, graph_launches, plan_outputs)
 
 
 class NativeLoop:
     """Owner of a bcg_loop handle and of the host/device arrays it points to."""
 
     def __init__(self, s: GuidedSampler, x, x_out=None, upload_batch=8, async_upload=False,
-                 cache_hint=None, timing_every=1):
+                 cache_hint=None, timing_every=1, device_plan=False, graph_launches=0,
+                 plan_outputs=True):
         n = s.n
         P = int(upload_batch)
         rows = 8 * P
@@ -217,8 +241,18 @@ class NativeLoop:
         stride = n * s.C * s.H * s.W * x.element_size()
         if cache_hint is None:  # several batches in rotation: stream them past the caches
             cache_hint = L.BCG_CACHE_STREAM if reps > 1 else L.BCG_CACHE_KEEP
-        self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
-        self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
+        if device_plan:
+            self.h_slab = self.d_slab = None
+            self.dev_steps = torch.empty((reps, 2, n), dtype=torch.int32, device=s.device)
+            self.plan_out = api.device_plan_arrays(n, s.nb, s.device) if plan_outputs else None
+            dplan = api.device_plan(s.steps, s.d_table, self.dev_steps[0, 0],
+                                    step_out=self.dev_steps[0, 1], cfg_override=s.d_override,
+                                    covered=s.d_covered, wrap=s.wrap, out=self.plan_out)
+        else:
+            self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
+            self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
+            self.dev_steps = self.plan_out = None
+            dplan = L.DevicePlan()
         keep = self._keep = []
 
         def npp(a, dt):
@@ -243,9 +277,10 @@ class NativeLoop:
                           ptr(s.d_region_box), ptr(s.d_region_strength), ptr(s.d_mu_region),
                           ptr(s.d_x_orig), ptr(s.d_mask), None, None, 0)
         self.desc = L.LoopDesc(plan, npp(s.start, np.int32), 1 if s.wrap else 0, rows,
-                               self.h_slab.data_ptr(), self.d_slab.data_ptr(), reps,
+                               api._ptr(self.h_slab), api._ptr(self.d_slab), reps,
                                stride if reps > 1 else 0, P, 1 if async_upload else 0,
-                               int(timing_every), step)
+                               int(timing_every), step, 1 if device_plan else 0,
+                               int(graph_launches), api._ptr(self.dev_steps), dplan)
         self.handle = ct.c_void_p()
         L.check(L.lib().bcg_loop_create(ct.byref(self.desc), ct.byref(self.handle)))
 

@@ -57,6 +57,8 @@ enum { BCG_CACHE_KEEP = 0, BCG_CACHE_STREAM = 1 };
 #define BCG_MAX_CHANNELS 64  /* latent channels */
 #define BCG_MAX_FEATHER 64   /* feather width in latent pixels */
 #define BCG_MAX_BUCKETS 4096
+#define BCG_MAX_DEVICE_BUCKETS 1024  /* buckets of a device-built plan */
+#define BCG_MAX_DEVICE_STEPS (1 << 20)  /* trajectory length of a device-built plan */
 
 /* Thread-local message describing the last failed call ("" if none). */
 const char* bcg_last_error(void);
@@ -173,8 +175,9 @@ int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out);
  *   Euler: x' = x + (sigma' - sigma)(x - pred)/sigma;  Heun adds a second
  *   evaluation at the Euler point and averages the slopes; x' = pred when
  *   sigma' = 0.
- * The evaluation order is a fixed sequence of fp32 operations (no fused
- * multiply-add); stores round to the storage dtype.
+ * The evaluation order is a fixed sequence of fp32 operations, with fused
+ * multiply-adds (one rounding) at fixed places; stores round to the storage
+ * dtype.
  *
  * x_out may equal x (in place); otherwise the two must not overlap.  Samples
  * not in order[0..n_active) are neither read nor written.  Entries of order
@@ -225,6 +228,76 @@ int guided_step(const bcg_step_args* args, void* stream);
 size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
 
 /*
+ * Device-built plans -- [B] section 2 (assign_bucket), section 3 (BucketPlan
+ * and the [uncond | cond] layout) and section 4 stage 3 (the plan of a step
+ * is fixed before that step's guidance runs), computed on the GPU from
+ * per-sample step indices held in device memory, so a step loop needs no
+ * host work and no upload per step (and can be captured in a graph).
+ *
+ * The plan is the one bcg_plan_build defines, bit for bit: for a sample with
+ * 0 <= t < steps, bucket = min(floor(t*num_buckets/steps), num_buckets-1),
+ * scale = cfg_override (if given and not NaN) else bucket_cfg[bucket], uncond
+ * skipped iff scale == 1.0f and covered; stable (bucket, i) order; offsets,
+ * rows and totals as in bcg_plan_out.  Coverage is not recomputed on the
+ * device: pass the flags bcg_plan_build returned in covered_out (they depend
+ * on the conds only).  Region boxes likewise come from bcg_plan_build.
+ *
+ * Step advance: if step_out is given, step_out[i] = t + 1, reduced modulo
+ * steps when wrap is set and t + 1 >= 0 (a sample with a negative index has
+ * not joined yet; with wrap, a sample that finished restarts at step 0:
+ * continuous batching with every slot refilled).  step_out must not overlap
+ * step_in; a loop alternates two buffers.
+ *
+ * The device arrays are not validated (a host plan build validates the same
+ * tables): bucket_cfg finite, cfg_override finite or NaN.
+ */
+typedef struct {
+    int32_t steps;                   /* trajectory length, [1, BCG_MAX_DEVICE_STEPS] */
+    int32_t num_buckets;             /* [1, BCG_MAX_DEVICE_BUCKETS] */
+    int32_t wrap;                    /* 0 | 1, see above */
+    const float* bucket_cfg;         /* device [num_buckets] */
+    const float* cfg_override;       /* device [n] or NULL; NaN = none */
+    const int32_t* covered;          /* device [n] coverage flags, or NULL = all covered
+                                        (required when the step has regions) */
+    const int32_t* step_in;          /* device [n] t_i of this step */
+    int32_t* step_out;               /* device [n] or NULL: the next step's t_i */
+    /* the full plan of this step, device arrays, all given or all NULL: */
+    int32_t* bucket_id;              /* [n] */
+    float* scale;                    /* [n] */
+    int32_t* uncond_row;             /* [n] */
+    int32_t* cond_row;               /* [n] */
+    int32_t* order;                  /* [n] (-1 past n_active) */
+    int32_t* bucket_count;           /* [num_buckets] */
+    int32_t* bucket_offset;          /* [num_buckets+1] */
+    int32_t* uncond_offset;          /* [num_buckets+1] */
+    int32_t* totals;                 /* [2]: n_active, n_uncond */
+} bcg_device_plan;
+
+/*
+ * bcg_plan_device -- the plan of one step for n samples, built by one
+ * workgroup on `stream` (and the step advance).  Needs the plan outputs or
+ * step_out (or both).
+ * Errors: BCG_EINVAL (sizes out of range, NULL table/step_in, outputs half
+ * given, nothing to write, step_out overlapping step_in), BCG_EHIP.
+ */
+int bcg_plan_device(int n, const bcg_device_plan* plan, void* stream);
+
+/*
+ * guided_step_dplan -- guided_step whose per-sample step index, scale and
+ * uncond decision come from a device-built plan, in the same launch: every
+ * sample with 0 <= step_in[i] < steps is advanced (the others are neither
+ * read nor written), and one extra workgroup of the launch writes the full
+ * plan (if requested) and step_out.  Results are bit-identical to
+ * guided_step with the host plan of the same step indices.
+ * args: as guided_step, except order, step_idx, scale and uncond_row must be
+ * NULL and n_active is ignored; stats are not available (they need the plan
+ * before the step); num_sigmas must be >= steps + 1; with regions
+ * (max_regions > 0), plan->covered is required.
+ * Errors: as guided_step and bcg_plan_device.
+ */
+int guided_step_dplan(const bcg_step_args* args, const bcg_device_plan* plan, void* stream);
+
+/*
  * latent_init -- [S] "deterministic noise", "disable_noise": the sampler
  * starts from the latent plus noise at the sample's first sigma,
  *   x_out[i] = latent[i] + noise[i] * sigmas[step_idx[i]]   (fp32, rounded on store)
@@ -265,48 +338,67 @@ int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void*
                const float* mask, int mask_per_sample, void* out, void* stream);
 
 /*
- * bcg_loop_* -- the sampler loop's per-step host work in native code: for
- * launches k = k0 .. k0+count-1, t_i = start[i] + k (mod steps when wrap is
- * set: steady-state continuous batching, every sample always active), the
- * bucket plan is built (bcg_plan_build) straight into pinned staging row
- * k mod rows, copied to the device row (hipMemcpyAsync, P rows per copy) and
- * one guided_step is launched with that row.  Every plan is built on the host
- * before its launch is queued; batching only merges the copies (a plan
- * depends on the step index, never on the state).  SGLang BCG write-up, section 4
- * stage 3: the plan is built by the scheduler before the launch and is
- * immutable while the step runs.  A staging row is rewritten only after its
- * previous copy has completed (an event per row).
+ * bcg_loop_* -- the sampler loop's per-step work in native code, for
+ * launches k = k0 .. k0+count-1.  Launch k advances replica r = k mod
+ * replicas (several independent batches served round-robin; 1 by default)
+ * by one step of its own trajectory: t_i = start[i] + floor(k / replicas),
+ * reduced modulo steps when wrap is set and t_i >= 0 (steady-state continuous
+ * batching: a finished slot restarts at step 0).
+ *
+ * Host plans (device_plan = 0): the bucket plan of each launch is built on
+ * the host (bcg_plan_build) straight into pinned staging row k mod rows,
+ * copied to the device row (hipMemcpyAsync, P rows per copy) and one
+ * guided_step is launched with that row.  Every plan is built before its
+ * launch is queued; batching only merges the copies (a plan depends on the
+ * step index, never on the state).  [B] section 4 stage 3: the plan is built
+ * by the scheduler before the launch and is immutable while the step runs.
+ * A staging row is rewritten only after its previous copy has completed.
+ * Row layout (4n int32): [step_idx | scale (float bits) | uncond_row | order].
+ *
+ * Device plans (device_plan = 1): each launch is one guided_step_dplan that
+ * builds the step's plan on the device (into dplan's plan outputs, if given)
+ * and advances the replica's step indices in dev_steps (two buffers per
+ * replica, alternating); no host work or copy per launch.  The indices are
+ * written from `start` at bcg_loop_create and again whenever a run starts at
+ * k0 = 0; otherwise k0 must continue the previous run.  With graph_launches
+ * G > 0 (a multiple of 2*replicas), runs of G launches starting at a multiple
+ * of 2*replicas are replays of one captured HIP graph (captured on first use
+ * on a stream of the loop's own).
  *
  * The descriptor is copied at create time; the arrays it points to (host plan
- * inputs, the staging rows, every device array of `step`) are owned by the
- * caller and must outlive the loop.  Row layout (4n int32):
- *   [step_idx | scale (float bits) | uncond_row | order].
- * step.order / step_idx / scale / uncond_row / n_active are ignored (filled
- * per launch).  With replicas > 1, launch k advances replica k mod replicas:
- * step.x and step.x_out are offset by (k mod replicas) * replica_stride bytes
- * (several independent batches served round-robin).  If kernel_ms is not
- * NULL, every timing_every-th guided_step launch is bracketed by HIP events
- * on `stream`, bcg_loop_run waits for the last one, and *kernel_ms receives
- * the mean duration of the bracketed launches (ms).
- * Errors: as bcg_plan_build and guided_step; BCG_EHIP for runtime failures.
+ * inputs, staging rows, dev_steps, every device array of `step` and `dplan`)
+ * are owned by the caller and must outlive the loop.  step.order / step_idx /
+ * scale / uncond_row / n_active are ignored (filled per launch); with
+ * replicas > 1, step.x and step.x_out are offset by r * replica_stride bytes.
+ * If kernel_ms is not NULL, every timing_every-th launch (each graph replay,
+ * in graph mode) is bracketed by HIP events on `stream`, bcg_loop_run waits
+ * for the last one, and *kernel_ms receives the mean time per bracketed
+ * launch (ms).
+ * Errors: as bcg_plan_build, guided_step and guided_step_dplan; BCG_EHIP.
  */
 typedef struct {
     bcg_plan_in plan;                /* plan.step_idx is ignored */
     const int32_t* start;            /* host [n] start step of each sample */
-    int32_t wrap;                    /* 1: t = (start + k) mod steps */
-    int32_t rows;                    /* staging rows, >= 1 */
-    int32_t* host_slab;              /* pinned host [rows][4n] */
-    int32_t* dev_slab;               /* device [rows][4n] */
+    int32_t wrap;                    /* 1: t reduced modulo steps once >= 0 */
+    int32_t rows;                    /* staging rows, >= 1 (host plans) */
+    int32_t* host_slab;              /* pinned host [rows][4n] (host plans) */
+    int32_t* dev_slab;               /* device [rows][4n] (host plans) */
     int32_t replicas;                /* >= 1 independent states of the batch */
     int64_t replica_stride;          /* bytes between replicas of x and x_out */
     int32_t upload_batch;            /* P in [1, 64]: plans of P consecutive launches are
                                         built, then uploaded with one copy; rows must
-                                        be a multiple of P */
+                                        be a multiple of P (host plans) */
     int32_t async_upload;            /* 1: uploads on the loop's own copy stream,
                                         overlapping earlier launches; 0: on `stream` */
     int32_t timing_every;            /* m >= 1: with kernel_ms, launches j with
                                         j % m == 0 are bracketed by events */
     bcg_step_args step;              /* launch template (replica 0) */
+    int32_t device_plan;             /* 0: host plans; 1: device plans */
+    int32_t graph_launches;          /* device plans: G >= 0, see above */
+    int32_t* dev_steps;              /* device plans: device [replicas][2][n] */
+    bcg_device_plan dplan;           /* device plans: template (steps, num_buckets and
+                                        wrap are taken from plan/wrap; step_in and
+                                        step_out are set per launch) */
 } bcg_loop_desc;
 
 typedef struct bcg_loop bcg_loop;

@@ -244,10 +244,10 @@ def test_native_loop_replicas_round_robin():
     torch.cuda.synchronize()
     loop.close()
     s2 = _sampler(inp)
-    for r in range(2):
+    for r in range(2):  # launches r, r+2, r+4 are replica r's steps 0, 1, 2
         y = s2.init_state()
-        for k in range(r, 6, 2):
-            s2.step(k, y)
+        for m in range(3):
+            s2.step(m, y)
         torch.cuda.synchronize()
         assert torch.equal(x[r], y)
 

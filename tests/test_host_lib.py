@@ -28,12 +28,12 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == 2
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 3
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -206,3 +206,74 @@ def test_plan_with_cached_coverage_equals_full_plan():
               "uncond_offset", "covered"):
         assert np.array_equal(getattr(full, k), getattr(fast, k)), k
     assert fast.n_active == full.n_active and fast.n_uncond == full.n_uncond
+
+
+def _fake(k):
+    """A non-NULL pointer value that validation accepts and nothing dereferences."""
+    return C.c_void_p(0x100000 * k)
+
+
+def test_device_plan_entry_points_validate_before_launch():
+    lib = L.lib()
+    d = L.DevicePlan(10, 4, 0, _fake(1), None, None, _fake(2), None)
+    assert lib.bcg_plan_device(3, C.byref(d), None) == L.BCG_EINVAL   # nothing to write
+    assert b"nothing" in lib.bcg_last_error()
+    assert lib.bcg_plan_device(0, C.byref(d), None) == L.BCG_OK       # no samples, no launch
+    d.step_out = _fake(2).value + 4                                  # overlaps step_in
+    assert lib.bcg_plan_device(3, C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlaps" in lib.bcg_last_error()
+    d.step_out = _fake(3)
+    d.bucket_id = _fake(4)                                           # outputs half given
+    assert lib.bcg_plan_device(3, C.byref(d), None) == L.BCG_EINVAL
+    d.bucket_id = None
+    for field, bad in (("steps", 0), ("steps", L.BCG_MAX_DEVICE_STEPS + 1),
+                       ("num_buckets", 0), ("num_buckets", L.BCG_MAX_DEVICE_BUCKETS + 1),
+                       ("wrap", 2)):
+        good = getattr(d, field)
+        setattr(d, field, bad)
+        assert lib.bcg_plan_device(3, C.byref(d), None) == L.BCG_EINVAL, field
+        setattr(d, field, good)
+    assert lib.bcg_plan_device(-1, C.byref(d), None) == L.BCG_ESHAPE
+
+    a = L.StepArgs()
+    a.n, a.C, a.H, a.W, a.num_sigmas, a.s2 = 2, 4, 8, 8, 11, 0.25
+    a.x = a.x_out = a.sigmas = a.mu_uncond = a.mu_cond = _fake(5)
+    assert lib.guided_step_dplan(C.byref(a), None, None) == L.BCG_EINVAL
+    a.scale = _fake(6)                                                # plan rows must be NULL
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"device plan" in lib.bcg_last_error()
+    a.scale = None
+    a.stats = _fake(7)
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    a.stats = None
+    a.num_sigmas = 10                                                 # < steps + 1
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    a.num_sigmas = 11
+    a.max_regions, a.region_count = 2, _fake(8)                       # regions need coverage
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"coverage" in lib.bcg_last_error()
+    a.max_regions, a.region_count = 0, None
+    a.n = 0                                                           # no samples, no launch
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_OK
+
+
+def test_loop_create_validates_device_plan_mode():
+    lib = L.lib()
+    start = np.zeros(2, np.int32)
+    table = np.float32([2.0, 1.5])
+    plan = L.PlanIn(2, 10, 2, 4, 8, 8, 0, table.ctypes.data, None, None, None, None, None, None)
+    step = L.StepArgs()
+    step.n, step.C, step.H, step.W, step.num_sigmas, step.s2 = 2, 4, 8, 8, 11, 0.25
+    d = L.LoopDesc(plan, start.ctypes.data, 0, 1, None, None, 1, 0, 1, 0, 1, step, 1, 3, None,
+                   L.DevicePlan(0, 0, 0, _fake(1)))
+    h = C.c_void_p()
+    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL   # dev_steps NULL
+    d.dev_steps = _fake(2)
+    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL   # 3 not a multiple of 2
+    assert b"graph_launches" in lib.bcg_last_error()
+    d.device_plan, d.graph_launches = 0, 4                               # graphs need device plans
+    d.host_slab = d.dev_slab = _fake(3)
+    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL
+    d.device_plan = 2
+    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL
+    assert not h.value
