@@ -5,8 +5,11 @@ One bench step = one sampler step of the large bf16 workload: 256 samples,
 latent 16x128x128 stored in bf16 (fp32 arithmetic), 2 feathered regional
 conds + uncond per sample, 8 guidance buckets on a linear 2.0 -> 1.2 curve,
 mixed per-sample progress over a 50-step log-linear Euler schedule.  Each
-step builds the bucket plan on the host, uploads it and runs one fused
-guided_step launch over every sample, all inside libbcg's native loop.
+step is one fused launch (guided_step_dplan) that builds the step's bucket
+plan on the device -- bucket ids, scales, uncond decisions, the stable
+(bucket, sample) order, offsets and rows -- and advances every sample, all
+inside libbcg's native loop (--plan host: the plan is built on the host and
+uploaded instead; --graph G: runs of G launches replay a captured graph).
 Progress is steady-state continuous batching (sample i at step
 (start_i + k) mod 50), so every launch is full and mixes all 8 buckets.
 With --replicas R > 1, R independent batches are served round-robin, which
@@ -31,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "latent element-steps/sec on 1 GPU + achieved HBM GB/s as % of peak"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_api.hip", "bcg_step_bf16.hip",
+KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_plan_dev.h", "bcg_api.hip", "bcg_step_bf16.hip",
                   "bcg_step_f32.hip", "bcg_step_bf16_nt.hip", "bcg_step_f32_nt.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "guided_step_large_bf16_traffic.json")
 
@@ -141,7 +144,12 @@ def main():
     ap.add_argument("--upload-batch", type=int, default=8)
     ap.add_argument("--async-upload", type=int, default=0)
     ap.add_argument("--timing-every", type=int, default=10,
-                    help="bracket every m-th launch with HIP events (kernel duration)")
+                    help="bracket every m-th launch with HIP events (kernel duration); "
+                         "with --graph, every replay is bracketed instead")
+    ap.add_argument("--plan", choices=("device", "host"), default="device")
+    ap.add_argument("--graph", type=int, default=40, metavar="G",
+                    help="device plans: replay a captured graph of G launches (a multiple of "
+                         "2 x replicas; 0 = direct launches)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the traffic record from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
@@ -175,8 +183,11 @@ def main():
     x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
     for r in range(R):
         s.init_state(x[r])
+    dev_plan = args.plan == "device"
+    G = args.graph - args.graph % (2 * R) if dev_plan else 0  # replays need a whole buffer period
     loop = s.native_loop(x if R > 1 else x[0], upload_batch=args.upload_batch,
-                         async_upload=bool(args.async_upload), timing_every=args.timing_every)
+                         async_upload=bool(args.async_upload), timing_every=args.timing_every,
+                         device_plan=dev_plan, graph_launches=G)
     loop.run(0, args.warmup)
     torch.cuda.synchronize()
     elems_per_launch = spec.n * spec.C * spec.H * spec.W  # every sample active (steady state)
@@ -187,6 +198,8 @@ def main():
     if not torch.isfinite(x.float()).all():
         raise RuntimeError("non-finite state after the timed steps")
 
+    if not launch_ms > 0:
+        raise RuntimeError("no launch was timed (use --steps >= --timing-every)")
     value = elems_per_launch * args.steps / wall
     bpe = bytes_per_element(spec)
     alg_bytes = bpe * elems_per_launch
@@ -213,16 +226,21 @@ def main():
         "config": {"workload": spec.name, "batch": spec.n, "latent": [spec.C, spec.H, spec.W],
                    "storage": spec.dtype, "sampler": spec.sampler, "schedule_steps": spec.steps,
                    "buckets": spec.num_buckets, "regions": spec.regions,
-                   "progress": "mixed, steady state", "replicas": R,
-                   "plan_upload_batch": args.upload_batch, "async_upload": bool(args.async_upload)},
+                   "progress": "mixed, steady state", "replicas": R, "plan": args.plan},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "kernel": {"name": "guided_step", "avg_launch_us": launch_ms * 1e3,
-                   "timed_launches": (args.steps + args.timing_every - 1) // args.timing_every,
+                   "timing": (f"HIP events around each replay of a {G}-launch graph"
+                              if G else
+                              f"HIP events around every {args.timing_every}th launch"),
                    "algorithmic_bytes_per_launch": alg_bytes, "bytes_per_element_step": bpe,
                    "element_steps_per_s_kernel_only": elems_per_launch / (launch_ms * 1e-3),
                    "kernel_hash": kernel_hash()},
     }
+    if dev_plan:
+        out["config"]["graph_launches"] = G
+    else:
+        out["config"].update(plan_upload_batch=args.upload_batch, async_upload=bool(args.async_upload))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     loop.close()

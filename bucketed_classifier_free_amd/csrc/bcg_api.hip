@@ -298,8 +298,9 @@ int grid_for(int64_t work, int block) {
 // ------------------------------------------------------------ device plan
 
 __global__ __launch_bounds__(256) void plan_kernel(const StepParams p) {
-    __shared__ int sh[2 * BCG_MAX_DEVICE_BUCKETS];
-    plan_workgroup(p, sh);
+    constexpr int kInts = 4 * BCG_MAX_DEVICE_BUCKETS;
+    __shared__ int sh[kInts];
+    plan_workgroup(p, sh, kInts);
 }
 
 // Checks a device plan for n samples; `step` says whether it drives a step.

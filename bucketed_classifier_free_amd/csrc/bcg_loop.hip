@@ -95,8 +95,8 @@ int launch_dplan(bcg_loop* L, int64_t k, hipStream_t st) {
     return guided_step_dplan(&a, &dp, st);
 }
 
-// Captures launches 0 .. G-1 (one period of the buffer pattern, repeated)
-// into a graph on the loop's own stream.
+// Captures launches 0 .. G-1 (whole periods of the buffer pattern) into a
+// graph on the loop's own stream; nothing runs until it is launched.
 int build_graph(bcg_loop* L) {
     const int G = L->d.graph_launches;
     int rc = hip_ok(hipStreamBeginCapture(L->copy, hipStreamCaptureModeThreadLocal), "bcg_loop: begin capture");
@@ -145,11 +145,11 @@ int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms)
     int64_t k = k0;
     int j = 0;
     size_t pairs = 0;
-    std::vector<int> weight;  // launches per bracketed pair
+    std::vector<int> weight;  // launches per bracketed pair, negative for direct launches
     while (j < count) {
-        const bool replay = G > 0 && k % period == 0 && count - j >= G;
+        const bool replay = L->graph_exec && k % period == 0 && count - j >= G;
         const int span = replay ? G : 1;
-        const bool timed = kernel_ms && (replay || (G == 0 && j % d.timing_every == 0));
+        const bool timed = kernel_ms && (replay || j % d.timing_every == 0);
         if (timed) {
             hipEvent_t* e = timing_event(L, 2 * pairs, &rc);
             if (rc) return rc;
@@ -157,10 +157,6 @@ int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms)
             if (rc) return rc;
         }
         if (replay) {
-            if (!L->graph_exec) {
-                rc = build_graph(L);
-                if (rc) return rc;
-            }
             rc = hip_ok(hipGraphLaunch(L->graph_exec, st), "bcg_loop_run: graph launch");
         } else {
             rc = launch_dplan(L, k, st);
@@ -171,7 +167,7 @@ int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms)
             if (rc) return rc;
             rc = hip_ok(hipEventRecord(*e, st), "bcg_loop_run: event record");
             if (rc) return rc;
-            weight.push_back(span);
+            weight.push_back(replay ? span : -1);
             ++pairs;
         }
         k += span;
@@ -183,14 +179,17 @@ int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms)
         if (pairs == 0) return BCG_OK;
         rc = hip_ok(hipEventSynchronize(L->t_ev[2 * pairs - 1]), "bcg_loop_run: timing wait");
         if (rc) return rc;
+        // graph replays when there were any, else the directly launched brackets
+        const bool any_replay = std::any_of(weight.begin(), weight.end(), [](int w) { return w > 0; });
         double total = 0.0;
         long long launches = 0;
         for (size_t q = 0; q < pairs; ++q) {
+            if (any_replay != (weight[q] > 0)) continue;
             float ms = 0.0f;
             rc = hip_ok(hipEventElapsedTime(&ms, L->t_ev[2 * q], L->t_ev[2 * q + 1]), "bcg_loop_run: elapsed");
             if (rc) return rc;
             total += ms;
-            launches += weight[q];
+            launches += weight[q] > 0 ? weight[q] : 1;
         }
         *kernel_ms = float(total / double(launches));
     }
@@ -290,6 +289,7 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
         dp.step_out = desc->dev_steps + n;
         int rc2 = check_dplan(L, "bcg_loop_create");
         if (rc2 == BCG_OK) rc2 = reset_steps(L, nullptr);
+        if (rc2 == BCG_OK && desc->graph_launches > 0 && n > 0) rc2 = build_graph(L);
         if (rc2) {
             bcg_loop_destroy(L);
             return rc2;

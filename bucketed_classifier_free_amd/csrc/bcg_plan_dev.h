@@ -37,7 +37,9 @@ __device__ __forceinline__ int dplan_next(const StepParams& p, int t) {
 }
 
 // The full plan and the step advance, by one workgroup (blockDim >= 64,
-// a multiple of 64).  `sh` holds 2 * nb ints of LDS.
+// a multiple of 64).  `sh` holds lds_ints >= 2 * nb ints of LDS; when
+// n <= lds_ints - 2 * nb it also keeps each sample's bucket and flags from
+// pass 1 for pass 3 (otherwise pass 3 derives them again).
 //   pass 1 (all lanes): per sample, bucket/scale (or the inactive markers)
 //     and the step advance; per-bucket counts of the cond and uncond halves
 //     by LDS atomics;
@@ -46,12 +48,14 @@ __device__ __forceinline__ int dplan_next(const StepParams& p, int t) {
 //   pass 3 (wavefront 0): samples in index order, 64 at a time; the lanes of
 //     one bucket take consecutive slots in lane order (ballot + popcount), so
 //     the order within a bucket is the sample order.
-__device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh) {
+__device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh, int lds_ints) {
     const int n = p.n, nb = p.nb;
     const int tid = (int)threadIdx.x, T = (int)blockDim.x;
     const bool full = p.plan_bucket_id != nullptr;
     int* cnt = sh;
     int* ucnt = sh + nb;
+    int* info = sh + 2 * nb;  // bucket | need_u << 16 | active << 17
+    const bool keep = n <= lds_ints - 2 * nb;
     if (full)
         for (int b = tid; b < nb; b += T) {
             cnt[b] = 0;
@@ -62,6 +66,7 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh) {
         const int t = p.step_idx[i];
         if (p.step_out) p.step_out[i] = dplan_next(p, t);
         if (!full) continue;
+        int v = 0;
         if (t >= 0 && t < p.steps) {
             int b;
             float w;
@@ -71,12 +76,14 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh) {
             p.plan_scale[i] = w;
             atomicAdd(&cnt[b], 1);
             if (need_u) atomicAdd(&ucnt[b], 1);
+            v = b | (need_u ? 1 << 16 : 0) | 1 << 17;
         } else {
             p.plan_bucket_id[i] = -1;
             p.plan_scale[i] = 0.0f;
             p.plan_uncond_row[i] = -1;
             p.plan_cond_row[i] = -1;
         }
+        if (keep) info[i] = v;
     }
     if (!full) return;
     __syncthreads();
@@ -118,12 +125,21 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh) {
     const unsigned long long below = tid == 0 ? 0ull : (~0ull >> (64 - tid));
     for (int i0 = 0; i0 < n; i0 += 64) {
         const int i = i0 + tid;
-        const int t = i < n ? p.step_idx[i] : -1;
-        const bool act = t >= 0 && t < p.steps;
+        bool act = false, need_u = false;
         int b = -1;
-        float w = 0.0f;
-        bool need_u = false;
-        if (act) dplan_sample(p, i, t, b, w, need_u);
+        if (i < n) {
+            if (keep) {
+                const int v = info[i];
+                act = (v >> 17) & 1;
+                need_u = (v >> 16) & 1;
+                b = act ? (v & 0xffff) : -1;
+            } else {
+                const int t = p.step_idx[i];
+                act = t >= 0 && t < p.steps;
+                float w;
+                if (act) dplan_sample(p, i, t, b, w, need_u);
+            }
+        }
         unsigned long long rest = __ballot(act);
         while (rest) {
             const int leader = __ffsll(rest) - 1;

@@ -42,6 +42,7 @@ namespace bcg {
 
 constexpr int kBranches = 2 + BCG_MAX_REGIONS;      // uncond, cond, regions
 constexpr int kSet = kBranches * BCG_MAX_CHANNELS;  // one sigma's coefficients
+constexpr int kPlanLds = 4 * 2 * kSet;              // ints of the coefficient LDS
 
 // Compile-time tuning of the streaming loop.
 template <int U_, bool NT_>
@@ -339,10 +340,10 @@ template <typename T, int V, int NR, bool INP, bool HEUN, typename TN = DefaultT
 __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     __shared__ union {
         float coef[4][2 * kSet];               // one slice per wavefront
-        int plan[2 * BCG_MAX_DEVICE_BUCKETS];  // the plan workgroup's counters
+        int plan[kPlanLds];                    // the plan workgroup's counters
     } sh;
     if ((int)blockIdx.x == p.plan_block) {
-        plan_workgroup(p, sh.plan);
+        plan_workgroup(p, sh.plan, kPlanLds);
         return;
     }
     float* coef = sh.coef[threadIdx.x >> 6];

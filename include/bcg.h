@@ -362,18 +362,19 @@ int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void*
  * written from `start` at bcg_loop_create and again whenever a run starts at
  * k0 = 0; otherwise k0 must continue the previous run.  With graph_launches
  * G > 0 (a multiple of 2*replicas), runs of G launches starting at a multiple
- * of 2*replicas are replays of one captured HIP graph (captured on first use
- * on a stream of the loop's own).
+ * of 2*replicas are replays of one HIP graph, captured at bcg_loop_create on
+ * a stream of the loop's own.
  *
  * The descriptor is copied at create time; the arrays it points to (host plan
  * inputs, staging rows, dev_steps, every device array of `step` and `dplan`)
  * are owned by the caller and must outlive the loop.  step.order / step_idx /
  * scale / uncond_row / n_active are ignored (filled per launch); with
  * replicas > 1, step.x and step.x_out are offset by r * replica_stride bytes.
- * If kernel_ms is not NULL, every timing_every-th launch (each graph replay,
- * in graph mode) is bracketed by HIP events on `stream`, bcg_loop_run waits
- * for the last one, and *kernel_ms receives the mean time per bracketed
- * launch (ms).
+ * If kernel_ms is not NULL, every graph replay and every timing_every-th
+ * direct launch is bracketed by HIP events on `stream`, bcg_loop_run waits
+ * for the last one, and *kernel_ms receives the mean time per launch (ms)
+ * inside the replays, or inside the bracketed direct launches if the run had
+ * no replay.
  * Errors: as bcg_plan_build, guided_step and guided_step_dplan; BCG_EHIP.
  */
 typedef struct {
