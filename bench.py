@@ -83,6 +83,50 @@ def cpu_baseline(inp, seconds: float):
                       f"{len(os.sched_getaffinity(0))} cores available), {dt:.1f} s"}
 
 
+def _oracle_worker(job):
+    """One process of the parallel oracle baseline: its own copy of the seeded
+    inputs, the float64 step on its share of the samples for `seconds`."""
+    import dataclasses
+    import numpy as np
+    import workloads as W
+    from oracle import definition as D
+    name, nb, idx, seconds = job
+    sp = W.config(name)
+    if nb:
+        sp = dataclasses.replace(sp, num_buckets=nb)
+    inp = W.make_inputs(sp)
+    sig, table, cov = D.run_setup(inp)
+    x = D.init_latent(inp, sig, sp.dtype)
+    t = inp.start_step.astype(np.int64)
+    plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+    elems = done = 0
+    t0 = time.perf_counter()
+    q = 0
+    while time.perf_counter() - t0 < seconds:
+        i = idx[q % len(idx)]
+        ti = int(t[i])
+        D.step(x[i], float(sig[ti]), float(sig[ti + 1]), float(plan["scale"][i]),
+               D.sample_params(inp, i), sp.sampler)
+        elems += sp.C * sp.H * sp.W
+        done += 1
+        q += 1
+    return elems, done, time.perf_counter() - t0
+
+
+def cpu_parallel(spec, nb, seconds: float, workers: int):
+    """The same oracle step sharded over `workers` fresh processes (samples dealt
+    round-robin), started before this process touches the GPU."""
+    import multiprocessing as mp
+    jobs = [(spec.name, nb, list(range(w, spec.n, workers)), seconds) for w in range(workers)]
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    elems = sum(r[0] for r in res)
+    rate = sum(r[0] / r[2] for r in res)
+    return {"value": rate, "unit": "element-steps/s", "cores": workers, "kind": "oracle",
+            "sample": f"{sum(r[1] for r in res)} sample-steps of {spec.name} over {workers} processes "
+                      f"(float64 NumPy definition, one thread each), {seconds:.0f} s each, {elems} element-steps"}
+
+
 def copy_probe(mib: int, iters: int):
     """Plain device copy of a known size (counter scale reference)."""
     import torch
@@ -131,6 +175,47 @@ def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
             "bytes_per_launch": f * 1024 * rf + w * 1024 * rw}
 
 
+def trajectory(inp, args):
+    """Whole trajectories end to end: latent init and every step of the
+    schedule (device plans, the steps replayed from one captured graph, one
+    batch in place), counting the active samples of each launch only."""
+    import numpy as np
+    import torch
+    from bucketed_classifier_free_amd import GuidedSampler
+    spec = inp.spec
+    s = GuidedSampler.from_inputs(inp)
+    x = s.alloc_state()
+    starts = inp.start_step.astype(np.int64)
+    launches = int(spec.steps - starts.min())
+    G = launches - launches % 2  # one graph replay per trajectory (a whole buffer period)
+    loop = s.native_loop(x, device_plan=True, graph_launches=G)
+    t = starts[:, None] + np.arange(launches)[None, :]
+    elems = int(((t >= 0) & (t < spec.steps)).sum()) * spec.C * spec.H * spec.W
+    reps = max(1, args.steps // launches)
+    for _ in range(2):  # warm-up trajectories
+        s.init_state(x)
+        loop.run(0, launches)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        s.init_state(x)
+        loop.run(0, launches)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    if not torch.isfinite(x.float()).all():
+        raise RuntimeError("non-finite state after the trajectories")
+    loop.close()
+    print(json.dumps({
+        "metric": "full-trajectory latent element-steps/sec on 1 GPU (init + every step, active samples only)",
+        "value": elems / wall, "unit": "element-steps/s", "n_gpus": 1, "trajectories": reps,
+        "ms_per_trajectory": wall * 1e3, "launches": launches, "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": spec.name, "batch": spec.n, "latent": [spec.C, spec.H, spec.W],
+                   "storage": spec.dtype, "sampler": spec.sampler, "schedule_steps": spec.steps,
+                   "buckets": spec.num_buckets, "regions": spec.regions, "inpaint": spec.inpaint,
+                   "plan": "device", "graph_launches": G}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +224,12 @@ def main():
     ap.add_argument("--workload", default="large_bf16")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-workers", type=int, default=-1,
+                    help="processes of the parallel oracle baseline (-1: the affinity cores, at most 16; 0: off)")
+    ap.add_argument("--buckets", type=int, default=0, help="override the workload's bucket count")
+    ap.add_argument("--trajectory", action="store_true",
+                    help="time whole trajectories (latent init + every step, active samples only) "
+                         "instead of the steady state")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--upload-batch", type=int, default=8)
@@ -165,10 +256,25 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
+    import workloads as W
+
+    spec = W.config(args.workload)
+    if args.buckets:
+        spec = dataclasses.replace(spec, num_buckets=args.buckets)
+    inp = W.make_inputs(spec) if not args.copy_probe else None
+    cpu = None
+    if not args.no_cpu_baseline and not args.copy_probe and not args.trajectory:
+        # the oracle legs run before anything here touches the GPU
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+        workers = args.cpu_workers if args.cpu_workers >= 0 else min(16, len(os.sched_getaffinity(0)))
+        if workers > 1:
+            cpu["parallel"] = cpu_parallel(spec, args.buckets, min(args.cpu_seconds, 10.0), workers)
+
     import numpy as np
     import torch
 
-    import workloads as W
     from bucketed_classifier_free_amd import GuidedSampler, load
 
     load()
@@ -176,8 +282,9 @@ def main():
         copy_probe(args.copy_probe, 50)
         return
     torch.cuda.set_device(0)
-    spec = W.config(args.workload)
-    inp = W.make_inputs(spec)
+    if args.trajectory:
+        trajectory(inp, args)
+        return
     s = GuidedSampler.from_inputs(inp, wrap=True)
     R = max(1, args.replicas)
     x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
@@ -241,8 +348,8 @@ def main():
         out["config"]["graph_launches"] = G
     else:
         out["config"].update(plan_upload_batch=args.upload_batch, async_upload=bool(args.async_upload))
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     loop.close()
     print(json.dumps(out), flush=True)
 

@@ -62,7 +62,8 @@ int check_dplan(bcg_loop* L, const char* who) {
     return BCG_OK;
 }
 
-// Writes the initial step indices into buffer 0 of every replica.
+// Writes the initial step indices into buffer 0 of every replica, in order on
+// `st` (the source is the loop's own host copy, which never changes).
 int reset_steps(bcg_loop* L, hipStream_t st) {
     const int n = L->d.plan.n;
     for (int r = 0; r < L->d.replicas && n > 0; ++r) {
@@ -72,7 +73,7 @@ int reset_steps(bcg_loop* L, hipStream_t st) {
         if (rc) return rc;
     }
     L->k_next = 0;
-    return hip_ok(hipStreamSynchronize(st), "bcg_loop: step index upload");
+    return BCG_OK;
 }
 
 // Launch k of a device-plan loop (replica k mod R, its own launch k / R).
@@ -289,6 +290,7 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
         dp.step_out = desc->dev_steps + n;
         int rc2 = check_dplan(L, "bcg_loop_create");
         if (rc2 == BCG_OK) rc2 = reset_steps(L, nullptr);
+        if (rc2 == BCG_OK) rc2 = hip_ok(hipStreamSynchronize(nullptr), "bcg_loop_create: step index upload");
         if (rc2 == BCG_OK && desc->graph_launches > 0 && n > 0) rc2 = build_graph(L);
         if (rc2) {
             bcg_loop_destroy(L);

@@ -45,9 +45,11 @@ __device__ __forceinline__ int dplan_next(const StepParams& p, int t) {
 //     by LDS atomics;
 //   pass 2 (wavefront 0): exclusive prefix sums of the counts, 64 buckets at
 //     a time, which become the running write cursors of each bucket;
-//   pass 3 (wavefront 0): samples in index order, 64 at a time; the lanes of
-//     one bucket take consecutive slots in lane order (ballot + popcount), so
-//     the order within a bucket is the sample order.
+//   pass 3 (wavefront 0): samples in index order, 64 at a time; each lane
+//     finds the lanes of its own bucket with one ballot per bit of the bucket
+//     id, and the lanes of one bucket take consecutive slots in lane order
+//     (popcount of the lanes below), so the order within a bucket is the
+//     sample order; the bucket's lowest lane then advances its cursors.
 __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh, int lds_ints) {
     const int n = p.n, nb = p.nb;
     const int tid = (int)threadIdx.x, T = (int)blockDim.x;
@@ -123,16 +125,17 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh, int
 
     const int m = urun;  // rows of the uncond half
     const unsigned long long below = tid == 0 ? 0ull : (~0ull >> (64 - tid));
+    const int kbits = nb > 1 ? 32 - __clz(nb - 1) : 0;  // bits of a bucket id
     for (int i0 = 0; i0 < n; i0 += 64) {
         const int i = i0 + tid;
         bool act = false, need_u = false;
-        int b = -1;
+        int b = 0;
         if (i < n) {
             if (keep) {
                 const int v = info[i];
                 act = (v >> 17) & 1;
                 need_u = (v >> 16) & 1;
-                b = act ? (v & 0xffff) : -1;
+                b = v & 0xffff;
             } else {
                 const int t = p.step_idx[i];
                 act = t >= 0 && t < p.steps;
@@ -140,25 +143,24 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh, int
                 if (act) dplan_sample(p, i, t, b, w, need_u);
             }
         }
-        unsigned long long rest = __ballot(act);
-        while (rest) {
-            const int leader = __ffsll(rest) - 1;
-            const int bl = __shfl(b, leader, 64);
-            const bool mine = act && b == bl;
-            const unsigned long long mm = __ballot(mine);
-            const unsigned long long mu = __ballot(mine && need_u);
-            const int cbase = cnt[bl], ubase = ucnt[bl];
-            if (mine) {
-                const int pos = cbase + __popcll(mm & below);
-                p.plan_order[pos] = i;
-                p.plan_cond_row[i] = m + pos;
-                p.plan_uncond_row[i] = need_u ? ubase + __popcll(mu & below) : -1;
+        // Lanes holding the same bucket, one ballot per bit of the id.
+        unsigned long long same = __ballot(act);
+        for (int k = 0; k < kbits; ++k) {
+            const bool bit = (b >> k) & 1;
+            const unsigned long long ones = __ballot(act && bit);
+            same &= bit ? ones : ~ones;
+        }
+        const unsigned long long needs = same & __ballot(act && need_u);
+        if (act) {
+            const int cbase = cnt[b], ubase = ucnt[b];
+            const int pos = cbase + __popcll(same & below);
+            p.plan_order[pos] = i;
+            p.plan_cond_row[i] = m + pos;
+            p.plan_uncond_row[i] = need_u ? ubase + __popcll(needs & below) : -1;
+            if ((same & below) == 0) {  // the bucket's first lane advances its cursors
+                cnt[b] = cbase + __popcll(same);
+                ucnt[b] = ubase + __popcll(needs);
             }
-            if (tid == leader) {
-                cnt[bl] = cbase + __popcll(mm);
-                ucnt[bl] = ubase + __popcll(mu);
-            }
-            rest &= ~mm;
         }
     }
     for (int j = run + tid; j < n; j += 64) p.plan_order[j] = -1;
