@@ -402,6 +402,63 @@ def step(x, sigma: float, sigma_next: float, w: float, prm: SampleParams,
     raise ValueError(sampler)
 
 
+# --------------------------------------------------------------------------
+# Materialised branches: the model's outputs given as rows of the plan layout
+# --------------------------------------------------------------------------
+
+
+def rows_pred(rows, plan, i: int, w: float, x_orig=None, mask=None):
+    """The guided, blended prediction of sample i from materialised branch
+    outputs.
+
+    ``rows`` is one model evaluation's output in the layout the plan defines
+    (write-up section 3, [uncond_0..uncond_m | cond_0..cond_n]): sample i's
+    cond prediction is row cond_row[i], its uncond prediction row
+    uncond_row[i] (absent when the uncond branch was skipped).  Reading: the
+    cond row already holds the regionally accumulated cond ("12 ·
+    Samplers...", "calc_cond_batch()"; area_accumulate builds it, with the
+    uncond prediction where no region has weight), so with w == 1 the
+    prediction is that row itself and no uncond row is used (section "the
+    cfg = 1 optimisation").
+    """
+    c = np.asarray(rows[plan["cond_row"][i]], np.float64)
+    if w == 1.0:
+        pred = c.copy()
+    else:
+        pred = cfg_combine(np.asarray(rows[plan["uncond_row"][i]], np.float64), c, w)
+    if mask is not None:
+        pred = inpaint_blend(pred, x_orig, mask)
+    return pred
+
+
+def euler_from_pred(x, P, sigma: float, sigma_next: float):
+    """Euler step given the prediction P at (x, sigma) (Karras et al. 2022,
+    Alg. 1); the step to sigma' = 0 lands on P."""
+    if sigma_next == 0.0:
+        return np.array(P, np.float64, copy=True)
+    return x + (sigma_next - sigma) * (x - P) / sigma
+
+
+def heun_predict(x, P, sigma: float, sigma_next: float):
+    """First call of a Heun step whose model evaluations are materialised:
+    returns (d, x~) with d = (x - P)/sigma and x~ = x + h d, the point the
+    model is evaluated at next.  On the last step (sigma' = 0) the step is
+    Euler's and lands on P: returns (None, P)."""
+    if sigma_next == 0.0:
+        return None, np.array(P, np.float64, copy=True)
+    d = (x - P) / sigma
+    return d, x + (sigma_next - sigma) * d
+
+
+def heun_correct(x, d, P2, sigma: float, sigma_next: float):
+    """Second call: with P2 the prediction at (x~, sigma'), the slopes are
+    averaged, x' = x + h (d + d')/2, d' = (x~ - P2)/sigma'."""
+    h = sigma_next - sigma
+    xt = x + h * d
+    d2 = (xt - P2) / sigma_next
+    return x + h * (d + d2) / 2.0
+
+
 def norm_stats(x, sigma: float, w: float, prm: SampleParams, need_uncond: bool):
     """Per-sample norm check before/after guidance.
 

@@ -41,6 +41,15 @@ per element:
     Heun:  d = (x - pb)*i; xt = fma(h, d, x); pb2 = P'(xt);
            d2 = (xt - pb2)*i'; x' = fma(d + d2, hh, x)
     store float32, or round to bf16 (nearest, ties to even)
+
+materialised branches (rows of the plan layout, storage dtype, read as float32):
+    pred = c                                 (scale == 1)
+         = fma(w, c - u, u)                  (otherwise)
+    pb = fma(m, pred, om*xo)  (inpaint)  else pred
+    Euler: sigma' == 0: x' = pb, else x' = fma(x - pb, q, x)
+    Heun, first call: d = (x - pb)*i; xt = fma(h, d, x); store d (float32) and
+           xt (storage dtype); sigma' == 0: xt = pb and no d
+    Heun, second call: xt = fma(h, d, x); d2 = (xt - pb2)*i'; x' = fma(d + d2, hh, x)
 """
 from __future__ import annotations
 
@@ -261,3 +270,50 @@ def mask_blend32(a, b, mask, dtype):
     m = np.asarray(mask, np.float32)
     om = f32(1) - m
     return _store(fma32(m, np.asarray(a, np.float32), om * np.asarray(b, np.float32)), dtype)
+
+
+def rows_pred32(c, u, w, mask=None, x_orig=None):
+    """Mode M prediction from materialised cond/uncond rows (float32 values)."""
+    c = np.asarray(c, np.float32)
+    w = f32(w)
+    if w == f32(1):
+        pred = c.copy()
+    else:
+        u = np.asarray(u, np.float32)
+        pred = fma32(w, c - u, u)
+    if mask is not None:
+        m = np.asarray(mask, np.float32)[None]
+        om = f32(1) - m
+        pred = fma32(m, pred, om * np.asarray(x_orig, np.float32))
+    return np.asarray(pred, np.float32)
+
+
+def rows_euler32(x, pb, sigma, sigma_next):
+    x = np.asarray(x, np.float32)
+    sigma, sigma_next = f32(sigma), f32(sigma_next)
+    if sigma_next == f32(0):
+        return np.asarray(pb, np.float32).copy()
+    q = (sigma_next - sigma) / sigma
+    return fma32(x - pb, q, x)
+
+
+def rows_heun_predict32(x, pb, sigma, sigma_next):
+    """Returns (d float32 or None, x~ float32, unstored)."""
+    x = np.asarray(x, np.float32)
+    sigma, sigma_next = f32(sigma), f32(sigma_next)
+    if sigma_next == f32(0):
+        return None, np.asarray(pb, np.float32).copy()
+    h = sigma_next - sigma
+    d = (x - pb) * (f32(1) / sigma)
+    return d.astype(np.float32), fma32(h, d, x)
+
+
+def rows_heun_correct32(x, d, pb2, sigma, sigma_next):
+    x = np.asarray(x, np.float32)
+    sigma, sigma_next = f32(sigma), f32(sigma_next)
+    h = sigma_next - sigma
+    i2 = f32(1) / sigma_next
+    hh = h * f32(0.5)
+    xt = fma32(h, d, x)
+    d2 = (xt - pb2) * i2
+    return fma32(d + d2, hh, x)

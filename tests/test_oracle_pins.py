@@ -495,3 +495,135 @@ def test_fma32_identities():
     assert np.array_equal(M.fma32(np.float32(0), x, y), y)
     assert np.array_equal(M.fma32(np.float32(1), x, np.float32(0)), x)
     assert np.array_equal(M.fma32(x, np.float32(2), np.float32(0)), x * np.float32(2))
+
+
+# ---------------------------------------------------------------- materialised branches
+
+def _rows_case(sampler="euler", seed=3):
+    sp = W.small_spec(n=5, C=3, H=12, W=20, regions=2, inpaint=True, steps=6, num_buckets=3,
+                      sampler=sampler, feather=3, seed=seed)
+    inp = W.make_inputs(sp)
+    inp.cfg_override[:] = [np.nan, 1.0, 0.0, 1.0, np.nan]
+    inp.region_count[3] = 0  # a sample without regions
+    sig, table, cov = D.run_setup(inp)
+    x = D.init_latent(inp, sig, "f32").astype(np.float64)
+    return inp, sig, table, cov, x
+
+
+def _stand_in_rows(inp, plan, xs, sigmas):
+    """One evaluation of the stand-in per branch, laid out as the plan says:
+    uncond rows (kept samples) then cond rows; sample i at xs[i], sigmas[i]."""
+    n = inp.spec.n
+    rows = np.full((plan["n_uncond"] + plan["n_active"],) + xs.shape[1:], np.nan)
+    for i in range(n):
+        if plan["bucket_id"][i] < 0:
+            continue
+        prm = D.sample_params(inp, i)
+        u = D.denoise(xs[i], sigmas[i], prm.mu_u, prm.s2)
+        if prm.regions:
+            preds = [D.denoise(xs[i], sigmas[i], mr, prm.s2) for _, _, mr in prm.regions]
+            c = D.regional_cond(preds, prm.weights, u)
+        else:
+            c = D.denoise(xs[i], sigmas[i], prm.mu_c, prm.s2)
+        rows[plan["cond_row"][i]] = c
+        if plan["uncond_row"][i] >= 0:
+            rows[plan["uncond_row"][i]] = u
+    return rows
+
+
+@pytest.mark.parametrize("k", [0, 3, 5])
+def test_rows_euler_equals_inline_step(k):
+    """Branch outputs laid out as the plan says, then combine + blend + Euler,
+    equal the inline definition of the step (a different code path)."""
+    inp, sig, table, cov, x = _rows_case("euler")
+    sp = inp.spec
+    t = inp.start_step.astype(np.int64) + k
+    plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+    act = [i for i in range(sp.n) if plan["bucket_id"][i] >= 0]
+    assert act
+    if k == 0:
+        assert plan["n_uncond"] < plan["n_active"]  # some uncond rows are compacted away
+    rows = _stand_in_rows(inp, plan, x, {i: float(sig[t[i]]) for i in act})
+    for i in act:
+        prm = D.sample_params(inp, i)
+        s0, s1 = float(sig[t[i]]), float(sig[t[i] + 1])
+        P = D.rows_pred(rows, plan, i, float(plan["scale"][i]), prm.x_orig, prm.mask)
+        got = D.euler_from_pred(x[i], P, s0, s1)
+        want = D.step(x[i], s0, s1, float(plan["scale"][i]), prm, "euler")
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), i
+
+
+@pytest.mark.parametrize("k", [0, 2, 5])
+def test_rows_heun_two_calls_equal_inline_step(k):
+    """Heun as two calls (predictor stores d and x~; the model runs at x~;
+    corrector) equals the inline Heun step, including the last step."""
+    inp, sig, table, cov, x = _rows_case("heun")
+    sp = inp.spec
+    t = inp.start_step.astype(np.int64) + k
+    plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+    act = [i for i in range(sp.n) if plan["bucket_id"][i] >= 0]
+    rows = _stand_in_rows(inp, plan, x, {i: float(sig[t[i]]) for i in act})
+    xt = x.copy()
+    ds = {}
+    for i in act:
+        prm = D.sample_params(inp, i)
+        P = D.rows_pred(rows, plan, i, float(plan["scale"][i]), prm.x_orig, prm.mask)
+        ds[i], xt[i] = D.heun_predict(x[i], P, float(sig[t[i]]), float(sig[t[i] + 1]))
+    rows2 = _stand_in_rows(inp, plan, xt, {i: float(sig[t[i] + 1]) for i in act})
+    for i in act:
+        prm = D.sample_params(inp, i)
+        s0, s1 = float(sig[t[i]]), float(sig[t[i] + 1])
+        want = D.step(x[i], s0, s1, float(plan["scale"][i]), prm, "heun")
+        if ds[i] is None:
+            got = xt[i]  # last step: the predictor's output is final
+            assert s1 == 0.0
+        else:
+            P2 = D.rows_pred(rows2, plan, i, float(plan["scale"][i]), prm.x_orig, prm.mask)
+            got = D.heun_correct(x[i], ds[i], P2, s0, s1)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), i
+
+
+def test_rows_scale_one_reads_no_uncond_row():
+    inp, sig, table, cov, x = _rows_case("euler")
+    sp = inp.spec
+    plan = D.build_plan(inp.start_step.astype(np.int64), sp.steps, sp.num_buckets, table,
+                        inp.cfg_override, cov)
+    rows = _stand_in_rows(inp, plan, x, {i: float(sig[inp.start_step[i]]) for i in range(sp.n)})
+    for i in range(sp.n):
+        if plan["bucket_id"][i] < 0 or plan["scale"][i] != np.float32(1):
+            continue
+        poisoned = rows.copy()
+        poisoned[:plan["n_uncond"]] = np.nan  # every uncond row
+        got = D.rows_pred(poisoned, plan, i, 1.0)
+        assert np.array_equal(got, rows[plan["cond_row"][i]])
+
+
+def test_rows_mirror_within_tolerance_and_exact_cases():
+    rng = np.random.default_rng(11)
+    C, H, Wd = 3, 8, 16
+    for trial in range(20):
+        x = rng.standard_normal((C, H, Wd)).astype(np.float32) * 3
+        c = rng.standard_normal((C, H, Wd)).astype(np.float32)
+        u = rng.standard_normal((C, H, Wd)).astype(np.float32)
+        xo = rng.standard_normal((C, H, Wd)).astype(np.float32)
+        m = (rng.random((H, Wd)) < 0.5).astype(np.float32)
+        w = [0.0, 1.0, 2.5, 7.0][trial % 4]
+        s0, s1 = np.float32(rng.uniform(0.5, 10)), np.float32(rng.uniform(0.05, 0.4))
+        pm = M.rows_pred32(c, u, w, m, xo)
+        pd = D.inpaint_blend(D.cfg_combine(u.astype(np.float64), c.astype(np.float64), w), xo, m)
+        assert np.allclose(pm, pd, rtol=0, atol=1e-5 * max(1.0, np.abs(pd).max()))
+        e_m = M.rows_euler32(x, pm, s0, s1)
+        e_d = D.euler_from_pred(x.astype(np.float64), pm.astype(np.float64), float(s0), float(s1))
+        assert np.abs(e_m - e_d).max() <= 1e-5 * np.abs(e_d).max()
+        d_m, xt_m = M.rows_heun_predict32(x, pm, s0, s1)
+        d_d, xt_d = D.heun_predict(x.astype(np.float64), pm.astype(np.float64), float(s0), float(s1))
+        assert np.abs(xt_m - xt_d).max() <= 1e-5 * np.abs(xt_d).max()
+        h_m = M.rows_heun_correct32(x, d_m, c, s0, s1)
+        h_d = D.heun_correct(x.astype(np.float64), d_d, c.astype(np.float64), float(s0), float(s1))
+        assert np.abs(h_m - h_d).max() <= 1e-5 * np.abs(h_d).max()
+    # exact cases: scale 1 takes c itself, mask 0 takes the original latent,
+    # sigma' = 0 lands on the prediction
+    assert np.array_equal(M.rows_pred32(c, u * np.nan, 1.0), c)
+    assert np.array_equal(M.rows_pred32(c, u, 3.0, np.zeros((H, Wd), np.float32), xo), xo)
+    assert np.array_equal(M.rows_euler32(x, c, s0, 0.0), c)
+    assert M.rows_heun_predict32(x, c, s0, 0.0)[0] is None
