@@ -13,6 +13,7 @@ BCG_F32, BCG_BF16 = 0, 1
 BCG_EULER, BCG_HEUN = 0, 1
 BCG_SCHED_LOGLINEAR = 0
 BCG_CACHE_KEEP, BCG_CACHE_STREAM = 0, 1
+BCG_PHASE = {"euler": 0, "heun_predict": 1, "heun_correct": 2}
 BCG_CURVE = {"const": 0, "linear": 1, "front_high": 2}
 BCG_MAX_REGIONS = 4
 BCG_MAX_CHANNELS = 64
@@ -24,7 +25,7 @@ ABI_VERSION = 3
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "bucket_table",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
-           "area_accumulate", "mask_blend", "bcg_plan_device", "guided_step_dplan",
+           "area_accumulate", "mask_blend", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
            "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy"]
 
 vp, i32p, i64p, f32p, f64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64),
@@ -57,6 +58,15 @@ class StepArgs(C.Structure):
                 ("region_count", vp), ("region_box", vp), ("region_strength", vp),
                 ("mu_region", vp), ("x_orig", vp), ("mask", vp), ("stats", vp),
                 ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+class RowsArgs(C.Structure):
+    _fields_ = [("n", C.c_int32), ("C", C.c_int32), ("H", C.c_int32), ("W", C.c_int32),
+                ("dtype", C.c_int32), ("phase", C.c_int32), ("n_active", C.c_int32),
+                ("num_sigmas", C.c_int32), ("rows", C.c_int32), ("mask_per_sample", C.c_int32),
+                ("cache_hint", C.c_int32), ("x", vp), ("x_out", vp), ("d", vp), ("x_tilde", vp),
+                ("pred", vp), ("sigmas", vp), ("order", vp), ("step_idx", vp), ("scale", vp),
+                ("uncond_row", vp), ("cond_row", vp), ("x_orig", vp), ("mask", vp)]
 
 
 class DevicePlan(C.Structure):
@@ -95,6 +105,7 @@ def lib():
         L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
         L.guided_step.argtypes = [C.POINTER(StepArgs), vp]
         L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]
+        L.guided_step_rows.argtypes = [C.POINTER(RowsArgs), vp]
         L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_workspace_size.argtypes = [C.c_int] * 5
         L.guided_step_workspace_size.restype = C.c_size_t

@@ -219,6 +219,49 @@ def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond,
     L.check(L.lib().guided_step(ct.byref(a), _stream(stream)))
 
 
+def guided_step_rows(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
+                     n_active: int, phase: str = "euler", d=None, x_tilde=None, x_orig=None,
+                     mask=None, cache_hint: int = 0, stream=None):
+    """The guided update from materialised branch predictions ``pred``
+    [rows, C, H, W] in the plan's [uncond | cond] layout (see include/bcg.h);
+    ``phase`` is "euler", "heun_predict" (writes ``d`` and x~ to x_out) or
+    "heun_correct" (reads ``d`` and, for last steps, ``x_tilde``)."""
+    _dev(x, "x")
+    if x.dim() != 4 or x.dtype not in _DT:
+        raise ValueError("x must be [n, C, H, W] float32 or bfloat16")
+    n, Cc, H, W = x.shape
+    _dev(x_out, "x_out", x.dtype, x.shape)
+    _dev(pred, "pred", x.dtype)
+    if pred.dim() != 4 or tuple(pred.shape[1:]) != (Cc, H, W):
+        raise ValueError("pred must be [rows, C, H, W]")
+    _dev(sigmas, "sigmas", torch.float32)
+    _dev(order, "order", torch.int32)
+    if order.numel() < n_active:
+        raise ValueError("order shorter than n_active")
+    for t, nm, dt in ((step_idx, "step_idx", torch.int32), (scale, "scale", torch.float32),
+                      (uncond_row, "uncond_row", torch.int32), (cond_row, "cond_row", torch.int32)):
+        _dev(t, nm, dt)
+        if t.numel() < n:
+            raise ValueError(f"{nm}: needs {n} entries")
+    if phase not in L.BCG_PHASE:
+        raise ValueError(f"unknown phase {phase!r}")
+    _dev(d, "d", torch.float32, x.shape, allow_none=True)
+    _dev(x_tilde, "x_tilde", x.dtype, x.shape, allow_none=True)
+    mps = 0
+    if x_orig is not None or mask is not None:
+        _dev(x_orig, "x_orig", x.dtype, x.shape)
+        _dev(mask, "mask", torch.float32)
+        if tuple(mask.shape) == (n, 1, H, W):
+            mps = 1
+        elif tuple(mask.shape) != (1, 1, H, W):
+            raise ValueError(f"mask: shape {tuple(mask.shape)} is neither [n,1,H,W] nor [1,1,H,W]")
+    a = L.RowsArgs(n, Cc, H, W, _DT[x.dtype], L.BCG_PHASE[phase], int(n_active), sigmas.numel(),
+                   pred.shape[0], mps, int(cache_hint), _ptr(x), _ptr(x_out), _ptr(d),
+                   _ptr(x_tilde), _ptr(pred), _ptr(sigmas), _ptr(order), _ptr(step_idx),
+                   _ptr(scale), _ptr(uncond_row), _ptr(cond_row), _ptr(x_orig), _ptr(mask))
+    L.check(L.lib().guided_step_rows(ct.byref(a), _stream(stream)))
+
+
 # ---------------------------------------------------------------- device plans
 
 _PLAN_KEYS = ("bucket_id", "scale", "uncond_row", "cond_row", "order", "bucket_count",

@@ -8,47 +8,12 @@
 #include "bcg_common.h"
 #include "bcg_device.h"
 #include "bcg_plan_dev.h"
+#include "bcg_launch.h"
 
 using bcg::fail;
 
 namespace bcg {
 namespace {
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-size_t elem_size(int dtype) { return dtype == BCG_BF16 ? 2 : 4; }
-
-// Two byte ranges overlap without being the same range.
-bool partial_overlap(const void* a, const void* b, size_t bytes) {
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    if (x == y) return false;
-    return x < y + bytes && y < x + bytes;
-}
-
-int hip_status(hipError_t e, const char* what) {
-    if (e != hipSuccess) return fail(BCG_EHIP, "%s: %s", what, hipGetErrorString(e));
-    return BCG_OK;
-}
-
-// Launch shape of the fused step: workgroups of `block` lanes, each lane
-// taking `vpt` vectors.  Large batches get about one resident round of
-// workgroups (4 per CU on 256 CUs) with vpt > 1, so the per-workgroup set-up
-// is amortised and no partial second round is left; small batches shrink the
-// workgroup so the grid still spreads over the CUs.
-struct LaunchShape {
-    int block, vpt;
-};
-LaunchShape pick_shape(int64_t samples, int64_t nvec) {
-    constexpr int64_t kResident = 256 * 4;
-    int bs = 256, vpt = 1;
-    auto blocks = [&](int b, int v) { return samples * ((nvec + (int64_t)b * v - 1) / ((int64_t)b * v)); };
-    if (blocks(bs, vpt) > kResident * 3 / 2) {
-        while (vpt < 8 && blocks(bs, vpt) > kResident * 3 / 2) vpt *= 2;
-    } else {
-        while (bs > 64 && blocks(bs, vpt) < kResident) bs /= 2;
-    }
-    return {bs, vpt};
-}
 
 // ------------------------------------------------------------ norm stats
 
@@ -502,6 +467,71 @@ extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
     p.plan_block = 0;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), p);
     return hip_status(hipGetLastError(), "bcg_plan_device: launch");
+}
+
+extern "C" int guided_step_rows(const bcg_rows_args* a, void* stream) {
+    bcg::clear_error();
+    const char* who = "guided_step_rows";
+    if (!a) return fail(BCG_EINVAL, "%s: args is NULL", who);
+    if (a->n < 0 || a->C < 1 || a->H < 1 || a->W < 1)
+        return fail(BCG_ESHAPE, "%s: bad shape n=%d C=%d H=%d W=%d", who, a->n, a->C, a->H, a->W);
+    const int64_t HW = (int64_t)a->H * a->W;
+    if (HW > (int64_t(1) << 30) || (int64_t)a->C * HW > (int64_t(1) << 36))
+        return fail(BCG_ESHAPE, "%s: C*H*W too large", who);
+    if (a->dtype != BCG_F32 && a->dtype != BCG_BF16) return fail(BCG_EDTYPE, "%s: unknown dtype %d", who, a->dtype);
+    if (a->phase != BCG_PHASE_EULER && a->phase != BCG_PHASE_HEUN_PREDICT && a->phase != BCG_PHASE_HEUN_CORRECT)
+        return fail(BCG_EINVAL, "%s: unknown phase %d", who, a->phase);
+    if (a->n_active < 0 || a->n_active > a->n) return fail(BCG_EINVAL, "%s: n_active %d not in [0, n]", who, a->n_active);
+    if (a->num_sigmas < 2) return fail(BCG_EINVAL, "%s: num_sigmas %d < 2", who, a->num_sigmas);
+    if (a->rows < 0) return fail(BCG_EINVAL, "%s: rows %d < 0", who, a->rows);
+    if (a->mask_per_sample != 0 && a->mask_per_sample != 1)
+        return fail(BCG_EINVAL, "%s: mask_per_sample must be 0 or 1", who);
+    if (a->cache_hint != BCG_CACHE_KEEP && a->cache_hint != BCG_CACHE_STREAM)
+        return fail(BCG_EINVAL, "%s: unknown cache_hint %d", who, a->cache_hint);
+    if (a->n_active == 0) return BCG_OK;
+    if (!a->x || !a->x_out || !a->pred || !a->sigmas || !a->order || !a->step_idx || !a->scale ||
+        !a->uncond_row || !a->cond_row)
+        return fail(BCG_EINVAL, "%s: NULL device pointer", who);
+    const bool heun = a->phase != BCG_PHASE_EULER;
+    if (heun && !a->d) return fail(BCG_EINVAL, "%s: Heun phases need d", who);
+    if (a->phase == BCG_PHASE_HEUN_CORRECT && !a->x_tilde) return fail(BCG_EINVAL, "%s: the corrector needs x_tilde", who);
+    if ((a->x_orig == nullptr) != (a->mask == nullptr))
+        return fail(BCG_EINVAL, "%s: x_orig and mask must be given together", who);
+    const size_t es = elem_size(a->dtype);
+    const size_t bytes = (size_t)a->n * a->C * HW * es;
+    const size_t pbytes = (size_t)a->rows * a->C * HW * es;
+    if (partial_overlap(a->x, a->x_out, bytes)) return fail(BCG_EINVAL, "%s: x and x_out partially overlap", who);
+    if (any_overlap(a->pred, pbytes, a->x_out, bytes)) return fail(BCG_EINVAL, "%s: pred overlaps x_out", who);
+    if (heun && any_overlap(a->d, (size_t)a->n * a->C * HW * 4, a->x_out, bytes))
+        return fail(BCG_EINVAL, "%s: d overlaps x_out", who);
+    if (a->x_tilde && a->phase == BCG_PHASE_HEUN_CORRECT && partial_overlap(a->x_tilde, a->x_out, bytes))
+        return fail(BCG_EINVAL, "%s: x_tilde and x_out partially overlap", who);
+    const bool inpaint = a->x_orig != nullptr;
+    const int VV = a->dtype == BCG_BF16 ? 8 : 4;
+    const bool vec = HW % VV == 0 && aligned16(a->x) && aligned16(a->x_out) && aligned16(a->pred) &&
+                     (!inpaint || (aligned16(a->x_orig) && aligned16(a->mask))) && (!heun || aligned16(a->d)) &&
+                     (a->phase != BCG_PHASE_HEUN_CORRECT || aligned16(a->x_tilde));
+    RowsParams p{};
+    p.n = a->n; p.C = a->C; p.n_active = a->n_active; p.num_sigmas = a->num_sigmas; p.rows = a->rows;
+    p.phase = a->phase;
+    p.HW = HW;
+    p.nvec = (int)(vec ? HW / VV : HW);
+    p.identity = a->n_active == a->n ? 1 : 0;
+    p.mask_stride = a->mask_per_sample ? (int)HW : 0;
+    p.x = a->x; p.x_out = a->x_out; p.d = heun ? a->d : nullptr;
+    p.x_tilde = a->phase == BCG_PHASE_HEUN_CORRECT ? a->x_tilde : nullptr;
+    p.pred = a->pred; p.sigmas = a->sigmas; p.order = a->order; p.step_idx = a->step_idx;
+    p.scale = a->scale; p.uncond_row = a->uncond_row; p.cond_row = a->cond_row;
+    p.x_orig = a->x_orig; p.mask = a->mask;
+    const LaunchShape shape = pick_shape(p.n_active, p.nvec);
+    p.vpt = shape.vpt;
+    p.tiles = (int)(((int64_t)p.nvec + (int64_t)shape.block * p.vpt - 1) / ((int64_t)shape.block * p.vpt));
+    if ((int64_t)p.n_active * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
+    const bool nt = a->cache_hint == BCG_CACHE_STREAM;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = a->dtype == BCG_BF16 ? launch_rows_bf16(p, vec, inpaint, nt, shape.block, st)
+                                              : launch_rows_f32(p, vec, inpaint, nt, shape.block, st);
+    return hip_status(e, "guided_step_rows: launch");
 }
 
 extern "C" int latent_init(int n, int C, int H, int W, int dtype, const float* noise, const void* latent,

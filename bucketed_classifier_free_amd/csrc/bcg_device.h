@@ -181,6 +181,33 @@ struct StepParams {
     int32_t* plan_totals;
 };
 
+// Launch parameter block of the materialised-branch step (device pointers).
+struct RowsParams {
+    int n, C, n_active, num_sigmas, rows;
+    int phase;                    // BCG_PHASE_*
+    int nvec, tiles, vpt;
+    int identity;                 // every sample active: workgroup j takes sample j
+    int mask_stride;              // HW if per-sample mask, else 0
+    int64_t HW;
+    const void* x;
+    void* x_out;
+    float* d;
+    const void* x_tilde;
+    const void* pred;
+    const float* sigmas;
+    const int32_t* order;
+    const int32_t* step_idx;
+    const float* scale;
+    const int32_t* uncond_row;
+    const int32_t* cond_row;
+    const void* x_orig;
+    const float* mask;
+};
+
+// Launchers of the materialised-branch step (bcg_rows_*.hip).
+hipError_t launch_rows_f32(const RowsParams& p, bool vec, bool inpaint, bool nt, int block, hipStream_t s);
+hipError_t launch_rows_bf16(const RowsParams& p, bool vec, bool inpaint, bool nt, int block, hipStream_t s);
+
 // Launchers, one per storage dtype and cache behaviour (bcg_step_*.hip).
 // `vec` selects the 128-bit path; the streaming launchers take only it.
 hipError_t launch_step_f32(const StepParams& p, bool vec, bool heun, bool inpaint, int block,

@@ -52,6 +52,8 @@ enum { BCG_CURVE_CONST = 0, BCG_CURVE_LINEAR = 1, BCG_CURVE_FRONT_HIGH = 2 };
  *                     again before the caches turn over (several batches served
  *                     round-robin, each larger than the cache) */
 enum { BCG_CACHE_KEEP = 0, BCG_CACHE_STREAM = 1 };
+/* Calls of a step whose branch outputs come from a model (guided_step_rows). */
+enum { BCG_PHASE_EULER = 0, BCG_PHASE_HEUN_PREDICT = 1, BCG_PHASE_HEUN_CORRECT = 2 };
 
 #define BCG_MAX_REGIONS 4    /* regional conds per sample */
 #define BCG_MAX_CHANNELS 64  /* latent channels */
@@ -296,6 +298,65 @@ int bcg_plan_device(int n, const bcg_device_plan* plan, void* stream);
  * Errors: as guided_step and bcg_plan_device.
  */
 int guided_step_dplan(const bcg_step_args* args, const bcg_device_plan* plan, void* stream);
+
+/*
+ * guided_step_rows -- the guided update when the branch predictions are
+ * materialised by a model: [B] section 3 (the [uncond_0..uncond_m |
+ * cond_0..cond_n] batch layout and its per-bucket split and combine, with the
+ * uncond half compacted to the samples that need it), [S] "core of CFG",
+ * "the cfg = 1 optimisation", "inpaint and mask", "one step may call the
+ * model more than steps times" (Heun evaluates the model twice per step).
+ *
+ * pred holds one model evaluation in the plan's layout: sample i's cond
+ * prediction is row cond_row[i], its uncond prediction row uncond_row[i]
+ * (bcg_plan_build gives both).  The cond row is the final cond (regional
+ * conds accumulated into it beforehand, e.g. by area_accumulate with the
+ * uncond prediction as fallback).  For i = order[j], j < n_active,
+ * t = step_idx[i], sigma = sigmas[t], sigma' = sigmas[t+1], w = scale[i]:
+ *   P = C if w == 1 (no uncond row is read), else U + w (C - U); inpaint:
+ *   P = m P + (1 - m) x_orig
+ *   BCG_PHASE_EULER: x_out = x + (sigma' - sigma)(x - P)/sigma; P if sigma' = 0
+ *   BCG_PHASE_HEUN_PREDICT: d = (x - P)/sigma (fp32, to `d`), x_out = x~ =
+ *     x + (sigma' - sigma) d, the point the model is evaluated at next; on a
+ *     last step (sigma' = 0) x_out = P and d is not written
+ *   BCG_PHASE_HEUN_CORRECT (pred evaluated at x~, sigma'): x~ = x + h d is
+ *     recomputed in fp32 from `d`, d' = (x~ - P)/sigma', x_out = x + h (d + d')/2;
+ *     on a last step x_out = x_tilde (the predictor's output)
+ * The fp32 evaluation order has fused multiply-adds at fixed places (as
+ * guided_step); stores round to the storage dtype.
+ * Samples whose rows are missing (cond_row outside [0, rows), or w != 1 with
+ * uncond_row outside [0, rows)), or whose t or t+1 falls outside
+ * [0, num_sigmas), are neither read nor written.  x_out may equal x; d,
+ * pred, x_tilde must not overlap x_out.
+ * Errors: BCG_ESHAPE, BCG_EDTYPE, BCG_EINVAL (NULL pointer, unknown phase,
+ * d missing for Heun, x_tilde missing for the corrector, inpaint arrays half
+ * given, overlaps), BCG_EHIP.
+ */
+typedef struct {
+    int32_t n, C, H, W;              /* n >= 0, C >= 1, H, W >= 1 */
+    int32_t dtype;                   /* BCG_F32 | BCG_BF16: x, x_out, x_tilde, pred, x_orig */
+    int32_t phase;                   /* BCG_PHASE_* */
+    int32_t n_active;                /* entries of order[] to process, [0, n] */
+    int32_t num_sigmas;              /* length of sigmas */
+    int32_t rows;                    /* rows of pred (n_uncond + n_active of the plan) */
+    int32_t mask_per_sample;         /* 1: mask [n,1,H,W]; 0: [1,1,H,W] */
+    int32_t cache_hint;              /* BCG_CACHE_KEEP | BCG_CACHE_STREAM */
+    const void* x;                   /* device [n,C,H,W], the state at sigma */
+    void* x_out;                     /* device [n,C,H,W] */
+    float* d;                        /* device fp32 [n,C,H,W] (Heun phases), else NULL */
+    const void* x_tilde;             /* device [n,C,H,W] (corrector), else NULL */
+    const void* pred;                /* device [rows,C,H,W] */
+    const float* sigmas;             /* device [num_sigmas] */
+    const int32_t* order;            /* device [n_active] */
+    const int32_t* step_idx;         /* device [n] */
+    const float* scale;              /* device [n] */
+    const int32_t* uncond_row;       /* device [n] */
+    const int32_t* cond_row;         /* device [n] */
+    const void* x_orig;              /* device [n,C,H,W] or NULL (no inpaint) */
+    const float* mask;               /* device mask or NULL (with x_orig) */
+} bcg_rows_args;
+
+int guided_step_rows(const bcg_rows_args* args, void* stream);
 
 /*
  * latent_init -- [S] "deterministic noise", "disable_noise": the sampler

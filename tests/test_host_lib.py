@@ -28,7 +28,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -277,3 +277,33 @@ def test_loop_create_validates_device_plan_mode():
     d.device_plan = 2
     assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL
     assert not h.value
+
+
+def test_rows_entry_point_validates_before_launch():
+    lib = L.lib()
+    a = L.RowsArgs()
+    a.n, a.C, a.H, a.W, a.num_sigmas, a.rows, a.n_active = 2, 4, 8, 8, 11, 4, 2
+    a.phase = 7
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EINVAL
+    a.phase = L.BCG_PHASE["euler"]
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EINVAL       # NULL pointers
+    for f, k in (("x", 1), ("x_out", 2), ("pred", 3), ("sigmas", 4), ("order", 5), ("step_idx", 6),
+                 ("scale", 7), ("uncond_row", 8), ("cond_row", 9)):
+        setattr(a, f, _fake(k))
+    a.pred = _fake(2).value + 64                                        # overlaps x_out
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EINVAL
+    assert b"overlaps" in lib.bcg_last_error()
+    a.pred = _fake(3)
+    a.phase = L.BCG_PHASE["heun_predict"]                               # needs d
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EINVAL
+    a.d = _fake(10)
+    a.phase = L.BCG_PHASE["heun_correct"]                               # needs x_tilde
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EINVAL
+    a.x_orig = _fake(11)                                                # half an inpaint
+    a.x_tilde = _fake(12)
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EINVAL
+    a.x_orig = None
+    a.dtype = 5
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EDTYPE
+    a.dtype, a.n_active = 0, 0                                          # nothing to do, no launch
+    assert lib.guided_step_rows(C.byref(a), None) == L.BCG_OK
