@@ -175,6 +175,110 @@ def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
             "bytes_per_launch": f * 1024 * rf + w * 1024 * rw}
 
 
+def rows_bench(inp, args):
+    """Steady state of the materialised-branch update: per step, the plan of
+    one batch is built on the device (bcg_plan_device) and guided_step_rows
+    reads that batch's model-output rows in the plan's layout.  The rows are
+    synthetic and resident (one buffer per batch and evaluation: no model
+    runs here); the uncond rows of samples whose uncond branch is skipped
+    are neither produced nor read."""
+    import numpy as np
+    import torch
+    from bucketed_classifier_free_amd import GuidedSampler, api
+    from bucketed_classifier_free_amd import _lib as L
+    spec = inp.spec
+    s = GuidedSampler.from_inputs(inp, wrap=True)
+    n, R = spec.n, max(1, args.replicas)
+    heun = spec.sampler == "heun"
+    evals = 2 if heun else 1
+    x = torch.empty((R, n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
+    for r in range(R):
+        s.init_state(x[r])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(spec.seed)
+    pred = torch.randn((R, evals, 2 * n, spec.C, spec.H, spec.W), generator=g, device="cuda").to(s.tdtype)
+    dbuf = torch.empty((n, spec.C, spec.H, spec.W), dtype=torch.float32, device="cuda") if heun else None
+    xt = torch.empty_like(x[0]) if heun else None
+    steps_state = torch.empty((R, 2, n), dtype=torch.int32, device="cuda")
+    steps_state[:, 0] = torch.from_numpy(s.step_indices(0)).cuda()
+    plans = [api.device_plan_arrays(n, s.nb) for _ in range(R)]
+    hint = L.BCG_CACHE_STREAM if R > 1 else L.BCG_CACHE_KEEP
+    opt = dict(x_orig=s.d_x_orig, mask=s.d_mask, cache_hint=hint)
+
+    def step(k):
+        r, m = k % R, k // R
+        st_in, st_out = steps_state[r, m & 1], steps_state[r, (m + 1) & 1]
+        pl = plans[r]
+        api.bcg_plan_device(s.steps, s.d_table, st_in, step_out=st_out, cfg_override=s.d_override,
+                            covered=s.d_covered, wrap=True, out=pl)
+        rows = dict(order=pl["order"], step_idx=st_in, scale=pl["scale"],
+                    uncond_row=pl["uncond_row"], cond_row=pl["cond_row"])
+        if heun:
+            api.guided_step_rows(x[r], xt, pred[r, 0], s.d_sigmas, n_active=n, phase="heun_predict",
+                                 d=dbuf, **rows, **opt)
+            api.guided_step_rows(x[r], x[r], pred[r, 1], s.d_sigmas, n_active=n, phase="heun_correct",
+                                 d=dbuf, x_tilde=xt, **rows, **opt)
+        else:
+            api.guided_step_rows(x[r], x[r], pred[r, 0], s.d_sigmas, n_active=n, phase="euler",
+                                 **rows, **opt)
+
+    # Whole steps (plan + update) replayed from a graph of G steps: G is a
+    # multiple of the step-buffer period 2R, so replays continue the sequence.
+    G = 2 * R * max(1, -(-16 // (2 * R)))
+    for k in range(G):
+        step(k)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(G):
+            step(k)
+    reps = max(1, args.steps // G)
+    for _ in range(max(1, args.warmup // G)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not torch.isfinite(x.float()).all():
+        raise RuntimeError("non-finite state after the timed steps")
+    nsteps = reps * G
+    step_ms = e0.elapsed_time(e1) / nsteps
+    # bytes per element-step: x read + x' write, the cond row, the uncond rows of the samples
+    # that keep them (the skip set does not change between steps here), per evaluation
+    p0 = s.plan(0)
+    keep = p0.n_uncond / max(p0.n_active, 1)
+    es = 2 if spec.dtype == "bf16" else 4
+    if heun:  # predictor: x, C, U, writes x~ and d; corrector: x, d, C, U, writes x'
+        bpe = (es + es + keep * es + es + 4) + (es + 4 + es + keep * es + es)
+    else:
+        bpe = es + es + keep * es + es
+    if spec.inpaint:
+        bpe += evals * (es + 4.0 / spec.C)
+    elems = n * spec.C * spec.H * spec.W
+    achieved = bpe * elems / (step_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "materialised-branch guided update, latent element-steps/sec on 1 GPU",
+        "value": elems * nsteps / wall, "unit": "element-steps/s", "n_gpus": 1,
+        "steps": nsteps, "warmup": G * max(1, args.warmup // G), "ms_per_step": wall * 1e3 / nsteps,
+        "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": spec.name, "batch": n, "latent": [spec.C, spec.H, spec.W],
+                   "storage": spec.dtype, "sampler": spec.sampler, "replicas": R,
+                   "uncond_rows_kept": keep, "plan": "device (its own launch before the update)",
+                   "graph_steps": G},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "kernel": {"name": "guided_step_rows", "calls_per_step": evals,
+                   "avg_us_per_step": step_ms * 1e3, "bytes_per_element_step": bpe,
+                   "timing": "events around the graph replays; a step is the plan launch plus "
+                             "the update launch(es), so achieved GB/s is a lower bound for the update"}}),
+        flush=True)
+
+
 def trajectory(inp, args):
     """Whole trajectories end to end: latent init and every step of the
     schedule (device plans, the steps replayed from one captured graph, one
@@ -227,6 +331,9 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=-1,
                     help="processes of the parallel oracle baseline (-1: the affinity cores, at most 16; 0: off)")
     ap.add_argument("--buckets", type=int, default=0, help="override the workload's bucket count")
+    ap.add_argument("--rows", action="store_true",
+                    help="materialised branches: time guided_step_rows on model-output rows laid out "
+                         "by a device-built plan (both Heun calls for a Heun workload)")
     ap.add_argument("--trajectory", action="store_true",
                     help="time whole trajectories (latent init + every step, active samples only) "
                          "instead of the steady state")
@@ -265,7 +372,7 @@ def main():
         spec = dataclasses.replace(spec, num_buckets=args.buckets)
     inp = W.make_inputs(spec) if not args.copy_probe else None
     cpu = None
-    if not args.no_cpu_baseline and not args.copy_probe and not args.trajectory:
+    if not args.no_cpu_baseline and not args.copy_probe and not args.trajectory and not args.rows:
         # the oracle legs run before anything here touches the GPU
         cpu = cpu_baseline(inp, args.cpu_seconds)
         workers = args.cpu_workers if args.cpu_workers >= 0 else min(16, len(os.sched_getaffinity(0)))
@@ -284,6 +391,9 @@ def main():
     torch.cuda.set_device(0)
     if args.trajectory:
         trajectory(inp, args)
+        return
+    if args.rows:
+        rows_bench(inp, args)
         return
     s = GuidedSampler.from_inputs(inp, wrap=True)
     R = max(1, args.replicas)
