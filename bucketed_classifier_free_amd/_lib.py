@@ -14,7 +14,7 @@ BCG_EULER, BCG_HEUN = 0, 1
 BCG_SCHED_LOGLINEAR = 0
 BCG_CACHE_KEEP, BCG_CACHE_STREAM = 0, 1
 BCG_PHASE = {"euler": 0, "heun_predict": 1, "heun_correct": 2}
-BCG_CURVE = {"const": 0, "linear": 1, "front_high": 2}
+BCG_CURVE = {"const": 0, "linear": 1, "front_high": 2, "mid_peak": 3}
 BCG_MAX_REGIONS = 4
 BCG_MAX_CHANNELS = 64
 BCG_MAX_FEATHER = 64
@@ -23,7 +23,7 @@ BCG_MAX_DEVICE_STEPS = 1 << 20
 ABI_VERSION = 3
 
 # Every symbol the header declares (checked by the CPU test suite).
-EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "bucket_table",
+EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
            "area_accumulate", "mask_blend", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
            "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy"]
@@ -102,6 +102,7 @@ def lib():
         L.sigma_schedule.argtypes = [C.c_int, C.c_double, C.c_double, C.c_int, C.c_double, vp,
                                      C.POINTER(C.c_int)]
         L.bucket_table.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp]
+        L.sigma_crop.argtypes = [vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, C.POINTER(C.c_int)]
         L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
         L.guided_step.argtypes = [C.POINTER(StepArgs), vp]
         L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]

@@ -70,6 +70,17 @@ def sigma_schedule(sigma_max: float, sigma_min: float, steps: int, denoise: floa
     return out, nb.value
 
 
+def sigma_crop(sigmas, start_step: int, last_step: int = -1, force_full_denoise: bool = False):
+    """sigmas[start_step .. last_step] (staged sampling), last sigma forced to
+    0 with ``force_full_denoise`` (see include/bcg.h)."""
+    s = _np(sigmas, np.float32, name="sigmas")
+    out = np.empty(max(s.size, 1), np.float32)
+    cnt = ct.c_int(0)
+    L.check(L.lib().sigma_crop(_np_ptr(s), s.size, int(start_step), int(last_step),
+                               1 if force_full_denoise else 0, _np_ptr(out), ct.byref(cnt)))
+    return out[:cnt.value].copy()
+
+
 def bucket_table(curve: str, p0: float, p1: float = 0.0, p2: float = 0.0, num_buckets: int = 1):
     if curve not in L.BCG_CURVE:
         raise ValueError(f"unknown curve {curve!r}")

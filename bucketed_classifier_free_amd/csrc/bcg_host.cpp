@@ -73,15 +73,34 @@ extern "C" int bucket_table(int curve, double p0, double p1, double p2, int num_
     if (!table) return fail(BCG_EINVAL, "bucket_table: table is NULL");
     if (!(std::isfinite(p0) && std::isfinite(p1) && std::isfinite(p2)))
         return fail(BCG_EINVAL, "bucket_table: non-finite curve parameter");
-    if (curve < BCG_CURVE_CONST || curve > BCG_CURVE_FRONT_HIGH)
+    if (curve < BCG_CURVE_CONST || curve > BCG_CURVE_MID_PEAK)
         return fail(BCG_EINVAL, "bucket_table: unknown curve %d", curve);
+    if (curve == BCG_CURVE_MID_PEAK && !(p2 > 0.0 && p2 < 1.0))
+        return fail(BCG_EINVAL, "bucket_table: mid-peak position %g not in (0, 1)", p2);
     for (int b = 0; b < num_buckets; ++b) {
         const double u = num_buckets == 1 ? 0.0 : double(b) / double(num_buckets - 1);
         double v = p0;
         if (curve == BCG_CURVE_LINEAR) v = p0 + (p1 - p0) * u;
         else if (curve == BCG_CURVE_FRONT_HIGH) v = u < p2 ? p0 : p1;
+        else if (curve == BCG_CURVE_MID_PEAK) v = p0 + (p1 - p0) * (u <= p2 ? u / p2 : (1.0 - u) / (1.0 - p2));
         table[b] = float(v);
     }
+    return BCG_OK;
+}
+
+extern "C" int sigma_crop(const float* sigmas, int num_sigmas, int start_step, int last_step,
+                          int force_full_denoise, float* out, int* count) {
+    bcg::clear_error();
+    if (!sigmas || !out || !count) return fail(BCG_EINVAL, "sigma_crop: NULL argument");
+    if (num_sigmas < 1) return fail(BCG_EINVAL, "sigma_crop: num_sigmas %d < 1", num_sigmas);
+    const int end = num_sigmas - 1;
+    const int last = (last_step < 0 || last_step > end) ? end : last_step;
+    if (start_step < 0 || start_step > last)
+        return fail(BCG_EINVAL, "sigma_crop: start_step %d not in [0, %d]", start_step, last);
+    const int m = last - start_step + 1;
+    for (int k = 0; k < m; ++k) out[k] = sigmas[start_step + k];
+    if (force_full_denoise && out[m - 1] != 0.0f) out[m - 1] = 0.0f;
+    *count = m;
     return BCG_OK;
 }
 

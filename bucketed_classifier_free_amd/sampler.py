@@ -43,7 +43,8 @@ class GuidedSampler:
                  sampler="euler", dtype="f32", sigma_max=14.6, sigma_min=0.03, denoise=1.0,
                  s2=0.25, cfg_override=None, region_count=None, region_frac=None,
                  region_strength=None, mu_region=None, feather=0, mask=None, x_orig=None,
-                 device="cuda", wrap=False):
+                 device="cuda", wrap=False, sigma_start=0, sigma_last=-1,
+                 force_full_denoise=False):
         noise = np.ascontiguousarray(noise, np.float32)
         self.n, self.C, self.H, self.W = noise.shape
         self.steps, self.nb, self.sampler, self.dtype = int(steps), int(num_buckets), sampler, dtype
@@ -53,6 +54,12 @@ class GuidedSampler:
         self.start = np.ascontiguousarray(start_step, np.int32)
         self.override = None if cfg_override is None else np.ascontiguousarray(cfg_override, np.float32)
         self.sigmas, self.base_steps = api.sigma_schedule(sigma_max, sigma_min, self.steps, denoise)
+        if sigma_start or sigma_last >= 0 or force_full_denoise:
+            # staged sampling: the cropped sequence is the schedule from here on
+            self.sigmas = api.sigma_crop(self.sigmas, sigma_start, sigma_last, force_full_denoise)
+            self.steps = self.sigmas.size - 1
+            if self.steps < 1:
+                raise ValueError("the cropped schedule has no step to run")
         kind, p0, p1, p2 = curve
         self.table = api.bucket_table(kind, p0, p1, p2, self.nb)
         n, R = self.n, 0

@@ -43,7 +43,7 @@ enum { BCG_OK = 0, BCG_EINVAL = -1, BCG_ESHAPE = -2, BCG_EDTYPE = -3, BCG_EHIP =
 enum { BCG_F32 = 0, BCG_BF16 = 1 };
 enum { BCG_EULER = 0, BCG_HEUN = 1 };
 enum { BCG_SCHED_LOGLINEAR = 0 };
-enum { BCG_CURVE_CONST = 0, BCG_CURVE_LINEAR = 1, BCG_CURVE_FRONT_HIGH = 2 };
+enum { BCG_CURVE_CONST = 0, BCG_CURVE_LINEAR = 1, BCG_CURVE_FRONT_HIGH = 2, BCG_CURVE_MID_PEAK = 3 };
 /* Cache behaviour of the latent streams of guided_step:
  *   BCG_CACHE_KEEP    ordinary loads/stores: the state is expected back soon
  *                     (one batch advanced in place; the 256 MB last-level cache
@@ -84,14 +84,34 @@ int sigma_schedule(int kind, double sigma_max, double sigma_min, int steps,
                    double denoise, float* sigmas, int* base_steps);
 
 /*
+ * sigma_crop -- [S] "denoise below 1" (start_step and last_step crop the
+ * sequence further, for staged sampling) and "force_full_denoise" (a cropped
+ * sequence that does not end at 0 gets 0 as its last sigma, so the output is
+ * fully denoised).  out = sigmas[start_step .. last], last = last_step, or
+ * the last index when last_step < 0 or beyond it; with force_full_denoise a
+ * nonzero out[count-1] becomes 0.  The cropped sequence is a schedule of
+ * count-1 steps (count = 1: nothing to run).
+ *   sigmas  host float[num_sigmas], num_sigmas >= 1
+ *   out     host float[num_sigmas] (room for the whole sequence), not aliasing sigmas
+ *   count   host int*, out
+ * Errors: BCG_EINVAL (NULL pointer, num_sigmas < 1, start_step outside
+ * [0, last]).
+ */
+int sigma_crop(const float* sigmas, int num_sigmas, int start_step, int last_step,
+               int force_full_denoise, float* out, int* count);
+
+/*
  * bucket_table -- [B] sections 2 and 5.  Guidance scale per bucket from a
  * continuous curve sampled at u = b/(num_buckets-1) (u = 0 for one bucket):
  *   BCG_CURVE_CONST       p0
  *   BCG_CURVE_LINEAR      p0 + (p1 - p0) u
  *   BCG_CURVE_FRONT_HIGH  p0 if u < p2 else p1
+ *   BCG_CURVE_MID_PEAK    p0 at both ends, p1 at u = p2 (0 < p2 < 1), linear
+ *                         in between: p0 + (p1 - p0) u/p2 for u <= p2, else
+ *                         p0 + (p1 - p0) (1 - u)/(1 - p2)
  * Evaluated in double, stored as float.  table: host float[num_buckets], out.
  * Errors: BCG_EINVAL (unknown curve, num_buckets out of [1, BCG_MAX_BUCKETS],
- * non-finite value).
+ * non-finite value, mid-peak position outside (0, 1)).
  */
 int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
                  float* table);

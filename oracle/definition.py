@@ -107,6 +107,27 @@ def sigma_schedule(sigma_max: float, sigma_min: float, steps: int,
     return sig, N
 
 
+def crop_sigmas(sig, start_step: int, last_step=None, force_full_denoise: bool = False):
+    """Staged sampling on a schedule ("12 · Samplers...", section "denoise
+    below 1": start_step and last_step crop the sequence further; section
+    "force_full_denoise": when the cropped sequence does not end at 0, the
+    option sets its last sigma to 0 so the output is fully denoised).
+
+    Reading: steps start_step .. last_step-1 are kept, i.e. the sigmas at
+    indices start_step .. last_step (last_step None, negative or beyond the
+    end: to the end); the cropped sequence is the schedule from then on.
+    """
+    sig = np.asarray(sig, np.float32)
+    end = len(sig) - 1
+    last = end if last_step is None or last_step < 0 or last_step > end else int(last_step)
+    if not 0 <= start_step <= last:
+        raise ValueError((start_step, last))
+    out = sig[start_step:last + 1].copy()
+    if force_full_denoise and out[-1] != 0:
+        out[-1] = np.float32(0.0)
+    return out
+
+
 # --------------------------------------------------------------------------
 # a2: bucket plan (SGLang write-up sections 2 and 3)
 # --------------------------------------------------------------------------
@@ -131,27 +152,37 @@ def bucket_id_bruteforce(t: int, steps: int, nb: int) -> int:
     raise AssertionError("no bucket")
 
 
+def curve_value(kind: str, p0: float, p1: float, p2: float, u: float) -> float:
+    """The continuous guidance curve at progress u in [0, 1] (float64).
+
+    Section 5 of the write-up names three shapes: linear decay (e.g. 2.0 ->
+    1.2), front-high (strong for the first 20% of progress, weak after) and
+    mid-peak (guidance raised in the middle stage).  Reading for mid-peak,
+    which the pages give no formula for: a triangle, p0 at both ends and p1
+    at u = p2, linear on each side.
+    """
+    if kind == "const":
+        return p0
+    if kind == "linear":
+        return p0 + (p1 - p0) * u
+    if kind == "front_high":
+        return p0 if u < p2 else p1
+    if kind == "mid_peak":
+        if not 0.0 < p2 < 1.0:
+            raise ValueError(p2)
+        return p0 + (p1 - p0) * (u / p2 if u <= p2 else (1.0 - u) / (1.0 - p2))
+    raise ValueError(kind)
+
+
 def bucket_table(kind: str, p0: float, p1: float, p2: float, nb: int):
     """Scale per bucket from a continuous guidance curve (float32 table).
 
     Section 2 of the write-up discretises a continuous curve into buckets,
-    constant within a bucket; section 5 names the shapes: linear decay (e.g.
-    2.0 -> 1.2) and front-high (strong for the first 20% of progress, weak
-    after).  Reading: bucket b samples the curve at u = b/(nb-1) (u = 0 when
-    nb = 1), so a linear curve hits both end values exactly.
+    constant within a bucket.  Reading: bucket b samples the curve at
+    u = b/(nb-1) (u = 0 when nb = 1), so a linear curve hits both end values
+    exactly.
     """
-    out = []
-    for b in range(nb):
-        u = 0.0 if nb == 1 else b / (nb - 1)
-        if kind == "const":
-            v = p0
-        elif kind == "linear":
-            v = p0 + (p1 - p0) * u
-        elif kind == "front_high":
-            v = p0 if u < p2 else p1
-        else:
-            raise ValueError(kind)
-        out.append(v)
+    out = [curve_value(kind, p0, p1, p2, 0.0 if nb == 1 else b / (nb - 1)) for b in range(nb)]
     return np.array(out, dtype=np.float64).astype(np.float32)
 
 

@@ -1,0 +1,76 @@
+"""Schedule and guidance variants on the GPU: staged sampling (sigma_crop),
+force_full_denoise and the mid-peak curve, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import definition as D
+from oracle import mirror32 as M
+
+from gpu_helpers import to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bucketed_classifier_free_amd
+    bucketed_classifier_free_amd.load()  # fails loudly without libbcg.so
+
+
+def _sampler(inp, **kw):
+    from bucketed_classifier_free_amd import GuidedSampler
+    return GuidedSampler.from_inputs(inp, **kw)
+
+
+def _staged_spec(sampler):
+    # one bucket and a common start: the guidance of a step does not depend on
+    # where the schedule was cut
+    return W.small_spec(n=4, C=3, H=16, W=24, regions=2, inpaint=True, steps=12, num_buckets=1,
+                        curve=W.Curve("const", 3.0), mixed_start=False, skip_frac=0.0,
+                        sampler=sampler, feather=3)
+
+
+@pytest.mark.parametrize("sampler", ["euler", "heun"])
+@pytest.mark.parametrize("cut", [1, 5, 11])
+def test_staged_sampling_equals_full_run(sampler, cut):
+    inp = W.make_inputs(_staged_spec(sampler))
+    full = _sampler(inp).run()
+    x = _sampler(inp, sigma_last=cut).run()
+    _sampler(inp, sigma_start=cut).run(x)
+    torch.cuda.synchronize()
+    assert torch.equal(x, full)
+
+
+@pytest.mark.parametrize("sampler", ["euler", "heun"])
+def test_force_full_denoise_ends_on_prediction(sampler):
+    inp = W.make_inputs(_staged_spec(sampler))
+    cut = 5
+    a = _sampler(inp, sigma_last=cut, force_full_denoise=True)
+    assert a.sigmas[-1] == 0 and a.steps == cut
+    x = a.run()
+    y = _sampler(inp, sigma_last=cut - 1).run()
+    torch.cuda.synchronize()
+    sig = a.sigmas
+    plan = a.plan(cut - 1)  # the last step of the forced schedule
+    got, before = to_np(x), to_np(y)
+    for i in range(inp.spec.n):
+        ref = M.step32(before[i], sig[cut - 1], np.float32(0), plan.scale[i], plan.uncond_row[i] >= 0,
+                       M.params32(inp, i), sampler)
+        assert np.array_equal(got[i], M._store(ref, inp.spec.dtype)), i
+    assert not torch.equal(x, _sampler(inp, sigma_last=cut).run())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mid_peak_curve_trajectory_matches_mirror(dtype):
+    sp = W.small_spec(n=5, C=2, H=16, W=16, steps=10, num_buckets=8, dtype=dtype,
+                      curve=W.Curve("mid_peak", 1.2, 3.0, 0.4), regions=1)
+    inp = W.make_inputs(sp)
+    s = _sampler(inp)
+    assert np.array_equal(s.table, D.bucket_table("mid_peak", 1.2, 3.0, 0.4, 8))
+    x = s.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(x), M.trajectory32(inp))

@@ -28,7 +28,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
@@ -307,3 +307,32 @@ def test_rows_entry_point_validates_before_launch():
     assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EDTYPE
     a.dtype, a.n_active = 0, 0                                          # nothing to do, no launch
     assert lib.guided_step_rows(C.byref(a), None) == L.BCG_OK
+
+
+def test_sigma_crop_bit_exact_and_errors():
+    rng = np.random.default_rng(3)
+    for _ in range(100):
+        steps = int(rng.integers(1, 60))
+        sig, _ = bcg.sigma_schedule(14.6, 0.03, steps, float(rng.choice([1.0, 0.6])))
+        last = int(rng.integers(-1, steps + 3))
+        end = steps if last < 0 or last > steps else last
+        start = int(rng.integers(0, end + 1))
+        force = bool(rng.integers(0, 2))
+        got = bcg.sigma_crop(sig, start, last, force)
+        want = D.crop_sigmas(sig, start, None if last < 0 else last, force)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    with pytest.raises(L.BCGError):
+        bcg.sigma_crop(sig, 5, 2)
+
+
+def test_mid_peak_table_bit_exact():
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        p0, p1, p2 = float(rng.uniform(1, 3)), float(rng.uniform(1, 8)), float(rng.uniform(0.05, 0.95))
+        nb = int(rng.integers(1, 40))
+        got = bcg.bucket_table("mid_peak", p0, p1, p2, nb)
+        want = D.bucket_table("mid_peak", p0, p1, p2, nb)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    for bad in (0.0, 1.0, -0.5):
+        with pytest.raises(L.BCGError):
+            bcg.bucket_table("mid_peak", 1.2, 2.0, bad, 4)

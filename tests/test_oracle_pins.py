@@ -627,3 +627,38 @@ def test_rows_mirror_within_tolerance_and_exact_cases():
     assert np.array_equal(M.rows_pred32(c, u, 3.0, np.zeros((H, Wd), np.float32), xo), xo)
     assert np.array_equal(M.rows_euler32(x, c, s0, 0.0), c)
     assert M.rows_heun_predict32(x, c, s0, 0.0)[0] is None
+
+
+# ---------------------------------------------------------------- schedule and curve variants
+
+@pytest.mark.parametrize("p2", [0.5, 0.3, 0.8])
+def test_mid_peak_curve_is_the_triangle(p2):
+    """p0 at both ends, p1 at the peak, linear between: numpy's piecewise-linear
+    interpolation through (0, p0), (p2, p1), (1, p0)."""
+    for nb in (1, 2, 5, 11, 16):
+        u = np.array([0.0]) if nb == 1 else np.arange(nb) / (nb - 1)
+        want = np.interp(u, [0.0, p2, 1.0], [1.2, 2.0, 1.2]).astype(np.float32)
+        got = D.bucket_table("mid_peak", 1.2, 2.0, p2, nb)
+        assert np.allclose(got, want, rtol=0, atol=2e-7), nb
+    t = D.bucket_table("mid_peak", 1.2, 2.0, 0.5, 11)
+    assert t[0] == t[-1] == np.float32(1.2) and t[5] == np.float32(2.0)
+    assert np.array_equal(t, t[::-1])
+    with pytest.raises(ValueError):
+        D.curve_value("mid_peak", 1.2, 2.0, 1.0, 0.5)
+
+
+def test_crop_sigmas_stages_compose_and_force():
+    full, _ = D.sigma_schedule(14.6, 0.03, 30)
+    assert np.array_equal(D.crop_sigmas(full, 0), full)
+    assert np.array_equal(D.crop_sigmas(full, 0, 99), full)
+    for k in (1, 7, 29):
+        a, b = D.crop_sigmas(full, 0, k), D.crop_sigmas(full, k)
+        assert a.size == k + 1 and b.size == 31 - k
+        assert a[-1] == b[0]                                  # the stages meet
+        assert np.array_equal(np.concatenate([a[:-1], b]), full)
+        f = D.crop_sigmas(full, 0, k, force_full_denoise=True)
+        assert np.array_equal(f[:-1], a[:-1]) and f[-1] == 0  # only the end changes
+    assert np.array_equal(D.crop_sigmas(full, 12, force_full_denoise=True), full[12:])  # already ends at 0
+    assert D.crop_sigmas(full, 30).size == 1                  # nothing left to run
+    with pytest.raises(ValueError):
+        D.crop_sigmas(full, 8, 5)

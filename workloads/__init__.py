@@ -30,11 +30,12 @@ __all__ = ["Spec", "Inputs", "CONFIGS", "config", "make_inputs", "small_spec"]
 
 @dataclass(frozen=True)
 class Curve:
-    """Guidance curve description: kind in {"const", "linear", "front_high"}.
+    """Guidance curve description: kind in {"const", "linear", "front_high", "mid_peak"}.
 
     const:      value = p0
     linear:     from p0 at progress 0 to p1 at progress 1
     front_high: p0 for the first ``p2`` fraction of progress, p1 after
+    mid_peak:   p0 at both ends, p1 at progress ``p2``
     """
     kind: str
     p0: float
