@@ -186,6 +186,30 @@ def bucket_table(kind: str, p0: float, p1: float, p2: float, nb: int):
     return np.array(out, dtype=np.float64).astype(np.float32)
 
 
+def bucket_bounds(kind: str, p0: float, p1: float, p2: float, nb: int):
+    """The curve at the edges of each bucket (float32 tables lo, hi).
+
+    Section 2 of the write-up cuts the continuous curve at the bucket
+    boundaries and, within a bucket, uses a constant or a simple linear
+    interpolation.  Bucket b covers progress [b/nb, (b+1)/nb) (that is what
+    bucket_id assigns), so its interpolation runs from the curve at b/nb to
+    the curve at (b+1)/nb.
+    """
+    lo = [curve_value(kind, p0, p1, p2, b / nb) for b in range(nb)]
+    hi = [curve_value(kind, p0, p1, p2, (b + 1) / nb) for b in range(nb)]
+    return (np.array(lo, np.float64).astype(np.float32), np.array(hi, np.float64).astype(np.float32))
+
+
+def interp_scale(t: int, steps: int, nb: int, lo, hi):
+    """Within-bucket linear interpolation (write-up section 2): the fraction of
+    the way through bucket b, f = (t*nb - b*steps)/steps, in float64, then
+    lo[b] + (hi[b] - lo[b]) * f rounded to float32."""
+    b = bucket_id(t, steps, nb)
+    f = (t * nb - b * steps) / steps
+    lo_b, hi_b = float(np.float32(lo[b])), float(np.float32(hi[b]))
+    return np.float32(lo_b + (hi_b - lo_b) * f)
+
+
 def area_box(frac, H: int, W: int):
     """Area fractions (fy, fx, fh, fw) -> half-open latent slice (y0, y1, x0, x1).
 
@@ -212,12 +236,14 @@ def covers_frame(boxes, strengths, H: int, W: int) -> bool:
     return bool(cov.all())
 
 
-def build_plan(t, steps: int, nb: int, table, override=None, covered=None):
+def build_plan(t, steps: int, nb: int, table, override=None, covered=None, table_end=None):
     """Bucket plan of one step: ids, scales, skip set, layout and offsets.
 
     * bucket id per active sample (t in [0, steps)), scale = its override if
-      given (not NaN) else table[bucket]   -- write-up sections 2, 4 (stage 1:
-      re-bucketing each step with update_guidance_scales).
+      given (not NaN) else table[bucket], or with ``table_end`` the
+      within-bucket interpolation from table[bucket] to table_end[bucket]
+      -- write-up sections 2, 4 (stage 1: re-bucketing each step with
+      update_guidance_scales).
     * the uncond branch is skipped when the scale is exactly 1 and nothing
       forces it ("12 · Samplers...", section "the cfg = 1 optimisation");
       a sample whose regional conds leave pixels uncovered is forced to keep
@@ -246,7 +272,12 @@ def build_plan(t, steps: int, nb: int, table, override=None, covered=None):
             continue
         b = bucket_id(int(t[i]), steps, nb)
         bid[i] = b
-        w = override[i] if not np.isnan(override[i]) else table[b]
+        if not np.isnan(override[i]):
+            w = override[i]
+        elif table_end is not None:
+            w = interp_scale(int(t[i]), steps, nb, table, table_end)
+        else:
+            w = table[b]
         scale[i] = w
         need_u[i] = not (w == np.float32(1.0) and covered[i])
     order = sorted((int(bid[i]), i) for i in range(n) if active[i])
@@ -548,12 +579,26 @@ def coverage(inp):
 
 
 def run_setup(inp):
-    """Schedule, bucket table, coverage and per-sample params of a workload."""
+    """Schedule, bucket table, coverage and per-sample params of a workload.
+    With within-bucket interpolation the table is the bucket-start values
+    (bucket_bounds) and table_end(inp) gives the bucket-end values."""
     sp = inp.spec
     sig, _ = sigma_schedule(sp.sigma_max, sp.sigma_min, sp.steps, sp.denoise)
     c = sp.curve
-    table = bucket_table(c.kind, c.p0, c.p1, c.p2, sp.num_buckets)
+    if sp.bucket_interp:
+        table = bucket_bounds(c.kind, c.p0, c.p1, c.p2, sp.num_buckets)[0]
+    else:
+        table = bucket_table(c.kind, c.p0, c.p1, c.p2, sp.num_buckets)
     return sig, table, coverage(inp)
+
+
+def table_end(inp):
+    """The bucket-end values when the workload interpolates within buckets."""
+    sp = inp.spec
+    if not sp.bucket_interp:
+        return None
+    c = sp.curve
+    return bucket_bounds(c.kind, c.p0, c.p1, c.p2, sp.num_buckets)[1]
 
 
 def init_latent(inp, sig, storage: str):
@@ -593,7 +638,8 @@ def trajectory(inp, storage: str | None = None, launches: int | None = None,
     L = sp.steps if launches is None else launches
     for k in range(L):
         t = inp.start_step.astype(np.int64) + k
-        plan = build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+        plan = build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov,
+                          table_end(inp))
         for i in idx:
             if plan["bucket_id"][i] < 0:
                 continue

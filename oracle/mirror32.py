@@ -225,7 +225,8 @@ def trajectory32(inp, launches=None, samples=None, keep=False):
     L = sp.steps if launches is None else launches
     for k in range(L):
         t = inp.start_step.astype(np.int64) + k
-        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov,
+                            D.table_end(inp))
         for i in idx:
             if plan["bucket_id"][i] < 0:
                 continue

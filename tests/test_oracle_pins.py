@@ -662,3 +662,29 @@ def test_crop_sigmas_stages_compose_and_force():
     assert D.crop_sigmas(full, 30).size == 1                  # nothing left to run
     with pytest.raises(ValueError):
         D.crop_sigmas(full, 8, 5)
+
+
+def test_within_bucket_interpolation_follows_the_curve():
+    """A linear curve interpolated within buckets is the continuous curve
+    itself: scale(t) = g(t/steps) for any bucket count (up to float32)."""
+    for steps, nb in ((50, 8), (30, 16), (20, 8), (7, 3), (12, 1), (10, 64)):
+        lo, hi = D.bucket_bounds("linear", 2.0, 1.2, 0.0, nb)
+        assert np.array_equal(lo[1:], hi[:-1])  # neighbouring buckets meet
+        plan = D.build_plan(np.arange(steps), steps, nb, lo, table_end=hi)
+        g = 2.0 + (1.2 - 2.0) * (np.arange(steps) / steps)
+        assert np.allclose(plan["scale"], g, rtol=0, atol=4e-7), (steps, nb)
+        for t in range(steps):  # at a bucket's first step the scale is its start value
+            b = D.bucket_id(t, steps, nb)
+            if t * nb == b * steps:
+                assert plan["scale"][t] == lo[b]
+
+
+def test_within_bucket_interpolation_of_a_step_curve_ramps_inside_one_bucket():
+    # front-high 2.0 -> 1.2 at 20%: with 4 buckets of 25%, the edge at 20%
+    # falls inside bucket 0, whose scale ramps from 2.0 to 1.2
+    lo, hi = D.bucket_bounds("front_high", 2.0, 1.2, 0.2, 4)
+    assert list(lo) == [np.float32(2.0)] + [np.float32(1.2)] * 3
+    assert list(hi) == [np.float32(1.2)] * 4
+    plan = D.build_plan(np.arange(20), 20, 4, lo, table_end=hi)
+    assert np.allclose(plan["scale"][:5], 2.0 - 0.8 * np.arange(5) / 5, atol=1e-7)
+    assert (plan["scale"][5:] == np.float32(1.2)).all()

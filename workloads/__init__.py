@@ -68,6 +68,7 @@ class Spec:
     region_hi: float = 0.8
     inpaint: bool = False      # ellipse denoise mask + original latent
     seed: int = 0
+    bucket_interp: bool = False  # scale interpolated within each bucket
 
 
 @dataclass
@@ -183,10 +184,10 @@ def config(name: str) -> Spec:
 def small_spec(name="small", *, n=3, C=3, H=17, W=40, dtype="f32", sampler="euler",
                steps=6, num_buckets=3, curve=None, regions=0, inpaint=False,
                mixed_start=True, skip_frac=0.34, feather=3, denoise=1.0, seed=7,
-               region_lo=0.2, region_hi=0.8, shared_mu=False) -> Spec:
+               region_lo=0.2, region_hi=0.8, shared_mu=False, bucket_interp=False) -> Spec:
     """A small shape for parity tests (several tiles, ragged tails)."""
     return Spec(name, n, C, H, W, dtype, sampler, steps, num_buckets,
                 curve or Curve("linear", 2.0, 1.2), denoise=denoise,
                 mixed_start=mixed_start, skip_frac=skip_frac, regions=regions,
                 feather=feather, inpaint=inpaint, seed=seed, region_lo=region_lo,
-                region_hi=region_hi, shared_mu=shared_mu)
+                region_hi=region_hi, shared_mu=shared_mu, bucket_interp=bucket_interp)
