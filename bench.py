@@ -210,7 +210,7 @@ def rows_bench(inp, args):
         st_in, st_out = steps_state[r, m & 1], steps_state[r, (m + 1) & 1]
         pl = plans[r]
         api.bcg_plan_device(s.steps, s.d_table, st_in, step_out=st_out, cfg_override=s.d_override,
-                            covered=s.d_covered, wrap=True, out=pl)
+                            covered=s.d_covered, wrap=True, out=pl, bucket_cfg_end=s.d_table_end)
         rows = dict(order=pl["order"], step_idx=st_in, scale=pl["scale"],
                     uncond_row=pl["uncond_row"], cond_row=pl["cond_row"])
         if heun:

@@ -8,7 +8,7 @@ fallback implementation).
 """
 from . import _lib
 from ._lib import BCGError
-from .api import (Plan, area_accumulate, bcg_plan_build, bcg_plan_device, bucket_table,
+from .api import (Plan, area_accumulate, bcg_plan_build, bcg_plan_device, bucket_bounds, bucket_table,
                   guided_step, guided_step_dplan, guided_step_rows, guided_step_workspace_size,
                   latent_init, mask_blend, sigma_crop, sigma_schedule)
 from .sampler import GuidedSampler, Interrupted
@@ -19,6 +19,6 @@ def load():
     return _lib.lib()
 
 __all__ = ["BCGError", "Plan", "GuidedSampler", "Interrupted", "area_accumulate",
-           "bcg_plan_build", "bcg_plan_device", "bucket_table", "guided_step", "guided_step_dplan",
-           "guided_step_rows", "guided_step_workspace_size", "latent_init", "mask_blend",
-           "sigma_crop", "sigma_schedule"]
+           "bcg_plan_build", "bcg_plan_device", "bucket_bounds", "bucket_table", "guided_step",
+           "guided_step_dplan", "guided_step_rows", "guided_step_workspace_size", "latent_init",
+           "mask_blend", "sigma_crop", "sigma_schedule"]

@@ -20,10 +20,11 @@ BCG_MAX_CHANNELS = 64
 BCG_MAX_FEATHER = 64
 BCG_MAX_DEVICE_BUCKETS = 1024
 BCG_MAX_DEVICE_STEPS = 1 << 20
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
+           "bucket_bounds",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
            "area_accumulate", "mask_blend", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
            "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy"]
@@ -38,7 +39,7 @@ class PlanIn(C.Structure):
                 ("max_regions", C.c_int32),
                 ("bucket_cfg", vp), ("step_idx", vp), ("cfg_override", vp),
                 ("region_count", vp), ("region_frac", vp), ("region_strength", vp),
-                ("covered", vp)]
+                ("covered", vp), ("bucket_cfg_end", vp)]
 
 
 class PlanOut(C.Structure):
@@ -74,7 +75,7 @@ class DevicePlan(C.Structure):
                 ("bucket_cfg", vp), ("cfg_override", vp), ("covered", vp), ("step_in", vp),
                 ("step_out", vp), ("bucket_id", vp), ("scale", vp), ("uncond_row", vp),
                 ("cond_row", vp), ("order", vp), ("bucket_count", vp), ("bucket_offset", vp),
-                ("uncond_offset", vp), ("totals", vp)]
+                ("uncond_offset", vp), ("totals", vp), ("bucket_cfg_end", vp)]
 
 
 class LoopDesc(C.Structure):
@@ -102,6 +103,7 @@ def lib():
         L.sigma_schedule.argtypes = [C.c_int, C.c_double, C.c_double, C.c_int, C.c_double, vp,
                                      C.POINTER(C.c_int)]
         L.bucket_table.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp]
+        L.bucket_bounds.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp, vp]
         L.sigma_crop.argtypes = [vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, C.POINTER(C.c_int)]
         L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
         L.guided_step.argtypes = [C.POINTER(StepArgs), vp]

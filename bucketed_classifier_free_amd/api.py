@@ -89,6 +89,18 @@ def bucket_table(curve: str, p0: float, p1: float = 0.0, p2: float = 0.0, num_bu
     return out
 
 
+def bucket_bounds(curve: str, p0: float, p1: float = 0.0, p2: float = 0.0, num_buckets: int = 1):
+    """The curve at the start and end of each bucket (float32 lo, hi): the
+    tables of the within-bucket interpolation."""
+    if curve not in L.BCG_CURVE:
+        raise ValueError(f"unknown curve {curve!r}")
+    lo = np.empty(max(num_buckets, 1), np.float32)
+    hi = np.empty(max(num_buckets, 1), np.float32)
+    L.check(L.lib().bucket_bounds(L.BCG_CURVE[curve], p0, p1, p2, num_buckets, _np_ptr(lo),
+                                  _np_ptr(hi)))
+    return lo, hi
+
+
 @dataclass
 class Plan:
     bucket_id: np.ndarray
@@ -120,11 +132,13 @@ def plan_out_arrays(n, nb, R, bucket_id=None, scale=None, uncond_row=None, order
 
 def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, W: int = 1,
                    cfg_override=None, region_count=None, region_frac=None,
-                   region_strength=None, max_regions: int = 0, covered=None, out=None) -> Plan:
+                   region_strength=None, max_regions: int = 0, covered=None, out=None,
+                   bucket_cfg_end=None) -> Plan:
     """Bucket plan of one step (host arrays in, host arrays out).
 
     ``covered`` (optional, [n] bool/uint8) supplies the per-sample coverage
-    flags of an earlier plan; the region arrays are then not used."""
+    flags of an earlier plan; the region arrays are then not used.
+    ``bucket_cfg_end`` (optional) turns on the within-bucket interpolation."""
     step_idx = _np(step_idx, np.int32, name="step_idx")
     n = step_idx.size
     cfg = _np(bucket_cfg, np.float32, name="bucket_cfg")
@@ -135,9 +149,10 @@ def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, 
     rf = _np(region_frac, np.float64, (n, R, 4), "region_frac") if rc is not None else None
     rs = _np(region_strength, np.float32, (n, R), "region_strength") if rc is not None else None
     cov = _np(covered, np.uint8, (n,), "covered")
+    cend = _np(bucket_cfg_end, np.float32, (nb,), "bucket_cfg_end")
     o = out if out is not None else plan_out_arrays(n, nb, R)
     pin = L.PlanIn(n, steps, nb, C, H, W, R, _np_ptr(cfg), _np_ptr(step_idx), _np_ptr(ov),
-                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs), _np_ptr(cov))
+                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs), _np_ptr(cov), _np_ptr(cend))
     pout = L.PlanOut(*(_np_ptr(o[k]) for k in ("bucket_id", "scale", "uncond_row", "cond_row",
                                                "order", "bucket_count", "bucket_offset",
                                                "uncond_offset", "region_box", "region_off",
@@ -289,7 +304,7 @@ def device_plan_arrays(n: int, nb: int, device="cuda") -> dict:
 
 
 def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
-                covered=None, wrap: bool = False, out=None) -> L.DevicePlan:
+                covered=None, wrap: bool = False, out=None, bucket_cfg_end=None) -> L.DevicePlan:
     """Packs the device arrays of a device-built plan (see include/bcg.h)."""
     _dev(step_in, "step_in", torch.int32)
     n = step_in.numel()
@@ -300,6 +315,7 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
         raise ValueError("step_out: needs n entries")
     _dev(cfg_override, "cfg_override", torch.float32, (n,), allow_none=True)
     _dev(covered, "covered", torch.int32, (n,), allow_none=True)
+    _dev(bucket_cfg_end, "bucket_cfg_end", torch.float32, (nb,), allow_none=True)
     ptrs = [None] * len(_PLAN_KEYS)
     if out is not None:
         for k, dt, size in (("bucket_id", torch.int32, n), ("scale", torch.float32, n),
@@ -312,20 +328,20 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
                 raise ValueError(f"{k}: needs {size} entries")
         ptrs = [_ptr(out[k]) for k in _PLAN_KEYS]
     return L.DevicePlan(int(steps), nb, 1 if wrap else 0, _ptr(bucket_cfg), _ptr(cfg_override),
-                        _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs)
+                        _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs, _ptr(bucket_cfg_end))
 
 
 def bcg_plan_device(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
-                    covered=None, wrap: bool = False, out=None, stream=None):
+                    covered=None, wrap: bool = False, out=None, bucket_cfg_end=None, stream=None):
     """The plan of one step built on the device (and the step advance)."""
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
-                    covered=covered, wrap=wrap, out=out)
+                    covered=covered, wrap=wrap, out=out, bucket_cfg_end=bucket_cfg_end)
     L.check(L.lib().bcg_plan_device(step_in.numel(), ct.byref(d), _stream(stream)))
 
 
 def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucket_cfg, step_in,
                       step_out=None, cfg_override=None, covered=None, wrap: bool = False,
-                      plan_out=None, sampler: str, s2: float, feather: int = 0,
+                      plan_out=None, bucket_cfg_end=None, sampler: str, s2: float, feather: int = 0,
                       region_count=None, region_box=None, region_strength=None, mu_region=None,
                       x_orig=None, mask=None, cache_hint: int = 0, stream=None):
     """guided_step with the plan of the step built on the device, same launch."""
@@ -336,7 +352,7 @@ def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucke
     if step_in.numel() != x.shape[0]:
         raise ValueError("step_in: needs one entry per sample")
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
-                    covered=covered, wrap=wrap, out=plan_out)
+                    covered=covered, wrap=wrap, out=plan_out, bucket_cfg_end=bucket_cfg_end)
     L.check(L.lib().guided_step_dplan(ct.byref(a), ct.byref(d), _stream(stream)))
 
 

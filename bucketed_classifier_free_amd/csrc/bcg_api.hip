@@ -298,6 +298,7 @@ void fill_dplan(StepParams& p, const bcg_device_plan* d) {
     p.nb = d->num_buckets;
     p.wrap = d->wrap;
     p.bucket_cfg = d->bucket_cfg;
+    p.bucket_cfg_end = d->bucket_cfg_end;
     p.cfg_override = d->cfg_override;
     p.covered = d->covered;
     p.step_idx = d->step_in;

@@ -167,6 +167,7 @@ struct StepParams {
     int steps, nb, wrap;
     int plan_block;
     const float* bucket_cfg;
+    const float* bucket_cfg_end;  // NULL: constant within a bucket
     const float* cfg_override;
     const int32_t* covered;
     int32_t* step_out;

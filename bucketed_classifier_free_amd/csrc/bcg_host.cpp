@@ -28,7 +28,7 @@ using bcg::fail;
 
 extern "C" const char* bcg_last_error(void) { return bcg::g_err; }
 
-extern "C" int bcg_abi_version(void) { return 3; }
+extern "C" int bcg_abi_version(void) { return 4; }
 
 // "12 · Samplers, schedulers and CFG", sections "sigma sequence" and
 // "denoise below 1": the schedule runs from high to low noise and ends at 0;
@@ -65,25 +65,52 @@ extern "C" int sigma_schedule(int kind, double sigma_max, double sigma_min, int 
 
 // SGLang BCG write-up, section 2 (a continuous curve cut into buckets,
 // constant per bucket) and section 5 (linear decay and front-high shapes).
+namespace {
+
+int check_curve(int curve, double p0, double p1, double p2, int num_buckets, const char* who) {
+    if (num_buckets < 1 || num_buckets > BCG_MAX_BUCKETS)
+        return fail(BCG_EINVAL, "%s: num_buckets %d out of range", who, num_buckets);
+    if (!(std::isfinite(p0) && std::isfinite(p1) && std::isfinite(p2)))
+        return fail(BCG_EINVAL, "%s: non-finite curve parameter", who);
+    if (curve < BCG_CURVE_CONST || curve > BCG_CURVE_MID_PEAK)
+        return fail(BCG_EINVAL, "%s: unknown curve %d", who, curve);
+    if (curve == BCG_CURVE_MID_PEAK && !(p2 > 0.0 && p2 < 1.0))
+        return fail(BCG_EINVAL, "%s: mid-peak position %g not in (0, 1)", who, p2);
+    return BCG_OK;
+}
+
+// [B] section 5's curve shapes at progress u (double).
+double curve_at(int curve, double p0, double p1, double p2, double u) {
+    if (curve == BCG_CURVE_LINEAR) return p0 + (p1 - p0) * u;
+    if (curve == BCG_CURVE_FRONT_HIGH) return u < p2 ? p0 : p1;
+    if (curve == BCG_CURVE_MID_PEAK) return p0 + (p1 - p0) * (u <= p2 ? u / p2 : (1.0 - u) / (1.0 - p2));
+    return p0;
+}
+
+}  // namespace
+
 extern "C" int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
                             float* table) {
     bcg::clear_error();
-    if (num_buckets < 1 || num_buckets > BCG_MAX_BUCKETS)
-        return fail(BCG_EINVAL, "bucket_table: num_buckets %d out of range", num_buckets);
+    const int rc = check_curve(curve, p0, p1, p2, num_buckets, "bucket_table");
+    if (rc) return rc;
     if (!table) return fail(BCG_EINVAL, "bucket_table: table is NULL");
-    if (!(std::isfinite(p0) && std::isfinite(p1) && std::isfinite(p2)))
-        return fail(BCG_EINVAL, "bucket_table: non-finite curve parameter");
-    if (curve < BCG_CURVE_CONST || curve > BCG_CURVE_MID_PEAK)
-        return fail(BCG_EINVAL, "bucket_table: unknown curve %d", curve);
-    if (curve == BCG_CURVE_MID_PEAK && !(p2 > 0.0 && p2 < 1.0))
-        return fail(BCG_EINVAL, "bucket_table: mid-peak position %g not in (0, 1)", p2);
     for (int b = 0; b < num_buckets; ++b) {
         const double u = num_buckets == 1 ? 0.0 : double(b) / double(num_buckets - 1);
-        double v = p0;
-        if (curve == BCG_CURVE_LINEAR) v = p0 + (p1 - p0) * u;
-        else if (curve == BCG_CURVE_FRONT_HIGH) v = u < p2 ? p0 : p1;
-        else if (curve == BCG_CURVE_MID_PEAK) v = p0 + (p1 - p0) * (u <= p2 ? u / p2 : (1.0 - u) / (1.0 - p2));
-        table[b] = float(v);
+        table[b] = float(curve_at(curve, p0, p1, p2, u));
+    }
+    return BCG_OK;
+}
+
+extern "C" int bucket_bounds(int curve, double p0, double p1, double p2, int num_buckets,
+                             float* lo, float* hi) {
+    bcg::clear_error();
+    const int rc = check_curve(curve, p0, p1, p2, num_buckets, "bucket_bounds");
+    if (rc) return rc;
+    if (!lo || !hi) return fail(BCG_EINVAL, "bucket_bounds: NULL output");
+    for (int b = 0; b < num_buckets; ++b) {
+        lo[b] = float(curve_at(curve, p0, p1, p2, double(b) / double(num_buckets)));
+        hi[b] = float(curve_at(curve, p0, p1, p2, double(b + 1) / double(num_buckets)));
     }
     return BCG_OK;
 }
@@ -174,8 +201,11 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
     const bool regions = R > 0 && in->region_count && !in->covered;
     if (regions && (!in->region_frac || !in->region_strength))
         return fail(BCG_EINVAL, "bcg_plan_build: region_count given without region_frac/strength");
-    for (int b = 0; b < nb; ++b)
+    for (int b = 0; b < nb; ++b) {
         if (!std::isfinite(in->bucket_cfg[b])) return fail(BCG_EINVAL, "bcg_plan_build: bucket_cfg[%d] not finite", b);
+        if (in->bucket_cfg_end && !std::isfinite(in->bucket_cfg_end[b]))
+            return fail(BCG_EINVAL, "bcg_plan_build: bucket_cfg_end[%d] not finite", b);
+    }
     for (int i = 0; i < n; ++i) {
         if (in->cfg_override) {
             const float o = in->cfg_override[i];
@@ -239,6 +269,11 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
         const int b = int(std::min<long long>(t * nb / steps, nb - 1));
         out->bucket_id[i] = b;
         float w = in->bucket_cfg[b];
+        if (in->bucket_cfg_end) {  // within-bucket interpolation
+            const double f = double(t * nb - (long long)b * steps) / double(steps);
+            const double lo = in->bucket_cfg[b], hi = in->bucket_cfg_end[b];
+            w = float(lo + (hi - lo) * f);
+        }
         if (in->cfg_override && !std::isnan(in->cfg_override[i])) w = in->cfg_override[i];
         out->scale[i] = w;
         need_u[i] = !(w == 1.0f && covered[i]);

@@ -3,7 +3,8 @@
 // [uncond | cond] layout; ComfyUI guide "12 · Samplers, schedulers and CFG",
 // "the cfg = 1 optimisation").  Same definition as the host plan build:
 //   bucket = min(floor(t * nb / steps), nb - 1)       exact integer arithmetic
-//   scale  = override if given and not NaN, else bucket_cfg[bucket]
+//   scale  = override if given and not NaN, else bucket_cfg[bucket] (or the
+//            within-bucket interpolation towards bucket_cfg_end[bucket])
 //   uncond kept unless scale == 1 and the sample's conds cover the frame
 //   order  = active samples stably sorted by (bucket, sample)
 // Included by the .hip translation units only.
@@ -20,6 +21,12 @@ __device__ __forceinline__ void dplan_sample(const StepParams& p, int i, int t, 
     b = (int)(((uint32_t)t * (uint32_t)p.nb) / (uint32_t)p.steps);
     b = b < p.nb - 1 ? b : p.nb - 1;
     w = p.bucket_cfg[b];
+    if (p.bucket_cfg_end) {  // within-bucket interpolation, in double as on the host
+        const double f = double((int)((uint32_t)t * (uint32_t)p.nb - (uint32_t)b * (uint32_t)p.steps)) /
+                         double(p.steps);
+        const double lo = w, hi = p.bucket_cfg_end[b];
+        w = float(lo + (hi - lo) * f);
+    }
     if (p.cfg_override) {
         const float o = p.cfg_override[i];
         if (o == o) w = o;  // NaN = no override

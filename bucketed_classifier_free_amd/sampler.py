@@ -44,7 +44,7 @@ class GuidedSampler:
                  s2=0.25, cfg_override=None, region_count=None, region_frac=None,
                  region_strength=None, mu_region=None, feather=0, mask=None, x_orig=None,
                  device="cuda", wrap=False, sigma_start=0, sigma_last=-1,
-                 force_full_denoise=False):
+                 force_full_denoise=False, bucket_interp=False):
         noise = np.ascontiguousarray(noise, np.float32)
         self.n, self.C, self.H, self.W = noise.shape
         self.steps, self.nb, self.sampler, self.dtype = int(steps), int(num_buckets), sampler, dtype
@@ -61,7 +61,10 @@ class GuidedSampler:
             if self.steps < 1:
                 raise ValueError("the cropped schedule has no step to run")
         kind, p0, p1, p2 = curve
-        self.table = api.bucket_table(kind, p0, p1, p2, self.nb)
+        if bucket_interp:  # scale interpolated within each bucket: start and end tables
+            self.table, self.table_end = api.bucket_bounds(kind, p0, p1, p2, self.nb)
+        else:
+            self.table, self.table_end = api.bucket_table(kind, p0, p1, p2, self.nb), None
         n, R = self.n, 0
         if region_count is not None and int(np.max(region_count, initial=0)) > 0:
             R = int(np.asarray(region_frac).shape[1])
@@ -99,6 +102,7 @@ class GuidedSampler:
             self.d_region_box = self.d_region_count = self.d_region_strength = self.d_mu_region = None
         # Device copies of the plan inputs, for plans built on the device.
         self.d_table = f32(self.table)
+        self.d_table_end = None if self.table_end is None else f32(self.table_end)
         self.d_override = None if self.override is None else f32(self.override)
         self.d_covered = (None if self.covered is None else
                           torch.from_numpy(self.covered.astype(np.int32)).to(dev))
@@ -116,7 +120,7 @@ class GuidedSampler:
                    region_count=inp.region_count if sp.regions > 0 else None,
                    region_frac=inp.region_frac, region_strength=inp.region_strength,
                    mu_region=inp.mu_region, feather=sp.feather, mask=inp.mask,
-                   x_orig=inp.x_orig, **kw)
+                   x_orig=inp.x_orig, bucket_interp=sp.bucket_interp, **kw)
 
     # ------------------------------------------------------------ host plan
 
@@ -126,7 +130,7 @@ class GuidedSampler:
                                   cfg_override=self.override, region_count=self.region_count,
                                   region_frac=self.region_frac,
                                   region_strength=self.region_strength, max_regions=self.R,
-                                  covered=cov, out=out)
+                                  covered=cov, out=out, bucket_cfg_end=self.table_end)
 
     def step_indices(self, k: int) -> np.ndarray:
         t = self.start.astype(np.int64) + k
@@ -193,6 +197,7 @@ class GuidedSampler:
                               self.d_mu_c, steps=self.steps, bucket_cfg=self.d_table,
                               step_in=step_in, step_out=step_out, cfg_override=self.d_override,
                               covered=self.d_covered, wrap=self.wrap, plan_out=plan_out,
+                              bucket_cfg_end=self.d_table_end,
                               sampler=self.sampler, s2=self.s2, feather=self.feather,
                               region_count=self.d_region_count, region_box=self.d_region_box,
                               region_strength=self.d_region_strength, mu_region=self.d_mu_region,
@@ -254,7 +259,8 @@ class NativeLoop:
             self.plan_out = api.device_plan_arrays(n, s.nb, s.device) if plan_outputs else None
             dplan = api.device_plan(s.steps, s.d_table, self.dev_steps[0, 0],
                                     step_out=self.dev_steps[0, 1], cfg_override=s.d_override,
-                                    covered=s.d_covered, wrap=s.wrap, out=self.plan_out)
+                                    covered=s.d_covered, wrap=s.wrap, out=self.plan_out,
+                                    bucket_cfg_end=s.d_table_end)
         else:
             self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
             self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
@@ -273,7 +279,7 @@ class NativeLoop:
         plan = L.PlanIn(n, s.steps, s.nb, s.C, s.H, s.W, R, npp(s.table, np.float32), None,
                         npp(s.override, np.float32), npp(s.region_count, np.int32),
                         npp(s.region_frac, np.float64), npp(s.region_strength, np.float32),
-                        npp(s.covered, np.uint8))
+                        npp(s.covered, np.uint8), npp(s.table_end, np.float32))
         ptr = api._ptr
         step = L.StepArgs(n, s.C, s.H, s.W, api._DT[s.tdtype], api._SAMPLER[s.sampler], R,
                           s.feather, 0, s.d_sigmas.numel(),

@@ -117,6 +117,18 @@ int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
                  float* table);
 
 /*
+ * bucket_bounds -- [B] section 2: the curve is cut at the bucket boundaries
+ * and, within a bucket, held constant or linearly interpolated.  Bucket b
+ * covers progress [b/num_buckets, (b+1)/num_buckets) (the bucket_id rule),
+ * so lo[b] = curve(b/num_buckets) and hi[b] = curve((b+1)/num_buckets) (curves
+ * as bucket_table; double, stored as float).  Passed to a plan as bucket_cfg
+ * (lo) and bucket_cfg_end (hi), they give the within-bucket interpolation.
+ * Errors: as bucket_table.
+ */
+int bucket_bounds(int curve, double p0, double p1, double p2, int num_buckets,
+                  float* lo, float* hi);
+
+/*
  * bcg_plan_build -- [B] section 2 (assign_bucket), section 3 (BucketPlan:
  * per-sample bucket and scale, per-bucket offsets; the [uncond | cond]
  * layout), section 4 stage 3 (the plan is built before launch and is
@@ -127,7 +139,10 @@ int bucket_table(int curve, double p0, double p1, double p2, int num_buckets,
  * (active):
  *   bucket_id[i] = min(floor(step_idx[i]*num_buckets/steps), num_buckets-1)
  *                  (exact integer arithmetic)
- *   scale[i]     = cfg_override[i] if given and not NaN, else bucket_cfg[bucket]
+ *   scale[i]     = cfg_override[i] if given and not NaN, else bucket_cfg[bucket],
+ *                  or, with bucket_cfg_end, the within-bucket interpolation
+ *                  float(lo + (hi - lo) * f) in double, lo = bucket_cfg[b],
+ *                  hi = bucket_cfg_end[b], f = (t*num_buckets - b*steps)/steps
  *   the uncond branch is skipped iff scale[i] == 1.0f and the sample's conds
  *   cover every latent pixel (no regions, or the boxes with strength > 0
  *   cover the frame); otherwise it is kept (uncovered pixels use it).
@@ -159,6 +174,8 @@ typedef struct {
                                         sample's conds cover the frame), e.g. from an
                                         earlier call's covered_out; when given, region
                                         arrays are not read and region outputs not written */
+    const float* bucket_cfg_end;     /* [num_buckets] or NULL: bucket-end scales for the
+                                        within-bucket interpolation (bucket_bounds) */
 } bcg_plan_in;
 
 typedef struct {
@@ -258,7 +275,8 @@ size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
  *
  * The plan is the one bcg_plan_build defines, bit for bit: for a sample with
  * 0 <= t < steps, bucket = min(floor(t*num_buckets/steps), num_buckets-1),
- * scale = cfg_override (if given and not NaN) else bucket_cfg[bucket], uncond
+ * scale = cfg_override (if given and not NaN) else bucket_cfg[bucket] (or the
+ * within-bucket interpolation towards bucket_cfg_end[bucket]), uncond
  * skipped iff scale == 1.0f and covered; stable (bucket, i) order; offsets,
  * rows and totals as in bcg_plan_out.  Coverage is not recomputed on the
  * device: pass the flags bcg_plan_build returned in covered_out (they depend
@@ -293,6 +311,7 @@ typedef struct {
     int32_t* bucket_offset;          /* [num_buckets+1] */
     int32_t* uncond_offset;          /* [num_buckets+1] */
     int32_t* totals;                 /* [2]: n_active, n_uncond */
+    const float* bucket_cfg_end;     /* device [num_buckets] or NULL (no interpolation) */
 } bcg_device_plan;
 
 /*

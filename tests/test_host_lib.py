@@ -28,12 +28,12 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == L.ABI_VERSION == 3
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 4
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -336,3 +336,27 @@ def test_mid_peak_table_bit_exact():
     for bad in (0.0, 1.0, -0.5):
         with pytest.raises(L.BCGError):
             bcg.bucket_table("mid_peak", 1.2, 2.0, bad, 4)
+
+
+def test_bucket_bounds_and_interpolated_plan_bit_exact():
+    rng = np.random.default_rng(5)
+    for kind, p in (("linear", (2.0, 1.2, 0.0)), ("front_high", (2.0, 1.2, 0.2)),
+                    ("mid_peak", (1.2, 3.0, 0.4)), ("const", (7.0, 0.0, 0.0))):
+        for nb in (1, 3, 8, 16, 37):
+            lo, hi = bcg.bucket_bounds(kind, *p, num_buckets=nb)
+            rlo, rhi = D.bucket_bounds(kind, *p, nb)
+            assert np.array_equal(lo.view(np.uint32), rlo.view(np.uint32))
+            assert np.array_equal(hi.view(np.uint32), rhi.view(np.uint32))
+            for _ in range(5):
+                n = int(rng.integers(1, 60))
+                steps = int(rng.integers(1, 80))
+                t = rng.integers(-2, steps + 2, n).astype(np.int32)
+                ov = np.where(rng.random(n) < 0.2, np.float32(1.0), np.float32(np.nan)).astype(np.float32)
+                got = bcg.bcg_plan_build(t, steps, lo, cfg_override=ov, bucket_cfg_end=hi)
+                ref = D.build_plan(t, steps, nb, rlo, ov, None, rhi)
+                assert np.array_equal(got.scale.view(np.uint32), ref["scale"].view(np.uint32))
+                assert np.array_equal(got.order[:got.n_active], ref["order"])
+                assert np.array_equal(got.uncond_row, ref["uncond_row"])
+    with pytest.raises(L.BCGError):
+        bcg.bcg_plan_build(np.zeros(1, np.int32), 5, np.float32([2.0]),
+                           bucket_cfg_end=np.float32([np.inf]))
