@@ -345,6 +345,8 @@ def main():
                     help="bracket every m-th launch with HIP events (kernel duration); "
                          "with --graph, every replay is bracketed instead")
     ap.add_argument("--plan", choices=("device", "host"), default="device")
+    ap.add_argument("--records", type=int, default=1,
+                    help="device plans: each launch's plan writes the next step's sample records")
     ap.add_argument("--graph", type=int, default=40, metavar="G",
                     help="device plans: replay a captured graph of G launches (a multiple of "
                          "2 x replicas; 0 = direct launches)")
@@ -404,7 +406,7 @@ def main():
     G = args.graph - args.graph % (2 * R) if dev_plan else 0  # replays need a whole buffer period
     loop = s.native_loop(x if R > 1 else x[0], upload_batch=args.upload_batch,
                          async_upload=bool(args.async_upload), timing_every=args.timing_every,
-                         device_plan=dev_plan, graph_launches=G)
+                         device_plan=dev_plan, graph_launches=G, records=bool(args.records))
     loop.run(0, args.warmup)
     torch.cuda.synchronize()
     elems_per_launch = spec.n * spec.C * spec.H * spec.W  # every sample active (steady state)

@@ -20,13 +20,13 @@ BCG_MAX_CHANNELS = 64
 BCG_MAX_FEATHER = 64
 BCG_MAX_DEVICE_BUCKETS = 1024
 BCG_MAX_DEVICE_STEPS = 1 << 20
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
            "bucket_bounds",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
-           "area_accumulate", "mask_blend", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
+           "area_accumulate", "mask_blend", "bcg_plan_records", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
            "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy"]
 
 vp, i32p, i64p, f32p, f64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64),
@@ -75,7 +75,8 @@ class DevicePlan(C.Structure):
                 ("bucket_cfg", vp), ("cfg_override", vp), ("covered", vp), ("step_in", vp),
                 ("step_out", vp), ("bucket_id", vp), ("scale", vp), ("uncond_row", vp),
                 ("cond_row", vp), ("order", vp), ("bucket_count", vp), ("bucket_offset", vp),
-                ("uncond_offset", vp), ("totals", vp), ("bucket_cfg_end", vp)]
+                ("uncond_offset", vp), ("totals", vp), ("bucket_cfg_end", vp),
+                ("record_in", vp), ("record_out", vp), ("sigmas", vp), ("num_sigmas", C.c_int32)]
 
 
 class LoopDesc(C.Structure):
@@ -84,7 +85,7 @@ class LoopDesc(C.Structure):
                 ("replica_stride", C.c_int64), ("upload_batch", C.c_int32),
                 ("async_upload", C.c_int32), ("timing_every", C.c_int32), ("step", StepArgs),
                 ("device_plan", C.c_int32), ("graph_launches", C.c_int32), ("dev_steps", vp),
-                ("dplan", DevicePlan)]
+                ("dplan", DevicePlan), ("dev_records", vp)]
 
 
 _lib = None
@@ -108,6 +109,7 @@ def lib():
         L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
         L.guided_step.argtypes = [C.POINTER(StepArgs), vp]
         L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]
+        L.bcg_plan_records.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, C.c_int, vp]
         L.guided_step_rows.argtypes = [C.POINTER(RowsArgs), vp]
         L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_workspace_size.argtypes = [C.c_int] * 5

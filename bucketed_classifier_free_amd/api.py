@@ -304,7 +304,8 @@ def device_plan_arrays(n: int, nb: int, device="cuda") -> dict:
 
 
 def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
-                covered=None, wrap: bool = False, out=None, bucket_cfg_end=None) -> L.DevicePlan:
+                covered=None, wrap: bool = False, out=None, bucket_cfg_end=None,
+                record_in=None, record_out=None, sigmas=None) -> L.DevicePlan:
     """Packs the device arrays of a device-built plan (see include/bcg.h)."""
     _dev(step_in, "step_in", torch.int32)
     n = step_in.numel()
@@ -316,6 +317,9 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
     _dev(cfg_override, "cfg_override", torch.float32, (n,), allow_none=True)
     _dev(covered, "covered", torch.int32, (n,), allow_none=True)
     _dev(bucket_cfg_end, "bucket_cfg_end", torch.float32, (nb,), allow_none=True)
+    _dev(record_in, "record_in", torch.float32, (n, 4), allow_none=True)
+    _dev(record_out, "record_out", torch.float32, (n, 4), allow_none=True)
+    _dev(sigmas, "sigmas", torch.float32, allow_none=True)
     ptrs = [None] * len(_PLAN_KEYS)
     if out is not None:
         for k, dt, size in (("bucket_id", torch.int32, n), ("scale", torch.float32, n),
@@ -328,20 +332,39 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
                 raise ValueError(f"{k}: needs {size} entries")
         ptrs = [_ptr(out[k]) for k in _PLAN_KEYS]
     return L.DevicePlan(int(steps), nb, 1 if wrap else 0, _ptr(bucket_cfg), _ptr(cfg_override),
-                        _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs, _ptr(bucket_cfg_end))
+                        _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs, _ptr(bucket_cfg_end),
+                        _ptr(record_in), _ptr(record_out), _ptr(sigmas),
+                        0 if sigmas is None else sigmas.numel())
+
+
+def plan_records(plan, step_idx, steps: int, sigmas):
+    """Sample records (float32 [n, 4]: sigma, sigma', scale, flag bits) of the
+    step indices of a host plan (see include/bcg.h)."""
+    t = _np(step_idx, np.int32, name="step_idx")
+    n = t.size
+    sg = _np(sigmas, np.float32, name="sigmas")
+    out = np.zeros((n, 4), np.float32)
+    L.check(L.lib().bcg_plan_records(n, int(steps), _np_ptr(t), _np_ptr(np.ascontiguousarray(plan.scale)),
+                                     _np_ptr(np.ascontiguousarray(plan.uncond_row)), _np_ptr(sg),
+                                     sg.size, _np_ptr(out)))
+    return out
 
 
 def bcg_plan_device(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
-                    covered=None, wrap: bool = False, out=None, bucket_cfg_end=None, stream=None):
-    """The plan of one step built on the device (and the step advance)."""
+                    covered=None, wrap: bool = False, out=None, bucket_cfg_end=None,
+                    record_out=None, sigmas=None, stream=None):
+    """The plan of one step built on the device (and the step advance, and
+    the next step's sample records)."""
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
-                    covered=covered, wrap=wrap, out=out, bucket_cfg_end=bucket_cfg_end)
+                    covered=covered, wrap=wrap, out=out, bucket_cfg_end=bucket_cfg_end,
+                    record_out=record_out, sigmas=sigmas)
     L.check(L.lib().bcg_plan_device(step_in.numel(), ct.byref(d), _stream(stream)))
 
 
 def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucket_cfg, step_in,
                       step_out=None, cfg_override=None, covered=None, wrap: bool = False,
-                      plan_out=None, bucket_cfg_end=None, sampler: str, s2: float, feather: int = 0,
+                      plan_out=None, bucket_cfg_end=None, record_in=None, record_out=None,
+                      sampler: str, s2: float, feather: int = 0,
                       region_count=None, region_box=None, region_strength=None, mu_region=None,
                       x_orig=None, mask=None, cache_hint: int = 0, stream=None):
     """guided_step with the plan of the step built on the device, same launch."""
@@ -352,7 +375,8 @@ def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucke
     if step_in.numel() != x.shape[0]:
         raise ValueError("step_in: needs one entry per sample")
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
-                    covered=covered, wrap=wrap, out=plan_out, bucket_cfg_end=bucket_cfg_end)
+                    covered=covered, wrap=wrap, out=plan_out, bucket_cfg_end=bucket_cfg_end,
+                    record_in=record_in, record_out=record_out)
     L.check(L.lib().guided_step_dplan(ct.byref(a), ct.byref(d), _stream(stream)))
 
 

@@ -283,12 +283,19 @@ int check_dplan(const bcg_device_plan* d, int n, bool step, const char* who) {
     int given = 0;
     for (const void* o : outs) given += o != nullptr;
     if (given != 0 && given != 9) return fail(BCG_EINVAL, "%s: plan outputs must be all given or all NULL", who);
-    if (!step && given == 0 && !d->step_out) return fail(BCG_EINVAL, "%s: nothing to write", who);
+    if (!step && given == 0 && !d->step_out && !d->record_out)
+        return fail(BCG_EINVAL, "%s: nothing to write", who);
     if (d->step_out) {
         const size_t bytes = (size_t)n * sizeof(int32_t);
         const uintptr_t a = reinterpret_cast<uintptr_t>(d->step_in), b = reinterpret_cast<uintptr_t>(d->step_out);
         if (a < b + bytes && b < a + bytes) return fail(BCG_EINVAL, "%s: step_out overlaps step_in", who);
     }
+    if (d->record_out && !step && (!d->sigmas || d->num_sigmas < 1))
+        return fail(BCG_EINVAL, "%s: record_out needs the schedule (sigmas, num_sigmas)", who);
+    if (d->record_in && !step) return fail(BCG_EINVAL, "%s: record_in is read by a step only", who);
+    if (d->record_in && d->record_out &&
+        any_overlap(d->record_in, (size_t)n * 16, d->record_out, (size_t)n * 16))
+        return fail(BCG_EINVAL, "%s: record_out overlaps record_in", who);
     return BCG_OK;
 }
 
@@ -312,6 +319,8 @@ void fill_dplan(StepParams& p, const bcg_device_plan* d) {
     p.plan_bucket_offset = d->bucket_offset;
     p.plan_uncond_offset = d->uncond_offset;
     p.plan_totals = d->totals;
+    p.record_in = d->record_in;
+    p.record_out = d->record_out;
 }
 
 }  // namespace
@@ -366,6 +375,8 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
             return fail(BCG_EINVAL, "%s: num_sigmas %d < steps + 1 = %d", who, a->num_sigmas, d->steps + 1);
         if (a->max_regions > 0 && a->region_count && !d->covered)
             return fail(BCG_EINVAL, "%s: a step with regions needs the coverage flags", who);
+        if ((d->record_in || d->record_out) && (!aligned16(d->record_in) || !aligned16(d->record_out)))
+            return fail(BCG_EINVAL, "%s: records must be 16-byte aligned", who);
     }
     const int n_run = d ? a->n : a->n_active;  // samples the grid covers
     if (n_run == 0) return BCG_OK;
@@ -416,7 +427,8 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     p.vpt = shape.vpt;
     p.tiles = (int)(((int64_t)p.nvec + (int64_t)block * p.vpt - 1) / ((int64_t)block * p.vpt));
     if ((int64_t)p.n_active * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
-    if (d && (d->step_out || d->bucket_id)) p.plan_block = (int)((int64_t)p.n_active * p.tiles);
+    if (d && (d->step_out || d->bucket_id || d->record_out))
+        p.plan_block = (int)((int64_t)p.n_active * p.tiles);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     if (a->stats) {
@@ -466,6 +478,8 @@ extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
     fill_dplan(p, d);
     p.t_end = d->steps;
     p.plan_block = 0;
+    p.sigmas = d->sigmas;
+    p.num_sigmas = d->num_sigmas;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), p);
     return hip_status(hipGetLastError(), "bcg_plan_device: launch");
 }

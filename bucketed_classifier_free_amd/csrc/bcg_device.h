@@ -180,6 +180,8 @@ struct StepParams {
     int32_t* plan_bucket_offset;
     int32_t* plan_uncond_offset;
     int32_t* plan_totals;
+    const float* record_in;       // [n][4] (sigma, sigma', scale, flags) per sample, or NULL
+    float* record_out;            // plan workgroup: the records of the next step's indices
 };
 
 // Launch parameter block of the materialised-branch step (device pointers).

@@ -28,7 +28,7 @@ using bcg::fail;
 
 extern "C" const char* bcg_last_error(void) { return bcg::g_err; }
 
-extern "C" int bcg_abi_version(void) { return 4; }
+extern "C" int bcg_abi_version(void) { return 5; }
 
 // "12 · Samplers, schedulers and CFG", sections "sigma sequence" and
 // "denoise below 1": the schedule runs from high to low noise and ends at 0;
@@ -302,5 +302,28 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
     for (int j = n_act; j < n; ++j) out->order[j] = -1;
     out->n_active = n_act;
     out->n_uncond = m;
+    return BCG_OK;
+}
+
+extern "C" int bcg_plan_records(int n, int steps, const int32_t* step_idx, const float* scale,
+                                const int32_t* uncond_row, const float* sigmas, int num_sigmas,
+                                float* records) {
+    bcg::clear_error();
+    if (n < 0 || steps < 1 || num_sigmas < 1) return fail(BCG_EINVAL, "bcg_plan_records: bad sizes");
+    if (n > 0 && (!step_idx || !scale || !uncond_row || !sigmas || !records))
+        return fail(BCG_EINVAL, "bcg_plan_records: NULL argument");
+    for (int i = 0; i < n; ++i) {
+        float* r = records + 4 * size_t(i);
+        const int t = step_idx[i];
+        if (t >= 0 && t < steps && t + 1 < num_sigmas) {
+            const uint32_t fl = uncond_row[i] >= 0 ? 3u : 1u;
+            r[0] = sigmas[t];
+            r[1] = sigmas[t + 1];
+            r[2] = scale[i];
+            std::memcpy(&r[3], &fl, sizeof fl);
+        } else {
+            r[0] = r[1] = r[2] = r[3] = 0.0f;
+        }
+    }
     return BCG_OK;
 }

@@ -32,6 +32,7 @@ struct bcg_loop {
     // device plans
     int64_t k_next = 0;               // launches done since the last restart
     std::vector<int32_t> t0;          // initial step indices (from start)
+    std::vector<float> rec0;          // their sample records (with dev_records)
     hipGraph_t graph = nullptr;
     hipGraphExec_t graph_exec = nullptr;
 };
@@ -62,15 +63,22 @@ int check_dplan(bcg_loop* L, const char* who) {
     return BCG_OK;
 }
 
-// Writes the initial step indices into buffer 0 of every replica, in order on
-// `st` (the source is the loop's own host copy, which never changes).
+// Writes the initial step indices (and sigma pairs) into buffer 0 of every
+// replica, in order on `st` (the sources are the loop's own host copies,
+// which never change).
 int reset_steps(bcg_loop* L, hipStream_t st) {
     const int n = L->d.plan.n;
     for (int r = 0; r < L->d.replicas && n > 0; ++r) {
-        const int rc = hip_ok(hipMemcpyAsync(L->d.dev_steps + size_t(2 * r) * n, L->t0.data(),
-                                             sizeof(int32_t) * size_t(n), hipMemcpyHostToDevice, st),
-                              "bcg_loop: step index upload");
+        int rc = hip_ok(hipMemcpyAsync(L->d.dev_steps + size_t(2 * r) * n, L->t0.data(),
+                                       sizeof(int32_t) * size_t(n), hipMemcpyHostToDevice, st),
+                        "bcg_loop: step index upload");
         if (rc) return rc;
+        if (L->d.dev_records) {
+            rc = hip_ok(hipMemcpyAsync(L->d.dev_records + size_t(2 * r) * n * 4, L->rec0.data(),
+                                       sizeof(float) * 4 * size_t(n), hipMemcpyHostToDevice, st),
+                        "bcg_loop: record upload");
+            if (rc) return rc;
+        }
     }
     L->k_next = 0;
     return BCG_OK;
@@ -93,6 +101,13 @@ int launch_dplan(bcg_loop* L, int64_t k, hipStream_t st) {
     bcg_device_plan dp = d.dplan;
     dp.step_in = d.dev_steps + size_t(2 * r + (m & 1)) * n;
     dp.step_out = d.dev_steps + size_t(2 * r + ((m + 1) & 1)) * n;
+    if (d.dev_records) {
+        dp.record_in = d.dev_records + size_t(2 * r + (m & 1)) * n * 4;
+        dp.record_out = d.dev_records + size_t(2 * r + ((m + 1) & 1)) * n * 4;
+    } else {
+        dp.record_in = nullptr;
+        dp.record_out = nullptr;
+    }
     return guided_step_dplan(&a, &dp, st);
 }
 
@@ -284,6 +299,43 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
             long long t = desc->start[i];
             if (desc->wrap && t >= 0) t %= desc->plan.steps;
             L->t0[size_t(i)] = int32_t(t);
+        }
+        if (desc->dev_records && n > 0) {  // the records of t0: host plan + schedule
+            const int ns = desc->step.num_sigmas;
+            if (ns < 1 || !desc->step.sigmas) {
+                bcg_loop_destroy(L);
+                return fail(BCG_EINVAL, "bcg_loop_create: dev_records needs step.sigmas");
+            }
+            const size_t nsz = size_t(ns);
+            std::vector<float> sg(nsz);
+            int rc3 = hip_ok(hipMemcpy(sg.data(), desc->step.sigmas, sizeof(float) * size_t(ns),
+                                       hipMemcpyDeviceToHost), "bcg_loop_create: schedule read");
+            if (rc3) {
+                bcg_loop_destroy(L);
+                return rc3;
+            }
+            std::vector<int32_t> bid(size_t(n) + 1), ur(size_t(n) + 1), cr(size_t(n) + 1), ord(size_t(n) + 1);
+            std::vector<float> scl(size_t(n) + 1);
+            bcg_plan_in pin = L->d.plan;
+            pin.step_idx = L->t0.data();
+            bcg_plan_out po{};
+            po.bucket_id = bid.data();
+            po.scale = scl.data();
+            po.uncond_row = ur.data();
+            po.cond_row = cr.data();
+            po.order = ord.data();
+            po.bucket_count = L->bucket_count.data();
+            po.bucket_offset = L->bucket_offset.data();
+            po.uncond_offset = L->uncond_offset.data();
+            L->rec0.assign(4 * size_t(n), 0.0f);
+            rc3 = bcg_plan_build(&pin, &po);
+            if (rc3 == BCG_OK)
+                rc3 = bcg_plan_records(n, desc->plan.steps, L->t0.data(), scl.data(), ur.data(), sg.data(), ns,
+                                       L->rec0.data());
+            if (rc3) {
+                bcg_loop_destroy(L);
+                return rc3;
+            }
         }
         // Check the launch template once with the first launch's pointers.
         dp.step_in = desc->dev_steps;

@@ -48,7 +48,7 @@ __device__ __forceinline__ int dplan_next(const StepParams& p, int t) {
 // n <= lds_ints - 2 * nb it also keeps each sample's bucket and flags from
 // pass 1 for pass 3 (otherwise pass 3 derives them again).
 //   pass 1 (all lanes): per sample, bucket/scale (or the inactive markers)
-//     and the step advance; per-bucket counts of the cond and uncond halves
+//     and the step advance (with the next step's sample record); per-bucket counts of the cond and uncond halves
 //     by LDS atomics;
 //   pass 2 (wavefront 0): exclusive prefix sums of the counts, 64 buckets at
 //     a time, which become the running write cursors of each bucket;
@@ -74,6 +74,18 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh, int
     for (int i = tid; i < n; i += T) {
         const int t = p.step_idx[i];
         if (p.step_out) p.step_out[i] = dplan_next(p, t);
+        if (p.record_out) {  // the next step's record (all zero when inactive)
+            const int nt = dplan_next(p, t);
+            float4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (nt >= 0 && nt < p.steps && nt + 1 < p.num_sigmas) {
+                int b2;
+                float w2;
+                bool need2;
+                dplan_sample(p, i, nt, b2, w2, need2);
+                r = float4{p.sigmas[nt], p.sigmas[nt + 1], w2, __uint_as_float(need2 ? 3u : 1u)};
+            }
+            reinterpret_cast<float4*>(p.record_out)[i] = r;
+        }
         if (!full) continue;
         int v = 0;
         if (t >= 0 && t < p.steps) {

@@ -378,19 +378,31 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         load_stage<T, V, TN, INP>(a, static_cast<const T*>(p.x) + base,
                                   INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, C, p.HW);
     }
-    const int t = p.step_idx[i];
-    if (t < 0 || t >= p.t_end) return;
-
-    const float sig = p.sigmas[t];
-    const float sgn = p.sigmas[t + 1];
+    // The sample's step: from its record when given (one load that waits for
+    // nothing else), else derived from its step index.
     StepScalars s;
+    float sig, sgn;
     bool keep_u;
-    if (p.dplan) {
-        int b;
-        dplan_sample(p, i, t, b, s.w, keep_u);
+    if (p.record_in) {
+        const float4 r = reinterpret_cast<const float4*>(p.record_in)[i];
+        const uint32_t fl = __float_as_uint(r.w);
+        if (!(fl & 1u)) return;
+        sig = r.x;
+        sgn = r.y;
+        s.w = r.z;
+        keep_u = (fl & 2u) != 0;
     } else {
-        s.w = p.scale[i];
-        keep_u = p.uncond_row[i] >= 0;
+        const int t = p.step_idx[i];
+        if (t < 0 || t >= p.t_end) return;
+        sig = p.sigmas[t];
+        sgn = p.sigmas[t + 1];
+        if (p.dplan) {
+            int b;
+            dplan_sample(p, i, t, b, s.w, keep_u);
+        } else {
+            s.w = p.scale[i];
+            keep_u = p.uncond_row[i] >= 0;
+        }
     }
     SampleRegions<NR> sr;
     sr.cnt = cnt;

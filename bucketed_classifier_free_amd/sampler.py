@@ -190,14 +190,22 @@ class GuidedSampler:
         self.launch(d, p.n_active, x, x_out, stats, workspace, cache_hint)
         return p
 
-    def dplan_step(self, x, step_in, step_out=None, x_out=None, plan_out=None, cache_hint=0):
+    def records(self, k: int):
+        """Sample records of launch k's step indices (host float32 [n, 4])."""
+        return api.plan_records(self.plan(k), self.step_indices(k), self.steps, self.sigmas)
+
+    def dplan_step(self, x, step_in, step_out=None, x_out=None, plan_out=None, cache_hint=0,
+                   record_in=None, record_out=None):
         """One fused step whose plan is built on the device from ``step_in``
-        (device int32 [n]); ``step_out`` receives the next step indices."""
+        (device int32 [n]); ``step_out`` receives the next step indices.
+        ``record_in`` / ``record_out`` (device float32 [n, 4]) carry the
+        sample records of this and the next step's indices."""
         api.guided_step_dplan(x, x if x_out is None else x_out, self.d_sigmas, self.d_mu_u,
                               self.d_mu_c, steps=self.steps, bucket_cfg=self.d_table,
                               step_in=step_in, step_out=step_out, cfg_override=self.d_override,
                               covered=self.d_covered, wrap=self.wrap, plan_out=plan_out,
-                              bucket_cfg_end=self.d_table_end,
+                              bucket_cfg_end=self.d_table_end, record_in=record_in,
+                              record_out=record_out,
                               sampler=self.sampler, s2=self.s2, feather=self.feather,
                               region_count=self.d_region_count, region_box=self.d_region_box,
                               region_strength=self.d_region_strength, mu_region=self.d_mu_region,
@@ -222,7 +230,8 @@ class GuidedSampler:
     # ------------------------------------------------------------ native loop
 
     def native_loop(self, x, x_out=None, upload_batch=8, async_upload=False, cache_hint=None,
-                    timing_every=1, device_plan=False, graph_launches=0, plan_outputs=True):
+                    timing_every=1, device_plan=False, graph_launches=0, plan_outputs=True,
+                    records=True):
         """A C++ loop (bcg_loop_*) advancing ``x`` (in place unless x_out).
 
         ``x`` may also be [replicas, n, C, H, W]: launch k then advances
@@ -232,7 +241,7 @@ class GuidedSampler:
         ``loop.plan_out`` when ``plan_outputs``); ``graph_launches`` > 0
         replays a captured graph of that many launches."""
         return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint, timing_every,
-                          device_plan, graph_launches, plan_outputs)
+                          device_plan, graph_launches, plan_outputs, records)
 
 
 class NativeLoop:
@@ -240,7 +249,7 @@ class NativeLoop:
 
     def __init__(self, s: GuidedSampler, x, x_out=None, upload_batch=8, async_upload=False,
                  cache_hint=None, timing_every=1, device_plan=False, graph_launches=0,
-                 plan_outputs=True):
+                 plan_outputs=True, records=True):
         n = s.n
         P = int(upload_batch)
         rows = 8 * P
@@ -256,15 +265,17 @@ class NativeLoop:
         if device_plan:
             self.h_slab = self.d_slab = None
             self.dev_steps = torch.empty((reps, 2, n), dtype=torch.int32, device=s.device)
+            self.dev_records = (torch.zeros((reps, 2, n, 4), dtype=torch.float32, device=s.device)
+                                if records else None)
             self.plan_out = api.device_plan_arrays(n, s.nb, s.device) if plan_outputs else None
             dplan = api.device_plan(s.steps, s.d_table, self.dev_steps[0, 0],
                                     step_out=self.dev_steps[0, 1], cfg_override=s.d_override,
                                     covered=s.d_covered, wrap=s.wrap, out=self.plan_out,
-                                    bucket_cfg_end=s.d_table_end)
+                                    bucket_cfg_end=s.d_table_end, sigmas=s.d_sigmas)
         else:
             self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
             self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
-            self.dev_steps = self.plan_out = None
+            self.dev_steps = self.dev_records = self.plan_out = None
             dplan = L.DevicePlan()
         keep = self._keep = []
 
@@ -293,7 +304,8 @@ class NativeLoop:
                                api._ptr(self.h_slab), api._ptr(self.d_slab), reps,
                                stride if reps > 1 else 0, P, 1 if async_upload else 0,
                                int(timing_every), step, 1 if device_plan else 0,
-                               int(graph_launches), api._ptr(self.dev_steps), dplan)
+                               int(graph_launches), api._ptr(self.dev_steps), dplan,
+                               api._ptr(self.dev_records))
         self.handle = ct.c_void_p()
         L.check(L.lib().bcg_loop_create(ct.byref(self.desc), ct.byref(self.handle)))
 

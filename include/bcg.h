@@ -288,6 +288,14 @@ size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
  * continuous batching with every slot refilled).  step_out must not overlap
  * step_in; a loop alternates two buffers.
  *
+ * Sample records (four floats per sample): (sigma, sigma', scale, flags) of
+ * the sample's step t, with sigma = sigmas[t], sigma' = sigmas[t+1], scale as
+ * above and flags the bit pattern of the fourth float: bit 0 = active
+ * (0 <= t < steps), bit 1 = uncond branch kept; an inactive sample's record
+ * is all zero bits.  A step that reads its records needs no load that waits
+ * on another (its plan wrote them one launch earlier); they must describe
+ * step_in.  bcg_plan_records builds them on the host for a first step.
+ *
  * The device arrays are not validated (a host plan build validates the same
  * tables): bucket_cfg finite, cfg_override finite or NaN.
  */
@@ -312,7 +320,26 @@ typedef struct {
     int32_t* uncond_offset;          /* [num_buckets+1] */
     int32_t* totals;                 /* [2]: n_active, n_uncond */
     const float* bucket_cfg_end;     /* device [num_buckets] or NULL (no interpolation) */
+    const float* record_in;          /* device [n][4] or NULL: this step's sample records, see
+                                        below; guided_step_dplan reads them instead of deriving
+                                        sigma, sigma', scale and the uncond decision from step_in */
+    float* record_out;               /* device [n][4] or NULL: the records of the next step's
+                                        indices (the next step's record_in); needs sigmas */
+    const float* sigmas;             /* device [num_sigmas]: the schedule, for record_out
+                                        (guided_step_dplan uses its own args->sigmas) */
+    int32_t num_sigmas;
 } bcg_device_plan;
+
+/*
+ * bcg_plan_records -- sample records (see above) of step indices step_idx from
+ * a host plan of the same indices (bcg_plan_build's scale and uncond_row) and
+ * the schedule; all host arrays, records [n][4] out.  Active means
+ * 0 <= t < steps and t + 1 < num_sigmas.
+ * Errors: BCG_EINVAL (NULL pointer, n < 0, steps < 1, num_sigmas < 1).
+ */
+int bcg_plan_records(int n, int steps, const int32_t* step_idx, const float* scale,
+                     const int32_t* uncond_row, const float* sigmas, int num_sigmas,
+                     float* records);
 
 /*
  * bcg_plan_device -- the plan of one step for n samples, built by one
@@ -458,9 +485,11 @@ int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void*
  * Device plans (device_plan = 1): each launch is one guided_step_dplan that
  * builds the step's plan on the device (into dplan's plan outputs, if given)
  * and advances the replica's step indices in dev_steps (two buffers per
- * replica, alternating); no host work or copy per launch.  The indices are
- * written from `start` at bcg_loop_create and again whenever a run starts at
- * k0 = 0; otherwise k0 must continue the previous run.  With graph_launches
+ * replica, alternating; with dev_records, the sample records of those
+ * indices too, which the next launch reads instead of deriving them); no
+ * host work or copy per launch.  The indices (and records) are written from
+ * `start` at bcg_loop_create and again whenever a run starts at k0 = 0;
+ * otherwise k0 must continue the previous run.  With graph_launches
  * G > 0 (a multiple of 2*replicas), runs of G launches starting at a multiple
  * of 2*replicas are replays of one HIP graph, captured at bcg_loop_create on
  * a stream of the loop's own.
@@ -500,6 +529,9 @@ typedef struct {
     bcg_device_plan dplan;           /* device plans: template (steps, num_buckets and
                                         wrap are taken from plan/wrap; step_in and
                                         step_out are set per launch) */
+    float* dev_records;              /* device plans: device [replicas][2][n][4] or NULL: the
+                                        sample records that go with dev_steps (each launch
+                                        reads one buffer and its plan writes the other) */
 } bcg_loop_desc;
 
 typedef struct bcg_loop bcg_loop;

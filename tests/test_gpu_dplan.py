@@ -284,3 +284,25 @@ def test_graph_replays_match_direct_launches_each_time():
             assert torch.equal(la.plan_out[k], lb.plan_out[k]), (r, k)
     la.close()
     lb.close()
+
+
+@pytest.mark.parametrize("name", ["mixed_bucket", "regional_inpaint", "throughput_bf16_heun"])
+def test_dplan_with_sample_records_equals_host_path(name):
+    """Steps that read the sample records their previous plan wrote (instead of
+    deriving sigma, scale and the skip from the step index) give the same
+    trajectory; every record written equals the host's records of that step."""
+    inp = W.make_inputs(W.config(name))
+    sp = inp.spec
+    s = _sampler(inp)
+    xh = s.run()
+    x = s.init_state()
+    t0 = s.step_indices(0)
+    steps = [_i32(t0), torch.empty_like(_i32(t0))]
+    recs = [torch.from_numpy(s.records(0)).cuda(), torch.full((sp.n, 4), np.nan, device="cuda")]
+    for k in range(sp.steps):
+        s.dplan_step(x, steps[k & 1], steps[(k + 1) & 1], record_in=recs[k & 1],
+                     record_out=recs[(k + 1) & 1])
+        torch.cuda.synchronize()
+        got = recs[(k + 1) & 1].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), s.records(k + 1).view(np.uint32)), k
+    assert torch.equal(x, xh)

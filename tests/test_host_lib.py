@@ -28,12 +28,12 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == L.ABI_VERSION == 4
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 5
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -360,3 +360,15 @@ def test_bucket_bounds_and_interpolated_plan_bit_exact():
     with pytest.raises(L.BCGError):
         bcg.bcg_plan_build(np.zeros(1, np.int32), 5, np.float32([2.0]),
                            bucket_cfg_end=np.float32([np.inf]))
+
+
+def test_plan_records_from_host_plan():
+    sig, _ = bcg.sigma_schedule(14.6, 0.03, 10)
+    t = np.int32([0, 9, 10, -1, 4])
+    table = np.float32([2.0, 1.0])
+    p = bcg.bcg_plan_build(t, 10, table, cfg_override=np.float32([np.nan, np.nan, np.nan, np.nan, 1.0]))
+    r = bcg.api.plan_records(p, t, 10, sig)
+    flags = r[:, 3].view(np.uint32)
+    assert list(flags) == [3, 1, 0, 0, 1]          # active, uncond kept / skipped at scale 1
+    assert r[0, 0] == sig[0] and r[1, 1] == sig[10] == 0 and r[4, 2] == np.float32(1.0)
+    assert (r[2:4] == 0).all()
