@@ -405,15 +405,19 @@ def inpaint_blend(pred, x_orig, mask):
 
 
 class SampleParams:
-    """Per-sample constants of the path (everything except x and t)."""
+    """Per-sample constants of the path (everything except x and t).
+    ``regional``: the sample's cond is regional (default: it has regions);
+    a regional sample none of whose regions is valid at a step keeps the
+    regional rule, C = U everywhere."""
 
     def __init__(self, mu_u, mu_c, s2, regions=(), feather=0, H=0, W=0,
-                 mask=None, x_orig=None):
+                 mask=None, x_orig=None, regional=None):
         self.mu_u = np.asarray(mu_u, np.float64)
         self.mu_c = np.asarray(mu_c, np.float64)
         self.s2 = float(s2)
         # regions: list of (box, strength, mu_r[C])
         self.regions = list(regions)
+        self.regional = bool(self.regions) if regional is None else bool(regional)
         self.weights = [region_weight(b, s, H, W, feather) for b, s, _ in self.regions]
         self.mask = None if mask is None else np.asarray(mask, np.float64)
         self.x_orig = None if x_orig is None else np.asarray(x_orig, np.float64)
@@ -422,7 +426,7 @@ class SampleParams:
 def guided_pred(x, sigma: float, w: float, prm: SampleParams):
     """The guided, blended prediction P(x, sigma) the sampler steps with."""
     u = denoise(x, sigma, prm.mu_u, prm.s2)
-    if prm.regions:
+    if prm.regional:
         preds = [denoise(x, sigma, mu_r, prm.s2) for _, _, mu_r in prm.regions]
         c = regional_cond(preds, prm.weights, u)
     else:
@@ -531,7 +535,7 @@ def norm_stats(x, sigma: float, w: float, prm: SampleParams, need_uncond: bool):
     (before the inpaint blend), from the evaluation at (x, sigma).
     """
     u = denoise(x, sigma, prm.mu_u, prm.s2)
-    if prm.regions:
+    if prm.regional:
         preds = [denoise(x, sigma, mu_r, prm.s2) for _, _, mu_r in prm.regions]
         c = regional_cond(preds, prm.weights, u)
     else:
@@ -546,17 +550,39 @@ def norm_stats(x, sigma: float, w: float, prm: SampleParams, need_uncond: bool):
 # --------------------------------------------------------------------------
 
 
-def sample_params(inp, i: int, sig_dtype=np.float64):
-    """SampleParams of sample i from a ``workloads.Inputs``."""
+def region_valid(rng, t: int, steps: int) -> bool:
+    """Whether a regional cond takes part in step t ("12 · Samplers...",
+    "calc_cond_batch()": each cond entry is checked for the current timestep
+    being valid).  Reading: a cond carries a range [start, end) of sampling
+    progress, the progress of step t being t/steps (float64, as for the
+    buckets); outside its range the cond contributes nothing."""
+    if rng is None:
+        return True
+    p = t / steps
+    return bool(rng[0] <= p < rng[1])
+
+
+def valid_regions(inp, i: int, t=None):
+    """Indices of sample i's regions that take part in step t (all if t is None)."""
+    k = int(inp.region_count[i])
+    if t is None or inp.region_range is None:
+        return list(range(k))
+    return [r for r in range(k) if region_valid(inp.region_range[i, r], int(t), inp.spec.steps)]
+
+
+def sample_params(inp, i: int, t=None):
+    """SampleParams of sample i from a ``workloads.Inputs`` (at step t when the
+    regions have validity ranges)."""
     sp = inp.spec
     regions = []
-    for r in range(int(inp.region_count[i])):
+    for r in valid_regions(inp, i, t):
         box = area_box(inp.region_frac[i, r], sp.H, sp.W)
         regions.append((box, float(inp.region_strength[i, r]), inp.mu_region[i, r]))
     return SampleParams(inp.mu_uncond[i], inp.mu_cond[i], sp.s2, regions,
                         sp.feather, sp.H, sp.W,
                         None if inp.mask is None else inp.mask[i, 0],
-                        None if inp.x_orig is None else stored_orig(inp)[i])
+                        None if inp.x_orig is None else stored_orig(inp)[i],
+                        regional=int(inp.region_count[i]) > 0)
 
 
 def stored_orig(inp):
@@ -566,15 +592,17 @@ def stored_orig(inp):
     return to_storage(inp.x_orig, inp.spec.dtype)
 
 
-def coverage(inp):
-    """Per-sample full-coverage flag (samples without regions are covered)."""
+def coverage(inp, t=None):
+    """Per-sample full-coverage flag (samples without regions are covered); with
+    validity ranges, of the regions valid at each sample's step t[i]."""
     sp = inp.spec
     out = np.ones(sp.n, bool)
     for i in range(sp.n):
         k = int(inp.region_count[i])
         if k > 0:
-            boxes = [area_box(inp.region_frac[i, r], sp.H, sp.W) for r in range(k)]
-            out[i] = covers_frame(boxes, inp.region_strength[i, :k], sp.H, sp.W)
+            rs = valid_regions(inp, i, None if t is None else t[i])
+            boxes = [area_box(inp.region_frac[i, r], sp.H, sp.W) for r in rs]
+            out[i] = covers_frame(boxes, inp.region_strength[i, rs], sp.H, sp.W)
     return out
 
 
@@ -636,16 +664,18 @@ def trajectory(inp, storage: str | None = None, launches: int | None = None,
     x = init_latent(inp, sig, storage)
     states = [x.copy()] if keep else None
     L = sp.steps if launches is None else launches
+    ranged = inp.region_range is not None
     for k in range(L):
         t = inp.start_step.astype(np.int64) + k
-        plan = build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov,
-                          table_end(inp))
+        plan = build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override,
+                          coverage(inp, t) if ranged else cov, table_end(inp))
         for i in idx:
             if plan["bucket_id"][i] < 0:
                 continue
             ti = int(t[i])
+            prm = sample_params(inp, i, ti) if ranged else prms[i]
             x[i] = to_storage(step(x[i], sig64[ti], sig64[ti + 1],
-                                   float(plan["scale"][i]), prms[i], sp.sampler),
+                                   float(plan["scale"][i]), prm, sp.sampler),
                               storage)
         if keep:
             states.append(x.copy())

@@ -123,12 +123,14 @@ class Params32:
     """Per-sample constants in float32."""
 
     def __init__(self, mu_u, mu_c, s2, boxes=(), strengths=(), mu_r=(), feather=0,
-                 H=0, W=0, mask=None, x_orig=None):
+                 H=0, W=0, mask=None, x_orig=None, regional=None):
         self.mu_u = np.asarray(mu_u, np.float32)
         self.mu_c = np.asarray(mu_c, np.float32)
         self.s2 = f32(s2)
         self.mu_r = [np.asarray(m, np.float32) for m in mu_r]
         self.nr = len(self.mu_r)
+        # a regional sample none of whose regions is valid at this step: C = U
+        self.regional = self.nr > 0 if regional is None else bool(regional)
         if self.nr:
             self.wh, self.covered, self.wsum = pixel_weights(boxes, strengths, H, W, feather)
         self.mask = None if mask is None else np.asarray(mask, np.float32)
@@ -148,7 +150,9 @@ def _coef(sigma, prm):
 def _pred(x, sigma, w, mode, prm):
     a, bu, bc, br = _coef(sigma, prm)
     u = fma32(a, x, bu[:, None, None])
-    if prm.nr == 0:
+    if prm.nr == 0 and prm.regional:
+        c = u
+    elif prm.nr == 0:
         c = fma32(a, x, bc[:, None, None])
     else:
         c = prm.wh[0][None] * fma32(a, x, br[0][:, None, None])
@@ -193,15 +197,17 @@ def step32(x, sigma, sigma_next, w, need_uncond, prm, sampler):
     return fma32(d + d2, hh, x)
 
 
-def params32(inp, i):
+def params32(inp, i, t=None):
+    """Params32 of sample i (at step t when the regions have validity ranges)."""
     sp = inp.spec
-    k = int(inp.region_count[i])
-    boxes = [D.area_box(inp.region_frac[i, r], sp.H, sp.W) for r in range(k)]
+    rs = D.valid_regions(inp, i, t)
+    boxes = [D.area_box(inp.region_frac[i, r], sp.H, sp.W) for r in rs]
     return Params32(inp.mu_uncond[i], inp.mu_cond[i], sp.s2, boxes,
-                    inp.region_strength[i, :k], [inp.mu_region[i, r] for r in range(k)],
+                    inp.region_strength[i, rs], [inp.mu_region[i, r] for r in rs],
                     sp.feather, sp.H, sp.W,
                     None if inp.mask is None else inp.mask[i, 0],
-                    None if inp.x_orig is None else _store(inp.x_orig[i], sp.dtype))
+                    None if inp.x_orig is None else _store(inp.x_orig[i], sp.dtype),
+                    regional=int(inp.region_count[i]) > 0)
 
 
 def init_latent32(inp, sig):
@@ -225,14 +231,16 @@ def trajectory32(inp, launches=None, samples=None, keep=False):
     L = sp.steps if launches is None else launches
     for k in range(L):
         t = inp.start_step.astype(np.int64) + k
-        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov,
-                            D.table_end(inp))
+        ranged = inp.region_range is not None
+        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override,
+                            D.coverage(inp, t) if ranged else cov, D.table_end(inp))
         for i in idx:
             if plan["bucket_id"][i] < 0:
                 continue
             ti = int(t[i])
+            prm = params32(inp, i, ti) if ranged else prms[i]
             x[i] = _store(step32(x[i], sig[ti], sig[ti + 1], plan["scale"][i],
-                                 bool(plan["need_uncond"][i]), prms[i], sp.sampler),
+                                 bool(plan["need_uncond"][i]), prm, sp.sampler),
                           sp.dtype)
         if keep:
             states.append(x.copy())

@@ -388,6 +388,7 @@ def test_bucket_count_invariance():
     dict(dtype="f32", sampler="heun", regions=3, inpaint=True),
     dict(dtype="bf16", sampler="heun"),
     dict(dtype="bf16", sampler="euler", regions=2),
+    dict(dtype="f32", sampler="heun", regions=3, region_ranges=True),
 ])
 def test_mirror_per_step_within_tolerance_of_definition(kw):
     sp = W.small_spec(n=4, C=3, H=12, W=16, steps=7, **kw)
@@ -396,15 +397,16 @@ def test_mirror_per_step_within_tolerance_of_definition(kw):
     x = D.init_latent(inp, sig, "f32")
     for k in range(sp.steps):
         t = inp.start_step.astype(np.int64) + k
-        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+        plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override,
+                            D.coverage(inp, t))
         for i in range(sp.n):
             if plan["bucket_id"][i] < 0:
                 continue
             ti = int(t[i])
             ref = D.step(x[i], float(sig[ti]), float(sig[ti + 1]), float(plan["scale"][i]),
-                         D.sample_params(inp, i), sp.sampler)
+                         D.sample_params(inp, i, ti), sp.sampler)
             got = M.step32(x[i].astype(np.float32), sig[ti], sig[ti + 1], plan["scale"][i],
-                           bool(plan["need_uncond"][i]), M.params32(inp, i), sp.sampler)
+                           bool(plan["need_uncond"][i]), M.params32(inp, i, ti), sp.sampler)
             assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
             x[i] = ref.astype(np.float32)
 
@@ -688,3 +690,43 @@ def test_within_bucket_interpolation_of_a_step_curve_ramps_inside_one_bucket():
     plan = D.build_plan(np.arange(20), 20, 4, lo, table_end=hi)
     assert np.allclose(plan["scale"][:5], 2.0 - 0.8 * np.arange(5) / 5, atol=1e-7)
     assert (plan["scale"][5:] == np.float32(1.2)).all()
+
+
+
+# ---------------------------------------------------------------- per-cond validity ranges
+
+def test_region_validity_boundaries_by_enumeration():
+    # [0.25, 0.5) of 20 steps: progress 5/20 .. 9/20 exactly
+    assert [t for t in range(20) if D.region_valid((0.25, 0.5), t, 20)] == [5, 6, 7, 8, 9]
+    assert all(D.region_valid(None, t, 20) for t in range(20))
+    assert not any(D.region_valid((1.0, 2.0), t, 20) for t in range(20))
+    assert [t for t in range(7) if D.region_valid((0.0, 1.0), t, 7)] == list(range(7))
+
+
+def test_full_ranges_change_nothing_and_an_unused_region_is_absent():
+    base = W.small_spec(n=4, C=2, H=12, W=16, steps=6, regions=2, region_ranges=True, seed=9)
+    inp = W.make_inputs(base)
+    plain = W.make_inputs(dataclasses_replace(base, region_ranges=False))
+    inp.region_range[:] = (0.0, 1.5)
+    assert np.array_equal(D.trajectory(inp), D.trajectory(plain))
+    # region 1 never valid == the samples with region 1 removed
+    inp.region_range[:, 1] = (2.0, 3.0)
+    one = W.make_inputs(dataclasses_replace(base, region_ranges=False))
+    one.region_count[:] = np.minimum(one.region_count, 1)
+    assert np.array_equal(D.trajectory(inp), D.trajectory(one))
+
+
+def test_no_valid_region_means_no_guidance():
+    """A regional sample with none of its regions valid: C = U everywhere, so
+    the prediction is the uncond prediction whatever the scale."""
+    base = W.small_spec(n=1, C=3, H=10, W=12, steps=5, regions=2, region_ranges=True,
+                        inpaint=False, seed=4)
+    inp = W.make_inputs(base)
+    inp.region_range[:] = (0.9, 1.0)  # not valid at step 0
+    prm = D.sample_params(inp, 0, 0)
+    assert prm.regional and not prm.regions
+    x = np.random.default_rng(2).standard_normal((3, 10, 12))
+    u = D.denoise(x, 3.0, prm.mu_u, prm.s2)
+    for w in (0.0, 1.0, 7.5):
+        assert np.array_equal(D.guided_pred(x, 3.0, w, prm), u)
+    assert not D.coverage(inp, np.array([0]))[0]  # the uncond branch is then needed

@@ -69,6 +69,7 @@ class Spec:
     inpaint: bool = False      # ellipse denoise mask + original latent
     seed: int = 0
     bucket_interp: bool = False  # scale interpolated within each bucket
+    region_ranges: bool = False  # each regional cond valid over a range of progress only
 
 
 @dataclass
@@ -85,6 +86,7 @@ class Inputs:
     mu_region: np.ndarray             # f32 [n,R,C]
     mask: np.ndarray | None           # f32 [n,1,H,W] binary, or None
     x_orig: np.ndarray | None         # f32 [n,C,H,W], or None
+    region_range: np.ndarray | None = None  # f64 [n,R,2] (start, end) progress, or None
 
     def subset(self, idx) -> "Inputs":
         """Inputs restricted to the samples ``idx`` (per-sample independence)."""
@@ -95,7 +97,7 @@ class Inputs:
                       take(self.start_step), take(self.cfg_override),
                       take(self.region_count), take(self.region_frac),
                       take(self.region_strength), take(self.mu_region),
-                      take(self.mask), take(self.x_orig))
+                      take(self.mask), take(self.x_orig), take(self.region_range))
 
 
 def _f32(a):
@@ -151,8 +153,12 @@ def make_inputs(spec: Spec, samples=None) -> Inputs:
                   + ((xx - cx[:, None, None]) / ax[:, None, None]) ** 2) <= 1.0
         mask = inside.astype(np.float32)[:, None, :, :]
         x_orig = _f32(rng.standard_normal((n, C, H, W)))
+    rng_ = None
+    if spec.region_ranges and spec.regions > 0:  # drawn last: the other inputs do not change
+        lo = rng.uniform(0.0, 0.6, size=(n, R))
+        rng_ = np.stack([lo, lo + rng.uniform(0.2, 1.0, size=(n, R))], axis=-1)
     inp = Inputs(spec, noise, mu_u, mu_c, start, override, count, frac, strength,
-                 mu_r, mask, x_orig)
+                 mu_r, mask, x_orig, rng_)
     return inp if samples is None else inp.subset(samples)
 
 
@@ -184,10 +190,12 @@ def config(name: str) -> Spec:
 def small_spec(name="small", *, n=3, C=3, H=17, W=40, dtype="f32", sampler="euler",
                steps=6, num_buckets=3, curve=None, regions=0, inpaint=False,
                mixed_start=True, skip_frac=0.34, feather=3, denoise=1.0, seed=7,
-               region_lo=0.2, region_hi=0.8, shared_mu=False, bucket_interp=False) -> Spec:
+               region_lo=0.2, region_hi=0.8, shared_mu=False, bucket_interp=False,
+               region_ranges=False) -> Spec:
     """A small shape for parity tests (several tiles, ragged tails)."""
     return Spec(name, n, C, H, W, dtype, sampler, steps, num_buckets,
                 curve or Curve("linear", 2.0, 1.2), denoise=denoise,
                 mixed_start=mixed_start, skip_frac=skip_frac, regions=regions,
                 feather=feather, inpaint=inpaint, seed=seed, region_lo=region_lo,
-                region_hi=region_hi, shared_mu=shared_mu, bucket_interp=bucket_interp)
+                region_hi=region_hi, shared_mu=shared_mu, bucket_interp=bucket_interp,
+                region_ranges=region_ranges)
