@@ -20,7 +20,7 @@ BCG_MAX_CHANNELS = 64
 BCG_MAX_FEATHER = 64
 BCG_MAX_DEVICE_BUCKETS = 1024
 BCG_MAX_DEVICE_STEPS = 1 << 20
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
@@ -39,14 +39,16 @@ class PlanIn(C.Structure):
                 ("max_regions", C.c_int32),
                 ("bucket_cfg", vp), ("step_idx", vp), ("cfg_override", vp),
                 ("region_count", vp), ("region_frac", vp), ("region_strength", vp),
-                ("covered", vp), ("bucket_cfg_end", vp)]
+                ("covered", vp), ("bucket_cfg_end", vp), ("region_range", vp),
+                ("covered_sets", vp)]
 
 
 class PlanOut(C.Structure):
     _fields_ = [("bucket_id", vp), ("scale", vp), ("uncond_row", vp), ("cond_row", vp),
                 ("order", vp), ("bucket_count", vp), ("bucket_offset", vp),
                 ("uncond_offset", vp), ("region_box", vp), ("region_off", vp),
-                ("covered_out", vp), ("n_active", C.c_int32), ("n_uncond", C.c_int32)]
+                ("covered_out", vp), ("n_active", C.c_int32), ("n_uncond", C.c_int32),
+                ("covered_sets_out", vp), ("region_valid", vp)]
 
 
 class StepArgs(C.Structure):
@@ -58,7 +60,8 @@ class StepArgs(C.Structure):
                 ("scale", vp), ("uncond_row", vp), ("mu_uncond", vp), ("mu_cond", vp),
                 ("region_count", vp), ("region_box", vp), ("region_strength", vp),
                 ("mu_region", vp), ("x_orig", vp), ("mask", vp), ("stats", vp),
-                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("workspace", vp), ("workspace_bytes", C.c_size_t), ("region_range", vp),
+                ("steps", C.c_int32)]
 
 
 class RowsArgs(C.Structure):
@@ -76,7 +79,9 @@ class DevicePlan(C.Structure):
                 ("step_out", vp), ("bucket_id", vp), ("scale", vp), ("uncond_row", vp),
                 ("cond_row", vp), ("order", vp), ("bucket_count", vp), ("bucket_offset", vp),
                 ("uncond_offset", vp), ("totals", vp), ("bucket_cfg_end", vp),
-                ("record_in", vp), ("record_out", vp), ("sigmas", vp), ("num_sigmas", C.c_int32)]
+                ("record_in", vp), ("record_out", vp), ("sigmas", vp), ("num_sigmas", C.c_int32),
+                ("region_range", vp), ("covered_sets", vp), ("region_count", vp),
+                ("max_regions", C.c_int32)]
 
 
 class LoopDesc(C.Structure):
@@ -109,7 +114,7 @@ def lib():
         L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
         L.guided_step.argtypes = [C.POINTER(StepArgs), vp]
         L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]
-        L.bcg_plan_records.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, C.c_int, vp]
+        L.bcg_plan_records.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, vp, C.c_int, vp]
         L.guided_step_rows.argtypes = [C.POINTER(RowsArgs), vp]
         L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_workspace_size.argtypes = [C.c_int] * 5

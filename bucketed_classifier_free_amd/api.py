@@ -116,6 +116,8 @@ class Plan:
     covered: np.ndarray
     n_active: int
     n_uncond: int
+    covered_sets: np.ndarray | None = None
+    region_valid: np.ndarray | None = None
 
 
 def plan_out_arrays(n, nb, R, bucket_id=None, scale=None, uncond_row=None, order=None):
@@ -127,18 +129,21 @@ def plan_out_arrays(n, nb, R, bucket_id=None, scale=None, uncond_row=None, order
                 bucket_offset=np.empty(nb + 1, np.int32), uncond_offset=np.empty(nb + 1, np.int32),
                 region_box=np.empty((n, R, 4), np.int32) if R > 0 else None,
                 region_off=np.empty(n * R + 1, np.int64) if R > 0 else None,
-                covered=np.empty(n, np.uint8))
+                covered=np.empty(n, np.uint8), covered_sets=np.empty(n, np.uint16),
+                region_valid=np.empty(n, np.int32))
 
 
 def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, W: int = 1,
                    cfg_override=None, region_count=None, region_frac=None,
                    region_strength=None, max_regions: int = 0, covered=None, out=None,
-                   bucket_cfg_end=None) -> Plan:
+                   bucket_cfg_end=None, region_range=None, covered_sets=None) -> Plan:
     """Bucket plan of one step (host arrays in, host arrays out).
 
     ``covered`` (optional, [n] bool/uint8) supplies the per-sample coverage
     flags of an earlier plan; the region arrays are then not used.
-    ``bucket_cfg_end`` (optional) turns on the within-bucket interpolation."""
+    ``bucket_cfg_end`` (optional) turns on the within-bucket interpolation.
+    ``region_range`` ([n, R, 2] progress ranges) limits each region to the
+    steps it is valid at; ``covered_sets`` caches the subset coverage."""
     step_idx = _np(step_idx, np.int32, name="step_idx")
     n = step_idx.size
     cfg = _np(bucket_cfg, np.float32, name="bucket_cfg")
@@ -150,19 +155,22 @@ def bcg_plan_build(step_idx, steps: int, bucket_cfg, *, C: int = 1, H: int = 1, 
     rs = _np(region_strength, np.float32, (n, R), "region_strength") if rc is not None else None
     cov = _np(covered, np.uint8, (n,), "covered")
     cend = _np(bucket_cfg_end, np.float32, (nb,), "bucket_cfg_end")
+    rr = _np(region_range, np.float64, (n, R, 2), "region_range") if R > 0 and region_range is not None else None
+    cs = _np(covered_sets, np.uint16, (n,), "covered_sets")
     o = out if out is not None else plan_out_arrays(n, nb, R)
     pin = L.PlanIn(n, steps, nb, C, H, W, R, _np_ptr(cfg), _np_ptr(step_idx), _np_ptr(ov),
-                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs), _np_ptr(cov), _np_ptr(cend))
+                   _np_ptr(rc), _np_ptr(rf), _np_ptr(rs), _np_ptr(cov), _np_ptr(cend), _np_ptr(rr),
+                   _np_ptr(cs))
     pout = L.PlanOut(*(_np_ptr(o[k]) for k in ("bucket_id", "scale", "uncond_row", "cond_row",
                                                "order", "bucket_count", "bucket_offset",
                                                "uncond_offset", "region_box", "region_off",
                                                "covered")),
-                     0, 0)
+                     0, 0, _np_ptr(o.get("covered_sets")), _np_ptr(o.get("region_valid")))
     L.check(L.lib().bcg_plan_build(ct.byref(pin), ct.byref(pout)))
     return Plan(o["bucket_id"], o["scale"], o["uncond_row"], o["cond_row"], o["order"],
                 o["bucket_count"], o["bucket_offset"], o["uncond_offset"], o["region_box"],
                 o["region_off"], o["covered"].astype(bool), int(pout.n_active),
-                int(pout.n_uncond))
+                int(pout.n_uncond), o.get("covered_sets"), o.get("region_valid"))
 
 
 # ---------------------------------------------------------------- device calls
@@ -173,7 +181,7 @@ def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
 
 def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sampler, s2, feather,
                region_count, region_box, region_strength, mu_region, x_orig, mask, stats,
-               workspace, cache_hint):
+               workspace, cache_hint, region_range=None, steps=0):
     """Checks the tensors of a guided step and packs them into StepArgs.
     ``plan_rows`` = (order, step_idx, scale, uncond_row) or None (device plan)."""
     _dev(x, "x")
@@ -223,25 +231,28 @@ def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sam
         wsb = workspace.numel() * workspace.element_size()
     if sampler not in _SAMPLER:
         raise ValueError(f"unknown sampler {sampler!r}")
+    if region_range is not None:
+        _dev(region_range, "region_range", torch.float64, (n, R, 2))
     return L.StepArgs(n, Cc, H, W, _DT[x.dtype], _SAMPLER[sampler], R, int(feather), int(n_active),
                       sigmas.numel(), mps, int(cache_hint), float(s2),
                       _ptr(x), _ptr(x_out), _ptr(sigmas), _ptr(order), _ptr(step_idx), _ptr(scale),
                       _ptr(uncond_row), _ptr(mu_uncond), _ptr(mu_cond), _ptr(region_count),
                       _ptr(region_box), _ptr(region_strength), _ptr(mu_region), _ptr(x_orig),
-                      _ptr(mask), _ptr(stats), _ptr(workspace), wsb)
+                      _ptr(mask), _ptr(stats), _ptr(workspace), wsb, _ptr(region_range), int(steps))
 
 
 def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond, mu_cond, *,
                 n_active: int, sampler: str, s2: float, feather: int = 0,
                 region_count=None, region_box=None, region_strength=None, mu_region=None,
                 x_orig=None, mask=None, stats=None, workspace=None, cache_hint: int = 0,
-                stream=None):
+                region_range=None, steps: int = 0, stream=None):
     """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU."""
     a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, (order, step_idx, scale, uncond_row),
                    n_active=n_active, sampler=sampler, s2=s2, feather=feather,
                    region_count=region_count, region_box=region_box,
                    region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
-                   stats=stats, workspace=workspace, cache_hint=cache_hint)
+                   stats=stats, workspace=workspace, cache_hint=cache_hint,
+                   region_range=region_range, steps=steps)
     L.check(L.lib().guided_step(ct.byref(a), _stream(stream)))
 
 
@@ -305,7 +316,8 @@ def device_plan_arrays(n: int, nb: int, device="cuda") -> dict:
 
 def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
                 covered=None, wrap: bool = False, out=None, bucket_cfg_end=None,
-                record_in=None, record_out=None, sigmas=None) -> L.DevicePlan:
+                record_in=None, record_out=None, sigmas=None, region_range=None,
+                covered_sets=None, region_count=None) -> L.DevicePlan:
     """Packs the device arrays of a device-built plan (see include/bcg.h)."""
     _dev(step_in, "step_in", torch.int32)
     n = step_in.numel()
@@ -317,6 +329,14 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
     _dev(cfg_override, "cfg_override", torch.float32, (n,), allow_none=True)
     _dev(covered, "covered", torch.int32, (n,), allow_none=True)
     _dev(bucket_cfg_end, "bucket_cfg_end", torch.float32, (nb,), allow_none=True)
+    R = 0
+    if region_range is not None:
+        _dev(region_range, "region_range", torch.float64)
+        if region_range.dim() != 3 or region_range.shape[0] != n or region_range.shape[2] != 2:
+            raise ValueError("region_range must be [n, R, 2]")
+        R = region_range.shape[1]
+        _dev(covered_sets, "covered_sets", torch.int16, (n,))
+    _dev(region_count, "region_count", torch.int32, (n,), allow_none=True)
     _dev(record_in, "record_in", torch.float32, (n, 4), allow_none=True)
     _dev(record_out, "record_out", torch.float32, (n, 4), allow_none=True)
     _dev(sigmas, "sigmas", torch.float32, allow_none=True)
@@ -334,10 +354,11 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
     return L.DevicePlan(int(steps), nb, 1 if wrap else 0, _ptr(bucket_cfg), _ptr(cfg_override),
                         _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs, _ptr(bucket_cfg_end),
                         _ptr(record_in), _ptr(record_out), _ptr(sigmas),
-                        0 if sigmas is None else sigmas.numel())
+                        0 if sigmas is None else sigmas.numel(), _ptr(region_range),
+                        _ptr(covered_sets), _ptr(region_count), R)
 
 
-def plan_records(plan, step_idx, steps: int, sigmas):
+def plan_records(plan, step_idx, steps: int, sigmas, ranged: bool = False):
     """Sample records (float32 [n, 4]: sigma, sigma', scale, flag bits) of the
     step indices of a host plan (see include/bcg.h)."""
     t = _np(step_idx, np.int32, name="step_idx")
@@ -345,25 +366,30 @@ def plan_records(plan, step_idx, steps: int, sigmas):
     sg = _np(sigmas, np.float32, name="sigmas")
     out = np.zeros((n, 4), np.float32)
     L.check(L.lib().bcg_plan_records(n, int(steps), _np_ptr(t), _np_ptr(np.ascontiguousarray(plan.scale)),
-                                     _np_ptr(np.ascontiguousarray(plan.uncond_row)), _np_ptr(sg),
+                                     _np_ptr(np.ascontiguousarray(plan.uncond_row)),
+                                     _np_ptr(np.ascontiguousarray(plan.region_valid)) if ranged else None,
+                                     _np_ptr(sg),
                                      sg.size, _np_ptr(out)))
     return out
 
 
 def bcg_plan_device(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
                     covered=None, wrap: bool = False, out=None, bucket_cfg_end=None,
-                    record_out=None, sigmas=None, stream=None):
+                    record_out=None, sigmas=None, region_range=None, covered_sets=None,
+                    region_count=None, stream=None):
     """The plan of one step built on the device (and the step advance, and
     the next step's sample records)."""
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
                     covered=covered, wrap=wrap, out=out, bucket_cfg_end=bucket_cfg_end,
-                    record_out=record_out, sigmas=sigmas)
+                    record_out=record_out, sigmas=sigmas, region_range=region_range,
+                    covered_sets=covered_sets, region_count=region_count)
     L.check(L.lib().bcg_plan_device(step_in.numel(), ct.byref(d), _stream(stream)))
 
 
 def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucket_cfg, step_in,
                       step_out=None, cfg_override=None, covered=None, wrap: bool = False,
                       plan_out=None, bucket_cfg_end=None, record_in=None, record_out=None,
+                      region_range=None, covered_sets=None,
                       sampler: str, s2: float, feather: int = 0,
                       region_count=None, region_box=None, region_strength=None, mu_region=None,
                       x_orig=None, mask=None, cache_hint: int = 0, stream=None):
@@ -376,7 +402,8 @@ def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucke
         raise ValueError("step_in: needs one entry per sample")
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
                     covered=covered, wrap=wrap, out=plan_out, bucket_cfg_end=bucket_cfg_end,
-                    record_in=record_in, record_out=record_out)
+                    record_in=record_in, record_out=record_out, region_range=region_range,
+                    covered_sets=covered_sets, region_count=region_count)
     L.check(L.lib().guided_step_dplan(ct.byref(a), ct.byref(d), _stream(stream)))
 
 

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const StepParams p, flo
     const bool keep_u = p.uncond_row[i] >= 0;
     int cnt = p.R > 0 ? p.region_count[i] : 0;
     cnt = std::max(0, std::min(cnt, std::min(p.R, BCG_MAX_REGIONS)));
+    const unsigned valid = (cnt > 0 && p.region_range) ? region_mask(p, i, t) : 0xfu;
     const float s2 = p.s2;
     const float v = sig * sig;
     const float den = s2 + v;
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void stats_rows_kernel(const StepParams p, flo
             br[r] = (v * p.mu_region[((int64_t)i * p.R + r) * p.C + c]) / den;
             const int32_t* b = p.region_box + ((int64_t)i * p.R + r) * 4;
             rd[r] = RegionDesc{b[0], b[1] - b[0], b[2], b[3] - b[2],
-                               p.region_strength[(int64_t)i * p.R + r]};
+                               ((valid >> r) & 1u) ? p.region_strength[(int64_t)i * p.R + r] : 0.0f};
         }
     }
     const T* xs = static_cast<const T*>(p.x) + ((int64_t)i * p.C + c) * p.HW + (int64_t)y * p.W;
@@ -321,6 +322,9 @@ void fill_dplan(StepParams& p, const bcg_device_plan* d) {
     p.plan_totals = d->totals;
     p.record_in = d->record_in;
     p.record_out = d->record_out;
+    p.region_range = d->region_range;
+    p.range_steps = d->steps;
+    p.covered_sets = d->covered_sets;
 }
 
 }  // namespace
@@ -373,11 +377,17 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         if (a->stats) return fail(BCG_EINVAL, "%s: stats need the host plan", who);
         if (a->num_sigmas < d->steps + 1)
             return fail(BCG_EINVAL, "%s: num_sigmas %d < steps + 1 = %d", who, a->num_sigmas, d->steps + 1);
-        if (a->max_regions > 0 && a->region_count && !d->covered)
+        if (a->max_regions > 0 && a->region_count && !d->covered && !(d->region_range && d->covered_sets))
             return fail(BCG_EINVAL, "%s: a step with regions needs the coverage flags", who);
+        if (d->region_range && (!d->covered_sets || d->max_regions != a->max_regions))
+            return fail(BCG_EINVAL, "%s: validity ranges need covered_sets and max_regions = R", who);
+        if (a->region_range && a->region_range != d->region_range)
+            return fail(BCG_EINVAL, "%s: give the validity ranges in the device plan", who);
         if ((d->record_in || d->record_out) && (!aligned16(d->record_in) || !aligned16(d->record_out)))
             return fail(BCG_EINVAL, "%s: records must be 16-byte aligned", who);
     }
+    if (!d && a->max_regions > 0 && a->region_range && a->steps < 1)
+        return fail(BCG_EINVAL, "%s: validity ranges need steps >= 1", who);
     const int n_run = d ? a->n : a->n_active;  // samples the grid covers
     if (n_run == 0) return BCG_OK;
     if (!a->x || !a->x_out || !a->sigmas || !a->mu_uncond || !a->mu_cond ||
@@ -418,6 +428,8 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     p.x_orig = a->x_orig; p.mask = a->mask;
     p.t_end = a->num_sigmas - 1;
     p.plan_block = -1;
+    p.region_range = a->max_regions > 0 ? a->region_range : nullptr;
+    p.range_steps = a->steps;
     if (d) {
         fill_dplan(p, d);
         p.t_end = d->steps;
@@ -478,6 +490,8 @@ extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
     fill_dplan(p, d);
     p.t_end = d->steps;
     p.plan_block = 0;
+    p.R = d->max_regions;
+    p.region_count = d->region_count;
     p.sigmas = d->sigmas;
     p.num_sigmas = d->num_sigmas;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), p);

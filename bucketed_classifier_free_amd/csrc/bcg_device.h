@@ -180,6 +180,9 @@ struct StepParams {
     int32_t* plan_bucket_offset;
     int32_t* plan_uncond_offset;
     int32_t* plan_totals;
+    const double* region_range;   // [n][R][2] validity ranges, or NULL (always valid)
+    int range_steps;              // trajectory length for the ranges
+    const uint16_t* covered_sets; // device plans with ranges: coverage of every region subset
     const float* record_in;       // [n][4] (sigma, sigma', scale, flags) per sample, or NULL
     float* record_out;            // plan workgroup: the records of the next step's indices
 };

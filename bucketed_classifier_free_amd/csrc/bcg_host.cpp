@@ -28,7 +28,7 @@ using bcg::fail;
 
 extern "C" const char* bcg_last_error(void) { return bcg::g_err; }
 
-extern "C" int bcg_abi_version(void) { return 5; }
+extern "C" int bcg_abi_version(void) { return 6; }
 
 // "12 · Samplers, schedulers and CFG", sections "sigma sequence" and
 // "denoise below 1": the schedule runs from high to low noise and ends at 0;
@@ -198,9 +198,16 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
     if (!out->bucket_id || !out->scale || !out->uncond_row || !out->cond_row || !out->order ||
         !out->bucket_count || !out->bucket_offset || !out->uncond_offset)
         return fail(BCG_EINVAL, "bcg_plan_build: NULL output array");
-    const bool regions = R > 0 && in->region_count && !in->covered;
+    const bool regions = R > 0 && in->region_count && !in->covered && !in->covered_sets;
     if (regions && (!in->region_frac || !in->region_strength))
         return fail(BCG_EINVAL, "bcg_plan_build: region_count given without region_frac/strength");
+    const bool ranged = R > 0 && in->region_range;
+    if (ranged && !regions && !in->covered_sets)
+        return fail(BCG_EINVAL, "bcg_plan_build: validity ranges need the region arrays or covered_sets");
+    for (int i = 0; ranged && i < n; ++i)
+        for (int q = 0; q < 2 * R; ++q)
+            if (std::isnan(in->region_range[size_t(i) * R * 2 + q]))
+                return fail(BCG_EINVAL, "bcg_plan_build: region_range of sample %d is NaN", i);
     for (int b = 0; b < nb; ++b) {
         if (!std::isfinite(in->bucket_cfg[b])) return fail(BCG_EINVAL, "bcg_plan_build: bucket_cfg[%d] not finite", b);
         if (in->bucket_cfg_end && !std::isfinite(in->bucket_cfg_end[b]))
@@ -226,10 +233,19 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
         }
     }
 
-    // Region boxes, crop offsets and per-sample coverage (unless given).
+    // Region boxes, crop offsets and per-sample coverage (unless given): of all
+    // regions, and of every subset of them (bit s of sets: the live regions in
+    // mask s cover the frame; a sample without regions is covered by any).
     std::vector<char> covered(size_t(n), 1);
+    std::vector<uint16_t> sets(size_t(n), 0xffff);
     if (in->covered)
         for (int i = 0; i < n; ++i) covered[i] = in->covered[i] != 0;
+    if (in->covered_sets)
+        for (int i = 0; i < n; ++i) {
+            sets[i] = in->covered_sets[i];
+            const int k = in->region_count ? std::max(0, std::min(in->region_count[i], R)) : R;
+            if (!in->covered) covered[i] = (sets[i] >> ((1u << k) - 1u)) & 1u;
+        }
     int64_t off = 0;
     for (int i = 0; regions && i < n; ++i) {
         const int k = in->region_count[i];
@@ -247,11 +263,25 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
             if (out->region_off) out->region_off[size_t(i) * R + r] = off;
             if (r < k) off += int64_t(in->C) * (boxes[r][1] - boxes[r][0]) * (boxes[r][3] - boxes[r][2]);
         }
-        if (k > 0) covered[i] = covers(live, nlive, in->H, in->W);
+        if (k > 0) {
+            covered[i] = covers(live, nlive, in->H, in->W);
+            uint16_t bits = 0;
+            for (unsigned s = 0; s < (1u << R); ++s) {
+                int32_t sub[BCG_MAX_REGIONS][4];
+                int m = 0;
+                for (int r = 0; r < k; ++r)
+                    if (((s >> r) & 1u) && in->region_strength[i * R + r] > 0.0f)
+                        std::memcpy(sub[m++], boxes[r], sizeof boxes[r]);
+                if (covers(sub, m, in->H, in->W)) bits = uint16_t(bits | (1u << s));
+            }
+            sets[i] = bits;
+        }
     }
     if (regions && out->region_off && R > 0) out->region_off[size_t(n) * R] = off;
     if (out->covered_out)
         for (int i = 0; i < n; ++i) out->covered_out[i] = covered[i] ? 1 : 0;
+    if (out->covered_sets_out)
+        for (int i = 0; i < n; ++i) out->covered_sets_out[i] = sets[i];
 
     // Buckets, scales and the skip decision.
     std::vector<char> need_u(size_t(n), 0);
@@ -261,11 +291,25 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
         const long long t = in->step_idx[i];
         out->uncond_row[i] = -1;
         out->cond_row[i] = -1;
+        if (out->region_valid) out->region_valid[i] = 0;
         if (t < 0 || t >= steps) {
             out->bucket_id[i] = -1;
             out->scale[i] = 0.0f;
             continue;
         }
+        // Regions taking part in this step ("calc_cond_batch()": valid timestep).
+        const int k = in->region_count ? std::max(0, std::min(in->region_count[i], R)) : R;
+        unsigned v = k > 0 ? (1u << k) - 1u : 0u;
+        if (ranged) {
+            const double prog = double(t) / double(steps);
+            v = 0;
+            for (int r = 0; r < k; ++r) {
+                const double* rg = in->region_range + (size_t(i) * R + r) * 2;
+                if (rg[0] <= prog && prog < rg[1]) v |= 1u << r;
+            }
+        }
+        if (out->region_valid) out->region_valid[i] = int32_t(v);
+        const bool cov = ranged ? ((sets[i] >> v) & 1u) != 0 : covered[i] != 0;
         const int b = int(std::min<long long>(t * nb / steps, nb - 1));
         out->bucket_id[i] = b;
         float w = in->bucket_cfg[b];
@@ -276,7 +320,7 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
         }
         if (in->cfg_override && !std::isnan(in->cfg_override[i])) w = in->cfg_override[i];
         out->scale[i] = w;
-        need_u[i] = !(w == 1.0f && covered[i]);
+        need_u[i] = !(w == 1.0f && cov);
         out->bucket_count[b] += 1;
         ++n_act;
     }
@@ -306,8 +350,8 @@ extern "C" int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out) {
 }
 
 extern "C" int bcg_plan_records(int n, int steps, const int32_t* step_idx, const float* scale,
-                                const int32_t* uncond_row, const float* sigmas, int num_sigmas,
-                                float* records) {
+                                const int32_t* uncond_row, const int32_t* region_valid,
+                                const float* sigmas, int num_sigmas, float* records) {
     bcg::clear_error();
     if (n < 0 || steps < 1 || num_sigmas < 1) return fail(BCG_EINVAL, "bcg_plan_records: bad sizes");
     if (n > 0 && (!step_idx || !scale || !uncond_row || !sigmas || !records))
@@ -316,7 +360,8 @@ extern "C" int bcg_plan_records(int n, int steps, const int32_t* step_idx, const
         float* r = records + 4 * size_t(i);
         const int t = step_idx[i];
         if (t >= 0 && t < steps && t + 1 < num_sigmas) {
-            const uint32_t fl = uncond_row[i] >= 0 ? 3u : 1u;
+            const uint32_t valid = region_valid ? uint32_t(region_valid[i]) & 0xfu : 0xfu;
+            const uint32_t fl = (uncond_row[i] >= 0 ? 3u : 1u) | (valid << 2);
             r[0] = sigmas[t];
             r[1] = sigmas[t + 1];
             r[2] = scale[i];

@@ -29,6 +29,7 @@ struct bcg_loop {
     std::vector<int32_t> region_box;
     std::vector<int64_t> region_off;
     std::vector<uint8_t> covered;     // per-sample coverage, computed once
+    std::vector<uint16_t> sets;       // coverage of every region subset (validity ranges)
     // device plans
     int64_t k_next = 0;               // launches done since the last restart
     std::vector<int32_t> t0;          // initial step indices (from start)
@@ -58,8 +59,8 @@ int check_dplan(bcg_loop* L, const char* who) {
     if (a.num_sigmas < d.steps + 1) return fail(BCG_EINVAL, "%s: num_sigmas < steps + 1", who);
     if (a.stats) return fail(BCG_EINVAL, "%s: stats need host plans", who);
     if (a.n > 0 && !d.bucket_cfg) return fail(BCG_EINVAL, "%s: dplan.bucket_cfg is NULL", who);
-    if (a.max_regions > 0 && a.region_count && !d.covered)
-        return fail(BCG_EINVAL, "%s: a step with regions needs dplan.covered", who);
+    if (a.max_regions > 0 && a.region_count && !d.covered && !(d.region_range && d.covered_sets))
+        return fail(BCG_EINVAL, "%s: a step with regions needs dplan.covered (or covered_sets with ranges)", who);
     return BCG_OK;
 }
 
@@ -266,7 +267,8 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
     L->covered.assign(size_t(n) + 1, 1);
     // Boxes and coverage depend on the conds only: derive the coverage flags
     // once, so each step's plan is the O(n) bucket work alone.
-    if (R > 0 && desc->plan.region_count && !desc->plan.covered && n > 0) {
+    L->sets.assign(size_t(n) + 1, 0xffff);
+    if (R > 0 && desc->plan.region_count && !desc->plan.covered && !desc->plan.covered_sets && n > 0) {
         const size_t nn = size_t(n);
         std::vector<int32_t> t0(nn, 0), sc(nn), ur(nn), ord(nn);
         std::vector<float> scale(nn);
@@ -282,12 +284,14 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
         po.bucket_offset = L->bucket_offset.data();
         po.uncond_offset = L->uncond_offset.data();
         po.covered_out = L->covered.data();
+        po.covered_sets_out = L->sets.data();
         const int rc2 = bcg_plan_build(&pin, &po);
         if (rc2) {
             bcg_loop_destroy(L);
             return rc2;
         }
-        L->d.plan.covered = L->covered.data();
+        if (desc->plan.region_range) L->d.plan.covered_sets = L->sets.data();
+        else L->d.plan.covered = L->covered.data();
     }
     if (desc->device_plan) {
         bcg_device_plan& dp = L->d.dplan;
@@ -316,6 +320,7 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
             }
             std::vector<int32_t> bid(size_t(n) + 1), ur(size_t(n) + 1), cr(size_t(n) + 1), ord(size_t(n) + 1);
             std::vector<float> scl(size_t(n) + 1);
+            std::vector<int32_t> rv(size_t(n) + 1);
             bcg_plan_in pin = L->d.plan;
             pin.step_idx = L->t0.data();
             bcg_plan_out po{};
@@ -327,10 +332,12 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
             po.bucket_count = L->bucket_count.data();
             po.bucket_offset = L->bucket_offset.data();
             po.uncond_offset = L->uncond_offset.data();
+            po.region_valid = rv.data();
             L->rec0.assign(4 * size_t(n), 0.0f);
             rc3 = bcg_plan_build(&pin, &po);
             if (rc3 == BCG_OK)
-                rc3 = bcg_plan_records(n, desc->plan.steps, L->t0.data(), scl.data(), ur.data(), sg.data(), ns,
+                rc3 = bcg_plan_records(n, desc->plan.steps, L->t0.data(), scl.data(), ur.data(),
+                                       L->d.plan.region_range ? rv.data() : nullptr, sg.data(), ns,
                                        L->rec0.data());
             if (rc3) {
                 bcg_loop_destroy(L);

@@ -14,10 +14,26 @@
 
 namespace bcg {
 
+// Regions of sample i taking part in step t (ComfyUI guide, "calc_cond_batch()":
+// the current timestep must be valid for a cond): start <= t/steps < end in
+// double; every region without ranges.
+__device__ __forceinline__ unsigned region_mask(const StepParams& p, int i, int t) {
+    int k = p.region_count ? p.region_count[i] : p.R;
+    k = k < 0 ? 0 : (k > p.R ? p.R : k);
+    if (!p.region_range) return (1u << k) - 1u;
+    const double prog = double(t) / double(p.range_steps);
+    unsigned v = 0;
+    for (int r = 0; r < k; ++r) {
+        const double* rg = p.region_range + ((int64_t)i * p.R + r) * 2;
+        if (rg[0] <= prog && prog < rg[1]) v |= 1u << r;
+    }
+    return v;
+}
+
 // Bucket, scale and uncond decision of sample i at an active step t.
 // t * nb < 2^20 * 2^10 fits 32 bits (both limits are checked on the host).
 __device__ __forceinline__ void dplan_sample(const StepParams& p, int i, int t, int& b, float& w,
-                                             bool& need_u) {
+                                             bool& need_u, unsigned* valid = nullptr) {
     b = (int)(((uint32_t)t * (uint32_t)p.nb) / (uint32_t)p.steps);
     b = b < p.nb - 1 ? b : p.nb - 1;
     w = p.bucket_cfg[b];
@@ -31,7 +47,14 @@ __device__ __forceinline__ void dplan_sample(const StepParams& p, int i, int t, 
         const float o = p.cfg_override[i];
         if (o == o) w = o;  // NaN = no override
     }
-    const bool cov = p.covered ? p.covered[i] != 0 : true;
+    bool cov = p.covered ? p.covered[i] != 0 : true;
+    if (p.region_range) {
+        const unsigned v = region_mask(p, i, t);
+        cov = ((p.covered_sets[i] >> v) & 1u) != 0;
+        if (valid) *valid = v;
+    } else if (valid) {
+        *valid = 0xfu;
+    }
     need_u = !(w == 1.0f && cov);
 }
 
@@ -81,8 +104,10 @@ __device__ __forceinline__ void plan_workgroup(const StepParams& p, int* sh, int
                 int b2;
                 float w2;
                 bool need2;
-                dplan_sample(p, i, nt, b2, w2, need2);
-                r = float4{p.sigmas[nt], p.sigmas[nt + 1], w2, __uint_as_float(need2 ? 3u : 1u)};
+                unsigned v2;
+                dplan_sample(p, i, nt, b2, w2, need2, &v2);
+                r = float4{p.sigmas[nt], p.sigmas[nt + 1], w2,
+                           __uint_as_float((need2 ? 3u : 1u) | ((v2 & 0xfu) << 2))};
             }
             reinterpret_cast<float4*>(p.record_out)[i] = r;
         }

@@ -383,6 +383,7 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     StepScalars s;
     float sig, sgn;
     bool keep_u;
+    unsigned valid = 0xfu;  // regions taking part in this step
     if (p.record_in) {
         const float4 r = reinterpret_cast<const float4*>(p.record_in)[i];
         const uint32_t fl = __float_as_uint(r.w);
@@ -391,6 +392,7 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         sgn = r.y;
         s.w = r.z;
         keep_u = (fl & 2u) != 0;
+        valid = (fl >> 2) & 0xfu;
     } else {
         const int t = p.step_idx[i];
         if (t < 0 || t >= p.t_end) return;
@@ -398,10 +400,11 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         sgn = p.sigmas[t + 1];
         if (p.dplan) {
             int b;
-            dplan_sample(p, i, t, b, s.w, keep_u);
+            dplan_sample(p, i, t, b, s.w, keep_u, &valid);
         } else {
             s.w = p.scale[i];
             keep_u = p.uncond_row[i] >= 0;
+            if (NR > 0 && p.region_range) valid = region_mask(p, i, t);
         }
     }
     SampleRegions<NR> sr;
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
                 sr.rd[r].h = b[1] - b[0];
                 sr.rd[r].x0 = b[2];
                 sr.rd[r].w = b[3] - b[2];
-                sr.rd[r].strength = p.region_strength[(int64_t)i * p.R + r];
+                sr.rd[r].strength = ((valid >> r) & 1u) ? p.region_strength[(int64_t)i * p.R + r] : 0.0f;
             } else {
                 sr.rd[r].y0 = sr.rd[r].x0 = 0;
                 sr.rd[r].h = sr.rd[r].w = 0;

@@ -44,7 +44,7 @@ class GuidedSampler:
                  s2=0.25, cfg_override=None, region_count=None, region_frac=None,
                  region_strength=None, mu_region=None, feather=0, mask=None, x_orig=None,
                  device="cuda", wrap=False, sigma_start=0, sigma_last=-1,
-                 force_full_denoise=False, bucket_interp=False):
+                 force_full_denoise=False, bucket_interp=False, region_range=None):
         noise = np.ascontiguousarray(noise, np.float32)
         self.n, self.C, self.H, self.W = noise.shape
         self.steps, self.nb, self.sampler, self.dtype = int(steps), int(num_buckets), sampler, dtype
@@ -72,6 +72,9 @@ class GuidedSampler:
         self.region_count = None if R == 0 else np.ascontiguousarray(region_count, np.int32)
         self.region_frac = None if R == 0 else np.ascontiguousarray(region_frac, np.float64)
         self.region_strength = None if R == 0 else np.ascontiguousarray(region_strength, np.float32)
+        # per-cond validity ranges of sampling progress (none: always valid)
+        self.region_range = (None if R == 0 or region_range is None
+                             else np.ascontiguousarray(region_range, np.float64))
         dev = self.device
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
         self.d_sigmas = f32(self.sigmas)
@@ -88,10 +91,13 @@ class GuidedSampler:
         self._tmp = api.plan_out_arrays(n, self.nb, R)
         # Region boxes and coverage do not change between steps: one full plan
         # gives them, later plans reuse the coverage flags.
-        self.covered = None
+        self.covered = self.covered_sets = None
         if R > 0:
             p = self._plan(np.zeros(n, np.int32), self._tmp)
-            self.covered = p.covered.astype(np.uint8)
+            if self.region_range is not None:  # coverage per subset of valid regions
+                self.covered_sets = p.covered_sets.copy()
+            else:
+                self.covered = p.covered.astype(np.uint8)
             self.d_region_box = torch.from_numpy(p.region_box.copy()).to(dev)
             self.d_region_count = torch.from_numpy(self.region_count).to(dev)
             self.d_region_strength = f32(self.region_strength)
@@ -106,6 +112,10 @@ class GuidedSampler:
         self.d_override = None if self.override is None else f32(self.override)
         self.d_covered = (None if self.covered is None else
                           torch.from_numpy(self.covered.astype(np.int32)).to(dev))
+        self.d_covered_sets = (None if self.covered_sets is None else
+                               torch.from_numpy(self.covered_sets.view(np.int16)).to(dev))
+        self.d_region_range = (None if self.region_range is None else
+                               torch.from_numpy(self.region_range).to(dev))
 
     @classmethod
     def from_inputs(cls, inp, **kw):
@@ -120,17 +130,20 @@ class GuidedSampler:
                    region_count=inp.region_count if sp.regions > 0 else None,
                    region_frac=inp.region_frac, region_strength=inp.region_strength,
                    mu_region=inp.mu_region, feather=sp.feather, mask=inp.mask,
-                   x_orig=inp.x_orig, bucket_interp=sp.bucket_interp, **kw)
+                   x_orig=inp.x_orig, bucket_interp=sp.bucket_interp,
+                   region_range=inp.region_range if sp.regions > 0 else None, **kw)
 
     # ------------------------------------------------------------ host plan
 
     def _plan(self, t, out):
         cov = getattr(self, "covered", None)
+        sets = getattr(self, "covered_sets", None)
         return api.bcg_plan_build(t, self.steps, self.table, C=self.C, H=self.H, W=self.W,
                                   cfg_override=self.override, region_count=self.region_count,
                                   region_frac=self.region_frac,
                                   region_strength=self.region_strength, max_regions=self.R,
-                                  covered=cov, out=out, bucket_cfg_end=self.table_end)
+                                  covered=cov, out=out, bucket_cfg_end=self.table_end,
+                                  region_range=self.region_range, covered_sets=sets)
 
     def step_indices(self, k: int) -> np.ndarray:
         t = self.start.astype(np.int64) + k
@@ -182,7 +195,8 @@ class GuidedSampler:
                         feather=self.feather, region_count=self.d_region_count,
                         region_box=self.d_region_box, region_strength=self.d_region_strength,
                         mu_region=self.d_mu_region, x_orig=self.d_x_orig, mask=self.d_mask,
-                        stats=stats, workspace=workspace, cache_hint=cache_hint)
+                        stats=stats, workspace=workspace, cache_hint=cache_hint,
+                        region_range=self.d_region_range, steps=self.steps)
 
     def step(self, k: int, x, x_out=None, stats=None, workspace=None, cache_hint=0):
         """Launch k of the loop: plan, upload, one fused guided step."""
@@ -192,7 +206,8 @@ class GuidedSampler:
 
     def records(self, k: int):
         """Sample records of launch k's step indices (host float32 [n, 4])."""
-        return api.plan_records(self.plan(k), self.step_indices(k), self.steps, self.sigmas)
+        return api.plan_records(self.plan(k), self.step_indices(k), self.steps, self.sigmas,
+                                ranged=self.region_range is not None)
 
     def dplan_step(self, x, step_in, step_out=None, x_out=None, plan_out=None, cache_hint=0,
                    record_in=None, record_out=None):
@@ -205,7 +220,8 @@ class GuidedSampler:
                               step_in=step_in, step_out=step_out, cfg_override=self.d_override,
                               covered=self.d_covered, wrap=self.wrap, plan_out=plan_out,
                               bucket_cfg_end=self.d_table_end, record_in=record_in,
-                              record_out=record_out,
+                              record_out=record_out, region_range=self.d_region_range,
+                              covered_sets=self.d_covered_sets,
                               sampler=self.sampler, s2=self.s2, feather=self.feather,
                               region_count=self.d_region_count, region_box=self.d_region_box,
                               region_strength=self.d_region_strength, mu_region=self.d_mu_region,
@@ -271,7 +287,9 @@ class NativeLoop:
             dplan = api.device_plan(s.steps, s.d_table, self.dev_steps[0, 0],
                                     step_out=self.dev_steps[0, 1], cfg_override=s.d_override,
                                     covered=s.d_covered, wrap=s.wrap, out=self.plan_out,
-                                    bucket_cfg_end=s.d_table_end, sigmas=s.d_sigmas)
+                                    bucket_cfg_end=s.d_table_end, sigmas=s.d_sigmas,
+                                    region_range=s.d_region_range, covered_sets=s.d_covered_sets,
+                                    region_count=s.d_region_count)
         else:
             self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
             self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
@@ -290,7 +308,8 @@ class NativeLoop:
         plan = L.PlanIn(n, s.steps, s.nb, s.C, s.H, s.W, R, npp(s.table, np.float32), None,
                         npp(s.override, np.float32), npp(s.region_count, np.int32),
                         npp(s.region_frac, np.float64), npp(s.region_strength, np.float32),
-                        npp(s.covered, np.uint8), npp(s.table_end, np.float32))
+                        npp(s.covered, np.uint8), npp(s.table_end, np.float32),
+                        npp(s.region_range, np.float64), npp(s.covered_sets, np.uint16))
         ptr = api._ptr
         step = L.StepArgs(n, s.C, s.H, s.W, api._DT[s.tdtype], api._SAMPLER[s.sampler], R,
                           s.feather, 0, s.d_sigmas.numel(),
@@ -299,7 +318,8 @@ class NativeLoop:
                           ptr(self.x), ptr(self.x_out), ptr(s.d_sigmas), None, None, None, None,
                           ptr(s.d_mu_u), ptr(s.d_mu_c), ptr(s.d_region_count),
                           ptr(s.d_region_box), ptr(s.d_region_strength), ptr(s.d_mu_region),
-                          ptr(s.d_x_orig), ptr(s.d_mask), None, None, 0)
+                          ptr(s.d_x_orig), ptr(s.d_mask), None, None, 0, ptr(s.d_region_range),
+                          s.steps)
         self.desc = L.LoopDesc(plan, npp(s.start, np.int32), 1 if s.wrap else 0, rows,
                                api._ptr(self.h_slab), api._ptr(self.d_slab), reps,
                                stride if reps > 1 else 0, P, 1 if async_upload else 0,

@@ -146,6 +146,11 @@ int bucket_bounds(int curve, double p0, double p1, double p2, int num_buckets,
  *   the uncond branch is skipped iff scale[i] == 1.0f and the sample's conds
  *   cover every latent pixel (no regions, or the boxes with strength > 0
  *   cover the frame); otherwise it is kept (uncovered pixels use it).
+ *   Validity ranges ([S] "calc_cond_batch()": each cond entry is checked for
+ *   the current timestep): with region_range, region r of sample i takes part
+ *   in step t iff start <= t/steps < end (double); region_valid[i] gets the
+ *   bit mask of those regions and coverage is that of the valid ones (a
+ *   sample with regions but none valid is not covered).
  * Layout: cond rows are the active samples stably ordered by (bucket, i) and
  * follow the uncond half; the uncond half is the same order without skipped
  * samples.  order[0..n_active) lists the active samples in that order.
@@ -176,6 +181,11 @@ typedef struct {
                                         arrays are not read and region outputs not written */
     const float* bucket_cfg_end;     /* [num_buckets] or NULL: bucket-end scales for the
                                         within-bucket interpolation (bucket_bounds) */
+    const double* region_range;      /* [n][R][2] (start, end) progress or NULL (always valid) */
+    const uint16_t* covered_sets;    /* [n] or NULL: precomputed coverage of every subset of
+                                        regions (bit s: the regions in bit mask s cover the
+                                        frame), e.g. an earlier call's covered_sets_out; needed
+                                        with region_range when the region arrays are not read */
 } bcg_plan_in;
 
 typedef struct {
@@ -189,9 +199,11 @@ typedef struct {
     int32_t* uncond_offset;          /* [num_buckets+1] exclusive prefix, uncond half */
     int32_t* region_box;             /* [n][R][4] or NULL */
     int64_t* region_off;             /* [n*R+1] or NULL */
-    uint8_t* covered_out;            /* [n] or NULL: coverage flags used for the skip */
+    uint8_t* covered_out;            /* [n] or NULL: coverage flags of all regions */
     int32_t n_active;                /* out */
     int32_t n_uncond;                /* out */
+    uint16_t* covered_sets_out;      /* [n] or NULL: coverage of every subset of regions */
+    int32_t* region_valid;           /* [n] or NULL: regions taking part in this step (bits) */
 } bcg_plan_out;
 
 int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out);
@@ -259,6 +271,9 @@ typedef struct {
     float* stats;                    /* device [n][3] or NULL */
     void* workspace;                 /* device scratch for stats, or NULL */
     size_t workspace_bytes;
+    const double* region_range;      /* device [n][R][2] (start, end) progress or NULL: region r
+                                        takes part iff start <= t/steps < end (as the plan) */
+    int32_t steps;                   /* trajectory length, with region_range */
 } bcg_step_args;
 
 int guided_step(const bcg_step_args* args, void* stream);
@@ -291,7 +306,8 @@ size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
  * Sample records (four floats per sample): (sigma, sigma', scale, flags) of
  * the sample's step t, with sigma = sigmas[t], sigma' = sigmas[t+1], scale as
  * above and flags the bit pattern of the fourth float: bit 0 = active
- * (0 <= t < steps), bit 1 = uncond branch kept; an inactive sample's record
+ * (0 <= t < steps), bit 1 = uncond branch kept, bits 2..5 = the regions
+ * valid at t (all of them without validity ranges); an inactive sample's record
  * is all zero bits.  A step that reads its records needs no load that waits
  * on another (its plan wrote them one launch earlier); they must describe
  * step_in.  bcg_plan_records builds them on the host for a first step.
@@ -328,18 +344,25 @@ typedef struct {
     const float* sigmas;             /* device [num_sigmas]: the schedule, for record_out
                                         (guided_step_dplan uses its own args->sigmas) */
     int32_t num_sigmas;
+    const double* region_range;      /* device [n][R][2] or NULL: validity ranges, as the host
+                                        plan (with them covered_sets replaces covered) */
+    const uint16_t* covered_sets;    /* device [n]: bcg_plan_build's covered_sets_out */
+    const int32_t* region_count;     /* device [n] (with region_range; guided_step_dplan uses
+                                        args->region_count) */
+    int32_t max_regions;             /* R, the stride of region_range */
 } bcg_device_plan;
 
 /*
  * bcg_plan_records -- sample records (see above) of step indices step_idx from
- * a host plan of the same indices (bcg_plan_build's scale and uncond_row) and
- * the schedule; all host arrays, records [n][4] out.  Active means
+ * a host plan of the same indices (bcg_plan_build's scale, uncond_row and
+ * region_valid, which may be NULL: every region valid) and the schedule; all
+ * host arrays, records [n][4] out.  Active means
  * 0 <= t < steps and t + 1 < num_sigmas.
  * Errors: BCG_EINVAL (NULL pointer, n < 0, steps < 1, num_sigmas < 1).
  */
 int bcg_plan_records(int n, int steps, const int32_t* step_idx, const float* scale,
-                     const int32_t* uncond_row, const float* sigmas, int num_sigmas,
-                     float* records);
+                     const int32_t* uncond_row, const int32_t* region_valid,
+                     const float* sigmas, int num_sigmas, float* records);
 
 /*
  * bcg_plan_device -- the plan of one step for n samples, built by one

@@ -111,3 +111,44 @@ def test_interpolated_scale_device_plan_matches_oracle_and_host_path():
         assert np.array_equal(out["scale"].cpu().numpy().view(np.uint32), ref["scale"].view(np.uint32)), k
         assert np.array_equal(out["uncond_row"].cpu().numpy(), ref["uncond_row"]), k
     assert torch.equal(x, xh)
+
+
+@pytest.mark.parametrize("dtype,sampler", [("f32", "euler"), ("bf16", "heun"), ("f32", "heun")])
+def test_region_validity_ranges_trajectory_matches_mirror(dtype, sampler):
+    sp = W.small_spec(n=7, C=3, H=16, W=24, steps=10, num_buckets=3, dtype=dtype, sampler=sampler,
+                      regions=3, region_ranges=True, inpaint=(sampler == "heun"), skip_frac=0.5,
+                      curve=W.Curve("linear", 2.0, 1.0), feather=3)
+    inp = W.make_inputs(sp)
+    inp.region_range[0] = (0.95, 1.0)  # sample 0: no region valid for most steps
+    s = _sampler(inp)
+    x = s.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(x), M.trajectory32(inp))
+
+
+def test_region_validity_ranges_device_plan_and_loop_equal_host_path():
+    from bucketed_classifier_free_amd import api
+    sp = W.small_spec(n=9, C=2, H=16, W=24, steps=12, num_buckets=4, regions=2,
+                      region_ranges=True, skip_frac=0.5, curve=W.Curve("linear", 2.0, 1.0))
+    inp = W.make_inputs(sp)
+    s = _sampler(inp)
+    xh = s.run()
+    # fused device-plan steps reading the records their plans write
+    x = s.init_state()
+    t0 = s.step_indices(0)
+    steps = [torch.from_numpy(t0).cuda(), torch.empty(sp.n, dtype=torch.int32, device="cuda")]
+    recs = [torch.from_numpy(s.records(0)).cuda(), torch.zeros((sp.n, 4), device="cuda")]
+    for k in range(sp.steps):
+        s.dplan_step(x, steps[k & 1], steps[(k + 1) & 1], record_in=recs[k & 1], record_out=recs[(k + 1) & 1])
+        torch.cuda.synchronize()
+        got = recs[(k + 1) & 1].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), s.records(k + 1).view(np.uint32)), k
+    assert torch.equal(x, xh)
+    # the native loop, host plans and device plans
+    for dev in (False, True):
+        y = s.init_state()
+        loop = s.native_loop(y, upload_batch=2, device_plan=dev)
+        loop.run(0, sp.steps)
+        torch.cuda.synchronize()
+        loop.close()
+        assert torch.equal(y, xh), dev

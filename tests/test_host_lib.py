@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == L.ABI_VERSION == 5
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 6
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -369,6 +369,34 @@ def test_plan_records_from_host_plan():
     p = bcg.bcg_plan_build(t, 10, table, cfg_override=np.float32([np.nan, np.nan, np.nan, np.nan, 1.0]))
     r = bcg.api.plan_records(p, t, 10, sig)
     flags = r[:, 3].view(np.uint32)
-    assert list(flags) == [3, 1, 0, 0, 1]          # active, uncond kept / skipped at scale 1
+    assert list(flags & 3) == [3, 1, 0, 0, 1]      # active, uncond kept / skipped at scale 1
+    assert list(flags >> 2) == [15, 15, 0, 0, 15]  # no validity ranges: every region valid
     assert r[0, 0] == sig[0] and r[1, 1] == sig[10] == 0 and r[4, 2] == np.float32(1.0)
     assert (r[2:4] == 0).all()
+
+
+def test_plan_with_validity_ranges_bit_exact():
+    sp = W.small_spec(n=40, C=2, H=24, W=32, steps=20, num_buckets=4, regions=3, region_ranges=True,
+                      curve=W.Curve("linear", 2.0, 1.0), skip_frac=0.5, seed=12)
+    inp = W.make_inputs(sp)
+    table = D.bucket_table("linear", 2.0, 1.0, 0.0, 4)
+    kw = dict(C=sp.C, H=sp.H, W=sp.W, cfg_override=inp.cfg_override, max_regions=3,
+              region_range=inp.region_range)
+    full0 = bcg.bcg_plan_build(np.zeros(sp.n, np.int32), sp.steps, table, region_count=inp.region_count,
+                               region_frac=inp.region_frac, region_strength=inp.region_strength, **kw)
+    for k in range(sp.steps):
+        t = (inp.start_step + k).astype(np.int32)
+        ref = D.build_plan(t, sp.steps, 4, table, inp.cfg_override, D.coverage(inp, t))
+        for p in (bcg.bcg_plan_build(t, sp.steps, table, region_count=inp.region_count,
+                                     region_frac=inp.region_frac,
+                                     region_strength=inp.region_strength, **kw),
+                  bcg.bcg_plan_build(t, sp.steps, table, region_count=inp.region_count,
+                                     covered_sets=full0.covered_sets, **kw)):
+            assert np.array_equal(p.uncond_row, ref["uncond_row"]), k
+            assert np.array_equal(p.scale.view(np.uint32), ref["scale"].view(np.uint32))
+            for i in range(sp.n):
+                if 0 <= t[i] < sp.steps:
+                    want = sum(1 << r for r in D.valid_regions(inp, i, int(t[i])))
+                    assert p.region_valid[i] == want, (k, i)
+    with pytest.raises(L.BCGError):  # ranges without region arrays or subset coverage
+        bcg.bcg_plan_build(np.zeros(sp.n, np.int32), sp.steps, table, covered=full0.covered, **kw)
