@@ -19,6 +19,11 @@ Two modes:
   kernel does it.  Mode M is itself pinned to mode D (per-step tolerance) and
   to the special cases the pages fix.
 
+A third module, ``weight_patch``, is the oracle of the weight-patch workload
+(a weight with its diff and low-rank patches applied, stored with stochastic
+rounding): float64 definition, the kernel's float32 order and the
+counter-based generator of the rounding bits.
+
 Parity status per function is stated in each module's header.
 """
-from . import definition, mirror32  # noqa: F401
+from . import definition, mirror32, weight_patch  # noqa: F401
