@@ -20,14 +20,17 @@ BCG_MAX_CHANNELS = 64
 BCG_MAX_FEATHER = 64
 BCG_MAX_DEVICE_BUCKETS = 1024
 BCG_MAX_DEVICE_STEPS = 1 << 20
-ABI_VERSION = 6
+BCG_MAX_PATCHES = 8
+BCG_PATCH = {"diff": 0, "lowrank": 1}
+BCG_ROUND = {"nearest": 0, "stochastic": 1}
+ABI_VERSION = 7
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
            "bucket_bounds",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
            "area_accumulate", "mask_blend", "bcg_plan_records", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
-           "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy"]
+           "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy", "weight_patch"]
 
 vp, i32p, i64p, f32p, f64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64),
                               C.POINTER(C.c_float), C.POINTER(C.c_double))
@@ -84,6 +87,18 @@ class DevicePlan(C.Structure):
                 ("max_regions", C.c_int32)]
 
 
+class Patch(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("offset", C.c_int32), ("rows", C.c_int32), ("rank", C.c_int32),
+                ("dtype", C.c_int32), ("strength_patch", C.c_float), ("strength_model", C.c_float),
+                ("reserved", C.c_int32), ("diff", vp), ("up", vp), ("down", vp)]
+
+
+class WeightArgs(C.Structure):
+    _fields_ = [("rows", C.c_int32), ("cols", C.c_int32), ("w_dtype", C.c_int32),
+                ("out_dtype", C.c_int32), ("num_patches", C.c_int32), ("rounding", C.c_int32),
+                ("seed", C.c_uint64), ("w", vp), ("out", vp), ("patches", vp)]
+
+
 class LoopDesc(C.Structure):
     _fields_ = [("plan", PlanIn), ("start", vp), ("wrap", C.c_int32), ("rows", C.c_int32),
                 ("host_slab", vp), ("dev_slab", vp), ("replicas", C.c_int32),
@@ -125,6 +140,7 @@ def lib():
         L.bcg_loop_create.argtypes = [C.POINTER(LoopDesc), C.POINTER(vp)]
         L.bcg_loop_run.argtypes = [vp, C.c_int, C.c_int, vp, C.POINTER(C.c_float)]
         L.bcg_loop_destroy.argtypes = [vp]
+        L.weight_patch.argtypes = [C.POINTER(WeightArgs), vp]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or C.c_int
         L.guided_step_workspace_size.restype = C.c_size_t

@@ -462,3 +462,56 @@ def mask_blend(a, b, mask, out, stream=None):
         raise ValueError(f"mask: shape {tuple(mask.shape)} is neither [n,1,H,W] nor [1,1,H,W]")
     L.check(L.lib().mask_blend(n, Cc, H, W, _DT[a.dtype], _ptr(a), _ptr(b), _ptr(mask), mps,
                                _ptr(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------- weight patches
+
+@dataclass
+class WeightPatch:
+    """One patch of weight_patch: a ``diff`` [rows, cols] (float32 or
+    bfloat16), or a low-rank pair ``up`` [rows, r] and ``down`` [r, cols]
+    (bfloat16), covering weight rows [offset, offset + rows)."""
+    strength_patch: float = 1.0
+    strength_model: float = 1.0
+    offset: int = 0
+    diff: torch.Tensor | None = None
+    up: torch.Tensor | None = None
+    down: torch.Tensor | None = None
+
+
+def _patch_struct(p: WeightPatch, cols: int):
+    if (p.diff is None) == (p.up is None and p.down is None):
+        raise ValueError("a patch is either a diff or a low-rank (up, down) pair")
+    if p.diff is not None:
+        _dev(p.diff, "diff")
+        if p.diff.dim() != 2 or p.diff.shape[1] != cols or p.diff.dtype not in _DT:
+            raise ValueError(f"diff must be [rows, {cols}] float32 or bfloat16")
+        return L.Patch(L.BCG_PATCH["diff"], int(p.offset), p.diff.shape[0], 0, _DT[p.diff.dtype],
+                       float(p.strength_patch), float(p.strength_model), 0, _ptr(p.diff), None, None)
+    _dev(p.up, "up", torch.bfloat16)
+    _dev(p.down, "down", torch.bfloat16)
+    if p.up.dim() != 2 or p.down.dim() != 2 or p.down.shape[1] != cols or p.up.shape[1] != p.down.shape[0]:
+        raise ValueError(f"up must be [rows, r] and down [r, {cols}]")
+    return L.Patch(L.BCG_PATCH["lowrank"], int(p.offset), p.up.shape[0], p.up.shape[1], L.BCG_BF16,
+                   float(p.strength_patch), float(p.strength_model), 0, None, _ptr(p.up), _ptr(p.down))
+
+
+def weight_patch(w, out, patches=(), *, rounding: str = "stochastic", seed: int = 0, stream=None):
+    """out = w with ``patches`` (WeightPatch list) applied in order and stored
+    in out's dtype (bfloat16: nearest or stochastic rounding keyed by ``seed``);
+    see include/bcg.h.  ``out`` may be ``w`` itself."""
+    _dev(w, "w")
+    if w.dim() != 2 or w.dtype not in _DT:
+        raise ValueError("w must be a [rows, cols] float32 or bfloat16 tensor")
+    _dev(out, "out", shape=w.shape)
+    if out.dtype not in _DT:
+        raise ValueError("out must be float32 or bfloat16")
+    if rounding not in L.BCG_ROUND:
+        raise ValueError(f"unknown rounding {rounding!r}")
+    if len(patches) > L.BCG_MAX_PATCHES:
+        raise ValueError(f"at most {L.BCG_MAX_PATCHES} patches per call")
+    rows, cols = w.shape
+    arr = (L.Patch * max(len(patches), 1))(*[_patch_struct(p, cols) for p in patches])
+    a = L.WeightArgs(rows, cols, _DT[w.dtype], _DT[out.dtype], len(patches), L.BCG_ROUND[rounding],
+                     int(seed) & (2 ** 64 - 1), _ptr(w), _ptr(out), ct.addressof(arr) if patches else None)
+    L.check(L.lib().weight_patch(ct.byref(a), _stream(stream)))

@@ -15,6 +15,9 @@
  *       "debug chain" (plan built in the scheduler before launch, guidance in
  *       fp32 for half-precision storage, norm logging), section 5 (guidance
  *       curve shapes).
+ *   [P] "10 · ModelPatcher and weight views" (ComfyUI guide, model-patcher
+ *       chapter): "patches record format", "how a weight is patched",
+ *       "strength_model and strength_patch", "offset patch".
  *
  * Conventions (all entry points):
  *   - Every function returns an int status: BCG_OK (0) or a negative code.
@@ -61,6 +64,11 @@ enum { BCG_PHASE_EULER = 0, BCG_PHASE_HEUN_PREDICT = 1, BCG_PHASE_HEUN_CORRECT =
 #define BCG_MAX_BUCKETS 4096
 #define BCG_MAX_DEVICE_BUCKETS 1024  /* buckets of a device-built plan */
 #define BCG_MAX_DEVICE_STEPS (1 << 20)  /* trajectory length of a device-built plan */
+#define BCG_MAX_PATCHES 8    /* patches of one weight_patch call */
+
+/* Patch kinds and weight rounding (weight_patch). */
+enum { BCG_PATCH_DIFF = 0, BCG_PATCH_LOWRANK = 1 };
+enum { BCG_ROUND_NEAREST = 0, BCG_ROUND_STOCHASTIC = 1 };
 
 /* Thread-local message describing the last failed call ("" if none). */
 const char* bcg_last_error(void);
@@ -486,6 +494,67 @@ int area_accumulate(int n, int C, int H, int W, int feather, int max_regions,
  */
 int mask_blend(int n, int C, int H, int W, int dtype, const void* a, const void* b,
                const float* mask, int mask_per_sample, void* out, void* stream);
+
+/*
+ * weight_patch -- one weight with its patches applied: [P] "patches record
+ * format" (a patch entry: strength_patch, the patch value, strength_model,
+ * an optional offset), "strength_model and strength_patch" (W' =
+ * strength_model W + strength_patch dW, dW a low-rank pair or a direct
+ * diff), "offset patch" (a patch on a slice of the tensor), "how a weight is
+ * patched" (every patch of the weight overlaid in a compute precision, then
+ * written back by stochastic rounding or a cast).
+ *
+ * w and out are device [rows, cols], row-major, in w_dtype and out_dtype.
+ * Patch q covers weight rows [offset_q, offset_q + rows_q).  Per element, in
+ * fp32 and in patch order:
+ *   a = w;  for q covering the row:  a = fma(sp_q, d_q, sm_q * a)
+ * with d_q = diff_q[row - offset_q, col] (BCG_PATCH_DIFF), or
+ * sum_k up_q[row - offset_q, k] down_q[k, col] (BCG_PATCH_LOWRANK: bf16
+ * factors, exact products summed in fp32 on the matrix cores, in an order
+ * the kernel chooses).  The store: out = a (BCG_F32), or bf16 of a, by
+ * nearest even (BCG_ROUND_NEAREST), or stochastically (BCG_ROUND_STOCHASTIC):
+ * 16 random bits r_e are added to a's fp32 bit pattern and the high 16 bits
+ * kept (rounds away from zero with probability equal to the dropped
+ * fraction; NaN and infinities round to nearest).  r_e of the element with
+ * flat index e = row * cols + col is the 16-bit half (e mod 2, low half
+ * first) of word (e mod 8) / 2 of Philox4x32-10 (Salmon et al., SC 2011)
+ * at counter (low, high word of e / 8, 0, 0) and key (low, high word of
+ * seed): a given seed rounds a given element the same way however the
+ * weight is tiled or launched.
+ *
+ * out may equal w (same dtype), in place; it must not otherwise overlap w or
+ * any patch tensor.  patches is a host array, read during the call only.
+ * Errors: BCG_ESHAPE (rows or cols negative, a patch outside the weight,
+ * rank < 1), BCG_EDTYPE (dtype not BCG_F32/BCG_BF16, low-rank factors not
+ * bf16), BCG_EINVAL (NULL pointer, num_patches outside [0,
+ * BCG_MAX_PATCHES], unknown kind or rounding, overlaps), BCG_EHIP.
+ */
+typedef struct {
+    int32_t kind;                    /* BCG_PATCH_DIFF | BCG_PATCH_LOWRANK */
+    int32_t offset;                  /* first weight row covered, >= 0 */
+    int32_t rows;                    /* rows covered, >= 0, offset + rows <= weight rows */
+    int32_t rank;                    /* low-rank r >= 1 (ignored for a diff) */
+    int32_t dtype;                   /* diff: BCG_F32 | BCG_BF16; low-rank: BCG_BF16 */
+    float strength_patch;            /* sp */
+    float strength_model;            /* sm */
+    int32_t reserved;                /* 0 */
+    const void* diff;                /* device [rows, cols] (diff), else NULL */
+    const void* up;                  /* device bf16 [rows, rank] (low-rank), else NULL */
+    const void* down;                /* device bf16 [rank, cols] (low-rank), else NULL */
+} bcg_patch;
+
+typedef struct {
+    int32_t rows, cols;              /* >= 0 */
+    int32_t w_dtype, out_dtype;      /* BCG_F32 | BCG_BF16 */
+    int32_t num_patches;             /* [0, BCG_MAX_PATCHES] */
+    int32_t rounding;                /* BCG_ROUND_* (bf16 out; ignored for f32) */
+    uint64_t seed;                   /* key of the stochastic rounding */
+    const void* w;                   /* device [rows, cols] */
+    void* out;                       /* device [rows, cols] */
+    const bcg_patch* patches;        /* host [num_patches] (NULL if none) */
+} bcg_weight_args;
+
+int weight_patch(const bcg_weight_args* args, void* stream);
 
 /*
  * bcg_loop_* -- the sampler loop's per-step work in native code, for

@@ -28,12 +28,12 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == L.ABI_VERSION == 6
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 7
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -400,3 +400,50 @@ def test_plan_with_validity_ranges_bit_exact():
                     assert p.region_valid[i] == want, (k, i)
     with pytest.raises(L.BCGError):  # ranges without region arrays or subset coverage
         bcg.bcg_plan_build(np.zeros(sp.n, np.int32), sp.steps, table, covered=full0.covered, **kw)
+
+
+def _weight_args(rows=64, cols=128, patches=()):
+    arr = (L.Patch * max(len(patches), 1))(*patches)
+    a = L.WeightArgs(rows, cols, L.BCG_BF16, L.BCG_BF16, len(patches), L.BCG_ROUND["stochastic"], 5,
+                     _fake(1), _fake(2), C.addressof(arr) if patches else None)
+    return a, arr
+
+
+def test_weight_patch_validates_before_launch():
+    lib = L.lib()
+    diff = lambda **kw: L.Patch(**{**dict(kind=0, offset=0, rows=64, rank=0, dtype=L.BCG_BF16,
+                                          strength_patch=1.0, strength_model=1.0, diff=_fake(3)), **kw})
+    lowr = lambda **kw: L.Patch(**{**dict(kind=1, offset=0, rows=64, rank=16, dtype=L.BCG_BF16,
+                                          strength_patch=1.0, strength_model=1.0, up=_fake(4),
+                                          down=_fake(5)), **kw})
+    assert lib.weight_patch(None, None) == L.BCG_EINVAL
+    cases = [
+        (dict(rows=-1), [], L.BCG_ESHAPE),
+        ({}, [diff(offset=10)], L.BCG_ESHAPE),           # rows [10, 74) outside 64
+        ({}, [diff(offset=-1, rows=4)], L.BCG_ESHAPE),
+        ({}, [lowr(rank=0)], L.BCG_ESHAPE),
+        ({}, [lowr(dtype=L.BCG_F32)], L.BCG_EDTYPE),
+        ({}, [diff(dtype=7)], L.BCG_EDTYPE),
+        ({}, [diff(kind=3)], L.BCG_EINVAL),
+        ({}, [diff(diff=None)], L.BCG_EINVAL),
+        ({}, [lowr(down=None)], L.BCG_EINVAL),
+        ({}, [diff(diff=C.c_void_p(_fake(2).value + 64))], L.BCG_EINVAL),  # diff overlaps out
+    ]
+    for kw, pats, code in cases:
+        a, keep = _weight_args(patches=pats, **{k: v for k, v in kw.items() if k in ("rows", "cols")})
+        assert lib.weight_patch(C.byref(a), None) == code, (kw, code, lib.bcg_last_error())
+    a, keep = _weight_args(patches=[diff()] * 9)
+    a.num_patches = 9
+    assert lib.weight_patch(C.byref(a), None) == L.BCG_EINVAL
+    a, keep = _weight_args()
+    a.rounding = 2
+    assert lib.weight_patch(C.byref(a), None) == L.BCG_EINVAL
+    a.rounding, a.w_dtype = 0, 5
+    assert lib.weight_patch(C.byref(a), None) == L.BCG_EDTYPE
+    a.w_dtype, a.out_dtype, a.out = L.BCG_F32, L.BCG_BF16, C.c_void_p(_fake(1).value + 2)
+    assert lib.weight_patch(C.byref(a), None) == L.BCG_EINVAL       # w and out overlap
+    assert b"overlap" in lib.bcg_last_error()
+    # an empty weight is a no-op, even with NULL arrays
+    a, keep = _weight_args(rows=0, patches=[diff(rows=0, diff=None)])
+    a.w = a.out = None
+    assert lib.weight_patch(C.byref(a), None) == L.BCG_OK
