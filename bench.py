@@ -279,6 +279,139 @@ def rows_bench(inp, args):
         flush=True)
 
 
+def weight_cpu_baseline(inp, seconds: float):
+    """The weight-patch oracle (float64 definition of the patched rows, then
+    the float32 order and the store) on consecutive blocks of 64 rows."""
+    from oracle import weight_patch as P
+    from workloads import weights as WW
+    sp = inp.spec
+    t0 = time.perf_counter()
+    done = 0
+    r = 0
+    while time.perf_counter() - t0 < seconds:
+        r1 = min(r + 64, sp.rows)
+        pats, specs = [], []
+        for pd in inp.patches:
+            ps = pd.spec
+            a, b = max(r, ps.offset), min(r1, ps.offset + pd.rows)
+            if a >= b:
+                continue
+            one = WW.PatchSpec(ps.kind, a - r, b - a, ps.rank, ps.strength_patch, ps.strength_model, ps.dtype)
+            specs.append(one)
+            k0, k1 = a - ps.offset, b - ps.offset
+            pats.append(WW.PatchData(one, b - a, None if pd.diff is None else pd.diff[k0:k1],
+                                     None if pd.up is None else pd.up[k0:k1], pd.down))
+        sub = WW.WeightInputs(WW.WeightSpec(sp.name, r1 - r, sp.cols, sp.w_dtype, sp.out_dtype, tuple(specs),
+                                            sp.rounding, sp.sr_seed, sp.seed), inp.w[r:r1], pats)
+        acc = P.reference32(sub)
+        P.reference(sub)
+        if sp.rounding == "stochastic" and sp.out_dtype == "bf16":
+            P.sr_bf16(acc, sp.sr_seed, base=r * sp.cols)
+        else:
+            P.store(acc, sp.out_dtype)
+        done += (r1 - r) * sp.cols
+        r = r1 % sp.rows
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "weight elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done // sp.cols} rows of {sp.name} in blocks of 64 (float64 definition, float32 "
+                      f"order and store, NumPy, one thread), {el:.1f} s"}
+
+
+def weight_bench(name, args, cpu=None):
+    """One weight_patch launch per step over resident inputs: the weight, its
+    patch tensors and the output, replicated R times (rotated per launch) so
+    the 256 MB last-level cache cannot hold them between launches; launches
+    captured in a graph and timed with HIP events around its replays."""
+    import torch
+    from bucketed_classifier_free_amd import WeightPatch, weight_patch
+    from workloads import weights as WW
+    sp = WW.weight_config(name)
+    if args.rounding:
+        import dataclasses
+        sp = dataclasses.replace(sp, rounding=args.rounding)
+    inp = WW.make_weight_inputs(sp)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    R = max(1, args.replicas)
+    reps = []
+    for _ in range(R):
+        w = torch.from_numpy(inp.w).cuda().to(tdt[sp.w_dtype])
+        out = torch.empty(w.shape, dtype=tdt[sp.out_dtype], device="cuda")
+        pats = []
+        for pd in inp.patches:
+            ps = pd.spec
+            if ps.kind == "diff":
+                pats.append(WeightPatch(ps.strength_patch, ps.strength_model, ps.offset,
+                                        diff=torch.from_numpy(pd.diff).cuda().to(tdt[ps.dtype])))
+            else:
+                pats.append(WeightPatch(ps.strength_patch, ps.strength_model, ps.offset,
+                                        up=torch.from_numpy(pd.up).cuda().to(torch.bfloat16),
+                                        down=torch.from_numpy(pd.down).cuda().to(torch.bfloat16)))
+        reps.append((w, out, pats))
+
+    def launch(k):
+        w, out, pats = reps[k % R]
+        weight_patch(w, out, pats, rounding=sp.rounding, seed=sp.sr_seed + k)
+
+    G = R * max(1, -(-16 // R))
+    for k in range(G):
+        launch(k)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(G):
+            launch(k)
+    nrep = max(1, args.steps // G)
+    for _ in range(max(1, args.warmup // G)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(nrep):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if not all(torch.isfinite(r[1].float()).all() for r in reps):
+        raise RuntimeError("non-finite weights after the timed launches")
+    n = nrep * G
+    launch_ms = e0.elapsed_time(e1) / n
+    elems = sp.rows * sp.cols
+    es = {"f32": 4, "bf16": 2}
+    alg = elems * (es[sp.w_dtype] + es[sp.out_dtype])
+    flops = 0
+    for pd in inp.patches:
+        ps = pd.spec
+        if ps.kind == "diff":
+            alg += pd.rows * sp.cols * es[ps.dtype]
+        else:
+            alg += 2 * (pd.rows * ps.rank + ps.rank * sp.cols)
+            flops += 2 * pd.rows * sp.cols * ps.rank
+    achieved = alg / (launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": "weight elements patched/sec on 1 GPU",
+        "value": elems * n / wall, "unit": "weight elements/s", "n_gpus": 1, "steps": n,
+        "warmup": G * max(1, args.warmup // G), "ms_per_step": wall * 1e3 / n,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": sp.name, "weight": [sp.rows, sp.cols], "w_dtype": sp.w_dtype,
+                   "out_dtype": sp.out_dtype, "rounding": sp.rounding,
+                   "patches": [{"kind": p.kind, "offset": p.offset, "rows": d.rows, "rank": p.rank,
+                                "strength_patch": p.strength_patch, "strength_model": p.strength_model}
+                               for p, d in zip(sp.patches, inp.patches)],
+                   "replicas": R, "graph_launches": G},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "kernel": {"name": "weight_patch", "avg_launch_us": launch_ms * 1e3,
+                   "timing": f"HIP events around replays of a {G}-launch graph",
+                   "algorithmic_bytes_per_launch": alg, "lowrank_flops_per_launch": flops,
+                   "mfma_tflops": flops / (launch_ms * 1e-3) / 1e12},
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
 def trajectory(inp, args):
     """Whole trajectories end to end: latent init and every step of the
     schedule (device plans, the steps replayed from one captured graph, one
@@ -337,6 +470,10 @@ def main():
     ap.add_argument("--trajectory", action="store_true",
                     help="time whole trajectories (latent init + every step, active samples only) "
                          "instead of the steady state")
+    ap.add_argument("--weight-patch", default="", metavar="WORKLOAD",
+                    help="time weight_patch on a weight workload (workloads/weights.py) instead")
+    ap.add_argument("--rounding", choices=("nearest", "stochastic"), default="",
+                    help="bf16 rounding of the weight workload (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--upload-batch", type=int, default=8)
@@ -368,6 +505,19 @@ def main():
     import dataclasses
 
     import workloads as W
+
+    if args.weight_patch:
+        from workloads import weights as WW
+        wcpu = None
+        if not args.no_cpu_baseline:  # before anything touches the GPU
+            wcpu = weight_cpu_baseline(WW.make_weight_inputs(WW.weight_config(args.weight_patch)),
+                                       min(args.cpu_seconds, 10.0))
+        import torch
+        from bucketed_classifier_free_amd import load
+        load()
+        torch.cuda.set_device(0)
+        weight_bench(args.weight_patch, args, wcpu)
+        return
 
     spec = W.config(args.workload)
     if args.buckets:

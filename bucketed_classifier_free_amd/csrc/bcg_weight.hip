@@ -3,32 +3,41 @@
 // and weight views": "patches record format", "strength_model and
 // strength_patch", "offset patch", "how a weight is patched").
 //
-// One fused, HBM-bound kernel.  A workgroup owns a 64 x 128 tile of the
-// weight; each lane holds four 8-element row vectors of it in fp32 registers
-// (16-byte accesses, consecutive lanes on consecutive addresses), applies the
-// patches in order and stores the result once.  A diff patch streams its
-// slice of the diff through the same lane layout.  A low-rank patch's delta
-// tile is a genuine contraction (up [64, r] x down [r, 128]) and runs on the
-// matrix cores: `down` is staged 32 k-rows at a time into LDS transposed
-// (k contiguous per column, the B-operand layout of v_mfma_f32_32x32x16_bf16),
-// `up` is read straight from global memory in the A-operand layout, each wave
-// accumulates two 32x32 fp32 sub-tiles, and the tile goes through LDS once to
-// reach the streaming layout.  The stochastic rounding bits come from
-// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
-// easy as 1, 2, 3", SC 2011), one call per 8 consecutive elements.
+// Two HBM-bound kernels; both apply the patches of a weight in order
+// (a = fma(sp, d, sm * a) per element in fp32 registers), load and store each
+// weight element once, and round on the store.
+//
+//   patch_stream_kernel  (no low-rank patch): the weight as a flat sequence
+//     of 8-element row vectors (16-byte accesses, consecutive lanes on
+//     consecutive addresses), each workgroup a contiguous share sized so the
+//     grid is about one resident round (no partly filled last round).
+//   patch_lowrank_kernel: 64 x 128 tiles, one 32 x 64 quarter per wave.  The
+//     low-rank deltas are genuine contractions and run on the matrix cores
+//     as the transposed product dW^T = down^T up^T (v_mfma_f32_32x32x16_bf16),
+//     with the columns of each 32 x 32 sub-tile relabelled so that a lane's
+//     16 accumulators are 16 consecutive weight columns of one weight row:
+//     each lane then holds 32 consecutive elements of one row, the delta is
+//     combined straight from the accumulators, and the weight, the diffs and
+//     the output move in that layout (16-byte accesses).  The factors of all
+//     low-rank patches meeting the tile are concatenated along k and staged
+//     through LDS 32 k-rows per round, double-buffered, by direct
+//     global-to-LDS loads issued one round ahead; `up` goes in k-contiguous
+//     (16-byte fragment reads, XOR-swizzled against bank conflicts), `down`
+//     row-major (the transposed fragment is gathered 2 bytes at a time, with
+//     padding that keeps the two lane halves on different banks).
+//
+// The stochastic rounding bits come from Philox4x32-10 (Salmon, Moraes, Dror
+// and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), one call
+// per 8 consecutive elements.
 #include "bcg_device.h"
 #include "bcg_launch.h"
 
 namespace bcg {
 namespace {
 
-constexpr int TR = 64;       // tile rows
-constexpr int TC = 128;      // tile columns
-constexpr int NT = 256;      // lanes per workgroup
-constexpr int KC = 32;       // rows of `down` staged per chunk
-constexpr int KP = KC + 8;   // LDS row of the transposed chunk, in bf16 (80 bytes)
-constexpr int DP = TC + 4;   // LDS row of the delta tile, in fp32 (528 bytes)
-constexpr int VPL = TR * TC / 8 / NT;  // 8-element vectors per lane (4)
+constexpr int TR = 64;        // low-rank tile rows
+constexpr int TC = 128;       // low-rank tile columns
+constexpr int NT = 256;       // lanes per workgroup
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -41,12 +50,32 @@ struct PatchDev {
     const bf16_t* down;
 };
 
+// One 16-row k-step of the concatenated low-rank factors (strip kernel).
+struct __attribute__((aligned(8))) StepDesc {
+    const bf16_t* up;  // `up` of the step's patch, advanced to the step's first k-column
+    int q;             // patch index
+    int sk;            // first k-row of the step inside the patch
+    int rank;          // the patch's rank
+    int off, rows;     // weight rows the patch covers
+    int flags;         // bit 0: `up` loads 16 bytes at a time; bit 1: last k-step of the patch
+    float sp, sm;      // the patch's strengths
+};
+
 struct WeightParams {
     int rows, cols;
-    int ctiles;       // column tiles
+    int ctiles;       // column tiles (low-rank kernel)
     int np;           // patches
     int stochastic;   // bf16 out: 1 = stochastic rounding
     int vec;          // cols % 8 == 0 and every streamed array 16-byte aligned
+    int kalloc;       // k-rows of one staging round (low-rank kernel)
+    int rtiles;       // 64-row tiles (strip kernel)
+    int grows;        // row-tile groups per column strip (strip kernel)
+    int kt_all;       // concatenated padded rank of every low-rank patch (strip kernel)
+    int steps;        // 16-row k-steps of that concatenation (strip kernel)
+    StepDesc sd[8];   // the k-steps (strip kernel)
+    int nvr;          // 8-element vectors per row (stream kernel)
+    int vpt;          // vectors per lane (stream kernel)
+    uint32_t nvec;    // vectors of the weight (stream kernel)
     uint32_t key0, key1;
     const void* w;
     void* out;
@@ -63,13 +92,13 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        // one 32 x 32 -> 64-bit product each (v_mad_u64_u32), not a low and a high multiply
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
         c0 = n0;
-        c1 = lo1;
+        c1 = (uint32_t)p1;
         c2 = n2;
-        c3 = lo0;
+        c3 = (uint32_t)p0;
     }
 }
 
@@ -172,144 +201,584 @@ __device__ __forceinline__ void store8(const WeightParams& p, TO* out, int64_t e
     }
 }
 
-// ---------------------------------------------------------------- low-rank delta tile
+// ---------------------------------------------------------------- patches in order
 
-struct LowRankLds {
-    bf16_t b[TC * KP];     // down chunk, transposed: b[col * KP + k]
-    float d[TR * DP];      // delta tile, d[row * DP + col]
-};
-
-// The low-rank delta of patch q over the tile at (r0, c0) into s.d (fp32;
-// rows outside the patch and columns outside the weight hold 0).  Called by
-// the whole workgroup (contains barriers); ends with a barrier after the
-// tile is written.
-__device__ __forceinline__ void lowrank_tile(const WeightParams& p, const PatchDev& q, int r0, int c0,
-                                             LowRankLds& s) {
-    const int t = (int)threadIdx.x, l = t & 63, wave = t >> 6;
-    const int wr = (wave & 1) * 32, wc = (wave >> 1) * 64;
-    const int hi = l >> 5, lo = l & 31;
-    // A operand: weight row r0 + wr + lo, i.e. patch row pr.
-    const int pr = r0 + wr + lo - q.offset;
-    const bool arow = pr >= 0 && pr < q.rows;
-    const bf16_t* urow = q.up + (int64_t)(arow ? pr : 0) * q.rank;
-    f32x16_t acc0 = {}, acc1 = {};
-    for (int kc = 0; kc < q.rank; kc += KC) {
-        __syncthreads();  // the previous chunk's B reads are done
+// Diff patch q on a lane vector: weight row `row`, columns c .. c+7 (n of them inside).
+template <typename TA>
+__device__ __forceinline__ void apply_diff(const WeightParams& p, const PatchDev& q, int row, int c, int n,
+                                           bool vec, float (&a)[8]) {
+    const int pr = row - q.offset;
+    if (pr < 0 || pr >= q.rows || n <= 0) return;
+    float d[8];
+    load8<TA>(static_cast<const TA*>(q.diff), (int64_t)pr * p.cols + c, n, vec, d);
 #pragma unroll
-        for (int j = 0; j < (KC * TC / 8) / NT; ++j) {
-            const int v = t + j * NT;
-            const int kr = v >> 4, cv = (v & 15) * 8;
-            const int k = kc + kr, col = c0 + cv;
-            float x[8];
-            if (k < q.rank && col < p.cols) {
-                load8<bf16_t>(q.down, (int64_t)k * p.cols + col, p.cols - col, p.vec != 0, x);
+    for (int e = 0; e < 8; ++e) a[e] = fmaf(q.sp, d[e], q.sm * a[e]);
+}
+
+__device__ __forceinline__ void apply_diff_any(const WeightParams& p, const PatchDev& q, int row, int c, int n,
+                                               bool vec, float (&a)[8]) {
+    if (q.dtype == BCG_BF16) apply_diff<bf16_t>(p, q, row, c, n, vec, a);
+    else apply_diff<float>(p, q, row, c, n, vec, a);
+}
+
+// ---------------------------------------------------------------- stream kernel
+
+template <typename TW, typename TO>
+__global__ __launch_bounds__(NT) void patch_stream_kernel(WeightParams p) {
+    const bool vec = p.vec != 0;
+    const TW* w = static_cast<const TW*>(p.w);
+    TO* out = static_cast<TO*>(p.out);
+    const uint32_t base = blockIdx.x * (uint32_t)(NT * p.vpt) + threadIdx.x;
+    for (int i = 0; i < p.vpt; ++i) {
+        const uint32_t v = base + (uint32_t)(i * NT);
+        if (v >= p.nvec) break;
+        const uint32_t row = v / (uint32_t)p.nvr;
+        const int c = (int)(v - row * (uint32_t)p.nvr) * 8;
+        const int n = p.cols - c;
+        const int64_t e = (int64_t)row * p.cols + c;
+        float a[8];
+        load8<TW>(w, e, n, vec, a);
+        for (int q = 0; q < p.np; ++q) apply_diff_any(p, p.p[q], (int)row, c, n, vec, a);
+        store8<TO>(p, out, e, n, vec, a);
+    }
+}
+
+// ---------------------------------------------------------------- low-rank kernel
+
+constexpr int KMAX = 128;  // concatenated k-rows staged per round (at most)
+
+__device__ __forceinline__ bool hits_tile(const PatchDev& q, int r0) {
+    return q.rows > 0 && r0 < q.offset + q.rows && r0 + TR > q.offset;
+}
+
+__host__ __device__ __forceinline__ int padded_rank(int rank) { return (rank + 15) & ~15; }
+
+// `down` area of a round: k-rows of 256 bytes (128 bf16 columns), 4 per KiB
+// block, 128 bytes of padding after every second block so that rows kl and
+// kl + 8 (read together by the two lane halves) sit on different LDS banks.
+__device__ __forceinline__ int sb_blk(int g) { return g * 1024 + (g >> 1) * 128; }
+__device__ __forceinline__ int sb_off(int kl) { return sb_blk(kl >> 2) + (kl & 3) * 256; }
+__host__ __device__ __forceinline__ int sb_bytes(int k) { return (k / 4) * 1024 + (k / 8) * 128; }
+
+// `up` area of a round: per patch piece of kp k-rows, C = kp / 8 chunks of
+// 16 bytes per tile row; chunk c of row n in slot n C + (c ^ swz(n)), a
+// swizzle (for power-of-two C) that puts 16 consecutive rows at one chunk on
+// 16 different 4-bank groups.
+__device__ __forceinline__ int su_swz(int n, int C) {
+    if (C & (C - 1)) return 0;
+    return (C >= 16 ? n : n / (16 / C)) & (C - 1);
+}
+__device__ __forceinline__ int su_slot(int n, int c, int C) { return n * C + (c ^ su_swz(n, C)); }
+
+// 8 consecutive elements of storage type T in their raw form.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> { u32x4_t v; };
+template <> struct Raw8<float> { f32x4_t a, b; };
+
+__device__ __forceinline__ Raw8<bf16_t> raw_load(const bf16_t* base, int64_t off, int n, bool vec) {
+    Raw8<bf16_t> r;
+    if (vec) {
+        r.v = *reinterpret_cast<const u32x4_t*>(base + off);
+    } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = e < n ? base[off + e] : 0u;
+        r.v = u32x4_t{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+    }
+    return r;
+}
+__device__ __forceinline__ Raw8<float> raw_load(const float* base, int64_t off, int n, bool vec) {
+    Raw8<float> r;
+    if (vec) {
+        r.a = *reinterpret_cast<const f32x4_t*>(base + off);
+        r.b = *reinterpret_cast<const f32x4_t*>(base + off + 4);
+    } else {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = e < n ? base[off + e] : 0.0f;
+        r.a = f32x4_t{x[0], x[1], x[2], x[3]};
+        r.b = f32x4_t{x[4], x[5], x[6], x[7]};
+    }
+    return r;
+}
+__device__ __forceinline__ void raw_store(bf16_t* base, int64_t off, int n, bool vec, const Raw8<bf16_t>& r) {
+    if (vec) {
+        *reinterpret_cast<u32x4_t*>(base + off) = r.v;
+    } else {
+        const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < n) base[off + e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+}
+__device__ __forceinline__ void raw_store(float* base, int64_t off, int n, bool vec, const Raw8<float>& r) {
+    if (vec) {
+        *reinterpret_cast<f32x4_t*>(base + off) = r.a;
+        *reinterpret_cast<f32x4_t*>(base + off + 4) = r.b;
+    } else {
+        const float x[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < n) base[off + e] = x[e];
+    }
+}
+__device__ __forceinline__ void raw_lds_st(unsigned char* q, const Raw8<bf16_t>& r) {
+    *reinterpret_cast<u32x4_t*>(q) = r.v;
+}
+__device__ __forceinline__ void raw_lds_st(unsigned char* q, const Raw8<float>& r) {
+    *reinterpret_cast<f32x4_t*>(q) = r.a;
+    *reinterpret_cast<f32x4_t*>(q + 16) = r.b;
+}
+template <typename T> __device__ __forceinline__ Raw8<T> raw_lds_ld(const unsigned char* q);
+template <> __device__ __forceinline__ Raw8<bf16_t> raw_lds_ld<bf16_t>(const unsigned char* q) {
+    return Raw8<bf16_t>{*reinterpret_cast<const u32x4_t*>(q)};
+}
+template <> __device__ __forceinline__ Raw8<float> raw_lds_ld<float>(const unsigned char* q) {
+    return Raw8<float>{*reinterpret_cast<const f32x4_t*>(q), *reinterpret_cast<const f32x4_t*>(q + 16)};
+}
+__device__ __forceinline__ void raw_unpack(const Raw8<bf16_t>& r, float (&v)[8]) {
+    v[0] = bf16_lo(r.v.x); v[1] = bf16_hi(r.v.x); v[2] = bf16_lo(r.v.y); v[3] = bf16_hi(r.v.y);
+    v[4] = bf16_lo(r.v.z); v[5] = bf16_hi(r.v.z); v[6] = bf16_lo(r.v.w); v[7] = bf16_hi(r.v.w);
+}
+__device__ __forceinline__ void raw_unpack(const Raw8<float>& r, float (&v)[8]) {
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+}
+// The stored form of the values v of flat elements e .. e + 7 (n inside the row).
+template <typename TO> __device__ __forceinline__ Raw8<TO> raw_pack(const WeightParams& p, const float (&v)[8],
+                                                                    int64_t e, int n, bool vec);
+template <> __device__ __forceinline__ Raw8<float> raw_pack<float>(const WeightParams&, const float (&v)[8],
+                                                                   int64_t, int, bool) {
+    return Raw8<float>{f32x4_t{v[0], v[1], v[2], v[3]}, f32x4_t{v[4], v[5], v[6], v[7]}};
+}
+template <> __device__ __forceinline__ Raw8<bf16_t> raw_pack<bf16_t>(const WeightParams& p, const float (&v)[8],
+                                                                     int64_t e, int n, bool vec) {
+    Raw8<bf16_t> r;
+    if (!p.stochastic) {
+        r.v = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+        return r;
+    }
+    uint32_t rb[8];
+    if (vec) {
+        random8(p, (uint64_t)e, rb);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rb[i] = i < n ? random16(p, (uint64_t)(e + i)) : 0u;
+    }
+    r.v = u32x4_t{sr_bf16(v[0], rb[0]) | sr_bf16(v[1], rb[1]) << 16, sr_bf16(v[2], rb[2]) | sr_bf16(v[3], rb[3]) << 16,
+                  sr_bf16(v[4], rb[4]) | sr_bf16(v[5], rb[5]) << 16, sr_bf16(v[6], rb[6]) | sr_bf16(v[7], rb[7]) << 16};
+    return r;
+}
+
+// Stage concatenated k-rows [kf0, kf0 + kalloc) of the low-rank patches
+// meeting the tile at (r0, c0) into the round areas sb (`down`) and su
+// (`up`): the patches are walked in order with uniform (scalar) control, each
+// patch's piece split into 1 KiB direct global-to-LDS loads dealt round-robin
+// to the 4 waves.  Zeros where a row is past a patch's rank, a tile row
+// outside the patch or a column outside the weight (and wherever the vector
+// path does not apply, the same slots are filled by ordinary loads).
+__device__ __forceinline__ void stage_round(const WeightParams& p, int r0, int c0, int kf0, int kalloc,
+                                            unsigned char* sb, unsigned char* su, bool vec) {
+    const int w = (int)(threadIdx.x >> 6), L = (int)(threadIdx.x & 63);
+    int kbase = 0, di = 0, ui = 0;
+    for (int q = 0; q < p.np; ++q) {
+        const PatchDev& d = p.p[q];
+        if (d.kind != BCG_PATCH_LOWRANK || !hits_tile(d, r0)) continue;
+        const int rp = padded_rank(d.rank);
+        const int lo_k = max(kbase, kf0), hi_k = min(kbase + rp, kf0 + kalloc);
+        kbase += rp;
+        if (lo_k >= hi_k) continue;
+        const int kq0 = lo_k - (kbase - rp);  // first k-row of the piece inside the patch
+        // down: (hi_k - lo_k) / 4 blocks of 4 k-rows x 128 columns
+        for (int i = 0; i < (hi_k - lo_k) / 4; ++i, ++di) {
+            if ((di & 3) != w) continue;
+            unsigned char* dst = sb + sb_blk((lo_k - kf0) / 4 + i);
+            const int k = kq0 + 4 * i + (L >> 4), col = c0 + 8 * (L & 15);
+            const bool ok = k < d.rank && col < p.cols;
+            const bf16_t* src = d.down + (int64_t)k * p.cols + col;
+            if (ok && vec) {
+                __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+                Raw8<bf16_t> r{u32x4_t{0u, 0u, 0u, 0u}};
+                if (ok) r = raw_load(src, 0, p.cols - col, false);
+                raw_lds_st(dst + L * 16, r);
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s.b[(cv + e) * KP + kr] = (bf16_t)(__float_as_uint(x[e]) >> 16);
         }
-        __syncthreads();
+        // up: 64 tile rows x C chunks, C 1 KiB loads
+        const int C = (hi_k - lo_k) / 8;
+        unsigned char* region = su + (lo_k - kf0) * TR * 2;
+        for (int i = 0; i < C; ++i, ++ui) {
+            if ((ui & 3) != w) continue;
+            const int sl = 64 * i + L, n = sl / C;
+            const int c = (sl % C) ^ su_swz(n, C);
+            const int k = kq0 + 8 * c, pr = r0 + n - d.offset;
+            const bool ok = k < d.rank && pr >= 0 && pr < d.rows;
+            const bf16_t* src = d.up + (int64_t)pr * d.rank + k;
+            unsigned char* dst = region + i * 1024;
+            if (ok && d.upvec) {
+                __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+            } else {
+                Raw8<bf16_t> r{u32x4_t{0u, 0u, 0u, 0u}};
+                if (ok) r = raw_load(src, 0, d.rank - k, false);
+                raw_lds_st(dst + L * 16, r);
+            }
+        }
+    }
+}
+
+// Sub-tile s of a wave: D^T[m][n] with n the weight row (lane % 32) and m
+// relabelled to weight column 4 (m / 8) + m % 4 + 32 ((m / 4) % 2) + 16 s of
+// the wave's 64 columns.  Accumulator v of a 32x32 MFMA sits at m = 8 (v / 4)
+// + 4 (lane / 32) + v % 4, i.e. at column v + 16 s + 32 (lane / 32): lane
+// vector 2 s + v / 8, element v % 8.
+__device__ __forceinline__ int sub_col(int lo, int s) {
+    return 4 * (lo >> 3) + (lo & 3) + 32 * ((lo >> 2) & 1) + 16 * s;
+}
+
+// Dynamic LDS: [transposition tile: 64 rows x trow bytes][down area: sb_bytes(kalloc)][up area: 64 x kalloc x 2].
+template <typename TW, typename TO>
+__global__ __launch_bounds__(NT) void patch_lowrank_kernel(WeightParams p) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
+    constexpr int TROW = TC * ES + 16;
+    unsigned char* st = lds;
+    unsigned char* sb = lds + TR * TROW;
+    unsigned char* su = sb + sb_bytes(p.kalloc);
+    const int tile = (int)blockIdx.x;
+    const int r0 = (tile / p.ctiles) * TR, c0 = (tile % p.ctiles) * TC;
+    const int t = (int)threadIdx.x, l = t & 63, wave = t >> 6;
+    const int hi = l >> 5, lo = l & 31;
+    const int wr = 32 * (wave & 1), wc = 64 * (wave >> 1);
+    const bool vec = p.vec != 0;
+
+    // Streaming layout: vector j of lane t at tile row t / 16 + 16 j, columns 8 (t % 16) .. +7.
+    const int scol = (t & 15) * 8, sn = p.cols - (c0 + scol);
+    Raw8<TW> wraw[4];
+    const TW* w = static_cast<const TW*>(p.w);
 #pragma unroll
-        for (int kk = 0; kk < KC; kk += 16) {
-            const int k = kc + kk + 8 * hi;  // this lane's 8 k of the step
-            if (kc + kk >= q.rank) break;    // uniform
-            bf16x8_t a;
-            if (arow && q.upvec && k < q.rank) {
-                a = *reinterpret_cast<const bf16x8_t*>(urow + k);
+    for (int j = 0; j < 4; ++j) {
+        const int row = r0 + (t >> 4) + 16 * j;
+        if (row < p.rows && sn > 0) wraw[j] = raw_load(w, (int64_t)row * p.cols + c0 + scol, sn, vec);
+        else wraw[j] = raw_load(w, 0, 0, false);  // zeros, nothing read
+    }
+    int kt = 0;  // concatenated k-rows of the tile
+    for (int q = 0; q < p.np; ++q)
+        if (p.p[q].kind == BCG_PATCH_LOWRANK && hits_tile(p.p[q], r0)) kt += padded_rank(p.p[q].rank);
+    if (kt > 0) stage_round(p, r0, c0, 0, p.kalloc, sb, su, vec);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw_lds_st(st + ((t >> 4) + 16 * j) * TROW + scol * sizeof(TW), wraw[j]);
+    __builtin_amdgcn_s_waitcnt(0);  // the staged factors have landed
+    __syncthreads();
+
+    // MFMA layout: this lane holds weight row `row`, columns cl .. cl + 31 (vector j at cl + 8 j).
+    const int row = r0 + wr + lo, cl = c0 + wc + 32 * hi;
+    const bool rin = row < p.rows;
+    float a[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        raw_unpack(raw_lds_ld<TW>(st + (wr + lo) * TROW + (wc + 32 * hi + 8 * j) * sizeof(TW)), a[j]);
+
+    int kbase = 0, kf0 = 0;
+    const int colw0 = wc + sub_col(lo, 0), colw1 = wc + sub_col(lo, 1);
+    for (int q = 0; q < p.np; ++q) {
+        const PatchDev& d = p.p[q];
+        if (d.kind == BCG_PATCH_DIFF) {
+            if (d.rows > 0 && rin)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) apply_diff_any(p, d, row, cl + 8 * j, p.cols - (cl + 8 * j), vec, a[j]);
+            continue;
+        }
+        if (!hits_tile(d, r0)) continue;
+        f32x16_t acc0 = {}, acc1 = {};
+        const int rp = padded_rank(d.rank);
+        for (int k0 = 0; k0 < rp; k0 += 16) {
+            const int kf = kbase + k0;
+            if (kf >= kf0 + p.kalloc) {  // the next round (more k-rows than one round holds)
+                __syncthreads();
+                kf0 += p.kalloc;
+                stage_round(p, r0, c0, kf0, p.kalloc, sb, su, vec);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+            const int lo_k = max(kbase, kf0);
+            const int C = (min(kbase + rp, kf0 + p.kalloc) - lo_k) / 8;
+            const unsigned char* region = su + (lo_k - kf0) * TR * 2;
+            const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(
+                region + su_slot(wr + lo, (kf - lo_k) / 8 + hi, C) * 16);
+            const int kl = kf - kf0 + 8 * hi;
+            bf16x8_t a0, a1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const unsigned char* rowp = sb + sb_off(kl + i);
+                a0[i] = *reinterpret_cast<const __bf16*>(rowp + colw0 * 2);
+                a1[i] = *reinterpret_cast<const __bf16*>(rowp + colw1 * 2);
+            }
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc1, 0, 0, 0);
+        }
+        kbase += rp;
+        const int pr = row - d.offset;
+        if (rin && pr >= 0 && pr < d.rows) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                a[v >> 3][v & 7] = fmaf(d.sp, acc0[v], d.sm * a[v >> 3][v & 7]);
+                a[2 + (v >> 3)][v & 7] = fmaf(d.sp, acc1[v], d.sm * a[2 + (v >> 3)][v & 7]);
+            }
+        }
+    }
+
+    // Round to the stored form in the MFMA layout, back through LDS to the streaming layout.
+    __syncthreads();  // every lane has read its weight values out of the tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = cl + 8 * j;
+        const Raw8<TO> r = raw_pack<TO>(p, a[j], (int64_t)row * p.cols + c, p.cols - c, vec);
+        raw_lds_st(st + (wr + lo) * TROW + (wc + 32 * hi + 8 * j) * sizeof(TO), r);
+    }
+    __syncthreads();
+    TO* out = static_cast<TO*>(p.out);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int srow = r0 + (t >> 4) + 16 * j;
+        if (srow < p.rows && sn > 0)
+            raw_store(out, (int64_t)srow * p.cols + c0 + scol, sn, vec,
+                      raw_lds_ld<TO>(st + ((t >> 4) + 16 * j) * TROW + scol * sizeof(TO)));
+    }
+}
+
+// ---------------------------------------------------------------- strip kernel
+
+constexpr int PSTEPS = 8;  // k-steps of 16 rows: concatenated padded rank <= 128
+
+// One workgroup per (column strip of 128, row-tile group): the strip's
+// `down` rows of every low-rank patch are staged once, transposed (k
+// contiguous per column: each MFMA A fragment is one 16-byte LDS read), and
+// stay in LDS, read-only, while the workgroup walks its row tiles rt =
+// group, group + grows, ...  After that staging the four waves run
+// independently (no workgroup barrier): wave w owns the 32 x 64 quarter
+// (rows 32 (w % 2), columns 64 (w / 2)) of every tile, moves it between
+// global memory and registers in a streaming layout (8 rows x 128 bytes per
+// instruction) and turns it to and from the MFMA layout through its own LDS
+// region; the next tile's quarter and its `up` fragments (global memory to
+// registers) are loaded before this tile's arithmetic.
+// Dynamic LDS: [4 wave regions: 32 rows x wrow bytes][down^T: 128 columns x (kt_all + 8) bf16].
+template <typename TW, typename TO>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void patch_lowrank_strip_kernel(WeightParams p) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
+    constexpr int WROW = 64 * ES + 16;
+    const int t = (int)threadIdx.x, l = t & 63, wave = t >> 6;
+    const int hi = l >> 5, lo = l & 31;
+    const int wr = 32 * (wave & 1), wc = 64 * (wave >> 1);
+    unsigned char* rg = lds + wave * 32 * WROW;  // this wave's region
+    bf16_t* sdt = reinterpret_cast<bf16_t*>(lds + 4 * 32 * WROW);
+    const int kp = p.kt_all + 8;
+    const int ct = (int)blockIdx.x % p.ctiles, gr = (int)blockIdx.x / p.ctiles;
+    const int c0 = ct * TC;
+    const bool vec = p.vec != 0;
+
+    __shared__ StepDesc sdl[PSTEPS];
+    if (t == 0) {
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) sdl[s] = p.sd[s];
+    }
+    // down^T of the strip: k-step s covers concatenated rows 16 s .. 16 s + 15, one 8-column vector per lane.
+    for (int s = 0; s < p.steps; ++s) {
+        const PatchDev& d = p.p[p.sd[s].q];
+        const int k = p.sd[s].sk + (t >> 4), cv = (t & 15) * 8, col = c0 + cv;
+        Raw8<bf16_t> r{u32x4_t{0u, 0u, 0u, 0u}};
+        if (k < d.rank && col < p.cols) r = raw_load(d.down, (int64_t)k * p.cols + col, p.cols - col, vec);
+        const uint32_t wv[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+        const int kf = 16 * s + (t >> 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sdt[(cv + e) * kp + kf] = (bf16_t)(wv[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();  // the only workgroup barrier: down^T and the step table are in place
+
+    // Streaming layout of the wave's quarter: vector j of lane l at quarter row l / 8 + 8 j, columns 8 (l % 8) .. +7.
+    const int qc = c0 + wc + 8 * (l & 7), qn = p.cols - qc;
+    const TW* w = static_cast<const TW*>(p.w);
+    TO* out = static_cast<TO*>(p.out);
+    // The next tile's quarter of the weight and its `up` fragments, loaded one
+    // tile ahead of the arithmetic.
+    Raw8<TW> wn[4];
+    bf16x8_t bn[PSTEPS];
+    auto load_next_w = [&](int rt) __attribute__((always_inline)) {
+        const int r0 = rt * TR;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = r0 + wr + (l >> 3) + 8 * j;
+            if (row < p.rows && qn > 0) wn[j] = raw_load(w, (int64_t)row * p.cols + qc, qn, vec);
+            else wn[j] = raw_load(w, 0, 0, false);
+        }
+    };
+    auto load_next_up = [&](int rt) __attribute__((always_inline)) {
+        const int r0 = rt * TR;
+        const int row = r0 + wr + lo;
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) {
+            bn[s] = bf16x8_t{};
+            if (s >= p.steps) continue;
+            const StepDesc sd = sdl[s];
+            const int pr = row - sd.off, k = 8 * hi, rem = sd.rank - sd.sk;
+            if (r0 >= sd.off + sd.rows || r0 + TR <= sd.off || pr < 0 || pr >= sd.rows || k >= rem) continue;
+            const bf16_t* src = sd.up + (int64_t)pr * sd.rank + k;
+            if (sd.flags & 1) {
+                bn[s] = *reinterpret_cast<const bf16x8_t*>(src);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    a[e] = (arow && k + e < q.rank) ? __builtin_bit_cast(__bf16, urow[k + e])
-                                                    : __builtin_bit_cast(__bf16, (bf16_t)0);
-            }
-            const int kb = kk + 8 * hi;
-            const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(&s.b[(wc + lo) * KP + kb]);
-            const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(&s.b[(wc + 32 + lo) * KP + kb]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc1, 0, 0, 0);
-        }
-    }
-    // D[m][n] of a 32x32 MFMA: lane n + 32 * ((m / 4) % 2), register (m % 4) + 4 * (m / 8).
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * hi + (v & 3);
-        s.d[(wr + m) * DP + wc + lo] = acc0[v];
-        s.d[(wr + m) * DP + wc + 32 + lo] = acc1[v];
-    }
-    __syncthreads();
-}
-
-// ---------------------------------------------------------------- the kernel
-
-template <typename TW, typename TO, bool LR>
-__global__ __launch_bounds__(NT) void weight_patch_kernel(WeightParams p) {
-    const int64_t tile = blockIdx.x;
-    const int r0 = (int)(tile / p.ctiles) * TR, c0 = (int)(tile % p.ctiles) * TC;
-    const int t = (int)threadIdx.x;
-    const bool vec = p.vec != 0;
-
-    // Lane vectors: j-th at tile row (t + 256 j) / 16, columns 8 * ((t + 256 j) % 16) .. +7.
-    float a[VPL][8];
-    int row[VPL];
-    const int cl = c0 + (t & 15) * 8;
-    const int ncol = p.cols - cl;  // elements of the lane's vectors inside the weight (<= 0: none)
-    const TW* w = static_cast<const TW*>(p.w);
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) {
-        row[j] = r0 + ((t + j * NT) >> 4);
-        if (row[j] < p.rows && ncol > 0) load8<TW>(w, (int64_t)row[j] * p.cols + cl, ncol, vec, a[j]);
-    }
-
-    extern __shared__ __align__(16) unsigned char lds_raw[];
-    for (int q = 0; q < p.np; ++q) {
-        const PatchDev& pq = p.p[q];
-        if (pq.rows <= 0 || r0 >= pq.offset + pq.rows || r0 + TR <= pq.offset) continue;  // uniform
-        if (pq.kind == BCG_PATCH_DIFF) {
-#pragma unroll
-            for (int j = 0; j < VPL; ++j) {
-                const int pr = row[j] - pq.offset;
-                if (pr < 0 || pr >= pq.rows || ncol <= 0) continue;
-                float d[8];
-                const int64_t off = (int64_t)pr * p.cols + cl;
-                if (pq.dtype == BCG_BF16) load8<bf16_t>(static_cast<const bf16_t*>(pq.diff), off, ncol, vec, d);
-                else load8<float>(static_cast<const float*>(pq.diff), off, ncol, vec, d);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[j][e] = fmaf(pq.sp, d[e], pq.sm * a[j][e]);
-            }
-        } else if constexpr (LR) {
-            LowRankLds& s = *reinterpret_cast<LowRankLds*>(lds_raw);
-            lowrank_tile(p, pq, r0, c0, s);
-#pragma unroll
-            for (int j = 0; j < VPL; ++j) {
-                const int pr = row[j] - pq.offset;
-                if (pr < 0 || pr >= pq.rows || ncol <= 0) continue;
-                const float* dr = &s.d[((t + j * NT) >> 4) * DP + (t & 15) * 8];
-                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(dr);
-                const f32x4_t y = *reinterpret_cast<const f32x4_t*>(dr + 4);
-                const float d[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[j][e] = fmaf(pq.sp, d[e], pq.sm * a[j][e]);
+                    bn[s][e] = __builtin_bit_cast(__bf16, (bf16_t)(k + e < rem ? src[e] : 0));
             }
         }
+    };
+    if (gr < p.rtiles) {
+        load_next_w(gr);
+        load_next_up(gr);
     }
+    const int colw0 = wc + sub_col(lo, 0), colw1 = wc + sub_col(lo, 1);
 
-    TO* out = static_cast<TO*>(p.out);
+    for (int rt = gr; rt < p.rtiles; rt += p.grows) {
+        const int r0 = rt * TR;
+        const int row = r0 + wr + lo, cl = c0 + wc + 32 * hi;
+        const bool rin = row < p.rows;
+        const bool more = rt + p.grows < p.rtiles;
+        // to the MFMA layout through the wave's region (LDS accesses of one wave
+        // are in order), then the next tile's quarter into the freed registers
 #pragma unroll
-    for (int j = 0; j < VPL; ++j)
-        if (row[j] < p.rows && ncol > 0) store8<TO>(p, out, (int64_t)row[j] * p.cols + cl, ncol, vec, a[j]);
+        for (int j = 0; j < 4; ++j) raw_lds_st(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * sizeof(TW), wn[j]);
+        if (more) load_next_w(rt + p.grows);
+        __builtin_amdgcn_wave_barrier();
+        float a[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw_unpack(raw_lds_ld<TW>(rg + lo * WROW + (32 * hi + 8 * j) * sizeof(TW)), a[j]);
+
+        // patches in order: k-steps of the low-rank ones, diffs in between
+        int qn_ = 0;
+        f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) {
+            if (s >= p.steps) break;
+            const StepDesc sd = sdl[s];
+            if (sd.sk == 0) {
+                for (; qn_ < sd.q; ++qn_) {
+                    const PatchDev& f = p.p[qn_];
+                    if (f.kind == BCG_PATCH_DIFF && f.rows > 0 && rin)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            apply_diff_any(p, f, row, cl + 8 * j, p.cols - (cl + 8 * j), vec, a[j]);
+                }
+                acc0 = f32x16_t{};
+                acc1 = f32x16_t{};
+            }
+            const bool hit = r0 < sd.off + sd.rows && r0 + TR > sd.off;
+            if (hit) {
+                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + colw0 * kp + 16 * s + 8 * hi);
+                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + colw1 * kp + 16 * s + 8 * hi);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], acc1, 0, 0, 0);
+            }
+            if (sd.flags & 2) {  // the patch's last k-step
+                const int pr = row - sd.off;
+                if (hit && rin && pr >= 0 && pr < sd.rows) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], sd.sm * a[v >> 3][v & 7]);
+                        a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], sd.sm * a[2 + (v >> 3)][v & 7]);
+                    }
+                }
+                qn_ = sd.q + 1;
+            }
+        }
+        if (more) load_next_up(rt + p.grows);  // the fragments are consumed: the next tile's into their registers
+        for (; qn_ < p.np; ++qn_) {
+            const PatchDev& f = p.p[qn_];
+            if (f.kind == BCG_PATCH_DIFF && f.rows > 0 && rin)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) apply_diff_any(p, f, row, cl + 8 * j, p.cols - (cl + 8 * j), vec, a[j]);
+        }
+
+        // stored form in the MFMA layout, back to the streaming layout through the region
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = cl + 8 * j;
+            const Raw8<TO> r = raw_pack<TO>(p, a[j], (int64_t)row * p.cols + c, p.cols - c, vec);
+            raw_lds_st(rg + lo * WROW + (32 * hi + 8 * j) * sizeof(TO), r);
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int srow = r0 + wr + (l >> 3) + 8 * j;
+            if (srow < p.rows && qn > 0)
+                raw_store(out, (int64_t)srow * p.cols + qc, qn, vec,
+                          raw_lds_ld<TO>(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * sizeof(TO)));
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
 }
+
+inline size_t strip_lds_bytes(int es, int kt_all) {
+    return (size_t)4 * 32 * (64 * es + 16) + (size_t)TC * (kt_all + 8) * 2;
+}
+
+// LDS bytes of the low-rank kernel for kalloc staged k-rows.
+inline size_t lowrank_lds_bytes(int es, int kalloc) {
+    return (size_t)TR * (TC * es + 16) + sb_bytes(kalloc) + (size_t)TR * kalloc * 2;
+}
+
+enum { K_STREAM = 0, K_TILE = 1, K_STRIP = 2 };
 
 template <typename TW, typename TO>
-hipError_t launch(const WeightParams& p, bool lr, int64_t tiles, hipStream_t s) {
-    if (lr) {
-        hipLaunchKernelGGL((weight_patch_kernel<TW, TO, true>), dim3((unsigned)tiles), dim3(NT),
-                           sizeof(LowRankLds), s, p);
+hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t s) {
+    constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
+    if (kind == K_TILE) {
+        // the round buffers exceed the default 64 KiB of dynamic LDS: raise the
+        // kernel's limit once (gfx950 has 160 KiB per CU)
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&patch_lowrank_kernel<TW, TO>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lowrank_lds_bytes(ES, KMAX));
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((patch_lowrank_kernel<TW, TO>), dim3(blocks), dim3(NT),
+                           lowrank_lds_bytes(ES, p.kalloc), s, p);
+    } else if (kind == K_STRIP) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO>), dim3(blocks), dim3(NT),
+                           strip_lds_bytes(ES, p.kt_all), s, p);
     } else {
-        hipLaunchKernelGGL((weight_patch_kernel<TW, TO, false>), dim3((unsigned)tiles), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((patch_stream_kernel<TW, TO>), dim3(blocks), dim3(NT), 0, s, p);
     }
     return hipGetLastError();
+}
+
+// The largest concatenated (padded) rank over the 64-row tiles: the set of
+// low-rank patches meeting a tile only changes at tiles holding a patch's
+// first or last row, so those tiles and the ones after them cover every case.
+int max_tile_k(const bcg_weight_args* a) {
+    const int64_t rtiles = ((int64_t)a->rows + TR - 1) / TR;
+    int best = 0;
+    for (int q = 0; q < a->num_patches; ++q) {
+        const bcg_patch& e = a->patches[q];
+        if (e.kind != BCG_PATCH_LOWRANK || e.rows <= 0) continue;
+        const int64_t cand[4] = {e.offset / TR, e.offset / TR + 1, ((int64_t)e.offset + e.rows - 1) / TR,
+                                 ((int64_t)e.offset + e.rows - 1) / TR + 1};
+        for (int64_t tr : cand) {
+            if (tr >= rtiles) continue;
+            const int64_t r0 = tr * TR;
+            int k = 0;
+            for (int u = 0; u < a->num_patches; ++u) {
+                const bcg_patch& f = a->patches[u];
+                if (f.kind == BCG_PATCH_LOWRANK && f.rows > 0 && r0 < (int64_t)f.offset + f.rows && r0 + TR > f.offset)
+                    k += padded_rank(f.rank);
+            }
+            best = k > best ? k : best;
+        }
+    }
+    return best;
 }
 
 }  // namespace
@@ -386,16 +855,65 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
         }
     }
     p.vec = vec;
-    const int64_t rtiles = ((int64_t)a->rows + TR - 1) / TR, ctiles = ((int64_t)a->cols + TC - 1) / TC;
-    if (rtiles * ctiles > INT32_MAX) return fail(BCG_ESHAPE, "%s: weight too large", who);
-    p.ctiles = (int)ctiles;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    int64_t blocks;
+    int kind = K_STREAM;
+    if (lr) {
+        const int64_t rtiles = ((int64_t)a->rows + TR - 1) / TR, ctiles = ((int64_t)a->cols + TC - 1) / TC;
+        if (rtiles * ctiles > INT32_MAX) return fail(BCG_ESHAPE, "%s: weight too large", who);
+        p.ctiles = (int)ctiles;
+        p.rtiles = (int)rtiles;
+        int kt_all = 0;
+        for (int q = 0; q < a->num_patches; ++q)
+            if (a->patches[q].kind == BCG_PATCH_LOWRANK && a->patches[q].rows > 0) kt_all += padded_rank(a->patches[q].rank);
+        if (kt_all <= 16 * PSTEPS) {
+            // the strip kernel: k-step table, one resident round (3 workgroups per CU on 256 CUs)
+            kind = K_STRIP;
+            p.kt_all = kt_all;
+            p.steps = 0;
+            for (int q = 0; q < a->num_patches; ++q) {
+                const bcg_patch& e = a->patches[q];
+                if (e.kind != BCG_PATCH_LOWRANK || e.rows <= 0) continue;
+                for (int k = 0; k < padded_rank(e.rank); k += 16, ++p.steps) {
+                    StepDesc& sd = p.sd[p.steps];
+                    sd.up = static_cast<const bf16_t*>(e.up) + k;
+                    sd.q = q;
+                    sd.sk = k;
+                    sd.rank = e.rank;
+                    sd.off = e.offset;
+                    sd.rows = e.rows;
+                    sd.flags = (e.rank % 8 == 0 && aligned16(e.up) ? 1 : 0) | (k + 16 >= padded_rank(e.rank) ? 2 : 0);
+                    sd.sp = e.strength_patch;
+                    sd.sm = e.strength_model;
+                }
+            }
+            constexpr int64_t kResident = 256 * 3;
+            int64_t g = kResident / ctiles;
+            g = g < 1 ? 1 : (g > rtiles ? rtiles : g);
+            p.grows = (int)g;
+            blocks = ctiles * g;
+        } else {
+            kind = K_TILE;
+            blocks = rtiles * ctiles;
+            const int kmax = max_tile_k(a);
+            p.kalloc = kmax < KMAX ? (kmax > 16 ? kmax : 16) : KMAX;
+        }
+    } else {
+        // about one resident round: 8 workgroups of 256 lanes per CU on 256 CUs
+        constexpr int64_t kResident = 256 * 8;
+        p.nvr = (a->cols + 7) / 8;
+        const int64_t nvec = (int64_t)a->rows * p.nvr;
+        if (nvec >= INT32_MAX) return fail(BCG_ESHAPE, "%s: weight too large", who);
+        p.nvec = (uint32_t)nvec;
+        p.vpt = (int)((nvec + kResident * NT - 1) / (kResident * NT));
+        blocks = (nvec + (int64_t)NT * p.vpt - 1) / ((int64_t)NT * p.vpt);
+    }
     hipError_t e;
     if (a->w_dtype == BCG_BF16)
-        e = a->out_dtype == BCG_BF16 ? launch<bf16_t, bf16_t>(p, lr, rtiles * ctiles, st)
-                                     : launch<bf16_t, float>(p, lr, rtiles * ctiles, st);
+        e = a->out_dtype == BCG_BF16 ? launch<bf16_t, bf16_t>(p, kind, (unsigned)blocks, st)
+                                     : launch<bf16_t, float>(p, kind, (unsigned)blocks, st);
     else
-        e = a->out_dtype == BCG_BF16 ? launch<float, bf16_t>(p, lr, rtiles * ctiles, st)
-                                     : launch<float, float>(p, lr, rtiles * ctiles, st);
+        e = a->out_dtype == BCG_BF16 ? launch<float, bf16_t>(p, kind, (unsigned)blocks, st)
+                                     : launch<float, float>(p, kind, (unsigned)blocks, st);
     return hip_status(e, "weight_patch: launch");
 }
