@@ -136,9 +136,9 @@ __device__ __forceinline__ void load8(const T* base, int64_t off, int n, bool ve
 
 template <>
 __device__ __forceinline__ void load8<float>(const float* base, int64_t off, int n, bool vec, float (&v)[8]) {
-    if (vec) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(base + off);
-        const f32x4_t b = *reinterpret_cast<const f32x4_t*>(base + off + 4);
+    if (vec) {  // streamed once: nontemporal
+        const f32x4_t a = ld<true>(reinterpret_cast<const f32x4_t*>(base + off));
+        const f32x4_t b = ld<true>(reinterpret_cast<const f32x4_t*>(base + off + 4));
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
@@ -149,8 +149,8 @@ __device__ __forceinline__ void load8<float>(const float* base, int64_t off, int
 
 template <>
 __device__ __forceinline__ void load8<bf16_t>(const bf16_t* base, int64_t off, int n, bool vec, float (&v)[8]) {
-    if (vec) {
-        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(base + off);
+    if (vec) {  // streamed once: nontemporal
+        const u32x4_t q = ld<true>(reinterpret_cast<const u32x4_t*>(base + off));
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     } else {
@@ -166,8 +166,8 @@ __device__ __forceinline__ void store8(const WeightParams& p, TO* out, int64_t e
                                        const float (&v)[8]) {
     if constexpr (sizeof(TO) == 4) {
         if (vec) {
-            *reinterpret_cast<f32x4_t*>(out + e) = f32x4_t{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4_t*>(out + e + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+            st<true>(reinterpret_cast<f32x4_t*>(out + e), f32x4_t{v[0], v[1], v[2], v[3]});
+            st<true>(reinterpret_cast<f32x4_t*>(out + e + 4), f32x4_t{v[4], v[5], v[6], v[7]});
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -182,7 +182,7 @@ __device__ __forceinline__ void store8(const WeightParams& p, TO* out, int64_t e
             q.y = sr_bf16(v[2], r[2]) | (sr_bf16(v[3], r[3]) << 16);
             q.z = sr_bf16(v[4], r[4]) | (sr_bf16(v[5], r[5]) << 16);
             q.w = sr_bf16(v[6], r[6]) | (sr_bf16(v[7], r[7]) << 16);
-            *reinterpret_cast<u32x4_t*>(out + e) = q;
+            st<true>(reinterpret_cast<u32x4_t*>(out + e), q);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -192,7 +192,7 @@ __device__ __forceinline__ void store8(const WeightParams& p, TO* out, int64_t e
         if (vec) {
             const u32x4_t q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-            *reinterpret_cast<u32x4_t*>(out + e) = q;
+            st<true>(reinterpret_cast<u32x4_t*>(out + e), q);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -275,10 +275,11 @@ template <typename T> struct Raw8;
 template <> struct Raw8<bf16_t> { u32x4_t v; };
 template <> struct Raw8<float> { f32x4_t a, b; };
 
+template <bool NT = false>
 __device__ __forceinline__ Raw8<bf16_t> raw_load(const bf16_t* base, int64_t off, int n, bool vec) {
     Raw8<bf16_t> r;
     if (vec) {
-        r.v = *reinterpret_cast<const u32x4_t*>(base + off);
+        r.v = ld<NT>(reinterpret_cast<const u32x4_t*>(base + off));
     } else {
         uint32_t h[8];
 #pragma unroll
@@ -287,11 +288,12 @@ __device__ __forceinline__ Raw8<bf16_t> raw_load(const bf16_t* base, int64_t off
     }
     return r;
 }
+template <bool NT = false>
 __device__ __forceinline__ Raw8<float> raw_load(const float* base, int64_t off, int n, bool vec) {
     Raw8<float> r;
     if (vec) {
-        r.a = *reinterpret_cast<const f32x4_t*>(base + off);
-        r.b = *reinterpret_cast<const f32x4_t*>(base + off + 4);
+        r.a = ld<NT>(reinterpret_cast<const f32x4_t*>(base + off));
+        r.b = ld<NT>(reinterpret_cast<const f32x4_t*>(base + off + 4));
     } else {
         float x[8];
 #pragma unroll
@@ -301,9 +303,10 @@ __device__ __forceinline__ Raw8<float> raw_load(const float* base, int64_t off, 
     }
     return r;
 }
+template <bool NT = false>
 __device__ __forceinline__ void raw_store(bf16_t* base, int64_t off, int n, bool vec, const Raw8<bf16_t>& r) {
     if (vec) {
-        *reinterpret_cast<u32x4_t*>(base + off) = r.v;
+        st<NT>(reinterpret_cast<u32x4_t*>(base + off), r.v);
     } else {
         const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
 #pragma unroll
@@ -311,10 +314,11 @@ __device__ __forceinline__ void raw_store(bf16_t* base, int64_t off, int n, bool
             if (e < n) base[off + e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
 }
+template <bool NT = false>
 __device__ __forceinline__ void raw_store(float* base, int64_t off, int n, bool vec, const Raw8<float>& r) {
     if (vec) {
-        *reinterpret_cast<f32x4_t*>(base + off) = r.a;
-        *reinterpret_cast<f32x4_t*>(base + off + 4) = r.b;
+        st<NT>(reinterpret_cast<f32x4_t*>(base + off), r.a);
+        st<NT>(reinterpret_cast<f32x4_t*>(base + off + 4), r.b);
     } else {
         const float x[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
@@ -563,7 +567,7 @@ constexpr int PSTEPS = 8;  // k-steps of 16 rows: concatenated padded rank <= 12
 // region; the next tile's quarter and its `up` fragments (global memory to
 // registers) are loaded before this tile's arithmetic.
 // Dynamic LDS: [4 wave regions: 32 rows x wrow bytes][down^T: 128 columns x (kt_all + 8) bf16].
-template <typename TW, typename TO>
+template <typename TW, typename TO, bool VEC>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void patch_lowrank_strip_kernel(WeightParams p) {
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
@@ -576,7 +580,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     const int kp = p.kt_all + 8;
     const int ct = (int)blockIdx.x % p.ctiles, gr = (int)blockIdx.x / p.ctiles;
     const int c0 = ct * TC;
-    const bool vec = p.vec != 0;
+    constexpr bool vec = VEC;  // 8-element accesses (the element path is its own instantiation)
 
     __shared__ StepDesc sdl[PSTEPS];
     if (t == 0) {
@@ -609,7 +613,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = r0 + wr + (l >> 3) + 8 * j;
-            if (row < p.rows && qn > 0) wn[j] = raw_load(w, (int64_t)row * p.cols + qc, qn, vec);
+            if (row < p.rows && qn > 0) wn[j] = raw_load<true>(w, (int64_t)row * p.cols + qc, qn, vec);
             else wn[j] = raw_load(w, 0, 0, false);
         }
     };
@@ -712,7 +716,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
         for (int j = 0; j < 4; ++j) {
             const int srow = r0 + wr + (l >> 3) + 8 * j;
             if (srow < p.rows && qn > 0)
-                raw_store(out, (int64_t)srow * p.cols + qc, qn, vec,
+                raw_store<true>(out, (int64_t)srow * p.cols + qc, qn, vec,
                           raw_lds_ld<TO>(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * sizeof(TO)));
         }
         __builtin_amdgcn_wave_barrier();
@@ -743,12 +747,20 @@ hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t 
         hipLaunchKernelGGL((patch_lowrank_kernel<TW, TO>), dim3(blocks), dim3(NT),
                            lowrank_lds_bytes(ES, p.kalloc), s, p);
     } else if (kind == K_STRIP) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO>),
+        static const hipError_t attr0 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO>), dim3(blocks), dim3(NT),
-                           strip_lds_bytes(ES, p.kt_all), s, p);
+        static const hipError_t attr1 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
+        if (attr0 != hipSuccess) return attr0;
+        if (attr1 != hipSuccess) return attr1;
+        if (p.vec)
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true>), dim3(blocks), dim3(NT),
+                               strip_lds_bytes(ES, p.kt_all), s, p);
+        else
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false>), dim3(blocks), dim3(NT),
+                               strip_lds_bytes(ES, p.kt_all), s, p);
     } else {
         hipLaunchKernelGGL((patch_stream_kernel<TW, TO>), dim3(blocks), dim3(NT), 0, s, p);
     }
