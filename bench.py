@@ -39,9 +39,16 @@ KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_plan_dev.h", "bcg_api.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "guided_step_large_bf16_traffic.json")
 
 
-def kernel_hash() -> str:
+WEIGHT_SOURCES = ["bcg_weight.hip", "bcg_device.h", "bcg_launch.h"]
+
+
+def weight_traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"weight_patch_{workload}_traffic.json")
+
+
+def kernel_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "bucketed_classifier_free_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -157,18 +164,20 @@ def _counter_means(path, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, workload):
-    """Per-launch HBM bytes of guided_step from two rocprofv3 --pmc runs
-    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
-    same counter reads for a plain device copy of copy_mib MiB."""
+def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, workload,
+                          kernel="guided_step_kernel", sources=None):
+    """Per-launch HBM bytes of a kernel (guided_step by default) from two
+    rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+    scaled by what the same counter reads for a plain device copy of copy_mib
+    MiB."""
     copy_bytes = copy_mib * (1 << 20)
     pick = lambda d, key: max((v for k, v in d.items() if key in k), default=None)
     cf = pick(_counter_means(copy_fetch_csv, "FETCH_SIZE"), "copyBuffer")
     cw = pick(_counter_means(copy_write_csv, "WRITE_SIZE"), "copyBuffer")
-    f = pick(_counter_means(fetch_csv, "FETCH_SIZE"), "guided_step_kernel")
-    w = pick(_counter_means(write_csv, "WRITE_SIZE"), "guided_step_kernel")
+    f = pick(_counter_means(fetch_csv, "FETCH_SIZE"), kernel)
+    w = pick(_counter_means(write_csv, "WRITE_SIZE"), kernel)
     rf, rw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    return {"workload": workload, "kernel_hash": kernel_hash(),
+    return {"workload": workload, "kernel": kernel, "kernel_hash": kernel_hash(sources),
             "fetch_kib_raw": f, "write_kib_raw": w, "copy_fetch_kib_raw": cf,
             "copy_write_kib_raw": cw, "copy_mib": copy_mib,
             "fetch_scale": rf, "write_scale": rw,
@@ -388,6 +397,13 @@ def weight_bench(name, args, cpu=None):
             alg += 2 * (pd.rows * ps.rank + ps.rank * sp.cols)
             flops += 2 * pd.rows * sp.cols * ps.rank
     achieved = alg / (launch_ms * 1e-3) / 1e9
+    traffic = None
+    tf = weight_traffic_file(sp.name)
+    if os.path.exists(tf) and not args.rounding:
+        with open(tf) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_hash") == kernel_hash(WEIGHT_SOURCES) and tr.get("workload") == sp.name:
+            traffic = tr.get("bytes_per_launch")
     out = {
         "metric": "weight elements patched/sec on 1 GPU",
         "value": elems * n / wall, "unit": "weight elements/s", "n_gpus": 1, "steps": n,
@@ -401,8 +417,9 @@ def weight_bench(name, args, cpu=None):
                                for p, d in zip(sp.patches, inp.patches)],
                    "replicas": R, "graph_launches": G},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "kernel": {"name": "weight_patch", "avg_launch_us": launch_ms * 1e3,
+                   "kernel_hash": kernel_hash(WEIGHT_SOURCES),
                    "timing": f"HIP events around replays of a {G}-launch graph",
                    "algorithmic_bytes_per_launch": alg, "lowrank_flops_per_launch": flops,
                    "mfma_tflops": flops / (launch_ms * 1e-3) / 1e12},
@@ -490,6 +507,13 @@ def main():
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the traffic record from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from and args.weight_patch:
+        kern = "patch_stream_kernel" if "diff" in args.weight_patch else "patch_lowrank_strip_kernel"
+        rec = traffic_from_counters(*args.traffic_from, 256, args.weight_patch, kern, WEIGHT_SOURCES)
+        with open(weight_traffic_file(args.weight_patch), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        return
     if args.traffic_from:
         rec = traffic_from_counters(*args.traffic_from, 256, args.workload)
         with open(TRAFFIC_FILE, "w") as fh:
