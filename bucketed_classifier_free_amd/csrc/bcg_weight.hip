@@ -73,6 +73,7 @@ struct WeightParams {
     int kt_all;       // concatenated padded rank of every low-rank patch (strip kernel)
     int steps;        // 16-row k-steps of that concatenation (strip kernel)
     StepDesc sd[8];   // the k-steps (strip kernel)
+    int sm1;          // every low-rank patch has strength_model 1 (strip kernel)
     int nvr;          // 8-element vectors per row (stream kernel)
     int vpt;          // vectors per lane (stream kernel)
     uint32_t nvec;    // vectors of the weight (stream kernel)
@@ -564,10 +565,11 @@ constexpr int PSTEPS = 8;  // k-steps of 16 rows: concatenated padded rank <= 12
 // (rows 32 (w % 2), columns 64 (w / 2)) of every tile, moves it between
 // global memory and registers in a streaming layout (8 rows x 128 bytes per
 // instruction) and turns it to and from the MFMA layout through its own LDS
-// region; the next tile's quarter and its `up` fragments (global memory to
-// registers) are loaded before this tile's arithmetic.
+// region; the next tile's quarter is loaded before this tile's arithmetic and
+// the tile's `up` fragments (global memory to registers) land while its
+// quarter is transposed.
 // Dynamic LDS: [4 wave regions: 32 rows x wrow bytes][down^T: 128 columns x (kt_all + 8) bf16].
-template <typename TW, typename TO, bool VEC>
+template <typename TW, typename TO, bool VEC, bool SM1>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void patch_lowrank_strip_kernel(WeightParams p) {
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     // The next tile's quarter of the weight and its `up` fragments, loaded one
     // tile ahead of the arithmetic.
     Raw8<TW> wn[4];
-    bf16x8_t bn[PSTEPS];
+    bf16x8_t bn[PSTEPS];  // this tile's `up` fragments
     auto load_next_w = [&](int rt) __attribute__((always_inline)) {
         const int r0 = rt * TR;
 #pragma unroll
@@ -637,10 +639,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             }
         }
     };
-    if (gr < p.rtiles) {
-        load_next_w(gr);
-        load_next_up(gr);
-    }
+    if (gr < p.rtiles) load_next_w(gr);
     const int colw0 = wc + sub_col(lo, 0), colw1 = wc + sub_col(lo, 1);
 
     for (int rt = gr; rt < p.rtiles; rt += p.grows) {
@@ -648,6 +647,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
         const int row = r0 + wr + lo, cl = c0 + wc + 32 * hi;
         const bool rin = row < p.rows;
         const bool more = rt + p.grows < p.rtiles;
+        load_next_up(rt);  // this tile's fragments: they land while the quarter is transposed
         // to the MFMA layout through the wave's region (LDS accesses of one wave
         // are in order), then the next tile's quarter into the freed registers
 #pragma unroll
@@ -688,14 +688,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
                 if (hit && rin && pr >= 0 && pr < sd.rows) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], sd.sm * a[v >> 3][v & 7]);
-                        a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], sd.sm * a[2 + (v >> 3)][v & 7]);
+                        if constexpr (SM1) {  // every strength_model is 1: 1 * a is a
+                            a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], a[v >> 3][v & 7]);
+                            a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], a[2 + (v >> 3)][v & 7]);
+                        } else {
+                            a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], sd.sm * a[v >> 3][v & 7]);
+                            a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], sd.sm * a[2 + (v >> 3)][v & 7]);
+                        }
                     }
                 }
                 qn_ = sd.q + 1;
             }
         }
-        if (more) load_next_up(rt + p.grows);  // the fragments are consumed: the next tile's into their registers
         for (; qn_ < p.np; ++qn_) {
             const PatchDev& f = p.p[qn_];
             if (f.kind == BCG_PATCH_DIFF && f.rows > 0 && rin)
@@ -748,19 +752,24 @@ hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t 
                            lowrank_lds_bytes(ES, p.kalloc), s, p);
     } else if (kind == K_STRIP) {
         static const hipError_t attr0 = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false>),
+            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false, false>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
         static const hipError_t attr1 = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true>),
+            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, false>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
+        static const hipError_t attr2 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, true>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
         if (attr0 != hipSuccess) return attr0;
         if (attr1 != hipSuccess) return attr1;
-        if (p.vec)
-            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true>), dim3(blocks), dim3(NT),
-                               strip_lds_bytes(ES, p.kt_all), s, p);
+        if (attr2 != hipSuccess) return attr2;
+        const size_t lds = strip_lds_bytes(ES, p.kt_all);
+        if (!p.vec)
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false, false>), dim3(blocks), dim3(NT), lds, s, p);
+        else if (p.sm1)
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, true>), dim3(blocks), dim3(NT), lds, s, p);
         else
-            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false>), dim3(blocks), dim3(NT),
-                               strip_lds_bytes(ES, p.kt_all), s, p);
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, false>), dim3(blocks), dim3(NT), lds, s, p);
     } else {
         hipLaunchKernelGGL((patch_stream_kernel<TW, TO>), dim3(blocks), dim3(NT), 0, s, p);
     }
@@ -883,9 +892,11 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
             kind = K_STRIP;
             p.kt_all = kt_all;
             p.steps = 0;
+            p.sm1 = 1;
             for (int q = 0; q < a->num_patches; ++q) {
                 const bcg_patch& e = a->patches[q];
                 if (e.kind != BCG_PATCH_LOWRANK || e.rows <= 0) continue;
+                if (e.strength_model != 1.0f) p.sm1 = 0;
                 for (int k = 0; k < padded_rank(e.rank); k += 16, ++p.steps) {
                     StepDesc& sd = p.sd[p.steps];
                     sd.up = static_cast<const bf16_t*>(e.up) + k;
