@@ -9,8 +9,8 @@
 //
 //   patch_stream_kernel  (no low-rank patch): the weight as a flat sequence
 //     of 8-element row vectors (16-byte accesses, consecutive lanes on
-//     consecutive addresses), each workgroup a contiguous share sized so the
-//     grid is about one resident round (no partly filled last round).
+//     consecutive addresses), a grid of about one resident round (no partly
+//     filled last round) sweeping it front to back.
 //   patch_lowrank_kernel: 64 x 128 tiles, one 32 x 64 quarter per wave.  The
 //     low-rank deltas are genuine contractions and run on the matrix cores
 //     as the transposed product dW^T = down^T up^T (v_mfma_f32_32x32x16_bf16),
@@ -229,9 +229,11 @@ __global__ __launch_bounds__(NT) void patch_stream_kernel(WeightParams p) {
     const bool vec = p.vec != 0;
     const TW* w = static_cast<const TW*>(p.w);
     TO* out = static_cast<TO*>(p.out);
-    const uint32_t base = blockIdx.x * (uint32_t)(NT * p.vpt) + threadIdx.x;
+    // round i covers vectors [i * grid * 256, (i + 1) * grid * 256): the whole grid
+    // sweeps the weight front to back together (better DRAM page locality than
+    // a contiguous share per workgroup)
     for (int i = 0; i < p.vpt; ++i) {
-        const uint32_t v = base + (uint32_t)(i * NT);
+        const uint32_t v = ((uint32_t)i * gridDim.x + blockIdx.x) * NT + threadIdx.x;
         if (v >= p.nvec) break;
         const uint32_t row = v / (uint32_t)p.nvr;
         const int c = (int)(v - row * (uint32_t)p.nvr) * 8;
