@@ -29,6 +29,8 @@
 // The stochastic rounding bits come from Philox4x32-10 (Salmon, Moraes, Dror
 // and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), one call
 // per 8 consecutive elements.
+#include <atomic>
+
 #include "bcg_device.h"
 #include "bcg_launch.h"
 
@@ -740,38 +742,48 @@ inline size_t lowrank_lds_bytes(int es, int kalloc) {
 
 enum { K_STREAM = 0, K_TILE = 1, K_STRIP = 2 };
 
+// Raise a kernel's dynamic-LDS limit above the default 64 KiB (gfx950 has 160
+// KiB per CU), once per kernel and device: `done` holds one bit per device.
+inline hipError_t lds_limit(const void* fn, size_t bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
+
 template <typename TW, typename TO>
 hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t s) {
     constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
     if (kind == K_TILE) {
-        // the round buffers exceed the default 64 KiB of dynamic LDS: raise the
-        // kernel's limit once (gfx950 has 160 KiB per CU)
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_kernel<TW, TO>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lowrank_lds_bytes(ES, KMAX));
+        static std::atomic<uint64_t> done{0};
+        const hipError_t attr = lds_limit(reinterpret_cast<const void*>(&patch_lowrank_kernel<TW, TO>),
+                                          lowrank_lds_bytes(ES, KMAX), done);
         if (attr != hipSuccess) return attr;
         hipLaunchKernelGGL((patch_lowrank_kernel<TW, TO>), dim3(blocks), dim3(NT),
                            lowrank_lds_bytes(ES, p.kalloc), s, p);
     } else if (kind == K_STRIP) {
-        static const hipError_t attr0 = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false, false>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
-        static const hipError_t attr1 = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, false>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
-        static const hipError_t attr2 = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, true>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes(ES, 16 * PSTEPS));
-        if (attr0 != hipSuccess) return attr0;
-        if (attr1 != hipSuccess) return attr1;
-        if (attr2 != hipSuccess) return attr2;
-        const size_t lds = strip_lds_bytes(ES, p.kt_all);
-        if (!p.vec)
+        static std::atomic<uint64_t> done[3] = {{0}, {0}, {0}};
+        const size_t lmax = strip_lds_bytes(ES, 16 * PSTEPS), lds = strip_lds_bytes(ES, p.kt_all);
+        if (!p.vec) {
+            const hipError_t e = lds_limit(
+                reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false, false>), lmax, done[0]);
+            if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false, false>), dim3(blocks), dim3(NT), lds, s, p);
-        else if (p.sm1)
+        } else if (p.sm1) {
+            const hipError_t e = lds_limit(
+                reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, true>), lmax, done[1]);
+            if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, true>), dim3(blocks), dim3(NT), lds, s, p);
-        else
+        } else {
+            const hipError_t e = lds_limit(
+                reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, false>), lmax, done[2]);
+            if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, false>), dim3(blocks), dim3(NT), lds, s, p);
+        }
     } else {
         hipLaunchKernelGGL((patch_stream_kernel<TW, TO>), dim3(blocks), dim3(NT), 0, s, p);
     }

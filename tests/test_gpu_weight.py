@@ -191,3 +191,55 @@ def test_weight_patch_large_workloads_sampled_rows(name):
             assert np.array_equal(got[r], code), f"row {r}"
         mism += int(np.sum(got[r] != code))
     assert mism <= 1e-3 * len(rows) * sp.cols
+
+
+def _misaligned(a, dtype=torch.bfloat16):
+    """A contiguous device copy of `a` whose data pointer is 2 bytes past a
+    16-byte boundary (a view one element into a larger buffer)."""
+    flat = torch.from_numpy(np.ascontiguousarray(a, np.float32).ravel()).cuda().to(dtype)
+    buf = torch.zeros(flat.numel() + 8, dtype=dtype, device="cuda")
+    buf[1:1 + flat.numel()] = flat
+    v = buf[1:1 + flat.numel()].view(a.shape)
+    assert v.is_contiguous() and v.data_ptr() % 16 != 0
+    return v
+
+
+def test_weight_patch_rank_total_at_the_strip_limit():
+    """Padded ranks summing to exactly 128 (the most the column-strip kernel
+    holds), an offset patch among them, bit-exact."""
+    pats = (WW.PatchSpec("lowrank", rank=64, strength_patch=0.5),
+            WW.PatchSpec("lowrank", offset=70, rows=80, rank=60, strength_patch=-1.5, strength_model=0.5))
+    inp = WW.make_weight_inputs(_spec(rows=150, cols=200, patches=pats, dyadic=True, seed=21))
+    got = _run(inp)
+    want = P.written(inp, P.reference32(inp))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("what", ["factors", "weight"])
+def test_weight_patch_misaligned_arrays_bit_exact(what):
+    """Factors (or the weight) 2 bytes off a 16-byte boundary take the element
+    paths (no 16-byte accesses on them); results unchanged."""
+    from bucketed_classifier_free_amd import WeightPatch, weight_patch
+    inp = WW.make_weight_inputs(_spec(rows=90, cols=136, dyadic=True, seed=22))
+    sp = inp.spec
+    pats = []
+    for pd in inp.patches:
+        ps = pd.spec
+        if ps.kind == "diff":
+            pats.append(WeightPatch(ps.strength_patch, ps.strength_model, ps.offset,
+                                    diff=torch.from_numpy(pd.diff).cuda().to(TDT[ps.dtype])))
+        elif what == "factors":
+            pats.append(WeightPatch(ps.strength_patch, ps.strength_model, ps.offset,
+                                    up=_misaligned(pd.up), down=_misaligned(pd.down)))
+        else:
+            pats.append(WeightPatch(ps.strength_patch, ps.strength_model, ps.offset,
+                                    up=torch.from_numpy(pd.up).cuda().to(torch.bfloat16),
+                                    down=torch.from_numpy(pd.down).cuda().to(torch.bfloat16)))
+    w = _misaligned(inp.w, TDT[sp.w_dtype]) if what == "weight" else \
+        torch.from_numpy(inp.w).cuda().to(TDT[sp.w_dtype])
+    out = torch.full(w.shape, float("nan"), dtype=TDT[sp.out_dtype], device="cuda")
+    weight_patch(w, out, pats, rounding=sp.rounding, seed=sp.sr_seed)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    want = P.written(inp, P.reference32(inp))
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
