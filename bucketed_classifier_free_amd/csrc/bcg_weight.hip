@@ -3,28 +3,31 @@
 // and weight views": "patches record format", "strength_model and
 // strength_patch", "offset patch", "how a weight is patched").
 //
-// Two HBM-bound kernels; both apply the patches of a weight in order
-// (a = fma(sp, d, sm * a) per element in fp32 registers), load and store each
-// weight element once, and round on the store.
+// Three kernels; all apply the patches of a weight in order (a = fma(sp, d,
+// sm * a) per element in fp32 registers), load and store each weight element
+// once, and round on the store.
 //
 //   patch_stream_kernel  (no low-rank patch): the weight as a flat sequence
 //     of 8-element row vectors (16-byte accesses, consecutive lanes on
 //     consecutive addresses), a grid of about one resident round (no partly
 //     filled last round) sweeping it front to back.
-//   patch_lowrank_kernel: 64 x 128 tiles, one 32 x 64 quarter per wave.  The
-//     low-rank deltas are genuine contractions and run on the matrix cores
-//     as the transposed product dW^T = down^T up^T (v_mfma_f32_32x32x16_bf16),
-//     with the columns of each 32 x 32 sub-tile relabelled so that a lane's
-//     16 accumulators are 16 consecutive weight columns of one weight row:
-//     each lane then holds 32 consecutive elements of one row, the delta is
-//     combined straight from the accumulators, and the weight, the diffs and
-//     the output move in that layout (16-byte accesses).  The factors of all
+//   patch_lowrank_strip_kernel (low-rank patches, padded ranks summing to at
+//     most 128): the deltas are genuine contractions and run on the matrix
+//     cores as the transposed product dW^T = down^T up^T
+//     (v_mfma_f32_32x32x16_bf16), with the columns of each 32 x 32 sub-tile
+//     relabelled so that a lane's 16 accumulators are 16 consecutive weight
+//     columns of one weight row, and combined straight from the accumulators.
+//     A workgroup keeps one 128-column strip of `down` in LDS (transposed
+//     once) and walks its row tiles with four independent waves (the kernel
+//     comment below has the details).
+//   patch_lowrank_kernel (larger ranks): 64 x 128 tiles; the factors of the
 //     low-rank patches meeting the tile are concatenated along k and staged
-//     through LDS 32 k-rows per round, double-buffered, by direct
-//     global-to-LDS loads issued one round ahead; `up` goes in k-contiguous
-//     (16-byte fragment reads, XOR-swizzled against bank conflicts), `down`
-//     row-major (the transposed fragment is gathered 2 bytes at a time, with
-//     padding that keeps the two lane halves on different banks).
+//     per tile, up to 128 k-rows per round, by direct global-to-LDS loads;
+//     `up` goes in k-contiguous (16-byte fragment reads, XOR-swizzled against
+//     bank conflicts), `down` row-major (the transposed fragment is gathered
+//     2 bytes at a time, with padding that keeps the two lane halves on
+//     different banks); the weight passes through a padded LDS tile between
+//     the streaming layout and the MFMA layout.
 //
 // The stochastic rounding bits come from Philox4x32-10 (Salmon, Moraes, Dror
 // and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), one call
