@@ -283,11 +283,11 @@ template <typename T> struct Raw8;
 template <> struct Raw8<bf16_t> { u32x4_t v; };
 template <> struct Raw8<float> { f32x4_t a, b; };
 
-template <bool NT = false>
+template <bool STREAM = false>  // STREAM: nontemporal (read or written once)
 __device__ __forceinline__ Raw8<bf16_t> raw_load(const bf16_t* base, int64_t off, int n, bool vec) {
     Raw8<bf16_t> r;
     if (vec) {
-        r.v = ld<NT>(reinterpret_cast<const u32x4_t*>(base + off));
+        r.v = ld<STREAM>(reinterpret_cast<const u32x4_t*>(base + off));
     } else {
         uint32_t h[8];
 #pragma unroll
@@ -296,12 +296,12 @@ __device__ __forceinline__ Raw8<bf16_t> raw_load(const bf16_t* base, int64_t off
     }
     return r;
 }
-template <bool NT = false>
+template <bool STREAM = false>  // STREAM: nontemporal (read or written once)
 __device__ __forceinline__ Raw8<float> raw_load(const float* base, int64_t off, int n, bool vec) {
     Raw8<float> r;
     if (vec) {
-        r.a = ld<NT>(reinterpret_cast<const f32x4_t*>(base + off));
-        r.b = ld<NT>(reinterpret_cast<const f32x4_t*>(base + off + 4));
+        r.a = ld<STREAM>(reinterpret_cast<const f32x4_t*>(base + off));
+        r.b = ld<STREAM>(reinterpret_cast<const f32x4_t*>(base + off + 4));
     } else {
         float x[8];
 #pragma unroll
@@ -311,10 +311,10 @@ __device__ __forceinline__ Raw8<float> raw_load(const float* base, int64_t off, 
     }
     return r;
 }
-template <bool NT = false>
+template <bool STREAM = false>  // STREAM: nontemporal (read or written once)
 __device__ __forceinline__ void raw_store(bf16_t* base, int64_t off, int n, bool vec, const Raw8<bf16_t>& r) {
     if (vec) {
-        st<NT>(reinterpret_cast<u32x4_t*>(base + off), r.v);
+        st<STREAM>(reinterpret_cast<u32x4_t*>(base + off), r.v);
     } else {
         const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
 #pragma unroll
@@ -322,11 +322,11 @@ __device__ __forceinline__ void raw_store(bf16_t* base, int64_t off, int n, bool
             if (e < n) base[off + e] = (bf16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
 }
-template <bool NT = false>
+template <bool STREAM = false>  // STREAM: nontemporal (read or written once)
 __device__ __forceinline__ void raw_store(float* base, int64_t off, int n, bool vec, const Raw8<float>& r) {
     if (vec) {
-        st<NT>(reinterpret_cast<f32x4_t*>(base + off), r.a);
-        st<NT>(reinterpret_cast<f32x4_t*>(base + off + 4), r.b);
+        st<STREAM>(reinterpret_cast<f32x4_t*>(base + off), r.a);
+        st<STREAM>(reinterpret_cast<f32x4_t*>(base + off + 4), r.b);
     } else {
         const float x[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
