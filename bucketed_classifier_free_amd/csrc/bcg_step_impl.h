@@ -44,7 +44,8 @@ constexpr int kBranches = 2 + BCG_MAX_REGIONS;      // uncond, cond, regions
 constexpr int kSet = kBranches * BCG_MAX_CHANNELS;  // one sigma's coefficients
 constexpr int kPlanLds = 4 * 2 * kSet;              // ints of the coefficient LDS
 
-// Compile-time tuning of the streaming loop.
+// Compile-time tuning of the streaming loop (the stage width U is chosen per
+// kernel variant at launch, see stage_width).
 template <int U_, bool NT_>
 struct Tune {
     static constexpr int U = U_;     // channels per pipeline stage
@@ -432,16 +433,31 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         run_sample<T, V, TN, NR, 0, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, keep_u, sig, sgn, mu_u, mu_c, mu_r);
 }
 
+// Channels per pipeline stage: 4 (more latent loads in flight per lane) where
+// the kernel still fits the 128 VGPRs of 4 waves per SIMD -- the occupancy the
+// launch shape of large batches assumes -- else 2 (measured: inpaint variants,
+// and bf16 with 3-4 regions or 2 regions under Heun, exceed 128 with 4).
+template <typename T, int NR, bool INP, bool HEUN>
+constexpr int stage_width() {
+    if (INP) return 2;
+    if (sizeof(T) == 4) return 4;
+    return (NR <= 1 || (NR == 2 && !HEUN)) ? 4 : 2;
+}
+
 template <typename T, int V, int NR, typename TN = DefaultTune>
 hipError_t launch_nr(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0))),
         blk((unsigned)block);
+    typedef Tune<stage_width<T, NR, true, true>(), TN::NT> TII;
+    typedef Tune<stage_width<T, NR, false, true>(), TN::NT> T0I;
+    typedef Tune<stage_width<T, NR, true, false>(), TN::NT> TI0;
+    typedef Tune<stage_width<T, NR, false, false>(), TN::NT> T00;
     if (heun) {
-        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true, TN>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true, TN>), grid, blk, 0, st, p);
+        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true, TII>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true, T0I>), grid, blk, 0, st, p);
     } else {
-        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, false, TN>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, false, TN>), grid, blk, 0, st, p);
+        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, false, TI0>), grid, blk, 0, st, p);
+        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, false, T00>), grid, blk, 0, st, p);
     }
     return hipGetLastError();
 }
