@@ -46,10 +46,11 @@ constexpr int kPlanLds = 4 * 2 * kSet;              // ints of the coefficient L
 
 // Compile-time tuning of the streaming loop (the stage width U is chosen per
 // kernel variant at launch, see stage_width).
-template <int U_, bool NT_>
+template <int U_, bool NT_, bool PF_ = false>
 struct Tune {
     static constexpr int U = U_;     // channels per pipeline stage
     static constexpr bool NT = NT_;  // nontemporal (streaming) loads and stores
+    static constexpr bool PF = PF_;  // next pass's head stage requested during this pass
 };
 typedef Tune<2, false> KeepTune;    // ordinary loads/stores (BCG_CACHE_KEEP)
 typedef Tune<2, true> StreamTune;   // nontemporal loads/stores (BCG_CACHE_STREAM)
@@ -174,20 +175,25 @@ __device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg,
 }
 
 // The channel walk, two stages in flight (ping-pong): stage `a` arrives
-// holding channels [0, U) already requested.
+// holding channels [0, U) already requested.  When the lane has a next pass
+// (nxs != nullptr), its head stage is requested into whichever buffer frees up
+// during this pass's last stage, so the walk does not drain between passes;
+// the return value says where it went (true: `b`, false: `a`).
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
-__device__ __forceinline__ void channel_loop(Stage<T, V, TN::U, INP>& a, const LaneState<V, NR>& L,
-                                             const StepScalars& s, const float* __restrict__ coef,
-                                             const T* xs, T* xd, const T* xo, int C, int64_t HW) {
+__device__ __forceinline__ bool channel_loop(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b,
+                                             const LaneState<V, NR>& L, const StepScalars& s,
+                                             const float* __restrict__ coef, const T* xs, T* xd, const T* xo,
+                                             const T* nxs, const T* nxo, int C, int64_t HW) {
     constexpr int U = TN::U;
-    Stage<T, V, U, INP> b;
     for (int c0 = 0;; c0 += 2 * U) {
         if (c0 + U < C) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, C, HW);
+        else if (nxs) load_stage<T, V, TN, INP>(b, nxs, nxo, 0, C, HW);
         compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, C, HW);
-        if (c0 + U >= C) break;
+        if (c0 + U >= C) return true;
         if (c0 + 2 * U < C) load_stage<T, V, TN, INP>(a, xs, xo, c0 + 2 * U, C, HW);
+        else if (nxs) load_stage<T, V, TN, INP>(a, nxs, nxo, 0, C, HW);
         compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, xd, c0 + U, C, HW);
-        if (c0 + 2 * U >= C) break;
+        if (c0 + 2 * U >= C) return false;
     }
 }
 
@@ -256,6 +262,7 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V
                                          int vi0, bool keep_u) {
     const int C = p.C;
     const int64_t sbase = (int64_t)i * C * p.HW;
+    Stage<T, V, TN::U, INP> b;
     for (int v = 0; v < p.vpt; ++v) {
         const int vi = vi0 + v * (int)blockDim.x;
         if (vi >= p.nvec) return;
@@ -263,11 +270,19 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V
         const T* xs = static_cast<const T*>(p.x) + sbase + p0;
         T* xd = static_cast<T*>(p.x_out) + sbase + p0;
         const T* xo = INP ? static_cast<const T*>(p.x_orig) + sbase + p0 : nullptr;
-        if (v > 0) {  // the first pass's head stage and pixel set-up come from the caller
-            load_stage<T, V, TN, INP>(a, xs, xo, 0, C, p.HW);
+        // the next pass's pixels (its head stage is requested during this pass)
+        const int nvi = vi + (int)blockDim.x;
+        const bool more = TN::PF && v + 1 < p.vpt && nvi < p.nvec;
+        const int64_t np0 = (int64_t)nvi * V;
+        const T* nxs = more ? static_cast<const T*>(p.x) + sbase + np0 : nullptr;
+        const T* nxo = (more && INP) ? static_cast<const T*>(p.x_orig) + sbase + np0 : nullptr;
+        if (v > 0) {
+            if (!TN::PF) load_stage<T, V, TN, INP>(a, xs, xo, 0, C, p.HW);  // else requested during the last pass
             setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
         }
-        channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xs, xd, xo, C, p.HW);
+        const bool in_b = channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, b, L, s, coef, xs, xd, xo,
+                                                                                  nxs, nxo, C, p.HW);
+        if (more && in_b) a = b;
     }
 }
 
@@ -433,25 +448,39 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         run_sample<T, V, TN, NR, 0, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, keep_u, sig, sgn, mu_u, mu_c, mu_r);
 }
 
-// Channels per pipeline stage: 4 (more latent loads in flight per lane) where
-// the kernel still fits the 128 VGPRs of 4 waves per SIMD -- the occupancy the
-// launch shape of large batches assumes -- else 2 (measured: inpaint variants,
-// and bf16 with 3-4 regions or 2 regions under Heun, exceed 128 with 4).
+// Pipeline shape of a kernel variant: channels per stage (4 puts more latent
+// loads in flight per lane than 2) and whether a lane's next pass has its head
+// stage requested during the current pass.  Per variant, the first of (4,
+// prefetch), (2, prefetch), (4, none), (2, none) whose register count keeps
+// the waves per SIMD of (2, none), at most 4 -- the occupancy the launch shape
+// of large batches assumes -- from the register counts of every variant under
+// this toolchain; inpaint variants stay at 2 (4 reaches the 256-register
+// ceiling).  Only the speed depends on the choice: every variant computes the
+// same values in the same order.
 template <typename T, int NR, bool INP, bool HEUN>
 constexpr int stage_width() {
     if (INP) return 2;
-    if (sizeof(T) == 4) return 4;
-    return (NR <= 1 || (NR == 2 && !HEUN)) ? 4 : 2;
+    if (sizeof(T) == 4) return (NR == 4 && HEUN) ? 2 : 4;
+    if (NR <= 1) return 4;
+    if (NR == 4 && !HEUN) return 4;
+    return 2;
+}
+template <typename T, int NR, bool INP, bool HEUN>
+constexpr bool stage_prefetch() {
+    if (sizeof(T) == 4)
+        return !(INP && ((NR == 2 && HEUN) || (NR == 4 && !HEUN)));
+    if (INP) return !(NR == 2 && !HEUN);
+    return !(NR == 3 && HEUN);
 }
 
 template <typename T, int V, int NR, typename TN = DefaultTune>
 hipError_t launch_nr(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0))),
         blk((unsigned)block);
-    typedef Tune<stage_width<T, NR, true, true>(), TN::NT> TII;
-    typedef Tune<stage_width<T, NR, false, true>(), TN::NT> T0I;
-    typedef Tune<stage_width<T, NR, true, false>(), TN::NT> TI0;
-    typedef Tune<stage_width<T, NR, false, false>(), TN::NT> T00;
+    typedef Tune<stage_width<T, NR, true, true>(), TN::NT, stage_prefetch<T, NR, true, true>()> TII;
+    typedef Tune<stage_width<T, NR, false, true>(), TN::NT, stage_prefetch<T, NR, false, true>()> T0I;
+    typedef Tune<stage_width<T, NR, true, false>(), TN::NT, stage_prefetch<T, NR, true, false>()> TI0;
+    typedef Tune<stage_width<T, NR, false, false>(), TN::NT, stage_prefetch<T, NR, false, false>()> T00;
     if (heun) {
         if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true, TII>), grid, blk, 0, st, p);
         else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true, T0I>), grid, blk, 0, st, p);
