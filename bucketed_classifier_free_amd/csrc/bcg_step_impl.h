@@ -450,43 +450,62 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
 
 // Pipeline shape of a kernel variant: channels per stage (4 puts more latent
 // loads in flight per lane than 2) and whether a lane's next pass has its head
-// stage requested during the current pass.  Per variant, the first of (4,
-// prefetch), (2, prefetch), (4, none), (2, none) whose register count keeps
-// the waves per SIMD of (2, none), at most 4 -- the occupancy the launch shape
-// of large batches assumes -- from the register counts of every variant under
-// this toolchain; inpaint variants stay at 2 (4 reaches the 256-register
-// ceiling).  Only the speed depends on the choice: every variant computes the
-// same values in the same order.
-template <typename T, int NR, bool INP, bool HEUN>
+// stage requested during the current pass.  Both pay only where a lane waits on
+// HBM with few bytes in flight: on the nontemporal (streaming) variants.  There,
+// per variant, the first of (4, prefetch), (2, prefetch), (4, none), (2, none)
+// whose register count keeps the waves per SIMD of (2, none), at most 4 -- the
+// occupancy the launch shape of large batches assumes -- from the register
+// counts of every variant under this toolchain.  Inpaint variants stay at
+// (2, none): width 4 reaches the 256-register ceiling, and the prefetch, which
+// costs them 8 registers, has no measurement in their favour.  The cache-keep
+// variants, whose batch is partly held by the last-level cache, keep (2, none):
+// in place, the 2-region bf16 step measured 44.8 us per launch there against
+// 46.2 with the prefetch and 47.2 at width 4.  Only the speed depends on the
+// choice: every variant computes the same values in the same order.
+template <typename T, int NR, bool INP, bool HEUN, bool NT>
 constexpr int stage_width() {
-    if (INP) return 2;
+    if (!NT || INP) return 2;
     if (sizeof(T) == 4) return (NR == 4 && HEUN) ? 2 : 4;
     if (NR <= 1) return 4;
     if (NR == 4 && !HEUN) return 4;
     return 2;
 }
-template <typename T, int NR, bool INP, bool HEUN>
+template <typename T, int NR, bool INP, bool HEUN, bool NT>
 constexpr bool stage_prefetch() {
-    if (sizeof(T) == 4)
-        return !(INP && ((NR == 2 && HEUN) || (NR == 4 && !HEUN)));
-    if (INP) return !(NR == 2 && !HEUN);
-    return !(NR == 3 && HEUN);
+    if (!NT || INP) return false;
+    return sizeof(T) == 4 || !(NR == 3 && HEUN);
+}
+
+template <typename T, int NR, bool INP, bool HEUN, bool NT>
+using StageTune = Tune<stage_width<T, NR, INP, HEUN, NT>(), NT, stage_prefetch<T, NR, INP, HEUN, NT>()>;
+
+// One variant at its pipeline shape.  The table's shape needs channels to
+// overlap: a latent of at most 4 channels, or with fewer than two of the
+// table's stages per pass, runs at (2, none).  On the 4-channel workloads
+// (f32 and bf16, Euler and Heun, with and without inpaint) that shape measured
+// at least as fast as any other (Heun bf16: 5.68 us per launch against 5.77
+// at (2, prefetch) and 6.05 at (4, prefetch)); the 16-channel large workload
+// gains from the table (51.4 us against 53.2 at (2, none)).
+template <typename T, int V, int NR, bool INP, bool HEUN, bool NT>
+void launch_variant(const StepParams& p, dim3 grid, dim3 blk, hipStream_t st) {
+    typedef StageTune<T, NR, INP, HEUN, NT> Wide;
+    typedef Tune<2, NT, false> Narrow;
+    if (p.C > 4 && p.C >= 2 * Wide::U)
+        hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, Wide>), grid, blk, 0, st, p);
+    else
+        hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, Narrow>), grid, blk, 0, st, p);
 }
 
 template <typename T, int V, int NR, typename TN = DefaultTune>
 hipError_t launch_nr(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
     const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0))),
         blk((unsigned)block);
-    typedef Tune<stage_width<T, NR, true, true>(), TN::NT, stage_prefetch<T, NR, true, true>()> TII;
-    typedef Tune<stage_width<T, NR, false, true>(), TN::NT, stage_prefetch<T, NR, false, true>()> T0I;
-    typedef Tune<stage_width<T, NR, true, false>(), TN::NT, stage_prefetch<T, NR, true, false>()> TI0;
-    typedef Tune<stage_width<T, NR, false, false>(), TN::NT, stage_prefetch<T, NR, false, false>()> T00;
     if (heun) {
-        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, true, TII>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, true, T0I>), grid, blk, 0, st, p);
+        if (inp) launch_variant<T, V, NR, true, true, TN::NT>(p, grid, blk, st);
+        else launch_variant<T, V, NR, false, true, TN::NT>(p, grid, blk, st);
     } else {
-        if (inp) hipLaunchKernelGGL((guided_step_kernel<T, V, NR, true, false, TI0>), grid, blk, 0, st, p);
-        else hipLaunchKernelGGL((guided_step_kernel<T, V, NR, false, false, T00>), grid, blk, 0, st, p);
+        if (inp) launch_variant<T, V, NR, true, false, TN::NT>(p, grid, blk, st);
+        else launch_variant<T, V, NR, false, false, TN::NT>(p, grid, blk, st);
     }
     return hipGetLastError();
 }

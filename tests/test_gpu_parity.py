@@ -219,6 +219,45 @@ def test_streaming_cache_hint_is_bit_identical(kw):
     assert torch.equal(a, b)
 
 
+# The streaming (nontemporal) variants take their pipeline shape from the
+# channel count: 2 channels per stage without prefetch up to 4 channels, the
+# per-variant stage table beyond.  Every variant at each shape: bit for bit
+# equal to the cache-keep variant on every sample, and to mode M on two.
+STREAM_SHAPES = [
+    (4, 16, 16, 32),   # the stage table's shape, one pass per lane
+    (3, 5, 16, 24),    # width-4 variants fall back; width 2 ends on a 1-channel stage
+    (3, 9, 13, 21),    # H*W odd (scalar path); width 4 ends on a 1-channel stage
+    (800, 8, 64, 64),  # several passes per lane: the next pass's head stage is prefetched
+]
+
+
+@pytest.mark.parametrize("shape", STREAM_SHAPES)
+@pytest.mark.parametrize("kw", SMALL)
+def test_streaming_pipeline_shapes(shape, kw):
+    n, C, H, Wd = shape
+    sp = W.small_spec(n=n, C=C, H=H, W=Wd, steps=5, num_buckets=3, feather=3, **kw)
+    inp = W.make_inputs(sp)
+    s = _sampler(inp)
+    sig, table, cov = D.run_setup(inp)
+    k = 1
+    x_in = D.init_latent(inp, sig, sp.dtype).astype(np.float32)
+    x = to_dev(x_in, sp.dtype)
+    keep, stream = torch.full_like(x, float("nan")), torch.full_like(x, float("nan"))
+    s.step(k, x, keep, cache_hint=0)
+    s.step(k, x, stream, cache_hint=1)
+    torch.cuda.synchronize()
+    got = to_np(stream)
+    assert np.array_equal(to_np(keep), got, equal_nan=True)
+    p = D.build_plan(inp.start_step.astype(np.int64) + k, sp.steps, sp.num_buckets, table,
+                     inp.cfg_override, cov)
+    active = np.flatnonzero(p["bucket_id"] >= 0)
+    assert active.size > 0
+    for i, r in oracle_step_M(inp, sig, p, k, x_in, [int(active[0]), int(active[-1])]).items():
+        assert np.array_equal(got[i], r), f"sample {i} differs from mode M"
+    for i in np.flatnonzero(p["bucket_id"] < 0):
+        assert np.isnan(got[i]).all()
+
+
 @pytest.mark.parametrize("upload_batch,async_upload", [(1, False), (3, False), (8, True), (2, True)])
 def test_native_loop_matches_python_loop(upload_batch, async_upload):
     inp = W.make_inputs(W.small_spec(n=5, C=3, H=16, W=24, regions=2, inpaint=True, steps=7,
