@@ -33,10 +33,13 @@ inline int hip_status(hipError_t e, const char* what) {
 }
 
 // Launch shape of the streaming step kernels: workgroups of `block` lanes,
-// each lane taking `vpt` vectors.  Large batches get about one resident round
-// of workgroups (4 per CU on 256 CUs) with vpt > 1, so the per-workgroup
-// set-up is amortised and no partial second round is left; small batches
-// shrink the workgroup so the grid still spreads over the CUs.
+// each lane taking `vpt` vectors.  One vector per lane: a large batch is
+// several rounds of workgroups, which the hardware dispatcher hands to CUs as
+// earlier ones retire, so CUs whose waves run ahead take more of the work
+// and the launch ends without a long tail (a single resident round of
+// longer workgroups leaves the waves that lose arbitration finishing last).
+// Small batches shrink the workgroup so the grid still spreads over the
+// CUs; only grids beyond 2^22 workgroups give lanes more vectors.
 struct LaunchShape {
     int block, vpt;
 };
@@ -44,11 +47,8 @@ inline LaunchShape pick_shape(int64_t samples, int64_t nvec) {
     constexpr int64_t kResident = 256 * 4;
     int bs = 256, vpt = 1;
     auto blocks = [&](int b, int v) { return samples * ((nvec + (int64_t)b * v - 1) / ((int64_t)b * v)); };
-    if (blocks(bs, vpt) > kResident * 3 / 2) {
-        while (vpt < 8 && blocks(bs, vpt) > kResident * 3 / 2) vpt *= 2;
-    } else {
-        while (bs > 64 && blocks(bs, vpt) < kResident) bs /= 2;
-    }
+    while (bs > 64 && blocks(bs, vpt) < kResident) bs /= 2;
+    while (vpt < 64 && blocks(bs, vpt) > ((int64_t)1 << 22)) vpt *= 2;
     return {bs, vpt};
 }
 

@@ -142,14 +142,22 @@ struct Stage {
     typename Io<T, V>::Raw o[INP ? U : 1];
 };
 
+// Channel visited at walk position c (0 <= c < C) by a workgroup whose walk
+// starts at channel rot (0 <= rot < C).
+__device__ __forceinline__ int walk_channel(int c, int rot, int C) {
+    const int r = c + rot;
+    return r >= C ? r - C : r;
+}
+
 template <typename T, int V, typename TN, bool INP>
 __device__ __forceinline__ void load_stage(Stage<T, V, TN::U, INP>& sg, const T* xs, const T* xo,
-                                           int c0, int C, int64_t HW) {
+                                           int c0, int rot, int C, int64_t HW) {
 #pragma unroll
     for (int u = 0; u < TN::U; ++u) {
         if (c0 + u < C) {
-            sg.x[u] = Io<T, V>::template load_raw<TN::NT>(xs + (c0 + u) * HW);
-            if constexpr (INP) sg.o[u] = Io<T, V>::template load_raw<TN::NT>(xo + (c0 + u) * HW);
+            const int64_t off = (int64_t)walk_channel(c0 + u, rot, C) * HW;
+            sg.x[u] = Io<T, V>::template load_raw<TN::NT>(xs + off);
+            if constexpr (INP) sg.o[u] = Io<T, V>::template load_raw<TN::NT>(xo + off);
         }
     }
 }
@@ -157,10 +165,11 @@ __device__ __forceinline__ void load_stage(Stage<T, V, TN::U, INP>& sg, const T*
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
 __device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg, const LaneState<V, NR>& L,
                                               const StepScalars& s, const float* __restrict__ coef,
-                                              T* xd, int c0, int C, int64_t HW) {
+                                              T* xd, int c0, int rot, int C, int64_t HW) {
 #pragma unroll
     for (int u = 0; u < TN::U; ++u) {
         if (c0 + u < C) {
+            const int c = walk_channel(c0 + u, rot, C);
             float xv[V], ov[V], out[V];
             Io<T, V>::unpack(sg.x[u], xv);
             if constexpr (INP) Io<T, V>::unpack(sg.o[u], ov);
@@ -168,8 +177,8 @@ __device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg,
 #pragma unroll
                 for (int e = 0; e < V; ++e) ov[e] = 0.f;
             }
-            update_vec<V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c0 + u, xv, ov, out);
-            Io<T, V>::template store<TN::NT>(xd + (c0 + u) * HW, out);
+            update_vec<V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c, xv, ov, out);
+            Io<T, V>::template store<TN::NT>(xd + (int64_t)c * HW, out);
         }
     }
 }
@@ -183,16 +192,16 @@ template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, 
 __device__ __forceinline__ bool channel_loop(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b,
                                              const LaneState<V, NR>& L, const StepScalars& s,
                                              const float* __restrict__ coef, const T* xs, T* xd, const T* xo,
-                                             const T* nxs, const T* nxo, int C, int64_t HW) {
+                                             const T* nxs, const T* nxo, int rot, int C, int64_t HW) {
     constexpr int U = TN::U;
     for (int c0 = 0;; c0 += 2 * U) {
-        if (c0 + U < C) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, C, HW);
-        else if (nxs) load_stage<T, V, TN, INP>(b, nxs, nxo, 0, C, HW);
-        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, C, HW);
+        if (c0 + U < C) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, rot, C, HW);
+        else if (nxs) load_stage<T, V, TN, INP>(b, nxs, nxo, 0, rot, C, HW);
+        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, rot, C, HW);
         if (c0 + U >= C) return true;
-        if (c0 + 2 * U < C) load_stage<T, V, TN, INP>(a, xs, xo, c0 + 2 * U, C, HW);
-        else if (nxs) load_stage<T, V, TN, INP>(a, nxs, nxo, 0, C, HW);
-        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, xd, c0 + U, C, HW);
+        if (c0 + 2 * U < C) load_stage<T, V, TN, INP>(a, xs, xo, c0 + 2 * U, rot, C, HW);
+        else if (nxs) load_stage<T, V, TN, INP>(a, nxs, nxo, 0, rot, C, HW);
+        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, xd, c0 + U, rot, C, HW);
         if (c0 + 2 * U >= C) return false;
     }
 }
@@ -259,7 +268,7 @@ template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, 
 __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V, NR>& L,
                                          const SampleRegions<NR>& sr, const StepParams& p,
                                          const StepScalars& s, const float* __restrict__ coef, int i,
-                                         int vi0, bool keep_u) {
+                                         int vi0, int rot, bool keep_u) {
     const int C = p.C;
     const int64_t sbase = (int64_t)i * C * p.HW;
     Stage<T, V, TN::U, INP> b;
@@ -277,11 +286,11 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V
         const T* nxs = more ? static_cast<const T*>(p.x) + sbase + np0 : nullptr;
         const T* nxo = (more && INP) ? static_cast<const T*>(p.x_orig) + sbase + np0 : nullptr;
         if (v > 0) {
-            if (!TN::PF) load_stage<T, V, TN, INP>(a, xs, xo, 0, C, p.HW);  // else requested during the last pass
+            if (!TN::PF) load_stage<T, V, TN, INP>(a, xs, xo, 0, rot, C, p.HW);  // else requested during the last pass
             setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
         }
         const bool in_b = channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, b, L, s, coef, xs, xd, xo,
-                                                                                  nxs, nxo, C, p.HW);
+                                                                                  nxs, nxo, rot, C, p.HW);
         if (more && in_b) a = b;
     }
 }
@@ -293,7 +302,7 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN>
 __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, bool lane_ok,
                                            const SampleRegions<NR>& sr, const StepParams& p,
-                                           StepScalars s, float* coef, int i, int vi0, bool keep_u,
+                                           StepScalars s, float* coef, int i, int vi0, int rot, bool keep_u,
                                            float sig, float sgn, float mu_u, float mu_c,
                                            const float (&mu_r)[NR > 0 ? NR : 1]) {
     LaneState<V, NR> L;
@@ -335,11 +344,11 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, bool lane
     const bool one = (s.w == 1.0f);
     const bool fin = (sgn == 0.0f);
     if (one) {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, L, sr, p, s, coef, i, vi0, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, L, sr, p, s, coef, i, vi0, keep_u);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
     } else {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, L, sr, p, s, coef, i, vi0, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, L, sr, p, s, coef, i, vi0, keep_u);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
     }
 }
 
@@ -372,27 +381,45 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
     const bool lane_ok = vi0 < p.nvec;
 
-    // Channel k's means (lane k), then the head stage of the latent.
+    // Channel k's means (lane k), the region tables and the head stage of the
+    // latent, all requested before anything waits: every region slot below NR
+    // is read (the slot index clamped to the table's R), and the sample's
+    // count only selects among them afterwards.
     const int k = (int)threadIdx.x & 63;
     const int kk = k < C ? k : 0;
     const float mu_u = p.mu_uncond[(int64_t)i * C + kk];
     const float mu_c = p.mu_cond[(int64_t)i * C + kk];
     int cnt = 0;
+    float mu_r[NR > 0 ? NR : 1];
+    int4 box[NR > 0 ? NR : 1];
+    float str[NR > 0 ? NR : 1];
     if constexpr (NR > 0) {
         cnt = p.region_count[i];
-        cnt = cnt < 0 ? 0 : cnt;
-        cnt = cnt > p.R ? p.R : cnt;
-        cnt = cnt > NR ? NR : cnt;
-    }
-    float mu_r[NR > 0 ? NR : 1];
 #pragma unroll
-    for (int r = 0; r < (NR > 0 ? NR : 1); ++r)
-        mu_r[r] = (NR > 0 && r < cnt) ? p.mu_region[((int64_t)i * p.R + r) * C + kk] : 0.0f;
+        for (int r = 0; r < NR; ++r) {
+            const int64_t slot = (int64_t)i * p.R + (r < p.R ? r : p.R - 1);
+            const int32_t* b = p.region_box + slot * 4;
+            box[r] = make_int4(b[0], b[1], b[2], b[3]);
+            str[r] = p.region_strength[slot];
+            mu_r[r] = p.mu_region[slot * C + kk];
+        }
+    }
+    // The workgroup's channel walk starts at channel 5*blockIdx mod C, so the
+    // workgroups in flight spread their requests over the channel planes
+    // instead of all reading one plane's rows at a time.
+    const int rot = (int)((5u * blockIdx.x) % (unsigned)C);
     Stage<T, V, TN::U, INP> a;
     if (lane_ok) {
         const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
         load_stage<T, V, TN, INP>(a, static_cast<const T*>(p.x) + base,
-                                  INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, C, p.HW);
+                                  INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, rot, C, p.HW);
+    }
+    if constexpr (NR > 0) {
+        cnt = cnt < 0 ? 0 : cnt;
+        cnt = cnt > p.R ? p.R : cnt;
+        cnt = cnt > NR ? NR : cnt;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) mu_r[r] = r < cnt ? mu_r[r] : 0.0f;
     }
     // The sample's step: from its record when given (one load that waits for
     // nothing else), else derived from its step index.
@@ -429,12 +456,11 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             if (r < cnt) {
-                const int32_t* b = p.region_box + ((int64_t)i * p.R + r) * 4;
-                sr.rd[r].y0 = b[0];
-                sr.rd[r].h = b[1] - b[0];
-                sr.rd[r].x0 = b[2];
-                sr.rd[r].w = b[3] - b[2];
-                sr.rd[r].strength = ((valid >> r) & 1u) ? p.region_strength[(int64_t)i * p.R + r] : 0.0f;
+                sr.rd[r].y0 = box[r].x;
+                sr.rd[r].h = box[r].y - box[r].x;
+                sr.rd[r].x0 = box[r].z;
+                sr.rd[r].w = box[r].w - box[r].z;
+                sr.rd[r].strength = ((valid >> r) & 1u) ? str[r] : 0.0f;
             } else {
                 sr.rd[r].y0 = sr.rd[r].x0 = 0;
                 sr.rd[r].h = sr.rd[r].w = 0;
@@ -443,32 +469,33 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         }
     }
     if (NR > 0 && cnt > 0)
-        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, keep_u, sig, sgn, mu_u, mu_c, mu_r);
+        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
     else
-        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, keep_u, sig, sgn, mu_u, mu_c, mu_r);
+        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
 }
 
 // Pipeline shape of a kernel variant: channels per stage (4 puts more latent
 // loads in flight per lane than 2) and whether a lane's next pass has its head
-// stage requested during the current pass.  Both pay only where a lane waits on
-// HBM with few bytes in flight: on the nontemporal (streaming) variants.  There,
-// per variant, the first of (4, prefetch), (2, prefetch), (4, none), (2, none)
-// whose register count keeps the waves per SIMD of (2, none), at most 4 -- the
-// occupancy the launch shape of large batches assumes -- from the register
-// counts of every variant under this toolchain.  Inpaint variants stay at
-// (2, none): width 4 reaches the 256-register ceiling, and the prefetch, which
-// costs them 8 registers, has no measurement in their favour.  The cache-keep
-// variants, whose batch is partly held by the last-level cache, keep (2, none):
-// in place, the 2-region bf16 step measured 44.8 us per launch there against
-// 46.2 with the prefetch and 47.2 at width 4.  Only the speed depends on the
-// choice: every variant computes the same values in the same order.
+// stage requested during the current pass (only lanes with more than one
+// vector have a next pass).  Both pay only where a lane waits on HBM with few
+// bytes in flight: on the nontemporal (streaming) variants.  There, from the
+// register counts of every variant under this toolchain: fp32 takes
+// (4, prefetch) at 4 waves per SIMD, except 4 regions under Heun (2, prefetch);
+// bf16 takes (4, prefetch) up to 2 regions (3 or 4 waves per SIMD), and width 2
+// with 3 or 4 regions (prefetch except 3 regions under Heun, where it would
+// cost a wave).  Measured on the large 2-region bf16 workload (one vector per
+// lane, several rounds of workgroups): (4, prefetch) 50.2 us per launch at 3
+// waves per SIMD against 50.9 at (2, prefetch) and 51.0 at (4, none), both at
+// 4.  Inpaint variants stay at (2, none): width 4 reaches the 256-register
+// ceiling, and the prefetch, which costs them 8 registers, has no measurement
+// in their favour.  The cache-keep variants, whose batch is partly held by the
+// last-level cache, keep (2, none).  Only the speed depends on the choice:
+// every variant computes the same values in the same order.
 template <typename T, int NR, bool INP, bool HEUN, bool NT>
 constexpr int stage_width() {
     if (!NT || INP) return 2;
     if (sizeof(T) == 4) return (NR == 4 && HEUN) ? 2 : 4;
-    if (NR <= 1) return 4;
-    if (NR == 4 && !HEUN) return 4;
-    return 2;
+    return NR <= 2 ? 4 : 2;
 }
 template <typename T, int NR, bool INP, bool HEUN, bool NT>
 constexpr bool stage_prefetch() {
@@ -485,7 +512,7 @@ using StageTune = Tune<stage_width<T, NR, INP, HEUN, NT>(), NT, stage_prefetch<T
 // (f32 and bf16, Euler and Heun, with and without inpaint) that shape measured
 // at least as fast as any other (Heun bf16: 5.68 us per launch against 5.77
 // at (2, prefetch) and 6.05 at (4, prefetch)); the 16-channel large workload
-// gains from the table (51.4 us against 53.2 at (2, none)).
+// gains from the table.
 template <typename T, int V, int NR, bool INP, bool HEUN, bool NT>
 void launch_variant(const StepParams& p, dim3 grid, dim3 blk, hipStream_t st) {
     typedef StageTune<T, NR, INP, HEUN, NT> Wide;
