@@ -213,7 +213,27 @@ struct SampleRegions {
     int cnt;
 };
 
-// Region weights, coverage and mask of the V pixels starting at p0.
+// Normalised weights, coverage flag and guided-scale of one pixel from its
+// region weights ws (sum, one correctly rounded reciprocal, products).
+template <int V, int NR, int NRB>
+__device__ __forceinline__ void finish_pixel(LaneState<V, NR>& L, int e, const float (&ws)[NRB], float w,
+                                             bool keep_u) {
+    float wsum = ws[0];
+#pragma unroll
+    for (int r = 1; r < NRB; ++r) wsum = wsum + ws[r];
+    const bool cv = wsum > 0.0f;
+    const float iw = cv ? 1.0f / wsum : 0.0f;
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) L.wh[r][e] = ws[r] * iw;
+    L.weff[e] = cv ? w : 0.0f;
+    L.sel[e] = keep_u ? cv : true;
+}
+
+// Region weights, coverage and mask of the V pixels starting at p0.  When
+// the lane's pixels share a row, the feather's row factor is the lane's and
+// each pixel adds its column factor: n = n_y * n_x with both factors products
+// of two clamped distances (at most F^2 <= 4096, so 24-bit multiplies are
+// exact), the same integer region_weight forms, converted and scaled alike.
 template <int V, int NR, int NRB, bool INP>
 __device__ __forceinline__ void setup_lane(LaneState<V, NR>& L, const SampleRegions<NR>& sr,
                                            const StepParams& p, int i, int64_t p0, float w,
@@ -223,37 +243,40 @@ __device__ __forceinline__ void setup_lane(LaneState<V, NR>& L, const SampleRegi
         const float inv_f4 = p.inv_f4;
         const int y = (int)(p0 / p.W);
         const int xx = (int)(p0 - (int64_t)y * p.W);
-        int ny[NRB];  // feather numerators of the lane's row (row-aligned lanes)
-#pragma unroll
-        for (int r = 0; r < NRB; ++r) {
-            const int dy = y - sr.rd[r].y0;
-            ny[r] = (dy >= 0 && dy < sr.rd[r].h) ? min(dy + 1, F) * min(sr.rd[r].h - dy, F) : 0;
-        }
-        const bool aligned = p.rows_aligned != 0;
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-            float ws[NRB];
+        if (p.rows_aligned != 0) {
+            unsigned ny[NRB];  // feather factors of the lane's row
+            int dx0[NRB];      // column of the lane's first pixel inside each box
 #pragma unroll
             for (int r = 0; r < NRB; ++r) {
-                if (aligned) {
-                    const int dx = xx + e - sr.rd[r].x0;
-                    const int nx = (dx >= 0 && dx < sr.rd[r].w) ? min(dx + 1, F) * min(sr.rd[r].w - dx, F) : 0;
-                    const float f = float(ny[r] * nx) * inv_f4;
+                const int dy = y - sr.rd[r].y0;
+                const unsigned f = __umul24((unsigned)min(dy + 1, F), (unsigned)min(sr.rd[r].h - dy, F));
+                ny[r] = (unsigned)dy < (unsigned)sr.rd[r].h ? f : 0u;
+                dx0[r] = xx - sr.rd[r].x0;
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float ws[NRB];
+#pragma unroll
+                for (int r = 0; r < NRB; ++r) {
+                    const int dx = dx0[r] + e;
+                    const unsigned fx = __umul24((unsigned)min(dx + 1, F), (unsigned)min(sr.rd[r].w - dx, F));
+                    const unsigned nx = (unsigned)dx < (unsigned)sr.rd[r].w ? fx : 0u;
+                    const float f = float(__umul24(ny[r], nx)) * inv_f4;
                     ws[r] = sr.rd[r].strength * f;
-                } else {
+                }
+                finish_pixel<V, NR, NRB>(L, e, ws, w, keep_u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float ws[NRB];
+#pragma unroll
+                for (int r = 0; r < NRB; ++r) {
                     const int px = xx + e;  // walk the row, wrapping to the next
                     ws[r] = region_weight(sr.rd[r], y + px / p.W, px - (px / p.W) * p.W, F, inv_f4);
                 }
+                finish_pixel<V, NR, NRB>(L, e, ws, w, keep_u);
             }
-            float wsum = ws[0];
-#pragma unroll
-            for (int r = 1; r < NRB; ++r) wsum = wsum + ws[r];
-            const bool cv = wsum > 0.0f;
-            const float iw = cv ? 1.0f / wsum : 0.0f;
-#pragma unroll
-            for (int r = 0; r < NRB; ++r) L.wh[r][e] = ws[r] * iw;
-            L.weff[e] = cv ? w : 0.0f;
-            L.sel[e] = keep_u ? cv : true;
         }
     }
     if constexpr (INP) {
