@@ -13,7 +13,8 @@
 //                    x' = fma(d + d', hh, x) (x~ copied on a last step).
 // Layout and streaming as the fused inline step: workgroup = sample x tile of
 // 16-byte vectors, lanes take vpt vectors blockDim apart and walk the channel
-// planes with the next channel's loads in flight; per-sample modes (scale 1,
+// planes (from a start channel rotated per workgroup) with the next channel's
+// loads in flight; per-sample modes (scale 1,
 // last step) are uniform branches outside the channel loop.
 #pragma once
 
@@ -136,7 +137,7 @@ __device__ __forceinline__ void rows_compute(const RowsStage<T, V, M>& sg, const
 
 template <typename T, int V, int PHASE, bool INP, bool NT, bool ONE, bool FIN>
 __device__ __forceinline__ void rows_sample(const RowsParams& p, const RowsScalars& s, int i, int cr,
-                                            int ur, int vi0) {
+                                            int ur, int vi0, int rot) {
     typedef RowsMode<PHASE, ONE, FIN, INP> M;
     const int C = p.C;
     const int64_t HW = p.HW;
@@ -153,12 +154,16 @@ __device__ __forceinline__ void rows_sample(const RowsParams& p, const RowsScala
 #pragma unroll
             for (int e = 0; e < V; ++e) om[e] = 1.0f - m[e];
         }
+        // walk position c is channel (c + rot) mod C
+        auto plane = [&](int c) { return (int64_t)(c + rot >= C ? c + rot - C : c + rot) * HW; };
         RowsStage<T, V, M> a, b;
-        rows_load<T, V, M, NT>(a, p, xb, cb, ub);
+        const int64_t o0 = plane(0);
+        rows_load<T, V, M, NT>(a, p, xb + o0, cb + o0, ub + o0);
         for (int c0 = 0;; c0 += 2) {
-            const int64_t o1 = (int64_t)(c0 + 1) * HW, o2 = (int64_t)(c0 + 2) * HW;
+            const int64_t oa = plane(c0);
+            const int64_t o1 = c0 + 1 < C ? plane(c0 + 1) : 0, o2 = c0 + 2 < C ? plane(c0 + 2) : 0;
             if (c0 + 1 < C) rows_load<T, V, M, NT>(b, p, xb + o1, cb + o1, ub + o1);
-            rows_compute<T, V, PHASE, M, NT>(a, p, s, m, om, xb + (int64_t)c0 * HW);
+            rows_compute<T, V, PHASE, M, NT>(a, p, s, m, om, xb + oa);
             if (c0 + 1 >= C) break;
             if (c0 + 2 < C) rows_load<T, V, M, NT>(a, p, xb + o2, cb + o2, ub + o2);
             rows_compute<T, V, PHASE, M, NT>(b, p, s, m, om, xb + o1);
@@ -192,12 +197,15 @@ __global__ __launch_bounds__(256) void rows_kernel(const RowsParams p) {
     s.isn = 1.0f / sgn;
     s.hh = s.h * 0.5f;
     const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
+    // the workgroup's walk starts at channel 5*blockIdx mod C, so the
+    // workgroups in flight spread their requests over the channel planes
+    const int rot = (int)((5u * blockIdx.x) % (unsigned)p.C);
     if (one) {
-        if (fin) rows_sample<T, V, PHASE, INP, NT, true, true>(p, s, i, cr, ur, vi0);
-        else rows_sample<T, V, PHASE, INP, NT, true, false>(p, s, i, cr, ur, vi0);
+        if (fin) rows_sample<T, V, PHASE, INP, NT, true, true>(p, s, i, cr, ur, vi0, rot);
+        else rows_sample<T, V, PHASE, INP, NT, true, false>(p, s, i, cr, ur, vi0, rot);
     } else {
-        if (fin) rows_sample<T, V, PHASE, INP, NT, false, true>(p, s, i, cr, ur, vi0);
-        else rows_sample<T, V, PHASE, INP, NT, false, false>(p, s, i, cr, ur, vi0);
+        if (fin) rows_sample<T, V, PHASE, INP, NT, false, true>(p, s, i, cr, ur, vi0, rot);
+        else rows_sample<T, V, PHASE, INP, NT, false, false>(p, s, i, cr, ur, vi0, rot);
     }
 }
 
