@@ -185,12 +185,15 @@ def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
 
 
 def rows_bench(inp, args):
-    """Steady state of the materialised-branch update: per step, the plan of
-    one batch is built on the device (bcg_plan_device) and guided_step_rows
-    reads that batch's model-output rows in the plan's layout.  The rows are
-    synthetic and resident (one buffer per batch and evaluation: no model
-    runs here); the uncond rows of samples whose uncond branch is skipped
-    are neither produced nor read."""
+    """Steady state of the materialised-branch update: guided_step_rows reads
+    each batch's model-output rows in the layout of that step's device-built
+    plan.  By default the launch also builds the batch's next plan
+    (guided_step_rows_dplan: the plan of step m+1 is due before the model's
+    forward of step m+1, i.e. after the update of step m); --rows-plan separate
+    builds each step's plan in its own launch (bcg_plan_device) first.  The rows
+    are synthetic and resident (one buffer per batch and evaluation: no model
+    runs here); the uncond rows of samples whose uncond branch is skipped are
+    neither produced nor read."""
     import numpy as np
     import torch
     from bucketed_classifier_free_amd import GuidedSampler, api
@@ -208,32 +211,47 @@ def rows_bench(inp, args):
     pred = torch.randn((R, evals, 2 * n, spec.C, spec.H, spec.W), generator=g, device="cuda").to(s.tdtype)
     dbuf = torch.empty((n, spec.C, spec.H, spec.W), dtype=torch.float32, device="cuda") if heun else None
     xt = torch.empty_like(x[0]) if heun else None
-    steps_state = torch.empty((R, 2, n), dtype=torch.int32, device="cuda")
+    fused = args.rows_plan == "fused"
+    # step indices: three buffers per batch (step m's, read by its update, while
+    # the fused plan of step m+1 reads m+1's and writes m+2's); two plans per batch
+    steps_state = torch.empty((R, 3, n), dtype=torch.int32, device="cuda")
     steps_state[:, 0] = torch.from_numpy(s.step_indices(0)).cuda()
-    plans = [api.device_plan_arrays(n, s.nb) for _ in range(R)]
+    plans = [[api.device_plan_arrays(n, s.nb) for _ in range(2)] for _ in range(R)]
     hint = L.BCG_CACHE_STREAM if R > 1 else L.BCG_CACHE_KEEP
     opt = dict(x_orig=s.d_x_orig, mask=s.d_mask, cache_hint=hint)
+    pkw = dict(cfg_override=s.d_override, covered=s.d_covered, wrap=True, bucket_cfg_end=s.d_table_end)
+
+    def build_plan(r, m):  # the plan of batch r's step m, in its own launch
+        api.bcg_plan_device(s.steps, s.d_table, steps_state[r, m % 3], step_out=steps_state[r, (m + 1) % 3],
+                            out=plans[r][m & 1], **pkw)
+
+    if fused:
+        for r in range(R):
+            build_plan(r, 0)
 
     def step(k):
         r, m = k % R, k // R
-        st_in, st_out = steps_state[r, m & 1], steps_state[r, (m + 1) & 1]
-        pl = plans[r]
-        api.bcg_plan_device(s.steps, s.d_table, st_in, step_out=st_out, cfg_override=s.d_override,
-                            covered=s.d_covered, wrap=True, out=pl, bucket_cfg_end=s.d_table_end)
-        rows = dict(order=pl["order"], step_idx=st_in, scale=pl["scale"],
+        if not fused:
+            build_plan(r, m)
+        pl = plans[r][m & 1]
+        rows = dict(order=pl["order"], step_idx=steps_state[r, m % 3], scale=pl["scale"],
                     uncond_row=pl["uncond_row"], cond_row=pl["cond_row"])
+        first = dict(phase="heun_predict", d=dbuf) if heun else dict(phase="euler")
+        out0 = xt if heun else x[r]
+        if fused:
+            nxt = api.device_plan(s.steps, s.d_table, steps_state[r, (m + 1) % 3],
+                                  step_out=steps_state[r, (m + 2) % 3], out=plans[r][(m + 1) & 1], **pkw)
+            api.guided_step_rows_dplan(x[r], out0, pred[r, 0], s.d_sigmas, n_active=n, plan=nxt,
+                                       **first, **rows, **opt)
+        else:
+            api.guided_step_rows(x[r], out0, pred[r, 0], s.d_sigmas, n_active=n, **first, **rows, **opt)
         if heun:
-            api.guided_step_rows(x[r], xt, pred[r, 0], s.d_sigmas, n_active=n, phase="heun_predict",
-                                 d=dbuf, **rows, **opt)
             api.guided_step_rows(x[r], x[r], pred[r, 1], s.d_sigmas, n_active=n, phase="heun_correct",
                                  d=dbuf, x_tilde=xt, **rows, **opt)
-        else:
-            api.guided_step_rows(x[r], x[r], pred[r, 0], s.d_sigmas, n_active=n, phase="euler",
-                                 **rows, **opt)
 
-    # Whole steps (plan + update) replayed from a graph of G steps: G is a
-    # multiple of the step-buffer period 2R, so replays continue the sequence.
-    G = 2 * R * max(1, -(-16 // (2 * R)))
+    # Whole steps replayed from a graph of G steps: G is a multiple of the
+    # step-buffer period 6R, so replays continue the sequence.
+    G = 6 * R * max(1, -(-16 // (6 * R)))
     for k in range(G):
         step(k)
     torch.cuda.synchronize()
@@ -277,14 +295,17 @@ def rows_bench(inp, args):
         "higher_is_better": True, "dtype": "f32", "data": "synthetic",
         "config": {"workload": spec.name, "batch": n, "latent": [spec.C, spec.H, spec.W],
                    "storage": spec.dtype, "sampler": spec.sampler, "replicas": R,
-                   "uncond_rows_kept": keep, "plan": "device (its own launch before the update)",
+                   "uncond_rows_kept": keep,
+                   "plan": ("device, the next step's built in the update's launch" if fused
+                            else "device (its own launch before the update)"),
                    "graph_steps": G},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None},
         "kernel": {"name": "guided_step_rows", "calls_per_step": evals,
                    "avg_us_per_step": step_ms * 1e3, "bytes_per_element_step": bpe,
-                   "timing": "events around the graph replays; a step is the plan launch plus "
-                             "the update launch(es), so achieved GB/s is a lower bound for the update"}}),
+                   "timing": "events around the graph replays; a step is the update launch(es) and "
+                             "the plan (in the first update launch, or its own launch), so achieved "
+                             "GB/s is a lower bound for the update"}}),
         flush=True)
 
 
@@ -481,6 +502,9 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=-1,
                     help="processes of the parallel oracle baseline (-1: the affinity cores, at most 16; 0: off)")
     ap.add_argument("--buckets", type=int, default=0, help="override the workload's bucket count")
+    ap.add_argument("--rows-plan", choices=("fused", "separate"), default="fused",
+                    help="with --rows: the next step's plan built in the update's launch (fused) or "
+                         "each step's plan in its own launch first (separate)")
     ap.add_argument("--rows", action="store_true",
                     help="materialised branches: time guided_step_rows on model-output rows laid out "
                          "by a device-built plan (both Heun calls for a Heun workload)")

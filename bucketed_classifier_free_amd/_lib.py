@@ -23,13 +23,14 @@ BCG_MAX_DEVICE_STEPS = 1 << 20
 BCG_MAX_PATCHES = 8
 BCG_PATCH = {"diff": 0, "lowrank": 1}
 BCG_ROUND = {"nearest": 0, "stochastic": 1}
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
            "bucket_bounds",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
            "area_accumulate", "mask_blend", "bcg_plan_records", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
+           "guided_step_rows_dplan",
            "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy", "weight_patch"]
 
 vp, i32p, i64p, f32p, f64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64),
@@ -131,6 +132,7 @@ def lib():
         L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]
         L.bcg_plan_records.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, vp, C.c_int, vp]
         L.guided_step_rows.argtypes = [C.POINTER(RowsArgs), vp]
+        L.guided_step_rows_dplan.argtypes = [C.POINTER(RowsArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_workspace_size.argtypes = [C.c_int] * 5
         L.guided_step_workspace_size.restype = C.c_size_t

@@ -256,13 +256,8 @@ def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond,
     L.check(L.lib().guided_step(ct.byref(a), _stream(stream)))
 
 
-def guided_step_rows(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
-                     n_active: int, phase: str = "euler", d=None, x_tilde=None, x_orig=None,
-                     mask=None, cache_hint: int = 0, stream=None):
-    """The guided update from materialised branch predictions ``pred``
-    [rows, C, H, W] in the plan's [uncond | cond] layout (see include/bcg.h);
-    ``phase`` is "euler", "heun_predict" (writes ``d`` and x~ to x_out) or
-    "heun_correct" (reads ``d`` and, for last steps, ``x_tilde``)."""
+def _rows_args(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
+               n_active, phase, d, x_tilde, x_orig, mask, cache_hint) -> L.RowsArgs:
     _dev(x, "x")
     if x.dim() != 4 or x.dtype not in _DT:
         raise ValueError("x must be [n, C, H, W] float32 or bfloat16")
@@ -296,7 +291,33 @@ def guided_step_rows(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row,
                    pred.shape[0], mps, int(cache_hint), _ptr(x), _ptr(x_out), _ptr(d),
                    _ptr(x_tilde), _ptr(pred), _ptr(sigmas), _ptr(order), _ptr(step_idx),
                    _ptr(scale), _ptr(uncond_row), _ptr(cond_row), _ptr(x_orig), _ptr(mask))
+    return a
+
+
+def guided_step_rows(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
+                     n_active: int, phase: str = "euler", d=None, x_tilde=None, x_orig=None,
+                     mask=None, cache_hint: int = 0, stream=None):
+    """The guided update from materialised branch predictions ``pred``
+    [rows, C, H, W] in the plan's [uncond | cond] layout (see include/bcg.h);
+    ``phase`` is "euler", "heun_predict" (writes ``d`` and x~ to x_out) or
+    "heun_correct" (reads ``d`` and, for last steps, ``x_tilde``)."""
+    a = _rows_args(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row,
+                   n_active=n_active, phase=phase, d=d, x_tilde=x_tilde, x_orig=x_orig, mask=mask,
+                   cache_hint=cache_hint)
     L.check(L.lib().guided_step_rows(ct.byref(a), _stream(stream)))
+
+
+def guided_step_rows_dplan(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
+                           n_active: int, plan: L.DevicePlan, phase: str = "euler", d=None,
+                           x_tilde=None, x_orig=None, mask=None, cache_hint: int = 0, stream=None):
+    """guided_step_rows, and in the same launch the device plan ``plan``
+    (from device_plan(): typically the next step's) as bcg_plan_device builds it."""
+    a = _rows_args(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row,
+                   n_active=n_active, phase=phase, d=d, x_tilde=x_tilde, x_orig=x_orig, mask=mask,
+                   cache_hint=cache_hint)
+    if not isinstance(plan, L.DevicePlan):
+        raise ValueError("plan must come from device_plan()")
+    L.check(L.lib().guided_step_rows_dplan(ct.byref(a), ct.byref(plan), _stream(stream)))
 
 
 # ---------------------------------------------------------------- device plans

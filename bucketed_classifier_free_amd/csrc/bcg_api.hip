@@ -479,12 +479,8 @@ extern "C" int guided_step_dplan(const bcg_step_args* a, const bcg_device_plan* 
     return step_impl(a, d, stream, "guided_step_dplan");
 }
 
-extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
-    bcg::clear_error();
-    if (n < 0 || n > (1 << 24)) return fail(BCG_ESHAPE, "bcg_plan_device: n %d out of range", n);
-    const int rc = check_dplan(d, n, false, "bcg_plan_device");
-    if (rc) return rc;
-    if (n == 0) return BCG_OK;
+// Parameters of a plan built on its own (no step in the same workgroup).
+static StepParams plan_only_params(int n, const bcg_device_plan* d) {
     StepParams p{};
     p.n = n;
     fill_dplan(p, d);
@@ -494,13 +490,30 @@ extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
     p.region_count = d->region_count;
     p.sigmas = d->sigmas;
     p.num_sigmas = d->num_sigmas;
+    return p;
+}
+
+extern "C" int bcg_plan_device(int n, const bcg_device_plan* d, void* stream) {
+    bcg::clear_error();
+    if (n < 0 || n > (1 << 24)) return fail(BCG_ESHAPE, "bcg_plan_device: n %d out of range", n);
+    const int rc = check_dplan(d, n, false, "bcg_plan_device");
+    if (rc) return rc;
+    if (n == 0) return BCG_OK;
+    const StepParams p = plan_only_params(n, d);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), p);
     return hip_status(hipGetLastError(), "bcg_plan_device: launch");
 }
 
-extern "C" int guided_step_rows(const bcg_rows_args* a, void* stream) {
-    bcg::clear_error();
-    const char* who = "guided_step_rows";
+// A rows call, validated, with its launch shape (launch is false when there
+// is no sample to update).
+struct RowsLaunch {
+    RowsParams p;
+    bool vec, inpaint, nt, launch;
+    int block;
+    int dtype;
+};
+
+static int rows_prepare(const bcg_rows_args* a, const char* who, RowsLaunch& L) {
     if (!a) return fail(BCG_EINVAL, "%s: args is NULL", who);
     if (a->n < 0 || a->C < 1 || a->H < 1 || a->W < 1)
         return fail(BCG_ESHAPE, "%s: bad shape n=%d C=%d H=%d W=%d", who, a->n, a->C, a->H, a->W);
@@ -517,7 +530,9 @@ extern "C" int guided_step_rows(const bcg_rows_args* a, void* stream) {
         return fail(BCG_EINVAL, "%s: mask_per_sample must be 0 or 1", who);
     if (a->cache_hint != BCG_CACHE_KEEP && a->cache_hint != BCG_CACHE_STREAM)
         return fail(BCG_EINVAL, "%s: unknown cache_hint %d", who, a->cache_hint);
-    if (a->n_active == 0) return BCG_OK;
+    L.launch = a->n_active > 0;
+    L.dtype = a->dtype;
+    if (!L.launch) return BCG_OK;
     if (!a->x || !a->x_out || !a->pred || !a->sigmas || !a->order || !a->step_idx || !a->scale ||
         !a->uncond_row || !a->cond_row)
         return fail(BCG_EINVAL, "%s: NULL device pointer", who);
@@ -540,7 +555,9 @@ extern "C" int guided_step_rows(const bcg_rows_args* a, void* stream) {
     const bool vec = HW % VV == 0 && aligned16(a->x) && aligned16(a->x_out) && aligned16(a->pred) &&
                      (!inpaint || (aligned16(a->x_orig) && aligned16(a->mask))) && (!heun || aligned16(a->d)) &&
                      (a->phase != BCG_PHASE_HEUN_CORRECT || aligned16(a->x_tilde));
-    RowsParams p{};
+    RowsParams& p = L.p;
+    p = RowsParams{};
+    p.plan_block = -1;
     p.n = a->n; p.C = a->C; p.n_active = a->n_active; p.num_sigmas = a->num_sigmas; p.rows = a->rows;
     p.phase = a->phase;
     p.HW = HW;
@@ -555,12 +572,74 @@ extern "C" int guided_step_rows(const bcg_rows_args* a, void* stream) {
     const LaunchShape shape = pick_shape(p.n_active, p.nvec);
     p.vpt = shape.vpt;
     p.tiles = (int)(((int64_t)p.nvec + (int64_t)shape.block * p.vpt - 1) / ((int64_t)shape.block * p.vpt));
-    if ((int64_t)p.n_active * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
-    const bool nt = a->cache_hint == BCG_CACHE_STREAM;
+    if ((int64_t)p.n_active * p.tiles >= INT32_MAX - 1) return fail(BCG_ESHAPE, "%s: grid too large", who);
+    L.vec = vec;
+    L.inpaint = inpaint;
+    L.nt = a->cache_hint == BCG_CACHE_STREAM;
+    L.block = shape.block;
+    return BCG_OK;
+}
+
+static int rows_launch(const RowsLaunch& L, void* stream, const char* who) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = a->dtype == BCG_BF16 ? launch_rows_bf16(p, vec, inpaint, nt, shape.block, st)
-                                              : launch_rows_f32(p, vec, inpaint, nt, shape.block, st);
-    return hip_status(e, "guided_step_rows: launch");
+    const hipError_t e = L.dtype == BCG_BF16 ? launch_rows_bf16(L.p, L.vec, L.inpaint, L.nt, L.block, st)
+                                             : launch_rows_f32(L.p, L.vec, L.inpaint, L.nt, L.block, st);
+    return hip_status(e, who);
+}
+
+extern "C" int guided_step_rows(const bcg_rows_args* a, void* stream) {
+    bcg::clear_error();
+    RowsLaunch L;
+    const int rc = rows_prepare(a, "guided_step_rows", L);
+    if (rc || !L.launch) return rc;
+    return rows_launch(L, stream, "guided_step_rows: launch");
+}
+
+extern "C" int guided_step_rows_dplan(const bcg_rows_args* a, const bcg_device_plan* d, void* stream) {
+    bcg::clear_error();
+    const char* who = "guided_step_rows_dplan";
+    RowsLaunch L;
+    int rc = rows_prepare(a, who, L);
+    if (rc) return rc;
+    const int n = a->n;
+    rc = check_dplan(d, n, false, who);
+    if (rc) return rc;
+    if (n == 0) return BCG_OK;
+    // The plan's workgroup runs alongside the update: nothing it writes may
+    // be read or written by the update, nor may it read the update's outputs.
+    const size_t es = elem_size(a->dtype);
+    const size_t xbytes = (size_t)a->n * a->C * a->H * a->W * es;
+    const size_t dbytes = a->d ? (size_t)a->n * a->C * a->H * a->W * 4 : 0;
+    const size_t in4 = (size_t)n * 4, nb4 = (size_t)(d->num_buckets + 1) * 4;
+    struct Span {
+        const void* p;
+        size_t bytes;
+    };
+    const Span writes[] = {{d->bucket_id, in4},    {d->scale, in4},         {d->uncond_row, in4},
+                           {d->cond_row, in4},     {d->order, in4},         {d->bucket_count, nb4},
+                           {d->bucket_offset, nb4}, {d->uncond_offset, nb4}, {d->totals, 8},
+                           {d->step_out, in4},     {d->record_out, in4 * 4}};
+    const Span upd_reads[] = {{a->order, (size_t)a->n_active * 4}, {a->step_idx, in4}, {a->scale, in4},
+                              {a->uncond_row, in4}, {a->cond_row, in4}, {a->sigmas, (size_t)a->num_sigmas * 4},
+                              {a->x_out, xbytes}, {a->d, dbytes}};
+    for (const Span& w : writes)
+        for (const Span& r : upd_reads)
+            if (w.p && r.p && r.bytes && any_overlap(w.p, w.bytes, r.p, r.bytes))
+                return fail(BCG_EINVAL, "%s: the plan's outputs overlap arrays of the update", who);
+    const Span plan_reads[] = {{d->step_in, in4}, {d->bucket_cfg, nb4}, {d->cfg_override, d->cfg_override ? in4 : 0},
+                               {d->covered, d->covered ? in4 : 0}};
+    for (const Span& r : plan_reads)
+        if (r.p && r.bytes && (any_overlap(r.p, r.bytes, a->x_out, xbytes) ||
+                               (dbytes && any_overlap(r.p, r.bytes, a->d, dbytes))))
+            return fail(BCG_EINVAL, "%s: the plan's inputs overlap the update's outputs", who);
+    if (!L.launch) {  // nothing to update: the plan alone
+        const StepParams p = plan_only_params(n, d);
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+        return hip_status(hipGetLastError(), "guided_step_rows_dplan: launch");
+    }
+    L.p.plan = plan_only_params(n, d);
+    L.p.plan_block = (int)((int64_t)L.p.n_active * L.p.tiles);
+    return rows_launch(L, stream, "guided_step_rows_dplan: launch");
 }
 
 extern "C" int latent_init(int n, int C, int H, int W, int dtype, const float* noise, const void* latent,

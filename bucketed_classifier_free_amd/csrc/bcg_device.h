@@ -208,6 +208,11 @@ struct RowsParams {
     const int32_t* cond_row;
     const void* x_orig;
     const float* mask;
+    // Workgroup plan_block (if >= 0), the last of the grid, builds the device
+    // plan `plan` describes (another step's, typically the next) alongside the
+    // update, as a one-workgroup plan launch would.
+    int plan_block;
+    StepParams plan;
 };
 
 // Launchers of the materialised-branch step (bcg_rows_*.hip).

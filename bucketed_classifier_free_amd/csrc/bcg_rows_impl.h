@@ -15,10 +15,13 @@
 // 16-byte vectors, lanes take vpt vectors blockDim apart and walk the channel
 // planes (from a start channel rotated per workgroup) with the next channel's
 // loads in flight; per-sample modes (scale 1,
-// last step) are uniform branches outside the channel loop.
+// last step) are uniform branches outside the channel loop.  With a device
+// plan to build (guided_step_rows_dplan), one extra workgroup, the last of the
+// grid, builds it while the others stream.
 #pragma once
 
 #include "bcg_device.h"
+#include "bcg_plan_dev.h"
 
 namespace bcg {
 
@@ -174,6 +177,12 @@ __device__ __forceinline__ void rows_sample(const RowsParams& p, const RowsScala
 
 template <typename T, int V, int PHASE, bool INP, bool NT>
 __global__ __launch_bounds__(256) void rows_kernel(const RowsParams p) {
+    if ((int)blockIdx.x == p.plan_block) {
+        constexpr int kInts = 4 * BCG_MAX_DEVICE_BUCKETS;
+        __shared__ int sh[kInts];
+        plan_workgroup(p.plan, sh, kInts);
+        return;
+    }
     const int j = blockIdx.x / p.tiles;
     const int tile = blockIdx.x - j * p.tiles;
     if (j >= p.n_active) return;
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const RowsParams p) {
 
 template <typename T, int V, bool INP, bool NT>
 hipError_t launch_rows_v(const RowsParams& p, int block, hipStream_t st) {
-    const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles)), blk((unsigned)block);
+    const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0))), blk((unsigned)block);
     switch (p.phase) {
         case BCG_PHASE_EULER: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_EULER, INP, NT>), grid, blk, 0, st, p); break;
         case BCG_PHASE_HEUN_PREDICT: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_HEUN_PREDICT, INP, NT>), grid, blk, 0, st, p); break;

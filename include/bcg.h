@@ -456,6 +456,25 @@ typedef struct {
 int guided_step_rows(const bcg_rows_args* args, void* stream);
 
 /*
+ * guided_step_rows_dplan -- guided_step_rows, and in the same launch the
+ * device plan `plan` describes for the same n samples, exactly as
+ * bcg_plan_device(args->n, plan) builds it (one extra workgroup of the launch
+ * builds it while the others update).  With a model in the loop the plan of
+ * step k+1 is due before the model's step-(k+1) forward, which comes after
+ * the update of step k: building it in that update's launch ([B] section 3's
+ * per-step BucketPlan, here on the device; [S] "calc_cond_batch()" batches the
+ * model's rows by that plan) takes its own launch off the step.
+ * The two run concurrently, so the plan's outputs (plan table, step_out,
+ * record_out) must overlap neither the update's plan arrays (order, step_idx,
+ * scale, uncond_row, cond_row), its sigmas, nor x_out or d, and the plan's
+ * step_in and tables must not overlap x_out or d; both are checked before the
+ * launch.  With n_active == 0 only the plan is built.
+ * Errors: as guided_step_rows and bcg_plan_device; BCG_EINVAL for the
+ * overlaps above.
+ */
+int guided_step_rows_dplan(const bcg_rows_args* args, const bcg_device_plan* plan, void* stream);
+
+/*
  * latent_init -- [S] "deterministic noise", "disable_noise": the sampler
  * starts from the latent plus noise at the sample's first sigma,
  *   x_out[i] = latent[i] + noise[i] * sigmas[step_idx[i]]   (fp32, rounded on store)

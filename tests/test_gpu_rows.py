@@ -201,3 +201,53 @@ def test_rows_large_shape_sampled():
         s0, s1 = case.sig[case.t[i]], case.sig[case.t[i] + 1]
         ref = M._store(M.rows_euler32(case.x[i], case.pb32(case.pred, i), s0, s1), "bf16")
         assert np.array_equal(got[k], ref), i
+
+
+@pytest.mark.parametrize("kw", [dict(dtype="f32"), dict(dtype="bf16", inpaint=True),
+                                dict(dtype="bf16", n=40, C=4, H=32, W=32)])
+def test_rows_dplan_equals_plan_then_update(kw):
+    """guided_step_rows_dplan = bcg_plan_device (the next step's plan) followed by
+    guided_step_rows: the update and every plan output bit for bit."""
+    from bucketed_classifier_free_amd import api
+    case = Case(**kw).device()
+    n = case.n
+    table = torch.from_numpy(api.bucket_table("linear", 2.0, 1.0, 0.0, 3)).cuda()
+    rng = np.random.default_rng(11)
+    t_next = _i32(rng.integers(-1, case.steps + 1, n))          # some inactive, some past the end
+    ov = torch.from_numpy(np.where(rng.random(n) < 0.3, np.float32(1.0), np.float32(np.nan))).cuda()
+    cov = _i32(rng.random(n) < 0.7)
+
+    def plan_into():
+        out = api.device_plan_arrays(n, 3)
+        for v in out.values():
+            v.fill_(-7)
+        so = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        return out, so
+
+    opt = dict(x_orig=None if case.xo is None else _dev(case.xo, case.dtype),
+               mask=None if case.mask is None else _dev(case.mask))
+    rows = _dev(case.pred, case.dtype)
+    x = _dev(case.x, case.dtype)
+
+    ref_plan, ref_so = plan_into()
+    api.bcg_plan_device(case.steps, table, t_next, step_out=ref_so, cfg_override=ov, covered=cov,
+                        wrap=True, out=ref_plan)
+    ref = x.clone()
+    api.guided_step_rows(x, ref, rows, case.d_sig, n_active=case.plan.n_active, phase="euler",
+                         **case.d_plan, **opt)
+
+    got_plan, got_so = plan_into()
+    pl = api.device_plan(case.steps, table, t_next, step_out=got_so, cfg_override=ov, covered=cov,
+                         wrap=True, out=got_plan)
+    got = x.clone()
+    api.guided_step_rows_dplan(x, got, rows, case.d_sig, n_active=case.plan.n_active, plan=pl,
+                               phase="euler", **case.d_plan, **opt)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16 if case.dtype == "bf16" else torch.int32),
+                       ref.view(torch.int16 if case.dtype == "bf16" else torch.int32))
+    assert torch.equal(got_so, ref_so)
+    for k in ref_plan:
+        g, r = got_plan[k], ref_plan[k]
+        if g.dtype == torch.float32:
+            g, r = g.view(torch.int32), r.view(torch.int32)
+        assert torch.equal(g, r), k

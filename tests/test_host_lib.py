@@ -28,12 +28,12 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == L.ABI_VERSION == 7
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 8
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -307,6 +307,39 @@ def test_rows_entry_point_validates_before_launch():
     assert lib.guided_step_rows(C.byref(a), None) == L.BCG_EDTYPE
     a.dtype, a.n_active = 0, 0                                          # nothing to do, no launch
     assert lib.guided_step_rows(C.byref(a), None) == L.BCG_OK
+
+
+def test_rows_dplan_entry_point_validates_before_launch():
+    lib = L.lib()
+    a = L.RowsArgs()
+    a.n, a.C, a.H, a.W, a.num_sigmas, a.rows, a.n_active = 2, 4, 8, 8, 11, 4, 2
+    a.phase = L.BCG_PHASE["euler"]
+    for f, k in (("x", 1), ("x_out", 2), ("pred", 3), ("sigmas", 4), ("order", 5), ("step_idx", 6),
+                 ("scale", 7), ("uncond_row", 8), ("cond_row", 9)):
+        setattr(a, f, _fake(k))
+    assert lib.guided_step_rows_dplan(C.byref(a), None, None) == L.BCG_EINVAL   # no plan
+    d = L.DevicePlan(10, 2, 1, _fake(20))
+    d.step_in = _fake(21)
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL  # nothing to write
+    d.step_out = _fake(7)                                              # the update's scale
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlap" in lib.bcg_last_error()
+    d.step_out = _fake(22)
+    d.record_out, d.sigmas, d.num_sigmas = _fake(5).value + 4, _fake(23), 11   # into the order
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    d.record_out = None
+    d.step_in = _fake(2).value + 64                                    # reads x_out as it is written
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlap" in lib.bcg_last_error()
+    d.step_in = _fake(21)
+    a.phase = 7                                                        # the update's own checks
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    a.phase = L.BCG_PHASE["euler"]
+    d.steps = 0                                                        # the plan's own checks
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    d.steps = 10
+    a.n, a.n_active = 0, 0                                             # no samples, no launch
+    assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_OK
 
 
 def test_sigma_crop_bit_exact_and_errors():
