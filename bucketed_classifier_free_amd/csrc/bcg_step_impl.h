@@ -18,10 +18,10 @@
 //   * each lane owns V consecutive pixels (16 bytes of storage) and computes
 //     their region weights, coverage, mask and normalisers once, then walks
 //     the C channels (stride H*W);
-//   * the first U channels are requested before the coefficient set-up (the
-//     LDS barrier waits on LDS traffic only), and the channel walk is
-//     software-pipelined: the loads of channels c+U.. are in flight while
-//     channels c.. are computed and stored;
+//   * the first two stages (2U channels) are requested before the pixel and
+//     coefficient set-up (the LDS barrier waits on LDS traffic only), and the
+//     channel walk is software-pipelined: the loads of channels c+U.. are in
+//     flight while channels c.. are computed and stored;
 //   * every element is read once and written once (in place allowed);
 //   * per-sample modes (scale == 1, last step, sample without regions) are
 //     uniform branches taken outside the channel loop.
@@ -184,7 +184,8 @@ __device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg,
 }
 
 // The channel walk, two stages in flight (ping-pong): stage `a` arrives
-// holding channels [0, U) already requested.  When the lane has a next pass
+// holding channels [0, U) already requested, and stage `b` channels [U, 2U)
+// when b_ready.  When the lane has a next pass
 // (nxs != nullptr), its head stage is requested into whichever buffer frees up
 // during this pass's last stage, so the walk does not drain between passes;
 // the return value says where it went (true: `b`, false: `a`).
@@ -192,10 +193,13 @@ template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, 
 __device__ __forceinline__ bool channel_loop(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b,
                                              const LaneState<V, NR>& L, const StepScalars& s,
                                              const float* __restrict__ coef, const T* xs, T* xd, const T* xo,
-                                             const T* nxs, const T* nxo, int rot, int C, int64_t HW) {
+                                             const T* nxs, const T* nxo, int rot, int C, int64_t HW,
+                                             bool b_ready) {
     constexpr int U = TN::U;
     for (int c0 = 0;; c0 += 2 * U) {
-        if (c0 + U < C) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, rot, C, HW);
+        if (c0 + U < C) {
+            if (c0 > 0 || !b_ready) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, rot, C, HW);
+        }
         else if (nxs) load_stage<T, V, TN, INP>(b, nxs, nxo, 0, rot, C, HW);
         compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, rot, C, HW);
         if (c0 + U >= C) return true;
@@ -288,13 +292,12 @@ __device__ __forceinline__ void setup_lane(LaneState<V, NR>& L, const SampleRegi
 
 // A lane's vectors vi0, vi0 + blockDim, ... (p.vpt of them) of one sample.
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
-__device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V, NR>& L,
-                                         const SampleRegions<NR>& sr, const StepParams& p,
-                                         const StepScalars& s, const float* __restrict__ coef, int i,
-                                         int vi0, int rot, bool keep_u) {
+__device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b,
+                                         LaneState<V, NR>& L, const SampleRegions<NR>& sr,
+                                         const StepParams& p, const StepScalars& s,
+                                         const float* __restrict__ coef, int i, int vi0, int rot, bool keep_u) {
     const int C = p.C;
     const int64_t sbase = (int64_t)i * C * p.HW;
-    Stage<T, V, TN::U, INP> b;
     for (int v = 0; v < p.vpt; ++v) {
         const int vi = vi0 + v * (int)blockDim.x;
         if (vi >= p.nvec) return;
@@ -313,17 +316,17 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, LaneState<V
             setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
         }
         const bool in_b = channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, b, L, s, coef, xs, xd, xo,
-                                                                                  nxs, nxo, rot, C, p.HW);
+                                                                                  nxs, nxo, rot, C, p.HW, v == 0);
         if (more && in_b) a = b;
     }
 }
 
-// After the head stage is requested: the first pass's pixel set-up (it
-// overlaps the latent loads), then the branch offsets into this wavefront's
+// After the first two stages are requested: the first pass's pixel set-up
+// (it overlaps the latent loads), then the branch offsets into this wavefront's
 // own LDS slice (lane k computes channel k's; no workgroup barrier), then the
 // channel walks.
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN>
-__device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, bool lane_ok,
+__device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b, bool lane_ok,
                                            const SampleRegions<NR>& sr, const StepParams& p,
                                            StepScalars s, float* coef, int i, int vi0, int rot, bool keep_u,
                                            float sig, float sgn, float mu_u, float mu_c,
@@ -367,11 +370,11 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, bool lane
     const bool one = (s.w == 1.0f);
     const bool fin = (sgn == 0.0f);
     if (one) {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
     } else {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
     }
 }
 
@@ -404,8 +407,8 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
     const bool lane_ok = vi0 < p.nvec;
 
-    // Channel k's means (lane k), the region tables and the head stage of the
-    // latent, all requested before anything waits: every region slot below NR
+    // Channel k's means (lane k), the region tables and the first two stages
+    // of the latent's walk, all requested before anything waits: every region slot below NR
     // is read (the slot index clamped to the table's R), and the sample's
     // count only selects among them afterwards.
     const int k = (int)threadIdx.x & 63;
@@ -431,11 +434,13 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     // workgroups in flight spread their requests over the channel planes
     // instead of all reading one plane's rows at a time.
     const int rot = (int)((5u * blockIdx.x) % (unsigned)C);
-    Stage<T, V, TN::U, INP> a;
+    Stage<T, V, TN::U, INP> a, b;
     if (lane_ok) {
         const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
-        load_stage<T, V, TN, INP>(a, static_cast<const T*>(p.x) + base,
-                                  INP ? static_cast<const T*>(p.x_orig) + base : nullptr, 0, rot, C, p.HW);
+        const T* xs0 = static_cast<const T*>(p.x) + base;
+        const T* xo0 = INP ? static_cast<const T*>(p.x_orig) + base : nullptr;
+        load_stage<T, V, TN, INP>(a, xs0, xo0, 0, rot, C, p.HW);
+        if (TN::U < C) load_stage<T, V, TN, INP>(b, xs0, xo0, TN::U, rot, C, p.HW);
     }
     if constexpr (NR > 0) {
         cnt = cnt < 0 ? 0 : cnt;
@@ -492,9 +497,9 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         }
     }
     if (NR > 0 && cnt > 0)
-        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
+        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, b, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
     else
-        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
+        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, b, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
 }
 
 // Pipeline shape of a kernel variant: channels per stage (4 puts more latent
