@@ -430,10 +430,13 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
             mu_r[r] = p.mu_region[slot * C + kk];
         }
     }
-    // The workgroup's channel walk starts at channel 5*blockIdx mod C, so the
+    // The workgroup's channel walk starts at channel 7*blockIdx mod C, so the
     // workgroups in flight spread their requests over the channel planes
-    // instead of all reading one plane's rows at a time.
-    const int rot = (int)((5u * blockIdx.x) % (unsigned)C);
+    // instead of all reading one plane's rows at a time.  (Workgroup b runs on
+    // XCD b mod 8; the multiplier sets which planes the XCDs stream together:
+    // on the 16-channel large workload 7 and 9 measured fastest, 5 and 3 0.6 us
+    // slower per launch, 1 and 15 1.2-2.5 us slower.)
+    const int rot = (int)((7u * blockIdx.x) % (unsigned)C);
     Stage<T, V, TN::U, INP> a, b;
     if (lane_ok) {
         const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
