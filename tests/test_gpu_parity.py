@@ -221,13 +221,19 @@ def test_streaming_cache_hint_is_bit_identical(kw):
 
 # The streaming (nontemporal) variants take their pipeline shape from the
 # channel count: 2 channels per stage without prefetch up to 4 channels, the
-# per-variant stage table beyond.  Every variant at each shape: bit for bit
-# equal to the cache-keep variant on every sample, and to mode M on two.
+# per-variant stage table beyond, and its full-stage form (no per-channel
+# bounds checks) when C is a multiple of two stages.  Every variant at each
+# shape: bit for bit equal to the cache-keep variant on every sample, and to
+# mode M on two.  (Lanes take one vector each here: several vectors per lane,
+# with the next one's head stage prefetched, only come with grids beyond 2^22
+# workgroups, which no test here reaches.)
 STREAM_SHAPES = [
-    (4, 16, 16, 32),   # the stage table's shape, one pass per lane
+    (4, 16, 16, 32),   # the stage table's shape, full stages
     (3, 5, 16, 24),    # width-4 variants fall back; width 2 ends on a 1-channel stage
     (3, 9, 13, 21),    # H*W odd (scalar path); width 4 ends on a 1-channel stage
-    (800, 8, 64, 64),  # several passes per lane: the next pass's head stage is prefetched
+    (5, 12, 16, 24),   # width 4 with bounds checks: the last stage pair is half full
+    (6, 24, 8, 16),    # full stages, three stage pairs
+    (800, 8, 64, 64),  # full stages, a grid of 1,600 workgroups
 ]
 
 
