@@ -175,12 +175,55 @@ __device__ __forceinline__ void rows_sample(const RowsParams& p, const RowsScala
     }
 }
 
+constexpr int kRowsPlanInts = 4 * BCG_MAX_DEVICE_BUCKETS;  // the plan workgroup's LDS
+
+// Dynamic LDS of a rows launch of `blocks` workgroups of `block` lanes: the
+// plan workgroup's counters when there is one, and, for the streaming
+// (nontemporal) variants when the grid is at least two rounds at 3 waves per
+// SIMD, an allocation that lets a CU hold no more workgroups than 3 waves per
+// SIMD (12 per CU) need.  With the 59-109 VGPRs
+// of these variants a CU would otherwise hold up to 8 waves per SIMD, and the
+// large shape's grid would be one resident round that ends on the waves that
+// lose arbitration: 94.7 us per step at 3 waves per SIMD against 96.7 at 8.
+// (The in-place batch, ordinary loads and partly cache-resident, measured
+// 93.0 us at 8 and 94.8 at 3: the cache-keep variants are not capped.)
+inline hipError_t rows_lds_bytes(int64_t blocks, int block, bool plan, bool nt, size_t& bytes) {
+    bytes = plan ? kRowsPlanInts * sizeof(int) : 0;
+    const int waves_per_wg = (block + 63) / 64;
+    const int wg_per_cu = 12 / waves_per_wg > 0 ? 12 / waves_per_wg : 1;
+    // CUs and LDS per CU of the current device, looked up once per device
+    // (concurrent first lookups store the same values)
+    constexpr int kDevices = 64;
+    static int cus_of[kDevices], lds_of[kDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cus = dev < kDevices ? cus_of[dev] : 0, lds_cu = dev < kDevices ? lds_of[dev] : 0;
+    if (cus == 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+        if (e != hipSuccess) return e;
+        if (dev < kDevices) {
+            lds_of[dev] = lds_cu;
+            cus_of[dev] = cus;
+        }
+    }
+    if (nt && blocks >= (int64_t)2 * wg_per_cu * cus && lds_cu > 0) {
+        // the largest allocation (in 1 KiB units) of which wg_per_cu fit and one more does not
+        const size_t cap = (size_t)(lds_cu / (wg_per_cu + 1) / 1024 + 1) * 1024;
+        if (cap * wg_per_cu <= (size_t)lds_cu && cap > bytes) bytes = cap;
+    }
+    return hipSuccess;
+}
+
 template <typename T, int V, int PHASE, bool INP, bool NT>
 __global__ __launch_bounds__(256) void rows_kernel(const RowsParams p) {
+    // Dynamic LDS: the plan workgroup's counters, and for large grids the
+    // allocation that holds a CU to 3 waves per SIMD (rows_lds_bytes).
+    extern __shared__ int rows_lds[];
     if ((int)blockIdx.x == p.plan_block) {
-        constexpr int kInts = 4 * BCG_MAX_DEVICE_BUCKETS;
-        __shared__ int sh[kInts];
-        plan_workgroup(p.plan, sh, kInts);
+        plan_workgroup(p.plan, rows_lds, kRowsPlanInts);
         return;
     }
     const int j = blockIdx.x / p.tiles;
@@ -221,11 +264,15 @@ __global__ __launch_bounds__(256) void rows_kernel(const RowsParams p) {
 
 template <typename T, int V, bool INP, bool NT>
 hipError_t launch_rows_v(const RowsParams& p, int block, hipStream_t st) {
-    const dim3 grid((unsigned)((int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0))), blk((unsigned)block);
+    const int64_t blocks = (int64_t)p.n_active * p.tiles + (p.plan_block >= 0 ? 1 : 0);
+    const dim3 grid((unsigned)blocks), blk((unsigned)block);
+    size_t lds = 0;
+    const hipError_t e = rows_lds_bytes(blocks, block, p.plan_block >= 0, NT, lds);
+    if (e != hipSuccess) return e;
     switch (p.phase) {
-        case BCG_PHASE_EULER: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_EULER, INP, NT>), grid, blk, 0, st, p); break;
-        case BCG_PHASE_HEUN_PREDICT: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_HEUN_PREDICT, INP, NT>), grid, blk, 0, st, p); break;
-        default: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_HEUN_CORRECT, INP, NT>), grid, blk, 0, st, p); break;
+        case BCG_PHASE_EULER: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_EULER, INP, NT>), grid, blk, lds, st, p); break;
+        case BCG_PHASE_HEUN_PREDICT: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_HEUN_PREDICT, INP, NT>), grid, blk, lds, st, p); break;
+        default: hipLaunchKernelGGL((rows_kernel<T, V, BCG_PHASE_HEUN_CORRECT, INP, NT>), grid, blk, lds, st, p); break;
     }
     return hipGetLastError();
 }
