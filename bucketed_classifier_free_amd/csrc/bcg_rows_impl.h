@@ -20,6 +20,7 @@
 // grid, builds it while the others stream.
 #pragma once
 
+#include <atomic>
 #include "bcg_device.h"
 #include "bcg_plan_dev.h"
 
@@ -192,21 +193,22 @@ inline hipError_t rows_lds_bytes(int64_t blocks, int block, bool plan, bool nt, 
     const int waves_per_wg = (block + 63) / 64;
     const int wg_per_cu = 12 / waves_per_wg > 0 ? 12 / waves_per_wg : 1;
     // CUs and LDS per CU of the current device, looked up once per device
-    // (concurrent first lookups store the same values)
+    // (concurrent first lookups store the same values; LDS is published first)
     constexpr int kDevices = 64;
-    static int cus_of[kDevices], lds_of[kDevices];
+    static std::atomic<int> cus_of[kDevices], lds_of[kDevices];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int cus = dev < kDevices ? cus_of[dev] : 0, lds_cu = dev < kDevices ? lds_of[dev] : 0;
+    int cus = dev >= 0 && dev < kDevices ? cus_of[dev].load(std::memory_order_acquire) : 0;
+    int lds_cu = cus > 0 ? lds_of[dev].load(std::memory_order_relaxed) : 0;
     if (cus == 0) {
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
         if (e != hipSuccess) return e;
-        if (dev < kDevices) {
-            lds_of[dev] = lds_cu;
-            cus_of[dev] = cus;
+        if (dev >= 0 && dev < kDevices) {
+            lds_of[dev].store(lds_cu, std::memory_order_relaxed);
+            cus_of[dev].store(cus, std::memory_order_release);
         }
     }
     if (nt && blocks >= (int64_t)2 * wg_per_cu * cus && lds_cu > 0) {
