@@ -204,11 +204,17 @@ def test_rows_large_shape_sampled():
 
 
 @pytest.mark.parametrize("kw", [dict(dtype="f32"), dict(dtype="bf16", inpaint=True),
-                                dict(dtype="bf16", n=40, C=4, H=32, W=32)])
+                                dict(dtype="bf16", n=40, C=4, H=32, W=32),
+                                dict(dtype="bf16", n=256, C=16, H=128, W=128, steps=50, hint=1)])
 def test_rows_dplan_equals_plan_then_update(kw):
     """guided_step_rows_dplan = bcg_plan_device (the next step's plan) followed by
-    guided_step_rows: the update and every plan output bit for bit."""
+    guided_step_rows: the update and every plan output bit for bit.  The last
+    case is the large workload's shape with the streaming hint: a grid of
+    several resident rounds, whose launch sizes its dynamic LDS to bound the
+    waves per CU, with the plan workgroup in it."""
     from bucketed_classifier_free_amd import api
+    kw = dict(kw)
+    hint = kw.pop("hint", 0)
     case = Case(**kw).device()
     n = case.n
     table = torch.from_numpy(api.bucket_table("linear", 2.0, 1.0, 0.0, 3)).cuda()
@@ -234,14 +240,14 @@ def test_rows_dplan_equals_plan_then_update(kw):
                         wrap=True, out=ref_plan)
     ref = x.clone()
     api.guided_step_rows(x, ref, rows, case.d_sig, n_active=case.plan.n_active, phase="euler",
-                         **case.d_plan, **opt)
+                         cache_hint=hint, **case.d_plan, **opt)
 
     got_plan, got_so = plan_into()
     pl = api.device_plan(case.steps, table, t_next, step_out=got_so, cfg_override=ov, covered=cov,
                          wrap=True, out=got_plan)
     got = x.clone()
     api.guided_step_rows_dplan(x, got, rows, case.d_sig, n_active=case.plan.n_active, plan=pl,
-                               phase="euler", **case.d_plan, **opt)
+                               phase="euler", cache_hint=hint, **case.d_plan, **opt)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16 if case.dtype == "bf16" else torch.int32),
                        ref.view(torch.int16 if case.dtype == "bf16" else torch.int32))
