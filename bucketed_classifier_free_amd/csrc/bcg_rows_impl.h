@@ -160,18 +160,33 @@ __device__ __forceinline__ void rows_sample(const RowsParams& p, const RowsScala
         }
         // walk position c is channel (c + rot) mod C
         auto plane = [&](int c) { return (int64_t)(c + rot >= C ? c + rot - C : c + rot) * HW; };
-        RowsStage<T, V, M> a, b;
+        // a ring of three single-channel stages: two channels' loads in
+        // flight while one is computed
+        RowsStage<T, V, M> a, b, d;
         const int64_t o0 = plane(0);
         rows_load<T, V, M, NT>(a, p, xb + o0, cb + o0, ub + o0);
-        for (int c0 = 0;; c0 += 2) {
+        if (1 < C) {
+            const int64_t o1 = plane(1);
+            rows_load<T, V, M, NT>(b, p, xb + o1, cb + o1, ub + o1);
+        }
+        for (int c0 = 0;; c0 += 3) {
             const int64_t oa = plane(c0);
-            const int64_t o1 = c0 + 1 < C ? plane(c0 + 1) : 0, o2 = c0 + 2 < C ? plane(c0 + 2) : 0;
-            if (c0 + 1 < C) rows_load<T, V, M, NT>(b, p, xb + o1, cb + o1, ub + o1);
+            const int64_t ob = c0 + 1 < C ? plane(c0 + 1) : 0, od = c0 + 2 < C ? plane(c0 + 2) : 0;
+            if (c0 + 2 < C) rows_load<T, V, M, NT>(d, p, xb + od, cb + od, ub + od);
             rows_compute<T, V, PHASE, M, NT>(a, p, s, m, om, xb + oa);
             if (c0 + 1 >= C) break;
-            if (c0 + 2 < C) rows_load<T, V, M, NT>(a, p, xb + o2, cb + o2, ub + o2);
-            rows_compute<T, V, PHASE, M, NT>(b, p, s, m, om, xb + o1);
+            if (c0 + 3 < C) {
+                const int64_t on = plane(c0 + 3);
+                rows_load<T, V, M, NT>(a, p, xb + on, cb + on, ub + on);
+            }
+            rows_compute<T, V, PHASE, M, NT>(b, p, s, m, om, xb + ob);
             if (c0 + 2 >= C) break;
+            if (c0 + 4 < C) {
+                const int64_t on = plane(c0 + 4);
+                rows_load<T, V, M, NT>(b, p, xb + on, cb + on, ub + on);
+            }
+            rows_compute<T, V, PHASE, M, NT>(d, p, s, m, om, xb + od);
+            if (c0 + 3 >= C) break;
         }
     }
 }
