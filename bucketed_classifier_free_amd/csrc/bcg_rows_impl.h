@@ -160,33 +160,32 @@ __device__ __forceinline__ void rows_sample(const RowsParams& p, const RowsScala
         }
         // walk position c is channel (c + rot) mod C
         auto plane = [&](int c) { return (int64_t)(c + rot >= C ? c + rot - C : c + rot) * HW; };
-        // a ring of three single-channel stages: two channels' loads in
-        // flight while one is computed
-        RowsStage<T, V, M> a, b, d;
-        const int64_t o0 = plane(0);
-        rows_load<T, V, M, NT>(a, p, xb + o0, cb + o0, ub + o0);
-        if (1 < C) {
-            const int64_t o1 = plane(1);
-            rows_load<T, V, M, NT>(b, p, xb + o1, cb + o1, ub + o1);
+        // a ring of K single-channel stages: K - 1 channels' loads in flight
+        // while one is computed (channel c lives in slot c mod K)
+        constexpr int K = 4;
+        RowsStage<T, V, M> st[K];
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) {
+            if (k < C) {
+                const int64_t o = plane(k);
+                rows_load<T, V, M, NT>(st[k], p, xb + o, cb + o, ub + o);
+            }
         }
-        for (int c0 = 0;; c0 += 3) {
-            const int64_t oa = plane(c0);
-            const int64_t ob = c0 + 1 < C ? plane(c0 + 1) : 0, od = c0 + 2 < C ? plane(c0 + 2) : 0;
-            if (c0 + 2 < C) rows_load<T, V, M, NT>(d, p, xb + od, cb + od, ub + od);
-            rows_compute<T, V, PHASE, M, NT>(a, p, s, m, om, xb + oa);
-            if (c0 + 1 >= C) break;
-            if (c0 + 3 < C) {
-                const int64_t on = plane(c0 + 3);
-                rows_load<T, V, M, NT>(a, p, xb + on, cb + on, ub + on);
+        bool done = false;
+        for (int c0 = 0; !done; c0 += K) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int c = c0 + k;
+                if (c + K - 1 < C) {  // into the slot of channel c - 1, already computed
+                    const int64_t o = plane(c + K - 1);
+                    rows_load<T, V, M, NT>(st[(k + K - 1) % K], p, xb + o, cb + o, ub + o);
+                }
+                rows_compute<T, V, PHASE, M, NT>(st[k], p, s, m, om, xb + plane(c));
+                if (c + 1 >= C) {
+                    done = true;
+                    break;
+                }
             }
-            rows_compute<T, V, PHASE, M, NT>(b, p, s, m, om, xb + ob);
-            if (c0 + 2 >= C) break;
-            if (c0 + 4 < C) {
-                const int64_t on = plane(c0 + 4);
-                rows_load<T, V, M, NT>(b, p, xb + on, cb + on, ub + on);
-            }
-            rows_compute<T, V, PHASE, M, NT>(d, p, s, m, om, xb + od);
-            if (c0 + 3 >= C) break;
         }
     }
 }
