@@ -13,7 +13,7 @@
 //                    x' = fma(d + d', hh, x) (x~ copied on a last step).
 // Layout and streaming as the fused inline step: workgroup = sample x tile of
 // 16-byte vectors, lanes take vpt vectors blockDim apart and walk the channel
-// planes (from a start channel rotated per workgroup) with the next two
+// planes (from a start channel rotated per workgroup) with the next three
 // channels' loads in flight; per-sample modes (scale 1,
 // last step) are uniform branches outside the channel loop.  With a device
 // plan to build (guided_step_rows_dplan), one extra workgroup, the last of the
