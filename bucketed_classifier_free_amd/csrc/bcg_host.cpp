@@ -133,15 +133,33 @@ extern "C" int sigma_crop(const float* sigmas, int num_sigmas, int start_step, i
 
 namespace {
 
-// "calc_cond_batch()": area fractions become latent slices.  Round half up,
-// then clamp so the box keeps at least one pixel and stays inside.
+// The integer nearest to the exact product f * n, a tie going to the larger
+// integer.  f is a finite double with |f| <= 1e6 (checked by the caller) and
+// 0 < n < 2^31.  f = M * 2^-k with M the 53-bit integer significand, so
+// f * n = P * 2^-k with P = M * n exact in 128 bits, and the nearest integer
+// with ties upward is floor((P + 2^(k-1)) / 2^k), an arithmetic shift.
+long long nearest_up(double f, int n) {
+    if (f == 0.0) return 0;
+    int e = 0;
+    const double m = std::frexp(f, &e);                 // f = m * 2^e, 0.5 <= |m| < 1
+    const long long M = (long long)std::ldexp(m, 53);   // exact: |M| < 2^53
+    const __int128 P = (__int128)M * n;                 // exact: |P| < 2^84
+    const int k = 53 - e;                               // f * n = P * 2^-k
+    if (k <= 0) return (long long)(P << -k);            // an integer already (|f*n| <= 1e6 * 2^31)
+    if (k > 100) return 0;                              // |f * n| < 2^84 * 2^-101 < 1/2
+    return (long long)((P + ((__int128)1 << (k - 1))) >> k);
+}
+
+// "calc_cond_batch()": area fractions become latent slices.  Each coordinate
+// is the integer nearest to the exact product of its fraction and the extent
+// (ties to the larger integer); the side is clamped so the box keeps at least
+// one pixel and the offset so the box stays inside.
 void area_slice(const double* f, int H, int W, int32_t* box) {
     const double fy = f[0], fx = f[1], fh = f[2], fw = f[3];
-    auto rnd = [](double v) -> long long { return (long long)std::floor(v + 0.5); };
-    long long h = std::min<long long>(std::max<long long>(rnd(fh * H), 1), H);
-    long long w = std::min<long long>(std::max<long long>(rnd(fw * W), 1), W);
-    long long y0 = std::min<long long>(std::max<long long>(rnd(fy * H), 0), H - h);
-    long long x0 = std::min<long long>(std::max<long long>(rnd(fx * W), 0), W - w);
+    long long h = std::min<long long>(std::max<long long>(nearest_up(fh, H), 1), H);
+    long long w = std::min<long long>(std::max<long long>(nearest_up(fw, W), 1), W);
+    long long y0 = std::min<long long>(std::max<long long>(nearest_up(fy, H), 0), H - h);
+    long long x0 = std::min<long long>(std::max<long long>(nearest_up(fx, W), 0), W - w);
     box[0] = int32_t(y0);
     box[1] = int32_t(y0 + h);
     box[2] = int32_t(x0);

@@ -18,13 +18,12 @@ be checked by eye against the pages.  Pages cited:
 
 Readings taken where the pages are silent are stated at each function.  Pins
 (tests/test_oracle_pins.py) tie every function here to closed forms, brute
-force, special cases the pages fix or library routines.  ``area_box`` is the
-one rule with no such pin beyond self-consistency: parity unpinned for the
-rounding of fractional box coordinates.
+force, special cases the pages fix or library routines.
 """
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -214,16 +213,22 @@ def area_box(frac, H: int, W: int):
     """Area fractions (fy, fx, fh, fw) -> half-open latent slice (y0, y1, x0, x1).
 
     "12 · Samplers...", calc_cond_batch(): area percentages are turned into
-    latent slices.  The rounding is not stated.  Reading: side lengths and
-    offsets round half up in float64, the side is clamped to [1, extent] and
-    the offset so that the box stays inside.  Parity unpinned (no example on
-    the pages); pinned only by bounds and self-consistency.
+    latent slices.  The rounding is not stated.  Reading: each coordinate is
+    the integer nearest to the exact product of the float64 fraction and the
+    extent, a tie (an exact half) going to the larger integer; then the side
+    is clamped to [1, extent] and the offset so that the box stays inside.
+    The product is taken exactly (a float64 fraction is a dyadic rational), so
+    the rule does not depend on how a float64 product would round.
     """
-    fy, fx, fh, fw = (float(v) for v in frac)
-    h = min(max(int(math.floor(fh * H + 0.5)), 1), H)
-    w = min(max(int(math.floor(fw * W + 0.5)), 1), W)
-    y0 = min(max(int(math.floor(fy * H + 0.5)), 0), H - h)
-    x0 = min(max(int(math.floor(fx * W + 0.5)), 0), W - w)
+    def nearest_up(f, n):
+        v = Fraction(float(f)) * n
+        return math.floor(v + Fraction(1, 2))
+
+    fy, fx, fh, fw = frac
+    h = min(max(nearest_up(fh, H), 1), H)
+    w = min(max(nearest_up(fw, W), 1), W)
+    y0 = min(max(nearest_up(fy, H), 0), H - h)
+    x0 = min(max(nearest_up(fx, W), 0), W - w)
     return (y0, y0 + h, x0, x0 + w)
 
 

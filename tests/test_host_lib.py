@@ -480,3 +480,24 @@ def test_weight_patch_validates_before_launch():
     a, keep = _weight_args(rows=0, patches=[diff(rows=0, diff=None)])
     a.w = a.out = None
     assert lib.weight_patch(C.byref(a), None) == L.BCG_OK
+
+
+def test_area_slices_round_exact_products_ties_up():
+    # The library's slices at and around every rounding tie of every extent
+    # n <= 256: one sample per fraction f, one region (f, 0, 0, f), so the row
+    # offset and the column side both come from f*n.
+    from area_cases import near_tie_fractions, nearest_by_search
+    for n in range(1, 257):
+        fr = near_tie_fractions(n)
+        k = len(fr)
+        frac = np.zeros((k, 1, 4))
+        frac[:, 0, 0] = fr
+        frac[:, 0, 3] = fr
+        got = bcg.bcg_plan_build(np.zeros(k, np.int32), 1, np.float32([2.0]), C=1, H=n, W=n,
+                                 region_count=np.ones(k, np.int32), region_frac=frac,
+                                 region_strength=np.ones((k, 1), np.float32), max_regions=1)
+        for j, f in enumerate(fr):
+            m = nearest_by_search(f, n)
+            y0 = min(max(m, 0), n - 1)
+            assert tuple(got.region_box[j, 0]) == (y0, y0 + 1, 0, min(max(m, 1), n)), (n, f)
+            assert tuple(got.region_box[j, 0]) == D.area_box(frac[j, 0], n, n)

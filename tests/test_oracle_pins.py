@@ -5,6 +5,7 @@ case the pages fix, or a library routine -- chosen so that a dropped term, a
 wrong sign or index, or a transposed operand fails at least one of them.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -730,3 +731,29 @@ def test_no_valid_region_means_no_guidance():
     for w in (0.0, 1.0, 7.5):
         assert np.array_equal(D.guided_pred(x, 3.0, w, prm), u)
     assert not D.coverage(inp, np.array([0]))[0]  # the uncond branch is then needed
+
+
+def test_area_box_rounds_exact_products_ties_up():
+    # Every tie (k + 1/2)/n of every extent n <= 256, and the float64 values on
+    # either side of it: the offset and the side are the integer nearest to the
+    # exact product, found by search, then clamped.  The other plausible rules
+    # each give a different slice somewhere in this set.
+    from area_cases import near_tie_fractions, nearest_by_search
+    alt = {"floor": lambda f, n: math.floor(f * n),
+           "half_even": lambda f, n: round(Fraction(f) * n),
+           "float64_half_up": lambda f, n: math.floor(f * n + 0.5)}
+    caught = dict.fromkeys(alt, 0)
+    cases = 0
+    for n in range(1, 257):
+        for f in near_tie_fractions(n):
+            m = nearest_by_search(f, n)
+            y0, y1, x0, x1 = D.area_box((f, 0.0, 0.0, f), n, n)
+            assert (y0, y1) == (min(max(m, 0), n - 1), min(max(m, 0), n - 1) + 1), (n, f)
+            assert (x0, x1) == (0, min(max(m, 1), n)), (n, f)
+            cases += 1
+            for name, rule in alt.items():
+                a = rule(f, n)
+                if min(max(a, 0), n - 1) != y0 or min(max(a, 1), n) != x1 - x0:
+                    caught[name] += 1
+    assert cases == 3 * sum(range(1, 257))
+    assert all(v > 0 for v in caught.values()), caught
