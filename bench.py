@@ -34,8 +34,9 @@ if ROOT not in sys.path:
 
 METRIC = "latent element-steps/sec on 1 GPU + achieved HBM GB/s as % of peak"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_plan_dev.h", "bcg_api.hip", "bcg_step_bf16.hip",
-                  "bcg_step_f32.hip", "bcg_step_bf16_nt.hip", "bcg_step_f32_nt.hip"]
+# the bench kernel's device code and its launch shape (a traffic record is
+# void once any of them changes)
+KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_plan_dev.h", "bcg_launch.h", "bcg_step_bf16_nt.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "guided_step_large_bf16_traffic.json")
 
 
@@ -462,7 +463,7 @@ def trajectory(inp, args):
     x = s.alloc_state()
     starts = inp.start_step.astype(np.int64)
     launches = int(spec.steps - starts.min())
-    G = launches - launches % 2  # one graph replay per trajectory (a whole buffer period)
+    G = launches  # one graph replay per trajectory
     loop = s.native_loop(x, device_plan=True, graph_launches=G)
     t = starts[:, None] + np.arange(launches)[None, :]
     elems = int(((t >= 0) & (t < spec.steps)).sum()) * spec.C * spec.H * spec.W
@@ -519,15 +520,12 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--upload-batch", type=int, default=8)
     ap.add_argument("--async-upload", type=int, default=0)
-    ap.add_argument("--timing-every", type=int, default=10,
-                    help="bracket every m-th launch with HIP events (kernel duration); "
-                         "with --graph, every replay is bracketed instead")
     ap.add_argument("--plan", choices=("device", "host"), default="device")
     ap.add_argument("--records", type=int, default=1,
                     help="device plans: each launch's plan writes the next step's sample records")
     ap.add_argument("--graph", type=int, default=40, metavar="G",
-                    help="device plans: replay a captured graph of G launches (a multiple of "
-                         "2 x replicas; 0 = direct launches)")
+                    help="device plans: the timed launches run as replays of a captured graph of "
+                         "min(G, --steps) launches (0 = direct launches)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the traffic record from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
@@ -601,10 +599,11 @@ def main():
     for r in range(R):
         s.init_state(x[r])
     dev_plan = args.plan == "device"
-    G = args.graph - args.graph % (2 * R) if dev_plan else 0  # replays need a whole buffer period
+    # one graph replay covers up to G launches of the timed run
+    G = min(args.graph, args.steps) if dev_plan else 0
     loop = s.native_loop(x if R > 1 else x[0], upload_batch=args.upload_batch,
-                         async_upload=bool(args.async_upload), timing_every=args.timing_every,
-                         device_plan=dev_plan, graph_launches=G, records=bool(args.records))
+                         async_upload=bool(args.async_upload), device_plan=dev_plan,
+                         graph_launches=G, records=bool(args.records))
     loop.run(0, args.warmup)
     torch.cuda.synchronize()
     elems_per_launch = spec.n * spec.C * spec.H * spec.W  # every sample active (steady state)
@@ -612,11 +611,12 @@ def main():
     launch_ms = loop.run(args.warmup, args.steps, timing=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    replayed, direct = loop.last_run()
     if not torch.isfinite(x.float()).all():
         raise RuntimeError("non-finite state after the timed steps")
 
     if not launch_ms > 0:
-        raise RuntimeError("no launch was timed (use --steps >= --timing-every)")
+        raise RuntimeError("no launch was timed (--steps must be >= 1)")
     value = elems_per_launch * args.steps / wall
     bpe = bytes_per_element(spec)
     alg_bytes = bpe * elems_per_launch
@@ -647,9 +647,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "kernel": {"name": "guided_step", "avg_launch_us": launch_ms * 1e3,
-                   "timing": (f"HIP events around each replay of a {G}-launch graph"
-                              if G else
-                              f"HIP events around every {args.timing_every}th launch"),
+                   "timing": (f"one pair of HIP events on the launch stream around all {args.steps} timed "
+                              f"launches ({replayed} inside replays of a {G}-launch graph, {direct} "
+                              f"launched directly); mean per launch, gaps between launches included"),
+                   "launches_replayed": replayed, "launches_direct": direct,
                    "algorithmic_bytes_per_launch": alg_bytes, "bytes_per_element_step": bpe,
                    "element_steps_per_s_kernel_only": elems_per_launch / (launch_ms * 1e-3),
                    "kernel_hash": kernel_hash()},

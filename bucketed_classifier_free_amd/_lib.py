@@ -23,7 +23,7 @@ BCG_MAX_DEVICE_STEPS = 1 << 20
 BCG_MAX_PATCHES = 8
 BCG_PATCH = {"diff": 0, "lowrank": 1}
 BCG_ROUND = {"nearest": 0, "stochastic": 1}
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 # Every symbol the header declares (checked by the CPU test suite).
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
@@ -31,7 +31,7 @@ EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", 
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
            "area_accumulate", "mask_blend", "bcg_plan_records", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
            "guided_step_rows_dplan",
-           "bcg_loop_create", "bcg_loop_run", "bcg_loop_destroy", "weight_patch"]
+           "bcg_loop_create", "bcg_loop_run", "bcg_loop_last_run", "bcg_loop_destroy", "weight_patch"]
 
 vp, i32p, i64p, f32p, f64p = (C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_int64),
                               C.POINTER(C.c_float), C.POINTER(C.c_double))
@@ -65,7 +65,7 @@ class StepArgs(C.Structure):
                 ("region_count", vp), ("region_box", vp), ("region_strength", vp),
                 ("mu_region", vp), ("x_orig", vp), ("mask", vp), ("stats", vp),
                 ("workspace", vp), ("workspace_bytes", C.c_size_t), ("region_range", vp),
-                ("steps", C.c_int32)]
+                ("steps", C.c_int32), ("launch_vpt", C.c_int32)]
 
 
 class RowsArgs(C.Structure):
@@ -74,7 +74,8 @@ class RowsArgs(C.Structure):
                 ("num_sigmas", C.c_int32), ("rows", C.c_int32), ("mask_per_sample", C.c_int32),
                 ("cache_hint", C.c_int32), ("x", vp), ("x_out", vp), ("d", vp), ("x_tilde", vp),
                 ("pred", vp), ("sigmas", vp), ("order", vp), ("step_idx", vp), ("scale", vp),
-                ("uncond_row", vp), ("cond_row", vp), ("x_orig", vp), ("mask", vp)]
+                ("uncond_row", vp), ("cond_row", vp), ("x_orig", vp), ("mask", vp),
+                ("launch_vpt", C.c_int32)]
 
 
 class DevicePlan(C.Structure):
@@ -104,7 +105,7 @@ class LoopDesc(C.Structure):
     _fields_ = [("plan", PlanIn), ("start", vp), ("wrap", C.c_int32), ("rows", C.c_int32),
                 ("host_slab", vp), ("dev_slab", vp), ("replicas", C.c_int32),
                 ("replica_stride", C.c_int64), ("upload_batch", C.c_int32),
-                ("async_upload", C.c_int32), ("timing_every", C.c_int32), ("step", StepArgs),
+                ("async_upload", C.c_int32), ("step", StepArgs),
                 ("device_plan", C.c_int32), ("graph_launches", C.c_int32), ("dev_steps", vp),
                 ("dplan", DevicePlan), ("dev_records", vp)]
 
@@ -142,6 +143,7 @@ def lib():
         L.bcg_loop_create.argtypes = [C.POINTER(LoopDesc), C.POINTER(vp)]
         L.bcg_loop_run.argtypes = [vp, C.c_int, C.c_int, vp, C.POINTER(C.c_float)]
         L.bcg_loop_destroy.argtypes = [vp]
+        L.bcg_loop_last_run.argtypes = [vp, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
         L.weight_patch.argtypes = [C.POINTER(WeightArgs), vp]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or C.c_int

@@ -181,7 +181,7 @@ def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
 
 def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sampler, s2, feather,
                region_count, region_box, region_strength, mu_region, x_orig, mask, stats,
-               workspace, cache_hint, region_range=None, steps=0):
+               workspace, cache_hint, region_range=None, steps=0, launch_vpt=0):
     """Checks the tensors of a guided step and packs them into StepArgs.
     ``plan_rows`` = (order, step_idx, scale, uncond_row) or None (device plan)."""
     _dev(x, "x")
@@ -238,26 +238,28 @@ def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sam
                       _ptr(x), _ptr(x_out), _ptr(sigmas), _ptr(order), _ptr(step_idx), _ptr(scale),
                       _ptr(uncond_row), _ptr(mu_uncond), _ptr(mu_cond), _ptr(region_count),
                       _ptr(region_box), _ptr(region_strength), _ptr(mu_region), _ptr(x_orig),
-                      _ptr(mask), _ptr(stats), _ptr(workspace), wsb, _ptr(region_range), int(steps))
+                      _ptr(mask), _ptr(stats), _ptr(workspace), wsb, _ptr(region_range), int(steps),
+                      int(launch_vpt))
 
 
 def guided_step(x, x_out, sigmas, order, step_idx, scale, uncond_row, mu_uncond, mu_cond, *,
                 n_active: int, sampler: str, s2: float, feather: int = 0,
                 region_count=None, region_box=None, region_strength=None, mu_region=None,
                 x_orig=None, mask=None, stats=None, workspace=None, cache_hint: int = 0,
-                region_range=None, steps: int = 0, stream=None):
-    """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU."""
+                region_range=None, steps: int = 0, launch_vpt: int = 0, stream=None):
+    """One fused guided sampler step (see include/bcg.h).  All tensors on the GPU.
+    ``launch_vpt`` > 0 fixes the pixel vectors per lane of the launch shape."""
     a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, (order, step_idx, scale, uncond_row),
                    n_active=n_active, sampler=sampler, s2=s2, feather=feather,
                    region_count=region_count, region_box=region_box,
                    region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
                    stats=stats, workspace=workspace, cache_hint=cache_hint,
-                   region_range=region_range, steps=steps)
+                   region_range=region_range, steps=steps, launch_vpt=launch_vpt)
     L.check(L.lib().guided_step(ct.byref(a), _stream(stream)))
 
 
 def _rows_args(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
-               n_active, phase, d, x_tilde, x_orig, mask, cache_hint) -> L.RowsArgs:
+               n_active, phase, d, x_tilde, x_orig, mask, cache_hint, launch_vpt=0) -> L.RowsArgs:
     _dev(x, "x")
     if x.dim() != 4 or x.dtype not in _DT:
         raise ValueError("x must be [n, C, H, W] float32 or bfloat16")
@@ -290,20 +292,21 @@ def _rows_args(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_
     a = L.RowsArgs(n, Cc, H, W, _DT[x.dtype], L.BCG_PHASE[phase], int(n_active), sigmas.numel(),
                    pred.shape[0], mps, int(cache_hint), _ptr(x), _ptr(x_out), _ptr(d),
                    _ptr(x_tilde), _ptr(pred), _ptr(sigmas), _ptr(order), _ptr(step_idx),
-                   _ptr(scale), _ptr(uncond_row), _ptr(cond_row), _ptr(x_orig), _ptr(mask))
+                   _ptr(scale), _ptr(uncond_row), _ptr(cond_row), _ptr(x_orig), _ptr(mask),
+                   int(launch_vpt))
     return a
 
 
 def guided_step_rows(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row, *,
                      n_active: int, phase: str = "euler", d=None, x_tilde=None, x_orig=None,
-                     mask=None, cache_hint: int = 0, stream=None):
+                     mask=None, cache_hint: int = 0, launch_vpt: int = 0, stream=None):
     """The guided update from materialised branch predictions ``pred``
     [rows, C, H, W] in the plan's [uncond | cond] layout (see include/bcg.h);
     ``phase`` is "euler", "heun_predict" (writes ``d`` and x~ to x_out) or
     "heun_correct" (reads ``d`` and, for last steps, ``x_tilde``)."""
     a = _rows_args(x, x_out, pred, sigmas, order, step_idx, scale, uncond_row, cond_row,
                    n_active=n_active, phase=phase, d=d, x_tilde=x_tilde, x_orig=x_orig, mask=mask,
-                   cache_hint=cache_hint)
+                   cache_hint=cache_hint, launch_vpt=launch_vpt)
     L.check(L.lib().guided_step_rows(ct.byref(a), _stream(stream)))
 
 

@@ -369,6 +369,8 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         return fail(BCG_EINVAL, "%s: mask_per_sample must be 0 or 1", who);
     if (a->cache_hint != BCG_CACHE_KEEP && a->cache_hint != BCG_CACHE_STREAM)
         return fail(BCG_EINVAL, "%s: unknown cache_hint %d", who, a->cache_hint);
+    if (a->launch_vpt < 0 || a->launch_vpt > 64)
+        return fail(BCG_EINVAL, "%s: launch_vpt %d not in [0, 64]", who, a->launch_vpt);
     if (d) {
         const int rc = check_dplan(d, a->n, true, who);
         if (rc) return rc;
@@ -399,6 +401,51 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         return fail(BCG_EINVAL, "%s: x_orig and mask must be given together", who);
     const size_t bytes = (size_t)a->n * a->C * HW * elem_size(a->dtype);
     if (partial_overlap(a->x, a->x_out, bytes)) return fail(BCG_EINVAL, "%s: x and x_out partially overlap", who);
+    if (d && (d->step_out || d->bucket_id || d->record_out)) {
+        // The plan's workgroup runs alongside the step: nothing it writes may
+        // be read or written by the step, nor may it read the step's output.
+        struct Span {
+            const void* p;
+            size_t bytes;
+        };
+        const size_t in4 = (size_t)a->n * 4, nb4 = (size_t)(d->num_buckets + 1) * 4;
+        const size_t cfg4 = (size_t)d->num_buckets * 4;
+        const size_t R = (size_t)a->max_regions, nC4 = (size_t)a->n * a->C * 4;
+        const size_t mbytes = a->mask ? (size_t)(a->mask_per_sample ? a->n : 1) * HW * 4 : 0;
+        const Span writes[] = {{d->bucket_id, in4},     {d->scale, in4},          {d->uncond_row, in4},
+                               {d->cond_row, in4},      {d->order, in4},          {d->bucket_count, nb4},
+                               {d->bucket_offset, nb4}, {d->uncond_offset, nb4},  {d->totals, 8},
+                               {d->step_out, in4},      {d->record_out, in4 * 4}};
+        const Span step_uses[] = {{a->x, bytes},       // [0], [1]: the state; inputs from [2] on
+                                  {a->x_out, bytes},
+                                  {a->x_orig, a->x_orig ? bytes : 0},
+                                  {a->mask, mbytes},
+                                  {a->sigmas, (size_t)a->num_sigmas * 4},
+                                  {a->mu_uncond, nC4},
+                                  {a->mu_cond, nC4},
+                                  {a->region_count, R ? in4 : 0},
+                                  {a->region_box, in4 * R * 4},
+                                  {a->region_strength, in4 * R},
+                                  {a->mu_region, nC4 * R},
+                                  {d->record_in, d->record_in ? in4 * 4 : 0},
+                                  {d->step_in, in4},
+                                  {d->bucket_cfg, cfg4},
+                                  {d->bucket_cfg_end, d->bucket_cfg_end ? cfg4 : 0},
+                                  {d->cfg_override, d->cfg_override ? in4 : 0},
+                                  {d->covered, d->covered ? in4 : 0},
+                                  {d->covered_sets, d->covered_sets ? (size_t)a->n * 2 : 0},
+                                  {d->region_range, d->region_range ? in4 * 4 * R : 0}};
+        for (const Span& w : writes)
+            for (const Span& r : step_uses)
+                if (w.p && r.p && r.bytes && any_overlap(w.p, w.bytes, r.p, r.bytes))
+                    return fail(BCG_EINVAL, "%s: the plan's outputs overlap arrays the step reads or writes", who);
+        // every input of the step and of its plan but x itself (x_out may be x) vs the output
+        for (size_t q = 2; q < sizeof(step_uses) / sizeof(step_uses[0]); ++q) {
+            const Span& r = step_uses[q];
+            if (r.p && r.bytes && any_overlap(r.p, r.bytes, a->x_out, bytes))
+                return fail(BCG_EINVAL, "%s: an input of the step or its plan overlaps x_out", who);
+        }
+    }
     if (a->stats) {
         const size_t need = guided_step_workspace_size(a->n_active, a->C, a->H, a->W, a->dtype);
         if (!a->workspace || a->workspace_bytes < need)
@@ -434,7 +481,7 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         fill_dplan(p, d);
         p.t_end = d->steps;
     }
-    const LaunchShape shape = pick_shape(p.n_active, p.nvec);
+    const LaunchShape shape = a->launch_vpt > 0 ? LaunchShape{256, a->launch_vpt} : pick_shape(p.n_active, p.nvec);
     const int block = shape.block;
     p.vpt = shape.vpt;
     p.tiles = (int)(((int64_t)p.nvec + (int64_t)block * p.vpt - 1) / ((int64_t)block * p.vpt));
@@ -530,6 +577,8 @@ static int rows_prepare(const bcg_rows_args* a, const char* who, RowsLaunch& L) 
         return fail(BCG_EINVAL, "%s: mask_per_sample must be 0 or 1", who);
     if (a->cache_hint != BCG_CACHE_KEEP && a->cache_hint != BCG_CACHE_STREAM)
         return fail(BCG_EINVAL, "%s: unknown cache_hint %d", who, a->cache_hint);
+    if (a->launch_vpt < 0 || a->launch_vpt > 64)
+        return fail(BCG_EINVAL, "%s: launch_vpt %d not in [0, 64]", who, a->launch_vpt);
     L.launch = a->n_active > 0;
     L.dtype = a->dtype;
     if (!L.launch) return BCG_OK;
@@ -569,7 +618,7 @@ static int rows_prepare(const bcg_rows_args* a, const char* who, RowsLaunch& L) 
     p.pred = a->pred; p.sigmas = a->sigmas; p.order = a->order; p.step_idx = a->step_idx;
     p.scale = a->scale; p.uncond_row = a->uncond_row; p.cond_row = a->cond_row;
     p.x_orig = a->x_orig; p.mask = a->mask;
-    const LaunchShape shape = pick_shape(p.n_active, p.nvec);
+    const LaunchShape shape = a->launch_vpt > 0 ? LaunchShape{256, a->launch_vpt} : pick_shape(p.n_active, p.nvec);
     p.vpt = shape.vpt;
     p.tiles = (int)(((int64_t)p.nvec + (int64_t)shape.block * p.vpt - 1) / ((int64_t)shape.block * p.vpt));
     if ((int64_t)p.n_active * p.tiles >= INT32_MAX - 1) return fail(BCG_ESHAPE, "%s: grid too large", who);

@@ -28,7 +28,7 @@ using bcg::fail;
 
 extern "C" const char* bcg_last_error(void) { return bcg::g_err; }
 
-extern "C" int bcg_abi_version(void) { return 8; }
+extern "C" int bcg_abi_version(void) { return 9; }
 
 // "12 · Samplers, schedulers and CFG", sections "sigma sequence" and
 // "denoise below 1": the schedule runs from high to low noise and ends at 0;

@@ -23,7 +23,9 @@ struct bcg_loop {
     std::vector<hipEvent_t> row_ev;   // per staging row: its last upload done
     std::vector<hipEvent_t> use_ev;   // per staging row: the last kernel reading it done
     std::vector<char> row_used;
-    std::vector<hipEvent_t> t_ev;     // timing pairs, grown on demand
+    hipEvent_t t_ev[2] = {nullptr, nullptr};  // the pair bracketing a timed run
+    int32_t last_replayed = 0;        // launches of the last run inside graph replays
+    int32_t last_direct = 0;          // launches of the last run launched directly
     // host scratch of the plan outputs that do not go to the device
     std::vector<int32_t> bucket_id, cond_row, bucket_count, bucket_offset, uncond_offset;
     std::vector<int32_t> region_box;
@@ -34,8 +36,10 @@ struct bcg_loop {
     int64_t k_next = 0;               // launches done since the last restart
     std::vector<int32_t> t0;          // initial step indices (from start)
     std::vector<float> rec0;          // their sample records (with dev_records)
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t graph_exec = nullptr;
+    // graph g replays launches k .. k+G-1 for any k = g (mod 2*replicas): one
+    // per phase of the buffer pattern, so a replay can start at any launch
+    std::vector<hipGraph_t> graph;
+    std::vector<hipGraphExec_t> graph_exec;
 };
 
 namespace {
@@ -112,42 +116,43 @@ int launch_dplan(bcg_loop* L, int64_t k, hipStream_t st) {
     return guided_step_dplan(&a, &dp, st);
 }
 
-// Captures launches 0 .. G-1 (whole periods of the buffer pattern) into a
-// graph on the loop's own stream; nothing runs until it is launched.
-int build_graph(bcg_loop* L) {
+// Captures, for each phase g of the buffer pattern (period 2*replicas),
+// launches g .. g+G-1 into a graph on the loop's own stream; nothing runs
+// until one is launched.  A launch's buffers depend on k only through
+// k mod (2*replicas), so graph g replays launches k .. k+G-1 of any
+// k = g (mod 2*replicas).
+int build_graphs(bcg_loop* L) {
     const int G = L->d.graph_launches;
-    int rc = hip_ok(hipStreamBeginCapture(L->copy, hipStreamCaptureModeThreadLocal), "bcg_loop: begin capture");
-    if (rc) return rc;
-    int rc_launch = BCG_OK;
-    for (int k = 0; k < G && rc_launch == BCG_OK; ++k) rc_launch = launch_dplan(L, k, L->copy);
-    hipGraph_t g = nullptr;
-    rc = hip_ok(hipStreamEndCapture(L->copy, &g), "bcg_loop: end capture");
-    if (rc_launch || rc) {
-        if (g) (void)hipGraphDestroy(g);
-        return rc_launch ? rc_launch : rc;
+    const int period = 2 * L->d.replicas;
+    L->graph.assign(size_t(period), nullptr);
+    L->graph_exec.assign(size_t(period), nullptr);
+    for (int ph = 0; ph < period; ++ph) {
+        int rc = hip_ok(hipStreamBeginCapture(L->copy, hipStreamCaptureModeThreadLocal), "bcg_loop: begin capture");
+        if (rc) return rc;
+        int rc_launch = BCG_OK;
+        for (int k = ph; k < ph + G && rc_launch == BCG_OK; ++k) rc_launch = launch_dplan(L, k, L->copy);
+        hipGraph_t g = nullptr;
+        rc = hip_ok(hipStreamEndCapture(L->copy, &g), "bcg_loop: end capture");
+        if (rc_launch || rc) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc_launch ? rc_launch : rc;
+        }
+        L->graph[size_t(ph)] = g;
+        rc = hip_ok(hipGraphInstantiate(&L->graph_exec[size_t(ph)], g, nullptr, nullptr, 0),
+                    "bcg_loop: graph instantiate");
+        if (rc) {
+            L->graph_exec[size_t(ph)] = nullptr;
+            return rc;
+        }
+        // the graph's first replay then needs no upload of its own
+        rc = hip_ok(hipGraphUpload(L->graph_exec[size_t(ph)], L->copy), "bcg_loop: graph upload");
+        if (rc) return rc;
     }
-    rc = hip_ok(hipGraphInstantiate(&L->graph_exec, g, nullptr, nullptr, 0), "bcg_loop: graph instantiate");
-    if (rc) {
-        (void)hipGraphDestroy(g);
-        L->graph_exec = nullptr;
-        return rc;
-    }
-    L->graph = g;
-    return BCG_OK;
-}
-
-hipEvent_t* timing_event(bcg_loop* L, size_t idx, int* rc) {
-    while (L->t_ev.size() <= idx) {
-        hipEvent_t e;
-        *rc = hip_ok(hipEventCreate(&e), "bcg_loop_run: hipEventCreate");
-        if (*rc) return nullptr;
-        L->t_ev.push_back(e);
-    }
-    return &L->t_ev[idx];
+    return hip_ok(hipStreamSynchronize(L->copy), "bcg_loop: graph upload");
 }
 
 // bcg_loop_run with device plans.
-int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms) {
+int run_device(bcg_loop* L, int k0, int count, hipStream_t st) {
     const bcg_loop_desc& d = L->d;
     int rc = BCG_OK;
     if (k0 == 0 && L->k_next != 0) {
@@ -161,54 +166,103 @@ int run_device(bcg_loop* L, int k0, int count, hipStream_t st, float* kernel_ms)
     const int64_t period = 2 * int64_t(d.replicas);
     int64_t k = k0;
     int j = 0;
-    size_t pairs = 0;
-    std::vector<int> weight;  // launches per bracketed pair, negative for direct launches
     while (j < count) {
-        const bool replay = L->graph_exec && k % period == 0 && count - j >= G;
+        const bool replay = !L->graph_exec.empty() && G > 0 && count - j >= G;
         const int span = replay ? G : 1;
-        const bool timed = kernel_ms && (replay || j % d.timing_every == 0);
-        if (timed) {
-            hipEvent_t* e = timing_event(L, 2 * pairs, &rc);
-            if (rc) return rc;
-            rc = hip_ok(hipEventRecord(*e, st), "bcg_loop_run: event record");
-            if (rc) return rc;
-        }
         if (replay) {
-            rc = hip_ok(hipGraphLaunch(L->graph_exec, st), "bcg_loop_run: graph launch");
+            rc = hip_ok(hipGraphLaunch(L->graph_exec[size_t(k % period)], st), "bcg_loop_run: graph launch");
         } else {
             rc = launch_dplan(L, k, st);
         }
         if (rc) return rc;
-        if (timed) {
-            hipEvent_t* e = timing_event(L, 2 * pairs + 1, &rc);
-            if (rc) return rc;
-            rc = hip_ok(hipEventRecord(*e, st), "bcg_loop_run: event record");
-            if (rc) return rc;
-            weight.push_back(replay ? span : -1);
-            ++pairs;
-        }
+        (replay ? L->last_replayed : L->last_direct) += span;
         k += span;
         j += span;
         L->k_next = k;
     }
-    if (kernel_ms) {
-        *kernel_ms = 0.0f;
-        if (pairs == 0) return BCG_OK;
-        rc = hip_ok(hipEventSynchronize(L->t_ev[2 * pairs - 1]), "bcg_loop_run: timing wait");
-        if (rc) return rc;
-        // graph replays when there were any, else the directly launched brackets
-        const bool any_replay = std::any_of(weight.begin(), weight.end(), [](int w) { return w > 0; });
-        double total = 0.0;
-        long long launches = 0;
-        for (size_t q = 0; q < pairs; ++q) {
-            if (any_replay != (weight[q] > 0)) continue;
-            float ms = 0.0f;
-            rc = hip_ok(hipEventElapsedTime(&ms, L->t_ev[2 * q], L->t_ev[2 * q + 1]), "bcg_loop_run: elapsed");
+    return BCG_OK;
+}
+
+// bcg_loop_run with host plans.
+int run_host(bcg_loop* L, int k0, int count, hipStream_t st) {
+    const bcg_loop_desc& d = L->d;
+    const int n = d.plan.n, steps = d.plan.steps, P = d.upload_batch;
+    hipStream_t up = d.async_upload ? L->copy : st;
+    const size_t row_elems = 4 * size_t(n);
+    int j = 0;
+    while (j < count) {
+        // One chunk: launches k .. k+m-1, all inside one aligned group of P rows.
+        const int k = k0 + j;
+        const int row0 = k % d.rows;
+        const int m = std::min(count - j, P - (row0 % P));
+        const int g = row0 / P;  // upload group (rows g*P .. g*P+P-1)
+        if (L->row_used[size_t(g)]) {
+            // the host rows are free once the group's previous copy is done; the
+            // device rows once the last launch that read them is done
+            int rc = hip_ok(hipEventSynchronize(L->row_ev[size_t(g)]), "bcg_loop_run: row wait");
             if (rc) return rc;
-            total += ms;
-            launches += weight[q] > 0 ? weight[q] : 1;
+            if (d.async_upload) {
+                rc = hip_ok(hipStreamWaitEvent(up, L->use_ev[size_t(g)], 0), "bcg_loop_run: row reuse wait");
+                if (rc) return rc;
+            }
         }
-        *kernel_ms = float(total / double(launches));
+        int n_active[64];
+        int32_t* h0 = d.host_slab + size_t(row0) * row_elems;
+        int32_t* dv0 = d.dev_slab + size_t(row0) * row_elems;
+        for (int q = 0; q < m; ++q) {
+            int32_t* h = h0 + size_t(q) * row_elems;
+            for (int i = 0; i < n; ++i) {
+                long long t = (long long)d.start[i] + (k + q) / d.replicas;
+                if (d.wrap && t >= 0) t %= steps;
+                h[i] = int32_t(t);
+            }
+            bcg_plan_in pin = d.plan;
+            pin.step_idx = h;
+            bcg_plan_out po{};
+            po.bucket_id = L->bucket_id.data();
+            po.scale = reinterpret_cast<float*>(h + n);
+            po.uncond_row = h + 2 * n;
+            po.cond_row = L->cond_row.data();
+            po.order = h + 3 * n;
+            po.bucket_count = L->bucket_count.data();
+            po.bucket_offset = L->bucket_offset.data();
+            po.uncond_offset = L->uncond_offset.data();
+            const int rc = bcg_plan_build(&pin, &po);
+            if (rc) return rc;
+            n_active[q] = po.n_active;
+        }
+        int rc = hip_ok(hipMemcpyAsync(dv0, h0, sizeof(int32_t) * row_elems * size_t(m),
+                                       hipMemcpyHostToDevice, up), "bcg_loop_run: plan upload");
+        if (rc) return rc;
+        rc = hip_ok(hipEventRecord(L->row_ev[size_t(g)], up), "bcg_loop_run: event record");
+        if (rc) return rc;
+        if (d.async_upload) {
+            rc = hip_ok(hipStreamWaitEvent(st, L->row_ev[size_t(g)], 0), "bcg_loop_run: upload wait");
+            if (rc) return rc;
+        }
+        L->row_used[size_t(g)] = 1;
+        for (int q = 0; q < m; ++q, ++j) {
+            const int kk = k + q;
+            const int32_t* dv = dv0 + size_t(q) * row_elems;
+            bcg_step_args a = d.step;
+            if (d.replicas > 1) {
+                const int64_t off = int64_t(kk % d.replicas) * d.replica_stride;
+                a.x = static_cast<const char*>(a.x) + off;
+                a.x_out = static_cast<char*>(a.x_out) + off;
+            }
+            a.step_idx = dv;
+            a.scale = reinterpret_cast<const float*>(dv + n);
+            a.uncond_row = dv + 2 * n;
+            a.order = dv + 3 * n;
+            a.n_active = n_active[q];
+            rc = guided_step(&a, st);
+            if (rc) return rc;
+            ++L->last_direct;
+        }
+        if (d.async_upload) {
+            rc = hip_ok(hipEventRecord(L->use_ev[size_t(g)], st), "bcg_loop_run: event record");
+            if (rc) return rc;
+        }
     }
     return BCG_OK;
 }
@@ -228,7 +282,6 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
     if (desc->step.max_regions != R) return fail(BCG_EINVAL, "bcg_loop_create: step/plan max_regions differ");
     if (desc->replicas < 1 || (desc->replicas > 1 && desc->replica_stride <= 0))
         return fail(BCG_EINVAL, "bcg_loop_create: replicas must be >= 1 with a positive stride");
-    if (desc->timing_every < 1) return fail(BCG_EINVAL, "bcg_loop_create: timing_every must be >= 1");
     if (desc->device_plan != 0 && desc->device_plan != 1)
         return fail(BCG_EINVAL, "bcg_loop_create: device_plan must be 0 or 1");
     if (!desc->device_plan &&
@@ -237,9 +290,8 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
                     desc->upload_batch, desc->rows);
     if (desc->device_plan) {
         if (n > 0 && !desc->dev_steps) return fail(BCG_EINVAL, "bcg_loop_create: dev_steps is NULL");
-        if (desc->graph_launches < 0 || desc->graph_launches % (2 * desc->replicas) != 0)
-            return fail(BCG_EINVAL, "bcg_loop_create: graph_launches %d must be a non-negative multiple of 2*replicas",
-                        desc->graph_launches);
+        if (desc->graph_launches < 0 || desc->graph_launches > 4096)
+            return fail(BCG_EINVAL, "bcg_loop_create: graph_launches %d not in [0, 4096]", desc->graph_launches);
     } else if (desc->graph_launches != 0) {
         return fail(BCG_EINVAL, "bcg_loop_create: graph_launches needs device plans");
     }
@@ -249,6 +301,7 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
     L->use_ev.assign(size_t(desc->rows), nullptr);
     L->row_used.assign(size_t(desc->rows), 0);
     hipError_t rc = hipStreamCreateWithFlags(&L->copy, hipStreamNonBlocking);
+    for (int q = 0; q < 2 && rc == hipSuccess; ++q) rc = hipEventCreate(&L->t_ev[q]);
     for (size_t r = 0; rc == hipSuccess && r < L->row_ev.size(); ++r) {
         rc = hipEventCreateWithFlags(&L->row_ev[r], hipEventDisableTiming);
         if (rc == hipSuccess) rc = hipEventCreateWithFlags(&L->use_ev[r], hipEventDisableTiming);
@@ -350,7 +403,7 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
         int rc2 = check_dplan(L, "bcg_loop_create");
         if (rc2 == BCG_OK) rc2 = reset_steps(L, nullptr);
         if (rc2 == BCG_OK) rc2 = hip_ok(hipStreamSynchronize(nullptr), "bcg_loop_create: step index upload");
-        if (rc2 == BCG_OK && desc->graph_launches > 0 && n > 0) rc2 = build_graph(L);
+        if (rc2 == BCG_OK && desc->graph_launches > 0 && n > 0) rc2 = build_graphs(L);
         if (rc2) {
             bcg_loop_destroy(L);
             return rc2;
@@ -370,8 +423,10 @@ extern "C" int bcg_loop_destroy(bcg_loop* L) {
     if (L->copy) (void)hipStreamDestroy(L->copy);
     for (auto e : L->t_ev)
         if (e) (void)hipEventDestroy(e);
-    if (L->graph_exec) (void)hipGraphExecDestroy(L->graph_exec);
-    if (L->graph) (void)hipGraphDestroy(L->graph);
+    for (auto e : L->graph_exec)
+        if (e) (void)hipGraphExecDestroy(e);
+    for (auto g : L->graph)
+        if (g) (void)hipGraphDestroy(g);
     delete L;
     return BCG_OK;
 }
@@ -381,117 +436,27 @@ extern "C" int bcg_loop_run(bcg_loop* L, int k0, int count, void* stream, float*
     if (!L) return fail(BCG_EINVAL, "bcg_loop_run: NULL loop");
     if (count < 0 || k0 < 0) return fail(BCG_EINVAL, "bcg_loop_run: negative k0/count");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bcg_loop_desc& d = L->d;
-    if (d.device_plan) return run_device(L, k0, count, st, kernel_ms);
-    const int n = d.plan.n, steps = d.plan.steps, P = d.upload_batch;
-    hipStream_t up = d.async_upload ? L->copy : st;
-    const int every = d.timing_every;
-    const int n_timed = (count + every - 1) / every;
+    L->last_replayed = L->last_direct = 0;
+    int rc = BCG_OK;
     if (kernel_ms) {
-        while (L->t_ev.size() < size_t(2 * n_timed)) {
-            hipEvent_t e;
-            int rc = hip_ok(hipEventCreate(&e), "bcg_loop_run: hipEventCreate");
-            if (rc) return rc;
-            L->t_ev.push_back(e);
-        }
         *kernel_ms = 0.0f;
-    }
-    const size_t row_elems = 4 * size_t(n);
-    int j = 0;
-    while (j < count) {
-        // One chunk: launches k .. k+m-1, all inside one aligned group of P rows.
-        const int k = k0 + j;
-        const int row0 = k % d.rows;
-        const int m = std::min(count - j, P - (row0 % P));
-        const int g = row0 / P;  // upload group (rows g*P .. g*P+P-1)
-        if (L->row_used[size_t(g)]) {
-            // the host rows are free once the group's previous copy is done; the
-            // device rows once the last launch that read them is done
-            int rc = hip_ok(hipEventSynchronize(L->row_ev[size_t(g)]), "bcg_loop_run: row wait");
-            if (rc) return rc;
-            if (d.async_upload) {
-                rc = hip_ok(hipStreamWaitEvent(up, L->use_ev[size_t(g)], 0), "bcg_loop_run: row reuse wait");
-                if (rc) return rc;
-            }
-        }
-        int n_active[64];
-        int32_t* h0 = d.host_slab + size_t(row0) * row_elems;
-        int32_t* dv0 = d.dev_slab + size_t(row0) * row_elems;
-        for (int q = 0; q < m; ++q) {
-            int32_t* h = h0 + size_t(q) * row_elems;
-            for (int i = 0; i < n; ++i) {
-                long long t = (long long)d.start[i] + (k + q) / d.replicas;
-                if (d.wrap && t >= 0) t %= steps;
-                h[i] = int32_t(t);
-            }
-            bcg_plan_in pin = d.plan;
-            pin.step_idx = h;
-            bcg_plan_out po{};
-            po.bucket_id = L->bucket_id.data();
-            po.scale = reinterpret_cast<float*>(h + n);
-            po.uncond_row = h + 2 * n;
-            po.cond_row = L->cond_row.data();
-            po.order = h + 3 * n;
-            po.bucket_count = L->bucket_count.data();
-            po.bucket_offset = L->bucket_offset.data();
-            po.uncond_offset = L->uncond_offset.data();
-            const int rc = bcg_plan_build(&pin, &po);
-            if (rc) return rc;
-            n_active[q] = po.n_active;
-        }
-        int rc = hip_ok(hipMemcpyAsync(dv0, h0, sizeof(int32_t) * row_elems * size_t(m),
-                                       hipMemcpyHostToDevice, up), "bcg_loop_run: plan upload");
+        rc = hip_ok(hipEventRecord(L->t_ev[0], st), "bcg_loop_run: event record");
         if (rc) return rc;
-        rc = hip_ok(hipEventRecord(L->row_ev[size_t(g)], up), "bcg_loop_run: event record");
-        if (rc) return rc;
-        if (d.async_upload) {
-            rc = hip_ok(hipStreamWaitEvent(st, L->row_ev[size_t(g)], 0), "bcg_loop_run: upload wait");
-            if (rc) return rc;
-        }
-        L->row_used[size_t(g)] = 1;
-        for (int q = 0; q < m; ++q, ++j) {
-            const int kk = k + q;
-            const int32_t* dv = dv0 + size_t(q) * row_elems;
-            bcg_step_args a = d.step;
-            if (d.replicas > 1) {
-                const int64_t off = int64_t(kk % d.replicas) * d.replica_stride;
-                a.x = static_cast<const char*>(a.x) + off;
-                a.x_out = static_cast<char*>(a.x_out) + off;
-            }
-            a.step_idx = dv;
-            a.scale = reinterpret_cast<const float*>(dv + n);
-            a.uncond_row = dv + 2 * n;
-            a.order = dv + 3 * n;
-            a.n_active = n_active[q];
-            const bool timed = kernel_ms && j % every == 0;
-            if (timed) {
-                rc = hip_ok(hipEventRecord(L->t_ev[size_t(2 * (j / every))], st), "bcg_loop_run: event record");
-                if (rc) return rc;
-            }
-            rc = guided_step(&a, stream);
-            if (rc) return rc;
-            if (timed) {
-                rc = hip_ok(hipEventRecord(L->t_ev[size_t(2 * (j / every) + 1)], st), "bcg_loop_run: event record");
-                if (rc) return rc;
-            }
-        }
-        if (d.async_upload) {
-            rc = hip_ok(hipEventRecord(L->use_ev[size_t(g)], st), "bcg_loop_run: event record");
-            if (rc) return rc;
-        }
     }
-    if (kernel_ms && count > 0) {
-        int rc = hip_ok(hipEventSynchronize(L->t_ev[size_t(2 * n_timed - 1)]), "bcg_loop_run: timing wait");
-        if (rc) return rc;
-        double total = 0.0;
-        for (int q = 0; q < n_timed; ++q) {
-            float ms = 0.0f;
-            rc = hip_ok(hipEventElapsedTime(&ms, L->t_ev[size_t(2 * q)], L->t_ev[size_t(2 * q + 1)]),
-                        "bcg_loop_run: elapsed");
-            if (rc) return rc;
-            total += ms;
-        }
-        *kernel_ms = float(total / n_timed);
-    }
+    rc = L->d.device_plan ? run_device(L, k0, count, st) : run_host(L, k0, count, st);
+    if (rc || !kernel_ms) return rc;
+    rc = hip_ok(hipEventRecord(L->t_ev[1], st), "bcg_loop_run: event record");
+    if (rc == BCG_OK) rc = hip_ok(hipEventSynchronize(L->t_ev[1]), "bcg_loop_run: timing wait");
+    float ms = 0.0f;
+    if (rc == BCG_OK) rc = hip_ok(hipEventElapsedTime(&ms, L->t_ev[0], L->t_ev[1]), "bcg_loop_run: elapsed");
+    if (rc == BCG_OK && count > 0) *kernel_ms = ms / float(count);
+    return rc;
+}
+
+extern "C" int bcg_loop_last_run(const bcg_loop* L, int32_t* replayed, int32_t* direct) {
+    bcg::clear_error();
+    if (!L) return fail(BCG_EINVAL, "bcg_loop_last_run: NULL loop");
+    if (replayed) *replayed = L->last_replayed;
+    if (direct) *direct = L->last_direct;
     return BCG_OK;
 }

@@ -187,7 +187,8 @@ class GuidedSampler:
         self._row_ev[row].record()
         return p, d
 
-    def launch(self, d, n_active, x, x_out=None, stats=None, workspace=None, cache_hint=0):
+    def launch(self, d, n_active, x, x_out=None, stats=None, workspace=None, cache_hint=0,
+               launch_vpt=0):
         n = self.n
         api.guided_step(x, x if x_out is None else x_out, self.d_sigmas, d[3 * n:4 * n], d[:n],
                         d[n:2 * n].view(torch.float32), d[2 * n:3 * n], self.d_mu_u, self.d_mu_c,
@@ -196,12 +197,12 @@ class GuidedSampler:
                         region_box=self.d_region_box, region_strength=self.d_region_strength,
                         mu_region=self.d_mu_region, x_orig=self.d_x_orig, mask=self.d_mask,
                         stats=stats, workspace=workspace, cache_hint=cache_hint,
-                        region_range=self.d_region_range, steps=self.steps)
+                        region_range=self.d_region_range, steps=self.steps, launch_vpt=launch_vpt)
 
-    def step(self, k: int, x, x_out=None, stats=None, workspace=None, cache_hint=0):
+    def step(self, k: int, x, x_out=None, stats=None, workspace=None, cache_hint=0, launch_vpt=0):
         """Launch k of the loop: plan, upload, one fused guided step."""
         p, d = self.upload_plan(k)
-        self.launch(d, p.n_active, x, x_out, stats, workspace, cache_hint)
+        self.launch(d, p.n_active, x, x_out, stats, workspace, cache_hint, launch_vpt)
         return p
 
     def records(self, k: int):
@@ -246,8 +247,7 @@ class GuidedSampler:
     # ------------------------------------------------------------ native loop
 
     def native_loop(self, x, x_out=None, upload_batch=8, async_upload=False, cache_hint=None,
-                    timing_every=1, device_plan=False, graph_launches=0, plan_outputs=True,
-                    records=True):
+                    device_plan=False, graph_launches=0, plan_outputs=True, records=True):
         """A C++ loop (bcg_loop_*) advancing ``x`` (in place unless x_out).
 
         ``x`` may also be [replicas, n, C, H, W]: launch k then advances
@@ -256,7 +256,7 @@ class GuidedSampler:
         each step's plan on the device inside the step's launch (into
         ``loop.plan_out`` when ``plan_outputs``); ``graph_launches`` > 0
         replays a captured graph of that many launches."""
-        return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint, timing_every,
+        return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint,
                           device_plan, graph_launches, plan_outputs, records)
 
 
@@ -264,7 +264,7 @@ class NativeLoop:
     """Owner of a bcg_loop handle and of the host/device arrays it points to."""
 
     def __init__(self, s: GuidedSampler, x, x_out=None, upload_batch=8, async_upload=False,
-                 cache_hint=None, timing_every=1, device_plan=False, graph_launches=0,
+                 cache_hint=None, device_plan=False, graph_launches=0,
                  plan_outputs=True, records=True):
         n = s.n
         P = int(upload_batch)
@@ -323,7 +323,7 @@ class NativeLoop:
         self.desc = L.LoopDesc(plan, npp(s.start, np.int32), 1 if s.wrap else 0, rows,
                                api._ptr(self.h_slab), api._ptr(self.d_slab), reps,
                                stride if reps > 1 else 0, P, 1 if async_upload else 0,
-                               int(timing_every), step, 1 if device_plan else 0,
+                               step, 1 if device_plan else 0,
                                int(graph_launches), api._ptr(self.dev_steps), dplan,
                                api._ptr(self.dev_records))
         self.handle = ct.c_void_p()
@@ -331,13 +331,20 @@ class NativeLoop:
 
     def run(self, k0: int, count: int, timing: bool = False):
         """Launches k0 .. k0+count-1 on the current stream; with ``timing`` the
-        mean guided_step duration (ms, HIP events around every timing_every-th
-        launch) is returned."""
+        mean time per launch (ms) between one pair of HIP events around the
+        whole run is returned."""
         ms = ct.c_float(0.0)
         L.check(L.lib().bcg_loop_run(self.handle, int(k0), int(count),
                                      torch.cuda.current_stream().cuda_stream,
                                      ct.byref(ms) if timing else None))
         return ms.value if timing else None
+
+    def last_run(self):
+        """(launches inside graph replays, launches launched directly) of the
+        last run."""
+        rep, dire = ct.c_int32(0), ct.c_int32(0)
+        L.check(L.lib().bcg_loop_last_run(self.handle, ct.byref(rep), ct.byref(dire)))
+        return rep.value, dire.value
 
     def close(self):
         if self.handle:

@@ -282,6 +282,9 @@ typedef struct {
     const double* region_range;      /* device [n][R][2] (start, end) progress or NULL: region r
                                         takes part iff start <= t/steps < end (as the plan) */
     int32_t steps;                   /* trajectory length, with region_range */
+    int32_t launch_vpt;              /* 0: launch shape chosen by the library; k in [1, 64]:
+                                        workgroups of 256 lanes, each lane taking k pixel
+                                        vectors (the shape only: results are identical) */
 } bcg_step_args;
 
 int guided_step(const bcg_step_args* args, void* stream);
@@ -451,6 +454,8 @@ typedef struct {
     const int32_t* cond_row;         /* device [n] */
     const void* x_orig;              /* device [n,C,H,W] or NULL (no inpaint) */
     const float* mask;               /* device mask or NULL (with x_orig) */
+    int32_t launch_vpt;              /* 0: launch shape chosen by the library; k in [1, 64]:
+                                        workgroups of 256 lanes, k pixel vectors per lane */
 } bcg_rows_args;
 
 int guided_step_rows(const bcg_rows_args* args, void* stream);
@@ -601,20 +606,23 @@ int weight_patch(const bcg_weight_args* args, void* stream);
  * host work or copy per launch.  The indices (and records) are written from
  * `start` at bcg_loop_create and again whenever a run starts at k0 = 0;
  * otherwise k0 must continue the previous run.  With graph_launches
- * G > 0 (a multiple of 2*replicas), runs of G launches starting at a multiple
- * of 2*replicas are replays of one HIP graph, captured at bcg_loop_create on
- * a stream of the loop's own.
+ * G > 0, every run of G launches is the replay of a HIP graph: at
+ * bcg_loop_create one graph per phase of the buffer pattern (launches
+ * g .. g+G-1, g < 2*replicas) is captured on a stream of the loop's own, so
+ * a replay can start at any launch; launches left over (fewer than G) are
+ * launched directly.
  *
  * The descriptor is copied at create time; the arrays it points to (host plan
  * inputs, staging rows, dev_steps, every device array of `step` and `dplan`)
  * are owned by the caller and must outlive the loop.  step.order / step_idx /
  * scale / uncond_row / n_active are ignored (filled per launch); with
  * replicas > 1, step.x and step.x_out are offset by r * replica_stride bytes.
- * If kernel_ms is not NULL, every graph replay and every timing_every-th
- * direct launch is bracketed by HIP events on `stream`, bcg_loop_run waits
- * for the last one, and *kernel_ms receives the mean time per launch (ms)
- * inside the replays, or inside the bracketed direct launches if the run had
- * no replay.
+ * If kernel_ms is not NULL, one pair of HIP events on `stream` brackets the
+ * whole run (the first recorded before its first launch, the second after
+ * its last), bcg_loop_run waits for the second, and *kernel_ms receives the
+ * elapsed time divided by count: the mean time per launch, gaps between
+ * launches included.  bcg_loop_last_run reports how many launches of the
+ * last run were graph replays and how many were launched directly.
  * Errors: as bcg_plan_build, guided_step and guided_step_dplan; BCG_EHIP.
  */
 typedef struct {
@@ -631,11 +639,9 @@ typedef struct {
                                         be a multiple of P (host plans) */
     int32_t async_upload;            /* 1: uploads on the loop's own copy stream,
                                         overlapping earlier launches; 0: on `stream` */
-    int32_t timing_every;            /* m >= 1: with kernel_ms, launches j with
-                                        j % m == 0 are bracketed by events */
     bcg_step_args step;              /* launch template (replica 0) */
     int32_t device_plan;             /* 0: host plans; 1: device plans */
-    int32_t graph_launches;          /* device plans: G >= 0, see above */
+    int32_t graph_launches;          /* device plans: G in [0, 4096], see above */
     int32_t* dev_steps;              /* device plans: device [replicas][2][n] */
     bcg_device_plan dplan;           /* device plans: template (steps, num_buckets and
                                         wrap are taken from plan/wrap; step_in and
@@ -649,6 +655,9 @@ typedef struct bcg_loop bcg_loop;
 
 int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out);
 int bcg_loop_run(bcg_loop* loop, int k0, int count, void* stream, float* kernel_ms);
+/* Launches of the last bcg_loop_run inside graph replays (*replayed) and
+ * launched directly (*direct); either pointer may be NULL. */
+int bcg_loop_last_run(const bcg_loop* loop, int32_t* replayed, int32_t* direct);
 int bcg_loop_destroy(bcg_loop* loop);
 
 #ifdef __cplusplus

@@ -78,3 +78,53 @@ def oracle_step_M(inp, sig, plan, k, x_in, idx):
                      bool(plan["need_uncond"][i]), M.params32(inp, i), inp.spec.sampler)
         out[i] = M._store(y, inp.spec.dtype)
     return out
+
+
+def storage_flip_bound(inp, i, launches=None):
+    """Per-element bound on |x_M - x_D| for sample i after the trajectory,
+    when both store every state in bf16 and the fp32 arithmetic is otherwise
+    within 1e-5 of exact.
+
+    Both sides round to bf16 after every step.  Where the exact step value
+    lies close to a rounding midpoint the two sides can take neighbouring
+    codes (a flip of one ulp of the state), and a flip made while |x| is large
+    is carried to the end by the later steps.  With the linear stand-in the
+    guided prediction is P(x) = A x + B per element, A = m s2/(s2 + sigma^2)
+    (m the inpaint mask, 1 without one; the regional weights sum to one and
+    the CFG combine keeps A), so one step maps a difference Delta to
+    J Delta with
+      Euler  J = 1 + (sigma'-sigma)/sigma (1 - A),
+      Heun   J = 1 + h/2 [(1-A)/sigma + (1-A2)/sigma' (1 + h (1-A)/sigma)],
+      last step (sigma' = 0) J = A,
+    and the stored difference after a step is at most |J| Delta plus one
+    ulp of the stored value (each side rounds to within half an ulp), plus
+    the fp32 slack.  Starting from one ulp of the initial latent, the bound
+    is the recurrence Delta_k = |J_k| Delta_{k-1} + ulp(X_k + |J_k| Delta_{k-1})
+    + 2e-6 max|X_k| over the launches where the sample is active, X_k the
+    mode D state."""
+    sub = inp.subset([i])
+    sp = sub.spec
+    sig, _, _ = D.run_setup(sub)
+    sig = sig.astype(np.float64)
+    _, states = D.trajectory(sub, launches=launches, keep=True)
+    m = 1.0 if sub.mask is None else sub.mask[0, 0].astype(np.float64)
+    s2 = float(sp.s2)
+    bound = bf16_ulp(states[0][0])
+    for k in range(1, len(states)):
+        t = int(sub.start_step[0]) + k - 1
+        if not 0 <= t < sp.steps:
+            continue
+        s0, s1 = sig[t], sig[t + 1]
+        A = m * s2 / (s2 + s0 * s0)
+        if s1 == 0.0:
+            J = A
+        elif sp.sampler == "euler":
+            J = 1.0 + (s1 - s0) / s0 * (1.0 - A)
+        else:
+            A2 = m * s2 / (s2 + s1 * s1)
+            h = s1 - s0
+            J = 1.0 + 0.5 * h * ((1.0 - A) / s0 + (1.0 - A2) / s1 * (1.0 + h * (1.0 - A) / s0))
+        X = np.abs(states[k][0])
+        carried = np.abs(J) * bound
+        bound = carried + bf16_ulp(X + carried) + 2e-6 * X.max()
+    return bound

@@ -210,7 +210,7 @@ def test_native_loop_device_plan_equals_host_plan(reps, wrap):
     sp = W.small_spec(n=5, C=2, H=8, W=16, regions=2, steps=6, num_buckets=3)
     inp = W.make_inputs(sp)
     inp.start_step[:] = [0, 2, -1, 5, -3]
-    runs = [(0, 5), (5, 19)]  # launches 0..23; with graphs, replays from launch 8 on
+    runs = [(0, 5), (5, 19)]  # launches 0..23; with graphs, replays start at launches 0, 5, 9, ...
     xh, _, _ = _loop_states(inp, reps, False, 0, runs, wrap)
     for graph in (0, 4 * reps):
         xd, plan, s = _loop_states(inp, reps, True, graph, runs, wrap)
@@ -306,3 +306,32 @@ def test_dplan_with_sample_records_equals_host_path(name):
         got = recs[(k + 1) & 1].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), s.records(k + 1).view(np.uint32)), k
     assert torch.equal(x, xh)
+
+
+def test_bench_loop_large_shape_matches_mirror():
+    """The bench's loop at the large workload's full size (256 x 16x128x128
+    bf16, 2 regions, Euler): device plans with sample records, replays of a
+    captured graph, two replicas served round robin with the streaming hint,
+    starts without wrapping (the oracle's trajectory).  After every replay the
+    sampled samples of both replicas equal mode M bit for bit; at the end they
+    are within the mode-D bars."""
+    from gpu_helpers import bf16_ulp, storage_flip_bound
+    inp = W.make_inputs(W.config("large_bf16"))
+    idx = [0, 37, 101, 255]
+    sub = inp.subset(idx)
+    _, ms = M.trajectory32(sub, launches=12, keep=True)
+    s = _sampler(inp)
+    x = torch.stack([s.init_state(), s.init_state()])
+    loop = s.native_loop(x, device_plan=True, graph_launches=8, records=True)
+    for r in range(3):
+        loop.run(8 * r, 8)          # one replay: 4 steps of each replica
+        assert loop.last_run() == (8, 0)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            got = to_np(x[rep, idx])
+            assert np.array_equal(got, ms[4 * (r + 1)]), f"replay {r} replica {rep}"
+    loop.close()
+    xd = D.trajectory(sub, launches=12)
+    err = np.abs(to_np(x[1, idx]).astype(np.float64) - xd)
+    for q in np.argwhere(err > np.maximum(2e-2, bf16_ulp(xd))):
+        assert err[tuple(q)] <= storage_flip_bound(sub, int(q[0]), 12)[tuple(q[1:])]

@@ -7,9 +7,10 @@ Bars (written into each test):
   * each step, teacher-forced from the mode D state, within 1e-5 of
     max|ref| per sample (fp32 storage), or within half a bf16 ulp of the
     unrounded mode D value plus that 1e-5 (bf16 storage);
-  * the final latent within 2e-2 absolute of mode M (bf16 storage; at most
-    1e-5 of the elements beyond it vs mode D, from storage rounding flips),
-    and within 1e-4 relative of mode D for fp32 storage.
+  * the final latent within 2e-2 absolute of mode M (bf16 storage), and
+    per element within max(2e-2, 1 bf16 ulp) of mode D unless inside the
+    bound of carried storage-rounding flips (storage_flip_bound); within
+    1e-4 relative of mode D for fp32 storage.
 """
 import dataclasses
 
@@ -22,7 +23,7 @@ from oracle import definition as D
 from oracle import mirror32 as M
 
 from gpu_helpers import (bf16_ulp, gpu_step_from, gpu_trajectory, oracle_step_D,
-                          oracle_step_M, per_sample_rel_err, to_dev, to_np)
+                          oracle_step_M, per_sample_rel_err, storage_flip_bound, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,12 +68,21 @@ def _check_full(inp, idx, launches=None):
     if sp.dtype == "bf16":
         # 2e-2 absolute vs mode M (the same fp32 decisions; in fact identical) ...
         assert np.abs(xg[idx] - xm[idx]).max() <= 2e-2
-        # ... and vs mode D, whose float64 arithmetic takes a different bf16 code
-        # now and then; a code flip while |x| is large survives the contraction
-        # of later steps as up to ~0.03 absolute.  Bound: at most 1e-5 of the
-        # elements beyond 2e-2, none beyond 0.0625.
-        assert (err > 2e-2).mean() <= 1e-5, float((err > 2e-2).mean())
-        assert err.max() <= 0.0625, float(err.max())
+        # ... and vs mode D per element within max(2e-2, one bf16 ulp of the
+        # reference).  Mode D's float64 steps round to a neighbouring bf16
+        # code now and then (a flip); a flip made while |x| is large is
+        # carried to the end by the later steps, so an element over that bar
+        # must be inside the bound the storage roundings allow
+        # (storage_flip_bound: the flips carried by the step Jacobians).
+        bar = np.maximum(2e-2, bf16_ulp(xd[idx]))
+        over = np.argwhere(err > bar)
+        for q in over:
+            i = idx[q[0]]
+            fb = storage_flip_bound(inp, i, launches)[tuple(q[1:])]
+            assert err[tuple(q)] <= fb, (f"{sp.name}: sample {i} element {tuple(q[1:])}: "
+                                         f"{err[tuple(q)]:.4g} over the flip bound {fb:.4g}")
+        print(f"{sp.name}: {int((err > 0).sum())} of {err.size} elements differ from mode D "
+              f"(bf16 code flips), {len(over)} over max(2e-2, 1 ulp), max {err.max():.4g}")
     else:
         assert per_sample_rel_err(xg, xd, idx).max() <= 1e-4
     return xg
@@ -134,6 +144,7 @@ def test_large_full_size_teacher_forced():
 # ---------------------------------------------------------------- small shapes, edge cases
 
 SMALL = [
+    dict(dtype="bf16", sampler="euler", regions=2),   # the large workload's variant
     dict(dtype="f32", sampler="euler"),
     dict(dtype="f32", sampler="heun"),
     dict(dtype="bf16", sampler="euler"),
@@ -157,9 +168,44 @@ def test_small_shapes_full_trajectory(shape, kw):
 
 
 def test_many_samples_multi_vector_lanes():
-    # enough samples that each lane takes several vectors, with a ragged last tile
+    # 700 samples with a ragged last tile (the automatic shape: one vector per lane)
     sp = W.small_spec(n=700, C=1, H=40, W=64, steps=3, regions=2, inpaint=True, feather=4)
     _check_full(W.make_inputs(sp), list(range(0, 700, 7)))
+
+
+MULTI_VECTOR = [dict(dtype="bf16", sampler="euler", regions=2),
+                dict(dtype="f32", sampler="heun", regions=3),
+                dict(dtype="bf16", sampler="heun", regions=1, inpaint=True),
+                dict(dtype="f32", sampler="euler")]
+
+
+@pytest.mark.parametrize("vpt", [2, 3])
+@pytest.mark.parametrize("hint", [0, 1])
+@pytest.mark.parametrize("C", [16, 12, 5])
+@pytest.mark.parametrize("kw", MULTI_VECTOR)
+def test_multi_vector_lanes_match_mirror(vpt, hint, C, kw):
+    # Lanes taking several vectors (the launch shape forced to vpt vectors per
+    # lane of 256): H*W = 40*64 is 320 bf16 / 640 fp32 vectors, so the last
+    # pass of each workgroup is ragged; the streaming variants request the next
+    # pass's head stage during the current one.  Every sample bit for bit equal
+    # to mode M and to the automatic launch shape.
+    sp = W.small_spec(n=3, C=C, H=40, W=64, steps=5, num_buckets=3, feather=3, **kw)
+    inp = W.make_inputs(sp)
+    s = _sampler(inp)
+    sig, table, cov = D.run_setup(inp)
+    k = 1
+    x_in = D.init_latent(inp, sig, sp.dtype).astype(np.float32)
+    x = to_dev(x_in, sp.dtype)
+    auto, forced = torch.full_like(x, float("nan")), torch.full_like(x, float("nan"))
+    s.step(k, x, auto, cache_hint=hint)
+    s.step(k, x, forced, cache_hint=hint, launch_vpt=vpt)
+    torch.cuda.synchronize()
+    got = to_np(forced)
+    assert np.array_equal(to_np(auto), got, equal_nan=True)
+    p = D.build_plan(inp.start_step.astype(np.int64) + k, sp.steps, sp.num_buckets, table,
+                     inp.cfg_override, cov)
+    for i, r in oracle_step_M(inp, sig, p, k, x_in, list(range(sp.n))).items():
+        assert np.array_equal(got[i], r), f"sample {i} differs from mode M"
 
 
 def test_region_edge_cases():
@@ -224,9 +270,9 @@ def test_streaming_cache_hint_is_bit_identical(kw):
 # per-variant stage table beyond, and its full-stage form (no per-channel
 # bounds checks) when C is a multiple of two stages.  Every variant at each
 # shape: bit for bit equal to the cache-keep variant on every sample, and to
-# mode M on two.  (Lanes take one vector each here: several vectors per lane,
-# with the next one's head stage prefetched, only come with grids beyond 2^22
-# workgroups, which no test here reaches.)
+# mode M on two.  (Lanes take one vector each here; several vectors per lane,
+# with the next one's head stage prefetched, are forced through the launch
+# shape in test_multi_vector_lanes_match_mirror.)
 STREAM_SHAPES = [
     (4, 16, 16, 32),   # the stage table's shape, full stages
     (3, 5, 16, 24),    # width-4 variants fall back; width 2 ends on a 1-channel stage

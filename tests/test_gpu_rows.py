@@ -96,13 +96,13 @@ class Case:
                            None if self.xo is None else self.xo[i].astype(np.float64),
                            None if self.mask is None else self.mask[i, 0])
 
-    def call(self, phase, x, out, rows, d=None, x_tilde=None, cache_hint=0):
+    def call(self, phase, x, out, rows, d=None, x_tilde=None, cache_hint=0, launch_vpt=0):
         from bucketed_classifier_free_amd import api
         api.guided_step_rows(x, out, _dev(rows, self.dtype), self.d_sig, n_active=self.plan.n_active,
                              phase=phase, d=d, x_tilde=x_tilde,
                              x_orig=None if self.xo is None else _dev(self.xo, self.dtype),
                              mask=None if self.mask is None else _dev(self.mask),
-                             cache_hint=cache_hint, **self.d_plan)
+                             cache_hint=cache_hint, launch_vpt=launch_vpt, **self.d_plan)
 
 
 def _check_D(case, got, ref, tag):
@@ -119,12 +119,29 @@ KW = [dict(dtype="f32"), dict(dtype="bf16"), dict(dtype="f32", inpaint=True),
       dict(dtype="bf16", H=13, W=21, inpaint=True), dict(dtype="bf16", n=3, C=1, H=1, W=8)]
 
 
-@pytest.mark.parametrize("kw", KW)
+# The walk is a ring of four single-channel stages: channel counts that are not
+# a multiple of four end on a partial pass (C = 5, 6, 7, 9), with both cache
+# hints; lanes forced to take two or three vectors (ragged last pass).
+RING = [dict(dtype="f32", C=5), dict(dtype="bf16", C=6, inpaint=True, hint=1),
+        dict(dtype="f32", C=7, inpaint=True), dict(dtype="bf16", C=9, hint=1),
+        dict(dtype="bf16", C=5, inpaint=True, hint=1), dict(dtype="f32", C=9, inpaint=True, hint=1),
+        dict(dtype="bf16", C=7), dict(dtype="f32", C=6),
+        dict(dtype="bf16", C=16, H=40, W=64, vpt=2, hint=1), dict(dtype="f32", C=5, H=40, W=64, vpt=3),
+        dict(dtype="bf16", C=6, H=40, W=64, vpt=3, inpaint=True, hint=1)]
+
+
+def _opts(kw):
+    kw = dict(kw)
+    return kw.pop("hint", 0), kw.pop("vpt", 0), kw
+
+
+@pytest.mark.parametrize("kw", KW + RING)
 def test_rows_euler_matches_oracle(kw):
+    hint, vpt, kw = _opts(kw)
     case = Case(**kw).device()
     x = _dev(case.x, case.dtype)
     out = torch.full_like(x, float("nan"))
-    case.call("euler", x, out, case.pred)
+    case.call("euler", x, out, case.pred, cache_hint=hint, launch_vpt=vpt)
     torch.cuda.synchronize()
     got = to_np(out)
     for i in range(case.n):
@@ -138,17 +155,18 @@ def test_rows_euler_matches_oracle(kw):
         _check_D(case, got[i], ref_d, f"sample {i}")
 
 
-@pytest.mark.parametrize("kw", KW)
+@pytest.mark.parametrize("kw", KW + RING)
 def test_rows_heun_two_calls_match_oracle(kw):
+    hint, vpt, kw = _opts(kw)
     case = Case(**kw).device()
     rng = np.random.default_rng(99)
     x = _dev(case.x, case.dtype)
     xt = torch.full_like(x, float("nan"))
     d = torch.full(x.shape, float("nan"), dtype=torch.float32, device="cuda")
-    case.call("heun_predict", x, xt, case.pred, d=d)
+    case.call("heun_predict", x, xt, case.pred, d=d, cache_hint=hint, launch_vpt=vpt)
     rows2 = case.make_rows(rng)
     out = torch.full_like(x, float("nan"))
-    case.call("heun_correct", x, out, rows2, d=d, x_tilde=xt)
+    case.call("heun_correct", x, out, rows2, d=d, x_tilde=xt, cache_hint=hint, launch_vpt=vpt)
     torch.cuda.synchronize()
     g_xt, g_d, got = to_np(xt), d.cpu().numpy(), to_np(out)
     for i in range(case.n):

@@ -28,12 +28,12 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     lib = C.CDLL(L.LIB_PATH)
     for nm in names:
         assert hasattr(lib, nm), nm
     assert sorted(L.EXPORTS) == names
-    assert lib.bcg_abi_version() == L.ABI_VERSION == 8
+    assert lib.bcg_abi_version() == L.ABI_VERSION == 9
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
@@ -264,12 +264,12 @@ def test_loop_create_validates_device_plan_mode():
     plan = L.PlanIn(2, 10, 2, 4, 8, 8, 0, table.ctypes.data, None, None, None, None, None, None)
     step = L.StepArgs()
     step.n, step.C, step.H, step.W, step.num_sigmas, step.s2 = 2, 4, 8, 8, 11, 0.25
-    d = L.LoopDesc(plan, start.ctypes.data, 0, 1, None, None, 1, 0, 1, 0, 1, step, 1, 3, None,
+    d = L.LoopDesc(plan, start.ctypes.data, 0, 1, None, None, 1, 0, 1, 0, step, 1, 5000, None,
                    L.DevicePlan(0, 0, 0, _fake(1)))
     h = C.c_void_p()
     assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL   # dev_steps NULL
     d.dev_steps = _fake(2)
-    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL   # 3 not a multiple of 2
+    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL   # G beyond 4096
     assert b"graph_launches" in lib.bcg_last_error()
     d.device_plan, d.graph_launches = 0, 4                               # graphs need device plans
     d.host_slab = d.dev_slab = _fake(3)
@@ -501,3 +501,37 @@ def test_area_slices_round_exact_products_ties_up():
             y0 = min(max(m, 0), n - 1)
             assert tuple(got.region_box[j, 0]) == (y0, y0 + 1, 0, min(max(m, 1), n)), (n, f)
             assert tuple(got.region_box[j, 0]) == D.area_box(frac[j, 0], n, n)
+
+
+def test_dplan_step_rejects_plan_overlaps():
+    # The plan's workgroup of guided_step_dplan runs alongside the step: its
+    # outputs may not alias anything the step reads or writes, and nothing the
+    # step or the plan reads may alias the step's output.  Every call below is
+    # rejected before any launch.
+    lib = L.lib()
+    n, Cc, H, Wd = 2, 4, 8, 8
+    a = L.StepArgs()
+    a.n, a.C, a.H, a.W, a.num_sigmas, a.s2 = n, Cc, H, Wd, 11, 0.25
+    a.x, a.x_out, a.sigmas, a.mu_uncond, a.mu_cond = _fake(5), _fake(6), _fake(7), _fake(8), _fake(9)
+    # (pointer fields of a ctypes structure read back as ints)
+    d = L.DevicePlan(10, 4, 0, _fake(1), None, None, _fake(2), _fake(3))
+    cases = [("step_out", a.x + 16),          # plan output inside x
+             ("step_out", a.x_out),           # ... inside x_out
+             ("step_out", a.mu_cond + 4),     # ... inside a mean table
+             ("step_out", a.sigmas)]          # ... over the schedule
+    for field, ptr in cases:
+        setattr(d, field, C.c_void_p(ptr))
+        assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL, (field, ptr)
+        assert b"overlap" in lib.bcg_last_error()
+    d.step_out = _fake(3)
+    d.record_out = C.c_void_p(a.mu_uncond)     # records over the uncond means
+    d.record_in = _fake(11)
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlap" in lib.bcg_last_error()
+    d.record_out = _fake(12)
+    a.x_out = C.c_void_p(d.step_in)                  # the step's output over the plan's input
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlap" in lib.bcg_last_error()
+    a.x_out = C.c_void_p(a.mu_cond - 64)       # ... over a mean table the step reads
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlap" in lib.bcg_last_error()

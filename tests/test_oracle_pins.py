@@ -757,3 +757,30 @@ def test_area_box_rounds_exact_products_ties_up():
                     caught[name] += 1
     assert cases == 3 * sum(range(1, 257))
     assert all(v > 0 for v in caught.values()), caught
+
+
+def test_bf16_flip_carried_to_the_end_pins_the_final_bar():
+    # The Heun bf16 workload's one final element whose fp32 order (mode M,
+    # which the GPU reproduces bit for bit) and float64 definition (mode D)
+    # differ by more than max(2e-2, 1 bf16 ulp): sample 44, element
+    # (3, 26, 60).  The two trajectories take neighbouring bf16 codes at an
+    # early step while |x| is large (a one-ulp flip of a state of magnitude
+    # >= 4); the later steps carry it to the end, where it is 4 ulps of the
+    # final value and inside the carried-flip bound.
+    from gpu_helpers import bf16_ulp, storage_flip_bound
+    inp = W.make_inputs(W.config("throughput_bf16_heun"))
+    sub = inp.subset([44])
+    q = (0, 3, 26, 60)
+    xm, ms = M.trajectory32(sub, keep=True)
+    xd, ds = D.trajectory(sub, keep=True)
+    err = abs(float(xm[q]) - float(xd[q]))
+    assert (float(xd[q]), float(xm[q])) == (-1.46875, -1.5)
+    assert err > max(2e-2, float(bf16_ulp(xd[q])))
+    assert err <= storage_flip_bound(inp, 44)[q[1:]]
+    first = next(k for k in range(len(ms)) if ms[k][q] != ds[k][q])
+    assert abs(float(ds[first][q])) >= 4.0
+    assert abs(float(ms[first][q]) - float(ds[first][q])) == float(bf16_ulp(ds[first][q]))
+    # every other element of the sample is inside max(2e-2, 1 ulp), and all inside the bound
+    e = np.abs(xm.astype(np.float64) - xd)[0]
+    assert int((e > np.maximum(2e-2, bf16_ulp(xd[0]))).sum()) == 1
+    assert np.all(e <= storage_flip_bound(inp, 44))
