@@ -416,12 +416,14 @@ def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucke
                       region_range=None, covered_sets=None,
                       sampler: str, s2: float, feather: int = 0,
                       region_count=None, region_box=None, region_strength=None, mu_region=None,
-                      x_orig=None, mask=None, cache_hint: int = 0, stream=None):
-    """guided_step with the plan of the step built on the device, same launch."""
+                      x_orig=None, mask=None, cache_hint: int = 0, stats=None, workspace=None,
+                      launch_vpt: int = 0, stream=None):
+    """guided_step with the plan of the step built on the device, same launch.
+    ``stats`` ([n, 3]) with ``workspace`` computes the norm statistics inside the step."""
     a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, None, n_active=0, sampler=sampler,
                    s2=s2, feather=feather, region_count=region_count, region_box=region_box,
                    region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
-                   stats=None, workspace=None, cache_hint=cache_hint)
+                   stats=stats, workspace=workspace, cache_hint=cache_hint, launch_vpt=launch_vpt)
     if step_in.numel() != x.shape[0]:
         raise ValueError("step_in: needs one entry per sample")
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,

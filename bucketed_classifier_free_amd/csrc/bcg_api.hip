@@ -138,6 +138,50 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const StepParams p, co
     if (threadIdx.x < 3 && i >= 0 && i < p.n) stats[(int64_t)i * 3 + threadIdx.x] = part[threadIdx.x][0] / float(CH);
 }
 
+// Means of the row norms per sample from the step's own partials (p.stats_part):
+// one workgroup per sample the step's grid covers; a sample the step skipped
+// (inactive) is not written.  Slot (tile, group) of a sample holds the sums of
+// the row norms of one lane group; slots whose group has no row are never
+// written and are skipped.  Fixed strided sums, then a fixed-order tree.
+__global__ __launch_bounds__(256) void stats_slots_final_kernel(const StepParams p, int block, float* stats) {
+    __shared__ float part[3][256];
+    const int j = blockIdx.x;
+    const int i = p.identity ? j : p.order[j];
+    if (i < 0 || i >= p.n) return;
+    bool active;
+    if (p.record_in) {
+        active = (__float_as_uint(p.record_in[(int64_t)i * 4 + 3]) & 1u) != 0;
+    } else {
+        const int t = p.step_idx[i];
+        active = t >= 0 && t < p.t_end;
+    }
+    if (!active) return;
+    const int gpw = block / p.stats_group;  // lane groups per workgroup
+    const int nslot = p.tiles * gpw;
+    const float* s0 = p.stats_part + (int64_t)i * nslot * 3;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f;
+    for (int q = threadIdx.x; q < nslot; q += 256) {
+        const int tile = q / gpw, g = q - (q / gpw) * gpw;
+        if ((int64_t)tile * block * p.vpt + (int64_t)g * p.stats_group >= p.nvec) continue;
+        a0 += s0[q * 3 + 0];
+        a1 += s0[q * 3 + 1];
+        a2 += s0[q * 3 + 2];
+    }
+    part[0][threadIdx.x] = a0;
+    part[1][threadIdx.x] = a1;
+    part[2][threadIdx.x] = a2;
+    __syncthreads();
+    for (int s = 128; s >= 1; s >>= 1) {
+        if ((int)threadIdx.x < s) {
+            part[0][threadIdx.x] += part[0][threadIdx.x + s];
+            part[1][threadIdx.x] += part[1][threadIdx.x + s];
+            part[2][threadIdx.x] += part[2][threadIdx.x + s];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < 3) stats[(int64_t)i * 3 + threadIdx.x] = part[threadIdx.x][0] / float((int64_t)p.C * p.H);
+}
+
 // ------------------------------------------------------------ latent init
 
 template <typename T, int V>
@@ -332,11 +376,14 @@ void fill_dplan(StepParams& p, const bcg_device_plan* d) {
 
 using namespace bcg;
 
+// Stats workspace: the row norms of the two-pass form ([n][C][H][3]) or the
+// step's own partials ([n][tiles][groups][3]: a row per lane group, fewer
+// than H + 256 slots a sample with the last tile's unused groups).
 extern "C" size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype) {
     (void)W;
     (void)dtype;
     if (n <= 0 || C <= 0 || H <= 0) return 0;
-    return (size_t)n * C * H * 3 * sizeof(float);
+    return (size_t)n * (size_t)std::max<int64_t>((int64_t)C * H, (int64_t)H + 256) * 3 * sizeof(float);
 }
 
 namespace {
@@ -376,7 +423,6 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         if (rc) return rc;
         if (a->order || a->step_idx || a->scale || a->uncond_row)
             return fail(BCG_EINVAL, "%s: order/step_idx/scale/uncond_row come from the device plan and must be NULL", who);
-        if (a->stats) return fail(BCG_EINVAL, "%s: stats need the host plan", who);
         if (a->num_sigmas < d->steps + 1)
             return fail(BCG_EINVAL, "%s: num_sigmas %d < steps + 1 = %d", who, a->num_sigmas, d->steps + 1);
         if (a->max_regions > 0 && a->region_count && !d->covered && !(d->region_range && d->covered_sets))
@@ -446,15 +492,23 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
                 return fail(BCG_EINVAL, "%s: an input of the step or its plan overlaps x_out", who);
         }
     }
-    if (a->stats) {
-        const size_t need = guided_step_workspace_size(a->n_active, a->C, a->H, a->W, a->dtype);
-        if (!a->workspace || a->workspace_bytes < need)
-            return fail(BCG_EINVAL, "%s: stats need a workspace of %zu bytes", who, need);
-    }
     const bool inpaint = a->x_orig != nullptr;
     const int VV = a->dtype == BCG_BF16 ? 8 : 4;
     const bool vec = HW % VV == 0 && aligned16(a->x) && aligned16(a->x_out) &&
                      (!inpaint || (aligned16(a->x_orig) && aligned16(a->mask)));
+    // Statistics inside the step when a latent row is a power-of-two group of
+    // at most 64 lanes (W a multiple of the vector, W / vector a power of
+    // two); otherwise (host plans only) two extra kernels read x again.
+    const int row_lanes = vec && a->W % VV == 0 ? a->W / VV : 0;
+    const bool fused_stats = a->stats && row_lanes >= 1 && row_lanes <= 64 && (row_lanes & (row_lanes - 1)) == 0;
+    if (a->stats) {
+        if (d && !fused_stats)
+            return fail(BCG_EINVAL, "%s: stats with a device plan need W to be a power-of-two multiple (at most 64) "
+                        "of the %d-pixel vector, and 16-byte aligned arrays", who, VV);
+        const size_t need = guided_step_workspace_size(d ? a->n : a->n_active, a->C, a->H, a->W, a->dtype);
+        if (!a->workspace || a->workspace_bytes < need)
+            return fail(BCG_EINVAL, "%s: stats need a workspace of %zu bytes", who, need);
+    }
 
     StepParams p{};
     p.n = a->n; p.C = a->C; p.H = a->H; p.W = a->W; p.R = a->max_regions;
@@ -486,11 +540,18 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     p.vpt = shape.vpt;
     p.tiles = (int)(((int64_t)p.nvec + (int64_t)block * p.vpt - 1) / ((int64_t)block * p.vpt));
     if ((int64_t)p.n_active * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
+    if (fused_stats) {
+        const size_t need = (size_t)a->n * p.tiles * (block / row_lanes) * 3 * sizeof(float);
+        if (a->workspace_bytes < need)
+            return fail(BCG_EINVAL, "%s: stats need a workspace of %zu bytes", who, need);
+        p.stats_part = static_cast<float*>(a->workspace);
+        p.stats_group = row_lanes;
+    }
     if (d && (d->step_out || d->bucket_id || d->record_out))
         p.plan_block = (int)((int64_t)p.n_active * p.tiles);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    if (a->stats) {
+    if (a->stats && !fused_stats) {
         float* rows = static_cast<float*>(a->workspace);
         const int64_t nrows = (int64_t)p.n_active * p.C * p.H;
         const int g = (int)((nrows + 3) / 4);
@@ -504,13 +565,16 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     }
     const bool heun = a->sampler == BCG_HEUN;
     hipError_t e;
-    if (vec && a->cache_hint == BCG_CACHE_STREAM)
+    if (vec && a->cache_hint == BCG_CACHE_STREAM && !fused_stats)  // the statistics run on the keep variants
         e = a->dtype == BCG_BF16 ? launch_step_bf16_stream(p, heun, inpaint, block, st)
                                  : launch_step_f32_stream(p, heun, inpaint, block, st);
     else
         e = a->dtype == BCG_BF16 ? launch_step_bf16(p, vec, heun, inpaint, block, st)
                                  : launch_step_f32(p, vec, heun, inpaint, block, st);
-    return hip_status_of(e, who, "launch");
+    int rc = hip_status_of(e, who, "launch");
+    if (rc || !fused_stats) return rc;
+    hipLaunchKernelGGL(stats_slots_final_kernel, dim3(p.n_active), dim3(256), 0, st, p, block, a->stats);
+    return hip_status_of(hipGetLastError(), who, "stats launch");
 }
 
 }  // namespace

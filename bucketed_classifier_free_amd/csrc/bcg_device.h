@@ -185,6 +185,11 @@ struct StepParams {
     const uint16_t* covered_sets; // device plans with ranges: coverage of every region subset
     const float* record_in;       // [n][4] (sigma, sigma', scale, flags) per sample, or NULL
     float* record_out;            // plan workgroup: the records of the next step's indices
+    // Norm statistics inside the step (NULL: none): the first lane of each
+    // group of stats_group lanes (one latent row) writes the sums of its
+    // row norms of C, U and pred to slot (sample, tile, group), 3 floats.
+    float* stats_part;
+    int stats_group;
 };
 
 // Launch parameter block of the materialised-branch step (device pointers).

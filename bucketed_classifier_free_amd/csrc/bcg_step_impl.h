@@ -46,13 +46,15 @@ constexpr int kPlanLds = 4 * 2 * kSet;              // ints of the coefficient L
 
 // Compile-time tuning of the streaming loop (the stage width U is chosen per
 // kernel variant at launch, see stage_width).
-template <int U_, bool NT_, bool PF_ = false, bool FULL_ = false>
+template <int U_, bool NT_, bool PF_ = false, bool FULL_ = false, bool STATS_ = false>
 struct Tune {
     static constexpr int U = U_;        // channels per pipeline stage
     static constexpr bool NT = NT_;     // nontemporal (streaming) loads and stores
     static constexpr bool PF = PF_;     // next pass's head stage requested during this pass
     static constexpr bool FULL = FULL_; // C is a multiple of 2U: every stage is full
+    static constexpr bool STATS = STATS_;  // norm statistics of the first evaluation
 };
+typedef Tune<2, false, false, false, true> StatsTune;  // ordinary loads/stores, with the statistics
 typedef Tune<2, false> KeepTune;    // ordinary loads/stores (BCG_CACHE_KEEP)
 typedef Tune<2, true> StreamTune;   // nontemporal loads/stores (BCG_CACHE_STREAM)
 typedef KeepTune DefaultTune;
@@ -71,13 +73,23 @@ struct LaneState {
     float wh[NR > 0 ? NR : 1][V];  // normalised region weights
     float weff[V];                  // scale where covered, else 0
     bool sel[V];                    // scale-1 path: take c (else u)
+    bool cov[V];                    // some region has weight (the statistics' C is U elsewhere)
     float m[V], om[V];              // inpaint mask and 1 - mask
 };
 
-template <int V, int NR, int NRB, bool INP, bool ONE>
+// Norm statistics of one lane: sums of squares of C, U and pred over the
+// lane's pixels of the current channel (sq), and the running sums of the row
+// norms of its lane group (tot; every lane of a group holds the same values).
+struct LaneStats {
+    float sq[3];
+    float tot[3];
+};
+
+template <int V, int NR, int NRB, bool INP, bool ONE, bool ST = false>
 __device__ __forceinline__ float guided_pred(const LaneState<V, NR>& L, int e, float x, float xo,
                                              float a, float w, float bu, float bc,
-                                             const float (&br)[NRB > 0 ? NRB : 1]) {
+                                             const float (&br)[NRB > 0 ? NRB : 1],
+                                             LaneStats* st = nullptr) {
     const float u = __builtin_fmaf(a, x, bu);
     float c;
     if constexpr (NRB == 0) {
@@ -95,15 +107,21 @@ __device__ __forceinline__ float guided_pred(const LaneState<V, NR>& L, int e, f
         if constexpr (NRB == 0) pred = c;
         else pred = L.sel[e] ? c : u;
     }
+    if constexpr (ST) {  // C (U where no region has weight), U, and pred before the blend
+        const float cs = (NRB == 0 || L.cov[e]) ? c : u;
+        st->sq[0] = __builtin_fmaf(cs, cs, st->sq[0]);
+        st->sq[1] = __builtin_fmaf(u, u, st->sq[1]);
+        st->sq[2] = __builtin_fmaf(pred, pred, st->sq[2]);
+    }
     if constexpr (INP) pred = __builtin_fmaf(L.m[e], pred, L.om[e] * xo);
     return pred;
 }
 
-template <int V, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+template <int V, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL, bool ST = false>
 __device__ __forceinline__ void update_vec(const LaneState<V, NR>& L, const StepScalars& s,
                                            const float* __restrict__ coef, int c,
                                            const float (&xv)[V], const float (&ov)[V],
-                                           float (&out)[V]) {
+                                           float (&out)[V], LaneStats* st = nullptr) {
     const float bu = coef[c];
     const float bc = coef[BCG_MAX_CHANNELS + c];
     float br[NRB > 0 ? NRB : 1];
@@ -120,7 +138,7 @@ __device__ __forceinline__ void update_vec(const LaneState<V, NR>& L, const Step
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         const float x = xv[e];
-        const float pb = guided_pred<V, NR, NRB, INP, ONE>(L, e, x, ov[e], s.a, s.w, bu, bc, br);
+        const float pb = guided_pred<V, NR, NRB, INP, ONE, ST>(L, e, x, ov[e], s.a, s.w, bu, bc, br, st);
         if constexpr (FINAL) {
             out[e] = pb;
         } else if constexpr (!HEUN) {
@@ -169,10 +187,24 @@ __device__ __forceinline__ void load_stage(Stage<T, V, TN::U, INP>& sg, const T*
     }
 }
 
+// The row norms of one channel for the statistics: the lanes of a latent row
+// (a group of `group` lanes, a power of two) add their sums of squares in a
+// fixed butterfly, and each lane adds the square roots to its running sums.
+__device__ __forceinline__ void stats_rows(LaneStats& st, int group) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        float v = st.sq[q];
+        for (int o = group >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        st.tot[q] += sqrtf(v);
+        st.sq[q] = 0.0f;
+    }
+}
+
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
 __device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg, const LaneState<V, NR>& L,
                                               const StepScalars& s, const float* __restrict__ coef,
-                                              T* xd, int c0, int rot, int C, int64_t HW) {
+                                              T* xd, int c0, int rot, int C, int64_t HW, LaneStats* st,
+                                              int group) {
 #pragma unroll
     for (int u = 0; u < TN::U; ++u) {
         if (TN::FULL || c0 + u < C) {
@@ -184,8 +216,9 @@ __device__ __forceinline__ void compute_stage(const Stage<T, V, TN::U, INP>& sg,
 #pragma unroll
                 for (int e = 0; e < V; ++e) ov[e] = 0.f;
             }
-            update_vec<V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c, xv, ov, out);
+            update_vec<V, NR, NRB, INP, HEUN, ONE, FINAL, TN::STATS>(L, s, coef, c, xv, ov, out, st);
             Io<T, V>::template store<TN::NT>(xd + plane_offset(c, HW), out);
+            if constexpr (TN::STATS) stats_rows(*st, group);
         }
     }
 }
@@ -201,18 +234,18 @@ __device__ __forceinline__ bool channel_loop(Stage<T, V, TN::U, INP>& a, Stage<T
                                              const LaneState<V, NR>& L, const StepScalars& s,
                                              const float* __restrict__ coef, const T* xs, T* xd, const T* xo,
                                              const T* nxs, const T* nxo, int rot, int C, int64_t HW,
-                                             bool b_ready) {
+                                             bool b_ready, LaneStats* st, int group) {
     constexpr int U = TN::U;
     for (int c0 = 0;; c0 += 2 * U) {
         if (c0 + U < C) {
             if (c0 > 0 || !b_ready) load_stage<T, V, TN, INP>(b, xs, xo, c0 + U, rot, C, HW);
         }
         else if (nxs) load_stage<T, V, TN, INP>(b, nxs, nxo, 0, rot, C, HW);
-        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, rot, C, HW);
+        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, xd, c0, rot, C, HW, st, group);
         if (c0 + U >= C) return true;
         if (c0 + 2 * U < C) load_stage<T, V, TN, INP>(a, xs, xo, c0 + 2 * U, rot, C, HW);
         else if (nxs) load_stage<T, V, TN, INP>(a, nxs, nxo, 0, rot, C, HW);
-        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, xd, c0 + U, rot, C, HW);
+        compute_stage<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, xd, c0 + U, rot, C, HW, st, group);
         if (c0 + 2 * U >= C) return false;
     }
 }
@@ -238,6 +271,7 @@ __device__ __forceinline__ void finish_pixel(LaneState<V, NR>& L, int e, const f
     for (int r = 0; r < NRB; ++r) L.wh[r][e] = ws[r] * iw;
     L.weff[e] = cv ? w : 0.0f;
     L.sel[e] = keep_u ? cv : true;
+    L.cov[e] = cv;
 }
 
 // Region weights, coverage and mask of the V pixels starting at p0.  When
@@ -302,7 +336,8 @@ template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, 
 __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b,
                                          LaneState<V, NR>& L, const SampleRegions<NR>& sr,
                                          const StepParams& p, const StepScalars& s,
-                                         const float* __restrict__ coef, int i, int vi0, int rot, bool keep_u) {
+                                         const float* __restrict__ coef, int i, int vi0, int rot, bool keep_u,
+                                         LaneStats* st) {
     const int C = p.C;
     const int64_t sbase = (int64_t)i * C * p.HW;
     for (int v = 0; v < p.vpt; ++v) {
@@ -323,7 +358,8 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, Stage<T, V,
             setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
         }
         const bool in_b = channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, b, L, s, coef, xs, xd, xo,
-                                                                                  nxs, nxo, rot, C, p.HW, v == 0);
+                                                                                  nxs, nxo, rot, C, p.HW, v == 0,
+                                                                                  st, p.stats_group);
         if (more && in_b) a = b;
     }
 }
@@ -376,12 +412,26 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, Stage<T, 
     s.hh = s.h * 0.5f;
     const bool one = (s.w == 1.0f);
     const bool fin = (sgn == 0.0f);
+    LaneStats st = {{0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f}};
     if (one) {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
     } else {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
+    }
+    if constexpr (TN::STATS) {
+        // the first lane of each row group writes the group's sums of row
+        // norms: slot (sample, tile, group) of the partials
+        const int g = (int)threadIdx.x / p.stats_group;
+        if ((int)threadIdx.x == g * p.stats_group) {
+            const int tile = (int)blockIdx.x - (int)(blockIdx.x / p.tiles) * p.tiles;
+            const int64_t slot = ((int64_t)i * p.tiles + tile) * ((int)blockDim.x / p.stats_group) + g;
+            float* o = p.stats_part + slot * 3;
+            o[0] = st.tot[0];
+            o[1] = keep_u ? st.tot[1] : 0.0f;
+            o[2] = st.tot[2];
+        }
     }
 }
 
@@ -559,6 +609,12 @@ void launch_variant(const StepParams& p, dim3 grid, dim3 blk, hipStream_t st) {
     typedef StageTune<T, NR, INP, HEUN, NT> Wide;
     typedef Tune<Wide::U, NT, Wide::PF, true> WideFull;
     typedef Tune<2, NT, false> Narrow;
+    if constexpr (!NT && V > 1) {  // the statistics: ordinary loads and stores, two-channel stages
+        if (p.stats_part) {
+            hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, StatsTune>), grid, blk, 0, st, p);
+            return;
+        }
+    }
     if (p.C > 4 && p.C % (2 * Wide::U) == 0)
         hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, WideFull>), grid, blk, 0, st, p);
     else if (p.C > 4 && p.C >= 2 * Wide::U)

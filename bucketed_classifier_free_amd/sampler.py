@@ -211,7 +211,7 @@ class GuidedSampler:
                                 ranged=self.region_range is not None)
 
     def dplan_step(self, x, step_in, step_out=None, x_out=None, plan_out=None, cache_hint=0,
-                   record_in=None, record_out=None):
+                   record_in=None, record_out=None, stats=None, workspace=None, launch_vpt=0):
         """One fused step whose plan is built on the device from ``step_in``
         (device int32 [n]); ``step_out`` receives the next step indices.
         ``record_in`` / ``record_out`` (device float32 [n, 4]) carry the
@@ -226,7 +226,8 @@ class GuidedSampler:
                               sampler=self.sampler, s2=self.s2, feather=self.feather,
                               region_count=self.d_region_count, region_box=self.d_region_box,
                               region_strength=self.d_region_strength, mu_region=self.d_mu_region,
-                              x_orig=self.d_x_orig, mask=self.d_mask, cache_hint=cache_hint)
+                              x_orig=self.d_x_orig, mask=self.d_mask, cache_hint=cache_hint,
+                              stats=stats, workspace=workspace, launch_vpt=launch_vpt)
 
     def run(self, x=None, launches=None, callback=None, cancel=None):
         """Whole loop from the initial latent; returns the final state.

@@ -245,7 +245,15 @@ int bcg_plan_build(const bcg_plan_in* in, bcg_plan_out* out);
  * each box edge (weight (d+1)/F ... 1), separable in y and x.
  * Stats (optional): stats[i][0..2] = mean over (c, row) of the L2 norm over W
  * of C, U (0 if skipped) and pred (before the inpaint blend), from the first
- * evaluation; needs a device workspace of guided_step_workspace_size() bytes.
+ * evaluation ([B] section 4 stage 2: norms logged around the guidance); needs
+ * a device workspace of guided_step_workspace_size() bytes.  When W is a
+ * power-of-two multiple (at most 64) of the 16-byte vector and the arrays are
+ * 16-byte aligned, the step computes them itself: the lanes of a latent row
+ * sum their squares in a fixed butterfly, each row group writes the sums of
+ * its row norms to the workspace, and a second small kernel adds a sample's
+ * groups in a fixed order (the step then runs with ordinary loads and stores
+ * whatever cache_hint says).  Other shapes take two kernels that read x again
+ * before the step.
  * Errors: BCG_ESHAPE (sizes), BCG_EDTYPE (dtype), BCG_EINVAL (NULL pointer,
  * sampler, R > 0 without region arrays, inpaint arrays half given, stats
  * without workspace or with too small a workspace), BCG_EHIP.
@@ -392,12 +400,15 @@ int bcg_plan_device(int n, const bcg_device_plan* plan, void* stream);
  * plan (if requested) and step_out.  Results are bit-identical to
  * guided_step with the host plan of the same step indices.
  * args: as guided_step, except order, step_idx, scale and uncond_row must be
- * NULL and n_active is ignored; stats are not available (they need the plan
- * before the step); num_sigmas must be >= steps + 1; with regions
- * (max_regions > 0), plan->covered is required.
+ * NULL and n_active is ignored; num_sigmas must be >= steps + 1; with regions
+ * (max_regions > 0), plan->covered is required.  Stats (optional, as
+ * guided_step's) are computed inside the step, which needs W to be a
+ * power-of-two multiple, at most 64, of the 16-byte vector (4 fp32 or 8 bf16
+ * pixels) and 16-byte aligned arrays (else BCG_EINVAL).
  * Errors: as guided_step and bcg_plan_device.
  */
 int guided_step_dplan(const bcg_step_args* args, const bcg_device_plan* plan, void* stream);
+
 
 /*
  * guided_step_rows -- the guided update when the branch predictions are

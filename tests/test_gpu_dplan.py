@@ -335,3 +335,45 @@ def test_bench_loop_large_shape_matches_mirror():
     err = np.abs(to_np(x[1, idx]).astype(np.float64) - xd)
     for q in np.argwhere(err > np.maximum(2e-2, bf16_ulp(xd))):
         assert err[tuple(q)] <= storage_flip_bound(sub, int(q[0]), 12)[tuple(q[1:])]
+
+
+@pytest.mark.parametrize("name,records", [("mixed_bucket", False), ("mixed_bucket", True),
+                                          ("throughput_bf16_heun", True), ("large_bf16", True)])
+def test_dplan_norm_stats_inside_the_step(name, records):
+    """Norm statistics of a device-plan step, computed inside the step from
+    per-row-group partials (no second pass over x) and summed per sample in a
+    fixed order: within 1e-5 of the float64 definition, the step's output
+    unchanged, and equal bit for bit to the host-plan path's statistics (the
+    same grid when every sample is active)."""
+    from bucketed_classifier_free_amd import guided_step_workspace_size
+    inp = W.make_inputs(W.config(name))
+    sp = inp.spec
+    s = _sampler(inp, wrap=True)
+    sig, table, cov = D.run_setup(inp)
+    x = s.init_state()
+    k = 3
+    t = s.step_indices(k)
+    ws = torch.empty(guided_step_workspace_size(sp.n, sp.C, sp.H, sp.W) // 4 + 1, device="cuda")
+    st_d = torch.full((sp.n, 3), float("nan"), device="cuda")
+    st_h = torch.full((sp.n, 3), float("nan"), device="cuda")
+    yd, y0, yh = (torch.full_like(x, float("nan")) for _ in range(3))
+    kw = dict(record_in=torch.from_numpy(s.records(k)).cuda()) if records else {}
+    s.dplan_step(x, _i32(t), None, x_out=yd, stats=st_d, workspace=ws, **kw)
+    s.dplan_step(x, _i32(t), None, x_out=y0, **kw)
+    p = s.step(k, x, yh, stats=st_h, workspace=ws)
+    torch.cuda.synchronize()
+    bits = torch.int16 if sp.dtype == "bf16" else torch.int32
+    assert torch.equal(yd.view(bits), y0.view(bits)) and torch.equal(yd.view(bits), yh.view(bits))
+    got = to_np(st_d)
+    if p.n_active == sp.n:
+        assert np.array_equal(got, to_np(st_h))
+    plan = D.build_plan(t, sp.steps, sp.num_buckets, table, inp.cfg_override, cov)
+    x_np = to_np(x)
+    idx = range(sp.n) if sp.n <= 64 else [0, 37, 101, 255]
+    for i in idx:
+        if plan["bucket_id"][i] < 0:
+            assert np.isnan(got[i]).all()
+            continue
+        ref = D.norm_stats(x_np[i].astype(np.float64), float(sig[t[i]]), float(plan["scale"][i]),
+                           D.sample_params(inp, i), bool(plan["need_uncond"][i]))
+        np.testing.assert_allclose(got[i], ref, rtol=1e-5, atol=1e-6)

@@ -425,6 +425,50 @@ def test_norm_stats_match_oracle(kw):
         np.testing.assert_allclose(got[i], ref, rtol=1e-5, atol=1e-6)
 
 
+FUSED_STATS = [dict(dtype="bf16", regions=2, H=12, W=128),              # 16 lanes a row
+               dict(dtype="f32", regions=3, inpaint=True, H=9, W=128),  # 32 lanes a row
+               dict(dtype="bf16", sampler="heun", H=20, W=32),           # 4 lanes a row
+               dict(dtype="f32", regions=1, sampler="heun", H=7, W=4),   # 1 lane a row
+               dict(dtype="bf16", regions=4, inpaint=True, H=40, W=64, vpt=2),
+               dict(dtype="f32", regions=2, H=64, W=256, vpt=3)]         # 64 lanes a row
+
+
+@pytest.mark.parametrize("kw", FUSED_STATS)
+def test_fused_norm_stats_match_oracle(kw):
+    # Shapes whose latent rows are power-of-two lane groups: the statistics
+    # come from the step itself (no second pass over x); the step's output is
+    # the same as without them, bit for bit.
+    from bucketed_classifier_free_amd import guided_step_workspace_size
+    kw = dict(kw)
+    vpt = kw.pop("vpt", 0)
+    inp = W.make_inputs(W.small_spec(n=5, C=3, steps=5, skip_frac=0.4, **kw))
+    sp = inp.spec
+    s = _sampler(inp)
+    sig, table, cov = D.run_setup(inp)
+    x = s.init_state()
+    x_np = to_np(x)
+    stats = torch.full((sp.n, 3), float("nan"), device="cuda")
+    ws = torch.empty(guided_step_workspace_size(sp.n, sp.C, sp.H, sp.W) // 4 + 1, device="cuda")
+    y, y0 = torch.full_like(x, float("nan")), torch.full_like(x, float("nan"))
+    k = 1
+    p = s.step(k, x, y, stats=stats, workspace=ws, launch_vpt=vpt)
+    s.step(k, x, y0, launch_vpt=vpt)
+    torch.cuda.synchronize()
+    bits = torch.int16 if sp.dtype == "bf16" else torch.int32
+    assert torch.equal(y.view(bits), y0.view(bits))
+    got = to_np(stats)
+    dplan = D.build_plan(inp.start_step.astype(np.int64) + k, sp.steps, sp.num_buckets, table,
+                         inp.cfg_override, cov)
+    for i in range(sp.n):
+        if p.bucket_id[i] < 0:
+            assert np.isnan(got[i]).all()
+            continue
+        t = int(inp.start_step[i]) + k
+        ref = D.norm_stats(x_np[i].astype(np.float64), float(sig[t]), float(p.scale[i]),
+                           D.sample_params(inp, i), bool(dplan["need_uncond"][i]))
+        np.testing.assert_allclose(got[i], ref, rtol=1e-5, atol=1e-6)
+
+
 # ---------------------------------------------------------------- standalone kernels
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
