@@ -10,7 +10,8 @@ fallback implementation).
 from . import _lib
 from ._lib import BCGError
 from .api import (Plan, area_accumulate, bcg_plan_build, bcg_plan_device, bucket_bounds, bucket_table,
-                  guided_step, guided_step_dplan, guided_step_rows, guided_step_rows_dplan,
+                  guided_step, guided_step_dplan, guided_step_dplan_static, guided_step_rows,
+                  guided_step_rows_dplan,
                   guided_step_workspace_size,
                   latent_init, mask_blend, sigma_crop, sigma_schedule, WeightPatch, weight_patch)
 from .sampler import GuidedSampler, Interrupted
@@ -22,6 +23,6 @@ def load():
 
 __all__ = ["BCGError", "Plan", "GuidedSampler", "Interrupted", "area_accumulate",
            "bcg_plan_build", "bcg_plan_device", "bucket_bounds", "bucket_table", "guided_step",
-           "guided_step_dplan", "guided_step_rows", "guided_step_rows_dplan", "guided_step_workspace_size",
+           "guided_step_dplan", "guided_step_dplan_static", "guided_step_rows", "guided_step_rows_dplan", "guided_step_workspace_size",
            "latent_init",
            "mask_blend", "sigma_crop", "sigma_schedule", "WeightPatch", "weight_patch"]

@@ -21,6 +21,7 @@ BCG_MAX_FEATHER = 64
 BCG_MAX_DEVICE_BUCKETS = 1024
 BCG_MAX_DEVICE_STEPS = 1 << 20
 BCG_MAX_PATCHES = 8
+BCG_STATIC_SCRATCH_BYTES = 4 << 20
 BCG_PATCH = {"diff": 0, "lowrank": 1}
 BCG_ROUND = {"nearest": 0, "stochastic": 1}
 ABI_VERSION = 9
@@ -29,7 +30,8 @@ ABI_VERSION = 9
 EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "sigma_crop", "bucket_table",
            "bucket_bounds",
            "bcg_plan_build", "guided_step", "guided_step_workspace_size", "latent_init",
-           "area_accumulate", "mask_blend", "bcg_plan_records", "bcg_plan_device", "guided_step_dplan", "guided_step_rows",
+           "area_accumulate", "mask_blend", "bcg_plan_records", "bcg_plan_device", "guided_step_dplan",
+           "guided_step_dplan_static", "guided_step_rows",
            "guided_step_rows_dplan",
            "bcg_loop_create", "bcg_loop_run", "bcg_loop_last_run", "bcg_loop_destroy", "weight_patch"]
 
@@ -135,6 +137,7 @@ def lib():
         L.guided_step_rows.argtypes = [C.POINTER(RowsArgs), vp]
         L.guided_step_rows_dplan.argtypes = [C.POINTER(RowsArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
+        L.guided_step_dplan_static.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
         L.guided_step_workspace_size.argtypes = [C.c_int] * 5
         L.guided_step_workspace_size.restype = C.c_size_t
         L.latent_init.argtypes = [C.c_int] * 5 + [vp, vp, vp, C.c_int, vp, vp, vp]

@@ -181,7 +181,7 @@ def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
 
 def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sampler, s2, feather,
                region_count, region_box, region_strength, mu_region, x_orig, mask, stats,
-               workspace, cache_hint, region_range=None, steps=0, launch_vpt=0):
+               workspace, cache_hint, region_range=None, steps=0, launch_vpt=0, static_scratch=False):
     """Checks the tensors of a guided step and packs them into StepArgs.
     ``plan_rows`` = (order, step_idx, scale, uncond_row) or None (device plan)."""
     _dev(x, "x")
@@ -227,8 +227,9 @@ def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sam
     wsb = 0
     if stats is not None:
         _dev(stats, "stats", torch.float32, (n, 3))
-        _dev(workspace, "workspace")
-        wsb = workspace.numel() * workspace.element_size()
+        if not static_scratch:  # the static entry point brings its own
+            _dev(workspace, "workspace")
+            wsb = workspace.numel() * workspace.element_size()
     if sampler not in _SAMPLER:
         raise ValueError(f"unknown sampler {sampler!r}")
     if region_range is not None:
@@ -431,6 +432,31 @@ def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucke
                     record_in=record_in, record_out=record_out, region_range=region_range,
                     covered_sets=covered_sets, region_count=region_count)
     L.check(L.lib().guided_step_dplan(ct.byref(a), ct.byref(d), _stream(stream)))
+
+
+
+def guided_step_dplan_static(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucket_cfg, step_in,
+                             step_out=None, cfg_override=None, covered=None, wrap: bool = False,
+                             plan_out=None, bucket_cfg_end=None, record_in=None, record_out=None,
+                             region_range=None, covered_sets=None,
+                             sampler: str, s2: float, feather: int = 0,
+                             region_count=None, region_box=None, region_strength=None, mu_region=None,
+                             x_orig=None, mask=None, cache_hint: int = 0, stats=None,
+                             launch_vpt: int = 0, stream=None):
+    """guided_step_dplan for callers that cannot allocate: the statistics'
+    partials go to the library's static scratch (no workspace argument)."""
+    a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, None, n_active=0, sampler=sampler,
+                   s2=s2, feather=feather, region_count=region_count, region_box=region_box,
+                   region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
+                   stats=stats, workspace=None, cache_hint=cache_hint, launch_vpt=launch_vpt,
+                   static_scratch=True)
+    if step_in.numel() != x.shape[0]:
+        raise ValueError("step_in: needs one entry per sample")
+    d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
+                    covered=covered, wrap=wrap, out=plan_out, bucket_cfg_end=bucket_cfg_end,
+                    record_in=record_in, record_out=record_out, region_range=region_range,
+                    covered_sets=covered_sets, region_count=region_count)
+    L.check(L.lib().guided_step_dplan_static(ct.byref(a), ct.byref(d), _stream(stream)))
 
 
 def latent_init(noise, sigmas, step_idx, x_out, latent=None, stream=None):

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "bcg_common.h"
 #include "bcg_device.h"
@@ -394,7 +395,8 @@ int hip_status_of(hipError_t e, const char* who, const char* what) {
 }
 
 // guided_step with the host plan (d == NULL) or a device-built one (d).
-int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, const char* who) {
+int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, const char* who,
+              bool static_ws = false) {
     if (!a) return fail(BCG_EINVAL, "%s: args is NULL", who);
     if (a->n < 0 || a->C < 1 || a->C > BCG_MAX_CHANNELS || a->H < 1 || a->W < 1)
         return fail(BCG_ESHAPE, "%s: bad shape n=%d C=%d H=%d W=%d (C must be in [1, %d])", who,
@@ -506,7 +508,7 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
             return fail(BCG_EINVAL, "%s: stats with a device plan need W to be a power-of-two multiple (at most 64) "
                         "of the %d-pixel vector, and 16-byte aligned arrays", who, VV);
         const size_t need = guided_step_workspace_size(d ? a->n : a->n_active, a->C, a->H, a->W, a->dtype);
-        if (!a->workspace || a->workspace_bytes < need)
+        if (!a->workspace || (!static_ws && a->workspace_bytes < need))
             return fail(BCG_EINVAL, "%s: stats need a workspace of %zu bytes", who, need);
     }
 
@@ -542,8 +544,12 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     if ((int64_t)p.n_active * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
     if (fused_stats) {
         const size_t need = (size_t)a->n * p.tiles * (block / row_lanes) * 3 * sizeof(float);
-        if (a->workspace_bytes < need)
+        if (a->workspace_bytes < need) {
+            if (static_ws)
+                return fail(BCG_EINVAL, "%s: the statistics of %d samples at this shape need %zu bytes, more than "
+                            "the library's static scratch of %zu bytes", who, a->n, need, a->workspace_bytes);
             return fail(BCG_EINVAL, "%s: stats need a workspace of %zu bytes", who, need);
+        }
         p.stats_part = static_cast<float*>(a->workspace);
         p.stats_group = row_lanes;
     }
@@ -588,6 +594,54 @@ extern "C" int guided_step_dplan(const bcg_step_args* a, const bcg_device_plan* 
     bcg::clear_error();
     if (!d) return fail(BCG_EINVAL, "guided_step_dplan: plan is NULL");
     return step_impl(a, d, stream, "guided_step_dplan");
+}
+
+// The statistics' partials of guided_step_dplan_static: one array per GPU, part
+// of the library's code object (no allocation call), held until the process ends.
+static __device__ __align__(256) float scratch[BCG_STATIC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept; the host-side name is only a stand-in
+// and is never passed to a kernel.
+int scratch_address(float** out, const char* who) {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static float* addr[kDevices] = {};
+    int dev = 0;
+    int rc = hip_status_of(hipGetDevice(&dev), who, "hipGetDevice");
+    if (rc) return rc;
+    if (dev < 0 || dev >= kDevices) return fail(BCG_EINVAL, "%s: device %d beyond %d", who, dev, kDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        rc = hip_status_of(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), who, "hipGetSymbolAddress(scratch)");
+        if (rc) return rc;
+        if (!ptr) return fail(BCG_EHIP, "%s: no device address for the static scratch", who);
+        addr[dev] = static_cast<float*>(ptr);
+    }
+    *out = addr[dev];
+    return BCG_OK;
+}
+
+}  // namespace
+
+extern "C" int guided_step_dplan_static(const bcg_step_args* a, const bcg_device_plan* d, void* stream) {
+    bcg::clear_error();
+    const char* who = "guided_step_dplan_static";
+    if (!a) return fail(BCG_EINVAL, "%s: args is NULL", who);
+    if (!d) return fail(BCG_EINVAL, "%s: plan is NULL", who);
+    if (a->workspace || a->workspace_bytes)
+        return fail(BCG_EINVAL, "%s: workspace must be NULL (the library's static scratch is used)", who);
+    if (!a->stats) return step_impl(a, d, stream, who);
+    float* ptr = nullptr;
+    const int rc = scratch_address(&ptr, who);
+    if (rc) return rc;
+    bcg_step_args b = *a;
+    b.workspace = ptr;
+    b.workspace_bytes = BCG_STATIC_SCRATCH_BYTES;
+    return step_impl(&b, d, stream, who, true);
 }
 
 // Parameters of a plan built on its own (no step in the same workgroup).

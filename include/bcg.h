@@ -409,6 +409,24 @@ int bcg_plan_device(int n, const bcg_device_plan* plan, void* stream);
  */
 int guided_step_dplan(const bcg_step_args* args, const bcg_device_plan* plan, void* stream);
 
+/*
+ * guided_step_dplan_static -- guided_step_dplan for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): args->workspace must be NULL and
+ * workspace_bytes 0, and the statistics' partials (when args->stats is given)
+ * go to a scratch array of the library's own, BCG_STATIC_SCRATCH_BYTES on each
+ * GPU, part of the library's code object and held until the process ends; no
+ * allocation or free is made.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams) race.  Every partial a
+ * call reads is written earlier in the same call, so nothing needs clearing
+ * between calls.  Results are bit-identical to guided_step_dplan with a
+ * workspace.
+ * Errors: as guided_step_dplan; BCG_EINVAL when a workspace is given or the
+ * partials of this call (n * tiles * row groups * 12 bytes, at most
+ * guided_step_workspace_size) exceed BCG_STATIC_SCRATCH_BYTES.
+ */
+#define BCG_STATIC_SCRATCH_BYTES (4u << 20)
+int guided_step_dplan_static(const bcg_step_args* args, const bcg_device_plan* plan, void* stream);
 
 /*
  * guided_step_rows -- the guided update when the branch predictions are
