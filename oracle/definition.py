@@ -687,6 +687,110 @@ def trajectory(inp, storage: str | None = None, launches: int | None = None,
     return (x, states) if keep else x
 
 
+# --------------------------------------------------------------------------
+# Continuous batching: slots refilled from a queue of requests
+# --------------------------------------------------------------------------
+
+
+def serve_schedule(start, steps: int, n_slots: int, n_requests: int, launches: int, ring: bool = False):
+    """Which request each slot of a continuously batched loop holds at each
+    launch, the step it takes there, and whether it joins at that launch.
+
+    SGLang write-up section 3 (one batch carries samples of several buckets)
+    and section 4 stage 3 (the scheduler builds each step's plan; samples move
+    between buckets from step to step).  The pages describe the mixed batch,
+    not how it is refilled.  Reading: slots 0..n_slots-1 begin with requests
+    0..n_slots-1 at their start steps (each in [0, steps)); a request takes
+    one step per launch; after the launch in which a request takes its last
+    step, its slot takes the next request of the queue at the next launch
+    (the freed slots in index order take the queued requests in id order),
+    and that request joins at step 0 from its own noise; once the queue is
+    exhausted a freed slot stays empty.  With ``ring`` the queue never ends:
+    request ids run modulo n_requests (a fixed pool served over and over).
+
+    Returns int arrays req[launches, n_slots] and t[launches, n_slots] (-1 in
+    both where the slot is empty) and a bool array join[launches, n_slots]
+    (the request's state is initialised before its step at that launch; every
+    initial request joins at launch 0).
+    """
+    start = np.asarray(start, np.int64)
+    if n_requests < n_slots:
+        raise ValueError("fewer requests than slots")
+    if ((start[:n_slots] < 0) | (start[:n_slots] >= steps)).any():
+        raise ValueError("initial start steps must lie in [0, steps)")
+    req = np.full((launches, n_slots), -1, np.int64)
+    tt = np.full((launches, n_slots), -1, np.int64)
+    join = np.zeros((launches, n_slots), bool)
+    cur_r = np.arange(n_slots, dtype=np.int64)
+    cur_t = start[:n_slots].copy()
+    cur_j = np.ones(n_slots, bool)
+    nxt = n_slots
+    for k in range(launches):
+        if k > 0:
+            for s in range(n_slots):
+                if cur_r[s] < 0 or cur_t[s] >= steps:  # empty, or its request has finished
+                    if ring or nxt < n_requests:
+                        cur_r[s] = nxt % n_requests if ring else nxt
+                        cur_t[s] = 0
+                        cur_j[s] = True
+                        nxt += 1
+                    else:
+                        cur_r[s] = -1
+                        cur_t[s] = -1
+        req[k], tt[k], join[k] = cur_r, cur_t, cur_j
+        for s in range(n_slots):
+            if cur_r[s] >= 0:
+                cur_t[s] += 1
+                cur_j[s] = False
+    return req, tt, join
+
+
+def init_sample(inp, i: int, sigma: float, storage: str):
+    """Request i's state when it joins at noise level sigma: its latent (the
+    original latent when inpainting, else zero) plus its noise times sigma,
+    stored in the storage dtype (the rule of init_latent for one sample)."""
+    x = np.asarray(inp.noise[i], np.float64) * float(sigma)
+    if inp.x_orig is not None:
+        x = stored_orig(inp)[i] + x
+    return to_storage(x, storage)
+
+
+def serve_trajectory(inp, n_slots: int, launches: int, ring: bool = False, slots=None, keep=False):
+    """Mode D of a continuously batched loop over the request pool ``inp``
+    (inp.spec.n requests; the first n_slots' start steps are the initial
+    progress): at each launch the plan of the slots' steps (each slot with its
+    request's override and coverage), then every active slot in ``slots``
+    (default all) takes its step, after joining if it joins there.  Returns
+    the final slot states and, with ``keep``, the state after every launch,
+    plus the schedule.  Validity ranges are not part of this mode."""
+    sp = inp.spec
+    if inp.region_range is not None:
+        raise ValueError("continuous batching takes no validity ranges")
+    sig, table, cov = run_setup(inp)
+    sig64 = sig.astype(np.float64)
+    req, tt, join = serve_schedule(inp.start_step, sp.steps, n_slots, sp.n, launches, ring)
+    x = np.zeros((n_slots, sp.C, sp.H, sp.W))
+    states = []
+    idx = range(n_slots) if slots is None else slots
+    ov = np.asarray(inp.cfg_override, np.float32)
+    for k in range(launches):
+        r = req[k]
+        ovk = np.where(r >= 0, ov[np.maximum(r, 0)], np.float32(np.nan)).astype(np.float32)
+        plan = build_plan(tt[k], sp.steps, sp.num_buckets, table, ovk, cov[np.maximum(r, 0)],
+                          table_end(inp))
+        for s in idx:
+            if r[s] < 0 or plan["bucket_id"][s] < 0:
+                continue
+            ti = int(tt[k, s])
+            if join[k, s]:
+                x[s] = init_sample(inp, int(r[s]), sig64[ti], sp.dtype)
+            x[s] = to_storage(step(x[s], sig64[ti], sig64[ti + 1], float(plan["scale"][s]),
+                                   sample_params(inp, int(r[s])), sp.sampler), sp.dtype)
+        if keep:
+            states.append(x.copy())
+    return x, states, (req, tt, join)
+
+
 def pf_ode_exact(x, sigma: float, sigma_next: float, mean, s2: float):
     """Exact probability-flow solution for Gaussian data N(mean, s^2).
 

@@ -247,6 +247,48 @@ def trajectory32(inp, launches=None, samples=None, keep=False):
     return (x, states) if keep else x
 
 
+def init_sample32(inp, i, sigma):
+    """Request i's joining state in mode M (init_latent32's rule for one sample)."""
+    sp = inp.spec
+    z = np.float32(sigma)
+    if inp.x_orig is not None:
+        x = fma32(inp.noise[i], np.full(inp.noise[i].shape, z, np.float32), _store(inp.x_orig[i], sp.dtype))
+    else:
+        x = inp.noise[i].astype(np.float32) * z
+    return _store(x, sp.dtype)
+
+
+def serve_trajectory32(inp, n_slots, launches, ring=False, slots=None, keep=False):
+    """The continuously batched loop in mode M (the schedule and plans of
+    definition.serve_trajectory)."""
+    sp = inp.spec
+    sig, table, cov = D.run_setup(inp)
+    req, tt, join = D.serve_schedule(inp.start_step, sp.steps, n_slots, sp.n, launches, ring)
+    x = np.zeros((n_slots, sp.C, sp.H, sp.W), np.float32)
+    states = []
+    idx = range(n_slots) if slots is None else slots
+    ov = np.asarray(inp.cfg_override, np.float32)
+    prms = {}
+    for k in range(launches):
+        r = req[k]
+        ovk = np.where(r >= 0, ov[np.maximum(r, 0)], np.float32(np.nan)).astype(np.float32)
+        plan = D.build_plan(tt[k], sp.steps, sp.num_buckets, table, ovk, cov[np.maximum(r, 0)],
+                            D.table_end(inp))
+        for s in idx:
+            if r[s] < 0 or plan["bucket_id"][s] < 0:
+                continue
+            ri, ti = int(r[s]), int(tt[k, s])
+            if ri not in prms:
+                prms[ri] = params32(inp, ri)
+            if join[k, s]:
+                x[s] = init_sample32(inp, ri, sig[ti])
+            x[s] = _store(step32(x[s], sig[ti], sig[ti + 1], plan["scale"][s],
+                                 bool(plan["need_uncond"][s]), prms[ri], sp.sampler), sp.dtype)
+        if keep:
+            states.append(x.copy())
+    return x, states, (req, tt, join)
+
+
 def area_accumulate32(crops, boxes, strengths, H, W, F, fallback=None):
     """Standalone regional accumulation in mode M.
 

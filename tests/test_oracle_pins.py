@@ -784,3 +784,74 @@ def test_bf16_flip_carried_to_the_end_pins_the_final_bar():
     e = np.abs(xm.astype(np.float64) - xd)[0]
     assert int((e > np.maximum(2e-2, bf16_ulp(xd[0]))).sum()) == 1
     assert np.all(e <= storage_flip_bound(inp, 44))
+
+
+# ---------------------------------------------------------------- continuous batching
+
+def _schedule_by_events(start, steps, n, Q, L, ring):
+    """The same schedule from events: a heap of (launch at which a slot is free
+    again, slot); each event takes the next request for `steps` launches."""
+    import heapq
+    req = np.full((L, n), -1, np.int64)
+    tt = np.full((L, n), -1, np.int64)
+    join = np.zeros((L, n), bool)
+    spans = [(s, s, 0, int(start[s])) for s in range(n)]
+    heap = [(steps - int(start[s]), s) for s in range(n)]
+    heapq.heapify(heap)
+    nxt = n
+    while heap:
+        k, s = heapq.heappop(heap)
+        if k >= L or (not ring and nxt >= Q):
+            continue
+        spans.append((s, nxt % Q if ring else nxt, k, 0))
+        nxt += 1
+        heapq.heappush(heap, (k + steps, s))
+    for s, r, k0, t0 in spans:
+        for j in range(steps - t0):
+            if k0 + j < L:
+                req[k0 + j, s], tt[k0 + j, s], join[k0 + j, s] = r, t0 + j, j == 0
+    return req, tt, join
+
+
+def test_serve_schedule_matches_event_simulation():
+    rng = np.random.default_rng(77)
+    for _ in range(300):
+        n = int(rng.integers(1, 6))
+        Q = int(rng.integers(n, 3 * n + 2))
+        steps = int(rng.integers(1, 7))
+        L = int(rng.integers(1, 4 * steps + 6))
+        ring = bool(rng.integers(0, 2))
+        start = rng.integers(0, steps, n)
+        got = D.serve_schedule(start, steps, n, Q, L, ring)
+        want = _schedule_by_events(start, steps, n, Q, L, ring)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w), (n, Q, steps, L, ring, start)
+    # a drained queue: every request served once, for steps - start launches
+    start = np.array([2, 0, 3])
+    req, tt, join = D.serve_schedule(start, 4, 3, 8, 20)
+    served = {int(r): int((req == r).sum()) for r in np.unique(req[req >= 0])}
+    assert sorted(served) == list(range(8))
+    assert all(served[r] == (4 - start[r] if r < 3 else 4) for r in served)
+    assert (req[-1] == -1).all() and int(join.sum()) == 8
+
+
+@pytest.mark.parametrize("kw", [dict(dtype="f32", regions=2, inpaint=True),
+                                dict(dtype="bf16", sampler="heun", regions=1)])
+def test_served_requests_equal_their_solo_runs(kw):
+    # Per-request independence through the queue: each request's state after
+    # its last step equals its own trajectory run alone (from its start step,
+    # or 0 when it came from the queue), bit for bit, in both modes.
+    sp = W.small_spec(n=7, C=2, H=8, W=16, steps=4, num_buckets=3, feather=2, **kw)
+    inp = W.make_inputs(sp)
+    n_slots, L = 3, 12
+    xd, dstates, (req, tt, join) = D.serve_trajectory(inp, n_slots, L, keep=True)
+    xm, mstates, _ = M.serve_trajectory32(inp, n_slots, L, keep=True)
+    for r in range(sp.n):
+        where = np.argwhere((req == r) & (tt == sp.steps - 1))
+        assert len(where) == 1, r
+        k, s = (int(v) for v in where[0])
+        solo = inp.subset([r])
+        solo.start_step[:] = inp.start_step[r] if r < n_slots else 0
+        left = sp.steps - int(solo.start_step[0])
+        assert np.array_equal(dstates[k][s], D.trajectory(solo, launches=left)[0]), r
+        assert np.array_equal(mstates[k][s], M.trajectory32(solo, launches=left)[0]), r
