@@ -36,7 +36,8 @@ METRIC = "latent element-steps/sec on 1 GPU + achieved HBM GB/s as % of peak"
 PEAK_HBM_GBS = 8000.0
 # the bench kernel's device code and its launch shape (a traffic record is
 # void once any of them changes)
-KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_plan_dev.h", "bcg_launch.h", "bcg_step_bf16_nt.hip"]
+KERNEL_SOURCES = ["bcg_step_impl.h", "bcg_device.h", "bcg_plan_dev.h", "bcg_launch.h", "bcg_step_bf16_nt.hip",
+                  "bcg_step_bf16_queue.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "guided_step_large_bf16_traffic.json")
 
 
@@ -521,6 +522,12 @@ def main():
     ap.add_argument("--upload-batch", type=int, default=8)
     ap.add_argument("--async-upload", type=int, default=0)
     ap.add_argument("--plan", choices=("device", "host"), default="device")
+    ap.add_argument("--join-front", type=int, default=-1, metavar="J",
+                    help="continuous batching: joins of a step dispatched first (-1: the loop's default)")
+    ap.add_argument("--queue", type=int, default=512, metavar="Q",
+                    help="continuous batching (device plans): the batch's slots are refilled from an "
+                         "endless queue over a pool of Q requests (0: every finished slot restarts "
+                         "at step 0 from its own latent instead)")
     ap.add_argument("--records", type=int, default=1,
                     help="device plans: each launch's plan writes the next step's sample records")
     ap.add_argument("--graph", type=int, default=40, metavar="G",
@@ -593,17 +600,28 @@ def main():
     if args.rows:
         rows_bench(inp, args)
         return
-    s = GuidedSampler.from_inputs(inp, wrap=True)
     R = max(1, args.replicas)
-    x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
-    for r in range(R):
-        s.init_state(x[r])
     dev_plan = args.plan == "device"
+    queue = dev_plan and args.queue > 0
+    if queue:
+        # the request pool: the workload's draws for Q requests (the first n
+        # start in the slots at their mixed start steps)
+        if args.queue < spec.n:
+            raise SystemExit("--queue must be at least the batch size")
+        s = GuidedSampler.from_inputs(W.make_inputs(dataclasses.replace(spec, n=args.queue)))
+        x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
+    else:
+        s = GuidedSampler.from_inputs(inp, wrap=True)
+        x = torch.empty((R, spec.n, spec.C, spec.H, spec.W), dtype=s.tdtype, device="cuda")
+        for r in range(R):
+            s.init_state(x[r])
     # one graph replay covers up to G launches of the timed run
     G = min(args.graph, args.steps) if dev_plan else 0
     loop = s.native_loop(x if R > 1 else x[0], upload_batch=args.upload_batch,
                          async_upload=bool(args.async_upload), device_plan=dev_plan,
-                         graph_launches=G, records=bool(args.records))
+                         graph_launches=G, records=bool(args.records) or queue,
+                         slots=spec.n if queue else None, ring=queue,
+                         join_front=None if args.join_front < 0 else args.join_front)
     loop.run(0, args.warmup)
     torch.cuda.synchronize()
     elems_per_launch = spec.n * spec.C * spec.H * spec.W  # every sample active (steady state)
@@ -620,6 +638,18 @@ def main():
     value = elems_per_launch * args.steps / wall
     bpe = bytes_per_element(spec)
     alg_bytes = bpe * elems_per_launch
+    joins = 0
+    if queue:
+        # a joining request reads its fp32 noise (4 B per element) instead of
+        # the slot's state: slot i's request finishes every `steps` launches of
+        # its replica, first after steps - start_i of them
+        st0 = s.start[:spec.n].astype(np.int64)
+        for k in range(args.warmup, args.warmup + args.steps):
+            m = k // R  # the replica's own launch index
+            first = spec.steps - st0
+            joins += int(((m >= first) & ((m - first) % spec.steps == 0)).sum())
+        es = 2 if spec.dtype == "bf16" else 4
+        alg_bytes += (4 - es) * spec.C * spec.H * spec.W * joins / args.steps
     achieved = alg_bytes / (launch_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -643,7 +673,10 @@ def main():
         "config": {"workload": spec.name, "batch": spec.n, "latent": [spec.C, spec.H, spec.W],
                    "storage": spec.dtype, "sampler": spec.sampler, "schedule_steps": spec.steps,
                    "buckets": spec.num_buckets, "regions": spec.regions,
-                   "progress": "mixed, steady state", "replicas": R, "plan": args.plan},
+                   "progress": ("continuous batching: slots refilled from an endless queue over "
+                                f"{args.queue} requests ({joins} joins in the timed launches)" if queue
+                                else "mixed, steady state (finished slots restart at step 0)"),
+                   "replicas": R, "plan": args.plan},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
         "kernel": {"name": "guided_step", "avg_launch_us": launch_ms * 1e3,

@@ -88,7 +88,10 @@ class DevicePlan(C.Structure):
                 ("uncond_offset", vp), ("totals", vp), ("bucket_cfg_end", vp),
                 ("record_in", vp), ("record_out", vp), ("sigmas", vp), ("num_sigmas", C.c_int32),
                 ("region_range", vp), ("covered_sets", vp), ("region_count", vp),
-                ("max_regions", C.c_int32)]
+                ("max_regions", C.c_int32),
+                ("queue_len", C.c_int32), ("queue_ring", C.c_int32), ("noise", vp),
+                ("slot_req_in", vp), ("slot_req_out", vp), ("queue_in", vp), ("queue_out", vp),
+                ("join_front", C.c_int32), ("join_in", vp), ("join_out", vp)]
 
 
 class Patch(C.Structure):
@@ -109,7 +112,9 @@ class LoopDesc(C.Structure):
                 ("replica_stride", C.c_int64), ("upload_batch", C.c_int32),
                 ("async_upload", C.c_int32), ("step", StepArgs),
                 ("device_plan", C.c_int32), ("graph_launches", C.c_int32), ("dev_steps", vp),
-                ("dplan", DevicePlan), ("dev_records", vp)]
+                ("dplan", DevicePlan), ("dev_records", vp),
+                ("queue_len", C.c_int32), ("queue_ring", C.c_int32), ("noise", vp), ("dev_queue", vp),
+                ("join_front", C.c_int32)]
 
 
 _lib = None

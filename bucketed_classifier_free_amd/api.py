@@ -181,7 +181,8 @@ def guided_step_workspace_size(n, C, H, W, dtype=torch.float32) -> int:
 
 def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sampler, s2, feather,
                region_count, region_box, region_strength, mu_region, x_orig, mask, stats,
-               workspace, cache_hint, region_range=None, steps=0, launch_vpt=0, static_scratch=False):
+               workspace, cache_hint, region_range=None, steps=0, launch_vpt=0, static_scratch=False,
+               tables=None):
     """Checks the tensors of a guided step and packs them into StepArgs.
     ``plan_rows`` = (order, step_idx, scale, uncond_row) or None (device plan)."""
     _dev(x, "x")
@@ -205,22 +206,23 @@ def _step_args(x, x_out, sigmas, mu_uncond, mu_cond, plan_rows, *, n_active, sam
             _dev(t, nm, dt)
             if t.numel() < n:
                 raise ValueError(f"{nm}: needs {n} entries")
-    _dev(mu_uncond, "mu_uncond", torch.float32, (n, Cc))
-    _dev(mu_cond, "mu_cond", torch.float32, (n, Cc))
+    nt = n if tables is None else int(tables)  # per-sample tables (requests under a queue)
+    _dev(mu_uncond, "mu_uncond", torch.float32, (nt, Cc))
+    _dev(mu_cond, "mu_cond", torch.float32, (nt, Cc))
     R = 0
     if region_count is not None:
-        _dev(region_count, "region_count", torch.int32, (n,))
+        _dev(region_count, "region_count", torch.int32, (nt,))
         _dev(region_box, "region_box", torch.int32)
-        if region_box.dim() != 3 or region_box.shape[0] != n or region_box.shape[2] != 4:
+        if region_box.dim() != 3 or region_box.shape[0] != nt or region_box.shape[2] != 4:
             raise ValueError("region_box must be [n, R, 4]")
         R = region_box.shape[1]
-        _dev(region_strength, "region_strength", torch.float32, (n, R))
-        _dev(mu_region, "mu_region", torch.float32, (n, R, Cc))
+        _dev(region_strength, "region_strength", torch.float32, (nt, R))
+        _dev(mu_region, "mu_region", torch.float32, (nt, R, Cc))
     mps = 0
     if x_orig is not None or mask is not None:
-        _dev(x_orig, "x_orig", x.dtype, x.shape)
+        _dev(x_orig, "x_orig", x.dtype, (nt, Cc, H, W))
         _dev(mask, "mask", torch.float32)
-        if tuple(mask.shape) == (n, 1, H, W):
+        if tuple(mask.shape) == (nt, 1, H, W):
             mps = 1
         elif tuple(mask.shape) != (1, 1, H, W):
             raise ValueError(f"mask: shape {tuple(mask.shape)} is neither [n,1,H,W] nor [1,1,H,W]")
@@ -342,17 +344,22 @@ def device_plan_arrays(n: int, nb: int, device="cuda") -> dict:
 def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=None,
                 covered=None, wrap: bool = False, out=None, bucket_cfg_end=None,
                 record_in=None, record_out=None, sigmas=None, region_range=None,
-                covered_sets=None, region_count=None) -> L.DevicePlan:
-    """Packs the device arrays of a device-built plan (see include/bcg.h)."""
+                covered_sets=None, region_count=None, queue=None) -> L.DevicePlan:
+    """Packs the device arrays of a device-built plan (see include/bcg.h).
+    ``queue`` (continuous batching) is a dict: len, ring, noise [len, C, H, W]
+    fp32, slot_req_in / slot_req_out [n] and queue_in / queue_out [1] int32,
+    optionally join_front J with join_in / join_out [J] int32; the per-sample
+    tables then hold ``len`` requests."""
     _dev(step_in, "step_in", torch.int32)
     n = step_in.numel()
+    nt = int(queue["len"]) if queue else n  # entries of the per-sample tables
     _dev(bucket_cfg, "bucket_cfg", torch.float32)
     nb = bucket_cfg.numel()
     _dev(step_out, "step_out", torch.int32, allow_none=True)
     if step_out is not None and step_out.numel() < n:
         raise ValueError("step_out: needs n entries")
-    _dev(cfg_override, "cfg_override", torch.float32, (n,), allow_none=True)
-    _dev(covered, "covered", torch.int32, (n,), allow_none=True)
+    _dev(cfg_override, "cfg_override", torch.float32, (nt,), allow_none=True)
+    _dev(covered, "covered", torch.int32, (nt,), allow_none=True)
     _dev(bucket_cfg_end, "bucket_cfg_end", torch.float32, (nb,), allow_none=True)
     R = 0
     if region_range is not None:
@@ -361,7 +368,7 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
             raise ValueError("region_range must be [n, R, 2]")
         R = region_range.shape[1]
         _dev(covered_sets, "covered_sets", torch.int16, (n,))
-    _dev(region_count, "region_count", torch.int32, (n,), allow_none=True)
+    _dev(region_count, "region_count", torch.int32, (nt,), allow_none=True)
     _dev(record_in, "record_in", torch.float32, (n, 4), allow_none=True)
     _dev(record_out, "record_out", torch.float32, (n, 4), allow_none=True)
     _dev(sigmas, "sigmas", torch.float32, allow_none=True)
@@ -376,11 +383,27 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
             if out[k].numel() < size:
                 raise ValueError(f"{k}: needs {size} entries")
         ptrs = [_ptr(out[k]) for k in _PLAN_KEYS]
+    q = [0, 0, None, None, None, None, None, 0, None, None]
+    if queue:
+        _dev(queue["noise"], "noise", torch.float32)
+        if queue["noise"].shape[0] != nt:
+            raise ValueError("noise: needs one entry per request")
+        for k in ("slot_req_in", "slot_req_out"):
+            _dev(queue[k], k, torch.int32, (n,))
+        for k in ("queue_in", "queue_out"):
+            _dev(queue[k], k, torch.int32, (1,))
+        J = int(queue.get("join_front", 0))
+        if J:
+            for k in ("join_in", "join_out"):
+                _dev(queue[k], k, torch.int32, (J,))
+        q = [nt, 1 if queue.get("ring") else 0, _ptr(queue["noise"]), _ptr(queue["slot_req_in"]),
+             _ptr(queue["slot_req_out"]), _ptr(queue["queue_in"]), _ptr(queue["queue_out"]), J,
+             _ptr(queue.get("join_in")) if J else None, _ptr(queue.get("join_out")) if J else None]
     return L.DevicePlan(int(steps), nb, 1 if wrap else 0, _ptr(bucket_cfg), _ptr(cfg_override),
                         _ptr(covered), _ptr(step_in), _ptr(step_out), *ptrs, _ptr(bucket_cfg_end),
                         _ptr(record_in), _ptr(record_out), _ptr(sigmas),
                         0 if sigmas is None else sigmas.numel(), _ptr(region_range),
-                        _ptr(covered_sets), _ptr(region_count), R)
+                        _ptr(covered_sets), _ptr(region_count), R, *q)
 
 
 def plan_records(plan, step_idx, steps: int, sigmas, ranged: bool = False):
@@ -418,19 +441,21 @@ def guided_step_dplan(x, x_out, sigmas, mu_uncond, mu_cond, *, steps: int, bucke
                       sampler: str, s2: float, feather: int = 0,
                       region_count=None, region_box=None, region_strength=None, mu_region=None,
                       x_orig=None, mask=None, cache_hint: int = 0, stats=None, workspace=None,
-                      launch_vpt: int = 0, stream=None):
+                      launch_vpt: int = 0, queue=None, stream=None):
     """guided_step with the plan of the step built on the device, same launch.
-    ``stats`` ([n, 3]) with ``workspace`` computes the norm statistics inside the step."""
+    ``stats`` ([n, 3]) with ``workspace`` computes the norm statistics inside the step.
+    ``queue`` (see device_plan) runs the n samples as slots of continuous batching."""
     a = _step_args(x, x_out, sigmas, mu_uncond, mu_cond, None, n_active=0, sampler=sampler,
                    s2=s2, feather=feather, region_count=region_count, region_box=region_box,
                    region_strength=region_strength, mu_region=mu_region, x_orig=x_orig, mask=mask,
-                   stats=stats, workspace=workspace, cache_hint=cache_hint, launch_vpt=launch_vpt)
+                   stats=stats, workspace=workspace, cache_hint=cache_hint, launch_vpt=launch_vpt,
+                   tables=None if not queue else int(queue["len"]))
     if step_in.numel() != x.shape[0]:
         raise ValueError("step_in: needs one entry per sample")
     d = device_plan(steps, bucket_cfg, step_in, step_out=step_out, cfg_override=cfg_override,
                     covered=covered, wrap=wrap, out=plan_out, bucket_cfg_end=bucket_cfg_end,
                     record_in=record_in, record_out=record_out, region_range=region_range,
-                    covered_sets=covered_sets, region_count=region_count)
+                    covered_sets=covered_sets, region_count=region_count, queue=queue)
     L.check(L.lib().guided_step_dplan(ct.byref(a), ct.byref(d), _stream(stream)))
 
 

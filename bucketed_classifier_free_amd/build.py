@@ -24,8 +24,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbcg.so")
 
 SOURCES = ["bcg_host.cpp", "bcg_api.hip", "bcg_loop.hip", "bcg_step_f32.hip", "bcg_step_bf16.hip",
-           "bcg_step_f32_nt.hip", "bcg_step_bf16_nt.hip", "bcg_rows_f32.hip", "bcg_rows_bf16.hip",
-           "bcg_weight.hip"]
+           "bcg_step_f32_nt.hip", "bcg_step_bf16_nt.hip", "bcg_step_f32_queue.hip", "bcg_step_bf16_queue.hip",
+           "bcg_rows_f32.hip", "bcg_rows_bf16.hip", "bcg_weight.hip"]
 ARCH = "gfx950"
 
 

@@ -342,6 +342,33 @@ int check_dplan(const bcg_device_plan* d, int n, bool step, const char* who) {
     if (d->record_in && d->record_out &&
         any_overlap(d->record_in, (size_t)n * 16, d->record_out, (size_t)n * 16))
         return fail(BCG_EINVAL, "%s: record_out overlaps record_in", who);
+    if (d->queue_len < 0 || d->queue_len >= (1 << 24))
+        return fail(BCG_EINVAL, "%s: queue_len %d not in [0, 2^24)", who, d->queue_len);
+    if (d->queue_len > 0) {
+        if (!step) return fail(BCG_EINVAL, "%s: continuous batching runs inside guided_step_dplan", who);
+        if (d->queue_ring != 0 && d->queue_ring != 1) return fail(BCG_EINVAL, "%s: queue_ring must be 0 or 1", who);
+        if (d->wrap) return fail(BCG_EINVAL, "%s: continuous batching replaces wrap (set it to 0)", who);
+        if (d->queue_len < n) return fail(BCG_EINVAL, "%s: queue_len %d < n %d slots", who, d->queue_len, n);
+        if (!d->noise || !d->slot_req_in || !d->slot_req_out || !d->queue_in || !d->queue_out ||
+            !d->record_in || !d->record_out || !d->step_out)
+            return fail(BCG_EINVAL, "%s: continuous batching needs noise, slot_req_in/out, queue_in/out, "
+                        "record_in/out and step_out", who);
+        if (d->region_range) return fail(BCG_EINVAL, "%s: continuous batching takes no validity ranges", who);
+        const size_t in4 = (size_t)n * 4;
+        if (any_overlap(d->slot_req_in, in4, d->slot_req_out, in4) || any_overlap(d->queue_in, 4, d->queue_out, 4))
+            return fail(BCG_EINVAL, "%s: slot_req_out / queue_out overlap their inputs", who);
+        if (d->join_front < 0 || d->join_front > n)
+            return fail(BCG_EINVAL, "%s: join_front %d not in [0, n]", who, d->join_front);
+        if (d->join_front > 0) {
+            const size_t j4 = (size_t)d->join_front * 4;
+            if (!d->join_in || !d->join_out) return fail(BCG_EINVAL, "%s: join_front needs join_in and join_out", who);
+            if (any_overlap(d->join_in, j4, d->join_out, j4))
+                return fail(BCG_EINVAL, "%s: join_out overlaps join_in", who);
+        }
+    } else if (d->slot_req_in || d->slot_req_out || d->queue_in || d->queue_out || d->noise || d->join_front ||
+               d->join_in || d->join_out) {
+        return fail(BCG_EINVAL, "%s: queue arrays given with queue_len = 0", who);
+    }
     return BCG_OK;
 }
 
@@ -370,6 +397,16 @@ void fill_dplan(StepParams& p, const bcg_device_plan* d) {
     p.region_range = d->region_range;
     p.range_steps = d->steps;
     p.covered_sets = d->covered_sets;
+    p.queue_len = d->queue_len;
+    p.queue_ring = d->queue_ring;
+    p.noise = d->noise;
+    p.slot_req = d->slot_req_in;
+    p.slot_req_out = d->slot_req_out;
+    p.queue_in = d->queue_in;
+    p.queue_out = d->queue_out;
+    p.join_front = d->queue_len > 0 ? d->join_front : 0;
+    p.join_in = d->join_in;
+    p.join_out = d->join_out;
 }
 
 }  // namespace
@@ -458,31 +495,41 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         };
         const size_t in4 = (size_t)a->n * 4, nb4 = (size_t)(d->num_buckets + 1) * 4;
         const size_t cfg4 = (size_t)d->num_buckets * 4;
-        const size_t R = (size_t)a->max_regions, nC4 = (size_t)a->n * a->C * 4;
-        const size_t mbytes = a->mask ? (size_t)(a->mask_per_sample ? a->n : 1) * HW * 4 : 0;
+        // per-sample tables: one entry per request under continuous batching
+        const size_t nt = d->queue_len > 0 ? (size_t)d->queue_len : (size_t)a->n;
+        const size_t t4 = nt * 4;
+        const size_t R = (size_t)a->max_regions, nC4 = t4 * a->C;
+        const size_t mbytes = a->mask ? (a->mask_per_sample ? nt : 1) * HW * 4 : 0;
+        const size_t obytes = nt * a->C * HW * elem_size(a->dtype);
         const Span writes[] = {{d->bucket_id, in4},     {d->scale, in4},          {d->uncond_row, in4},
                                {d->cond_row, in4},      {d->order, in4},          {d->bucket_count, nb4},
                                {d->bucket_offset, nb4}, {d->uncond_offset, nb4},  {d->totals, 8},
-                               {d->step_out, in4},      {d->record_out, in4 * 4}};
+                               {d->step_out, in4},      {d->record_out, in4 * 4},
+                               {d->slot_req_out, d->queue_len ? in4 : 0}, {d->queue_out, d->queue_len ? 4u : 0u},
+                               {d->join_out, d->queue_len ? (size_t)d->join_front * 4 : 0}};
         const Span step_uses[] = {{a->x, bytes},       // [0], [1]: the state; inputs from [2] on
                                   {a->x_out, bytes},
-                                  {a->x_orig, a->x_orig ? bytes : 0},
+                                  {a->x_orig, a->x_orig ? obytes : 0},
                                   {a->mask, mbytes},
                                   {a->sigmas, (size_t)a->num_sigmas * 4},
                                   {a->mu_uncond, nC4},
                                   {a->mu_cond, nC4},
-                                  {a->region_count, R ? in4 : 0},
-                                  {a->region_box, in4 * R * 4},
-                                  {a->region_strength, in4 * R},
+                                  {a->region_count, R ? t4 : 0},
+                                  {a->region_box, t4 * R * 4},
+                                  {a->region_strength, t4 * R},
                                   {a->mu_region, nC4 * R},
                                   {d->record_in, d->record_in ? in4 * 4 : 0},
                                   {d->step_in, in4},
                                   {d->bucket_cfg, cfg4},
                                   {d->bucket_cfg_end, d->bucket_cfg_end ? cfg4 : 0},
-                                  {d->cfg_override, d->cfg_override ? in4 : 0},
-                                  {d->covered, d->covered ? in4 : 0},
-                                  {d->covered_sets, d->covered_sets ? (size_t)a->n * 2 : 0},
-                                  {d->region_range, d->region_range ? in4 * 4 * R : 0}};
+                                  {d->cfg_override, d->cfg_override ? t4 : 0},
+                                  {d->covered, d->covered ? t4 : 0},
+                                  {d->covered_sets, d->covered_sets ? nt * 2 : 0},
+                                  {d->region_range, d->region_range ? t4 * 4 * R : 0},
+                                  {d->noise, d->noise ? nt * a->C * HW * 4 : 0},
+                                  {d->slot_req_in, d->slot_req_in ? in4 : 0},
+                                  {d->queue_in, d->queue_in ? 4u : 0u},
+                                  {d->join_in, d->queue_len ? (size_t)d->join_front * 4 : 0}};
         for (const Span& w : writes)
             for (const Span& r : step_uses)
                 if (w.p && r.p && r.bytes && any_overlap(w.p, w.bytes, r.p, r.bytes))
@@ -501,6 +548,13 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     // Statistics inside the step when a latent row is a power-of-two group of
     // at most 64 lanes (W a multiple of the vector, W / vector a power of
     // two); otherwise (host plans only) two extra kernels read x again.
+    if (d && d->queue_len > 0) {
+        if (!vec)
+            return fail(BCG_EINVAL, "%s: continuous batching needs the 16-byte vector path (H*W a multiple of %d, "
+                        "16-byte aligned arrays)", who, VV);
+        if (a->stats) return fail(BCG_EINVAL, "%s: stats are not available with continuous batching", who);
+        if (!aligned16(d->noise)) return fail(BCG_EINVAL, "%s: noise must be 16-byte aligned", who);
+    }
     const int row_lanes = vec && a->W % VV == 0 ? a->W / VV : 0;
     const bool fused_stats = a->stats && row_lanes >= 1 && row_lanes <= 64 && (row_lanes & (row_lanes - 1)) == 0;
     if (a->stats) {
@@ -553,8 +607,10 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
         p.stats_part = static_cast<float*>(a->workspace);
         p.stats_group = row_lanes;
     }
+    const int64_t lead = p.join_front;
+    if ((lead + p.n_active) * p.tiles >= INT32_MAX) return fail(BCG_ESHAPE, "%s: grid too large", who);
     if (d && (d->step_out || d->bucket_id || d->record_out))
-        p.plan_block = (int)((int64_t)p.n_active * p.tiles);
+        p.plan_block = (int)((lead + p.n_active) * p.tiles);
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     if (a->stats && !fused_stats) {
@@ -571,7 +627,11 @@ int step_impl(const bcg_step_args* a, const bcg_device_plan* d, void* stream, co
     }
     const bool heun = a->sampler == BCG_HEUN;
     hipError_t e;
-    if (vec && a->cache_hint == BCG_CACHE_STREAM && !fused_stats)  // the statistics run on the keep variants
+    const bool queue = d && d->queue_len > 0;  // continuous batching runs on the streaming variants
+    if (queue)
+        e = a->dtype == BCG_BF16 ? launch_step_bf16_queue(p, heun, inpaint, block, st)
+                                 : launch_step_f32_queue(p, heun, inpaint, block, st);
+    else if (vec && a->cache_hint == BCG_CACHE_STREAM && !fused_stats)  // the statistics run on the keep variants
         e = a->dtype == BCG_BF16 ? launch_step_bf16_stream(p, heun, inpaint, block, st)
                                  : launch_step_f32_stream(p, heun, inpaint, block, st);
     else

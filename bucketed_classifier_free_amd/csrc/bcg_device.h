@@ -65,6 +65,7 @@ template <> struct Io<float, 4> {
         v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
     }
     __device__ static __forceinline__ void load(const float* p, float (&v)[4]) { unpack(load_raw(p), v); }
+    __device__ static __forceinline__ Raw pack(const float (&v)[4]) { return f32x4_t{v[0], v[1], v[2], v[3]}; }
     template <bool NT = false> __device__ static __forceinline__ void store(float* p, const float (&v)[4]) {
         const f32x4_t q = {v[0], v[1], v[2], v[3]};
         st<NT>(reinterpret_cast<f32x4_t*>(p), q);
@@ -95,6 +96,11 @@ template <> struct Io<bf16_t, 8> {
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     }
     __device__ static __forceinline__ void load(const bf16_t* p, float (&v)[8]) { unpack(load_raw(p), v); }
+    // round to nearest even
+    __device__ static __forceinline__ Raw pack(const float (&v)[8]) {
+        return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7])};
+    }
     template <bool NT = false> __device__ static __forceinline__ void store(bf16_t* p, const float (&v)[8]) {
         const u32x4_t q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
@@ -190,6 +196,27 @@ struct StepParams {
     // row norms of C, U and pred to slot (sample, tile, group), 3 floats.
     float* stats_part;
     int stats_group;
+    // Continuous batching (queue_len > 0): x and x_out hold n slots, and every
+    // other per-sample table (means, regions, override, coverage, x_orig,
+    // mask, noise) is indexed by request, queue_len of them.  A slot's record
+    // carries its request (flags >> 8) and whether the request joins at this
+    // step (flags bit 6: its state is built from its noise before the step).
+    // The plan workgroup refills the slots whose request takes its last step
+    // with the next queued requests (slot order), for the next step.
+    int queue_len;
+    int queue_ring;               // request ids modulo queue_len (an endless queue)
+    const float* noise;           // [queue_len, C, H, W] fp32
+    const int32_t* slot_req;      // [n] request of each slot at this step
+    int32_t* slot_req_out;        // [n] ... at the next step
+    const int32_t* queue_in;      // [1] next request of the queue
+    int32_t* queue_out;           // [1]
+    // Joins dispatched first: the grid starts with join_front groups of
+    // `tiles` workgroups; group q takes slot join_in[q] (-1: none), whose
+    // record carries flag bit 7 so the slot's own workgroups leave it.  The
+    // plan workgroup lists the next step's first join_front joins in join_out.
+    int join_front;
+    const int32_t* join_in;       // [join_front]
+    int32_t* join_out;            // [join_front]
 };
 
 // Launch parameter block of the materialised-branch step (device pointers).
@@ -234,5 +261,8 @@ hipError_t launch_step_f32_stream(const StepParams& p, bool heun, bool inpaint, 
                                   hipStream_t s);
 hipError_t launch_step_bf16_stream(const StepParams& p, bool heun, bool inpaint, int block,
                                    hipStream_t s);
+// Continuous batching (p.queue_len > 0), 16-byte vector path only (bcg_step_*_queue.hip).
+hipError_t launch_step_f32_queue(const StepParams& p, bool heun, bool inpaint, int block, hipStream_t s);
+hipError_t launch_step_bf16_queue(const StepParams& p, bool heun, bool inpaint, int block, hipStream_t s);
 
 }  // namespace bcg

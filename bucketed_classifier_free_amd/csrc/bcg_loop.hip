@@ -36,6 +36,7 @@ struct bcg_loop {
     int64_t k_next = 0;               // launches done since the last restart
     std::vector<int32_t> t0;          // initial step indices (from start)
     std::vector<float> rec0;          // their sample records (with dev_records)
+    std::vector<int32_t> q0;          // continuous batching: slot s holds request s, next = n
     // graph g replays launches k .. k+G-1 for any k = g (mod 2*replicas): one
     // per phase of the buffer pattern, so a replay can start at any launch
     std::vector<hipGraph_t> graph;
@@ -84,6 +85,13 @@ int reset_steps(bcg_loop* L, hipStream_t st) {
                         "bcg_loop: record upload");
             if (rc) return rc;
         }
+        if (L->d.queue_len > 0) {
+            const size_t qn = size_t(n) + 1 + size_t(L->d.join_front);
+            rc = hip_ok(hipMemcpyAsync(L->d.dev_queue + size_t(2 * r) * qn, L->q0.data(), sizeof(int32_t) * qn,
+                                       hipMemcpyHostToDevice, st),
+                        "bcg_loop: queue upload");
+            if (rc) return rc;
+        }
     }
     L->k_next = 0;
     return BCG_OK;
@@ -112,6 +120,21 @@ int launch_dplan(bcg_loop* L, int64_t k, hipStream_t st) {
     } else {
         dp.record_in = nullptr;
         dp.record_out = nullptr;
+    }
+    if (d.queue_len > 0) {
+        const size_t qn = size_t(n) + 1 + size_t(d.join_front);
+        int32_t* qi = d.dev_queue + size_t(2 * r + (m & 1)) * qn;
+        int32_t* qo = d.dev_queue + size_t(2 * r + ((m + 1) & 1)) * qn;
+        dp.queue_len = d.queue_len;
+        dp.queue_ring = d.queue_ring;
+        dp.noise = d.noise;
+        dp.slot_req_in = qi;
+        dp.slot_req_out = qo;
+        dp.queue_in = qi + n;
+        dp.queue_out = qo + n;
+        dp.join_front = d.join_front;
+        dp.join_in = d.join_front > 0 ? qi + n + 1 : nullptr;
+        dp.join_out = d.join_front > 0 ? qo + n + 1 : nullptr;
     }
     return guided_step_dplan(&a, &dp, st);
 }
@@ -288,6 +311,19 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
         (desc->upload_batch < 1 || desc->upload_batch > 64 || desc->rows % desc->upload_batch != 0))
         return fail(BCG_EINVAL, "bcg_loop_create: upload_batch %d must be in [1, 64] and divide rows %d",
                     desc->upload_batch, desc->rows);
+    if (desc->queue_len != 0) {
+        if (!desc->device_plan || !desc->dev_records || !desc->dev_queue || !desc->noise)
+            return fail(BCG_EINVAL, "bcg_loop_create: continuous batching needs device plans, dev_records, "
+                        "dev_queue and noise");
+        if (desc->queue_len < n || desc->wrap)
+            return fail(BCG_EINVAL, "bcg_loop_create: continuous batching needs queue_len >= n and wrap = 0");
+        if (desc->join_front < 0 || desc->join_front > n)
+            return fail(BCG_EINVAL, "bcg_loop_create: join_front %d not in [0, n]", desc->join_front);
+        for (int i = 0; i < n; ++i)
+            if (desc->start[i] < 0 || desc->start[i] >= desc->plan.steps)
+                return fail(BCG_EINVAL, "bcg_loop_create: start[%d] = %d not in [0, steps) (continuous batching)",
+                            i, desc->start[i]);
+    }
     if (desc->device_plan) {
         if (n > 0 && !desc->dev_steps) return fail(BCG_EINVAL, "bcg_loop_create: dev_steps is NULL");
         if (desc->graph_launches < 0 || desc->graph_launches > 4096)
@@ -395,6 +431,19 @@ extern "C" int bcg_loop_create(const bcg_loop_desc* desc, bcg_loop** out) {
             if (rc3) {
                 bcg_loop_destroy(L);
                 return rc3;
+            }
+            if (desc->queue_len > 0) {  // every slot's first request joins at the first launch
+                const int J = desc->join_front;
+                L->q0.assign(size_t(n) + 1 + size_t(J), -1);
+                for (int i = 0; i < n; ++i) {
+                    L->q0[size_t(i)] = i;
+                    uint32_t fl;
+                    std::memcpy(&fl, &L->rec0[size_t(i) * 4 + 3], 4);
+                    fl |= 64u | (uint32_t(i) << 8) | (i < J ? 128u : 0u);  // the first J go to the front groups
+                    std::memcpy(&L->rec0[size_t(i) * 4 + 3], &fl, 4);
+                }
+                L->q0[size_t(n)] = n;
+                for (int q = 0; q < J; ++q) L->q0[size_t(n) + 1 + size_t(q)] = q;
             }
         }
         // Check the launch template once with the first launch's pointers.

@@ -13,8 +13,8 @@
 // Design for gfx950 (bandwidth-bound, no contraction => no MFMA):
 //   * one workgroup = one sample x a tile of `blockDim` 128-bit pixel vectors;
 //     per-sample scalars come from uniform (scalar) loads, the per-channel
-//     branch offsets b_k[c] = sigma^2 mu_k[c] / (s2 + sigma^2) are computed
-//     once per workgroup into LDS and read back as broadcasts;
+//     tables of the update (below) are computed once per workgroup into LDS
+//     and read back as broadcasts;
 //   * each lane owns V consecutive pixels (16 bytes of storage) and computes
 //     their region weights, coverage, mask and normalisers once, then walks
 //     the C channels (stride H*W);
@@ -26,13 +26,24 @@
 //   * per-sample modes (scale == 1, last step, sample without regions) are
 //     uniform branches taken outside the channel loop.
 // Evaluation order (fp32; contraction off, so the only fused operations are
-// the explicit fma(a, b, c) = a*b + c rounded once), identical for every path:
-//   u = fma(a, x, bu);  c = fma(a, x, bc)  |  c = wh_0*t_0, c = fma(wh_r, t_r, c)
-//                                              with t_r = fma(a, x, br_r)
-//   pred = fma(w, c - u, u) | fma(weff, c - u, u) | c | (sel ? c : u)
-//   pred = fma(m, pred, (1-m)*xo);  Euler x' = fma(x - pred, q, x)
-//   Heun d = (x - pred)*is; xt = fma(h, d, x); d2 = (xt - pred(xt))*isn;
-//        x' = fma(d + d2, hh, x);  last step x' = pred.
+// the explicit fma(a, b, c) = a*b + c rounded once).  The stand-in denoiser
+// is affine in x, so every branch, the CFG combine, the inpaint blend and
+// both of Heun's evaluations fold into x' = K x + B: K per sample (per pixel
+// when inpainting), B from per-channel tables and per-pixel region weights:
+//   per sample:  a = s2/den, b1 = v/den (v = sigma^2, den = s2 + v);
+//     last step  g = 1, K = a;  Euler q = (sigma'-sigma)/sigma, g = -q,
+//     K = fma(q, b1, 1);  Heun e1 = b1/sigma, e2 = b2/sigma',
+//     K = fma(hh, fma(e2, fma(h, e1, 1), e1), 1), c1 = (-hh/sigma) fma(h, e2, 1),
+//     c2 = -hh/sigma'
+//   per channel: bu = v mu_u/den; without regions one offset
+//     P = fma(w, v (mu_c - mu_u)/den, bu) (v mu_c/den at scale 1); with
+//     regions t0 = bu, t_r = v (mu_r - mu_u)/den (also when the uncond is
+//     skipped: where no region has weight the cond is the uncond); tables
+//     g*t, or fma(c1, t, c2*t') for Heun (t' at sigma')
+//   per pixel:   om_r = (covered ? w : 0) * wh_r (normalised region weights)
+//   per element: B = T0, B = fma(om_r, T_r, B);  x' = fma(K, x, B)
+//   inpaint:     x' = fma(k, x, fma(l1, B1, [fma(l2, B2,] lo*xo)) with the
+//                per-pixel k, l1, l2, lo of the mask, B1/B2 unscaled chains.
 #pragma once
 
 #include "bcg_device.h"
@@ -46,14 +57,17 @@ constexpr int kPlanLds = 4 * 2 * kSet;              // ints of the coefficient L
 
 // Compile-time tuning of the streaming loop (the stage width U is chosen per
 // kernel variant at launch, see stage_width).
-template <int U_, bool NT_, bool PF_ = false, bool FULL_ = false, bool STATS_ = false>
+template <int U_, bool NT_, bool PF_ = false, bool FULL_ = false, bool STATS_ = false, bool QUEUE_ = false>
 struct Tune {
     static constexpr int U = U_;        // channels per pipeline stage
     static constexpr bool NT = NT_;     // nontemporal (streaming) loads and stores
     static constexpr bool PF = PF_;     // next pass's head stage requested during this pass
     static constexpr bool FULL = FULL_; // C is a multiple of 2U: every stage is full
     static constexpr bool STATS = STATS_;  // norm statistics of the first evaluation
+    static constexpr bool QUEUE = QUEUE_;  // continuous batching: slots hold requests
 };
+template <typename TN>
+using QueueOf = Tune<TN::U, TN::NT, TN::PF, TN::FULL, false, true>;
 typedef Tune<2, false, false, false, true> StatsTune;  // ordinary loads/stores, with the statistics
 typedef Tune<2, false> KeepTune;    // ordinary loads/stores (BCG_CACHE_KEEP)
 typedef Tune<2, true> StreamTune;   // nontemporal loads/stores (BCG_CACHE_STREAM)
@@ -65,6 +79,9 @@ struct StepScalars {
     float w;               // guidance scale
     float q;               // Euler: (sigma' - sigma)/sigma
     float h, is, isn, hh;  // Heun: sigma' - sigma, 1/sigma, 1/sigma', h*0.5
+    float g;               // Euler and last step: the tables' factor (-q, or 1)
+    float K;               // x' = K x + B
+    float c1, c2;          // Heun: the tables' weights at sigma and sigma'
 };
 
 // Per-lane, per-pixel state (V pixels).
@@ -72,9 +89,11 @@ template <int V, int NR>
 struct LaneState {
     float wh[NR > 0 ? NR : 1][V];  // normalised region weights
     float weff[V];                  // scale where covered, else 0
-    bool sel[V];                    // scale-1 path: take c (else u)
-    bool cov[V];                    // some region has weight (the statistics' C is U elsewhere)
+    bool sel[V];                    // scale-1 path: take c (else u) (statistics)
+    bool cov[V];                    // some region has weight
     float m[V], om[V];              // inpaint mask and 1 - mask
+    float wr[NR > 0 ? NR : 1][V];  // folded: weff * wh_r
+    float k[V], l1[V], l2[V], lo[V];  // folded inpaint: x' = fma(k, x, fma(l1, B1, [fma(l2, B2,] lo*xo))
 };
 
 // Norm statistics of one lane: sums of squares of C, U and pred over the
@@ -85,11 +104,16 @@ struct LaneStats {
     float tot[3];
 };
 
-template <int V, int NR, int NRB, bool INP, bool ONE, bool ST = false>
-__device__ __forceinline__ float guided_pred(const LaneState<V, NR>& L, int e, float x, float xo,
-                                             float a, float w, float bu, float bc,
-                                             const float (&br)[NRB > 0 ? NRB : 1],
-                                             LaneStats* st = nullptr) {
+// The norm statistics of one element: the branch predictions U and C and
+// their combine (before the inpaint blend), each as its own sequence --
+// u = fma(a, x, bu); c = fma(a, x, bc), or c = wh_0*fma(a, x, br_0),
+// c = fma(wh_r, fma(a, x, br_r), c); pred = fma(w, c - u, u) or
+// fma(weff, c - u, u), c (sel ? c : u) at scale 1 -- added to the lane's
+// sums of squares (C is U where no region has weight).
+template <int V, int NR, int NRB, bool ONE>
+__device__ __forceinline__ void stats_element(const LaneState<V, NR>& L, int e, float x, float a, float w,
+                                              float bu, float bc, const float (&br)[NRB > 0 ? NRB : 1],
+                                              LaneStats* st) {
     const float u = __builtin_fmaf(a, x, bu);
     float c;
     if constexpr (NRB == 0) {
@@ -107,48 +131,56 @@ __device__ __forceinline__ float guided_pred(const LaneState<V, NR>& L, int e, f
         if constexpr (NRB == 0) pred = c;
         else pred = L.sel[e] ? c : u;
     }
-    if constexpr (ST) {  // C (U where no region has weight), U, and pred before the blend
-        const float cs = (NRB == 0 || L.cov[e]) ? c : u;
-        st->sq[0] = __builtin_fmaf(cs, cs, st->sq[0]);
-        st->sq[1] = __builtin_fmaf(u, u, st->sq[1]);
-        st->sq[2] = __builtin_fmaf(pred, pred, st->sq[2]);
-    }
-    if constexpr (INP) pred = __builtin_fmaf(L.m[e], pred, L.om[e] * xo);
-    return pred;
+    const float cs = (NRB == 0 || L.cov[e]) ? c : u;
+    st->sq[0] = __builtin_fmaf(cs, cs, st->sq[0]);
+    st->sq[1] = __builtin_fmaf(u, u, st->sq[1]);
+    st->sq[2] = __builtin_fmaf(pred, pred, st->sq[2]);
 }
 
+// One channel's V elements: x' = K x + B, B = T0 + sum_r om_r T_r from the
+// channel's tables (coef: slot 0 and slots 1.. of the regions; the inpaint
+// blend of Heun's step keeps the chains at sigma and sigma' apart, the second
+// at kSet; the statistics' branch offsets at 2 kSet).
 template <int V, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL, bool ST = false>
 __device__ __forceinline__ void update_vec(const LaneState<V, NR>& L, const StepScalars& s,
                                            const float* __restrict__ coef, int c,
                                            const float (&xv)[V], const float (&ov)[V],
                                            float (&out)[V], LaneStats* st = nullptr) {
-    const float bu = coef[c];
-    const float bc = coef[BCG_MAX_CHANNELS + c];
-    float br[NRB > 0 ? NRB : 1];
+    constexpr bool TWO = INP && HEUN && !FINAL;
+    constexpr int NB = NRB > 0 ? NRB : 1;
+    const float t0 = coef[c];
+    float tr[NB];
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) br[r] = coef[(2 + r) * BCG_MAX_CHANNELS + c];
-    float bu2 = 0.f, bc2 = 0.f;
-    float br2[NRB > 0 ? NRB : 1];
-    if constexpr (HEUN && !FINAL) {
-        bu2 = coef[kSet + c];
-        bc2 = coef[kSet + BCG_MAX_CHANNELS + c];
+    for (int r = 0; r < NRB; ++r) tr[r] = coef[(1 + r) * BCG_MAX_CHANNELS + c];
+    float t0b = 0.0f, trb[NB];
+    if constexpr (TWO) {
+        t0b = coef[kSet + c];
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) br2[r] = coef[kSet + (2 + r) * BCG_MAX_CHANNELS + c];
+        for (int r = 0; r < NRB; ++r) trb[r] = coef[kSet + (1 + r) * BCG_MAX_CHANNELS + c];
+    }
+    float bu = 0.0f, bc = 0.0f, br[NB];
+    if constexpr (ST) {
+        bu = coef[2 * kSet + c];
+        bc = coef[2 * kSet + BCG_MAX_CHANNELS + c];
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) br[r] = coef[2 * kSet + (2 + r) * BCG_MAX_CHANNELS + c];
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         const float x = xv[e];
-        const float pb = guided_pred<V, NR, NRB, INP, ONE, ST>(L, e, x, ov[e], s.a, s.w, bu, bc, br, st);
-        if constexpr (FINAL) {
-            out[e] = pb;
-        } else if constexpr (!HEUN) {
-            out[e] = __builtin_fmaf(x - pb, s.q, x);
+        if constexpr (ST) stats_element<V, NR, NRB, ONE>(L, e, x, s.a, s.w, bu, bc, br, st);
+        float B = t0;
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) B = __builtin_fmaf(L.wr[r][e], tr[r], B);
+        if constexpr (!INP) {
+            out[e] = __builtin_fmaf(s.K, x, B);
+        } else if constexpr (TWO) {
+            float B2 = t0b;
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) B2 = __builtin_fmaf(L.wr[r][e], trb[r], B2);
+            out[e] = __builtin_fmaf(L.k[e], x, __builtin_fmaf(L.l1[e], B, __builtin_fmaf(L.l2[e], B2, L.lo[e] * ov[e])));
         } else {
-            const float d = (x - pb) * s.is;
-            const float xt = __builtin_fmaf(s.h, d, x);
-            const float pb2 = guided_pred<V, NR, NRB, INP, ONE>(L, e, xt, ov[e], s.a2, s.w, bu2, bc2, br2);
-            const float d2 = (xt - pb2) * s.isn;
-            out[e] = __builtin_fmaf(d + d2, s.hh, x);
+            out[e] = __builtin_fmaf(L.k[e], x, __builtin_fmaf(L.l1[e], B, L.lo[e] * ov[e]));
         }
     }
 }
@@ -331,36 +363,162 @@ __device__ __forceinline__ void setup_lane(LaneState<V, NR>& L, const SampleRegi
     }
 }
 
+// The per-pixel factors of the folded update: the region weights times the
+// pixel's guidance (om_r = weff * wh_r), and with inpainting the mask's
+// coefficients:
+//   last   k = m a, l1 = g m, lo = g (1 - m)
+//   Euler  k = fma(q, fma(-m, a, 1), 1), l1 = g m, lo = g (1 - m)
+//   Heun   A = fma(-m, a, 1) at sigma and sigma', f = A/sigma, f' = A'/sigma',
+//          G = fma(h, f', 1), k = fma(hh, fma(f', fma(h, f, 1), f), 1),
+//          l1 = ((-hh/sigma) G) m, l2 = (-hh/sigma') m, lo = (-hh fma(1/sigma, G, 1/sigma')) (1 - m)
+// (each "/sigma" a product with the correctly rounded reciprocal).
+template <int V, int NR, int NRB, bool INP, bool HEUN, bool FINAL>
+__device__ __forceinline__ void fold_lane(LaneState<V, NR>& L, const StepScalars& s) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) L.wr[r][e] = L.weff[e] * L.wh[r][e];
+        if constexpr (INP) {
+            const float m = L.m[e], om = L.om[e];
+            const float al = s.a;
+            if constexpr (FINAL) {
+                L.k[e] = m * al;
+                L.l1[e] = s.g * m;
+                L.lo[e] = s.g * om;
+            } else if constexpr (!HEUN) {
+                L.k[e] = __builtin_fmaf(s.q, __builtin_fmaf(-m, al, 1.0f), 1.0f);
+                L.l1[e] = s.g * m;
+                L.lo[e] = s.g * om;
+            } else {
+                const float f1 = s.is * __builtin_fmaf(-m, al, 1.0f);
+                const float f2 = s.isn * __builtin_fmaf(-m, s.a2, 1.0f);
+                const float G = __builtin_fmaf(s.h, f2, 1.0f);
+                const float nh = -s.hh;
+                L.k[e] = __builtin_fmaf(s.hh, __builtin_fmaf(f2, __builtin_fmaf(s.h, f1, 1.0f), f1), 1.0f);
+                L.l1[e] = ((nh * s.is) * G) * m;
+                L.l2[e] = (nh * s.isn) * m;
+                L.lo[e] = (nh * __builtin_fmaf(s.is, G, s.isn)) * om;
+            }
+        }
+    }
+}
+
 // A lane's vectors vi0, vi0 + blockDim, ... (p.vpt of them) of one sample.
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
 __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b,
                                          LaneState<V, NR>& L, const SampleRegions<NR>& sr,
                                          const StepParams& p, const StepScalars& s,
-                                         const float* __restrict__ coef, int i, int vi0, int rot, bool keep_u,
-                                         LaneStats* st) {
+                                         const float* __restrict__ coef, int i, int ri, int vi0, int rot,
+                                         bool keep_u, LaneStats* st) {
     const int C = p.C;
-    const int64_t sbase = (int64_t)i * C * p.HW;
+    const int64_t sbase = (int64_t)i * C * p.HW;   // the slot's state
+    const int64_t rbase = (int64_t)ri * C * p.HW;  // its request's original latent
     for (int v = 0; v < p.vpt; ++v) {
         const int vi = vi0 + v * (int)blockDim.x;
         if (vi >= p.nvec) return;
         const int64_t p0 = (int64_t)vi * V;
         const T* xs = static_cast<const T*>(p.x) + sbase + p0;
         T* xd = static_cast<T*>(p.x_out) + sbase + p0;
-        const T* xo = INP ? static_cast<const T*>(p.x_orig) + sbase + p0 : nullptr;
+        const T* xo = INP ? static_cast<const T*>(p.x_orig) + rbase + p0 : nullptr;
         // the next pass's pixels (its head stage is requested during this pass)
         const int nvi = vi + (int)blockDim.x;
         const bool more = TN::PF && v + 1 < p.vpt && nvi < p.nvec;
         const int64_t np0 = (int64_t)nvi * V;
         const T* nxs = more ? static_cast<const T*>(p.x) + sbase + np0 : nullptr;
-        const T* nxo = (more && INP) ? static_cast<const T*>(p.x_orig) + sbase + np0 : nullptr;
+        const T* nxo = (more && INP) ? static_cast<const T*>(p.x_orig) + rbase + np0 : nullptr;
         if (v > 0) {
             if (!TN::PF) load_stage<T, V, TN, INP>(a, xs, xo, 0, rot, C, p.HW);  // else requested during the last pass
-            setup_lane<V, NR, NRB, INP>(L, sr, p, i, p0, s.w, keep_u);
+            setup_lane<V, NR, NRB, INP>(L, sr, p, ri, p0, s.w, keep_u);
         }
+        fold_lane<V, NR, NRB, INP, HEUN, FINAL>(L, s);
         const bool in_b = channel_loop<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, b, L, s, coef, xs, xd, xo,
                                                                                   nxs, nxo, rot, C, p.HW, v == 0,
                                                                                   st, p.stats_group);
         if (more && in_b) a = b;
+    }
+}
+
+// A request joining at this step (continuous batching): its state is built
+// from its noise at the step's sigma -- noise * sigma, plus its original
+// latent when inpainting (one fused multiply-add), stored in the storage
+// dtype -- and stepped at once; the slot's previous contents are not read.
+// The walk is pipelined like the slot's own (two stages, the next one's loads
+// in flight during a compute), a stage holding UJ channels of fp32 noise: half
+// the stage width for bf16 storage, so the noise takes the registers the
+// state's stages take.
+template <typename T, int V, typename TN, bool INP>
+struct JoinStage {
+    static constexpr int UJ = sizeof(T) == 2 ? (TN::U > 1 ? TN::U / 2 : 1) : TN::U;
+    f32x4_t nz[UJ][V / 4];
+    typename Io<T, V>::Raw o[INP ? UJ : 1];
+};
+
+template <typename T, int V, typename TN, bool INP>
+__device__ __forceinline__ void join_load(JoinStage<T, V, TN, INP>& sg, const StepParams& p, int64_t rbase,
+                                          int64_t p0, int c0, int rot) {
+    constexpr int UJ = JoinStage<T, V, TN, INP>::UJ;
+#pragma unroll
+    for (int u = 0; u < UJ; ++u) {
+        if (c0 + u < p.C) {
+            const int64_t ro = rbase + plane_offset(walk_channel(c0 + u, rot, p.C), p.HW) + p0;
+#pragma unroll
+            for (int q = 0; q < V / 4; ++q)
+                sg.nz[u][q] = ld<TN::NT>(reinterpret_cast<const f32x4_t*>(p.noise + ro) + q);
+            if constexpr (INP) sg.o[u] = Io<T, V>::template load_raw<TN::NT>(static_cast<const T*>(p.x_orig) + ro);
+        }
+    }
+}
+
+template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+__device__ __forceinline__ void join_compute(const JoinStage<T, V, TN, INP>& sg, const LaneState<V, NR>& L,
+                                             const StepScalars& s, const float* __restrict__ coef,
+                                             const StepParams& p, T* xd, int c0, int rot, float sig) {
+    constexpr int UJ = JoinStage<T, V, TN, INP>::UJ;
+#pragma unroll
+    for (int u = 0; u < UJ; ++u) {
+        if (c0 + u < p.C) {
+            const int c = walk_channel(c0 + u, rot, p.C);
+            float ov[V], xv[V], out[V];
+            if constexpr (INP) Io<T, V>::unpack(sg.o[u], ov);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float nz = sg.nz[u][e / 4][e % 4];
+                if constexpr (!INP) ov[e] = 0.0f;
+                xv[e] = INP ? __builtin_fmaf(nz, sig, ov[e]) : nz * sig;
+            }
+            Io<T, V>::unpack(Io<T, V>::pack(xv), xv);  // the stored state
+            update_vec<V, NR, NRB, INP, HEUN, ONE, FINAL>(L, s, coef, c, xv, ov, out);
+            Io<T, V>::template store<TN::NT>(xd + plane_offset(c, p.HW), out);
+        }
+    }
+}
+
+template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN, bool ONE, bool FINAL>
+__device__ __forceinline__ void join_lane(LaneState<V, NR>& L, const SampleRegions<NR>& sr, const StepParams& p,
+                                          const StepScalars& s, const float* __restrict__ coef, int i, int ri,
+                                          int vi0, int rot, bool keep_u, float sig) {
+    typedef JoinStage<T, V, TN, INP> JS;
+    constexpr int UJ = JS::UJ;
+    const int C = p.C;
+    const int64_t rbase = (int64_t)ri * C * p.HW;
+    for (int v = 0; v < p.vpt; ++v) {
+        const int vi = vi0 + v * (int)blockDim.x;
+        if (vi >= p.nvec) return;
+        const int64_t p0 = (int64_t)vi * V;
+        T* xd = static_cast<T*>(p.x_out) + (int64_t)i * C * p.HW + p0;
+        JS a, b;
+        join_load<T, V, TN, INP>(a, p, rbase, p0, 0, rot);
+        if (UJ < C) join_load<T, V, TN, INP>(b, p, rbase, p0, UJ, rot);
+        if (v > 0) setup_lane<V, NR, NRB, INP>(L, sr, p, ri, p0, s.w, keep_u);
+        fold_lane<V, NR, NRB, INP, HEUN, FINAL>(L, s);
+        for (int c0 = 0;; c0 += 2 * UJ) {
+            join_compute<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(a, L, s, coef, p, xd, c0, rot, sig);
+            if (c0 + UJ >= C) break;
+            if (c0 + 2 * UJ < C) join_load<T, V, TN, INP>(a, p, rbase, p0, c0 + 2 * UJ, rot);
+            join_compute<T, V, TN, NR, NRB, INP, HEUN, ONE, FINAL>(b, L, s, coef, p, xd, c0 + UJ, rot, sig);
+            if (c0 + 2 * UJ >= C) break;
+            if (c0 + 3 * UJ < C) join_load<T, V, TN, INP>(b, p, rbase, p0, c0 + 3 * UJ, rot);
+        }
     }
 }
 
@@ -371,11 +529,11 @@ __device__ __forceinline__ void run_lane(Stage<T, V, TN::U, INP>& a, Stage<T, V,
 template <typename T, int V, typename TN, int NR, int NRB, bool INP, bool HEUN>
 __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, Stage<T, V, TN::U, INP>& b, bool lane_ok,
                                            const SampleRegions<NR>& sr, const StepParams& p,
-                                           StepScalars s, float* coef, int i, int vi0, int rot, bool keep_u,
-                                           float sig, float sgn, float mu_u, float mu_c,
+                                           StepScalars s, float* coef, int i, int ri, bool join, int vi0,
+                                           int rot, bool keep_u, float sig, float sgn, float mu_u, float mu_c,
                                            const float (&mu_r)[NR > 0 ? NR : 1]) {
     LaneState<V, NR> L;
-    if (lane_ok) setup_lane<V, NR, NRB, INP>(L, sr, p, i, (int64_t)vi0 * V, s.w, keep_u);
+    if (lane_ok) setup_lane<V, NR, NRB, INP>(L, sr, p, ri, (int64_t)vi0 * V, s.w, keep_u);
 
     const int C = p.C;
     const float s2 = p.s2;
@@ -383,18 +541,80 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, Stage<T, 
     const float den = s2 + v;
     const float v2 = sgn * sgn;
     const float den2 = s2 + v2;
+    const bool one = (s.w == 1.0f);
+    const bool fin = (sgn == 0.0f);
+    const bool two = HEUN && !fin;  // Heun's second evaluation takes part
+    // the sample's scalars of the folded update
+    s.a = s2 / den;
+    s.a2 = s2 / den2;
+    const float b1 = v / den;
+    s.h = sgn - sig;
+    s.q = s.h / sig;
+    s.is = 1.0f / sig;
+    s.isn = 1.0f / sgn;
+    s.hh = s.h * 0.5f;
+    s.c1 = 0.0f;
+    s.c2 = 0.0f;
+    if (!two) {
+        s.g = fin ? 1.0f : -s.q;
+        s.K = fin ? s.a : __builtin_fmaf(s.q, b1, 1.0f);
+    } else {
+        const float e1 = b1 * s.is, e2 = (v2 / den2) * s.isn, nh = -s.hh;
+        s.g = 1.0f;
+        s.K = __builtin_fmaf(s.hh, __builtin_fmaf(e2, __builtin_fmaf(s.h, e1, 1.0f), e1), 1.0f);
+        s.c1 = (nh * s.is) * __builtin_fmaf(s.h, e2, 1.0f);
+        s.c2 = nh * s.isn;
+    }
+    // Channel k's tables (lane k): the offsets at sigma (and sigma'), folded
+    // with the step's weights unless the inpaint blend needs them apart.
     const int k = (int)threadIdx.x & 63;
     if (k < C) {
-        coef[k] = (v * mu_u) / den;
-        coef[BCG_MAX_CHANNELS + k] = (v * mu_c) / den;
-        if constexpr (HEUN) {
-            coef[kSet + k] = (v2 * mu_u) / den2;
-            coef[kSet + BCG_MAX_CHANNELS + k] = (v2 * mu_c) / den2;
-        }
+        constexpr int NB = NRB > 0 ? NRB : 1;
+        float t0, tr[NB], t0b = 0.0f, trb[NB];
+        const float bu = (v * mu_u) / den;
+        if constexpr (NRB == 0) {
+            t0 = one ? (v * mu_c) / den : __builtin_fmaf(s.w, (v * (mu_c - mu_u)) / den, bu);
+        } else {
+            t0 = bu;
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) {
-            coef[(2 + r) * BCG_MAX_CHANNELS + k] = (v * mu_r[r]) / den;
-            if constexpr (HEUN) coef[kSet + (2 + r) * BCG_MAX_CHANNELS + k] = (v2 * mu_r[r]) / den2;
+            for (int r = 0; r < NRB; ++r) tr[r] = (v * (mu_r[r] - mu_u)) / den;
+        }
+        if (two) {
+            const float bub = (v2 * mu_u) / den2;
+            if constexpr (NRB == 0) {
+                t0b = one ? (v2 * mu_c) / den2 : __builtin_fmaf(s.w, (v2 * (mu_c - mu_u)) / den2, bub);
+            } else {
+                t0b = bub;
+#pragma unroll
+                for (int r = 0; r < NRB; ++r) trb[r] = (v2 * (mu_r[r] - mu_u)) / den2;
+            }
+        }
+        if constexpr (!INP) {
+            if (two) {
+                coef[k] = __builtin_fmaf(s.c1, t0, s.c2 * t0b);
+#pragma unroll
+                for (int r = 0; r < NRB; ++r)
+                    coef[(1 + r) * BCG_MAX_CHANNELS + k] = __builtin_fmaf(s.c1, tr[r], s.c2 * trb[r]);
+            } else {
+                coef[k] = s.g * t0;
+#pragma unroll
+                for (int r = 0; r < NRB; ++r) coef[(1 + r) * BCG_MAX_CHANNELS + k] = s.g * tr[r];
+            }
+        } else {
+            coef[k] = t0;
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) coef[(1 + r) * BCG_MAX_CHANNELS + k] = tr[r];
+            if (two) {
+                coef[kSet + k] = t0b;
+#pragma unroll
+                for (int r = 0; r < NRB; ++r) coef[kSet + (1 + r) * BCG_MAX_CHANNELS + k] = trb[r];
+            }
+        }
+        if constexpr (TN::STATS) {  // the branch offsets of the statistics
+            coef[2 * kSet + k] = bu;
+            coef[2 * kSet + BCG_MAX_CHANNELS + k] = (v * mu_c) / den;
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) coef[2 * kSet + (2 + r) * BCG_MAX_CHANNELS + k] = (v * mu_r[r]) / den;
         }
     }
     // LDS writes of this wavefront become visible to all its lanes.
@@ -403,22 +623,25 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, Stage<T, 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (!lane_ok) return;
 
-    s.a = s2 / den;
-    s.a2 = s2 / den2;
-    s.q = (sgn - sig) / sig;
-    s.h = sgn - sig;
-    s.is = 1.0f / sig;
-    s.isn = 1.0f / sgn;
-    s.hh = s.h * 0.5f;
-    const bool one = (s.w == 1.0f);
-    const bool fin = (sgn == 0.0f);
     LaneStats st = {{0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f}};
+    if constexpr (TN::QUEUE) {
+        if (join) {
+            if (one) {
+                if (fin) join_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(L, sr, p, s, coef, i, ri, vi0, rot, keep_u, sig);
+                else join_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(L, sr, p, s, coef, i, ri, vi0, rot, keep_u, sig);
+            } else {
+                if (fin) join_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(L, sr, p, s, coef, i, ri, vi0, rot, keep_u, sig);
+                else join_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(L, sr, p, s, coef, i, ri, vi0, rot, keep_u, sig);
+            }
+            return;
+        }
+    }
     if (one) {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, true, true>(a, b, L, sr, p, s, coef, i, ri, vi0, rot, keep_u, &st);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, true, false>(a, b, L, sr, p, s, coef, i, ri, vi0, rot, keep_u, &st);
     } else {
-        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
-        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, b, L, sr, p, s, coef, i, vi0, rot, keep_u, &st);
+        if (fin) run_lane<T, V, TN, NR, NRB, INP, HEUN, false, true>(a, b, L, sr, p, s, coef, i, ri, vi0, rot, keep_u, &st);
+        else run_lane<T, V, TN, NR, NRB, INP, HEUN, false, false>(a, b, L, sr, p, s, coef, i, ri, vi0, rot, keep_u, &st);
     }
     if constexpr (TN::STATS) {
         // the first lane of each row group writes the group's sums of row
@@ -447,7 +670,7 @@ __device__ __forceinline__ void run_sample(Stage<T, V, TN::U, INP>& a, Stage<T, 
 template <typename T, int V, int NR, bool INP, bool HEUN, typename TN = DefaultTune>
 __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     __shared__ union {
-        float coef[4][2 * kSet];               // one slice per wavefront
+        float coef[4][(TN::STATS ? 3 : 2) * kSet];  // one slice per wavefront
         int plan[kPlanLds];                    // the plan workgroup's counters
     } sh;
     if ((int)blockIdx.x == p.plan_block) {
@@ -455,8 +678,23 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         return;
     }
     float* coef = sh.coef[threadIdx.x >> 6];
-    const int j = blockIdx.x / p.tiles;
-    const int tile = blockIdx.x - j * p.tiles;
+    // Continuous batching puts join_front groups of workgroups first, each
+    // taking a slot whose request joins now (the plan lists them).
+    int jb = (int)blockIdx.x;
+    bool front = false;
+    if constexpr (TN::QUEUE) {
+        const int nf = p.join_front * p.tiles;
+        if (jb < nf) {
+            const int fslot = p.join_in[jb / p.tiles];
+            if (fslot < 0 || fslot >= p.n) return;
+            front = true;
+            jb = fslot * p.tiles + (jb - (jb / p.tiles) * p.tiles);
+        } else {
+            jb -= nf;
+        }
+    }
+    const int j = jb / p.tiles;
+    const int tile = jb - j * p.tiles;
     if (j >= p.n_active) return;
     const int i = p.identity ? j : p.order[j];
     if (i < 0 || i >= p.n) return;
@@ -464,29 +702,6 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     const int vi0 = tile * (int)blockDim.x * p.vpt + (int)threadIdx.x;
     const bool lane_ok = vi0 < p.nvec;
 
-    // Channel k's means (lane k), the region tables and the first two stages
-    // of the latent's walk, all requested before anything waits: every region slot below NR
-    // is read (the slot index clamped to the table's R), and the sample's
-    // count only selects among them afterwards.
-    const int k = (int)threadIdx.x & 63;
-    const int kk = k < C ? k : 0;
-    const float mu_u = p.mu_uncond[(int64_t)i * C + kk];
-    const float mu_c = p.mu_cond[(int64_t)i * C + kk];
-    int cnt = 0;
-    float mu_r[NR > 0 ? NR : 1];
-    int4 box[NR > 0 ? NR : 1];
-    float str[NR > 0 ? NR : 1];
-    if constexpr (NR > 0) {
-        cnt = p.region_count[i];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const int64_t slot = (int64_t)i * p.R + (r < p.R ? r : p.R - 1);
-            const int32_t* b = p.region_box + slot * 4;
-            box[r] = make_int4(b[0], b[1], b[2], b[3]);
-            str[r] = p.region_strength[slot];
-            mu_r[r] = p.mu_region[slot * C + kk];
-        }
-    }
     // The workgroup's channel walk starts at channel 7*blockIdx mod C, so the
     // workgroups in flight spread their requests over the channel planes
     // instead of all reading one plane's rows at a time.  (Workgroup b runs on
@@ -495,10 +710,57 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     // slower per launch, 1 and 15 1.2-2.5 us slower.)
     const int rot = (int)((7u * blockIdx.x) % (unsigned)C);
     Stage<T, V, TN::U, INP> a, b;
-    if (lane_ok) {
-        const int64_t base = (int64_t)i * C * p.HW + (int64_t)vi0 * V;
-        const T* xs0 = static_cast<const T*>(p.x) + base;
-        const T* xo0 = INP ? static_cast<const T*>(p.x_orig) + base : nullptr;
+    const int64_t p0 = (int64_t)vi0 * V;
+    const T* xs0 = static_cast<const T*>(p.x) + (int64_t)i * C * p.HW + p0;
+
+    // Continuous batching: the slot's record names its request, whose tables
+    // the step reads, and says whether the request joins now.  Without
+    // inpainting the slot's first stages are requested before the record is
+    // consulted (they are in bounds whatever it says, and unused when the
+    // request joins).
+    int ri = i;
+    bool join = false;
+    float4 qrec;
+    if constexpr (TN::QUEUE) {
+        qrec = reinterpret_cast<const float4*>(p.record_in)[i];
+        if constexpr (!INP) {
+            if (lane_ok && !front) {
+                load_stage<T, V, TN, INP>(a, xs0, nullptr, 0, rot, C, p.HW);
+                if (TN::U < C) load_stage<T, V, TN, INP>(b, xs0, nullptr, TN::U, rot, C, p.HW);
+            }
+        }
+        const uint32_t fl = __float_as_uint(qrec.w);
+        if (!(fl & 1u)) return;
+        if (((fl & 128u) != 0) != front) return;  // a front join: left to (or taken by) the front groups
+        ri = (int)(fl >> 8);
+        join = (fl & 64u) != 0;
+    }
+
+    // Channel k's means (lane k), the region tables and the first two stages
+    // of the latent's walk, all requested before anything waits: every region slot below NR
+    // is read (the slot index clamped to the table's R), and the sample's
+    // count only selects among them afterwards.
+    const int k = (int)threadIdx.x & 63;
+    const int kk = k < C ? k : 0;
+    const float mu_u = p.mu_uncond[(int64_t)ri * C + kk];
+    const float mu_c = p.mu_cond[(int64_t)ri * C + kk];
+    int cnt = 0;
+    float mu_r[NR > 0 ? NR : 1];
+    int4 box[NR > 0 ? NR : 1];
+    float str[NR > 0 ? NR : 1];
+    if constexpr (NR > 0) {
+        cnt = p.region_count[ri];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int64_t slot = (int64_t)ri * p.R + (r < p.R ? r : p.R - 1);
+            const int32_t* b = p.region_box + slot * 4;
+            box[r] = make_int4(b[0], b[1], b[2], b[3]);
+            str[r] = p.region_strength[slot];
+            mu_r[r] = p.mu_region[slot * C + kk];
+        }
+    }
+    if (lane_ok && !join && !(TN::QUEUE && !INP)) {
+        const T* xo0 = INP ? static_cast<const T*>(p.x_orig) + (int64_t)ri * C * p.HW + p0 : nullptr;
         load_stage<T, V, TN, INP>(a, xs0, xo0, 0, rot, C, p.HW);
         if (TN::U < C) load_stage<T, V, TN, INP>(b, xs0, xo0, TN::U, rot, C, p.HW);
     }
@@ -516,7 +778,9 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
     bool keep_u;
     unsigned valid = 0xfu;  // regions taking part in this step
     if (p.record_in) {
-        const float4 r = reinterpret_cast<const float4*>(p.record_in)[i];
+        float4 r;
+        if constexpr (TN::QUEUE) r = qrec;
+        else r = reinterpret_cast<const float4*>(p.record_in)[i];
         const uint32_t fl = __float_as_uint(r.w);
         if (!(fl & 1u)) return;
         sig = r.x;
@@ -557,9 +821,11 @@ __global__ __launch_bounds__(256) void guided_step_kernel(const StepParams p) {
         }
     }
     if (NR > 0 && cnt > 0)
-        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, b, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
+        run_sample<T, V, TN, NR, NR, INP, HEUN>(a, b, lane_ok, sr, p, s, coef, i, ri, join, vi0, rot, keep_u, sig, sgn,
+                                                mu_u, mu_c, mu_r);
     else
-        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, b, lane_ok, sr, p, s, coef, i, vi0, rot, keep_u, sig, sgn, mu_u, mu_c, mu_r);
+        run_sample<T, V, TN, NR, 0, INP, HEUN>(a, b, lane_ok, sr, p, s, coef, i, ri, join, vi0, rot, keep_u, sig, sgn,
+                                               mu_u, mu_c, mu_r);
 }
 
 // Pipeline shape of a kernel variant: channels per stage (4 puts more latent
@@ -621,6 +887,46 @@ void launch_variant(const StepParams& p, dim3 grid, dim3 blk, hipStream_t st) {
         hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, Wide>), grid, blk, 0, st, p);
     else
         hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, Narrow>), grid, blk, 0, st, p);
+}
+
+// Continuous batching: the streaming variants whose slots hold requests (the
+// full-stage shape where C allows it, else two-channel stages).
+template <typename T, int V, int NR, bool INP, bool HEUN>
+void launch_queue_variant(const StepParams& p, dim3 grid, dim3 blk, hipStream_t st) {
+    typedef StageTune<T, NR, INP, HEUN, true> Wide;
+    typedef Tune<Wide::U, true, Wide::PF, true> WideFull;
+    typedef Tune<2, true, false> Narrow;
+    if (p.C > 4 && p.C % (2 * Wide::U) == 0)
+        hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, QueueOf<WideFull>>), grid, blk, 0, st, p);
+    else
+        hipLaunchKernelGGL((guided_step_kernel<T, V, NR, INP, HEUN, QueueOf<Narrow>>), grid, blk, 0, st, p);
+}
+
+template <typename T, int NR>
+hipError_t launch_queue_nr(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
+    constexpr int V = VecWidth<T>::value;
+    const dim3 grid((unsigned)((int64_t)(p.join_front + p.n_active) * p.tiles + (p.plan_block >= 0 ? 1 : 0))),
+        blk((unsigned)block);
+    if (heun) {
+        if (inp) launch_queue_variant<T, V, NR, true, true>(p, grid, blk, st);
+        else launch_queue_variant<T, V, NR, false, true>(p, grid, blk, st);
+    } else {
+        if (inp) launch_queue_variant<T, V, NR, true, false>(p, grid, blk, st);
+        else launch_queue_variant<T, V, NR, false, false>(p, grid, blk, st);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_step_queue(const StepParams& p, bool heun, bool inp, int block, hipStream_t st) {
+    if (p.n_active == 0) return hipSuccess;
+    switch (p.R) {
+        case 0: return launch_queue_nr<T, 0>(p, heun, inp, block, st);
+        case 1: return launch_queue_nr<T, 1>(p, heun, inp, block, st);
+        case 2: return launch_queue_nr<T, 2>(p, heun, inp, block, st);
+        case 3: return launch_queue_nr<T, 3>(p, heun, inp, block, st);
+        default: return launch_queue_nr<T, 4>(p, heun, inp, block, st);
+    }
 }
 
 template <typename T, int V, int NR, typename TN = DefaultTune>

@@ -248,7 +248,8 @@ class GuidedSampler:
     # ------------------------------------------------------------ native loop
 
     def native_loop(self, x, x_out=None, upload_batch=8, async_upload=False, cache_hint=None,
-                    device_plan=False, graph_launches=0, plan_outputs=True, records=True):
+                    device_plan=False, graph_launches=0, plan_outputs=True, records=True,
+                    slots=None, ring=False, join_front=None):
         """A C++ loop (bcg_loop_*) advancing ``x`` (in place unless x_out).
 
         ``x`` may also be [replicas, n, C, H, W]: launch k then advances
@@ -256,9 +257,15 @@ class GuidedSampler:
         (independent batches served round-robin).  ``device_plan`` builds
         each step's plan on the device inside the step's launch (into
         ``loop.plan_out`` when ``plan_outputs``); ``graph_launches`` > 0
-        replays a captured graph of that many launches."""
+        replays a captured graph of that many launches.  ``slots`` (device
+        plans) runs continuous batching: x holds that many slots, this
+        sampler's samples are the queue of requests (the first ``slots``
+        start in the slots at their start steps, the rest wait), and a freed
+        slot takes the next request; ``ring`` serves the queue over and over;
+        ``join_front`` joins a step are dispatched first (default: twice the
+        mean refills per step plus 8, at most ``slots``)."""
         return NativeLoop(self, x, x_out, upload_batch, async_upload, cache_hint,
-                          device_plan, graph_launches, plan_outputs, records)
+                          device_plan, graph_launches, plan_outputs, records, slots, ring, join_front)
 
 
 class NativeLoop:
@@ -266,8 +273,14 @@ class NativeLoop:
 
     def __init__(self, s: GuidedSampler, x, x_out=None, upload_batch=8, async_upload=False,
                  cache_hint=None, device_plan=False, graph_launches=0,
-                 plan_outputs=True, records=True):
-        n = s.n
+                 plan_outputs=True, records=True, slots=None, ring=False, join_front=None):
+        queue = slots is not None
+        if queue and not (device_plan and records and 1 <= int(slots) <= s.n):
+            raise ValueError("continuous batching needs device plans with records and 1 <= slots <= n")
+        n = int(slots) if queue else s.n
+        J = 0
+        if queue:
+            J = min(n, 2 * (-(-n // s.steps)) + 8) if join_front is None else int(join_front)
         P = int(upload_batch)
         rows = 8 * P
         self.s = s
@@ -284,17 +297,25 @@ class NativeLoop:
             self.dev_steps = torch.empty((reps, 2, n), dtype=torch.int32, device=s.device)
             self.dev_records = (torch.zeros((reps, 2, n, 4), dtype=torch.float32, device=s.device)
                                 if records else None)
+            self.dev_queue = (torch.zeros((reps, 2, n + 1 + J), dtype=torch.int32, device=s.device)
+                              if queue else None)
             self.plan_out = api.device_plan_arrays(n, s.nb, s.device) if plan_outputs else None
+            qd = None
+            if queue:
+                qd = dict(len=s.n, ring=ring, noise=s.d_noise, slot_req_in=self.dev_queue[0, 0, :n],
+                          slot_req_out=self.dev_queue[0, 1, :n], queue_in=self.dev_queue[0, 0, n:n + 1],
+                          queue_out=self.dev_queue[0, 1, n:n + 1], join_front=J,
+                          join_in=self.dev_queue[0, 0, n + 1:], join_out=self.dev_queue[0, 1, n + 1:])
             dplan = api.device_plan(s.steps, s.d_table, self.dev_steps[0, 0],
                                     step_out=self.dev_steps[0, 1], cfg_override=s.d_override,
                                     covered=s.d_covered, wrap=s.wrap, out=self.plan_out,
                                     bucket_cfg_end=s.d_table_end, sigmas=s.d_sigmas,
                                     region_range=s.d_region_range, covered_sets=s.d_covered_sets,
-                                    region_count=s.d_region_count)
+                                    region_count=s.d_region_count, queue=qd)
         else:
             self.h_slab = torch.empty((rows, 4 * n), dtype=torch.int32, pin_memory=True)
             self.d_slab = torch.empty((rows, 4 * n), dtype=torch.int32, device=s.device)
-            self.dev_steps = self.dev_records = self.plan_out = None
+            self.dev_steps = self.dev_records = self.plan_out = self.dev_queue = None
             dplan = L.DevicePlan()
         keep = self._keep = []
 
@@ -314,19 +335,20 @@ class NativeLoop:
         ptr = api._ptr
         step = L.StepArgs(n, s.C, s.H, s.W, api._DT[s.tdtype], api._SAMPLER[s.sampler], R,
                           s.feather, 0, s.d_sigmas.numel(),
-                          1 if s.d_mask is not None and s.d_mask.shape[0] == n else 0,
+                          1 if s.d_mask is not None and s.d_mask.shape[0] == s.n else 0,
                           int(cache_hint), s.s2,
                           ptr(self.x), ptr(self.x_out), ptr(s.d_sigmas), None, None, None, None,
                           ptr(s.d_mu_u), ptr(s.d_mu_c), ptr(s.d_region_count),
                           ptr(s.d_region_box), ptr(s.d_region_strength), ptr(s.d_mu_region),
                           ptr(s.d_x_orig), ptr(s.d_mask), None, None, 0, ptr(s.d_region_range),
                           s.steps)
-        self.desc = L.LoopDesc(plan, npp(s.start, np.int32), 1 if s.wrap else 0, rows,
+        self.desc = L.LoopDesc(plan, npp(s.start[:n], np.int32), 1 if s.wrap else 0, rows,
                                api._ptr(self.h_slab), api._ptr(self.d_slab), reps,
                                stride if reps > 1 else 0, P, 1 if async_upload else 0,
                                step, 1 if device_plan else 0,
                                int(graph_launches), api._ptr(self.dev_steps), dplan,
-                               api._ptr(self.dev_records))
+                               api._ptr(self.dev_records), s.n if queue else 0, 1 if ring else 0,
+                               api._ptr(s.d_noise) if queue else None, api._ptr(self.dev_queue), J)
         self.handle = ct.c_void_p()
         L.check(L.lib().bcg_loop_create(ct.byref(self.desc), ct.byref(self.handle)))
 

@@ -331,6 +331,28 @@ size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
  * on another (its plan wrote them one launch earlier); they must describe
  * step_in.  bcg_plan_records builds them on the host for a first step.
  *
+ * Continuous batching (queue_len > 0; [B] section 3: one batch carries
+ * samples of several buckets, section 4 stage 3: the scheduler builds every
+ * step's plan): the n samples are slots, each holding a request of a queue of
+ * queue_len.  slot_req_in[s] is the request of slot s (-1: empty), step_in[s]
+ * its step; every per-sample table (cfg_override, covered, and the step's
+ * mu / region / x_orig / mask arrays) and `noise` are indexed by request.
+ * The plan (rows, order, ...) is over slots.  For the next step the plan
+ * workgroup writes step_out, slot_req_out, record_out and queue_out: a slot
+ * whose request takes its last step now (t = steps - 1), and an empty slot,
+ * takes the next queued request (freed slots in slot order, requests in
+ * queue order from *queue_in), which joins at step 0; with queue_ring the
+ * request ids run modulo queue_len (the pool is served over and over), else a
+ * slot left without a request gets step -1, request -1 and an all-zero
+ * record.  Records then also carry bit 6 = the request joins at this step
+ * and bits 8..31 = the request; a joining request's state is built inside
+ * guided_step_dplan from noise[r] * sigma (+ the stored x_orig[r] when
+ * inpainting, one fused multiply-add), rounded to the storage dtype, then
+ * stepped; the slot's previous contents are not read.  Requires records in
+ * and out, step_out, the 16-byte vector path, no stats and no validity
+ * ranges; wrap must be 0.  bcg_plan_records (OR'ing in the join bit and the
+ * request) gives the first step's records.
+ *
  * The device arrays are not validated (a host plan build validates the same
  * tables): bucket_cfg finite, cfg_override finite or NaN.
  */
@@ -369,6 +391,23 @@ typedef struct {
     const int32_t* region_count;     /* device [n] (with region_range; guided_step_dplan uses
                                         args->region_count) */
     int32_t max_regions;             /* R, the stride of region_range */
+    /* continuous batching (see above): */
+    int32_t queue_len;               /* 0: off; else the requests of the queue, < 2^24 */
+    int32_t queue_ring;              /* 0 | 1: request ids modulo queue_len */
+    const float* noise;              /* device fp32 [queue_len, C, H, W] */
+    const int32_t* slot_req_in;      /* device [n] request of each slot at this step */
+    int32_t* slot_req_out;           /* device [n] ... at the next step */
+    const int32_t* queue_in;         /* device [1] next queued request */
+    int32_t* queue_out;              /* device [1] ... after this step's refills */
+    int32_t join_front;              /* J in [0, n]: the launch starts with J groups of
+                                        workgroups that take this step's first J joins,
+                                        listed in join_in (-1: none), before the slots' own
+                                        (a joining request's step reads its fp32 noise, so it
+                                        runs first rather than at the end of the grid); the
+                                        plan lists the next step's in join_out, and flags
+                                        those records with bit 7 */
+    const int32_t* join_in;          /* device [J] */
+    int32_t* join_out;               /* device [J] */
 } bcg_device_plan;
 
 /*
@@ -678,6 +717,19 @@ typedef struct {
     float* dev_records;              /* device plans: device [replicas][2][n][4] or NULL: the
                                         sample records that go with dev_steps (each launch
                                         reads one buffer and its plan writes the other) */
+    /* continuous batching (device plans with records; see bcg_device_plan): the n samples
+       are slots, slot s starts with request s at step start[s] (in [0, steps)) and joins at
+       the first launch (its state is built there from its noise; x need not be initialised);
+       freed slots take the next queued requests.  The per-sample arrays of `plan`, `step`
+       and `dplan` hold queue_len requests (dplan.covered for every request when the step
+       has regions); wrap must be 0. */
+    int32_t queue_len;               /* 0: off; else the requests of the queue (>= n) */
+    int32_t queue_ring;              /* 0 | 1: request ids modulo queue_len */
+    const float* noise;              /* device fp32 [queue_len, C, H, W] */
+    int32_t* dev_queue;              /* device [replicas][2][n + 1 + join_front]: the slots'
+                                        requests, the next queued request and the list of
+                                        joins dispatched first (alternating like dev_steps) */
+    int32_t join_front;              /* J in [0, n], see bcg_device_plan */
 } bcg_loop_desc;
 
 typedef struct bcg_loop bcg_loop;

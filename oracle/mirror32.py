@@ -13,34 +13,59 @@ evaluated in the order written.  Mode M is pinned to mode D (``definition``) by 
 per-step tolerance and to the exact special cases (scale 0 -> uncond, scale 1
 -> cond, mask 0 -> original latent, ...).
 
-The evaluation order (a specification both sides implement independently):
+The evaluation order (a specification both sides implement independently).
+The update is linear in x for every path: pred = alpha*x + P with P free of
+x, so x' = K*x + B with K per sample (per pixel when inpainting) and B from
+per-channel tables; the tables and K are built once, and each element costs
+one fused multiply-add per region plus one.
 
-per sample, from sigma = sig[t], sigma' = sig[t+1]:
-    v = sigma*sigma; den = s2 + v; a = s2/den; b_k[c] = (v*mu_k[c])/den
-    Euler: q = (sigma' - sigma)/sigma
-    Heun:  h = sigma' - sigma; i = 1/sigma; i' = 1/sigma'; hh = h*0.5,
-           and a', b'_k from sigma' as above
+per sample, from sigma = sig[t], sigma' = sig[t+1], scale w:
+    v = sigma*sigma; den = s2 + v; a = s2/den; b1 = v/den
+    last step (sigma' == 0), Euler or Heun:  g = 1; K = a
+    Euler:  q = (sigma' - sigma)/sigma; g = -q; K = fma(q, b1, 1)
+    Heun:   v' = sigma'*sigma'; den' = s2 + v'; a' = s2/den'; b2 = v'/den'
+            h = sigma' - sigma; i1 = 1/sigma; i2 = 1/sigma'; hh = h*0.5; nh = -hh
+            e1 = b1*i1; e2 = b2*i2
+            K  = fma(hh, fma(e2, fma(h, e1, 1), e1), 1)
+            c1 = (nh*i1)*fma(h, e2, 1); c2 = nh*i2
+    mode A: scale != 1; mode B: scale == 1, uncond kept; mode C: uncond skipped
+    (a regional sample in mode C is stepped as in mode B: where no region has
+    weight the cond is the uncond, as the definition's regional sum falls back
+    to it; the plan skips the uncond only where the regions cover the latent)
+per channel c, at sigma (and at sigma' with v', den' for Heun):
+    bu = (v*mu_u)/den
+    no regions:  P = fma(w, (v*(mu_c - mu_u))/den, bu)   (mode A)
+                 P = (v*mu_c)/den                        (modes B, C)
+    regions:     t0 = bu, t_r = (v*(mu_r - mu_u))/den
+    (a regional sample none of whose regions is valid: regions, none of them)
+    tables without inpaint: T0 = g*t0, T_r = g*t_r (P: g*P)       (Euler, last)
+                            T0 = fma(c1, t0, c2*t0'), T_r likewise (Heun)
 per pixel (regional launches):
     f_r = float(ny_r*nx_r) * (1/F^4)  with ny = min(dy+1,F)*min(h_r-dy,F),
                                            nx likewise, 0 outside the box
     w_r = strength_r*f_r; W = ((w_0 + w_1) + w_2) ...
     covered = W > 0; iW = 1/W (0 if not covered); wh_r = w_r*iW
-    inpaint: om = 1 - m
-per element:
-    u  = fma(a, x, bu[c])
-    c  = fma(a, x, bc[c])                          (no regions)
-       = fma(wh_1, fma(a, x, br_1[c]), wh_0*fma(a, x, br_0[c])) ...   (regions:
-         c = wh_0*t_0, then c = fma(wh_r, t_r, c) for r = 1, 2, ...)
-    pred = fma(w, c - u, u)                  (scale != 1, no regions)
-         = fma(covered ? w : 0, c - u, u)    (scale != 1, regions)
-         = covered ? c : u                   (scale == 1, uncond kept)
-         = c                                 (uncond skipped)
-    pb = fma(m, pred, om*xo)  (inpaint)  else pred
-    sigma' == 0: x' = pb
-    Euler: x' = fma(x - pb, q, x)
-    Heun:  d = (x - pb)*i; xt = fma(h, d, x); pb2 = P'(xt);
-           d2 = (xt - pb2)*i'; x' = fma(d + d2, hh, x)
-    store float32, or round to bf16 (nearest, ties to even)
+    om_r = (covered ? w : 0)*wh_r
+per element, without inpaint:
+    B = T0 (or the P table); B = fma(om_r, T_r, B) for r = 0, 1, ...
+    x' = fma(K, x, B)
+with inpaint (mask m, om = 1 - m, original latent xo), per pixel:
+    last:  k = m*a; l1 = g*m; lo = g*om
+    Euler: k = fma(q, fma(-m, a, 1), 1); l1 = g*m; lo = g*om
+    Heun:  A1 = fma(-m, a, 1); A2 = fma(-m, a', 1); f1 = i1*A1;
+           f2 = i2*A2; G = fma(h, f2, 1); k = fma(hh, fma(f2, fma(h, f1, 1), f1), 1)
+           l1 = ((nh*i1)*G)*m; l2 = (nh*i2)*m; lo = (nh*fma(i1, G, i2))*om
+    per element: B1 = t0-chain at sigma (B1 = t0; B1 = fma(om_r, t_r, B1)), or P;
+           B2 likewise at sigma' (Heun)
+    Euler, last: x' = fma(k, x, fma(l1, B1, lo*xo))
+    Heun:        x' = fma(k, x, fma(l1, B1, fma(l2, B2, lo*xo)))
+store float32, or round to bf16 (nearest, ties to even)
+
+The two evaluations of Heun's step and the guidance combine are folded
+into K and the tables exactly (in real arithmetic): x' = x + h/2 (d + d2)
+with d = (x - pred(x))/sigma, xt = x + h d, d2 = (xt - pred(xt))/sigma',
+pred(x) = alpha x + P, gives the coefficients above; the regional cond
+sum_r wh_r (a x + b_r) uses sum_r wh_r = 1 on covered pixels.
 
 materialised branches (rows of the plan layout, storage dtype, read as float32):
     pred = c                                 (scale == 1)
@@ -137,42 +162,26 @@ class Params32:
         self.x_orig = None if x_orig is None else np.asarray(x_orig, np.float32)
 
 
-def _coef(sigma, prm):
+def _tables(sigma, w, mode, prm):
+    """Per-channel offsets at one sigma: (t0, [t_r]) for a regional sample,
+    (P, None) otherwise."""
     v = sigma * sigma
     den = prm.s2 + v
-    a = prm.s2 / den
     bu = (v * prm.mu_u) / den
-    bc = (v * prm.mu_c) / den
-    br = [(v * m) / den for m in prm.mu_r]
-    return a, bu, bc, br
+    if not prm.regional:
+        if mode == "A":
+            return fma32(w, (v * (prm.mu_c - prm.mu_u)) / den, bu), None
+        return (v * prm.mu_c) / den, None
+    return bu, [(v * (m - prm.mu_u)) / den for m in prm.mu_r]
 
 
-def _pred(x, sigma, w, mode, prm):
-    a, bu, bc, br = _coef(sigma, prm)
-    u = fma32(a, x, bu[:, None, None])
-    if prm.nr == 0 and prm.regional:
-        c = u
-    elif prm.nr == 0:
-        c = fma32(a, x, bc[:, None, None])
-    else:
-        c = prm.wh[0][None] * fma32(a, x, br[0][:, None, None])
-        for r in range(1, prm.nr):
-            c = fma32(prm.wh[r][None], fma32(a, x, br[r][:, None, None]), c)
-    if mode == "C":
-        pred = c
-    elif mode == "B":
-        pred = c if prm.nr == 0 else np.where(prm.covered[None], c, u)
-    else:
-        if prm.nr == 0:
-            pred = fma32(w, c - u, u)
-        else:
-            weff = np.where(prm.covered, w, f32(0)).astype(np.float32)
-            pred = fma32(weff[None], c - u, u)
-    if prm.mask is not None:
-        m = prm.mask[None]
-        om = f32(1) - m
-        pred = fma32(m, pred, om * prm.x_orig)
-    return np.asarray(pred, np.float32)
+def _chain(t0, tr, om):
+    """B = t0; B = fma(om_r, t_r, B) over the regions, per element."""
+    B = np.broadcast_to(t0[:, None, None], (t0.shape[0],) + (om[0].shape if om else (1, 1)))
+    B = np.asarray(B, np.float32)
+    for o, t in zip(om, tr or []):
+        B = fma32(o[None], t[:, None, None], B)
+    return B
 
 
 def step32(x, sigma, sigma_next, w, need_uncond, prm, sampler):
@@ -180,21 +189,66 @@ def step32(x, sigma, sigma_next, w, need_uncond, prm, sampler):
     x = np.asarray(x, np.float32)
     sigma, sigma_next, w = f32(sigma), f32(sigma_next), f32(w)
     mode = "C" if not need_uncond else ("B" if w == f32(1) else "A")
-    pb = _pred(x, sigma, w, mode, prm)
-    if sigma_next == f32(0):
-        return pb
-    if sampler == "euler":
+    one, s2 = f32(1), prm.s2
+    v = sigma * sigma
+    den = s2 + v
+    a = s2 / den
+    b1 = v / den
+    last = sigma_next == f32(0)
+    heun = sampler == "heun" and not last
+    if last:
+        g, K = one, a
+    elif not heun:
         q = (sigma_next - sigma) / sigma
-        return fma32(x - pb, q, x)
-    h = sigma_next - sigma
-    i1 = f32(1) / sigma
-    i2 = f32(1) / sigma_next
-    hh = h * f32(0.5)
-    d = (x - pb) * i1
-    xt = fma32(h, d, x)
-    pb2 = _pred(xt, sigma_next, w, mode, prm)
-    d2 = (xt - pb2) * i2
-    return fma32(d + d2, hh, x)
+        g, K = -q, fma32(q, b1, one)
+    else:
+        v2 = sigma_next * sigma_next
+        den2 = s2 + v2
+        a2 = s2 / den2
+        b2 = v2 / den2
+        h = sigma_next - sigma
+        i1 = one / sigma
+        i2 = one / sigma_next
+        hh = h * f32(0.5)
+        nh = -hh
+        e1 = b1 * i1
+        e2 = b2 * i2
+        K = fma32(hh, fma32(e2, fma32(h, e1, one), e1), one)
+        c1 = (nh * i1) * fma32(h, e2, one)
+        c2 = nh * i2
+    t0, tr = _tables(sigma, w, mode, prm)
+    if heun:
+        t0b, trb = _tables(sigma_next, w, mode, prm)
+    om = []
+    if prm.regional and prm.nr:
+        weff = np.where(prm.covered, w, f32(0)).astype(np.float32)
+        om = [weff * wh for wh in prm.wh]
+    if prm.mask is None:
+        if heun:
+            T0 = fma32(c1, t0, c2 * t0b)
+            Tr = [fma32(c1, t, c2 * u) for t, u in zip(tr, trb)] if tr is not None else None
+        else:
+            T0 = g * t0
+            Tr = [g * t for t in tr] if tr is not None else None
+        return fma32(K, x, _chain(T0, Tr, om))
+    m = prm.mask[None]
+    omk = f32(1) - m
+    B1 = _chain(t0, tr, om)
+    xo = prm.x_orig
+    if not heun:
+        k = m * a if last else fma32(q, fma32(-m, a, one), one)
+        return fma32(k, x, fma32(g * m, B1, (g * omk) * xo))
+    A1 = fma32(-m, a, one)
+    A2 = fma32(-m, a2, one)
+    f1 = i1 * A1
+    f2 = i2 * A2
+    G = fma32(h, f2, one)
+    k = fma32(hh, fma32(f2, fma32(h, f1, one), f1), one)
+    l1 = ((nh * i1) * G) * m
+    l2 = (nh * i2) * m
+    lo = (nh * fma32(i1, G, i2)) * omk
+    B2 = _chain(t0b, trb, om)
+    return fma32(k, x, fma32(l1, B1, fma32(l2, B2, lo * xo)))
 
 
 def params32(inp, i, t=None):

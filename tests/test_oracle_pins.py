@@ -390,6 +390,9 @@ def test_bucket_count_invariance():
     dict(dtype="bf16", sampler="heun"),
     dict(dtype="bf16", sampler="euler", regions=2),
     dict(dtype="f32", sampler="heun", regions=3, region_ranges=True),
+    dict(dtype="f32", sampler="euler", regions=2, inpaint=True),
+    dict(dtype="bf16", sampler="euler", inpaint=True),
+    dict(dtype="f32", sampler="heun", inpaint=True),
 ])
 def test_mirror_per_step_within_tolerance_of_definition(kw):
     sp = W.small_spec(n=4, C=3, H=12, W=16, steps=7, **kw)
@@ -410,6 +413,30 @@ def test_mirror_per_step_within_tolerance_of_definition(kw):
                            bool(plan["need_uncond"][i]), M.params32(inp, i, ti), sp.sampler)
             assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
             x[i] = ref.astype(np.float32)
+
+
+@pytest.mark.parametrize("sampler", ["euler", "heun"])
+@pytest.mark.parametrize("inpaint", [False, True])
+def test_mirror_scale_one_within_tolerance_of_definition(sampler, inpaint):
+    """Scale 1, uncond skipped and kept, where one region covers the latent
+    and where coverage is partial, against the definition at w = 1, at an
+    interior step and at the last one (where no region has weight the cond
+    is the uncond in both)."""
+    sp = W.small_spec(n=2, C=3, H=12, W=16, steps=5, regions=2, inpaint=inpaint, sampler=sampler)
+    inp = W.make_inputs(sp)
+    inp.region_frac[0, 0] = (0.0, 0.0, 1.0, 1.0)
+    rng = np.random.default_rng(5)
+    for i, need_uncond in ((0, False), (1, True), (1, False)):
+        prmD, prmM = D.sample_params(inp, i), M.params32(inp, i)
+        if i == 0:
+            assert prmM.covered.all()
+        else:
+            assert not prmM.covered.all()
+        x = (3.0 * rng.standard_normal((sp.C, sp.H, sp.W))).astype(np.float32)
+        for s0, s1 in ((3.0, 2.0), (0.4, 0.0)):
+            ref = D.step(x, s0, s1, 1.0, prmD, sampler)
+            got = M.step32(x, s0, s1, 1.0, need_uncond, prmM, sampler)
+            assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
 
 
 def test_mirror_exact_special_cases():
