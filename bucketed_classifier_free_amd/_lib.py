@@ -120,6 +120,51 @@ class LoopDesc(C.Structure):
 _lib = None
 
 
+def _signatures():
+    """Argument and result types of every exported function."""
+    ip = C.POINTER(C.c_int)
+    return {
+        "bcg_last_error": ([], C.c_char_p),
+        "bcg_abi_version": ([], C.c_int),
+        "sigma_schedule": ([C.c_int, C.c_double, C.c_double, C.c_int, C.c_double, vp, ip], C.c_int),
+        "bucket_table": ([C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp], C.c_int),
+        "bucket_bounds": ([C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp, vp], C.c_int),
+        "sigma_crop": ([vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, ip], C.c_int),
+        "bcg_plan_build": ([C.POINTER(PlanIn), C.POINTER(PlanOut)], C.c_int),
+        "bcg_plan_records": ([C.c_int, C.c_int, vp, vp, vp, vp, vp, C.c_int, vp], C.c_int),
+        "guided_step": ([C.POINTER(StepArgs), vp], C.c_int),
+        "bcg_plan_device": ([C.c_int, C.POINTER(DevicePlan), vp], C.c_int),
+        "guided_step_rows": ([C.POINTER(RowsArgs), vp], C.c_int),
+        "guided_step_rows_dplan": ([C.POINTER(RowsArgs), C.POINTER(DevicePlan), vp], C.c_int),
+        "guided_step_dplan": ([C.POINTER(StepArgs), C.POINTER(DevicePlan), vp], C.c_int),
+        "guided_step_dplan_static": ([C.POINTER(StepArgs), C.POINTER(DevicePlan), vp], C.c_int),
+        "guided_step_workspace_size": ([C.c_int] * 5, C.c_size_t),
+        "latent_init": ([C.c_int] * 5 + [vp, vp, vp, C.c_int, vp, vp, vp], C.c_int),
+        "area_accumulate": ([C.c_int] * 6 + [vp, C.c_int64] + [vp] * 7 + [vp], C.c_int),
+        "mask_blend": ([C.c_int] * 5 + [vp, vp, vp, C.c_int, vp, vp], C.c_int),
+        "bcg_loop_create": ([C.POINTER(LoopDesc), C.POINTER(vp)], C.c_int),
+        "bcg_loop_run": ([vp, C.c_int, C.c_int, vp, C.POINTER(C.c_float)], C.c_int),
+        "bcg_loop_destroy": ([vp], C.c_int),
+        "bcg_loop_last_run": ([vp, C.POINTER(C.c_int32), C.POINTER(C.c_int32)], C.c_int),
+        "weight_patch": ([C.POINTER(WeightArgs), vp], C.c_int),
+    }
+
+
+# The functions of the host half (bcg_host.cpp: plain C++, no GPU calls).
+HOST_EXPORTS = ["bcg_last_error", "bcg_abi_version", "sigma_schedule", "bucket_table", "bucket_bounds",
+                "sigma_crop", "bcg_plan_build", "bcg_plan_records"]
+
+
+def configure(cdll, names):
+    """Set the argument and result types of the functions ``names`` of a
+    loaded library and return it."""
+    sig = _signatures()
+    for name in names:
+        fn = getattr(cdll, name)
+        fn.argtypes, fn.restype = sig[name]
+    return cdll
+
+
 def lib():
     """The loaded library (raises if it is missing)."""
     global _lib
@@ -127,37 +172,7 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libbcg.so not found at {LIB_PATH}; build it with "
                                "`python -m bucketed_classifier_free_amd.build`")
-        L = C.CDLL(LIB_PATH)
-        L.bcg_last_error.restype = C.c_char_p
-        L.bcg_abi_version.restype = C.c_int
-        L.sigma_schedule.argtypes = [C.c_int, C.c_double, C.c_double, C.c_int, C.c_double, vp,
-                                     C.POINTER(C.c_int)]
-        L.bucket_table.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp]
-        L.bucket_bounds.argtypes = [C.c_int, C.c_double, C.c_double, C.c_double, C.c_int, vp, vp]
-        L.sigma_crop.argtypes = [vp, C.c_int, C.c_int, C.c_int, C.c_int, vp, C.POINTER(C.c_int)]
-        L.bcg_plan_build.argtypes = [C.POINTER(PlanIn), C.POINTER(PlanOut)]
-        L.guided_step.argtypes = [C.POINTER(StepArgs), vp]
-        L.bcg_plan_device.argtypes = [C.c_int, C.POINTER(DevicePlan), vp]
-        L.bcg_plan_records.argtypes = [C.c_int, C.c_int, vp, vp, vp, vp, vp, C.c_int, vp]
-        L.guided_step_rows.argtypes = [C.POINTER(RowsArgs), vp]
-        L.guided_step_rows_dplan.argtypes = [C.POINTER(RowsArgs), C.POINTER(DevicePlan), vp]
-        L.guided_step_dplan.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
-        L.guided_step_dplan_static.argtypes = [C.POINTER(StepArgs), C.POINTER(DevicePlan), vp]
-        L.guided_step_workspace_size.argtypes = [C.c_int] * 5
-        L.guided_step_workspace_size.restype = C.c_size_t
-        L.latent_init.argtypes = [C.c_int] * 5 + [vp, vp, vp, C.c_int, vp, vp, vp]
-        L.area_accumulate.argtypes = [C.c_int] * 6 + [vp, C.c_int64] + [vp] * 7 + [vp]
-        L.mask_blend.argtypes = [C.c_int] * 5 + [vp, vp, vp, C.c_int, vp, vp]
-        L.bcg_loop_create.argtypes = [C.POINTER(LoopDesc), C.POINTER(vp)]
-        L.bcg_loop_run.argtypes = [vp, C.c_int, C.c_int, vp, C.POINTER(C.c_float)]
-        L.bcg_loop_destroy.argtypes = [vp]
-        L.bcg_loop_last_run.argtypes = [vp, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
-        L.weight_patch.argtypes = [C.POINTER(WeightArgs), vp]
-        for name in EXPORTS:
-            getattr(L, name).restype = getattr(L, name).restype or C.c_int
-        L.guided_step_workspace_size.restype = C.c_size_t
-        L.bcg_last_error.restype = C.c_char_p
-        _lib = L
+        _lib = configure(C.CDLL(LIB_PATH), EXPORTS)
     return _lib
 
 

@@ -9,3 +9,4 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU-side check")
+    config.addinivalue_line("markers", "host: calls only the host half of the library (bcg_host.cpp)")

@@ -1,5 +1,8 @@
 """Host half of libbcg against the oracle, on the CPU (no GPU calls).
 
+Cases marked ``host`` call only the functions of bcg_host.cpp; they also run
+against its sanitized host-only build (test_host_sanitized.py).
+
 The library must load and export every function include/bcg.h declares;
 sigma_schedule, bucket_table and bcg_plan_build are plain host code and are
 compared with the oracle bit for bit; argument errors come back as status
@@ -36,6 +39,7 @@ def test_library_exports_every_declared_function():
     assert lib.bcg_abi_version() == L.ABI_VERSION == 9
 
 
+@pytest.mark.host
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
 def test_sigma_schedule_bit_exact_on_workloads(name):
     sp = W.config(name)
@@ -45,6 +49,7 @@ def test_sigma_schedule_bit_exact_on_workloads(name):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.host
 def test_sigma_schedule_bit_exact_random():
     rng = np.random.default_rng(8)
     for _ in range(200):
@@ -58,6 +63,7 @@ def test_sigma_schedule_bit_exact_random():
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.host
 def test_bucket_table_bit_exact():
     for kind, p in (("const", (7.0, 0, 0)), ("linear", (2.0, 1.2, 0)), ("front_high", (2.0, 1.2, 0.2)),
                     ("linear", (0.5, 9.0, 0))):
@@ -77,6 +83,7 @@ def _compare_plan(got, want):
     assert np.all(got.order[got.n_active:] == -1)
 
 
+@pytest.mark.host
 def test_plan_build_bit_exact_random():
     rng = np.random.default_rng(9)
     for _ in range(400):
@@ -90,6 +97,7 @@ def test_plan_build_bit_exact_random():
         _compare_plan(got, D.build_plan(t, steps, nb, table, ov, None))
 
 
+@pytest.mark.host
 @pytest.mark.parametrize("name", ["regional_inpaint", "large_bf16"])
 def test_plan_regions_bit_exact_on_workloads(name):
     inp = W.make_inputs(W.config(name))
@@ -112,6 +120,7 @@ def test_plan_regions_bit_exact_on_workloads(name):
     assert got.region_off[-1] == off
 
 
+@pytest.mark.host
 def test_plan_coverage_forces_uncond_at_scale_one():
     # two samples at cfg 1: one fully covered by its regions, one not
     frac = np.array([[[0, 0, 1, 0.5], [0, 0.5, 1, 0.5]],
@@ -127,6 +136,7 @@ def test_plan_coverage_forces_uncond_at_scale_one():
     assert plan.uncond_row[0] >= 0
 
 
+@pytest.mark.host
 def test_plan_coverage_matches_bruteforce_random():
     rng = np.random.default_rng(12)
     for _ in range(200):
@@ -147,6 +157,7 @@ def test_plan_coverage_matches_bruteforce_random():
                 assert tuple(plan.region_box[i, r]) == boxes[r]
 
 
+@pytest.mark.host
 def test_error_paths_return_codes():
     with pytest.raises(L.BCGError) as e:
         bcg.sigma_schedule(1.0, 2.0, 10)
@@ -190,6 +201,7 @@ def test_device_entry_points_validate_before_launch():
     assert lib.guided_step_workspace_size(4, 16, 128, 128, 1) == 4 * 16 * 128 * 3 * 4
 
 
+@pytest.mark.host
 def test_plan_with_cached_coverage_equals_full_plan():
     inp = W.make_inputs(W.config("regional_inpaint"))
     sp = inp.spec
@@ -342,6 +354,7 @@ def test_rows_dplan_entry_point_validates_before_launch():
     assert lib.guided_step_rows_dplan(C.byref(a), C.byref(d), None) == L.BCG_OK
 
 
+@pytest.mark.host
 def test_sigma_crop_bit_exact_and_errors():
     rng = np.random.default_rng(3)
     for _ in range(100):
@@ -358,6 +371,7 @@ def test_sigma_crop_bit_exact_and_errors():
         bcg.sigma_crop(sig, 5, 2)
 
 
+@pytest.mark.host
 def test_mid_peak_table_bit_exact():
     rng = np.random.default_rng(4)
     for _ in range(50):
@@ -371,6 +385,7 @@ def test_mid_peak_table_bit_exact():
             bcg.bucket_table("mid_peak", 1.2, 2.0, bad, 4)
 
 
+@pytest.mark.host
 def test_bucket_bounds_and_interpolated_plan_bit_exact():
     rng = np.random.default_rng(5)
     for kind, p in (("linear", (2.0, 1.2, 0.0)), ("front_high", (2.0, 1.2, 0.2)),
@@ -395,6 +410,7 @@ def test_bucket_bounds_and_interpolated_plan_bit_exact():
                            bucket_cfg_end=np.float32([np.inf]))
 
 
+@pytest.mark.host
 def test_plan_records_from_host_plan():
     sig, _ = bcg.sigma_schedule(14.6, 0.03, 10)
     t = np.int32([0, 9, 10, -1, 4])
@@ -408,6 +424,7 @@ def test_plan_records_from_host_plan():
     assert (r[2:4] == 0).all()
 
 
+@pytest.mark.host
 def test_plan_with_validity_ranges_bit_exact():
     sp = W.small_spec(n=40, C=2, H=24, W=32, steps=20, num_buckets=4, regions=3, region_ranges=True,
                       curve=W.Curve("linear", 2.0, 1.0), skip_frac=0.5, seed=12)
@@ -482,6 +499,7 @@ def test_weight_patch_validates_before_launch():
     assert lib.weight_patch(C.byref(a), None) == L.BCG_OK
 
 
+@pytest.mark.host
 def test_area_slices_round_exact_products_ties_up():
     # The library's slices at and around every rounding tie of every extent
     # n <= 256: one sample per fraction f, one region (f, 0, 0, f), so the row
