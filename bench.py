@@ -155,19 +155,27 @@ def copy_probe(mib: int, iters: int):
     print(json.dumps({"copy_probe_mib": mib, "ms": ms, "GBps": 2 * mib * (1 << 20) / ms / 1e6}))
 
 
-def _counter_means(path, counter):
+def _counter_means(path, counter, last=0):
+    """Mean per dispatch of a counter, per kernel name (over the last `last`
+    dispatches of each kernel when last > 0: the timed launches, after the
+    warm-up's)."""
     import csv
     import collections
-    acc = collections.defaultdict(list)
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
     with open(path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] == counter:
-                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+                acc[r["Kernel_Name"]][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    out = {}
+    for k, d in acc.items():
+        v = [d[i] for i in sorted(d)]
+        v = v[-last:] if last > 0 else v
+        out[k] = sum(v) / len(v)
+    return out
 
 
 def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, workload,
-                          kernel="guided_step_kernel", sources=None):
+                          kernel="guided_step_kernel", sources=None, last=0):
     """Per-launch HBM bytes of a kernel (guided_step by default) from two
     rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
     scaled by what the same counter reads for a plain device copy of copy_mib
@@ -176,12 +184,12 @@ def traffic_from_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, 
     pick = lambda d, key: max((v for k, v in d.items() if key in k), default=None)
     cf = pick(_counter_means(copy_fetch_csv, "FETCH_SIZE"), "copyBuffer")
     cw = pick(_counter_means(copy_write_csv, "WRITE_SIZE"), "copyBuffer")
-    f = pick(_counter_means(fetch_csv, "FETCH_SIZE"), kernel)
-    w = pick(_counter_means(write_csv, "WRITE_SIZE"), kernel)
+    f = pick(_counter_means(fetch_csv, "FETCH_SIZE", last), kernel)
+    w = pick(_counter_means(write_csv, "WRITE_SIZE", last), kernel)
     rf, rw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
     return {"workload": workload, "kernel": kernel, "kernel_hash": kernel_hash(sources),
             "fetch_kib_raw": f, "write_kib_raw": w, "copy_fetch_kib_raw": cf,
-            "copy_write_kib_raw": cw, "copy_mib": copy_mib,
+            "copy_write_kib_raw": cw, "copy_mib": copy_mib, "dispatches": last or "all",
             "fetch_scale": rf, "write_scale": rw,
             "bytes_per_launch": f * 1024 * rf + w * 1024 * rw}
 
@@ -533,18 +541,22 @@ def main():
     ap.add_argument("--graph", type=int, default=40, metavar="G",
                     help="device plans: the timed launches run as replays of a captured graph of "
                          "min(G, --steps) launches (0 = direct launches)")
+    ap.add_argument("--counter-last", type=int, default=0, metavar="N",
+                    help="--traffic-from: average the kernel's counters over its last N dispatches (the timed "
+                         "launches of the counted run; 0: all)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the traffic record from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
     if args.traffic_from and args.weight_patch:
         kern = "patch_stream_kernel" if "diff" in args.weight_patch else "patch_lowrank_strip_kernel"
-        rec = traffic_from_counters(*args.traffic_from, 256, args.weight_patch, kern, WEIGHT_SOURCES)
+        rec = traffic_from_counters(*args.traffic_from, 256, args.weight_patch, kern, WEIGHT_SOURCES,
+                                    args.counter_last)
         with open(weight_traffic_file(args.weight_patch), "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec))
         return
     if args.traffic_from:
-        rec = traffic_from_counters(*args.traffic_from, 256, args.workload)
+        rec = traffic_from_counters(*args.traffic_from, 256, args.workload, last=args.counter_last)
         with open(TRAFFIC_FILE, "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec))
