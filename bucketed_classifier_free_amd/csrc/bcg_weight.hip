@@ -79,6 +79,8 @@ struct WeightParams {
     int steps;        // 16-row k-steps of that concatenation (strip kernel)
     StepDesc sd[8];   // the k-steps (strip kernel)
     int sm1;          // every low-rank patch has strength_model 1 (strip kernel)
+    int nodiff;       // no diff patch with rows (strip kernel)
+    int full;         // every low-rank patch covers every row, ranks multiples of 16 with 16-byte `up` rows, rows a multiple of 64
     int nvr;          // 8-element vectors per row (stream kernel)
     int vpt;          // vectors per lane (stream kernel)
     uint32_t nvec;    // vectors of the weight (stream kernel)
@@ -374,6 +376,23 @@ template <> __device__ __forceinline__ Raw8<bf16_t> raw_pack<bf16_t>(const Weigh
     uint32_t rb[8];
     if (vec) {
         random8(p, (uint64_t)e, rb);
+        // Adding the random bits and keeping the high halves is the rounding for
+        // every value but NaN (an infinity keeps its code: the bits stay below
+        // the exponent); two results per word by one byte permute, and the
+        // lanes with a NaN redo their vector below.
+        uint32_t q[4];
+        bool nan = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t s0 = __float_as_uint(v[2 * i]) + rb[2 * i];
+            const uint32_t s1 = __float_as_uint(v[2 * i + 1]) + rb[2 * i + 1];
+            q[i] = __builtin_amdgcn_perm(s1, s0, 0x07060302u);
+            nan = nan || v[2 * i] != v[2 * i] || v[2 * i + 1] != v[2 * i + 1];
+        }
+        if (__builtin_expect(!nan, 1)) {
+            r.v = u32x4_t{q[0], q[1], q[2], q[3]};
+            return r;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) rb[i] = i < n ? random16(p, (uint64_t)(e + i)) : 0u;
@@ -574,9 +593,14 @@ constexpr int PSTEPS = 8;  // k-steps of 16 rows: concatenated padded rank <= 12
 // instruction) and turns it to and from the MFMA layout through its own LDS
 // region; the next tile's quarter is loaded before this tile's arithmetic and
 // the tile's `up` fragments (global memory to registers) land while its
-// quarter is transposed.
+// quarter is transposed.  Specialisations: SM1 (every strength_model is 1:
+// no product by it), DIFF = false (no diff patch: no diff walks between the
+// low-rank patches), FULL (every low-rank patch covers every row, ranks are
+// multiples of 16 with 16-byte `up` rows and the rows a multiple of 64: no
+// per-tile or per-lane coverage tests).  Each patch's first k-step starts
+// its accumulators from an inline zero.
 // Dynamic LDS: [4 wave regions: 32 rows x wrow bytes][down^T: 128 columns x (kt_all + 8) bf16].
-template <typename TW, typename TO, bool VEC, bool SM1>
+template <typename TW, typename TO, bool VEC, bool SM1, bool DIFF = true, bool FULL = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void patch_lowrank_strip_kernel(WeightParams p) {
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
@@ -635,7 +659,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             if (s >= p.steps) continue;
             const StepDesc sd = sdl[s];
             const int pr = row - sd.off, k = 8 * hi, rem = sd.rank - sd.sk;
-            if (r0 >= sd.off + sd.rows || r0 + TR <= sd.off || pr < 0 || pr >= sd.rows || k >= rem) continue;
+            if (!FULL && (r0 >= sd.off + sd.rows || r0 + TR <= sd.off || pr < 0 || pr >= sd.rows || k >= rem)) continue;
             const bf16_t* src = sd.up + (int64_t)pr * sd.rank + k;
             if (sd.flags & 1) {
                 bn[s] = *reinterpret_cast<const bf16x8_t*>(src);
@@ -673,26 +697,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             if (s >= p.steps) break;
             const StepDesc sd = sdl[s];
             if (sd.sk == 0) {
-                for (; qn_ < sd.q; ++qn_) {
+                if constexpr (DIFF) for (; qn_ < sd.q; ++qn_) {
                     const PatchDev& f = p.p[qn_];
                     if (f.kind == BCG_PATCH_DIFF && f.rows > 0 && rin)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             apply_diff_any(p, f, row, cl + 8 * j, p.cols - (cl + 8 * j), vec, a[j]);
                 }
-                acc0 = f32x16_t{};
-                acc1 = f32x16_t{};
             }
-            const bool hit = r0 < sd.off + sd.rows && r0 + TR > sd.off;
+            const bool hit = FULL || (r0 < sd.off + sd.rows && r0 + TR > sd.off);
             if (hit) {
                 const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + colw0 * kp + 16 * s + 8 * hi);
                 const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + colw1 * kp + 16 * s + 8 * hi);
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], acc1, 0, 0, 0);
+                if (sd.sk == 0) {  // a patch's first k-step starts from zero (an inline operand)
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], f32x16_t{}, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], f32x16_t{}, 0, 0, 0);
+                } else {
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], acc1, 0, 0, 0);
+                }
             }
             if (sd.flags & 2) {  // the patch's last k-step
                 const int pr = row - sd.off;
-                if (hit && rin && pr >= 0 && pr < sd.rows) {
+                if (FULL || (hit && rin && pr >= 0 && pr < sd.rows)) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         if constexpr (SM1) {  // every strength_model is 1: 1 * a is a
@@ -707,7 +734,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
                 qn_ = sd.q + 1;
             }
         }
-        for (; qn_ < p.np; ++qn_) {
+        if constexpr (DIFF) for (; qn_ < p.np; ++qn_) {
             const PatchDev& f = p.p[qn_];
             if (f.kind == BCG_PATCH_DIFF && f.rows > 0 && rin)
 #pragma unroll
@@ -776,6 +803,18 @@ hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t 
                 reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false, false>), lmax, done[0]);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false, false>), dim3(blocks), dim3(NT), lds, s, p);
+        } else if (p.sm1 && p.nodiff && p.full) {
+            static std::atomic<uint64_t> done4{0};
+            const hipError_t e = lds_limit(
+                reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, true, false, true>), lmax, done4);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, true, false, true>), dim3(blocks), dim3(NT), lds, s, p);
+        } else if (p.sm1 && p.nodiff) {
+            static std::atomic<uint64_t> done3{0};
+            const hipError_t e = lds_limit(
+                reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, true, false>), lmax, done3);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, true, false>), dim3(blocks), dim3(NT), lds, s, p);
         } else if (p.sm1) {
             const hipError_t e = lds_limit(
                 reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, true, true>), lmax, done[1]);
@@ -910,6 +949,16 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
             p.kt_all = kt_all;
             p.steps = 0;
             p.sm1 = 1;
+            p.nodiff = 1;
+            for (int q = 0; q < a->num_patches; ++q)
+                if (a->patches[q].kind == BCG_PATCH_DIFF && a->patches[q].rows > 0) p.nodiff = 0;
+            p.full = a->rows % TR == 0;
+            for (int q = 0; q < a->num_patches; ++q) {
+                const bcg_patch& e = a->patches[q];
+                if (e.kind == BCG_PATCH_LOWRANK && e.rows > 0 &&
+                    (e.offset != 0 || e.rows != a->rows || e.rank % 16 != 0 || !aligned16(e.up)))
+                    p.full = 0;
+            }
             for (int q = 0; q < a->num_patches; ++q) {
                 const bcg_patch& e = a->patches[q];
                 if (e.kind != BCG_PATCH_LOWRANK || e.rows <= 0) continue;

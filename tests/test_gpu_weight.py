@@ -126,6 +126,40 @@ def test_weight_patch_bit_exact_on_dyadic_factors(kw):
         f"{np.sum(got != want)} of {got.size} elements differ"
 
 
+NONFINITE = {
+    # every low-rank patch over every row (the strip kernel's full-cover path)
+    "full": (WW.PatchSpec("lowrank", rank=16, strength_patch=0.7),
+             WW.PatchSpec("lowrank", rank=32, strength_patch=-0.5)),
+    # low-rank patches over parts of the rows
+    "offset": (WW.PatchSpec("lowrank", offset=8, rows=100, rank=16, strength_patch=0.7),
+               WW.PatchSpec("lowrank", offset=64, rows=64, rank=8, strength_patch=1.5, strength_model=0.5)),
+    # diffs only (the streaming kernel)
+    "diff": (WW.PatchSpec("diff", strength_patch=1.3, strength_model=0.9),),
+}
+
+
+@pytest.mark.parametrize("rounding", ["stochastic", "nearest"])
+@pytest.mark.parametrize("kind", list(NONFINITE))
+def test_weight_patch_non_finite_weights(kind, rounding):
+    """NaN and infinities in the weight: an infinity keeps its code, a NaN
+    stays a NaN, and every finite element is bit-exact (dyadic factors), on
+    each kernel's path."""
+    inp = WW.make_weight_inputs(_spec(rows=128, cols=256, dyadic=True, w_dtype="bf16", out_dtype="bf16",
+                                      rounding=rounding, patches=NONFINITE[kind]))
+    idx = np.random.default_rng(11).choice(inp.w.size, 96, replace=False)
+    inp.w.flat[idx[:32]] = np.nan
+    inp.w.flat[idx[32:64]] = np.inf
+    inp.w.flat[idx[64:]] = -np.inf
+    got = _run(inp)
+    with np.errstate(all="ignore"):  # the oracle's float64 steps on infinities and NaN
+        want = P.written(inp, P.reference32(inp))
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn) and gn.sum() >= 32
+    assert np.isinf(got).sum() >= 64
+    assert np.array_equal(got[~gn].view(np.uint32), want[~wn].view(np.uint32)), \
+        f"{np.sum(got[~gn] != want[~wn])} finite or infinite elements differ"
+
+
 @pytest.mark.parametrize("out_dtype,rounding", [("f32", "nearest"), ("bf16", "nearest"), ("bf16", "stochastic")])
 def test_weight_patch_random_factors_within_derived_bound(out_dtype, rounding):
     inp = WW.make_weight_inputs(_spec(rows=200, cols=264, w_dtype="f32", out_dtype=out_dtype,
