@@ -10,7 +10,9 @@
 //   patch_stream_kernel  (no low-rank patch): the weight as a flat sequence
 //     of 8-element row vectors (16-byte accesses, consecutive lanes on
 //     consecutive addresses), a grid of about one resident round (no partly
-//     filled last round) sweeping it front to back.
+//     filled last round) sweeping it front to back; with one diff over every
+//     row (patch_stream1_kernel) each lane's next vectors are requested
+//     before the current ones are combined.
 //   patch_lowrank_strip_kernel (low-rank patches, padded ranks summing to at
 //     most 128): the deltas are genuine contractions and run on the matrix
 //     cores as the transposed product dW^T = down^T up^T
@@ -79,6 +81,7 @@ struct WeightParams {
     int steps;        // 16-row k-steps of that concatenation (strip kernel)
     StepDesc sd[8];   // the k-steps (strip kernel)
     int sm1;          // every low-rank patch has strength_model 1 (strip kernel)
+    int onediff;      // one diff patch over every row, vector path (stream kernel)
     int nodiff;       // no diff patch with rows (strip kernel)
     int full;         // every low-rank patch covers every row, ranks multiples of 16 with 16-byte `up` rows, rows a multiple of 64
     int nvr;          // 8-element vectors per row (stream kernel)
@@ -400,6 +403,41 @@ template <> __device__ __forceinline__ Raw8<bf16_t> raw_pack<bf16_t>(const Weigh
     r.v = u32x4_t{sr_bf16(v[0], rb[0]) | sr_bf16(v[1], rb[1]) << 16, sr_bf16(v[2], rb[2]) | sr_bf16(v[3], rb[3]) << 16,
                   sr_bf16(v[4], rb[4]) | sr_bf16(v[5], rb[5]) << 16, sr_bf16(v[6], rb[6]) | sr_bf16(v[7], rb[7]) << 16};
     return r;
+}
+
+// ---------------------------------------------------------------- stream kernel, one full diff
+
+// One diff patch over every row on the 8-element vector path (the flat index
+// of vector v's first element is 8 v): the grid sweeps the weight as the
+// stream kernel does, and each lane requests its next round's weight and
+// diff vectors before this round's arithmetic.
+template <typename TW, typename TO, typename TD>
+__global__ __launch_bounds__(NT) void patch_stream1_kernel(WeightParams p) {
+    const TW* w = static_cast<const TW*>(p.w);
+    const TD* d = static_cast<const TD*>(p.p[0].diff);
+    TO* out = static_cast<TO*>(p.out);
+    const float sp = p.p[0].sp, sm = p.p[0].sm;
+    const uint32_t step = gridDim.x * NT;
+    uint32_t v = blockIdx.x * NT + threadIdx.x;
+    if (v >= p.nvec) return;
+    Raw8<TW> wc = raw_load<true>(w, (int64_t)v * 8, 8, true);
+    Raw8<TD> dc = raw_load<true>(d, (int64_t)v * 8, 8, true);
+    for (;;) {
+        const bool more = p.nvec > step && v < p.nvec - step;  // the next round's vector v + step exists
+        const uint32_t nv = more ? v + step : v;
+        const Raw8<TW> wn = raw_load<true>(w, (int64_t)nv * 8, 8, true);
+        const Raw8<TD> dn = raw_load<true>(d, (int64_t)nv * 8, 8, true);
+        float a[8], b[8];
+        raw_unpack(wc, a);
+        raw_unpack(dc, b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = fmaf(sp, b[k], sm * a[k]);
+        store8<TO>(p, out, (int64_t)v * 8, 8, true, a);
+        if (!more) break;
+        v = nv;
+        wc = wn;
+        dc = dn;
+    }
 }
 
 // Stage concatenated k-rows [kf0, kf0 + kalloc) of the low-rank patches
@@ -826,6 +864,11 @@ hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t 
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, true, false>), dim3(blocks), dim3(NT), lds, s, p);
         }
+    } else if (p.onediff) {
+        if (p.p[0].dtype == BCG_BF16)
+            hipLaunchKernelGGL((patch_stream1_kernel<TW, TO, bf16_t>), dim3(blocks), dim3(NT), 0, s, p);
+        else
+            hipLaunchKernelGGL((patch_stream1_kernel<TW, TO, float>), dim3(blocks), dim3(NT), 0, s, p);
     } else {
         hipLaunchKernelGGL((patch_stream_kernel<TW, TO>), dim3(blocks), dim3(NT), 0, s, p);
     }
@@ -995,6 +1038,8 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
         if (nvec >= INT32_MAX) return fail(BCG_ESHAPE, "%s: weight too large", who);
         p.nvec = (uint32_t)nvec;
         p.vpt = (int)((nvec + kResident * NT - 1) / (kResident * NT));
+        p.onediff = vec && a->num_patches == 1 && a->patches[0].kind == BCG_PATCH_DIFF &&
+                    a->patches[0].offset == 0 && a->patches[0].rows == a->rows;
         blocks = (nvec + (int64_t)NT * p.vpt - 1) / ((int64_t)NT * p.vpt);
     }
     hipError_t e;

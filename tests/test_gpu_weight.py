@@ -133,8 +133,12 @@ NONFINITE = {
     # low-rank patches over parts of the rows
     "offset": (WW.PatchSpec("lowrank", offset=8, rows=100, rank=16, strength_patch=0.7),
                WW.PatchSpec("lowrank", offset=64, rows=64, rank=8, strength_patch=1.5, strength_model=0.5)),
-    # diffs only (the streaming kernel)
+    # one diff over every row (the pipelined streaming kernel), bf16 and fp32 diffs
     "diff": (WW.PatchSpec("diff", strength_patch=1.3, strength_model=0.9),),
+    "diff_f32": (WW.PatchSpec("diff", strength_patch=-0.7, strength_model=1.1, dtype="f32"),),
+    # two diffs over parts of the rows (the general streaming kernel)
+    "diffs": (WW.PatchSpec("diff", offset=3, rows=90, strength_patch=1.3, strength_model=0.9),
+              WW.PatchSpec("diff", offset=40, rows=88, strength_patch=0.5, dtype="f32")),
 }
 
 
