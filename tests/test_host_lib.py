@@ -269,6 +269,80 @@ def test_device_plan_entry_points_validate_before_launch():
     assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_OK
 
 
+@pytest.mark.parametrize("field,bad,word", [
+    ("queue_len", 1, b"queue_len"),                # fewer requests than the 2 slots
+    ("queue_len", 1 << 24, b"queue_len"),
+    ("queue_ring", 2, b"queue_ring"),
+    ("wrap", 1, b"wrap"),
+    ("noise", None, b"noise"),
+    ("slot_req_out", None, b"slot_req"),
+    ("queue_out", None, b"queue_in/out"),
+    ("region_range", 9, b"validity"),
+    ("join_front", 3, b"join_front"),              # more than the 2 slots
+    ("join_in", None, b"join_in"),
+])
+def test_queue_plan_validates_before_launch(field, bad, word):
+    """Continuous batching's device-plan fields: each inconsistent setting is
+    rejected with a message before anything is launched."""
+    lib = L.lib()
+    d = L.DevicePlan(10, 4, 0, _fake(1), None, None, _fake(2), _fake(3))
+    d.record_in, d.record_out, d.sigmas, d.num_sigmas = _fake(10), _fake(11), _fake(12), 11
+    d.queue_len, d.queue_ring, d.noise = 4, 1, _fake(13)
+    d.slot_req_in, d.slot_req_out, d.queue_in, d.queue_out = _fake(14), _fake(15), _fake(16), _fake(17)
+    d.join_front, d.join_in, d.join_out = 1, _fake(18), _fake(19)
+    a = L.StepArgs()
+    a.n, a.C, a.H, a.W, a.num_sigmas, a.s2 = 2, 4, 8, 8, 11, 0.25
+    a.x, a.x_out, a.sigmas, a.mu_uncond, a.mu_cond = _fake(5), _fake(6), _fake(12), _fake(7), _fake(8)
+    if field == "region_range":
+        d.region_range = _fake(bad)
+    else:
+        setattr(d, field, bad)
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL, field
+    assert word in lib.bcg_last_error(), lib.bcg_last_error()
+
+
+def test_queue_plan_other_rejections():
+    lib = L.lib()
+    d = L.DevicePlan(10, 4, 0, _fake(1), None, None, _fake(2), _fake(3))
+    d.record_in, d.record_out, d.sigmas, d.num_sigmas = _fake(10), _fake(11), _fake(12), 11
+    d.queue_len, d.queue_ring, d.noise = 4, 1, _fake(13)
+    d.slot_req_in, d.slot_req_out, d.queue_in, d.queue_out = _fake(14), _fake(15), _fake(16), _fake(17)
+    a = L.StepArgs()
+    a.n, a.C, a.H, a.W, a.num_sigmas, a.s2 = 2, 4, 8, 8, 11, 0.25
+    a.x, a.x_out, a.sigmas, a.mu_uncond, a.mu_cond = _fake(5), _fake(6), _fake(12), _fake(7), _fake(8)
+    d.slot_req_out = _fake(14).value + 4                                # overlaps slot_req_in
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"overlap" in lib.bcg_last_error()
+    d.slot_req_out = _fake(15)
+    d.join_front, d.join_in, d.join_out = 2, _fake(18), _fake(18).value + 4  # join_out overlaps join_in
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"join_out" in lib.bcg_last_error()
+    d.join_front, d.join_in, d.join_out = 0, None, None
+    a.stats = _fake(20)                                                 # no statistics with a queue
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"stats" in lib.bcg_last_error()
+    a.stats = None
+    a.H = a.W = 7                                                       # the vector path is required
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"vector" in lib.bcg_last_error()
+    a.H = a.W = 8
+    d.noise = _fake(13).value + 4                                       # misaligned noise
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    d.noise = _fake(13)
+    rin = d.record_in
+    d.record_in = None                                                  # (a plan launch reads no records)
+    assert lib.bcg_plan_device(2, C.byref(d), None) == L.BCG_EINVAL     # a queue needs the step
+    assert b"inside guided_step_dplan" in lib.bcg_last_error()
+    d.record_in = rin
+    q = d.queue_len
+    d.queue_len = 0                                                     # queue arrays without a queue
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_EINVAL
+    assert b"queue_len = 0" in lib.bcg_last_error()
+    d.queue_len = q
+    a.n = 0                                                             # no slots: nothing launched
+    assert lib.guided_step_dplan(C.byref(a), C.byref(d), None) == L.BCG_OK
+
+
 def test_loop_create_validates_device_plan_mode():
     lib = L.lib()
     start = np.zeros(2, np.int32)
@@ -288,6 +362,21 @@ def test_loop_create_validates_device_plan_mode():
     assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL
     d.device_plan = 2
     assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL
+    assert not h.value
+    # continuous batching: device plans with records, the queue state and the noise
+    d.device_plan, d.graph_launches, d.dev_records = 1, 0, _fake(4)
+    d.queue_len, d.noise, d.dev_queue = 4, _fake(5), _fake(6)
+    for field, bad, word in (("dev_queue", None, b"dev_queue"), ("noise", None, b"noise"),
+                             ("dev_records", None, b"dev_records"), ("queue_len", 1, b"queue_len >= n"),
+                             ("wrap", 1, b"wrap = 0"), ("join_front", 3, b"join_front")):
+        good = getattr(d, field)
+        setattr(d, field, bad)
+        assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL, field
+        assert word in lib.bcg_last_error(), (field, lib.bcg_last_error())
+        setattr(d, field, good)
+    start[1] = 10                                                        # a start step past the schedule
+    assert lib.bcg_loop_create(C.byref(d), C.byref(h)) == L.BCG_EINVAL
+    assert b"start[1]" in lib.bcg_last_error()
     assert not h.value
 
 
