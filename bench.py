@@ -548,7 +548,7 @@ def main():
                     help="write the traffic record from rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
     if args.traffic_from and args.weight_patch:
-        kern = "patch_stream_kernel" if "diff" in args.weight_patch else "patch_lowrank_strip_kernel"
+        kern = "patch_stream" if "diff" in args.weight_patch else "patch_lowrank"
         rec = traffic_from_counters(*args.traffic_from, 256, args.weight_patch, kern, WEIGHT_SOURCES,
                                     args.counter_last)
         with open(weight_traffic_file(args.weight_patch), "w") as fh:

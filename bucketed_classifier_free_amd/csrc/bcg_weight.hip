@@ -22,6 +22,11 @@
 //     A workgroup keeps one 128-column strip of `down` in LDS (transposed
 //     once) and walks its row tiles with four independent waves (the kernel
 //     comment below has the details).
+//   patch_lowrank_wide_kernel (bf16 weight and output, every low-rank patch
+//     over every row, ranks multiples of 16, rows a multiple of 128): the
+//     strip kernel with 128-row tiles, each wave taking 32 rows of both of
+//     the strip's 64-column halves in turn, so each `up` fragment it loads
+//     serves 128 columns.
 //   patch_lowrank_kernel (larger ranks): 64 x 128 tiles; the factors of the
 //     low-rank patches meeting the tile are concatenated along k and staged
 //     per tile, up to 128 k-rows per round, by direct global-to-LDS loads;
@@ -84,6 +89,7 @@ struct WeightParams {
     int onediff;      // one diff patch over every row, vector path (stream kernel)
     int nodiff;       // no diff patch with rows (strip kernel)
     int full;         // every low-rank patch covers every row, ranks multiples of 16 with 16-byte `up` rows, rows a multiple of 64
+    int wide;         // full, ranks up to 64 and rows a multiple of 128: the 128-row tiles
     int nvr;          // 8-element vectors per row (stream kernel)
     int vpt;          // vectors per lane (stream kernel)
     uint32_t nvec;    // vectors of the weight (stream kernel)
@@ -799,6 +805,133 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     }
 }
 
+
+// The full-cover case (every patch low-rank over every row, ranks multiples of
+// 16 up to 64, rows a multiple of 128) with 128-row tiles: wave w owns rows
+// 32 w of the tile and walks its two 64-column halves through its LDS region
+// in turn, so each `up` fragment it loads serves both halves (half the `up`
+// traffic of the 64-row tiles, where two waves load the same rows).
+template <typename TW, typename TO, bool SM1>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void patch_lowrank_wide_kernel(WeightParams p) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int ES = sizeof(TW) > sizeof(TO) ? sizeof(TW) : sizeof(TO);
+    constexpr int WROW = 64 * ES + 16;
+    constexpr int TRW = 128;  // tile rows
+    const int t = (int)threadIdx.x, l = t & 63, wave = t >> 6;
+    const int hi = l >> 5, lo = l & 31;
+    const int wr = 32 * wave;
+    unsigned char* rg = lds + wave * 32 * WROW;  // this wave's region
+    bf16_t* sdt = reinterpret_cast<bf16_t*>(lds + 4 * 32 * WROW);
+    const int kp = p.kt_all + 8;
+    const int ct = (int)blockIdx.x % p.ctiles, gr = (int)blockIdx.x / p.ctiles;
+    const int c0 = ct * TC;
+    const int nrt = p.rows / TRW;
+
+    __shared__ StepDesc sdl[PSTEPS];
+    if (t == 0) {
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) sdl[s] = p.sd[s];
+    }
+    for (int s = 0; s < p.steps; ++s) {
+        const PatchDev& d = p.p[p.sd[s].q];
+        const int k = p.sd[s].sk + (t >> 4), cv = (t & 15) * 8, col = c0 + cv;
+        Raw8<bf16_t> r{u32x4_t{0u, 0u, 0u, 0u}};
+        if (k < d.rank && col < p.cols) r = raw_load(d.down, (int64_t)k * p.cols + col, p.cols - col, true);
+        const uint32_t wv[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+        const int kf = 16 * s + (t >> 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sdt[(cv + e) * kp + kf] = (bf16_t)(wv[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();  // the only workgroup barrier: down^T and the step table are in place
+
+    const TW* w = static_cast<const TW*>(p.w);
+    TO* out = static_cast<TO*>(p.out);
+    Raw8<TW> wn[4];
+    bf16x8_t bn[PSTEPS];
+    // the quarter (32 rows x 64 columns, half h of the strip) of tile rt, streaming layout
+    auto load_w = [&](int rt, int h) __attribute__((always_inline)) {
+        const int qc = c0 + 64 * h + 8 * (l & 7), qn = p.cols - qc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = rt * TRW + wr + (l >> 3) + 8 * j;
+            if (qn > 0) wn[j] = raw_load<true>(w, (int64_t)row * p.cols + qc, qn, true);
+            else wn[j] = raw_load(w, 0, 0, false);
+        }
+    };
+    auto load_up = [&](int rt) __attribute__((always_inline)) {
+        const int row = rt * TRW + wr + lo;
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) {
+            bn[s] = bf16x8_t{};
+            if (s >= p.steps) continue;
+            const StepDesc sd = sdl[s];
+            bn[s] = *reinterpret_cast<const bf16x8_t*>(sd.up + (int64_t)(row - sd.off) * sd.rank + 8 * hi);
+        }
+    };
+    if (gr < nrt) load_w(gr, 0);
+    for (int rt = gr; rt < nrt; rt += p.grows) {
+        const int row = rt * TRW + wr + lo;
+        load_up(rt);  // serves both halves
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int wc = 64 * h, cl = c0 + wc + 32 * hi;
+            const int qc = c0 + wc + 8 * (l & 7), qn = p.cols - qc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) raw_lds_st(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * sizeof(TW), wn[j]);
+            if (h == 0) load_w(rt, 1);
+            else if (rt + p.grows < nrt) load_w(rt + p.grows, 0);
+            __builtin_amdgcn_wave_barrier();
+            float a[4][8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) raw_unpack(raw_lds_ld<TW>(rg + lo * WROW + (32 * hi + 8 * j) * sizeof(TW)), a[j]);
+            const int colw0 = wc + sub_col(lo, 0), colw1 = wc + sub_col(lo, 1);
+            f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int s = 0; s < PSTEPS; ++s) {
+                if (s >= p.steps) break;
+                const StepDesc sd = sdl[s];
+                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + colw0 * kp + 16 * s + 8 * hi);
+                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + colw1 * kp + 16 * s + 8 * hi);
+                if (sd.sk == 0) {
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], f32x16_t{}, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], f32x16_t{}, 0, 0, 0);
+                } else {
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], acc1, 0, 0, 0);
+                }
+                if (sd.flags & 2) {  // the patch's last k-step
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        if constexpr (SM1) {
+                            a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], a[v >> 3][v & 7]);
+                            a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], a[2 + (v >> 3)][v & 7]);
+                        } else {
+                            a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], sd.sm * a[v >> 3][v & 7]);
+                            a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], sd.sm * a[2 + (v >> 3)][v & 7]);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = cl + 8 * j;
+                const Raw8<TO> r = raw_pack<TO>(p, a[j], (int64_t)row * p.cols + c, p.cols - c, true);
+                raw_lds_st(rg + lo * WROW + (32 * hi + 8 * j) * sizeof(TO), r);
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int srow = rt * TRW + wr + (l >> 3) + 8 * j;
+                if (qn > 0)
+                    raw_store<true>(out, (int64_t)srow * p.cols + qc, qn, true,
+                                    raw_lds_ld<TO>(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * sizeof(TO)));
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 inline size_t strip_lds_bytes(int es, int kt_all) {
     return (size_t)4 * 32 * (64 * es + 16) + (size_t)TC * (kt_all + 8) * 2;
 }
@@ -841,6 +974,17 @@ hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t 
                 reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false, false>), lmax, done[0]);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false, false>), dim3(blocks), dim3(NT), lds, s, p);
+        } else if (sizeof(TW) == 2 && sizeof(TO) == 2 && p.nodiff && p.full && p.wide) {  // bf16 in and out
+            static std::atomic<uint64_t> done5[2] = {{0}, {0}};
+            if (p.sm1) {
+                const hipError_t e = lds_limit(reinterpret_cast<const void*>(&patch_lowrank_wide_kernel<TW, TO, true>), lmax, done5[0]);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL((patch_lowrank_wide_kernel<TW, TO, true>), dim3(blocks), dim3(NT), lds, s, p);
+            } else {
+                const hipError_t e = lds_limit(reinterpret_cast<const void*>(&patch_lowrank_wide_kernel<TW, TO, false>), lmax, done5[1]);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL((patch_lowrank_wide_kernel<TW, TO, false>), dim3(blocks), dim3(NT), lds, s, p);
+            }
         } else if (p.sm1 && p.nodiff && p.full) {
             static std::atomic<uint64_t> done4{0};
             const hipError_t e = lds_limit(
@@ -1002,6 +1146,7 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
                     (e.offset != 0 || e.rows != a->rows || e.rank % 16 != 0 || !aligned16(e.up)))
                     p.full = 0;
             }
+            p.wide = p.full && a->rows % 128 == 0 && p.vec;
             for (int q = 0; q < a->num_patches; ++q) {
                 const bcg_patch& e = a->patches[q];
                 if (e.kind != BCG_PATCH_LOWRANK || e.rows <= 0) continue;

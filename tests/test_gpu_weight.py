@@ -113,6 +113,12 @@ EXACT = [dict(w_dtype="bf16", out_dtype="bf16", rounding="stochastic"),
                        WW.PatchSpec("lowrank", offset=64, rows=100, rank=40, strength_patch=-1.2,
                                     strength_model=0.75),
                        WW.PatchSpec("lowrank", offset=150, rows=50, rank=3, strength_patch=2.0))),
+         # every patch over every row, rows a multiple of 128 (the 128-row tiles), strength_model != 1
+         dict(rows=256, cols=384, w_dtype="bf16", out_dtype="bf16", rounding="stochastic",
+              patches=(WW.PatchSpec("lowrank", rank=32, strength_patch=0.9, strength_model=0.75),
+                       WW.PatchSpec("lowrank", rank=16, strength_patch=-1.2))),
+         dict(rows=256, cols=136, w_dtype="bf16", out_dtype="bf16", rounding="nearest",
+              patches=(WW.PatchSpec("lowrank", rank=48, strength_patch=0.6),)),
          dict(rows=129, cols=8, w_dtype="bf16", out_dtype="bf16", rounding="stochastic",
               patches=(WW.PatchSpec("lowrank", rank=16), WW.PatchSpec("diff", offset=1, rows=127)))]
 
