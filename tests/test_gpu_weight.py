@@ -119,6 +119,12 @@ EXACT = [dict(w_dtype="bf16", out_dtype="bf16", rounding="stochastic"),
                        WW.PatchSpec("lowrank", rank=16, strength_patch=-1.2))),
          dict(rows=256, cols=136, w_dtype="bf16", out_dtype="bf16", rounding="nearest",
               patches=(WW.PatchSpec("lowrank", rank=48, strength_patch=0.6),)),
+         # patches on 128-row boundaries (each 128-row tile inside or outside each of them)
+         dict(rows=384, cols=256, w_dtype="bf16", out_dtype="bf16", rounding="stochastic",
+              patches=(WW.PatchSpec("lowrank", offset=128, rows=128, rank=16, strength_patch=1.5),
+                       WW.PatchSpec("lowrank", offset=0, rows=256, rank=32, strength_patch=-0.5,
+                                    strength_model=0.5),
+                       WW.PatchSpec("lowrank", offset=256, rows=128, rank=48, strength_patch=0.25))),
          dict(rows=129, cols=8, w_dtype="bf16", out_dtype="bf16", rounding="stochastic",
               patches=(WW.PatchSpec("lowrank", rank=16), WW.PatchSpec("diff", offset=1, rows=127)))]
 
