@@ -54,6 +54,16 @@ constexpr int NT = 256;       // lanes per workgroup
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// Loads of `up` through pointers read out of LDS (the step table): the
+// compiler cannot tell where such a pointer points and would emit flat
+// accesses, which also count against the LDS counter, so that each wait for a
+// step descriptor in LDS would wait for the `up` loads before it as well.
+// These name the global address space.
+typedef __attribute__((address_space(1))) const bf16x8_t gbf16x8_t;
+typedef __attribute__((address_space(1))) const bf16_t gbf16_t;
+__device__ __forceinline__ bf16x8_t ld_up8(const bf16_t* q) { return *(gbf16x8_t*)q; }
+__device__ __forceinline__ bf16_t ld_up1(const bf16_t* q) { return *(gbf16_t*)q; }
+
 struct PatchDev {
     int kind, offset, rows, rank, dtype, upvec;
     float sp, sm;
@@ -101,6 +111,11 @@ struct WeightParams {
 
 // ---------------------------------------------------------------- Philox4x32-10
 
+// a ^ b ^ c in one instruction (v_bitop3_b32 with truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, (unsigned char)0x96);
+}
+
 __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
                                               uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -111,7 +126,7 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
         }
         // one 32 x 32 -> 64-bit product each (v_mad_u64_u32), not a low and a high multiply
         const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0), n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c0 = n0;
         c1 = (uint32_t)p1;
         c2 = n2;
@@ -511,6 +526,47 @@ __device__ __forceinline__ int sub_col(int lo, int s) {
     return 4 * (lo >> 3) + (lo & 3) + 32 * ((lo >> 2) & 1) + 16 * s;
 }
 
+// Slot of strip column c in the transposed `down` area of the strip kernels:
+// each group of 8 columns is rotated by its index (c + c / 8 modulo 8 inside
+// the group).  The row pitch is an odd number of 16-byte units (kt_all + 8
+// for a concatenated rank that is a multiple of 16), so slots that differ
+// modulo 8 lie on different banks of a 128-byte bank cycle.  The fragment
+// reads of 8 consecutive lanes (columns a .. a + 3 and a + 32 .. a + 35,
+// sub_col) then take 8 distinct residues, and so do the staging stores of 8
+// consecutive lanes (column j of 8 consecutive groups).
+__device__ __forceinline__ int dslot(int c) { return (c & ~7) | ((c + (c >> 3)) & 7); }
+
+// down^T of the strip into LDS, k-step s covering concatenated k-rows 16 s ..
+// 16 s + 15, and slot dslot(c) holding column c's k-values contiguously (pitch
+// kp).  Each lane takes an 8 x 8 block (8 k-rows of one patch, 8 columns):
+// eight 16-byte row loads (16 lanes on 256 contiguous bytes of a row), a
+// transposition in registers (each dword two bfloat16 of one column from two
+// rows) and eight 16-byte stores, one per column.  Rows past the rank and
+// columns past the weight stage as zeros.
+__device__ __forceinline__ void stage_down(const WeightParams& p, bf16_t* sdt, int kp, int c0, bool vec) {
+    for (int u = (int)threadIdx.x; u < 32 * p.steps; u += NT) {
+        const int g = u & 15, kb = (u >> 4) & 1, s = u >> 5;
+        const StepDesc& sd = p.sd[s];
+        const PatchDev& d = p.p[sd.q];
+        const int col = c0 + 8 * g, k0 = sd.sk + 8 * kb;
+        u32x4_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (k0 + i < d.rank && col < p.cols) v[i] = raw_load(d.down, (int64_t)(k0 + i) * p.cols + col, p.cols - col, vec).v;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // the high or the low halves
+            const u32x4_t f = {__builtin_amdgcn_perm(v[1][j >> 1], v[0][j >> 1], sel),
+                               __builtin_amdgcn_perm(v[3][j >> 1], v[2][j >> 1], sel),
+                               __builtin_amdgcn_perm(v[5][j >> 1], v[4][j >> 1], sel),
+                               __builtin_amdgcn_perm(v[7][j >> 1], v[6][j >> 1], sel)};
+            *reinterpret_cast<u32x4_t*>(sdt + dslot(8 * g + j) * kp + 16 * s + 8 * kb) = f;
+        }
+    }
+}
+
 // Dynamic LDS: [transposition tile: 64 rows x trow bytes][down area: sb_bytes(kalloc)][up area: 64 x kalloc x 2].
 template <typename TW, typename TO>
 __global__ __launch_bounds__(NT) void patch_lowrank_kernel(WeightParams p) {
@@ -664,17 +720,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 #pragma unroll
         for (int s = 0; s < PSTEPS; ++s) sdl[s] = p.sd[s];
     }
-    // down^T of the strip: k-step s covers concatenated rows 16 s .. 16 s + 15, one 8-column vector per lane.
-    for (int s = 0; s < p.steps; ++s) {
-        const PatchDev& d = p.p[p.sd[s].q];
-        const int k = p.sd[s].sk + (t >> 4), cv = (t & 15) * 8, col = c0 + cv;
-        Raw8<bf16_t> r{u32x4_t{0u, 0u, 0u, 0u}};
-        if (k < d.rank && col < p.cols) r = raw_load(d.down, (int64_t)k * p.cols + col, p.cols - col, vec);
-        const uint32_t wv[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
-        const int kf = 16 * s + (t >> 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sdt[(cv + e) * kp + kf] = (bf16_t)(wv[e >> 1] >> (16 * (e & 1)));
-    }
+    stage_down(p, sdt, kp, c0, vec);
     __syncthreads();  // the only workgroup barrier: down^T and the step table are in place
 
     // Streaming layout of the wave's quarter: vector j of lane l at quarter row l / 8 + 8 j, columns 8 (l % 8) .. +7.
@@ -706,11 +752,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             if (!FULL && (r0 >= sd.off + sd.rows || r0 + TR <= sd.off || pr < 0 || pr >= sd.rows || k >= rem)) continue;
             const bf16_t* src = sd.up + (int64_t)pr * sd.rank + k;
             if (sd.flags & 1) {
-                bn[s] = *reinterpret_cast<const bf16x8_t*>(src);
+                bn[s] = ld_up8(src);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    bn[s][e] = __builtin_bit_cast(__bf16, (bf16_t)(k + e < rem ? src[e] : 0));
+                    bn[s][e] = __builtin_bit_cast(__bf16, (bf16_t)(k + e < rem ? ld_up1(src + e) : 0));
             }
         }
     };
@@ -751,8 +797,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             }
             const bool hit = FULL || (r0 < sd.off + sd.rows && r0 + TR > sd.off);
             if (hit) {
-                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + colw0 * kp + 16 * s + 8 * hi);
-                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + colw1 * kp + 16 * s + 8 * hi);
+                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + dslot(colw0) * kp + 16 * s + 8 * hi);
+                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + dslot(colw1) * kp + 16 * s + 8 * hi);
                 if (sd.sk == 0) {  // a patch's first k-step starts from zero (an inline operand)
                     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], f32x16_t{}, 0, 0, 0);
                     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], f32x16_t{}, 0, 0, 0);
@@ -832,17 +878,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 #pragma unroll
         for (int s = 0; s < PSTEPS; ++s) sdl[s] = p.sd[s];
     }
-    for (int s = 0; s < p.steps; ++s) {
-        const PatchDev& d = p.p[p.sd[s].q];
-        const int k = p.sd[s].sk + (t >> 4), cv = (t & 15) * 8, col = c0 + cv;
-        Raw8<bf16_t> r{u32x4_t{0u, 0u, 0u, 0u}};
-        if (k < d.rank && col < p.cols) r = raw_load(d.down, (int64_t)k * p.cols + col, p.cols - col, true);
-        const uint32_t wv[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
-        const int kf = 16 * s + (t >> 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sdt[(cv + e) * kp + kf] = (bf16_t)(wv[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();  // the only workgroup barrier: down^T and the step table are in place
 
     const TW* w = static_cast<const TW*>(p.w);
     TO* out = static_cast<TO*>(p.out);
@@ -858,17 +893,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             else wn[j] = raw_load(w, 0, 0, false);
         }
     };
+    // Every fragment load is issued on every path (past the table: the last
+    // step's fragment again, never used), so that the waits for the weight
+    // loads before them need not wait for these.
     auto load_up = [&](int rt) __attribute__((always_inline)) {
         const int row = rt * TRW + wr + lo;
 #pragma unroll
         for (int s = 0; s < PSTEPS; ++s) {
-            bn[s] = bf16x8_t{};
-            if (s >= p.steps) continue;
-            const StepDesc sd = sdl[s];
-            bn[s] = *reinterpret_cast<const bf16x8_t*>(sd.up + (int64_t)(row - sd.off) * sd.rank + 8 * hi);
+            const StepDesc& sd = sdl[s < p.steps ? s : p.steps - 1];
+            bn[s] = ld_up8(sd.up + (int64_t)(row - sd.off) * sd.rank + 8 * hi);
         }
     };
-    if (gr < nrt) load_w(gr, 0);
+    if (gr < nrt) load_w(gr, 0);  // in flight while down^T is staged
+    stage_down(p, sdt, kp, c0, true);
+    __syncthreads();  // the only workgroup barrier: down^T and the step table are in place
+
     for (int rt = gr; rt < nrt; rt += p.grows) {
         const int row = rt * TRW + wr + lo;
         load_up(rt);  // serves both halves
@@ -890,8 +929,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             for (int s = 0; s < PSTEPS; ++s) {
                 if (s >= p.steps) break;
                 const StepDesc sd = sdl[s];
-                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + colw0 * kp + 16 * s + 8 * hi);
-                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + colw1 * kp + 16 * s + 8 * hi);
+                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + dslot(colw0) * kp + 16 * s + 8 * hi);
+                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + dslot(colw1) * kp + 16 * s + 8 * hi);
                 if (sd.sk == 0) {
                     acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], f32x16_t{}, 0, 0, 0);
                     acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], f32x16_t{}, 0, 0, 0);
