@@ -100,6 +100,7 @@ struct WeightParams {
     int nodiff;       // no diff patch with rows (strip kernel)
     int full;         // every low-rank patch covers every row, ranks multiples of 16 with 16-byte `up` rows, rows a multiple of 64
     int wide;         // full, ranks up to 64 and rows a multiple of 128: the 128-row tiles
+    int unit;         // wide, rows and columns multiples of 384 in a multiple of 256 units: the unit kernel
     int nvr;          // 8-element vectors per row (stream kernel)
     int vpt;          // vectors per lane (stream kernel)
     uint32_t nvec;    // vectors of the weight (stream kernel)
@@ -539,13 +540,16 @@ __device__ __forceinline__ int dslot(int c) { return (c & ~7) | ((c + (c >> 3)) 
 // down^T of the strip into LDS, k-step s covering concatenated k-rows 16 s ..
 // 16 s + 15, and slot dslot(c) holding column c's k-values contiguously (pitch
 // kp).  Each lane takes an 8 x 8 block (8 k-rows of one patch, 8 columns):
-// eight 16-byte row loads (16 lanes on 256 contiguous bytes of a row), a
+// eight 16-byte row loads (the lanes of one k-row on NCOL contiguous columns), a
 // transposition in registers (each dword two bfloat16 of one column from two
 // rows) and eight 16-byte stores, one per column.  Rows past the rank and
 // columns past the weight stage as zeros.
+template <int NCOL = TC, int NTH = NT>  // strip columns, lanes of the workgroup
 __device__ __forceinline__ void stage_down(const WeightParams& p, bf16_t* sdt, int kp, int c0, bool vec) {
-    for (int u = (int)threadIdx.x; u < 32 * p.steps; u += NT) {
-        const int g = u & 15, kb = (u >> 4) & 1, s = u >> 5;
+    constexpr int NG = NCOL / 8;  // 8-column groups (a multiple of 8: 8 consecutive lanes take 8 consecutive groups)
+    static_assert(NG % 8 == 0, "strip width");
+    for (int u = (int)threadIdx.x; u < 2 * NG * p.steps; u += NTH) {
+        const int g = u % NG, kb = (u / NG) & 1, s = u / (2 * NG);
         const StepDesc& sd = p.sd[s];
         const PatchDev& d = p.p[sd.q];
         const int col = c0 + 8 * g, k0 = sd.sk + 8 * kb;
@@ -893,15 +897,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
             else wn[j] = raw_load(w, 0, 0, false);
         }
     };
-    // Every fragment load is issued on every path (past the table: the last
-    // step's fragment again, never used), so that the waits for the weight
-    // loads before them need not wait for these.
+    // Every fragment load is issued on every path, so that the waits for the
+    // weight loads before them need not wait for these; past the table every
+    // lane reads the first fragment of the first step (one cache line; never
+    // used).
     auto load_up = [&](int rt) __attribute__((always_inline)) {
         const int row = rt * TRW + wr + lo;
 #pragma unroll
         for (int s = 0; s < PSTEPS; ++s) {
-            const StepDesc& sd = sdl[s < p.steps ? s : p.steps - 1];
-            bn[s] = ld_up8(sd.up + (int64_t)(row - sd.off) * sd.rank + 8 * hi);
+            const StepDesc& sd = sdl[s < p.steps ? s : 0];
+            bn[s] = ld_up8(s < p.steps ? sd.up + (int64_t)(row - sd.off) * sd.rank + 8 * hi : sd.up);
         }
     };
     if (gr < nrt) load_w(gr, 0);  // in flight while down^T is staged
@@ -971,6 +976,123 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     }
 }
 
+
+// The unit kernel: bf16 weight and output, every low-rank patch over every
+// row (ranks multiples of 16), one workgroup of 12 waves per CU (3 per SIMD)
+// and per unit of UR = 384 rows x UC = 384 columns.  down^T of the unit's
+// columns is staged once; wave w owns rows 32 w of the unit, loads their `up`
+// fragments once and walks the unit's six 64-column quarters through its LDS
+// region, so each fragment serves 384 columns (three times the wide kernel's
+// 128) and its rows are read by a third as many workgroups.  Units are
+// numbered row block first: workgroup b runs on XCD b % 8, so with a multiple
+// of 8 row blocks each row block's `up` rows are read on one XCD.
+constexpr int UW = 12;       // waves per workgroup
+constexpr int UNT = 64 * UW; // lanes per workgroup
+constexpr int UR = 32 * UW;  // unit rows
+constexpr int UQ = 6;        // 64-column quarters per unit
+constexpr int UC = 64 * UQ;  // unit columns
+
+inline size_t unit_lds_bytes(int kt_all) {
+    return (size_t)UW * 32 * (64 * 2 + 16) + (size_t)UC * (kt_all + 8) * 2;
+}
+
+template <bool SM1>
+__global__ __launch_bounds__(UNT) __attribute__((amdgpu_waves_per_eu(3, 3))) void patch_lowrank_unit_kernel(WeightParams p) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int WROW = 64 * 2 + 16;
+    const int t = (int)threadIdx.x, l = t & 63, wave = t >> 6;
+    const int hi = l >> 5, lo = l & 31;
+    unsigned char* rg = lds + wave * 32 * WROW;  // this wave's region
+    bf16_t* sdt = reinterpret_cast<bf16_t*>(lds + UW * 32 * WROW);
+    const int kp = p.kt_all + 8;
+    const int nrb = p.rows / UR;
+    const int rb = (int)blockIdx.x % nrb, cs = (int)blockIdx.x / nrb;
+    const int c0 = cs * UC, r0 = rb * UR + 32 * wave;  // the unit's first column, the wave's first row
+
+    __shared__ StepDesc sdl[PSTEPS];
+    if (t == 0) {
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) sdl[s] = p.sd[s];
+    }
+    const bf16_t* w = static_cast<const bf16_t*>(p.w);
+    bf16_t* out = static_cast<bf16_t*>(p.out);
+    Raw8<bf16_t> wn[4];
+    bf16x8_t bn[PSTEPS];
+    // quarter h of the wave's rows, streaming layout
+    auto load_w = [&](int h) __attribute__((always_inline)) {
+        const int qc = c0 + 64 * h + 8 * (l & 7);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wn[j] = raw_load<true>(w, (int64_t)(r0 + (l >> 3) + 8 * j) * p.cols + qc, 8, true);
+    };
+    load_w(0);  // in flight while down^T is staged
+    stage_down<UC, UNT>(p, sdt, kp, c0, true);
+    __syncthreads();  // the only workgroup barrier: down^T and the step table are in place
+    {
+        // every fragment load on every path; past the table every lane reads
+        // the first fragment of the first step (never used)
+        const int row = r0 + lo;
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) {
+            const StepDesc& sd = sdl[s < p.steps ? s : 0];
+            bn[s] = ld_up8(s < p.steps ? sd.up + (int64_t)(row - sd.off) * sd.rank + 8 * hi : sd.up);
+        }
+    }
+    const int row = r0 + lo;
+#pragma unroll
+    for (int h = 0; h < UQ; ++h) {
+        const int wc = 64 * h, cl = c0 + wc + 32 * hi;
+        const int qc = c0 + wc + 8 * (l & 7);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw_lds_st(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * 2, wn[j]);
+        if (h + 1 < UQ) load_w(h + 1);
+        __builtin_amdgcn_wave_barrier();
+        float a[4][8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw_unpack(raw_lds_ld<bf16_t>(rg + lo * WROW + (32 * hi + 8 * j) * 2), a[j]);
+        const int colw0 = wc + sub_col(lo, 0), colw1 = wc + sub_col(lo, 1);
+        f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < PSTEPS; ++s) {
+            if (s >= p.steps) break;
+            const StepDesc sd = sdl[s];
+            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(sdt + dslot(colw0) * kp + 16 * s + 8 * hi);
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(sdt + dslot(colw1) * kp + 16 * s + 8 * hi);
+            if (sd.sk == 0) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], f32x16_t{}, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], f32x16_t{}, 0, 0, 0);
+            } else {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bn[s], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bn[s], acc1, 0, 0, 0);
+            }
+            if (sd.flags & 2) {  // the patch's last k-step
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    if constexpr (SM1) {
+                        a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], a[v >> 3][v & 7]);
+                        a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], a[2 + (v >> 3)][v & 7]);
+                    } else {
+                        a[v >> 3][v & 7] = fmaf(sd.sp, acc0[v], sd.sm * a[v >> 3][v & 7]);
+                        a[2 + (v >> 3)][v & 7] = fmaf(sd.sp, acc1[v], sd.sm * a[2 + (v >> 3)][v & 7]);
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = cl + 8 * j;
+            const Raw8<bf16_t> r = raw_pack<bf16_t>(p, a[j], (int64_t)row * p.cols + c, 8, true);
+            raw_lds_st(rg + lo * WROW + (32 * hi + 8 * j) * 2, r);
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            raw_store<true>(out, (int64_t)(r0 + (l >> 3) + 8 * j) * p.cols + qc, 8, true,
+                            raw_lds_ld<bf16_t>(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * 2));
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 inline size_t strip_lds_bytes(int es, int kt_all) {
     return (size_t)4 * 32 * (64 * es + 16) + (size_t)TC * (kt_all + 8) * 2;
 }
@@ -1013,6 +1135,15 @@ hipError_t launch(const WeightParams& p, int kind, unsigned blocks, hipStream_t 
                 reinterpret_cast<const void*>(&patch_lowrank_strip_kernel<TW, TO, false, false>), lmax, done[0]);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL((patch_lowrank_strip_kernel<TW, TO, false, false>), dim3(blocks), dim3(NT), lds, s, p);
+        } else if (sizeof(TW) == 2 && sizeof(TO) == 2 && p.nodiff && p.full && p.wide && p.unit) {  // bf16 in and out
+            static std::atomic<uint64_t> done6[2] = {{0}, {0}};
+            const size_t umax = unit_lds_bytes(16 * PSTEPS), ulds = unit_lds_bytes(p.kt_all);
+            const void* fn = p.sm1 ? reinterpret_cast<const void*>(&patch_lowrank_unit_kernel<true>)
+                                   : reinterpret_cast<const void*>(&patch_lowrank_unit_kernel<false>);
+            const hipError_t e = lds_limit(fn, umax, done6[p.sm1 ? 0 : 1]);
+            if (e != hipSuccess) return e;
+            if (p.sm1) hipLaunchKernelGGL((patch_lowrank_unit_kernel<true>), dim3(blocks), dim3(UNT), ulds, s, p);
+            else hipLaunchKernelGGL((patch_lowrank_unit_kernel<false>), dim3(blocks), dim3(UNT), ulds, s, p);
         } else if (sizeof(TW) == 2 && sizeof(TO) == 2 && p.nodiff && p.full && p.wide) {  // bf16 in and out
             static std::atomic<uint64_t> done5[2] = {{0}, {0}};
             if (p.sm1) {
@@ -1186,6 +1317,8 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
                     p.full = 0;
             }
             p.wide = p.full && a->rows % 128 == 0 && p.vec;
+            const int64_t units = (int64_t)(a->rows / UR) * (a->cols / UC);
+            p.unit = p.wide && a->rows % UR == 0 && a->cols % UC == 0 && units % 256 == 0;
             for (int q = 0; q < a->num_patches; ++q) {
                 const bcg_patch& e = a->patches[q];
                 if (e.kind != BCG_PATCH_LOWRANK || e.rows <= 0) continue;
@@ -1207,7 +1340,7 @@ extern "C" int weight_patch(const bcg_weight_args* a, void* stream) {
             int64_t g = kResident / ctiles;
             g = g < 1 ? 1 : (g > rtiles ? rtiles : g);
             p.grows = (int)g;
-            blocks = ctiles * g;
+            blocks = p.unit ? units : ctiles * g;
         } else {
             kind = K_TILE;
             blocks = rtiles * ctiles;

@@ -243,6 +243,34 @@ def test_weight_patch_large_workloads_sampled_rows(name):
     assert mism <= 1e-3 * len(rows) * sp.cols
 
 
+# Every low-rank patch over a 12288 x 3072 weight: 256 units of 384 x 384, one
+# workgroup per CU (the unit kernel); strength_model != 1 in the first set,
+# the most concatenated rank (128) in the second.
+UNIT = {"three_sets_sm": (WW.PatchSpec("lowrank", rank=16, strength_patch=1.0),
+                          WW.PatchSpec("lowrank", rank=32, strength_patch=0.8, strength_model=0.75),
+                          WW.PatchSpec("lowrank", rank=64, strength_patch=-0.6)),
+        "rank_128": (WW.PatchSpec("lowrank", rank=48, strength_patch=0.5),
+                     WW.PatchSpec("lowrank", rank=80, strength_patch=-1.5))}
+
+
+@pytest.mark.parametrize("name", list(UNIT))
+def test_weight_patch_unit_kernel_sampled_rows_bit_exact(name):
+    """Dyadic factors (every partial sum a float32 number): sampled rows, in
+    every unit row position and every wave of a unit, bit for bit against the
+    oracle's float32 order with its Philox bits."""
+    sp = WW.WeightSpec(name="unit", rows=12288, cols=3072, w_dtype="bf16", out_dtype="bf16",
+                       patches=UNIT[name], rounding="stochastic", sr_seed=0x0F1E_2D3C_4B5A_6978,
+                       seed=7, dyadic=True)
+    inp = WW.make_weight_inputs(sp)
+    got = _run(inp)
+    rng = np.random.default_rng(11)
+    rows = sorted({0, 31, 32, 383, 384, 6143, 12287} | {int(r) for r in rng.integers(0, sp.rows, 40)})
+    for r in rows:
+        sub = _row_inputs(inp, r)
+        code = P.sr_bf16(P.reference32(sub)[0], sp.sr_seed, base=r * sp.cols)
+        assert np.array_equal(got[r], code), f"row {r}: {np.sum(got[r] != code)} elements differ"
+
+
 def _misaligned(a, dtype=torch.bfloat16):
     """A contiguous device copy of `a` whose data pointer is 2 bytes past a
     16-byte boundary (a view one element into a larger buffer)."""
