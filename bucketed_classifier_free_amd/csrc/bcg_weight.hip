@@ -3,9 +3,9 @@
 // and weight views": "patches record format", "strength_model and
 // strength_patch", "offset patch", "how a weight is patched").
 //
-// Three kernels; all apply the patches of a weight in order (a = fma(sp, d,
-// sm * a) per element in fp32 registers), load and store each weight element
-// once, and round on the store.
+// Every kernel applies the patches of a weight in order (a = fma(sp, d,
+// sm * a) per element in fp32 registers), loads and stores each weight
+// element once, and rounds on the store.
 //
 //   patch_stream_kernel  (no low-rank patch): the weight as a flat sequence
 //     of 8-element row vectors (16-byte accesses, consecutive lanes on
@@ -27,6 +27,9 @@
 //     strip kernel with 128-row tiles, each wave taking 32 rows of both of
 //     the strip's 64-column halves in turn, so each `up` fragment it loads
 //     serves 128 columns.
+//   patch_lowrank_unit_kernel (the same conditions, rows and columns
+//     multiples of 384 in a multiple of 256 units): one 12-wave workgroup per
+//     CU and 384 x 384 unit, each wave's `up` fragments serving 384 columns.
 //   patch_lowrank_kernel (larger ranks): 64 x 128 tiles; the factors of the
 //     low-rank patches meeting the tile are concatenated along k and staged
 //     per tile, up to 128 k-rows per round, by direct global-to-LDS loads;
