@@ -984,8 +984,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 // row (ranks multiples of 16), one workgroup of 12 waves per CU (3 per SIMD)
 // and per unit of UR = 384 rows x UC = 384 columns.  down^T of the unit's
 // columns is staged once; wave w owns rows 32 w of the unit, loads their `up`
-// fragments once and walks the unit's six 64-column quarters through its LDS
-// region, so each fragment serves 384 columns (three times the wide kernel's
+// fragments once and walks the unit's six 64-column quarters (from a
+// staggered start) through its LDS region, so each fragment serves 384
+// columns (three times the wide kernel's
 // 128) and its rows are read by a third as many workgroups.  Units are
 // numbered row block first: workgroup b runs on XCD b % 8, so with a multiple
 // of 8 row blocks each row block's `up` rows are read on one XCD.
@@ -1021,9 +1022,14 @@ __global__ __launch_bounds__(UNT) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     bf16_t* out = static_cast<bf16_t*>(p.out);
     Raw8<bf16_t> wn[4];
     bf16x8_t bn[PSTEPS];
-    // quarter h of the wave's rows, streaming layout
+    // The wave walks the unit's quarters starting at (strip + wave) mod 6, so
+    // that the waves of a CU, and the units of a row block, stream different
+    // columns at a time (measured 0.4 us faster than every wave in column
+    // order, 0.6 us than one start per workgroup).
+    auto qof = [&](int h) { return (h + cs + wave) % UQ; };
+    // step h of the walk: its quarter of the wave's rows, streaming layout
     auto load_w = [&](int h) __attribute__((always_inline)) {
-        const int qc = c0 + 64 * h + 8 * (l & 7);
+        const int qc = c0 + 64 * qof(h) + 8 * (l & 7);
 #pragma unroll
         for (int j = 0; j < 4; ++j) wn[j] = raw_load<true>(w, (int64_t)(r0 + (l >> 3) + 8 * j) * p.cols + qc, 8, true);
     };
@@ -1043,7 +1049,7 @@ __global__ __launch_bounds__(UNT) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int row = r0 + lo;
 #pragma unroll
     for (int h = 0; h < UQ; ++h) {
-        const int wc = 64 * h, cl = c0 + wc + 32 * hi;
+        const int wc = 64 * qof(h), cl = c0 + wc + 32 * hi;
         const int qc = c0 + wc + 8 * (l & 7);
 #pragma unroll
         for (int j = 0; j < 4; ++j) raw_lds_st(rg + ((l >> 3) + 8 * j) * WROW + 8 * (l & 7) * 2, wn[j]);
