@@ -243,14 +243,21 @@ def test_weight_patch_large_workloads_sampled_rows(name):
     assert mism <= 1e-3 * len(rows) * sp.cols
 
 
-# Every low-rank patch over a 12288 x 3072 weight: 256 units of 384 x 384, one
-# workgroup per CU (the unit kernel); strength_model != 1 in the first set,
-# the most concatenated rank (128) in the second.
-UNIT = {"three_sets_sm": (WW.PatchSpec("lowrank", rank=16, strength_patch=1.0),
-                          WW.PatchSpec("lowrank", rank=32, strength_patch=0.8, strength_model=0.75),
-                          WW.PatchSpec("lowrank", rank=64, strength_patch=-0.6)),
-        "rank_128": (WW.PatchSpec("lowrank", rank=48, strength_patch=0.5),
-                     WW.PatchSpec("lowrank", rank=80, strength_patch=-1.5))}
+# Every low-rank patch over every row of a weight of 384 x 384 units, a
+# multiple of 256 of them (the unit kernel, one workgroup per CU): strength_model
+# != 1, the most concatenated rank (128), two rounds of workgroups, four strips.
+UNIT = {"three_sets_sm": ((12288, 3072), (WW.PatchSpec("lowrank", rank=16, strength_patch=1.0),
+                                         WW.PatchSpec("lowrank", rank=32, strength_patch=0.8, strength_model=0.75),
+                                         WW.PatchSpec("lowrank", rank=64, strength_patch=-0.6))),
+        "rank_128": ((12288, 3072), (WW.PatchSpec("lowrank", rank=48, strength_patch=0.5),
+                                    WW.PatchSpec("lowrank", rank=80, strength_patch=-1.5))),
+        # 512 units: two rounds of workgroups
+        "two_rounds": ((12288, 6144), (WW.PatchSpec("lowrank", rank=32, strength_patch=0.7),
+                                       WW.PatchSpec("lowrank", rank=64, strength_patch=-0.3, strength_model=1.25))),
+        # four 384-column strips, 64 row blocks
+        "four_strips": ((24576, 1536), (WW.PatchSpec("lowrank", rank=16, strength_patch=2.0),
+                                        WW.PatchSpec("lowrank", rank=16, strength_patch=-1.0),
+                                        WW.PatchSpec("lowrank", rank=48, strength_patch=0.25)))}
 
 
 @pytest.mark.parametrize("name", list(UNIT))
@@ -258,13 +265,14 @@ def test_weight_patch_unit_kernel_sampled_rows_bit_exact(name):
     """Dyadic factors (every partial sum a float32 number): sampled rows, in
     every unit row position and every wave of a unit, bit for bit against the
     oracle's float32 order with its Philox bits."""
-    sp = WW.WeightSpec(name="unit", rows=12288, cols=3072, w_dtype="bf16", out_dtype="bf16",
-                       patches=UNIT[name], rounding="stochastic", sr_seed=0x0F1E_2D3C_4B5A_6978,
+    (rows, cols), pats = UNIT[name]
+    sp = WW.WeightSpec(name="unit", rows=rows, cols=cols, w_dtype="bf16", out_dtype="bf16",
+                       patches=pats, rounding="stochastic", sr_seed=0x0F1E_2D3C_4B5A_6978,
                        seed=7, dyadic=True)
     inp = WW.make_weight_inputs(sp)
     got = _run(inp)
     rng = np.random.default_rng(11)
-    rows = sorted({0, 31, 32, 383, 384, 6143, 12287} | {int(r) for r in rng.integers(0, sp.rows, 40)})
+    rows = sorted({0, 31, 32, 383, 384, sp.rows // 2 - 1, sp.rows - 1} | {int(r) for r in rng.integers(0, sp.rows, 40)})
     for r in rows:
         sub = _row_inputs(inp, r)
         code = P.sr_bf16(P.reference32(sub)[0], sp.sr_seed, base=r * sp.cols)
