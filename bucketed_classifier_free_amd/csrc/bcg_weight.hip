@@ -986,8 +986,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 // columns is staged once; wave w owns rows 32 w of the unit, loads their `up`
 // fragments once and walks the unit's six 64-column quarters (from a
 // staggered start) through its LDS region, so each fragment serves 384
-// columns (three times the wide kernel's
-// 128) and its rows are read by a third as many workgroups.  Units are
+// columns (three times the wide kernel's 128) and its rows are read by a
+// third as many workgroups.  Units are
 // numbered row block first: workgroup b runs on XCD b % 8, so with a multiple
 // of 8 row blocks each row block's `up` rows are read on one XCD.
 constexpr int UW = 12;       // waves per workgroup
@@ -1024,8 +1024,8 @@ __global__ __launch_bounds__(UNT) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     bf16x8_t bn[PSTEPS];
     // The wave walks the unit's quarters starting at (strip + wave) mod 6, so
     // that the waves of a CU, and the units of a row block, stream different
-    // columns at a time (measured 0.4 us faster than every wave in column
-    // order, 0.6 us than one start per workgroup).
+    // columns at a time (measured 1.0 us faster than every wave in column
+    // order, 0.6 us faster than one start per workgroup at strip mod 6).
     auto qof = [&](int h) { return (h + cs + wave) % UQ; };
     // step h of the walk: its quarter of the wave's rows, streaming layout
     auto load_w = [&](int h) __attribute__((always_inline)) {
