@@ -364,10 +364,10 @@ def device_plan(steps: int, bucket_cfg, step_in, *, step_out=None, cfg_override=
     R = 0
     if region_range is not None:
         _dev(region_range, "region_range", torch.float64)
-        if region_range.dim() != 3 or region_range.shape[0] != n or region_range.shape[2] != 2:
-            raise ValueError("region_range must be [n, R, 2]")
+        if region_range.dim() != 3 or region_range.shape[0] != nt or region_range.shape[2] != 2:
+            raise ValueError("region_range must be [n, R, 2] (one row per request under continuous batching)")
         R = region_range.shape[1]
-        _dev(covered_sets, "covered_sets", torch.int16, (n,))
+        _dev(covered_sets, "covered_sets", torch.int16, (nt,))
     _dev(region_count, "region_count", torch.int32, (nt,), allow_none=True)
     _dev(record_in, "record_in", torch.float32, (n, 4), allow_none=True)
     _dev(record_out, "record_out", torch.float32, (n, 4), allow_none=True)

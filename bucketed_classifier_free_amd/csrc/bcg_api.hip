@@ -353,7 +353,6 @@ int check_dplan(const bcg_device_plan* d, int n, bool step, const char* who) {
             !d->record_in || !d->record_out || !d->step_out)
             return fail(BCG_EINVAL, "%s: continuous batching needs noise, slot_req_in/out, queue_in/out, "
                         "record_in/out and step_out", who);
-        if (d->region_range) return fail(BCG_EINVAL, "%s: continuous batching takes no validity ranges", who);
         const size_t in4 = (size_t)n * 4;
         if (any_overlap(d->slot_req_in, in4, d->slot_req_out, in4) || any_overlap(d->queue_in, 4, d->queue_out, 4))
             return fail(BCG_EINVAL, "%s: slot_req_out / queue_out overlap their inputs", who);

@@ -335,8 +335,10 @@ size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
  * samples of several buckets, section 4 stage 3: the scheduler builds every
  * step's plan): the n samples are slots, each holding a request of a queue of
  * queue_len.  slot_req_in[s] is the request of slot s (-1: empty), step_in[s]
- * its step; every per-sample table (cfg_override, covered, and the step's
- * mu / region / x_orig / mask arrays) and `noise` are indexed by request.
+ * its step; every per-sample table (cfg_override, covered, region_range,
+ * covered_sets, region_count, and the step's mu / region / x_orig / mask
+ * arrays) and `noise` are indexed by request, so a request's regions take
+ * part over its own validity ranges of its own progress.
  * The plan (rows, order, ...) is over slots.  For the next step the plan
  * workgroup writes step_out, slot_req_out, record_out and queue_out: a slot
  * whose request takes its last step now (t = steps - 1), and an empty slot,
@@ -349,8 +351,7 @@ size_t guided_step_workspace_size(int n, int C, int H, int W, int dtype);
  * guided_step_dplan from noise[r] * sigma (+ the stored x_orig[r] when
  * inpainting, one fused multiply-add), rounded to the storage dtype, then
  * stepped; the slot's previous contents are not read.  Requires records in
- * and out, step_out, the 16-byte vector path, no stats and no validity
- * ranges; wrap must be 0.  bcg_plan_records (OR'ing in the join bit and the
+ * and out, step_out, the 16-byte vector path and no stats; wrap must be 0.  bcg_plan_records (OR'ing in the join bit and the
  * request) gives the first step's records.
  *
  * The device arrays are not validated (a host plan build validates the same

@@ -597,18 +597,21 @@ def stored_orig(inp):
     return to_storage(inp.x_orig, inp.spec.dtype)
 
 
+def covered_at(inp, i: int, t=None) -> bool:
+    """Whether sample i's regions valid at step t (all of them if t is None)
+    cover the frame; a sample without regions is covered."""
+    sp = inp.spec
+    if int(inp.region_count[i]) == 0:
+        return True
+    rs = valid_regions(inp, i, t)
+    boxes = [area_box(inp.region_frac[i, r], sp.H, sp.W) for r in rs]
+    return bool(covers_frame(boxes, inp.region_strength[i, rs], sp.H, sp.W))
+
+
 def coverage(inp, t=None):
     """Per-sample full-coverage flag (samples without regions are covered); with
     validity ranges, of the regions valid at each sample's step t[i]."""
-    sp = inp.spec
-    out = np.ones(sp.n, bool)
-    for i in range(sp.n):
-        k = int(inp.region_count[i])
-        if k > 0:
-            rs = valid_regions(inp, i, None if t is None else t[i])
-            boxes = [area_box(inp.region_frac[i, r], sp.H, sp.W) for r in rs]
-            out[i] = covers_frame(boxes, inp.region_strength[i, rs], sp.H, sp.W)
-    return out
+    return np.array([covered_at(inp, i, None if t is None else t[i]) for i in range(inp.spec.n)], bool)
 
 
 def run_setup(inp):
@@ -762,10 +765,12 @@ def serve_trajectory(inp, n_slots: int, launches: int, ring: bool = False, slots
     request's override and coverage), then every active slot in ``slots``
     (default all) takes its step, after joining if it joins there.  Returns
     the final slot states and, with ``keep``, the state after every launch,
-    plus the schedule.  Validity ranges are not part of this mode."""
+    plus the schedule.  With validity ranges ([S] "calc_cond_batch()": a cond
+    takes part while the current timestep is in its range) a request's
+    regions, and so its coverage, follow its own progress: the reading is
+    that serving a request changes nothing of its own trajectory."""
     sp = inp.spec
-    if inp.region_range is not None:
-        raise ValueError("continuous batching takes no validity ranges")
+    ranged = inp.region_range is not None
     sig, table, cov = run_setup(inp)
     sig64 = sig.astype(np.float64)
     req, tt, join = serve_schedule(inp.start_step, sp.steps, n_slots, sp.n, launches, ring)
@@ -776,8 +781,11 @@ def serve_trajectory(inp, n_slots: int, launches: int, ring: bool = False, slots
     for k in range(launches):
         r = req[k]
         ovk = np.where(r >= 0, ov[np.maximum(r, 0)], np.float32(np.nan)).astype(np.float32)
-        plan = build_plan(tt[k], sp.steps, sp.num_buckets, table, ovk, cov[np.maximum(r, 0)],
-                          table_end(inp))
+        if ranged:
+            covk = np.array([r[s] < 0 or covered_at(inp, int(r[s]), int(tt[k, s])) for s in range(n_slots)])
+        else:
+            covk = cov[np.maximum(r, 0)]
+        plan = build_plan(tt[k], sp.steps, sp.num_buckets, table, ovk, covk, table_end(inp))
         for s in idx:
             if r[s] < 0 or plan["bucket_id"][s] < 0:
                 continue
@@ -785,7 +793,8 @@ def serve_trajectory(inp, n_slots: int, launches: int, ring: bool = False, slots
             if join[k, s]:
                 x[s] = init_sample(inp, int(r[s]), sig64[ti], sp.dtype)
             x[s] = to_storage(step(x[s], sig64[ti], sig64[ti + 1], float(plan["scale"][s]),
-                                   sample_params(inp, int(r[s])), sp.sampler), sp.dtype)
+                                   sample_params(inp, int(r[s]), ti if ranged else None), sp.sampler),
+                              sp.dtype)
         if keep:
             states.append(x.copy())
     return x, states, (req, tt, join)

@@ -313,9 +313,10 @@ def init_sample32(inp, i, sigma):
 
 
 def serve_trajectory32(inp, n_slots, launches, ring=False, slots=None, keep=False):
-    """The continuously batched loop in mode M (the schedule and plans of
-    definition.serve_trajectory)."""
+    """The continuously batched loop in mode M (the schedule, plans and
+    validity ranges of definition.serve_trajectory)."""
     sp = inp.spec
+    ranged = inp.region_range is not None
     sig, table, cov = D.run_setup(inp)
     req, tt, join = D.serve_schedule(inp.start_step, sp.steps, n_slots, sp.n, launches, ring)
     x = np.zeros((n_slots, sp.C, sp.H, sp.W), np.float32)
@@ -326,18 +327,22 @@ def serve_trajectory32(inp, n_slots, launches, ring=False, slots=None, keep=Fals
     for k in range(launches):
         r = req[k]
         ovk = np.where(r >= 0, ov[np.maximum(r, 0)], np.float32(np.nan)).astype(np.float32)
-        plan = D.build_plan(tt[k], sp.steps, sp.num_buckets, table, ovk, cov[np.maximum(r, 0)],
-                            D.table_end(inp))
+        if ranged:
+            covk = np.array([r[s] < 0 or D.covered_at(inp, int(r[s]), int(tt[k, s])) for s in range(n_slots)])
+        else:
+            covk = cov[np.maximum(r, 0)]
+        plan = D.build_plan(tt[k], sp.steps, sp.num_buckets, table, ovk, covk, D.table_end(inp))
         for s in idx:
             if r[s] < 0 or plan["bucket_id"][s] < 0:
                 continue
             ri, ti = int(r[s]), int(tt[k, s])
-            if ri not in prms:
-                prms[ri] = params32(inp, ri)
+            key = (ri, ti) if ranged else ri
+            if key not in prms:
+                prms[key] = params32(inp, ri, ti if ranged else None)
             if join[k, s]:
                 x[s] = init_sample32(inp, ri, sig[ti])
             x[s] = _store(step32(x[s], sig[ti], sig[ti + 1], plan["scale"][s],
-                                 bool(plan["need_uncond"][s]), prms[ri], sp.sampler), sp.dtype)
+                                 bool(plan["need_uncond"][s]), prms[key], sp.sampler), sp.dtype)
         if keep:
             states.append(x.copy())
     return x, states, (req, tt, join)

@@ -93,6 +93,28 @@ def test_queue_drains_matching_mirror_every_launch(kw, shape):
     _check_final(inp, n, got[-1], xd, req)
 
 
+# the schedule and guidance variants under continuous batching: a mid-peak
+# curve with within-bucket interpolation, regions with validity ranges (each
+# request's own), Heun with inpainting
+QUEUE_VARIANTS = [dict(dtype="f32", sampler="euler", regions=2, region_ranges=True, bucket_interp=True,
+                       curve=W.Curve("mid_peak", 1.2, 3.0, 0.4)),
+                  dict(dtype="bf16", sampler="heun", regions=1, region_ranges=True, inpaint=True,
+                       curve=W.Curve("linear", 2.0, 1.0))]
+
+
+@pytest.mark.parametrize("kw", QUEUE_VARIANTS)
+def test_queue_variants_match_mirror_every_launch(kw):
+    n, Q = 4, 11
+    sp = W.small_spec(n=Q, C=3, H=16, W=24, steps=5, num_buckets=3, feather=3, skip_frac=0.25, **kw)
+    inp = W.make_inputs(sp)
+    launches = -(-Q // n) * sp.steps + sp.steps
+    got = _serve_gpu(inp, n, launches)
+    _, mstates, (req, _, _) = M.serve_trajectory32(inp, n, launches, keep=True)
+    for k in range(launches):
+        assert np.array_equal(got[k], mstates[k]), f"launch {k} differs from mode M"
+    assert (req[-1] == -1).all()
+
+
 @pytest.mark.parametrize("reps,graph,jf", [(1, 0, None), (2, 6, 0), (3, 4, 1), (1, 5, 2)])
 def test_queue_ring_replicas_and_graphs(reps, graph, jf):
     # the endless queue (request ids modulo the pool), several replicas served

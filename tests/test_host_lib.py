@@ -277,7 +277,7 @@ def test_device_plan_entry_points_validate_before_launch():
     ("noise", None, b"noise"),
     ("slot_req_out", None, b"slot_req"),
     ("queue_out", None, b"queue_in/out"),
-    ("region_range", 9, b"validity"),
+    ("region_range", 9, b"validity"),              # validity ranges without covered_sets
     ("join_front", 3, b"join_front"),              # more than the 2 slots
     ("join_in", None, b"join_in"),
 ])

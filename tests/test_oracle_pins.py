@@ -863,7 +863,11 @@ def test_serve_schedule_matches_event_simulation():
 
 
 @pytest.mark.parametrize("kw", [dict(dtype="f32", regions=2, inpaint=True),
-                                dict(dtype="bf16", sampler="heun", regions=1)])
+                                dict(dtype="bf16", sampler="heun", regions=1),
+                                # validity ranges follow each request's own progress
+                                dict(dtype="f32", regions=2, region_ranges=True, inpaint=True),
+                                dict(dtype="bf16", sampler="heun", regions=2, region_ranges=True,
+                                     bucket_interp=True, curve=W.Curve("mid_peak", 1.2, 3.0, 0.4))])
 def test_served_requests_equal_their_solo_runs(kw):
     # Per-request independence through the queue: each request's state after
     # its last step equals its own trajectory run alone (from its start step,
